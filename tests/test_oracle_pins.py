@@ -1,0 +1,355 @@
+"""Pins for the CPU oracle: checks against things other than the oracle.
+
+Each pin ties the oracle to something fixed outside it: a library routine
+(scipy's Sylvester Hadamard, torch's scaled-dot-product attention), a
+textbook matrix, hand-derived fixtures under tests/golden/, a closed-form
+identity, or a brute-force loop on tiny inputs.  The mutation test at the
+end plants plausible mistakes in a copy of the oracle (on the CPU) and
+checks that some pin fails for every one of them.
+"""
+import inspect
+import json
+import math
+import os
+import types
+
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+from oracle import kvq_oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rand_orthogonal(rng, d):
+    qm, rm = np.linalg.qr(rng.standard_normal((d, d)))
+    return qm * np.sign(np.diag(rm))[None, :]
+
+
+# ---------------------------------------------------------------- rotation
+def pin_hadamard_scipy(orc):
+    """Popcount definition == scipy's Sylvester construction (RotateKV (i))."""
+    for d in (2, 4, 32, 128):
+        H = orc.hadamard_rotation(d) * math.sqrt(d)
+        assert np.array_equal(np.rint(H), scipy.linalg.hadamard(d))
+        assert np.allclose(H, np.rint(H), atol=1e-12)
+
+
+def pin_hadamard_golden4(orc):
+    H4 = np.array(_load("hadamard4.json")["H4"], dtype=np.float64)
+    assert np.allclose(orc.hadamard_rotation(4) * 2.0, H4, atol=1e-15)
+
+
+def pin_hadamard_orthogonal(orc):
+    H = orc.hadamard_rotation(128)
+    Hi = np.rint(H * math.sqrt(128)).astype(np.int64)
+    assert np.array_equal(Hi @ Hi.T, 128 * np.eye(128, dtype=np.int64))
+    assert np.abs(H @ H.T - np.eye(128)).max() < 1e-14
+
+
+def pin_rotate_onehot_dense(orc):
+    """Row-vector convention: e_k R is row k of R (a non-symmetric R)."""
+    rng = np.random.default_rng(7)
+    R = _rand_orthogonal(rng, 128).astype(np.float32)
+    for k in (0, 5, 127):
+        e = np.zeros(128, np.float32)
+        e[k] = 1
+        y = orc.rotate_rows(e[None], R)[0]
+        assert np.array_equal(y, R[k])
+
+
+def pin_parseval_and_dot_invariance(orc):
+    """|xR| = |x| and (qR).(kR) = q.k for orthogonal R (fp64 rotation)."""
+    rng = np.random.default_rng(11)
+    for R in (orc.hadamard_rotation(128), _rand_orthogonal(rng, 128)):
+        x = rng.standard_normal((16, 128))
+        y = orc.rotate_rows(x, R).astype(np.float64)
+        rel = np.abs(np.linalg.norm(y, axis=1) / np.linalg.norm(x, axis=1) - 1)
+        assert rel.max() < 1e-6          # fp32 rounding of the result only
+        q = rng.standard_normal(128)
+        qr = q @ R
+        assert abs((qr @ (x @ R).T - q @ x.T)).max() < 1e-10
+
+
+# --------------------------------------------------------------- quantizer
+def _golden_group(case):
+    vals = [np.float32(float(v)) for v in case["values"]]
+    codes = list(case["codes"])
+    if case.get("fill_pattern_repeat"):
+        reps = 32 // len(vals)
+        vals = vals * reps
+        codes = codes * reps
+    else:
+        fill = np.float32(float(case["fill"]))
+        codes = codes + [0] * (32 - len(vals))
+        vals = vals + [fill] * (32 - len(vals))
+    return np.array(vals, np.float32), np.array(codes, np.uint8)
+
+
+def pin_quant_golden(orc):
+    for case in _load("quant_group_cases.json")["cases"]:
+        y, want_codes = _golden_group(case)
+        if case.get("fill") is not None and not case.get("fill_pattern_repeat"):
+            # the fill entries' codes follow from the fill value itself
+            fill = np.float32(float(case["fill"]))
+            want_codes = _fill_codes(case, want_codes, fill)
+        row = np.tile(y, 4)[None]               # four identical groups
+        codes, s, z = orc.quantize_rows(row)
+        assert float(s[0, 0]) == float(case["scale"]), case["name"]
+        assert float(z[0, 0]) == float(case["zero"]), case["name"]
+        assert np.array_equal(codes[0, :32], want_codes), case["name"]
+
+
+def _fill_codes(case, codes, fill):
+    n = len(case["values"])
+    vals = [np.float32(float(v)) for v in case["values"]]
+    for i in range(n, 32):
+        # the fill value equals one of the listed values; copy its code
+        j = vals.index(fill)
+        codes[i] = case["codes"][j]
+    return codes
+
+
+def pin_quant_grid_random(orc):
+    """Grid data z + j*s (exact in fp32) is recovered exactly."""
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        z = np.float16(rng.uniform(-4, 4))
+        s = np.float16(2.0 ** rng.uniform(-4, 1))
+        j = rng.integers(0, 4, size=(4, 32))
+        j[:, :4] = [0, 1, 2, 3]                   # every level present
+        y64 = float(z) + j * float(s)
+        y = y64.astype(np.float32)
+        if not np.array_equal(y.astype(np.float64), y64):
+            continue
+        codes, sc, zz = orc.quantize_rows(y.reshape(1, 128))
+        assert np.all(sc == s) and np.all(zz == z)
+        assert np.array_equal(codes.reshape(4, 32), j.astype(np.uint8))
+        xh = orc.dequantize(codes, sc, zz)
+        assert np.array_equal(xh.reshape(4, 32), y64)
+
+
+def pin_quant_nearest_level(orc):
+    """Every code picks the nearest of the four levels of its group (fp32
+    slop only), for random outlier data in both bases."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((64, 128)) * np.where(np.arange(128) % 37 == 3, 20, 1)
+    for R in (None, orc.hadamard_rotation(128)):
+        y = orc.rotate_rows(x, R)
+        codes, s, z = orc.quantize_rows(y)
+        lv = (np.arange(4)[None, None, :] * s.astype(np.float64)[..., None]
+              + z.astype(np.float64)[..., None])          # [64, 4, 4]
+        yg = y.astype(np.float64).reshape(64, 4, 32)
+        err = np.abs(yg[..., None] - lv[:, :, None, :])     # [64,4,32,4]
+        chosen = np.take_along_axis(err, codes.reshape(64, 4, 32, 1).astype(np.int64), -1)[..., 0]
+        best = err.min(-1)
+        slop = 1e-6 * (np.abs(yg) + 1)
+        assert np.all(chosen <= best + slop)
+
+
+# ----------------------------------------------------------------- packing
+def pin_pack_golden(orc):
+    for case in _load("pack_row.json")["cases"]:
+        c = np.array(case["codes"], np.uint8)[None]
+        assert list(orc.pack_codes(c)[0]) == case["bytes"]
+        assert np.array_equal(orc.unpack_codes(np.array([case["bytes"]], np.uint8)), c)
+
+
+def pin_pack_roundtrip(orc):
+    allb = np.arange(256, dtype=np.uint8)[None]
+    assert np.array_equal(orc.pack_codes(orc.unpack_codes(allb)), allb)
+    for b in range(256):
+        c = orc.unpack_codes(np.array([[b]], np.uint8))[0]
+        assert sum(int(c[i]) << (2 * i) for i in range(4)) == b
+
+
+# ------------------------------------------------------------------ decode
+def _random_cache(rng, B, H, T, d=128):
+    codes = rng.integers(0, 4, size=(B, H, T, d)).astype(np.uint8)
+    scales = rng.uniform(0.05, 0.6, size=(B, H, T, d // 32)).astype(np.float16)
+    zeros = rng.uniform(-1.0, 0.2, size=(B, H, T, d // 32)).astype(np.float16)
+    packed = kvq_oracle.pack_codes(codes)
+    return codes, scales, zeros, packed
+
+
+def _deq(codes, scales, zeros):
+    c = codes.reshape(*codes.shape[:-1], 4, 32).astype(np.float64)
+    return (c * scales.astype(np.float64)[..., None]
+            + zeros.astype(np.float64)[..., None]).reshape(codes.shape)
+
+
+def pin_decode_vs_sdpa(orc):
+    """Rotate q / un-rotate o over an exact cache == plain attention in the
+    original basis (torch SDPA, fp64), with GQA, dense per-head R and fp16
+    sink / residual tokens."""
+    rng = np.random.default_rng(9)
+    B, Hkv, G, T, d = 2, 2, 2, 12, 128
+    Hq = Hkv * G
+    Rh = np.stack([_rand_orthogonal(rng, d) for _ in range(Hkv)])
+    for R_heads, scale in ((Rh, None), (orc.hadamard_rotation(d), None), (None, 0.3)):
+        kcodes, ks, kz, kp = _random_cache(rng, B, Hkv, T)
+        vcodes, vs, vz, vp = _random_cache(rng, B, Hkv, T)
+        sink_k = rng.standard_normal((B, Hkv, 2, d)).astype(np.float16)
+        sink_v = rng.standard_normal((B, Hkv, 2, d)).astype(np.float16)
+        res_k = rng.standard_normal((B, Hkv, 3, d)).astype(np.float16)
+        res_v = rng.standard_normal((B, Hkv, 3, d)).astype(np.float16)
+        q = rng.standard_normal((B, Hq, d))
+        out = orc.decode_attention(q, (kp, ks, kz), (vp, vs, vz), 0, T, R_heads,
+                                   sink_k=sink_k, sink_v=sink_v, res_k=res_k,
+                                   res_v=res_v, softmax_scale=scale)
+        kr = _deq(kcodes, ks, kz)
+        vr = _deq(vcodes, vs, vz)
+        if R_heads is not None:
+            Rs = R_heads if R_heads.ndim == 3 else np.stack([R_heads] * Hkv)
+            kr = np.einsum("bhtj,hcj->bhtc", kr, Rs)   # k = k_rot R^T
+            vr = np.einsum("bhtj,hcj->bhtc", vr, Rs)
+        K = np.concatenate([sink_k.astype(np.float64), kr, res_k.astype(np.float64)], 2)
+        V = np.concatenate([sink_v.astype(np.float64), vr, res_v.astype(np.float64)], 2)
+        Kq = torch.from_numpy(np.repeat(K, G, axis=1))
+        Vq = torch.from_numpy(np.repeat(V, G, axis=1))
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q)[:, :, None, :], Kq, Vq, scale=scale)[:, :, 0].numpy()
+        assert np.abs(out - ref).max() <= 1e-11 * np.abs(ref).max()
+
+
+def pin_decode_bruteforce(orc):
+    """Plain loops over un-rotated tokens (k = k_hat R^T) with the original
+    query, T <= 16, Hadamard built by scipy."""
+    rng = np.random.default_rng(21)
+    d, T = 128, 9
+    R = scipy.linalg.hadamard(d) / math.sqrt(d)
+    kcodes, ks, kz, kp = _random_cache(rng, 1, 1, T)
+    vcodes, vs, vz, vp = _random_cache(rng, 1, 1, T)
+    q = rng.standard_normal((1, 1, d)).astype(np.float16)
+    out = orc.decode_attention(q, (kp, ks, kz), (vp, vs, vz), 0, T, R)[0, 0]
+
+    qv = [float(v) for v in q[0, 0]]
+    korig, vorig = [], []
+    for t in range(T):
+        for codes, sc, zz, dst in ((kcodes, ks, kz, korig), (vcodes, vs, vz, vorig)):
+            rot = [int(codes[0, 0, t, c]) * float(sc[0, 0, t, c // 32])
+                   + float(zz[0, 0, t, c // 32]) for c in range(d)]
+            dst.append([sum(rot[j] * R[c, j] for j in range(d)) for c in range(d)])
+    s = [sum(qv[c] * korig[t][c] for c in range(d)) / math.sqrt(d) for t in range(T)]
+    m = max(s)
+    p = [math.exp(x - m) for x in s]
+    L = sum(p)
+    ref = [sum(p[t] * vorig[t][c] for t in range(T)) / L for c in range(d)]
+    assert np.abs(out - np.array(ref)).max() < 1e-12 * max(abs(r) for r in ref)
+
+
+def pin_decode_large_scores(orc):
+    """Scores of order 1e4 (x50 sink-like keys) stay finite: softmax is
+    max-subtracted, and the result equals the limit (all mass on the top
+    token)."""
+    rng = np.random.default_rng(13)
+    d, T = 128, 8
+    kcodes, ks, kz, kp = _random_cache(rng, 1, 1, T)
+    vcodes, vs, vz, vp = _random_cache(rng, 1, 1, T)
+    sink_k = (rng.standard_normal((1, 1, 1, d)) * 50).astype(np.float16)
+    sink_v = rng.standard_normal((1, 1, 1, d)).astype(np.float16)
+    q = (sink_k[0, 0].astype(np.float64) * 2)          # aligned with the sink
+    out = orc.decode_attention(q[None], (kp, ks, kz), (vp, vs, vz), 0, T, None,
+                               sink_k=sink_k, sink_v=sink_v)
+    assert np.all(np.isfinite(out))
+    assert np.allclose(out[0, 0], sink_v[0, 0, 0].astype(np.float64), atol=1e-12)
+
+
+PINS = [
+    pin_hadamard_scipy, pin_hadamard_golden4, pin_hadamard_orthogonal,
+    pin_rotate_onehot_dense, pin_parseval_and_dot_invariance,
+    pin_quant_golden, pin_quant_grid_random, pin_quant_nearest_level,
+    pin_pack_golden, pin_pack_roundtrip,
+    pin_decode_vs_sdpa, pin_decode_bruteforce, pin_decode_large_scores,
+]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin(kvq_oracle)
+
+
+# ---------------------------------------------------- properties and format
+def test_hadamard_reduces_int2_error_on_outliers():
+    """Hadamard rotation lowers INT2 error on outlier data (KVLinC abstract:
+    the rotation reduces quantization error).  Property, not parity."""
+    from workloads import config, kv_tokens
+    cfg = config(1)
+    H = kvq_oracle.hadamard_rotation(128)
+    for which in ("K", "V"):
+        x = kv_tokens(cfg, which).numpy()[0, :, 0]            # [T, d] fp32
+        errs = []
+        for R in (None, H):
+            y = kvq_oracle.rotate_rows(x, R)
+            c, s, z = kvq_oracle.quantize_rows(y)
+            errs.append(np.mean((kvq_oracle.dequantize(c, s, z) - y) ** 2))
+        assert errs[1] < 0.6 * errs[0]
+
+
+def test_format_bits_per_element():
+    """2-bit codes + fp16 scale and zero per 32 channels = 3 bits/element,
+    18.75% of fp16 (the OptR page quotes roughly 75% savings, Key Details)."""
+    x = np.random.default_rng(0).standard_normal((3, 128)).astype(np.float32)
+    c, s, z = kvq_oracle.quantize_rows(x)
+    p = kvq_oracle.pack_codes(c)
+    nbytes = p.nbytes + s.nbytes + z.nbytes
+    assert nbytes * 8 / x.size == 3.0
+    assert nbytes / (x.size * 2) == 0.1875
+
+
+def test_tie_distance_marks_half_integers():
+    y = np.array([[0.0, 0.75, 0.125, 0.375] + [0.0] * 124], np.float32)
+    c, s, z = kvq_oracle.quantize_rows(y)
+    dist = kvq_oracle.tie_distance(y, None, s, z)
+    assert dist[0, 2] == 0.0 and dist[0, 3] == 0.0
+    assert dist[0, 1] == 0.5
+
+
+# ----------------------------------------------------------- mutation test
+MUTATIONS = [
+    ("un-rotation with R instead of R^T", "o_rot @ R64.T", "o_rot @ R64"),
+    ("query rotated by R^T", "qv @ R64\n", "qv @ R64.T\n"),
+    ("zero-point dropped in dequantization", "(c * s + z)", "(c * s)"),
+    ("round half up instead of half even", "np.clip(np.rint(u), 0, QMAX)",
+     "np.clip(np.floor(u + 0.5), 0, QMAX)"),
+    ("softmax scale 1/d", "1.0 / np.sqrt(float(d))", "1.0 / float(d)"),
+    ("divisor 4 instead of 3", "np.float32(QMAX), dtype", "np.float32(4), dtype"),
+    ("packing order swapped", "c[..., 0] | (c[..., 1] << 2)", "c[..., 1] | (c[..., 0] << 2)"),
+    ("fp16 values taken from keys", "p_f16 @ fv", "p_f16 @ fk"),
+    ("Hadamard parity or-ed", "parity ^= bits & 1", "parity |= bits & 1"),
+    ("GQA head mapping interleaved", "hq = hk * G + g", "hq = g * Hkv + hk"),
+    ("no max subtraction", "np.exp(s_int2 - m)", "np.exp(s_int2)"),
+    ("zero from the max", "zero_h = mn.astype", "zero_h = mx.astype"),
+    ("no clamp", "np.clip(np.rint(u), 0, QMAX)", "np.rint(u)"),
+    ("rotation transposed", "x64 @ np.asarray(R, dtype=np.float64)",
+     "x64 @ np.asarray(R, dtype=np.float64).T"),
+]
+
+
+def _mutant(old, new):
+    src = inspect.getsource(kvq_oracle)
+    assert src.count(old) >= 1, old
+    mod = types.ModuleType("oracle_mutant")
+    with np.errstate(all="ignore"):
+        exec(compile(src.replace(old, new, 1), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_planted_mistake(name, old, new):
+    mod = _mutant(old, new)
+    caught = []
+    for pin in PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(mod)
+        except Exception:  # AssertionError, or the mutant crashing
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches: {name}"
