@@ -90,13 +90,15 @@ def quantize_rows(y32: np.ndarray, group: int = GROUP):
     Per row and per group of `group` contiguous channels:
         mn, mx = min, max                       (exact)
         s32    = fp32( fp32(mx - mn) / 3 )      (IEEE fp32 ops)
-        scale  = fp16_rne(s32);  zero = fp16_rne(mn)
+        scale  = fp16_rne(s32);  zero = fp16_rne(mn + 0.0)
         if scale == 0: every code is 0
         else:  inv  = fp32(1 / fp32(scale))
                u    = fp32( fp32(y - fp32(zero)) * inv )
                code = clamp(rint_half_even(u), 0, 3)
     Codes are taken against the stored fp16 scale and zero so that
-    dequantization code*scale + zero is self-consistent.
+    dequantization code*scale + zero is self-consistent.  Adding +0.0 to the
+    minimum makes a zero minimum +0 whatever the signs of the group's zeros
+    (the minimum of -0 and +0 is otherwise unspecified).
 
     Returns (codes uint8 [..., d], scales fp16 [..., d/group],
     zeros fp16 [..., d/group]).
@@ -114,7 +116,7 @@ def quantize_rows(y32: np.ndarray, group: int = GROUP):
     rng32 = np.subtract(mx, mn, dtype=np.float32)
     s32 = np.divide(rng32, np.float32(QMAX), dtype=np.float32)
     scale_h = s32.astype(np.float16)
-    zero_h = mn.astype(np.float16)
+    zero_h = np.add(mn, np.float32(0), dtype=np.float32).astype(np.float16)
 
     scale32 = scale_h.astype(np.float32)
     zero32 = zero_h.astype(np.float32)

@@ -104,6 +104,8 @@ def pin_quant_golden(orc):
         codes, s, z = orc.quantize_rows(row)
         assert float(s[0, 0]) == float(case["scale"]), case["name"]
         assert float(z[0, 0]) == float(case["zero"]), case["name"]
+        if "zero_bits" in case:
+            assert int(z[0, 0].view(np.uint16)) == case["zero_bits"], case["name"]
         assert np.array_equal(codes[0, :32], want_codes), case["name"]
 
 
@@ -326,7 +328,8 @@ MUTATIONS = [
     ("Hadamard parity or-ed", "parity ^= bits & 1", "parity |= bits & 1"),
     ("GQA head mapping interleaved", "hq = hk * G + g", "hq = g * Hkv + hk"),
     ("no max subtraction", "np.exp(s_int2 - m)", "np.exp(s_int2)"),
-    ("zero from the max", "zero_h = mn.astype", "zero_h = mx.astype"),
+    ("zero from the max", "np.add(mn, np.float32(0)", "np.add(mx, np.float32(0)"),
+    ("signed zero kept", "np.add(mn, np.float32(0), dtype=np.float32)", "mn"),
     ("no clamp", "np.clip(np.rint(u), 0, QMAX)", "np.rint(u)"),
     ("rotation transposed", "x64 @ np.asarray(R, dtype=np.float64)",
      "x64 @ np.asarray(R, dtype=np.float64).T"),
