@@ -1,0 +1,164 @@
+/*
+ * kvq.h -- C ABI of the rotated INT2 KV-cache library (MI355X / gfx950).
+ *
+ * Two operations make up the hot path:
+ *
+ *   kvq_quantize          write path: rotate K and V rows by a per-head
+ *                         orthogonal R, quantize them to asymmetric 2-bit
+ *                         codes in channel groups, pack four codes per byte.
+ *   kvq_decode_attention  read path: one decode query per (batch, query
+ *                         head) attends over the packed cache (plus optional
+ *                         fp16 sink / residual tokens); the query is rotated
+ *                         by R, the output un-rotated by R^T.
+ *
+ * The method: "Output-Aware Rotation for INT2 KV-Cache Quantization"
+ * (woor.ai page, section "Key Details": a per-head orthogonal rotation is
+ * applied before INT2 quantization and removed after the attention
+ * computation; section "What You Need to Know": the readout is scaled
+ * dot-product attention).  The Hadamard form and its fast transform:
+ * RotateKV (IJCAI 2025 record, abstract item (i)) and KVLinC (fugumt page,
+ * abstract).  Sinks kept at higher precision: RotateKV abstract, item (iii).
+ * The pages fix no group size, scale format, rounding rule or bit layout;
+ * the format below is this library's.
+ *
+ * Conventions for every entry point
+ *  - Tensor pointers are DEVICE pointers (HIP global memory) owned by the
+ *    caller.  The library never allocates, frees or synchronizes on these
+ *    calls; work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *    stream) and runs asynchronously.
+ *  - Arguments are validated on the host before anything is enqueued.  A
+ *    failed check returns an error status and enqueues nothing.  A failed
+ *    kernel launch returns KVQ_ERR_HIP.  No C++ exception crosses the ABI.
+ *  - Device pointers must be 16-byte aligned (checked).
+ *  - Preconditions not checked: inputs are finite; every group's range
+ *    (max - min) / 3 and its minimum are within the fp16 range; buffers are
+ *    as large as the shapes say.
+ *  - There is no mutable global state; calls on different streams may run
+ *    concurrently as long as they do not write the same memory.
+ *
+ * Cache format (one side, K or V), head-major:
+ *    codes  uint8  [B][Hkv][T_cap][d/4]   channel 4b+i in bits 2i..2i+1 of
+ *                                          byte b
+ *    scales fp16   [B][Hkv][T_cap][d/32]   fp32(max-min)/3 rounded to fp16
+ *    zeros  fp16   [B][Hkv][T_cap][d/32]   group minimum rounded to fp16
+ *  with channel groups of 32 contiguous channels of the rotated row and
+ *    code = clamp(rint_half_even((y - zero) * fp32(1/scale)), 0, 3)
+ *  (all codes 0 when scale == 0), so that y ~= code * scale + zero.
+ *  3 bits per element; 18.75% of an fp16 cache.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_ABI_VERSION 1
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID_ARG = 1,        /* NULL/misaligned pointer, bad shape or range */
+  KVQ_ERR_UNSUPPORTED = 2,        /* valid but not implemented (d != 128, group != 32, ...) */
+  KVQ_ERR_WORKSPACE_TOO_SMALL = 3,
+  KVQ_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
+} kvq_status;
+
+typedef enum { KVQ_F16 = 0, KVQ_F32 = 1 } kvq_dtype;
+
+typedef enum {
+  KVQ_ROT_NONE = 0,      /* identity: rows are quantized as given            */
+  KVQ_ROT_HADAMARD = 1,  /* R = H_d / sqrt(d), H[i][j] = (-1)^popcount(i&j)  */
+  KVQ_ROT_DENSE = 2      /* R = caller's fp32 [Hkv][d][d] row-major, y = x R */
+} kvq_rot;
+
+/* One side (K or V) of an INT2 cache; all three arrays are device memory
+ * laid out as described above, sized for T_cap tokens per (b, head). */
+typedef struct {
+  uint8_t *codes;
+  uint16_t *scales;
+  uint16_t *zeros;
+  int64_t T_cap;
+} kvq_int2_cache;
+
+/*
+ * kvq_quantize -- rotate, quantize and pack T_new new tokens of K and V.
+ *
+ *  K, V       token rows, element type in_dtype; row (b, t, h) starts at
+ *             element b*stride_b + t*stride_t + h*stride_h and its d
+ *             channels are contiguous (channel stride 1).  For token-major
+ *             [B][T_new][Hkv][d]: stride_b = T_new*Hkv*d, stride_t = Hkv*d,
+ *             stride_h = d.  Either side may be skipped by passing NULL for
+ *             both its input and its cache; not both.
+ *  rot, R     KVQ_ROT_NONE / KVQ_ROT_HADAMARD with R == NULL, or
+ *             KVQ_ROT_DENSE with R = fp32 [Hkv][d][d] (device), y = x R_h.
+ *             The dense path needs in_dtype == KVQ_F16.
+ *  group      channels per scale/zero group; must be 32.
+ *  t_offset   the rows land in cache slots [t_offset, t_offset + T_new) of
+ *             every (b, h); must satisfy 0 <= t_offset, t_offset + T_new <=
+ *             T_cap of each cache.
+ *  d          head dimension; must be 128.
+ *  T_new == 0 (or B == 0) is a no-op returning KVQ_OK.
+ */
+kvq_status kvq_quantize(const void *K, const void *V, kvq_dtype in_dtype,
+                        int64_t B, int64_t T_new, int64_t Hkv, int64_t d,
+                        int64_t stride_b, int64_t stride_t, int64_t stride_h,
+                        kvq_rot rot, const float *R, int group,
+                        int64_t t_offset, const kvq_int2_cache *kc,
+                        const kvq_int2_cache *vc, void *stream);
+
+/*
+ * kvq_decode_workspace_bytes -- bytes of device workspace that
+ * kvq_decode_attention needs for these sizes (0 on invalid sizes).  Pure
+ * host arithmetic; calls nothing in HIP.
+ */
+size_t kvq_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
+                                  int64_t n_int2_tokens, int64_t n_sink,
+                                  int64_t n_res);
+
+/*
+ * kvq_decode_attention -- out[b][h] = softmax(q' K_hat^T * scale) V_hat R^T
+ * over INT2 tokens [t_begin, t_end) of the cache, jointly normalized with
+ * the optional fp16 tokens, for every batch b and query head h.
+ *
+ *  q          [B][Hq][d] contiguous, q_dtype.  Query head h reads KV head
+ *             h / (Hq/Hkv); Hq must be a multiple of Hkv.
+ *  kc, vc     INT2 caches (rotated basis); t_begin <= t_end <= T_cap.
+ *  rot, R     as for kvq_quantize; must match what wrote the cache.
+ *  sink_k/v   fp16 [B][Hkv][n_sink][d] tokens kept unquantized in the
+ *             ORIGINAL basis (NULL allowed when n_sink == 0).
+ *  res_k/v    fp16 [B][Hkv][n_res][d], same (a recent-token window).
+ *  softmax_scale  score multiplier; <= 0 selects 1/sqrt(d).
+ *  out        [B][Hq][d] contiguous, out_dtype.
+ *  workspace  device scratch of at least
+ *             kvq_decode_workspace_bytes(B, Hq, Hkv, d, t_end - t_begin,
+ *             n_sink, n_res) bytes; contents on entry are ignored.
+ *  The total token count (t_end - t_begin + n_sink + n_res) must be >= 1.
+ */
+kvq_status kvq_decode_attention(const void *q, kvq_dtype q_dtype,
+                                int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
+                                const kvq_int2_cache *kc,
+                                const kvq_int2_cache *vc,
+                                int64_t t_begin, int64_t t_end,
+                                kvq_rot rot, const float *R, int group,
+                                const uint16_t *sink_k, const uint16_t *sink_v,
+                                int64_t n_sink,
+                                const uint16_t *res_k, const uint16_t *res_v,
+                                int64_t n_res, float softmax_scale,
+                                void *out, kvq_dtype out_dtype,
+                                void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *kvq_status_str(kvq_status s);
+
+/* KVQ_ABI_VERSION of the built library. */
+int kvq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,47 @@
+"""Build the gfx950 shared library libkvq.so in-tree with hipcc."""
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libkvq.so")
+
+SOURCES = ["api.cpp", "kv_rotate_quant.hip", "kv_rotate_quant_dense.hip", "kv_decode.hip"]
+
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    # packed fp32 VALU ops stay disabled in device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def hipcc():
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    return os.path.join(rocm, "bin", "hipcc")
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile every HIP/C++ source into libkvq.so (always recompiles)."""
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    errs = [ln for ln in res.stderr.splitlines()
+            if "packed-fp32-ops' is not a recognized feature" not in ln]
+    if res.returncode != 0:
+        sys.stderr.write("\n".join(errs) + "\n")
+        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+    if verbose and errs:
+        sys.stderr.write("\n".join(errs) + "\n")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,184 @@
+// C ABI of the kvq library: argument validation (host only, before any HIP
+// call) and dispatch to the gfx950 kernels.  The operations are defined in
+// include/kvq.h.
+#include "kvq.h"
+
+#include <math.h>
+
+#include "kvq_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxFp16Tokens = 8192;   // sink + residual tokens per call
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool valid_dtype(kvq_dtype t) { return t == KVQ_F16 || t == KVQ_F32; }
+bool valid_rot(kvq_rot r) {
+  return r == KVQ_ROT_NONE || r == KVQ_ROT_HADAMARD || r == KVQ_ROT_DENSE;
+}
+
+kvq_status check_rotation(kvq_rot rot, const float *R) {
+  if (!valid_rot(rot)) return KVQ_ERR_INVALID_ARG;
+  if (rot == KVQ_ROT_DENSE) {
+    if (R == nullptr || !aligned16(R)) return KVQ_ERR_INVALID_ARG;
+  } else if (R != nullptr) {
+    return KVQ_ERR_INVALID_ARG;
+  }
+  return KVQ_OK;
+}
+
+kvq_status check_cache(const kvq_int2_cache *c) {
+  if (c == nullptr) return KVQ_ERR_INVALID_ARG;
+  if (c->codes == nullptr || c->scales == nullptr || c->zeros == nullptr) return KVQ_ERR_INVALID_ARG;
+  if (!aligned16(c->codes) || !aligned16(c->scales) || !aligned16(c->zeros)) return KVQ_ERR_INVALID_ARG;
+  if (c->T_cap <= 0) return KVQ_ERR_INVALID_ARG;
+  return KVQ_OK;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+size_t workspace_bytes(int64_t B, int64_t Hq, int64_t n_splits) {
+  const size_t qprep = align256((size_t)B * Hq * kvq::kQprepDwordsPerHead * 4);
+  const size_t parts = (size_t)B * Hq * n_splits * kvq::kPartialStride * sizeof(float);
+  return qprep + parts;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_quantize(const void *K, const void *V, kvq_dtype in_dtype, int64_t B,
+                        int64_t T_new, int64_t Hkv, int64_t d, int64_t stride_b,
+                        int64_t stride_t, int64_t stride_h, kvq_rot rot, const float *R,
+                        int group, int64_t t_offset, const kvq_int2_cache *kc,
+                        const kvq_int2_cache *vc, void *stream) {
+  if (!valid_dtype(in_dtype)) return KVQ_ERR_INVALID_ARG;
+  if (B < 0 || T_new < 0 || Hkv <= 0 || t_offset < 0) return KVQ_ERR_INVALID_ARG;
+  if (stride_b < 0 || stride_t < 0 || stride_h < 0) return KVQ_ERR_INVALID_ARG;
+  if (d != 128 || group != 32) return KVQ_ERR_UNSUPPORTED;
+  kvq_status st = check_rotation(rot, R);
+  if (st != KVQ_OK) return st;
+  if (rot == KVQ_ROT_DENSE && in_dtype != KVQ_F16) return KVQ_ERR_UNSUPPORTED;
+  if ((K == nullptr) != (kc == nullptr) || (V == nullptr) != (vc == nullptr)) return KVQ_ERR_INVALID_ARG;
+  if (K == nullptr && V == nullptr) return KVQ_ERR_INVALID_ARG;
+  const int64_t esize = in_dtype == KVQ_F32 ? 4 : 2;
+  if ((stride_b * esize) % 16 || (stride_t * esize) % 16 || (stride_h * esize) % 16) return KVQ_ERR_INVALID_ARG;
+
+  kvq::QuantArgs a{};
+  a.n_sides = 0;
+  const void *xs[2] = {K, V};
+  const kvq_int2_cache *cs[2] = {kc, vc};
+  for (int s = 0; s < 2; ++s) {
+    if (xs[s] == nullptr) continue;
+    if (!aligned16(xs[s])) return KVQ_ERR_INVALID_ARG;
+    st = check_cache(cs[s]);
+    if (st != KVQ_OK) return st;
+    if (t_offset > cs[s]->T_cap || T_new > cs[s]->T_cap - t_offset) return KVQ_ERR_INVALID_ARG;
+    kvq::QuantSide &q = a.side[a.n_sides++];
+    q.x = xs[s];
+    q.codes = cs[s]->codes;
+    q.scales = cs[s]->scales;
+    q.zeros = cs[s]->zeros;
+    q.T_cap = cs[s]->T_cap;
+  }
+  if (B * a.n_sides > 65535 || Hkv > 65535 || (T_new + 63) / 64 > 0x7FFFFFFF) return KVQ_ERR_UNSUPPORTED;
+  if (B == 0 || T_new == 0) return KVQ_OK;
+
+  a.in_f32 = in_dtype == KVQ_F32;
+  a.B = B; a.T_new = T_new; a.Hkv = Hkv;
+  a.stride_b = stride_b; a.stride_t = stride_t; a.stride_h = stride_h;
+  a.t_offset = t_offset;
+  a.rot = (int)rot;
+  a.R = R;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = (rot == KVQ_ROT_DENSE) ? kvq::launch_quantize_dense(a, s)
+                                        : kvq::launch_quantize_rows(a, s);
+  if (e == hipErrorNotSupported) return KVQ_ERR_UNSUPPORTED;
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+size_t kvq_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
+                                  int64_t n_int2_tokens, int64_t n_sink, int64_t n_res) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || d != 128) return 0;
+  if (n_int2_tokens < 0 || n_sink < 0 || n_res < 0) return 0;
+  const kvq::SplitPlan p = kvq::plan_splits(B, Hkv, n_int2_tokens);
+  return workspace_bytes(B, Hq, p.n_splits);
+}
+
+kvq_status kvq_decode_attention(const void *q, kvq_dtype q_dtype, int64_t B, int64_t Hq,
+                                int64_t Hkv, int64_t d, const kvq_int2_cache *kc,
+                                const kvq_int2_cache *vc, int64_t t_begin, int64_t t_end,
+                                kvq_rot rot, const float *R, int group,
+                                const uint16_t *sink_k, const uint16_t *sink_v, int64_t n_sink,
+                                const uint16_t *res_k, const uint16_t *res_v, int64_t n_res,
+                                float softmax_scale, void *out, kvq_dtype out_dtype,
+                                void *workspace, size_t workspace_bytes_given, void *stream) {
+  if (!valid_dtype(q_dtype) || !valid_dtype(out_dtype)) return KVQ_ERR_INVALID_ARG;
+  if (q == nullptr || out == nullptr || !aligned16(q) || !aligned16(out)) return KVQ_ERR_INVALID_ARG;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return KVQ_ERR_INVALID_ARG;
+  if (d != 128 || group != 32) return KVQ_ERR_UNSUPPORTED;
+  kvq_status st = check_rotation(rot, R);
+  if (st != KVQ_OK) return st;
+  if (t_begin < 0 || t_end < t_begin) return KVQ_ERR_INVALID_ARG;
+  const int64_t n_int2 = t_end - t_begin;
+  if (n_int2 > 0) {
+    if ((st = check_cache(kc)) != KVQ_OK) return st;
+    if ((st = check_cache(vc)) != KVQ_OK) return st;
+    if (t_end > kc->T_cap || t_end > vc->T_cap) return KVQ_ERR_INVALID_ARG;
+  }
+  if (n_sink < 0 || n_res < 0) return KVQ_ERR_INVALID_ARG;
+  if (n_sink > 0 && (sink_k == nullptr || sink_v == nullptr || !aligned16(sink_k) || !aligned16(sink_v)))
+    return KVQ_ERR_INVALID_ARG;
+  if (n_res > 0 && (res_k == nullptr || res_v == nullptr || !aligned16(res_k) || !aligned16(res_v)))
+    return KVQ_ERR_INVALID_ARG;
+  if (n_int2 + n_sink + n_res < 1) return KVQ_ERR_INVALID_ARG;
+  if (n_sink + n_res > kMaxFp16Tokens) return KVQ_ERR_UNSUPPORTED;
+  if (B * Hq > 0x7FFFFFFF) return KVQ_ERR_UNSUPPORTED;
+  if (!(softmax_scale == softmax_scale)) return KVQ_ERR_INVALID_ARG;   // NaN
+  const kvq::SplitPlan plan = kvq::plan_splits(B, Hkv, n_int2);
+  const size_t need = workspace_bytes(B, Hq, plan.n_splits);
+  if (workspace == nullptr || ((uintptr_t)workspace & 255u) != 0) return KVQ_ERR_INVALID_ARG;
+  if (workspace_bytes_given < need) return KVQ_ERR_WORKSPACE_TOO_SMALL;
+
+  kvq::DecodeArgs a{};
+  a.q = q;
+  a.q_f32 = q_dtype == KVQ_F32;
+  a.out_f32 = out_dtype == KVQ_F32;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv;
+  if (n_int2 > 0) {
+    a.kcodes = kc->codes; a.kscales = kc->scales; a.kzeros = kc->zeros; a.kT_cap = kc->T_cap;
+    a.vcodes = vc->codes; a.vscales = vc->scales; a.vzeros = vc->zeros; a.vT_cap = vc->T_cap;
+  }
+  a.t_begin = t_begin;
+  a.n_int2 = n_int2;
+  a.rot = (int)rot;
+  a.R = R;
+  a.sink_k = sink_k; a.sink_v = sink_v; a.n_sink = n_sink;
+  a.res_k = res_k; a.res_v = res_v; a.n_res = n_res;
+  const double scale = softmax_scale > 0.0f ? (double)softmax_scale : 1.0 / sqrt(128.0);
+  a.qscale = (float)(scale * 1.4426950408889634);   // natural -> base-2 exponent
+  a.out = out;
+  a.qprep = reinterpret_cast<int32_t *>(workspace);
+  a.partials = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) +
+                                         align256((size_t)B * Hq * kvq::kQprepDwordsPerHead * 4));
+  a.n_splits = plan.n_splits;
+  a.tokens_per_split = plan.tokens_per_split;
+  hipError_t e = kvq::launch_decode(a, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+const char *kvq_status_str(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "KVQ_OK";
+    case KVQ_ERR_INVALID_ARG: return "KVQ_ERR_INVALID_ARG";
+    case KVQ_ERR_UNSUPPORTED: return "KVQ_ERR_UNSUPPORTED";
+    case KVQ_ERR_WORKSPACE_TOO_SMALL: return "KVQ_ERR_WORKSPACE_TOO_SMALL";
+    case KVQ_ERR_HIP: return "KVQ_ERR_HIP";
+  }
+  return "KVQ_ERR_UNKNOWN";
+}
+
+int kvq_abi_version(void) { return KVQ_ABI_VERSION; }
+
+}  // extern "C"

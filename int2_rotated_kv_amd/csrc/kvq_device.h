@@ -1,0 +1,54 @@
+// Device-side helpers shared by the gfx950 kernels of the kvq library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+constexpr int kD = 128;        // head dimension
+constexpr int kGroup = 32;     // channels per scale/zero group
+constexpr int kNGroups = kD / kGroup;
+constexpr int kCodeBytes = kD / 4;   // packed bytes per row
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bits_as_float(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t float_as_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+// fp32 -> fp16 with round-to-nearest-even (v_cvt_f16_f32 in the default
+// rounding mode); subnormal fp16 results are kept.
+__device__ __forceinline__ uint16_t float_to_half_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Cross-lane moves inside a quad of four lanes (DPP quad_perm).
+// kQuadXor1: lane i reads lane i^1; kQuadXor2: lane i reads lane i^2.
+constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+
+template <int CTRL>
+__device__ __forceinline__ float quad_swap(float v) {
+  return bits_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)float_as_bits(v), CTRL, 0xF, 0xF, true));
+}
+
+// Butterfly across lanes of a quad: lanes whose bit is 0 get own + partner,
+// lanes whose bit is 1 get partner - own.  `neg` is -1.0f on the latter.
+template <int CTRL>
+__device__ __forceinline__ float quad_butterfly(float own, float neg) {
+  float other = quad_swap<CTRL>(own);
+  return __builtin_fmaf(own, neg, other);   // exact: own * (+-1) + other, one rounding
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+}  // namespace kvq

@@ -1,0 +1,66 @@
+// Internal host-side interface between the C ABI (api.cpp) and the kernel
+// translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvq {
+
+// One side (K or V) of a quantize call.
+struct QuantSide {
+  const void *x;        // token rows, channel stride 1
+  uint8_t *codes;
+  uint16_t *scales;
+  uint16_t *zeros;
+  int64_t T_cap;
+};
+
+struct QuantArgs {
+  QuantSide side[2];    // K, V (a side with x == nullptr is skipped)
+  int n_sides;
+  bool in_f32;
+  int64_t B, T_new, Hkv;
+  int64_t stride_b, stride_t, stride_h;
+  int64_t t_offset;
+  int rot;              // 0 none, 1 Hadamard, 2 dense
+  const float *R;       // dense: [Hkv][128][128]
+};
+
+hipError_t launch_quantize_rows(const QuantArgs &a, hipStream_t stream);
+hipError_t launch_quantize_dense(const QuantArgs &a, hipStream_t stream);
+
+// Decode.
+struct DecodeArgs {
+  const void *q;
+  bool q_f32, out_f32;
+  int64_t B, Hq, Hkv;
+  const uint8_t *kcodes; const uint16_t *kscales; const uint16_t *kzeros; int64_t kT_cap;
+  const uint8_t *vcodes; const uint16_t *vscales; const uint16_t *vzeros; int64_t vT_cap;
+  int64_t t_begin, n_int2;
+  int rot; const float *R;
+  const uint16_t *sink_k, *sink_v; int64_t n_sink;
+  const uint16_t *res_k, *res_v; int64_t n_res;
+  float qscale;         // softmax_scale * log2(e)
+  void *out;
+  // workspace carve-up (device pointers)
+  int32_t *qprep;       // [B][Hq][128] dwords
+  float *partials;      // [B][Hq][n_splits][kPartialStride]
+  int64_t n_splits;     // wave-splits per (b, kv head)
+  int64_t tokens_per_split;
+};
+
+// Split plan shared by the workspace query and the attention call.
+struct SplitPlan {
+  int64_t n_splits;
+  int64_t tokens_per_split;
+};
+SplitPlan plan_splits(int64_t B, int64_t Hkv, int64_t n_int2);
+
+constexpr int kQprepDwordsPerHead = 128;
+constexpr int kPartialStride = 132;   // o'[128], m, l, 2 pad (16-byte rows)
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
+}  // namespace kvq

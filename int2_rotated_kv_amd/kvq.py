@@ -1,0 +1,205 @@
+"""Thin ctypes binding over libkvq.so (the C ABI declared in include/kvq.h).
+
+Argument marshalling only: torch tensors are passed as device pointers and
+the current torch stream as the HIP stream.  Every step of the hot path
+runs in the library's HIP kernels; there is no fallback.  Loading fails
+loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
+
+KVQ_OK = 0
+KVQ_ERR_INVALID_ARG = 1
+KVQ_ERR_UNSUPPORTED = 2
+KVQ_ERR_WORKSPACE_TOO_SMALL = 3
+KVQ_ERR_HIP = 4
+
+KVQ_F16, KVQ_F32 = 0, 1
+KVQ_ROT_NONE, KVQ_ROT_HADAMARD, KVQ_ROT_DENSE = 0, 1, 2
+_ROT = {"none": KVQ_ROT_NONE, "hadamard": KVQ_ROT_HADAMARD, "dense": KVQ_ROT_DENSE}
+
+EXPORTED_SYMBOLS = ("kvq_quantize", "kvq_decode_workspace_bytes",
+                    "kvq_decode_attention", "kvq_status_str", "kvq_abi_version")
+
+D_HEAD = 128
+GROUP = 32
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {kvq_status_str(status)} ({status})")
+        self.status = status
+
+
+class kvq_int2_cache(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("zeros", ctypes.c_void_p), ("T_cap", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libkvq.so once; raise if it is missing (no fallback path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build() "
+                           "(hipcc --offload-arch=gfx950)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, vp, i32, f32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    cp = ctypes.POINTER(kvq_int2_cache)
+    lib.kvq_quantize.restype = i32
+    lib.kvq_quantize.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, i64, i64,
+                                 i32, vp, i32, i64, cp, cp, vp]
+    lib.kvq_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.kvq_decode_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, i64]
+    lib.kvq_decode_attention.restype = i32
+    lib.kvq_decode_attention.argtypes = [vp, i32, i64, i64, i64, i64, cp, cp, i64, i64,
+                                         i32, vp, i32, vp, vp, i64, vp, vp, i64, f32,
+                                         vp, i32, vp, ctypes.c_size_t, vp]
+    lib.kvq_status_str.restype = ctypes.c_char_p
+    lib.kvq_status_str.argtypes = [i32]
+    lib.kvq_abi_version.restype = i32
+    lib.kvq_abi_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def kvq_status_str(status: int) -> str:
+    return load_library().kvq_status_str(int(status)).decode()
+
+
+def kvq_abi_version() -> int:
+    return int(load_library().kvq_abi_version())
+
+
+def _check(status: int, where: str):
+    if status != KVQ_OK:
+        raise KvqError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float16:
+        return KVQ_F16
+    if t.dtype == torch.float32:
+        return KVQ_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class Int2Cache:
+    """Device buffers of one side (K or V) of an INT2 cache.
+
+    codes  uint8 [B, Hkv, T_cap, d/4]; scales / zeros fp16 [B, Hkv, T_cap, d/32]
+    """
+
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor):
+        self.codes, self.scales, self.zeros = codes, scales, zeros
+        self.T_cap = codes.shape[2]
+
+    @classmethod
+    def empty(cls, B: int, Hkv: int, T_cap: int, device="cuda", d: int = D_HEAD):
+        codes = torch.empty((B, Hkv, T_cap, d // 4), dtype=torch.uint8, device=device)
+        scales = torch.empty((B, Hkv, T_cap, d // GROUP), dtype=torch.float16, device=device)
+        zeros = torch.empty((B, Hkv, T_cap, d // GROUP), dtype=torch.float16, device=device)
+        return cls(codes, scales, zeros)
+
+    def c_struct(self) -> kvq_int2_cache:
+        return kvq_int2_cache(self.codes.data_ptr(), self.scales.data_ptr(),
+                              self.zeros.data_ptr(), self.T_cap)
+
+    def nbytes(self) -> int:
+        return self.codes.nbytes + self.scales.nbytes + self.zeros.nbytes
+
+
+def kvq_quantize(K, V, cache_k: Int2Cache | None, cache_v: Int2Cache | None,
+                 rot: str = "hadamard", R: torch.Tensor | None = None,
+                 group: int = GROUP, t_offset: int = 0, stream=None):
+    """Rotate, quantize and pack K/V rows [B, T_new, Hkv, d] (channel stride 1)
+    into cache slots [t_offset, t_offset + T_new).  Either side may be None."""
+    x = K if K is not None else V
+    for t in (K, V):
+        if t is not None and (t.dim() != 4 or t.stride(3) != 1):
+            raise ValueError("K/V must be [B, T_new, Hkv, d] with unit channel stride")
+    if K is not None and V is not None and (K.shape != V.shape or K.stride() != V.stride()
+                                            or K.dtype != V.dtype):
+        raise ValueError("K and V must share shape, strides and dtype")
+    B, T_new, Hkv, d = x.shape
+    kc = cache_k.c_struct() if cache_k is not None else None
+    vc = cache_v.c_struct() if cache_v is not None else None
+    st = load_library().kvq_quantize(
+        _ptr(K), _ptr(V), _dtype_code(x), B, T_new, Hkv, d,
+        x.stride(0), x.stride(1), x.stride(2), _ROT[rot], _ptr(R), group, t_offset,
+        ctypes.byref(kc) if kc is not None else None,
+        ctypes.byref(vc) if vc is not None else None, _stream(stream))
+    _check(st, "kvq_quantize")
+
+
+def kvq_decode_workspace_bytes(B, Hq, Hkv, d, n_int2_tokens, n_sink=0, n_res=0) -> int:
+    return int(load_library().kvq_decode_workspace_bytes(B, Hq, Hkv, d, n_int2_tokens,
+                                                         n_sink, n_res))
+
+
+def kvq_decode_attention(q: torch.Tensor, cache_k: Int2Cache | None,
+                         cache_v: Int2Cache | None, t_begin: int, t_end: int,
+                         rot: str = "hadamard", R: torch.Tensor | None = None,
+                         group: int = GROUP, sink_k=None, sink_v=None, res_k=None,
+                         res_v=None, softmax_scale: float = 0.0,
+                         out: torch.Tensor | None = None,
+                         workspace: torch.Tensor | None = None, stream=None):
+    """Decode attention for q [B, Hq, d] over INT2 tokens [t_begin, t_end)
+    plus optional fp16 sink / residual tokens [B, Hkv, n, d].  Returns out
+    [B, Hq, d] in q's dtype (or writes `out`)."""
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous [B, Hq, d]")
+    B, Hq, d = q.shape
+    Hkv = (cache_k.codes.shape[1] if cache_k is not None
+           else (sink_k if sink_k is not None else res_k).shape[1])
+    n_sink = 0 if sink_k is None else sink_k.shape[2]
+    n_res = 0 if res_k is None else res_k.shape[2]
+    for t in (sink_k, sink_v, res_k, res_v):
+        if t is not None and (t.dtype != torch.float16 or not t.is_contiguous()):
+            raise ValueError("sink/residual tensors must be contiguous fp16 [B, Hkv, n, d]")
+    if out is None:
+        out = torch.empty_like(q)
+    need = kvq_decode_workspace_bytes(B, Hq, Hkv, d, t_end - t_begin, n_sink, n_res)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    kc = cache_k.c_struct() if cache_k is not None else None
+    vc = cache_v.c_struct() if cache_v is not None else None
+    st = load_library().kvq_decode_attention(
+        _ptr(q), _dtype_code(q), B, Hq, Hkv, d,
+        ctypes.byref(kc) if kc is not None else None,
+        ctypes.byref(vc) if vc is not None else None,
+        t_begin, t_end, _ROT[rot], _ptr(R), group,
+        _ptr(sink_k), _ptr(sink_v), n_sink, _ptr(res_k), _ptr(res_v), n_res,
+        float(softmax_scale), _ptr(out), _dtype_code(out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "kvq_decode_attention")
+    return out
+
+
+def default_softmax_scale(d: int = D_HEAD) -> float:
+    return 1.0 / math.sqrt(d)

@@ -1,0 +1,171 @@
+"""CPU checks of the C-ABI library: it loads, exports every function the
+header declares, and rejects bad arguments on the host before any HIP call.
+
+No call here reaches a kernel launch: every call fails validation (fake,
+never dereferenced pointer values are used only where validation stops
+first), except the pure-arithmetic workspace query.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from int2_rotated_kv_amd import kvq as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+FAKE = 0x10000          # 16-byte aligned, never dereferenced
+FAKE_MISALIGNED = 0x10008
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return K.load_library()
+
+
+def test_header_declares_the_boundary():
+    assert header_functions() == sorted(K.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_header_function(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", K.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s+(kvq_\w+)", out))
+    for name in header_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_version_and_status_strings(lib):
+    assert K.kvq_abi_version() == 1
+    names = [K.kvq_status_str(s) for s in range(5)]
+    assert names == ["KVQ_OK", "KVQ_ERR_INVALID_ARG", "KVQ_ERR_UNSUPPORTED",
+                     "KVQ_ERR_WORKSPACE_TOO_SMALL", "KVQ_ERR_HIP"]
+    assert K.kvq_status_str(99) == "KVQ_ERR_UNKNOWN"
+
+
+def _cache(T_cap=64, codes=FAKE, scales=FAKE, zeros=FAKE):
+    return K.kvq_int2_cache(codes, scales, zeros, T_cap)
+
+
+def _quant(lib, **kw):
+    a = dict(K=FAKE, V=FAKE, dt=K.KVQ_F16, B=1, T=8, H=2, d=128, sb=8 * 2 * 128,
+             st=2 * 128, sh=128, rot=K.KVQ_ROT_HADAMARD, R=None, group=32, toff=0,
+             kc=_cache(), vc=_cache())
+    a.update(kw)
+    kc = ctypes.byref(a["kc"]) if a["kc"] is not None else None
+    vc = ctypes.byref(a["vc"]) if a["vc"] is not None else None
+    return lib.kvq_quantize(a["K"], a["V"], a["dt"], a["B"], a["T"], a["H"], a["d"],
+                            a["sb"], a["st"], a["sh"], a["rot"], a["R"], a["group"],
+                            a["toff"], kc, vc, None)
+
+
+QUANT_ERRORS = [
+    (dict(d=64), K.KVQ_ERR_UNSUPPORTED),
+    (dict(group=64), K.KVQ_ERR_UNSUPPORTED),
+    (dict(dt=7), K.KVQ_ERR_INVALID_ARG),
+    (dict(rot=9), K.KVQ_ERR_INVALID_ARG),
+    (dict(B=-1), K.KVQ_ERR_INVALID_ARG),
+    (dict(T=-1), K.KVQ_ERR_INVALID_ARG),
+    (dict(H=0), K.KVQ_ERR_INVALID_ARG),
+    (dict(toff=-1), K.KVQ_ERR_INVALID_ARG),
+    (dict(st=-128), K.KVQ_ERR_INVALID_ARG),
+    (dict(K=None), K.KVQ_ERR_INVALID_ARG),                 # input without cache
+    (dict(K=None, kc=None, V=None, vc=None), K.KVQ_ERR_INVALID_ARG),
+    (dict(K=FAKE_MISALIGNED), K.KVQ_ERR_INVALID_ARG),
+    (dict(sh=100), K.KVQ_ERR_INVALID_ARG),                 # row start not 16-byte aligned
+    (dict(kc=_cache(codes=0)), K.KVQ_ERR_INVALID_ARG),
+    (dict(kc=_cache(scales=FAKE_MISALIGNED)), K.KVQ_ERR_INVALID_ARG),
+    (dict(kc=_cache(T_cap=0)), K.KVQ_ERR_INVALID_ARG),
+    (dict(toff=60), K.KVQ_ERR_INVALID_ARG),                # 60 + 8 > T_cap 64
+    (dict(vc=_cache(T_cap=4)), K.KVQ_ERR_INVALID_ARG),
+    (dict(rot=K.KVQ_ROT_HADAMARD, R=FAKE), K.KVQ_ERR_INVALID_ARG),
+    (dict(rot=K.KVQ_ROT_DENSE, R=None), K.KVQ_ERR_INVALID_ARG),
+    (dict(rot=K.KVQ_ROT_DENSE, R=FAKE, dt=K.KVQ_F32, sb=8 * 2 * 128, st=256, sh=128),
+     K.KVQ_ERR_UNSUPPORTED),
+    (dict(B=70000), K.KVQ_ERR_UNSUPPORTED),                # grid z limit
+]
+
+
+@pytest.mark.parametrize("kw,want", QUANT_ERRORS, ids=[str(e[0]) for e in QUANT_ERRORS])
+def test_quantize_rejects(lib, kw, want):
+    assert _quant(lib, **kw) == want
+
+
+def test_quantize_empty_is_noop(lib):
+    # validated, then nothing to do: returns before any HIP call
+    assert _quant(lib, T=0) == K.KVQ_OK
+    assert _quant(lib, B=0) == K.KVQ_OK
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, qdt=K.KVQ_F16, B=2, Hq=4, Hkv=2, d=128, kc=_cache(), vc=_cache(),
+             tb=0, te=64, rot=K.KVQ_ROT_HADAMARD, R=None, group=32, sk=None, sv=None,
+             ns=0, rk=None, rv=None, nr=0, scale=0.0, out=FAKE, odt=K.KVQ_F16,
+             ws=FAKE * 16, wsb=1 << 30)
+    a.update(kw)
+    kc = ctypes.byref(a["kc"]) if a["kc"] is not None else None
+    vc = ctypes.byref(a["vc"]) if a["vc"] is not None else None
+    return lib.kvq_decode_attention(a["q"], a["qdt"], a["B"], a["Hq"], a["Hkv"], a["d"],
+                                    kc, vc, a["tb"], a["te"], a["rot"], a["R"], a["group"],
+                                    a["sk"], a["sv"], a["ns"], a["rk"], a["rv"], a["nr"],
+                                    a["scale"], a["out"], a["odt"], a["ws"], a["wsb"], None)
+
+
+DECODE_ERRORS = [
+    (dict(d=256), K.KVQ_ERR_UNSUPPORTED),
+    (dict(group=16), K.KVQ_ERR_UNSUPPORTED),
+    (dict(q=None), K.KVQ_ERR_INVALID_ARG),
+    (dict(out=FAKE_MISALIGNED), K.KVQ_ERR_INVALID_ARG),
+    (dict(qdt=3), K.KVQ_ERR_INVALID_ARG),
+    (dict(Hq=3), K.KVQ_ERR_INVALID_ARG),                   # not a multiple of Hkv
+    (dict(B=0), K.KVQ_ERR_INVALID_ARG),
+    (dict(tb=10, te=5), K.KVQ_ERR_INVALID_ARG),
+    (dict(te=65), K.KVQ_ERR_INVALID_ARG),                  # beyond T_cap
+    (dict(kc=None), K.KVQ_ERR_INVALID_ARG),
+    (dict(vc=_cache(zeros=0)), K.KVQ_ERR_INVALID_ARG),
+    (dict(ns=4), K.KVQ_ERR_INVALID_ARG),                   # sinks without pointers
+    (dict(nr=2, rk=FAKE, rv=None), K.KVQ_ERR_INVALID_ARG),
+    (dict(nr=9000, rk=FAKE, rv=FAKE), K.KVQ_ERR_UNSUPPORTED),
+    (dict(tb=0, te=0), K.KVQ_ERR_INVALID_ARG),             # no tokens at all
+    (dict(rot=K.KVQ_ROT_DENSE), K.KVQ_ERR_INVALID_ARG),    # dense without R
+    (dict(ws=None), K.KVQ_ERR_INVALID_ARG),
+    (dict(ws=FAKE + 16), K.KVQ_ERR_INVALID_ARG),           # workspace not 256-aligned
+    (dict(wsb=100), K.KVQ_ERR_WORKSPACE_TOO_SMALL),
+    (dict(scale=float("nan")), K.KVQ_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("kw,want", DECODE_ERRORS, ids=[str(e[0]) for e in DECODE_ERRORS])
+def test_decode_rejects(lib, kw, want):
+    assert _decode(lib, **kw) == want
+
+
+def test_workspace_bytes():
+    # invalid sizes give 0
+    assert K.kvq_decode_workspace_bytes(0, 4, 2, 128, 10) == 0
+    assert K.kvq_decode_workspace_bytes(1, 3, 2, 128, 10) == 0
+    assert K.kvq_decode_workspace_bytes(1, 4, 2, 64, 10) == 0
+    # query block (512 B per head, 256-aligned) + 132 floats per (head, split)
+    qprep = 16 * 32 * 512
+    ws = K.kvq_decode_workspace_bytes(16, 32, 32, 128, 32768)
+    assert ws > qprep and (ws - qprep) % (16 * 32 * 132 * 4) == 0
+    n_splits = (ws - qprep) // (16 * 32 * 132 * 4)
+    assert 1 <= n_splits <= 32768 // 256
+    # no INT2 tokens: only the query block
+    assert K.kvq_decode_workspace_bytes(1, 4, 2, 128, 0, 4, 8) == 4 * 512
+    # more tokens never need fewer splits
+    prev = 0
+    for n in (1, 100, 1000, 10000, 100000, 1000000):
+        w = K.kvq_decode_workspace_bytes(1, 8, 8, 128, n)
+        assert w >= prev
+        prev = w

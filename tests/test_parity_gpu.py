@@ -1,0 +1,274 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs.
+
+Bars:
+* quantize with no rotation: codes, scales and zeros bit-exact;
+* quantize with a rotation: <= 1e-5 of codes differ, each by one and at a
+  rounding tie (or in a group whose scale/zero is one fp16 ulp off);
+* decode: normwise relative error <= 2e-3 per (batch, query head) row
+  against the oracle run on the same cache bytes.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import kvq_oracle as O
+import workloads as W
+import int2_rotated_kv_amd as kvq
+from parity_util import (SENTINEL, require_gpu, empty_cache, cache_to_numpy,
+                         cache_from_numpy, rot_matrix, compare_codes_at_ties,
+                         normwise_rel_err, elementwise_rel_err)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+ATTN_TOL = 2e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _report(name, **kw):
+    print(f"[parity] {name} " + json.dumps(kw), flush=True)
+
+
+# ------------------------------------------------------------ quantize
+def _gpu_quantize(x_tok, rot, R=None, T_cap=None, t_offset=0, side="K"):
+    B, T, H, d = x_tok.shape
+    T_cap = T_cap or (T + t_offset)
+    c = empty_cache(B, H, T_cap)
+    xg = x_tok.to(DEV)
+    Rg = None if R is None else torch.as_tensor(R, dtype=torch.float32, device=DEV).contiguous()
+    if side == "K":
+        kvq.kvq_quantize(xg, None, c, None, rot=rot, R=Rg, t_offset=t_offset)
+    else:
+        kvq.kvq_quantize(None, xg, None, c, rot=rot, R=Rg, t_offset=t_offset)
+    torch.cuda.synchronize()
+    return cache_to_numpy(c)
+
+
+def _oracle_quantize(x_tok, rot, R=None):
+    x = x_tok.permute(0, 2, 1, 3).contiguous().numpy()   # [B, H, T, d]
+    return O.quantize_cache(x, rot_matrix(rot, R))
+
+
+def _outlier_rows(rng, shape, dtype):
+    x = rng.standard_normal(shape)
+    x[..., 3] *= 20
+    x[..., 77] *= 12
+    return torch.from_numpy(x.astype(dtype))
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float16])
+def test_quantize_no_rotation_bitexact(dtype):
+    """Ragged T (not a multiple of the 64-token block), t_offset > 0, three
+    heads, two batches; regions outside the written slots stay untouched."""
+    rng = np.random.default_rng(1)
+    x = _outlier_rows(rng, (2, 203, 3, 128), dtype)
+    toff, T_cap = 5, 230
+    gp, gs, gz = _gpu_quantize(x, "none", T_cap=T_cap, t_offset=toff)
+    op, os_, oz = _oracle_quantize(x, "none")
+    sl = slice(toff, toff + 203)
+    assert np.array_equal(gp[:, :, sl], op)
+    assert np.array_equal(gs[:, :, sl].view(np.uint16), os_.view(np.uint16))
+    assert np.array_equal(gz[:, :, sl].view(np.uint16), oz.view(np.uint16))
+    for arr in (gp, gs.view(np.uint8), gz.view(np.uint8)):
+        assert np.all(arr[:, :, :toff] == SENTINEL)
+        assert np.all(arr[:, :, toff + 203:] == SENTINEL)
+
+
+def _golden_rows():
+    import test_oracle_pins as P
+    rows = []
+    for case in P._load("quant_group_cases.json")["cases"]:
+        y, _ = P._golden_group(case)
+        rows.append(np.tile(y, 4))
+    return np.stack(rows).astype(np.float32)
+
+
+def test_quantize_special_groups_bitexact():
+    """Hand-derived golden groups (ties, constant group, clamps, subnormal
+    scale), fp16 subnormals, signed zeros and wide-range groups, fp32 input."""
+    rng = np.random.default_rng(2)
+    rows = [_golden_rows()]
+    sub = (rng.integers(-60, 60, size=(8, 128)) * 2.0 ** -24).astype(np.float32)
+    rows.append(sub)                                   # fp16-subnormal values
+    z = np.zeros((4, 128), np.float32)
+    z[1] = -0.0
+    z[2, ::2] = -0.0
+    z[3, 5] = 1e-30
+    rows.append(z)
+    wide = rng.uniform(-60000, 60000, size=(8, 128)).astype(np.float32)
+    rows.append(wide)
+    grid = []
+    for _ in range(8):
+        zz = np.float16(rng.uniform(-8, 8))
+        ss = np.float16(2.0 ** rng.uniform(-6, 2))
+        j = rng.integers(0, 4, size=128)
+        grid.append((float(zz) + j * float(ss)))
+    rows.append(np.array(grid, np.float32))
+    y = np.concatenate(rows)
+    x = torch.from_numpy(y.reshape(1, -1, 1, 128))
+    gp, gs, gz = _gpu_quantize(x, "none")
+    op, os_, oz = _oracle_quantize(x, "none")
+    assert np.array_equal(gp, op)
+    assert np.array_equal(gs.view(np.uint16), os_.view(np.uint16))
+    assert np.array_equal(gz.view(np.uint16), oz.view(np.uint16))
+
+
+def test_quantize_strided_input_and_value_side():
+    """Non-contiguous input (padded rows, device-side view) through the V
+    side of the call."""
+    rng = np.random.default_rng(3)
+    big = _outlier_rows(rng, (2, 70, 2, 256), np.float16).to(DEV)
+    x = big[..., 64:192]                                # channel stride 1, padded rows
+    assert not x.is_contiguous() and x.stride(3) == 1
+    c = empty_cache(2, 2, 70)
+    kvq.kvq_quantize(None, x, None, c, rot="none")
+    torch.cuda.synchronize()
+    gp, gs, gz = cache_to_numpy(c)
+    op, os_, oz = _oracle_quantize(x.cpu().contiguous(), "none")
+    assert np.array_equal(gp, op)
+    assert np.array_equal(gs.view(np.uint16), os_.view(np.uint16))
+    assert np.array_equal(gz.view(np.uint16), oz.view(np.uint16))
+
+
+@pytest.mark.parametrize("cid", [1, 2])
+def test_quantize_hadamard_ties(cid):
+    """Configs 1 (fp32, T=1024) and 2 (fp16, 32 heads, T=4096)."""
+    cfg = W.config(cid)
+    for which in ("K", "V"):
+        x = W.kv_tokens(cfg, which)
+        gpu = _gpu_quantize(x, "hadamard")
+        ora = _oracle_quantize(x, "hadamard")
+        xr = x.permute(0, 2, 1, 3).contiguous().numpy()
+        st = compare_codes_at_ties(xr, rot_matrix("hadamard"), gpu, ora)
+        _report(f"quantize_hadamard c{cid} {which}", **st)
+
+
+def test_quantize_both_sides_one_call():
+    cfg = W.small_config(W.config(2), T=300, Hkv=4, Hq=4)
+    K = W.kv_tokens(cfg, "K").to(DEV)
+    V = W.kv_tokens(cfg, "V").to(DEV)
+    ck, cv = empty_cache(1, 4, 300), empty_cache(1, 4, 300)
+    kvq.kvq_quantize(K, V, ck, cv, rot="hadamard")
+    torch.cuda.synchronize()
+    for x, c in ((K, ck), (V, cv)):
+        ora = _oracle_quantize(x.cpu(), "hadamard")
+        xr = x.cpu().permute(0, 2, 1, 3).contiguous().numpy()
+        compare_codes_at_ties(xr, rot_matrix("hadamard"), cache_to_numpy(c), ora)
+
+
+# -------------------------------------------------------------- decode
+def _decode_case(cfg, rot="hadamard", R=None, t_begin=None, t_end=None, n_sink=None,
+                 n_res=None, scale=0.0, seed_q=None, name=""):
+    """Oracle-quantized cache uploaded to the GPU; GPU decode vs oracle decode."""
+    tb0, te0 = cfg.int2_range
+    t_begin = tb0 if t_begin is None else t_begin
+    t_end = te0 if t_end is None else t_end
+    n_sink = cfg.n_sink if n_sink is None else n_sink
+    n_res = cfg.n_res if n_res is None else n_res
+    K = W.kv_tokens(cfg, "K")
+    V = W.kv_tokens(cfg, "V")
+    Rm = rot_matrix(rot, R)
+    kh = K.permute(0, 2, 1, 3).contiguous().numpy()
+    vh = V.permute(0, 2, 1, 3).contiguous().numpy()
+    kcache = O.quantize_cache(kh, Rm)
+    vcache = O.quantize_cache(vh, Rm)
+    q = W.queries(cfg)
+    sink = lambda a: np.ascontiguousarray(a[:, :, :n_sink]).astype(np.float16)
+    resw = lambda a: np.ascontiguousarray(a[:, :, cfg.T - n_res:]).astype(np.float16)
+    sk, sv = (sink(kh), sink(vh)) if n_sink else (None, None)
+    rk, rv = (resw(kh), resw(vh)) if n_res else (None, None)
+    ref = O.decode_attention(q.numpy(), kcache, vcache, t_begin, t_end, Rm,
+                             sink_k=sk, sink_v=sv, res_k=rk, res_v=rv,
+                             softmax_scale=scale if scale > 0 else None)
+    up = lambda a: None if a is None else torch.from_numpy(a).to(DEV)
+    Rg = None if rot != "dense" else torch.as_tensor(R, device=DEV).contiguous()
+    out = kvq.kvq_decode_attention(q.to(DEV), cache_from_numpy(*kcache),
+                                   cache_from_numpy(*vcache), t_begin, t_end, rot=rot,
+                                   R=Rg, sink_k=up(sk), sink_v=up(sv), res_k=up(rk),
+                                   res_v=up(rv), softmax_scale=scale)
+    torch.cuda.synchronize()
+    out = out.float().cpu().numpy()
+    err = normwise_rel_err(out, ref)
+    _report(f"decode {name or cfg.name}", normwise=err, elementwise=elementwise_rel_err(out, ref))
+    assert np.all(np.isfinite(out))
+    assert err <= ATTN_TOL
+    return out, ref
+
+
+def test_decode_config1_fp32():
+    _decode_case(W.config(1), name="c1")
+
+
+def test_decode_config2():
+    _decode_case(W.config(2), name="c2")
+
+
+@pytest.mark.parametrize("T", [1, 31, 33, 97, 300])
+def test_decode_ragged_lengths(T):
+    cfg = W.small_config(W.config(2), T=T, Hkv=3, Hq=3, B=2)
+    _decode_case(cfg, name=f"ragged T={T}")
+
+
+def test_decode_token_subrange_and_scale():
+    cfg = W.small_config(W.config(3), T=500, Hkv=4, Hq=4, B=2)
+    _decode_case(cfg, t_begin=37, t_end=411, scale=0.05, name="subrange")
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_decode_gqa_dense_rotation(G):
+    cfg = W.small_config(W.config(4), T=700, B=2, Hkv=2, Hq=2 * G, t_new=0)
+    R = W.dense_rotations(cfg)
+    _decode_case(cfg, rot="dense", R=R, name=f"dense G={G}")
+
+
+def test_decode_gqa_hadamard_g3():
+    cfg = W.small_config(W.config(2), T=257, B=1, Hkv=2, Hq=6)
+    _decode_case(cfg, name="G=3")
+
+
+def test_decode_no_rotation():
+    cfg = W.small_config(W.config(2), T=129, B=1, Hkv=2, Hq=2)
+    _decode_case(cfg, rot="none", name="rot none")
+
+
+def test_decode_sinks_and_residual():
+    cfg = W.small_config(W.config(5), T=900, B=2, Hkv=3, Hq=3)
+    _decode_case(cfg, name="sinks+res full")
+    _decode_case(cfg, n_sink=0, n_res=0, name="sinks+res INT2 only")
+
+
+def test_decode_fp16_tokens_only():
+    cfg = W.small_config(W.config(5), T=200, B=1, Hkv=2, Hq=4)
+    _decode_case(cfg, t_begin=4, t_end=4, n_sink=4, n_res=60, name="fp16 only")
+
+
+# ---------------------------------------------------------- end to end
+@pytest.mark.parametrize("cid", [1, 2])
+def test_end_to_end_gpu_codes(cid):
+    """GPU quantize -> GPU decode, against the oracle decode on the GPU's own
+    codes; the GPU codes themselves are checked against the oracle's."""
+    cfg = W.config(cid)
+    K = W.kv_tokens(cfg, "K").to(DEV)
+    V = W.kv_tokens(cfg, "V").to(DEV)
+    ck = empty_cache(cfg.B, cfg.Hkv, cfg.T)
+    cv = empty_cache(cfg.B, cfg.Hkv, cfg.T)
+    kvq.kvq_quantize(K, V, ck, cv, rot="hadamard")
+    q = W.queries(cfg).to(DEV)
+    out = kvq.kvq_decode_attention(q, ck, cv, 0, cfg.T, rot="hadamard")
+    torch.cuda.synchronize()
+    H = rot_matrix("hadamard")
+    gk, gv = cache_to_numpy(ck), cache_to_numpy(cv)
+    for x, g in ((K, gk), (V, gv)):
+        xr = x.cpu().permute(0, 2, 1, 3).contiguous().numpy()
+        compare_codes_at_ties(xr, H, g, O.quantize_cache(xr, H))
+    ref = O.decode_attention(q.cpu().numpy(), gk, gv, 0, cfg.T, H)
+    err = normwise_rel_err(out.float().cpu().numpy(), ref)
+    _report(f"end_to_end c{cid}", normwise=err)
+    assert err <= ATTN_TOL
