@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark of the rotated INT2 KV-cache hot path on one MI355X.
+
+One step = the whole path over one batch of the throughput workload
+(B=16, T=32768, 32 heads, d=128, fp16 K/V, Hadamard rotation, group 32):
+  1. kvq_quantize: rotate + quantize + pack all K and V rows into the cache;
+  2. kvq_decode_attention: one decode query per (batch, head) over the
+     whole INT2 cache (query rotation, split-K attention, merge,
+     un-rotation).
+Inputs are generated on the GPU before timing (seeded, synthetic) and are
+resident in HBM when the timed region starts.
+
+Prints ONE JSON line.  `value` is the decode attention's effective HBM
+bandwidth (algorithmic bytes / time of the decode call); the quantize
+throughput, per-kernel rooflines and the oracle's CPU throughput on a
+bounded sample are extra fields.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "INT2 decode attention effective HBM GB/s (% of peak) + quantize tokens/s"
+
+# algorithmic bytes (fp16 K/V input)
+QUANT_BYTES_PER_TOKEN_HEAD = 2 * 256 + 2 * 48     # read K and V rows, write 2 INT2 rows
+DECODE_BYTES_PER_TOKEN_HEAD = 2 * 48              # read one INT2 K row and one V row
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", type=int, default=3, help="workload id (3 = throughput case)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run only a 1 GiB device copy (for counter calibration)")
+    return p.parse_args()
+
+
+def file_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(kernel, src_file, n_launch_units):
+    """HBM bytes per launch from a committed counter summary, or None when
+    no summary exists or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != file_sha(src_file):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_each_way": n, "launches": 5}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import int2_rotated_kv_amd as kvq
+    import workloads as W
+
+    kvq.load_library()
+    cfg = W.config(args.config)
+    if cfg.rot != "hadamard" or cfg.n_sink or cfg.n_res or cfg.Hq != cfg.Hkv:
+        print("bench.py times the Hadamard, no-sink workloads", file=sys.stderr)
+        sys.exit(2)
+    dev = "cuda"
+    B, T, H, d = cfg.B, cfg.T, cfg.Hkv, cfg.d
+    print(f"[bench] generating {cfg.name} on the GPU", file=sys.stderr, flush=True)
+    t0 = time.time()
+    K = W.kv_tokens(cfg, "K", device=dev)
+    V = W.kv_tokens(cfg, "V", device=dev)
+    q = W.queries(cfg, device=dev)
+    ck = kvq.Int2Cache.empty(B, H, T, device=dev)
+    cv = kvq.Int2Cache.empty(B, H, T, device=dev)
+    ws_bytes = kvq.kvq_decode_workspace_bytes(B, cfg.Hq, H, d, T)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        kvq.kvq_quantize(K, V, ck, cv, rot="hadamard")
+        if ev is not None:
+            ev[1].record(stream)
+        kvq.kvq_decode_attention(q, ck, cv, 0, T, rot="hadamard", out=out, workspace=ws)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    quant_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    ms_per_step = wall * 1e3 / args.steps
+
+    q_bytes = B * T * H * QUANT_BYTES_PER_TOKEN_HEAD
+    d_bytes = B * T * H * DECODE_BYTES_PER_TOKEN_HEAD + 2 * B * cfg.Hq * d * 2
+    q_ms, d_ms = float(np.median(quant_ms)), float(np.median(dec_ms))
+    dec_gbs = d_bytes / (d_ms * 1e-3) / 1e9
+    q_gbs = q_bytes / (q_ms * 1e-3) / 1e9
+    q_tok_s = B * T / (q_ms * 1e-3)
+
+    csrc = os.path.join(ROOT, "int2_rotated_kv_amd", "csrc")
+    roof_q = {"bound": "hbm", "achieved": round(q_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+              "frac": round(q_gbs / PEAK_HBM_GBS, 4),
+              "traffic": traffic_from_profile("kv_rotate_quant_rows",
+                                              os.path.join(csrc, "kv_rotate_quant.hip"), B * T * H),
+              "kernel": "kv_rotate_quant_rows", "algorithmic_bytes_per_launch": q_bytes,
+              "bytes_per_unit": QUANT_BYTES_PER_TOKEN_HEAD, "unit_of_work": "(token, kv head)",
+              "units_per_launch": B * T * H, "avg_ms": round(q_ms, 4)}
+    roof_d = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+              "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+              "traffic": traffic_from_profile("kv_int2_decode_attn",
+                                              os.path.join(csrc, "kv_decode.hip"), B * T * H),
+              "kernel": "decode call (kv_prep_query + kv_int2_decode_attn + kv_combine_unrotate)",
+              "algorithmic_bytes_per_launch": d_bytes,
+              "bytes_per_unit": DECODE_BYTES_PER_TOKEN_HEAD, "unit_of_work": "(INT2 token, kv head)",
+              "units_per_launch": B * T * H, "avg_ms": round(d_ms, 4)}
+    dominant, other = (roof_q, roof_d) if q_ms >= d_ms else (roof_d, roof_q)
+
+    rec = {
+        "metric": METRIC, "value": round(dec_gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "B": B, "T": T, "Hkv": H, "Hq": cfg.Hq, "d": d,
+                   "kv_input": "f16", "cache": "int2 codes + f16 scale/zero, group 32",
+                   "rotation": "hadamard"},
+        "decode_pct_of_peak": round(100 * dec_gbs / PEAK_HBM_GBS, 2),
+        "decode_ms": round(d_ms, 4), "quantize_ms": round(q_ms, 4),
+        "quantize_tokens_per_s": round(q_tok_s, 1),
+        "quantize_gbs": round(q_gbs, 1),
+        "roofline": dominant, "roofline_other": other,
+        "timing": {"quantize_ms_p10_p90": [round(float(np.percentile(quant_ms, 10)), 4),
+                                           round(float(np.percentile(quant_ms, 90)), 4)],
+                   "decode_ms_p10_p90": [round(float(np.percentile(dec_ms, 10)), 4),
+                                         round(float(np.percentile(dec_ms, 90)), 4)]},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(cfg, K, V, q)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(cfg, K, V, q):
+    """The oracle, untouched, on a bounded sample of the same workload:
+    batch 0, all KV heads, all tokens (1/B of the job).  The sample's
+    inputs are the generator's values (copied from the device)."""
+    import numpy as np
+    from oracle import kvq_oracle as O
+    from threadpoolctl import threadpool_info
+
+    H = O.hadamard_rotation(cfg.d)
+    kh = K[0:1].permute(0, 2, 1, 3).contiguous().cpu().numpy()
+    vh = V[0:1].permute(0, 2, 1, 3).contiguous().cpu().numpy()
+    qs = q[0:1].cpu().numpy()
+    t0 = time.perf_counter()
+    kc = O.quantize_cache(kh, H)
+    vc = O.quantize_cache(vh, H)
+    t1 = time.perf_counter()
+    O.decode_attention(qs, kc, vc, 0, cfg.T, H)
+    t2 = time.perf_counter()
+    d_bytes = cfg.T * cfg.Hkv * DECODE_BYTES_PER_TOKEN_HEAD + 2 * cfg.Hq * cfg.d * 2
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(d_bytes / (t2 - t1) / 1e9, 4), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"batch 0 of {cfg.B} (all {cfg.Hkv} heads, {cfg.T} tokens): oracle "
+                      "rotate+quantize+pack of K and V, then oracle decode of the "
+                      f"{cfg.Hq} queries; value = decode GB/s over the sample's bytes",
+            "quantize_tokens_per_s": round(cfg.T / (t1 - t0), 1),
+            "quantize_s": round(t1 - t0, 3), "decode_s": round(t2 - t1, 3),
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()

@@ -199,25 +199,28 @@ def dense_rotations(cfg: Config) -> np.ndarray:
 # --------------------------------------------------------------------------
 def kv_tokens(cfg: Config, which: str, b0: int = 0, b1: int | None = None,
               t0: int = 0, t1: int | None = None, device="cpu",
-              out: torch.Tensor | None = None,
-              chunk_elems: int = 1 << 25) -> torch.Tensor:
-    """Token-major K or V rows [b1-b0, t1-t0, Hkv, d] in the config dtype.
+              out: torch.Tensor | None = None, h0: int = 0,
+              h1: int | None = None, chunk_elems: int = 1 << 25) -> torch.Tensor:
+    """Token-major K or V rows [b1-b0, t1-t0, h1-h0, d] in the config dtype.
 
     Element (b, t, h, c) is normal_at(key, ((b*T + t)*Hkv + h)*d + c)
-    times sigma[h, c], times the sink gain for t < n_sink.
+    times sigma[h, c], times the sink gain for t < n_sink, so any slice of
+    batches, tokens and heads is reproducible on its own.
     """
     b1 = cfg.B if b1 is None else b1
     t1 = cfg.T if t1 is None else t1
-    nb, nt = b1 - b0, t1 - t0
-    H, d = cfg.Hkv, cfg.d
+    h1 = cfg.Hkv if h1 is None else h1
+    nb, nt, nh = b1 - b0, t1 - t0, h1 - h0
+    d = cfg.d
     if out is None:
-        out = torch.empty((nb, nt, H, d), dtype=cfg.torch_dtype, device=device)
+        out = torch.empty((nb, nt, nh, d), dtype=cfg.torch_dtype, device=device)
     key = _key(cfg, S_K if which == "K" else S_V)
-    sig = torch.as_tensor(channel_sigma(cfg, which), dtype=torch.float64,
+    sig = torch.as_tensor(channel_sigma(cfg, which)[h0:h1], dtype=torch.float64,
                           device=out.device)
-    row = H * d
-    rows_per_chunk = max(1, chunk_elems // row)
-    ar = torch.arange(row, dtype=torch.int64, device=out.device)
+    row = cfg.Hkv * d
+    ar = ((torch.arange(h0, h1, dtype=torch.int64, device=out.device) * d)[:, None]
+          + torch.arange(d, dtype=torch.int64, device=out.device)[None, :]).reshape(-1)
+    rows_per_chunk = max(1, chunk_elems // (nh * d))
     for bi in range(nb):
         b = b0 + bi
         for ts in range(0, nt, rows_per_chunk):
@@ -225,7 +228,7 @@ def kv_tokens(cfg: Config, which: str, b0: int = 0, b1: int | None = None,
             tok = torch.arange(t0 + ts, t0 + te, dtype=torch.int64,
                                device=out.device)
             idx = ((b * cfg.T + tok) * row)[:, None] + ar[None, :]
-            z = normal_at(key, idx).view(te - ts, H, d) * sig[None]
+            z = normal_at(key, idx).view(te - ts, nh, d) * sig[None]
             if cfg.n_sink and cfg.sink_gain != 1.0:
                 gain = torch.where(tok < cfg.n_sink, cfg.sink_gain, 1.0)
                 z = z * gain.to(torch.float64)[:, None, None]
