@@ -7,8 +7,12 @@ One step = the whole path over one batch of the throughput workload
   2. kvq_decode_attention: one decode query per (batch, head) over the
      whole INT2 cache (query rotation, split-K attention, merge,
      un-rotation).
-Inputs are generated on the GPU before timing (seeded, synthetic) and are
-resident in HBM when the timed region starts.
+The workload times the quantize kernel and the decode attention
+separately, so the timed region runs the K quantize calls back to back and
+then the K decode calls back to back (each call bracketed by events);
+ms_per_step is the sum per step.  Inputs are generated on the GPU before
+timing (seeded, synthetic) and are resident in HBM when the timed region
+starts.
 
 Prints ONE JSON line.  `value` is the decode attention's effective HBM
 bandwidth (algorithmic bytes / time of the decode call); the quantize
@@ -42,7 +46,7 @@ def parse():
     p.add_argument("--config", type=int, default=3, help="workload id (3 = throughput case)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
-                   help="run only a 1 GiB device copy (for counter calibration)")
+                   help="run only a 1 GiB elementwise device copy (counter calibration)")
     return p.parse_args()
 
 
@@ -66,15 +70,33 @@ def traffic_from_profile(kernel, src_file, n_launch_units):
 
 def copy_calibration():
     import torch
-    n = 1 << 30
-    a = torch.empty(n, dtype=torch.uint8, device="cuda")
-    b = torch.empty(n, dtype=torch.uint8, device="cuda")
-    a.fill_(1)
+    n = 1 << 28                                # fp32 elements: 1 GiB each way
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty(n, dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     for _ in range(5):
-        b.copy_(a)
+        torch.neg(a, out=b)                    # one elementwise kernel: read 1 GiB, write 1 GiB
     torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration_bytes_each_way": n, "launches": 5}), flush=True)
+    print(json.dumps({"copy_calibration_bytes_each_way": 4 * n, "launches": 5}), flush=True)
+
+
+def copy_bandwidth():
+    """Bandwidth of a plain streaming elementwise kernel on this GPU (read
+    1 GiB + write 1 GiB per launch): the practical ceiling for context."""
+    import torch
+    n = 1 << 28
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.neg(a, out=b)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        torch.neg(a, out=b)
+    e1.record()
+    torch.cuda.synchronize()
+    return round(8 * n / (e0.elapsed_time(e1) / 10) / 1e6, 1)
 
 
 def main():
@@ -118,30 +140,35 @@ def main():
 
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def quant():
         kvq.kvq_quantize(K, V, ck, cv, rot="hadamard")
-        if ev is not None:
-            ev[1].record(stream)
+
+    def decode():
         kvq.kvq_decode_attention(q, ck, cv, 0, T, rot="hadamard", out=out, workspace=ws)
-        if ev is not None:
-            ev[2].record(stream)
 
     for _ in range(args.warmup):
-        step()
+        quant()
+        decode()
     torch.cuda.synchronize()
     print("[bench] warmup done", file=sys.stderr, flush=True)
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    def phase(fn, n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        return evs
+
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
+    q_evs = phase(quant, args.steps)
+    d_evs = phase(decode, args.steps)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    quant_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    quant_ms = np.array([a.elapsed_time(b) for a, b in q_evs])
+    dec_ms = np.array([a.elapsed_time(b) for a, b in d_evs])
     ms_per_step = wall * 1e3 / args.steps
 
     q_bytes = B * T * H * QUANT_BYTES_PER_TOKEN_HEAD
@@ -187,6 +214,7 @@ def main():
                    "decode_ms_p10_p90": [round(float(np.percentile(dec_ms, 10)), 4),
                                          round(float(np.percentile(dec_ms, 90)), 4)]},
     }
+    rec["copy_reference_gbs"] = copy_bandwidth()
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, K, V, q)
     print(json.dumps(rec), flush=True)

@@ -10,7 +10,8 @@
 // Three launches on the caller's stream:
 //   1. kv_prep_query     per (b, query head): q' = q R (FWHT or dense), scaled
 //                        by softmax_scale*log2(e), turned into a per-group
-//                        23-bit fixed-point vector split into three int8 limbs.
+//                        19-bit fixed-point vector split into five signed
+//                        4-bit limbs.
 //   2. kv_int2_decode_attn  one wave per (b, kv head, token split): flash-
 //                        decoding over its tokens with an online softmax; every
 //                        loaded K/V row serves all G query heads of the group.
@@ -21,8 +22,8 @@
 //
 // Scores never dequantize a key: with per-group scale s and zero z,
 //   q'.k_hat = sum_j s_j * (sum_{c in j} q'_c code_c) + z_j * (sum_{c in j} q'_c),
-// and the inner sum is an exact int32 dot product (v_dot4 on int8 code
-// bytes and int8 query limbs).  Values: o'_c += sum_t p_t s_{t,j} code_{t,c}
+// and the inner sum is an exact int32 dot product (v_dot8 on 4-bit code
+// nibbles and 4-bit query limbs).  Values: o'_c += sum_t p_t s_{t,j} code_{t,c}
 // + sum_t p_t z_{t,j}; the first term runs as v_dot2 over token pairs with
 // codes placed in fp16 subnormal encodings (code * 2^(e-24)) and the
 // weights p*s in fp16, accumulated in fp32.
@@ -86,6 +87,7 @@ struct PrepArgs {
   uint8_t *qprep;    // [B][Hq][128 dwords]
 };
 
+
 // grid: B*Hq blocks of 128 threads; thread c owns channel c.
 __global__ __launch_bounds__(128) void kv_prep_query(PrepArgs a) {
   __shared__ float buf[128];
@@ -106,26 +108,41 @@ __global__ __launch_bounds__(128) void kv_prep_query(PrepArgs a) {
   int e = 0;
   (void)frexpf(amax, &e);                    // amax < 2^e
   const bool zero_group = !(amax > 0.0f);
-  const int E = 22 - e;                      // |x| * 2^E < 2^22
+  const int E = 18 - e;                      // |x| * 2^E < 2^18
   const int qi = zero_group ? 0 : (int)__builtin_rintf(ldexpf(x, E));
   const float step = zero_group ? 0.0f : ldexpf(1.0f, -E);
   int isum = qi;
 #pragma unroll
   for (int m = 1; m < 32; m <<= 1) isum += __shfl_xor(isum, m, 32);
 
-  // balanced base-256 digits: qi = hi*65536 + mid*256 + lo, each in int8
-  const int lo = (int)(int8_t)(qi & 0xFF);
-  const int r1 = (qi - lo) >> 8;
-  const int mid = (int)(int8_t)(r1 & 0xFF);
-  const int hi = (r1 - mid) >> 8;
+  // balanced base-16 digits in [-8, 7]: qi = sum_L d_L * 16^(4-L), L = 0 most
+  // significant.  |qi| <= 2^18 fits five digits.
+  int dig[5];
+  int r = qi;
+#pragma unroll
+  for (int L = 4; L >= 0; --L) {
+    const int dl = ((r + 8) & 15) - 8;
+    dig[L] = dl;
+    r = (r - dl) >> 4;
+  }
 
+  // Codes arrive as nibbles: of a code dword w (channels 16w..16w+15 of the
+  // group), the masked copy (w & 0x33333333) holds channel 16w + 2k in nibble
+  // k and ((w >> 2) & 0x33333333) holds channel 16w + 2k + 1.  Limb dword
+  // (L, w, parity) packs the matching digits of the query the same way.
   const int j = c >> 5, cg = c & 31;
-  const int w = cg >> 4, bsel = (cg >> 2) & 3, k = cg & 3;
-  uint8_t *base = a.qprep + bh * (kQprepDwordsPerHead * 4) + j * 128;
-  const int off = (w * 4 + k) * 4 + bsel;
-  base[0 * 32 + off] = (uint8_t)hi;
-  base[1 * 32 + off] = (uint8_t)mid;
-  base[2 * 32 + off] = (uint8_t)lo;
+  const int w = cg >> 4, par = cg & 1, k = (cg & 15) >> 1;
+  uint32_t *base = reinterpret_cast<uint32_t *>(a.qprep) + bh * kQprepDwordsPerHead + j * 32;
+  // assemble limb dwords with a 16-lane OR-reduction of shifted digits
+#pragma unroll
+  for (int L = 0; L < 5; ++L) {
+    uint32_t part = ((uint32_t)dig[L] & 15u) << (4 * k);
+    // lanes of one dword: same (w, par), k = 0..7 -> lane offsets 2k within cg
+    part |= __shfl_xor(part, 2, 32);
+    part |= __shfl_xor(part, 4, 32);
+    part |= __shfl_xor(part, 8, 32);
+    if (k == 0) base[L * 4 + w * 2 + par] = part;
+  }
   if (cg == 0) {
     float *fb = reinterpret_cast<float *>(base);
     fb[24] = (float)isum * step;             // sum of the group's fixed-point q
@@ -153,173 +170,455 @@ __device__ __forceinline__ constexpr float chan_unscale(int x) {
   return x <= 4 ? (float)(1u << (24 - 2 * x)) : (float)(1u << (30 - 2 * x));
 }
 
+// Lane layout of the attention kernel: lane l handles token slot ts = l/2 of
+// a 64-token tile (tokens ts and 32 + ts) on channel half h = l%2, i.e. the
+// two groups 2h and 2h+1 (64 channels).  Codes arrive as one 16-byte load
+// per token and lane (1 KB per wave instruction); scales and zeros as one
+// 4-byte load (both groups) per token and lane.
+struct TileRegs {
+  u32x4_t kA, kB, vA, vB;          // codes of tokens A (= ts) and B (= 32 + ts)
+  uint32_t ksA, kzA, ksB, kzB;     // two fp16 scales / zeros each
+  uint32_t vsA, vzA, vsB, vzB;
+};
+
+template <int GC>
+struct AttnState {
+  float m[GC], l[GC], zacc[GC][2], acc[GC][64];
+};
+
+// Per-lane query data for the lane's two channel groups of GC heads.
+template <int GC>
+struct QueryLimbs {
+  uint32_t limb[GC][2][20];   // [head][group in half][L*4 + w*2 + parity]
+  float qsum[GC][2], qstep[GC][2];
+};
+
+__device__ __forceinline__ float lo_half(uint32_t w) { return half_bits_to_float((uint16_t)(w & 0xFFFFu)); }
+__device__ __forceinline__ float hi_half(uint32_t w) { return half_bits_to_float((uint16_t)(w >> 16)); }
+
+// exact int32 dot product of one group's 32 codes (two code dwords) with the
+// five 4-bit limbs of the fixed-point query
+__device__ __forceinline__ int group_dot(const uint32_t (&limb)[20], uint32_t c0, uint32_t c1) {
+  const uint32_t n[4] = {c0 & 0x33333333u, (c0 >> 2) & 0x33333333u,
+                         c1 & 0x33333333u, (c1 >> 2) & 0x33333333u};
+  int acc = 0;
+#pragma unroll
+  for (int L = 0; L < 5; ++L) {
+    if (L) acc <<= 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_sdot8((int)limb[4 * L + i], (int)n[i], acc, false);
+  }
+  return acc;
+}
+
+template <int GC>
+__device__ __forceinline__ void attn_tile(AttnState<GC> &st, const QueryLimbs<GC> &q,
+                                          const TileRegs &r, bool va, bool vb) {
+  const uint32_t kAw[4] = {r.kA.x, r.kA.y, r.kA.z, r.kA.w};
+  const uint32_t kBw[4] = {r.kB.x, r.kB.y, r.kB.z, r.kB.w};
+  half2_t wp[GC][2];
+#pragma unroll
+  for (int g = 0; g < GC; ++g) {
+    float sa = 0.0f, sb = 0.0f;
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const int ia = group_dot(q.limb[g][gi], kAw[2 * gi], kAw[2 * gi + 1]);
+      const int ib = group_dot(q.limb[g][gi], kBw[2 * gi], kBw[2 * gi + 1]);
+      const float skA = gi ? hi_half(r.ksA) : lo_half(r.ksA);
+      const float zkA = gi ? hi_half(r.kzA) : lo_half(r.kzA);
+      const float skB = gi ? hi_half(r.ksB) : lo_half(r.ksB);
+      const float zkB = gi ? hi_half(r.kzB) : lo_half(r.kzB);
+      sa += __builtin_fmaf((float)ia, skA * q.qstep[g][gi], zkA * q.qsum[g][gi]);
+      sb += __builtin_fmaf((float)ib, skB * q.qstep[g][gi], zkB * q.qsum[g][gi]);
+    }
+    sa += quad_swap<kQuadXor1>(sa);          // the other half of the row
+    sb += quad_swap<kQuadXor1>(sb);
+    sa = va ? sa : kNegInf;
+    sb = vb ? sb : kNegInf;
+
+    // online softmax (log2 domain); the tile max is wave-uniform
+    float mx = fmaxf(sa, sb);
+    mx = fmaxf(mx, row_ror<2>(mx));
+    mx = fmaxf(mx, row_ror<4>(mx));
+    mx = fmaxf(mx, row_ror<8>(mx));
+    mx = fmaxf(mx, shfl_xor_f(mx, 16));
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    if (mx > st.m[g]) {
+      const float alpha = __builtin_amdgcn_exp2f(st.m[g] - mx);
+      st.l[g] *= alpha;
+      st.zacc[g][0] *= alpha;
+      st.zacc[g][1] *= alpha;
+#pragma unroll
+      for (int i = 0; i < 64; ++i) st.acc[g][i] *= alpha;
+      st.m[g] = mx;
+    }
+    const float pA = __builtin_amdgcn_exp2f(sa - st.m[g]);   // 0 for masked tokens
+    const float pB = __builtin_amdgcn_exp2f(sb - st.m[g]);
+    st.l[g] += pA + pB;
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const float svA = gi ? hi_half(r.vsA) : lo_half(r.vsA);
+      const float zvA = gi ? hi_half(r.vzA) : lo_half(r.vzA);
+      const float svB = gi ? hi_half(r.vsB) : lo_half(r.vsB);
+      const float zvB = gi ? hi_half(r.vzB) : lo_half(r.vzB);
+      st.zacc[g][gi] = __builtin_fmaf(pA, zvA, __builtin_fmaf(pB, zvB, st.zacc[g][gi]));
+      wp[g][gi].x = (_Float16)(pA * svA);
+      wp[g][gi].y = (_Float16)(pB * svB);
+    }
+  }
+
+  // V: token pair (A in the low half, B in the high half) per channel
+  const uint32_t vAw[4] = {r.vA.x, r.vA.y, r.vA.z, r.vA.w};
+  const uint32_t vBw[4] = {r.vB.x, r.vB.y, r.vB.z, r.vB.w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {               // code dword d: group d/2, dword w = d%2
+    const int gi = d >> 1, w = d & 1;
+    const uint32_t X = __builtin_amdgcn_perm(vBw[d], vAw[d], 0x05040100u);   // lo16(A) | lo16(B) << 16
+    const uint32_t Y = __builtin_amdgcn_perm(vBw[d], vAw[d], 0x07060302u);   // hi16(A) | hi16(B) << 16
+    const uint32_t X6 = X >> 6, Y6 = Y >> 6;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const uint32_t px = x <= 4 ? (X & (0x00030003u << (2 * x))) : (X6 & (0x00030003u << (2 * x - 6)));
+      const uint32_t py = x <= 4 ? (Y & (0x00030003u << (2 * x))) : (Y6 & (0x00030003u << (2 * x - 6)));
+      const half2_t hx = __builtin_bit_cast(half2_t, px);
+      const half2_t hy = __builtin_bit_cast(half2_t, py);
+#pragma unroll
+      for (int g = 0; g < GC; ++g) {
+        float &ax = st.acc[g][32 * gi + 16 * w + x];
+        float &ay = st.acc[g][32 * gi + 16 * w + 8 + x];
+        ax = __builtin_amdgcn_fdot2(hx, wp[g][gi], ax, false);
+        ay = __builtin_amdgcn_fdot2(hy, wp[g][gi], ay, false);
+      }
+    }
+  }
+}
+
 template <int GC>
 __global__ __launch_bounds__(256) void kv_int2_decode_attn(AttnArgs a) {
   const int lane = threadIdx.x & 63;
-  const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  // wave index made explicitly uniform so every per-wave quantity is scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
   if (gw >= a.total_waves) return;           // whole wave leaves together
   const int64_t split = gw % a.n_splits;
   const int64_t bh = gw / a.n_splits;        // b*Hkv + hkv
   const int hkv = (int)(bh % a.Hkv);
   const int64_t b = bh / a.Hkv;
-  const int ts = lane >> 2;                  // token slot 0..15
-  const int j = lane & 3;                    // channel group
+  const int ts = lane >> 1;                  // token slot 0..31
+  const int h = lane & 1;                    // channel half: groups 2h, 2h+1
   const int64_t s0 = split * a.tps;
   const int64_t s1 = (s0 + a.tps < a.n_int2) ? s0 + a.tps : a.n_int2;
 
-  uint32_t qh[GC][8], qm[GC][8], ql[GC][8];
-  float qsum[GC], qstep[GC];
+  QueryLimbs<GC> q;
 #pragma unroll
   for (int g = 0; g < GC; ++g) {
     const int hq = hkv * a.G + a.g0 + g;
-    const uint32_t *p = a.qprep + (b * a.Hq + hq) * kQprepDwordsPerHead + j * 32;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) { qh[g][i] = p[i]; qm[g][i] = p[8 + i]; ql[g][i] = p[16 + i]; }
-    qsum[g] = bits_as_float(p[24]);
-    qstep[g] = bits_as_float(p[25]);
+    for (int gi = 0; gi < 2; ++gi) {
+      const uint32_t *p = a.qprep + (b * a.Hq + hq) * kQprepDwordsPerHead + (2 * h + gi) * 32;
+#pragma unroll
+      for (int i = 0; i < 20; ++i) q.limb[g][gi][i] = p[i];
+      q.qsum[g][gi] = bits_as_float(p[24]);
+      q.qstep[g][gi] = bits_as_float(p[25]);
+    }
   }
 
-  float m[GC], l[GC], zacc[GC], acc[GC][32];
+  AttnState<GC> st;
 #pragma unroll
   for (int g = 0; g < GC; ++g) {
-    m[g] = kNegInf; l[g] = 0.0f; zacc[g] = 0.0f;
+    st.m[g] = kNegInf; st.l[g] = 0.0f; st.zacc[g][0] = 0.0f; st.zacc[g][1] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) acc[g][i] = 0.0f;
+    for (int i = 0; i < 64; ++i) st.acc[g][i] = 0.0f;
   }
 
-  const int64_t krow0 = bh * a.kT_cap + a.t_begin;
-  const int64_t vrow0 = bh * a.vT_cap + a.t_begin;
-  const uint8_t *kc = a.kcodes + krow0 * kCodeBytes + 8 * j;
-  const uint16_t *ks = a.kscales + krow0 * kNGroups + j;
-  const uint16_t *kz = a.kzeros + krow0 * kNGroups + j;
-  const uint8_t *vc = a.vcodes + vrow0 * kCodeBytes + 8 * j;
-  const uint16_t *vs = a.vscales + vrow0 * kNGroups + j;
-  const uint16_t *vz = a.vzeros + vrow0 * kNGroups + j;
+  // Row r of the split: codes at *c + r*32 bytes, scales/zeros at *s + r*4
+  // halves.  Lane offsets are 32-bit; tile bases are wave-uniform.
+  const int64_t krow0 = bh * a.kT_cap + a.t_begin + s0;
+  const int64_t vrow0 = bh * a.vT_cap + a.t_begin + s0;
+  const uint8_t *kc = a.kcodes + krow0 * kCodeBytes;
+  const uint8_t *vc = a.vcodes + vrow0 * kCodeBytes;
+  const uint16_t *ks = a.kscales + krow0 * kNGroups, *kz = a.kzeros + krow0 * kNGroups;
+  const uint16_t *vs = a.vscales + vrow0 * kNGroups, *vz = a.vzeros + vrow0 * kNGroups;
+  const int64_t n = s1 - s0;
+  const int64_t nfull = n & ~(int64_t)63;
 
-  for (int64_t t = s0; t < s1; t += 32) {
-    const int64_t ta = t + ts, tb = t + 16 + ts;
-    const bool va = ta < s1, vb = tb < s1;
-    const int64_t la = va ? ta : s0, lb = vb ? tb : s0;
-    const uint2 kA = *reinterpret_cast<const uint2 *>(kc + la * kCodeBytes);
-    const uint2 kB = *reinterpret_cast<const uint2 *>(kc + lb * kCodeBytes);
-    const uint2 vA = *reinterpret_cast<const uint2 *>(vc + la * kCodeBytes);
-    const uint2 vB = *reinterpret_cast<const uint2 *>(vc + lb * kCodeBytes);
-    const float skA = half_bits_to_float(ks[la * kNGroups]);
-    const float zkA = half_bits_to_float(kz[la * kNGroups]);
-    const float skB = half_bits_to_float(ks[lb * kNGroups]);
-    const float zkB = half_bits_to_float(kz[lb * kNGroups]);
-    const float svA = half_bits_to_float(vs[la * kNGroups]);
-    const float zvA = half_bits_to_float(vz[la * kNGroups]);
-    const float svB = half_bits_to_float(vs[lb * kNGroups]);
-    const float zvB = half_bits_to_float(vz[lb * kNGroups]);
+  // Loads of one lane: codes at tile base + oc (+1 KB for token B), scales
+  // and zeros at tile base + os halves (+64 halves for token B).  Tile bases
+  // are wave-uniform, lane offsets 32-bit.
+  const uint32_t oc = (uint32_t)(ts * kCodeBytes + 16 * h);
+  const uint32_t os = (uint32_t)(ts * kNGroups + 2 * h);
+  auto load_tile = [&](int64_t first_row) {
+    TileRegs r;
+    const uint8_t *kct = kc + first_row * kCodeBytes, *vct = vc + first_row * kCodeBytes;
+    const uint16_t *kst = ks + first_row * kNGroups, *kzt = kz + first_row * kNGroups;
+    const uint16_t *vst = vs + first_row * kNGroups, *vzt = vz + first_row * kNGroups;
+    r.kA = *reinterpret_cast<const u32x4_t *>(kct + oc);
+    r.kB = *reinterpret_cast<const u32x4_t *>(kct + oc + 32 * kCodeBytes);
+    r.vA = *reinterpret_cast<const u32x4_t *>(vct + oc);
+    r.vB = *reinterpret_cast<const u32x4_t *>(vct + oc + 32 * kCodeBytes);
+    r.ksA = *reinterpret_cast<const uint32_t *>(kst + os);
+    r.kzA = *reinterpret_cast<const uint32_t *>(kzt + os);
+    r.ksB = *reinterpret_cast<const uint32_t *>(kst + os + 32 * kNGroups);
+    r.kzB = *reinterpret_cast<const uint32_t *>(kzt + os + 32 * kNGroups);
+    r.vsA = *reinterpret_cast<const uint32_t *>(vst + os);
+    r.vzA = *reinterpret_cast<const uint32_t *>(vzt + os);
+    r.vsB = *reinterpret_cast<const uint32_t *>(vst + os + 32 * kNGroups);
+    r.vzB = *reinterpret_cast<const uint32_t *>(vzt + os + 32 * kNGroups);
+    return r;
+  };
 
-    // K codes -> int8 bytes: cX[w*4+k] byte b = code of channel 16w+4b+k
-    uint32_t cA[8], cB[8];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      cA[k] = (kA.x >> (2 * k)) & 0x03030303u;
-      cA[4 + k] = (kA.y >> (2 * k)) & 0x03030303u;
-      cB[k] = (kB.x >> (2 * k)) & 0x03030303u;
-      cB[4 + k] = (kB.y >> (2 * k)) & 0x03030303u;
+  // Full tiles, software-pipelined two deep: while tile i is computed the
+  // loads of tile i+1 are in flight.  A prefetch past the last full tile is
+  // clamped to it (a re-read of valid rows, result unused).
+  const int64_t ntiles = nfull >> 6;
+  if (ntiles > 0) {
+    const int64_t last = ntiles - 1;
+    TileRegs r0 = load_tile(0), r1;
+    int64_t i = 0;
+    for (; i + 2 <= ntiles; i += 2) {
+      r1 = load_tile(64 * (i + 1));
+      attn_tile<GC>(st, q, r0, true, true);
+      r0 = load_tile(64 * (i + 2 < last ? i + 2 : last));
+      attn_tile<GC>(st, q, r1, true, true);
     }
-
-    half2_t wp[GC];
-    float pA[GC], pB[GC];
-#pragma unroll
-    for (int g = 0; g < GC; ++g) {
-      int ia = 0, ib = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        ia = __builtin_amdgcn_sdot4((int)qh[g][i], (int)cA[i], ia, false);
-        ib = __builtin_amdgcn_sdot4((int)qh[g][i], (int)cB[i], ib, false);
-      }
-      ia <<= 8; ib <<= 8;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        ia = __builtin_amdgcn_sdot4((int)qm[g][i], (int)cA[i], ia, false);
-        ib = __builtin_amdgcn_sdot4((int)qm[g][i], (int)cB[i], ib, false);
-      }
-      ia <<= 8; ib <<= 8;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        ia = __builtin_amdgcn_sdot4((int)ql[g][i], (int)cA[i], ia, false);
-        ib = __builtin_amdgcn_sdot4((int)ql[g][i], (int)cB[i], ib, false);
-      }
-      float sa = (float)ia * (skA * qstep[g]) + zkA * qsum[g];
-      float sb = (float)ib * (skB * qstep[g]) + zkB * qsum[g];
-      sa += quad_swap<kQuadXor1>(sa);
-      sb += quad_swap<kQuadXor1>(sb);
-      sa += quad_swap<kQuadXor2>(sa);
-      sb += quad_swap<kQuadXor2>(sb);
-      sa = va ? sa : kNegInf;
-      sb = vb ? sb : kNegInf;
-
-      // online softmax (log2 domain); the tile max is wave-uniform
-      float mx = fmaxf(sa, sb);
-      mx = fmaxf(mx, shfl_xor_f(mx, 4));
-      mx = fmaxf(mx, shfl_xor_f(mx, 8));
-      mx = fmaxf(mx, shfl_xor_f(mx, 16));
-      mx = fmaxf(mx, shfl_xor_f(mx, 32));
-      if (mx > m[g]) {
-        const float alpha = __builtin_amdgcn_exp2f(m[g] - mx);
-        l[g] *= alpha;
-        zacc[g] *= alpha;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) acc[g][i] *= alpha;
-        m[g] = mx;
-      }
-      pA[g] = va ? __builtin_amdgcn_exp2f(sa - m[g]) : 0.0f;
-      pB[g] = vb ? __builtin_amdgcn_exp2f(sb - m[g]) : 0.0f;
-      l[g] += pA[g] + pB[g];
-      zacc[g] = __builtin_fmaf(pA[g], zvA, __builtin_fmaf(pB[g], zvB, zacc[g]));
-      wp[g].x = (_Float16)(pA[g] * svA);
-      wp[g].y = (_Float16)(pB[g] * svB);
-    }
-
-    // V: token pair (A in the low half, B in the high half) per channel
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      const uint32_t a32 = w ? vA.y : vA.x;
-      const uint32_t b32 = w ? vB.y : vB.x;
-      const uint32_t X = (a32 & 0xFFFFu) | (b32 << 16);           // channels 16w+0..7
-      const uint32_t Y = (a32 >> 16) | (b32 & 0xFFFF0000u);       // channels 16w+8..15
-      const uint32_t X6 = X >> 6, Y6 = Y >> 6;
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        const uint32_t px = x <= 4 ? (X & (0x00030003u << (2 * x))) : (X6 & (0x00030003u << (2 * x - 6)));
-        const uint32_t py = x <= 4 ? (Y & (0x00030003u << (2 * x))) : (Y6 & (0x00030003u << (2 * x - 6)));
-        const half2_t hx = __builtin_bit_cast(half2_t, px);
-        const half2_t hy = __builtin_bit_cast(half2_t, py);
-#pragma unroll
-        for (int g = 0; g < GC; ++g) {
-          acc[g][16 * w + x] = __builtin_amdgcn_fdot2(hx, wp[g], acc[g][16 * w + x], false);
-          acc[g][16 * w + 8 + x] = __builtin_amdgcn_fdot2(hy, wp[g], acc[g][16 * w + 8 + x], false);
-        }
-      }
-    }
+    if (i < ntiles) attn_tile<GC>(st, q, r0, true, true);
+  }
+  if (nfull < n) {                          // tail tile: clamp rows into the split
+    const int64_t ta = nfull + ts, tb = nfull + 32 + ts;
+    const bool va = ta < n, vb = tb < n;
+    const int64_t ra = va ? ta : 0, rb = vb ? tb : 0;
+    TileRegs r;
+    r.kA = *reinterpret_cast<const u32x4_t *>(kc + ra * kCodeBytes + 16 * h);
+    r.kB = *reinterpret_cast<const u32x4_t *>(kc + rb * kCodeBytes + 16 * h);
+    r.vA = *reinterpret_cast<const u32x4_t *>(vc + ra * kCodeBytes + 16 * h);
+    r.vB = *reinterpret_cast<const u32x4_t *>(vc + rb * kCodeBytes + 16 * h);
+    r.ksA = *reinterpret_cast<const uint32_t *>(ks + ra * kNGroups + 2 * h);
+    r.kzA = *reinterpret_cast<const uint32_t *>(kz + ra * kNGroups + 2 * h);
+    r.ksB = *reinterpret_cast<const uint32_t *>(ks + rb * kNGroups + 2 * h);
+    r.kzB = *reinterpret_cast<const uint32_t *>(kz + rb * kNGroups + 2 * h);
+    r.vsA = *reinterpret_cast<const uint32_t *>(vs + ra * kNGroups + 2 * h);
+    r.vzA = *reinterpret_cast<const uint32_t *>(vz + ra * kNGroups + 2 * h);
+    r.vsB = *reinterpret_cast<const uint32_t *>(vs + rb * kNGroups + 2 * h);
+    r.vzB = *reinterpret_cast<const uint32_t *>(vz + rb * kNGroups + 2 * h);
+    attn_tile<GC>(st, q, r, va, vb);
   }
 
-  // reduce over the 16 token slots (lanes sharing j), then write the partial
+  // reduce over the 32 token slots (lanes sharing h), then write the partial
 #pragma unroll
   for (int g = 0; g < GC; ++g) {
+    float l = st.l[g], z0 = st.zacc[g][0], z1 = st.zacc[g][1];
 #pragma unroll
-    for (int msk = 4; msk < 64; msk <<= 1) {
-      l[g] += shfl_xor_f(l[g], msk);
-      zacc[g] += shfl_xor_f(zacc[g], msk);
+    for (int msk = 2; msk < 64; msk <<= 1) {
+      l += shfl_xor_f(l, msk);
+      z0 += shfl_xor_f(z0, msk);
+      z1 += shfl_xor_f(z1, msk);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) acc[g][i] += shfl_xor_f(acc[g][i], msk);
+      for (int i = 0; i < 64; ++i) st.acc[g][i] += shfl_xor_f(st.acc[g][i], msk);
     }
     if (ts == 0) {
       const int hq = hkv * a.G + a.g0 + g;
       float *dst = a.partials + ((b * a.Hq + hq) * a.n_splits + split) * kPartialStride;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
+      for (int i = 0; i < 64; ++i) {
         const int x = i & 7;
-        dst[32 * j + i] = __builtin_fmaf(acc[g][i], chan_unscale(x), zacc[g]);
+        dst[64 * h + i] = __builtin_fmaf(st.acc[g][i], chan_unscale(x), i < 32 ? z0 : z1);
       }
+      if (h == 0) {
+        dst[128] = st.m[g];
+        dst[129] = l;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// GQA variant: lane (ts, j) = (l/4, l%4) handles tokens ts and 16 + ts of a
+// 32-token tile on channel group j for GC query heads at once, so each
+// loaded K/V code serves GC heads.  Registers allow GC = 2 with a three-deep
+// load pipeline.
+// ---------------------------------------------------------------------------
+struct QuadTileRegs {
+  uint2 kA, kB, vA, vB;
+  uint16_t h[8];   // kscale A, kzero A, kscale B, kzero B, vscale A, vzero A, vscale B, vzero B
+};
+
+template <int GC>
+struct QuadState {
+  float m[GC], l[GC], zacc[GC], acc[GC][32];
+};
+
+template <int GC>
+struct QuadQuery {
+  uint32_t limb[GC][20];
+  float qsum[GC], qstep[GC];
+};
+
+template <int GC>
+__device__ __forceinline__ void quad_tile(QuadState<GC> &st, const QuadQuery<GC> &q,
+                                          const QuadTileRegs &r, bool va, bool vb) {
+  const float skA = half_bits_to_float(r.h[0]), zkA = half_bits_to_float(r.h[1]);
+  const float skB = half_bits_to_float(r.h[2]), zkB = half_bits_to_float(r.h[3]);
+  const float svA = half_bits_to_float(r.h[4]), zvA = half_bits_to_float(r.h[5]);
+  const float svB = half_bits_to_float(r.h[6]), zvB = half_bits_to_float(r.h[7]);
+  half2_t wp[GC];
+#pragma unroll
+  for (int g = 0; g < GC; ++g) {
+    const int ia = group_dot(q.limb[g], r.kA.x, r.kA.y);
+    const int ib = group_dot(q.limb[g], r.kB.x, r.kB.y);
+    float sa = __builtin_fmaf((float)ia, skA * q.qstep[g], zkA * q.qsum[g]);
+    float sb = __builtin_fmaf((float)ib, skB * q.qstep[g], zkB * q.qsum[g]);
+    sa += quad_swap<kQuadXor1>(sa);
+    sb += quad_swap<kQuadXor1>(sb);
+    sa += quad_swap<kQuadXor2>(sa);
+    sb += quad_swap<kQuadXor2>(sb);
+    sa = va ? sa : kNegInf;
+    sb = vb ? sb : kNegInf;
+    float mx = fmaxf(sa, sb);
+    mx = fmaxf(mx, row_ror<4>(mx));
+    mx = fmaxf(mx, row_ror<8>(mx));
+    mx = fmaxf(mx, shfl_xor_f(mx, 16));
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    if (mx > st.m[g]) {
+      const float alpha = __builtin_amdgcn_exp2f(st.m[g] - mx);
+      st.l[g] *= alpha;
+      st.zacc[g] *= alpha;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) st.acc[g][i] *= alpha;
+      st.m[g] = mx;
+    }
+    const float pA = __builtin_amdgcn_exp2f(sa - st.m[g]);
+    const float pB = __builtin_amdgcn_exp2f(sb - st.m[g]);
+    st.l[g] += pA + pB;
+    st.zacc[g] = __builtin_fmaf(pA, zvA, __builtin_fmaf(pB, zvB, st.zacc[g]));
+    wp[g].x = (_Float16)(pA * svA);
+    wp[g].y = (_Float16)(pB * svB);
+  }
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const uint32_t a32 = w ? r.vA.y : r.vA.x;
+    const uint32_t b32 = w ? r.vB.y : r.vB.x;
+    const uint32_t X = __builtin_amdgcn_perm(b32, a32, 0x05040100u);
+    const uint32_t Y = __builtin_amdgcn_perm(b32, a32, 0x07060302u);
+    const uint32_t X6 = X >> 6, Y6 = Y >> 6;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const uint32_t px = x <= 4 ? (X & (0x00030003u << (2 * x))) : (X6 & (0x00030003u << (2 * x - 6)));
+      const uint32_t py = x <= 4 ? (Y & (0x00030003u << (2 * x))) : (Y6 & (0x00030003u << (2 * x - 6)));
+      const half2_t hx = __builtin_bit_cast(half2_t, px);
+      const half2_t hy = __builtin_bit_cast(half2_t, py);
+#pragma unroll
+      for (int g = 0; g < GC; ++g) {
+        st.acc[g][16 * w + x] = __builtin_amdgcn_fdot2(hx, wp[g], st.acc[g][16 * w + x], false);
+        st.acc[g][16 * w + 8 + x] = __builtin_amdgcn_fdot2(hy, wp[g], st.acc[g][16 * w + 8 + x], false);
+      }
+    }
+  }
+}
+
+template <int GC>
+__global__ __launch_bounds__(256) void kv_int2_decode_attn_gqa(AttnArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
+  if (gw >= a.total_waves) return;
+  const int64_t split = gw % a.n_splits;
+  const int64_t bh = gw / a.n_splits;
+  const int hkv = (int)(bh % a.Hkv);
+  const int64_t b = bh / a.Hkv;
+  const int ts = lane >> 2;
+  const int j = lane & 3;
+  const int64_t s0 = split * a.tps;
+  const int64_t s1 = (s0 + a.tps < a.n_int2) ? s0 + a.tps : a.n_int2;
+
+  QuadQuery<GC> q;
+#pragma unroll
+  for (int g = 0; g < GC; ++g) {
+    const int hq = hkv * a.G + a.g0 + g;
+    const uint32_t *p = a.qprep + (b * a.Hq + hq) * kQprepDwordsPerHead + j * 32;
+#pragma unroll
+    for (int i = 0; i < 20; ++i) q.limb[g][i] = p[i];
+    q.qsum[g] = bits_as_float(p[24]);
+    q.qstep[g] = bits_as_float(p[25]);
+  }
+  QuadState<GC> st;
+#pragma unroll
+  for (int g = 0; g < GC; ++g) {
+    st.m[g] = kNegInf; st.l[g] = 0.0f; st.zacc[g] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) st.acc[g][i] = 0.0f;
+  }
+  const int64_t krow0 = bh * a.kT_cap + a.t_begin + s0;
+  const int64_t vrow0 = bh * a.vT_cap + a.t_begin + s0;
+  const uint8_t *kc = a.kcodes + krow0 * kCodeBytes, *vc = a.vcodes + vrow0 * kCodeBytes;
+  const uint16_t *ks = a.kscales + krow0 * kNGroups, *kz = a.kzeros + krow0 * kNGroups;
+  const uint16_t *vs = a.vscales + vrow0 * kNGroups, *vz = a.vzeros + vrow0 * kNGroups;
+  const uint32_t oc = (uint32_t)(ts * kCodeBytes + 8 * j);
+  const uint32_t os = (uint32_t)(ts * kNGroups + j);
+  const int64_t n = s1 - s0;
+  const int64_t nfull = n & ~(int64_t)31;
+  auto load_tile = [&](int64_t first_row) {
+    QuadTileRegs r;
+    const uint8_t *kct = kc + first_row * kCodeBytes, *vct = vc + first_row * kCodeBytes;
+    const uint16_t *kst = ks + first_row * kNGroups, *kzt = kz + first_row * kNGroups;
+    const uint16_t *vst = vs + first_row * kNGroups, *vzt = vz + first_row * kNGroups;
+    r.kA = *reinterpret_cast<const uint2 *>(kct + oc);
+    r.kB = *reinterpret_cast<const uint2 *>(kct + oc + 16 * kCodeBytes);
+    r.vA = *reinterpret_cast<const uint2 *>(vct + oc);
+    r.vB = *reinterpret_cast<const uint2 *>(vct + oc + 16 * kCodeBytes);
+    r.h[0] = kst[os]; r.h[1] = kzt[os];
+    r.h[2] = kst[os + 16 * kNGroups]; r.h[3] = kzt[os + 16 * kNGroups];
+    r.h[4] = vst[os]; r.h[5] = vzt[os];
+    r.h[6] = vst[os + 16 * kNGroups]; r.h[7] = vzt[os + 16 * kNGroups];
+    return r;
+  };
+  const int64_t ntiles = nfull >> 5;
+  if (ntiles > 0) {
+    const int64_t last = ntiles - 1;
+    QuadTileRegs r0 = load_tile(0), r1 = load_tile(32 * (last < 1 ? last : 1)), r2;
+    int64_t i = 0;
+    for (; i + 3 <= ntiles; i += 3) {
+      r2 = load_tile(32 * (i + 2 < last ? i + 2 : last));
+      quad_tile<GC>(st, q, r0, true, true);
+      r0 = load_tile(32 * (i + 3 < last ? i + 3 : last));
+      quad_tile<GC>(st, q, r1, true, true);
+      r1 = load_tile(32 * (i + 4 < last ? i + 4 : last));
+      quad_tile<GC>(st, q, r2, true, true);
+    }
+    if (i < ntiles) quad_tile<GC>(st, q, r0, true, true);
+    if (i + 1 < ntiles) quad_tile<GC>(st, q, r1, true, true);
+  }
+  if (nfull < n) {
+    const int64_t ta = nfull + ts, tb = nfull + 16 + ts;
+    const bool va = ta < n, vb = tb < n;
+    const int64_t ra = va ? ta : 0, rb = vb ? tb : 0;
+    QuadTileRegs r;
+    r.kA = *reinterpret_cast<const uint2 *>(kc + ra * kCodeBytes + 8 * j);
+    r.kB = *reinterpret_cast<const uint2 *>(kc + rb * kCodeBytes + 8 * j);
+    r.vA = *reinterpret_cast<const uint2 *>(vc + ra * kCodeBytes + 8 * j);
+    r.vB = *reinterpret_cast<const uint2 *>(vc + rb * kCodeBytes + 8 * j);
+    r.h[0] = ks[ra * kNGroups + j]; r.h[1] = kz[ra * kNGroups + j];
+    r.h[2] = ks[rb * kNGroups + j]; r.h[3] = kz[rb * kNGroups + j];
+    r.h[4] = vs[ra * kNGroups + j]; r.h[5] = vz[ra * kNGroups + j];
+    r.h[6] = vs[rb * kNGroups + j]; r.h[7] = vz[rb * kNGroups + j];
+    quad_tile<GC>(st, q, r, va, vb);
+  }
+#pragma unroll
+  for (int g = 0; g < GC; ++g) {
+#pragma unroll
+    for (int msk = 4; msk < 64; msk <<= 1) {
+      st.l[g] += shfl_xor_f(st.l[g], msk);
+      st.zacc[g] += shfl_xor_f(st.zacc[g], msk);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) st.acc[g][i] += shfl_xor_f(st.acc[g][i], msk);
+    }
+    if (ts == 0) {
+      const int hq = hkv * a.G + a.g0 + g;
+      float *dst = a.partials + ((b * a.Hq + hq) * a.n_splits + split) * kPartialStride;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) dst[32 * j + i] = __builtin_fmaf(st.acc[g][i], chan_unscale(i & 7), st.zacc[g]);
       if (j == 0) {
-        dst[128] = m[g];
-        dst[129] = l[g];
+        dst[128] = st.m[g];
+        dst[129] = st.l[g];
       }
     }
   }
@@ -478,15 +777,21 @@ hipError_t launch_decode(const DecodeArgs &d, hipStream_t stream) {
     a.Hkv = (int)d.Hkv; a.Hq = (int)d.Hq; a.G = G;
     a.qprep = reinterpret_cast<const uint32_t *>(d.qprep);
     a.partials = d.partials;
-    const int GC = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
     const dim3 grid((unsigned)((a.total_waves + 3) / 4));
-    for (int g0 = 0; g0 < G; g0 += GC) {
-      a.g0 = g0;
-      if (GC == 4) hipLaunchKernelGGL(kv_int2_decode_attn<4>, grid, dim3(256), 0, stream, a);
-      else if (GC == 2) hipLaunchKernelGGL(kv_int2_decode_attn<2>, grid, dim3(256), 0, stream, a);
-      else hipLaunchKernelGGL(kv_int2_decode_attn<1>, grid, dim3(256), 0, stream, a);
+    if (G == 1) {
+      a.g0 = 0;
+      hipLaunchKernelGGL(kv_int2_decode_attn<1>, grid, dim3(256), 0, stream, a);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
+    } else {
+      const int GC = (G % 2 == 0) ? 2 : 1;
+      for (int g0 = 0; g0 < G; g0 += GC) {
+        a.g0 = g0;
+        if (GC == 2) hipLaunchKernelGGL(kv_int2_decode_attn_gqa<2>, grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL(kv_int2_decode_attn_gqa<1>, grid, dim3(256), 0, stream, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
     }
   }
   {

@@ -11,79 +11,139 @@
 // values, so min/max need no cross-lane traffic, and the lane packs its 32
 // codes into 8 bytes.  Consecutive quads handle consecutive tokens of one
 // (batch, head), so a wave's code stores cover 512 contiguous bytes.
+//
+// The kernel is bound by VALU issue as much as by HBM (2.4 bytes of traffic
+// per element), so the per-element work is kept small: the fp16->fp32
+// conversion rides on the first butterfly (v_fma_mix), the 1/sqrt(128)
+// normalization rides on the quantizer's subtraction (one FMA), and
+// rounding + clamping + packing take three instructions per code (med3,
+// magic-number add, shift-add).
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
 namespace kvq {
 
-// The quantizer as a fixed sequence of IEEE fp32 operations (no fused
-// multiply-add): s = fp32(fp32(max - min) / 3); scale = fp16(s);
-// zero = fp16(min + 0) (a zero minimum is +0 whatever the signs of the
-// group's zeros); code = clamp(rint((y - zero) * fp32(1/scale)), 0, 3).
-__device__ __forceinline__ void quantize_group32(const float (&v)[32], uint32_t &w0,
-                                                 uint32_t &w1, uint16_t &sbits,
-                                                 uint16_t &zbits) {
-#pragma clang fp contract(off)
-  float mn = v[0], mx = v[0];
+// Adding 1.5 * 2^23 to t in [0, 3] rounds t to an integer with round half
+// to even and leaves that integer in the low mantissa bits.
+constexpr float kRoundMagic = 12582912.0f;          // 0x4B400000
+constexpr uint32_t kRoundMagicBits = 0x4B400000u;
+
+// Sum over i < 16 of (kRoundMagicBits << 2i) mod 2^32: what the shift-add
+// packing of 16 magic-biased codes adds on top of the codes themselves.
+constexpr uint32_t magic_pack_bias() {
+  uint32_t s = 0;
+  for (int i = 0; i < 16; ++i) s += kRoundMagicBits << (2 * i);
+  return s;
+}
+constexpr uint32_t kPackBias = magic_pack_bias();
+
+// (x << s) + acc in one instruction (v_lshl_add_u32).
+__device__ __forceinline__ uint32_t shl_add(uint32_t x, uint32_t sh, uint32_t acc) {
+  uint32_t r;
+  asm("v_lshl_add_u32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(sh), "v"(acc));
+  return r;
+}
+
+__device__ __forceinline__ uint32_t code_bits(float u) {
+  const float t = __builtin_amdgcn_fmed3f(u, 0.0f, 3.0f);
+  return float_as_bits(t + kRoundMagic);            // = 0x4B400000 | code
+}
+
+// Group min/max over 32 values.
+__device__ __forceinline__ void minmax32(const float (&v)[32], float &mn, float &mx) {
+  mn = v[0];
+  mx = v[0];
 #pragma unroll
   for (int i = 1; i < 32; ++i) {
     mn = fminf(mn, v[i]);
     mx = fmaxf(mx, v[i]);
   }
+}
+
+// Scale and zero of a group whose fp32 min / max are mn / mx:
+// s = fp32(fp32(mx - mn) / 3); scale = fp16(s); zero = fp16(mn + 0), so a
+// zero minimum gives +0 whatever the signs of the group's zeros.
+__device__ __forceinline__ void scale_zero(float mn, float mx, uint16_t &sbits, uint16_t &zbits,
+                                           float &sf, float &zf) {
+#pragma clang fp contract(off)
   const float range = mx - mn;
-  const float s32 = range / 3.0f;            // correctly rounded fp32 division
+  const float s32 = range / 3.0f;                   // correctly rounded division
   sbits = float_to_half_bits(s32);
-  zbits = float_to_half_bits(mn + 0.0f);   // -0 + 0 = +0 in round-to-nearest
-  const float sf = half_bits_to_float(sbits);
-  const float zf = half_bits_to_float(zbits);
+  zbits = float_to_half_bits(mn + 0.0f);
+  sf = half_bits_to_float(sbits);
+  zf = half_bits_to_float(zbits);
+}
+
+// Exact quantizer on the rows as given (no rotation): the fixed IEEE fp32
+// sequence u = fp32(fp32(y - zero) * fp32(1/scale)), code = clamp(rint(u), 0, 3),
+// bit-for-bit.  clamp-then-round equals round-then-clamp for [0, 3].
+__device__ __forceinline__ void quantize_group32_exact(const float (&v)[32], uint32_t &w0,
+                                                       uint32_t &w1, uint16_t &sbits,
+                                                       uint16_t &zbits) {
+#pragma clang fp contract(off)
+  float mn, mx, sf, zf;
+  minmax32(v, mn, mx);
+  scale_zero(mn, mx, sbits, zbits, sf, zf);
   const bool degenerate = (sf == 0.0f);
   const float inv = 1.0f / (degenerate ? 1.0f : sf);
   uint32_t a = 0, b = 0;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float u = (v[i] - zf) * inv;
-    float r = __builtin_rintf(u);           // round half to even
-    r = fminf(fmaxf(r, 0.0f), 3.0f);
-    const uint32_t c = (uint32_t)r;
-    if (i < 16) a |= c << (2 * i);
-    else        b |= c << (2 * (i - 16));
+  for (int i = 0; i < 16; ++i) {
+    a = shl_add(code_bits((v[i] - zf) * inv), 2 * i, a);
+    b = shl_add(code_bits((v[16 + i] - zf) * inv), 2 * i, b);
   }
-  w0 = degenerate ? 0u : a;
-  w1 = degenerate ? 0u : b;
+  w0 = degenerate ? 0u : a - kPackBias;
+  w1 = degenerate ? 0u : b - kPackBias;
 }
 
-template <typename TIn>
-__device__ __forceinline__ void load_row32(const TIn *src, float (&v)[32]);
-
-template <>
-__device__ __forceinline__ void load_row32<_Float16>(const _Float16 *src, float (&v)[32]) {
-  const u32x4_t *p = reinterpret_cast<const u32x4_t *>(src);
+// Quantizer on unnormalized FWHT outputs z (the rotated row is y = z * c,
+// c = fp32(1/sqrt(128))).  min/max of y are taken as c * min/max of z (the
+// rounding of a positive scaling is monotonic, so they equal the min/max of
+// the rounded y).  Per element: d = fp32(fma(z, c, -zero)) (y - zero with one
+// rounding), clamped to [0, 3*scale], then fma(d, 1/scale, magic) rounds
+// d/scale to the nearest code with a single rounding.  This differs from the
+// three-rounding reference sequence only for arguments within a few ulps of
+// a half-integer.
+__device__ __forceinline__ void quantize_group32_fwht(const float (&z)[32], uint32_t &w0,
+                                                      uint32_t &w1, uint16_t &sbits,
+                                                      uint16_t &zbits) {
+  constexpr float c = 0.08838834764831845f;         // fp32(1/sqrt(128))
+  float zmn, zmx, sf, zf;
+  minmax32(z, zmn, zmx);
+  scale_zero(zmn * c, zmx * c, sbits, zbits, sf, zf);
+  const bool degenerate = (sf == 0.0f);
+  const float inv = 1.0f / (degenerate ? 1.0f : sf);
+  const float top = 3.0f * sf;                      // exact: sf has 11 significant bits
+  uint32_t a = 0, b = 0;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const u32x4_t u = __builtin_nontemporal_load(p + k);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[8 * k + 2 * e] = half_bits_to_float((uint16_t)(w[e] & 0xFFFFu));
-      v[8 * k + 2 * e + 1] = half_bits_to_float((uint16_t)(w[e] >> 16));
-    }
+  for (int i = 0; i < 16; ++i) {
+    const float da = __builtin_amdgcn_fmed3f(__builtin_fmaf(z[i], c, -zf), 0.0f, top);
+    const float db = __builtin_amdgcn_fmed3f(__builtin_fmaf(z[16 + i], c, -zf), 0.0f, top);
+    a = shl_add(float_as_bits(__builtin_fmaf(da, inv, kRoundMagic)), 2 * i, a);
+    b = shl_add(float_as_bits(__builtin_fmaf(db, inv, kRoundMagic)), 2 * i, b);
   }
+  w0 = degenerate ? 0u : a - kPackBias;
+  w1 = degenerate ? 0u : b - kPackBias;
 }
 
-template <>
-__device__ __forceinline__ void load_row32<float>(const float *src, float (&v)[32]) {
-  const float4_t *p = reinterpret_cast<const float4_t *>(src);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const float4_t u = __builtin_nontemporal_load(p + k);
-    v[4 * k] = u.x; v[4 * k + 1] = u.y; v[4 * k + 2] = u.z; v[4 * k + 3] = u.w;
-  }
+// lo + hi and lo - hi of the two fp16 halves of a dword, in fp32 with one
+// rounding (v_fma_mix_f32 reads fp16 operands directly).
+__device__ __forceinline__ float mix_sum(uint32_t w) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, 1.0, %1 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(w));
+  return r;
+}
+__device__ __forceinline__ float mix_diff(uint32_t w) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, -1.0, %1 op_sel:[1,0,0] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(w));
+  return r;
 }
 
-// Normalized FWHT of a 128-vector spread over a quad (32 values per lane).
-__device__ __forceinline__ void fwht128_quad(float (&v)[32], int j) {
+// Unnormalized FWHT stages 2..7 of a 128-vector spread over a quad, after
+// stage 1 (stride 1) was applied while loading.
+__device__ __forceinline__ void fwht128_quad_rest(float (&v)[32], int j) {
 #pragma unroll
-  for (int hs = 1; hs < 32; hs <<= 1) {
+  for (int hs = 2; hs < 32; hs <<= 1) {
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       if ((i & hs) == 0) {
@@ -99,9 +159,65 @@ __device__ __forceinline__ void fwht128_quad(float (&v)[32], int j) {
   for (int i = 0; i < 32; ++i) v[i] = quad_butterfly<kQuadXor1>(v[i], n1);
 #pragma unroll
   for (int i = 0; i < 32; ++i) v[i] = quad_butterfly<kQuadXor2>(v[i], n2);
-  const float norm = 0.08838834764831845f;  // fp32(1/sqrt(128))
+}
+
+// Load a lane's 32 channels.  ROT: apply FWHT stage 1 on the way in.
+template <typename TIn, bool ROT>
+__device__ __forceinline__ void load_row32(const TIn *src, float (&v)[32]);
+
+template <>
+__device__ __forceinline__ void load_row32<_Float16, true>(const _Float16 *src, float (&v)[32]) {
+  const u32x4_t *p = reinterpret_cast<const u32x4_t *>(src);
 #pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] *= norm;
+  for (int k = 0; k < 4; ++k) {
+    const u32x4_t u = __builtin_nontemporal_load(p + k);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[8 * k + 2 * e] = mix_sum(w[e]);
+      v[8 * k + 2 * e + 1] = mix_diff(w[e]);
+    }
+  }
+}
+
+template <>
+__device__ __forceinline__ void load_row32<_Float16, false>(const _Float16 *src, float (&v)[32]) {
+  const u32x4_t *p = reinterpret_cast<const u32x4_t *>(src);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const u32x4_t u = __builtin_nontemporal_load(p + k);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[8 * k + 2 * e] = half_bits_to_float((uint16_t)(w[e] & 0xFFFFu));
+      v[8 * k + 2 * e + 1] = half_bits_to_float((uint16_t)(w[e] >> 16));
+    }
+  }
+}
+
+template <bool ROT>
+__device__ __forceinline__ void load_row32_f32(const float *src, float (&v)[32]) {
+  const float4_t *p = reinterpret_cast<const float4_t *>(src);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float4_t u = __builtin_nontemporal_load(p + k);
+    if (ROT) {
+      v[4 * k] = u.x + u.y;
+      v[4 * k + 1] = u.x - u.y;
+      v[4 * k + 2] = u.z + u.w;
+      v[4 * k + 3] = u.z - u.w;
+    } else {
+      v[4 * k] = u.x; v[4 * k + 1] = u.y; v[4 * k + 2] = u.z; v[4 * k + 3] = u.w;
+    }
+  }
+}
+template <>
+__device__ __forceinline__ void load_row32<float, true>(const float *src, float (&v)[32]) {
+  load_row32_f32<true>(src, v);
+}
+template <>
+__device__ __forceinline__ void load_row32<float, false>(const float *src, float (&v)[32]) {
+  load_row32_f32<false>(src, v);
 }
 
 struct RowsKernelArgs {
@@ -129,16 +245,111 @@ __global__ __launch_bounds__(256) void kv_rotate_quant_rows(RowsKernelArgs a) {
   const TIn *src = reinterpret_cast<const TIn *>(s.x) + b * a.stride_b + tl * a.stride_t +
                    (int64_t)h * a.stride_h + 32 * j;
   float v[32];
-  load_row32<TIn>(src, v);
-  if (ROT) fwht128_quad(v, j);
+  load_row32<TIn, ROT>(src, v);
   uint32_t w0, w1;
   uint16_t sb, zb;
-  quantize_group32(v, w0, w1, sb, zb);
+  if (ROT) {
+    fwht128_quad_rest(v, j);
+    quantize_group32_fwht(v, w0, w1, sb, zb);
+  } else {
+    quantize_group32_exact(v, w0, w1, sb, zb);
+  }
   if (valid) {
     const int64_t row = (b * a.Hkv + h) * s.T_cap + a.t_offset + t;
     *reinterpret_cast<uint2 *>(s.codes + row * kCodeBytes + 8 * j) = make_uint2(w0, w1);
     s.scales[row * kNGroups + j] = sb;
     s.zeros[row * kNGroups + j] = zb;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp16 input + Hadamard: one row per lane, all seven butterfly stages in
+// registers (no cross-lane traffic).  A wave handles 64 consecutive tokens
+// of one (batch, head, side).  Rows are first brought into LDS with fully
+// coalesced 16-byte loads (16 lanes per 256-byte row) and read back one row
+// per lane; rows are padded by 16 bytes so the row-per-lane reads hit
+// distinct banks.
+// ---------------------------------------------------------------------------
+constexpr int kStageRowDwords = 64 + 4;     // 128 fp16 + 16-byte pad
+
+// grid: x = token blocks of 64, y = KV head, z = batch * n_sides + side;
+// block = one wave.
+__global__ __launch_bounds__(64) void kv_rotate_quant_fwht_f16(RowsKernelArgs a) {
+  __shared__ uint32_t stage[64 * kStageRowDwords];
+  const int lane = threadIdx.x;
+  const int h = blockIdx.y;
+  const int sidx = (int)(blockIdx.z % (unsigned)a.n_sides);
+  const int64_t b = blockIdx.z / (unsigned)a.n_sides;
+  const QuantSide s = sidx ? a.side[1] : a.side[0];
+  const int64_t t0 = (int64_t)blockIdx.x * 64;
+  const _Float16 *base = reinterpret_cast<const _Float16 *>(s.x) + b * a.stride_b +
+                         (int64_t)h * a.stride_h;
+
+  // coalesced staging: instruction i covers rows 4i..4i+3, 16 lanes per row
+  const int chunk = lane & 15;
+  const int r0 = lane >> 4;
+  if (t0 + 64 <= a.T_new) {
+    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(base + (t0 + r0) * a.stride_t) + chunk;
+    const int64_t step = 4 * a.stride_t / 8;        // 4 rows, in 16-byte units
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const u32x4_t u = __builtin_nontemporal_load(src + i * step);
+      *reinterpret_cast<u32x4_t *>(&stage[(4 * i + r0) * kStageRowDwords + 4 * chunk]) = u;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 4 * i + r0;
+      const int64_t t = t0 + row;
+      const int64_t tl = t < a.T_new ? t : 0;
+      const u32x4_t u = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t *>(base + tl * a.stride_t) + chunk);
+      *reinterpret_cast<u32x4_t *>(&stage[row * kStageRowDwords + 4 * chunk]) = u;
+    }
+  }
+  __syncthreads();
+
+  float v[128];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const u32x4_t u = *reinterpret_cast<const u32x4_t *>(&stage[lane * kStageRowDwords + 4 * k]);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[8 * k + 2 * e] = mix_sum(w[e]);          // FWHT stage 1 on the way in
+      v[8 * k + 2 * e + 1] = mix_diff(w[e]);
+    }
+  }
+#pragma unroll
+  for (int hs = 2; hs < 128; hs <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 128; ++i) {
+      if ((i & hs) == 0) {
+        const float x = v[i], y = v[i + hs];
+        v[i] = x + y;
+        v[i + hs] = x - y;
+      }
+    }
+  }
+  uint32_t w[8];
+  uint16_t sb[4], zb[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const float(&z)[32] = *reinterpret_cast<const float(*)[32]>(&v[32 * g]);
+    quantize_group32_fwht(z, w[2 * g], w[2 * g + 1], sb[g], zb[g]);
+  }
+  const int64_t t = t0 + lane;
+  if (t < a.T_new) {
+    const int64_t row = (b * a.Hkv + h) * s.T_cap + a.t_offset + t;
+    u32x4_t c0 = {w[0], w[1], w[2], w[3]};
+    u32x4_t c1 = {w[4], w[5], w[6], w[7]};
+    u32x4_t *cp = reinterpret_cast<u32x4_t *>(s.codes + row * kCodeBytes);
+    cp[0] = c0;
+    cp[1] = c1;
+    *reinterpret_cast<uint2 *>(s.scales + row * kNGroups) =
+        make_uint2((uint32_t)sb[0] | ((uint32_t)sb[1] << 16), (uint32_t)sb[2] | ((uint32_t)sb[3] << 16));
+    *reinterpret_cast<uint2 *>(s.zeros + row * kNGroups) =
+        make_uint2((uint32_t)zb[0] | ((uint32_t)zb[1] << 16), (uint32_t)zb[2] | ((uint32_t)zb[3] << 16));
   }
 }
 
@@ -154,8 +365,12 @@ hipError_t launch_quantize_rows(const QuantArgs &q, hipStream_t stream) {
   a.Hkv = (int)q.Hkv;
   a.n_sides = q.n_sides;
   dim3 grid((unsigned)((q.T_new + 63) / 64), (unsigned)q.Hkv, (unsigned)(q.B * q.n_sides));
-  dim3 block(256);
   const bool rot = (q.rot == 1);
+  if (rot && !q.in_f32) {
+    hipLaunchKernelGGL(kv_rotate_quant_fwht_f16, grid, dim3(64), 0, stream, a);
+    return hipGetLastError();
+  }
+  dim3 block(256);
   if (q.in_f32) {
     if (rot) hipLaunchKernelGGL((kv_rotate_quant_rows<float, true>), grid, block, 0, stream, a);
     else     hipLaunchKernelGGL((kv_rotate_quant_rows<float, false>), grid, block, 0, stream, a);

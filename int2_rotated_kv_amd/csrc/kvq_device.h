@@ -47,6 +47,12 @@ __device__ __forceinline__ float quad_butterfly(float own, float neg) {
   return __builtin_fmaf(own, neg, other);   // exact: own * (+-1) + other, one rounding
 }
 
+// Rotate right by N lanes within each row of 16 lanes (DPP row_ror).
+template <int N>
+__device__ __forceinline__ float row_ror(float v) {
+  return bits_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)float_as_bits(v), 0x120 + N, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
