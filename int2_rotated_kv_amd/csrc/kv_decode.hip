@@ -23,10 +23,13 @@
 // Scores never dequantize a key: with per-group scale s and zero z,
 //   q'.k_hat = sum_j s_j * (sum_{c in j} q'_c code_c) + z_j * (sum_{c in j} q'_c),
 // and the inner sum is an exact int32 dot product (v_dot8 on 4-bit code
-// nibbles and 4-bit query limbs).  Values: o'_c += sum_t p_t s_{t,j} code_{t,c}
-// + sum_t p_t z_{t,j}; the first term runs as v_dot2 over token pairs with
-// codes placed in fp16 subnormal encodings (code * 2^(e-24)) and the
-// weights p*s in fp16, accumulated in fp32.
+// nibbles and 4-bit query limbs).  Values: with w_t = fp16(p_t s_{t,j}),
+//   o'_c = sum_t w_t code_{t,c} - 1.5 sum_t w_t + sum_t p_t (z_{t,j} + 1.5 s_{t,j});
+// the first term runs as v_dot2 over token pairs with codes placed in fp16
+// subnormal encodings (code * 2^(e-24)), accumulated in fp32.  Centering the
+// codes on 1.5 makes the fp16 rounding of w multiply code - 1.5 in
+// [-1.5, 1.5], so it does not get amplified by the cancellation between the
+// code and zero-point terms.
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
@@ -183,8 +186,10 @@ struct TileRegs {
 
 template <int GC>
 struct AttnState {
-  float m[GC], l[GC], zacc[GC][2], acc[GC][64];
+  float m[GC], l[GC], zacc[GC][2], wsum[GC][2], acc[GC][64];
 };
+
+constexpr uint32_t kHalf2Ones = 0x3C003C00u;   // (1.0, 1.0) in fp16
 
 // Per-lane query data for the lane's two channel groups of GC heads.
 template <int GC>
@@ -248,6 +253,8 @@ __device__ __forceinline__ void attn_tile(AttnState<GC> &st, const QueryLimbs<GC
       st.l[g] *= alpha;
       st.zacc[g][0] *= alpha;
       st.zacc[g][1] *= alpha;
+      st.wsum[g][0] *= alpha;
+      st.wsum[g][1] *= alpha;
 #pragma unroll
       for (int i = 0; i < 64; ++i) st.acc[g][i] *= alpha;
       st.m[g] = mx;
@@ -261,9 +268,12 @@ __device__ __forceinline__ void attn_tile(AttnState<GC> &st, const QueryLimbs<GC
       const float zvA = gi ? hi_half(r.vzA) : lo_half(r.vzA);
       const float svB = gi ? hi_half(r.vsB) : lo_half(r.vsB);
       const float zvB = gi ? hi_half(r.vzB) : lo_half(r.vzB);
-      st.zacc[g][gi] = __builtin_fmaf(pA, zvA, __builtin_fmaf(pB, zvB, st.zacc[g][gi]));
+      st.zacc[g][gi] = __builtin_fmaf(pA, __builtin_fmaf(1.5f, svA, zvA),
+                                      __builtin_fmaf(pB, __builtin_fmaf(1.5f, svB, zvB), st.zacc[g][gi]));
       wp[g][gi].x = (_Float16)(pA * svA);
       wp[g][gi].y = (_Float16)(pB * svB);
+      st.wsum[g][gi] = __builtin_amdgcn_fdot2(wp[g][gi], __builtin_bit_cast(half2_t, kHalf2Ones),
+                                              st.wsum[g][gi], false);
     }
   }
 
@@ -327,6 +337,7 @@ __global__ __launch_bounds__(256) void kv_int2_decode_attn(AttnArgs a) {
 #pragma unroll
   for (int g = 0; g < GC; ++g) {
     st.m[g] = kNegInf; st.l[g] = 0.0f; st.zacc[g][0] = 0.0f; st.zacc[g][1] = 0.0f;
+    st.wsum[g][0] = 0.0f; st.wsum[g][1] = 0.0f;
 #pragma unroll
     for (int i = 0; i < 64; ++i) st.acc[g][i] = 0.0f;
   }
@@ -406,7 +417,9 @@ __global__ __launch_bounds__(256) void kv_int2_decode_attn(AttnArgs a) {
   // reduce over the 32 token slots (lanes sharing h), then write the partial
 #pragma unroll
   for (int g = 0; g < GC; ++g) {
-    float l = st.l[g], z0 = st.zacc[g][0], z1 = st.zacc[g][1];
+    float l = st.l[g];
+    float z0 = __builtin_fmaf(-1.5f, st.wsum[g][0], st.zacc[g][0]);
+    float z1 = __builtin_fmaf(-1.5f, st.wsum[g][1], st.zacc[g][1]);
 #pragma unroll
     for (int msk = 2; msk < 64; msk <<= 1) {
       l += shfl_xor_f(l, msk);
@@ -444,7 +457,7 @@ struct QuadTileRegs {
 
 template <int GC>
 struct QuadState {
-  float m[GC], l[GC], zacc[GC], acc[GC][32];
+  float m[GC], l[GC], zacc[GC], wsum[GC], acc[GC][32];
 };
 
 template <int GC>
@@ -482,6 +495,7 @@ __device__ __forceinline__ void quad_tile(QuadState<GC> &st, const QuadQuery<GC>
       const float alpha = __builtin_amdgcn_exp2f(st.m[g] - mx);
       st.l[g] *= alpha;
       st.zacc[g] *= alpha;
+      st.wsum[g] *= alpha;
 #pragma unroll
       for (int i = 0; i < 32; ++i) st.acc[g][i] *= alpha;
       st.m[g] = mx;
@@ -489,9 +503,11 @@ __device__ __forceinline__ void quad_tile(QuadState<GC> &st, const QuadQuery<GC>
     const float pA = __builtin_amdgcn_exp2f(sa - st.m[g]);
     const float pB = __builtin_amdgcn_exp2f(sb - st.m[g]);
     st.l[g] += pA + pB;
-    st.zacc[g] = __builtin_fmaf(pA, zvA, __builtin_fmaf(pB, zvB, st.zacc[g]));
+    st.zacc[g] = __builtin_fmaf(pA, __builtin_fmaf(1.5f, svA, zvA),
+                                __builtin_fmaf(pB, __builtin_fmaf(1.5f, svB, zvB), st.zacc[g]));
     wp[g].x = (_Float16)(pA * svA);
     wp[g].y = (_Float16)(pB * svB);
+    st.wsum[g] = __builtin_amdgcn_fdot2(wp[g], __builtin_bit_cast(half2_t, kHalf2Ones), st.wsum[g], false);
   }
 #pragma unroll
   for (int w = 0; w < 2; ++w) {
@@ -543,7 +559,7 @@ __global__ __launch_bounds__(256) void kv_int2_decode_attn_gqa(AttnArgs a) {
   QuadState<GC> st;
 #pragma unroll
   for (int g = 0; g < GC; ++g) {
-    st.m[g] = kNegInf; st.l[g] = 0.0f; st.zacc[g] = 0.0f;
+    st.m[g] = kNegInf; st.l[g] = 0.0f; st.zacc[g] = 0.0f; st.wsum[g] = 0.0f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) st.acc[g][i] = 0.0f;
   }
@@ -604,6 +620,7 @@ __global__ __launch_bounds__(256) void kv_int2_decode_attn_gqa(AttnArgs a) {
   }
 #pragma unroll
   for (int g = 0; g < GC; ++g) {
+    st.zacc[g] = __builtin_fmaf(-1.5f, st.wsum[g], st.zacc[g]);
 #pragma unroll
     for (int msk = 4; msk < 64; msk <<= 1) {
       st.l[g] += shfl_xor_f(st.l[g], msk);

@@ -1,0 +1,137 @@
+"""Parity at the workloads' full sizes, in the launch configuration the
+benchmark uses (same shapes, so the same grid and split plan).
+
+The whole cache is written and read on the GPU; the oracle recomputes
+sampled (batch, KV head) slices one at a time: the codes of that head must
+match at ties, and the decode outputs of the head's query heads must be
+within the attention bar against the oracle run on the GPU's own codes of
+that head.  The sample's inputs are regenerated on the CPU from the seeded
+generator and checked equal to the device copy first.
+"""
+import json
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import kvq_oracle as O
+import workloads as W
+import int2_rotated_kv_amd as kvq
+from parity_util import (require_gpu, rot_matrix, compare_codes_at_ties, normwise_rel_err)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+ATTN_TOL = 2e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    yield
+    torch.cuda.empty_cache()
+
+
+def _report(name, **kw):
+    print(f"[fullsize] {name} " + json.dumps(kw), flush=True)
+
+
+def _head_slice_cpu(cfg, which, b, h, t0=0, t1=None):
+    """[T, d] rows of (batch b, KV head h) regenerated on the CPU."""
+    return W.kv_tokens(cfg, which, b0=b, b1=b + 1, h0=h, h1=h + 1, t0=t0, t1=t1)[0, :, 0]
+
+
+def _check_head(cfg, Kd, Vd, ck, cv, out, q, b, hk, rot, R, t_begin, t_end,
+                sink=None, res=None):
+    """Codes of head (b, hk) vs oracle at ties; decode of its query heads vs
+    the oracle on the GPU codes."""
+    Rm = rot_matrix(rot, R)
+    Rh = Rm if rot != "dense" else Rm[hk]
+    stats = {}
+    for which, xd, c in (("K", Kd, ck), ("V", Vd, cv)):
+        x_cpu = _head_slice_cpu(cfg, which, b, hk)
+        x_dev = xd[b, :, hk].cpu()
+        assert torch.equal(x_cpu, x_dev), "generator differs between CPU and GPU"
+        xr = x_cpu[t_begin:t_end].numpy()[None]                # [1, T, d]
+        gpu = tuple(a[b, hk, t_begin:t_end].cpu().numpy()[None]
+                    for a in (c.codes, c.scales, c.zeros))
+        ora = O.quantize_cache(xr[:, None], Rh)
+        ora = tuple(a[:, 0] for a in ora)
+        stats[which] = compare_codes_at_ties(xr, Rh, gpu, ora)
+    G = cfg.G
+    hq = slice(hk * G, hk * G + G)
+    kc = tuple(a[b:b + 1, hk:hk + 1].cpu().numpy() for a in (ck.codes, ck.scales, ck.zeros))
+    vc = tuple(a[b:b + 1, hk:hk + 1].cpu().numpy() for a in (cv.codes, cv.scales, cv.zeros))
+    kw = {}
+    if sink is not None:
+        kw.update(sink_k=sink[0][b:b + 1, hk:hk + 1].cpu().numpy(),
+                  sink_v=sink[1][b:b + 1, hk:hk + 1].cpu().numpy())
+    if res is not None:
+        kw.update(res_k=res[0][b:b + 1, hk:hk + 1].cpu().numpy(),
+                  res_v=res[1][b:b + 1, hk:hk + 1].cpu().numpy())
+    Rd = Rh if Rh is None or rot != "dense" else Rh[None]
+    ref = O.decode_attention(q[b:b + 1, hq].cpu().numpy(), kc, vc, t_begin, t_end, Rd, **kw)
+    err = normwise_rel_err(out[b:b + 1, hq].float().cpu().numpy(), ref)
+    return stats, err
+
+
+def test_fullsize_config3_throughput():
+    cfg = W.config(3)
+    B, T, H, d = cfg.B, cfg.T, cfg.Hkv, cfg.d
+    K = W.kv_tokens(cfg, "K", device=DEV)
+    V = W.kv_tokens(cfg, "V", device=DEV)
+    q = W.queries(cfg, device=DEV)
+    ck, cv = kvq.Int2Cache.empty(B, H, T), kvq.Int2Cache.empty(B, H, T)
+    kvq.kvq_quantize(K, V, ck, cv, rot="hadamard")
+    out = kvq.kvq_decode_attention(q, ck, cv, 0, T, rot="hadamard")
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    for b, hk in ((0, 0), (7, 13), (15, 31)):
+        stats, err = _check_head(cfg, K, V, ck, cv, out, q, b, hk, "hadamard", None, 0, T)
+        _report(f"c3 b={b} h={hk}", normwise=err, K=stats["K"], V=stats["V"])
+        assert err <= ATTN_TOL
+
+
+def test_fullsize_config4_dense_gqa():
+    cfg = W.config(4)
+    B, T, H, d = cfg.B, cfg.T, cfg.Hkv, cfg.d
+    R = W.dense_rotations(cfg)
+    Rg = torch.as_tensor(R, device=DEV).contiguous()
+    K = W.kv_tokens(cfg, "K", device=DEV)
+    V = W.kv_tokens(cfg, "V", device=DEV)
+    q = W.queries(cfg, device=DEV)
+    ck, cv = kvq.Int2Cache.empty(B, H, T), kvq.Int2Cache.empty(B, H, T)
+    p0, p1 = cfg.quant_range                     # prefill slice [98304, 131072)
+    kvq.kvq_quantize(K[:, :p0], V[:, :p0], ck, cv, rot="dense", R=Rg)
+    kvq.kvq_quantize(K[:, p0:p1], V[:, p0:p1], ck, cv, rot="dense", R=Rg, t_offset=p0)
+    out = kvq.kvq_decode_attention(q, ck, cv, 0, T, rot="dense", R=Rg)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    for b, hk in ((0, 0), (3, 5)):
+        stats, err = _check_head(cfg, K, V, ck, cv, out, q, b, hk, "dense", R, 0, T)
+        _report(f"c4 b={b} h={hk}", normwise=err, K=stats["K"], V=stats["V"])
+        assert err <= ATTN_TOL
+
+
+def test_fullsize_config5_sinks_residual():
+    cfg = W.config(5)
+    B, T, H, d = cfg.B, cfg.T, cfg.Hkv, cfg.d
+    tb, te = cfg.int2_range                     # [4, 65408)
+    K = W.kv_tokens(cfg, "K", device=DEV)
+    V = W.kv_tokens(cfg, "V", device=DEV)
+    q = W.queries(cfg, device=DEV)
+    ck, cv = kvq.Int2Cache.empty(B, H, T), kvq.Int2Cache.empty(B, H, T)
+    kvq.kvq_quantize(K[:, tb:te], V[:, tb:te], ck, cv, rot="hadamard", t_offset=tb)
+    sink = tuple(x[:, :tb].permute(0, 2, 1, 3).contiguous() for x in (K, V))
+    res = tuple(x[:, te:].permute(0, 2, 1, 3).contiguous() for x in (K, V))
+    out = kvq.kvq_decode_attention(q, ck, cv, tb, te, rot="hadamard", sink_k=sink[0],
+                                   sink_v=sink[1], res_k=res[0], res_v=res[1])
+    out_int2 = kvq.kvq_decode_attention(q, ck, cv, tb, te, rot="hadamard")
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(out_int2.float()).all()
+    for b, hk in ((0, 0), (5, 27)):
+        stats, err = _check_head(cfg, K, V, ck, cv, out, q, b, hk, "hadamard", None, tb, te,
+                                 sink=sink, res=res)
+        _, err2 = _check_head(cfg, K, V, ck, cv, out_int2, q, b, hk, "hadamard", None, tb, te)
+        _report(f"c5 b={b} h={hk}", normwise_full=err, normwise_int2_only=err2,
+                K=stats["K"], V=stats["V"])
+        assert err <= ATTN_TOL and err2 <= ATTN_TOL

@@ -150,6 +150,49 @@ def test_quantize_hadamard_ties(cid):
         _report(f"quantize_hadamard c{cid} {which}", **st)
 
 
+@pytest.mark.parametrize("T,toff", [(300, 0), (517, 9), (1, 0), (33, 40)])
+def test_quantize_dense_rotation_ties(T, toff):
+    """Dense per-head rotation (MFMA path): ragged token counts (not a
+    multiple of the 512-token block), t_offset, three heads, two batches."""
+    cfg = W.small_config(W.config(4), B=2, T=T, Hkv=3, Hq=3, t_new=0)
+    R = W.dense_rotations(cfg)
+    for which in ("K", "V"):
+        x = W.kv_tokens(cfg, which)
+        gp, gs, gz = _gpu_quantize(x, "dense", R=R, T_cap=T + toff + 7, t_offset=toff)
+        sl = slice(toff, toff + T)
+        gpu = (gp[:, :, sl], gs[:, :, sl], gz[:, :, sl])
+        for arr in (gp, gs.view(np.uint8), gz.view(np.uint8)):
+            assert np.all(arr[:, :, :toff] == SENTINEL)
+            assert np.all(arr[:, :, toff + T:] == SENTINEL)
+        ora = _oracle_quantize(x, "dense", R)
+        xr = x.permute(0, 2, 1, 3).contiguous().numpy()
+        # per-head rotation: compare head by head
+        for h in range(cfg.Hkv):
+            st = compare_codes_at_ties(xr[:, h], R[h], tuple(a[:, h] for a in gpu),
+                                       tuple(a[:, h] for a in ora))
+        _report(f"quantize_dense T={T} {which}", **st)
+
+
+def test_quantize_dense_config4_slice():
+    """Config 4 shapes on the prefill slice (32768 new tokens of one
+    sequence, all 8 heads)."""
+    cfg = W.config(4)
+    R = W.dense_rotations(cfg)
+    t0, t1 = cfg.quant_range
+    x = W.kv_tokens(cfg, "K", b0=0, b1=1, t0=t0, t1=t1)
+    gpu = _gpu_quantize(x, "dense", R=R)
+    ora = _oracle_quantize(x, "dense", R)
+    xr = x.permute(0, 2, 1, 3).contiguous().numpy()
+    tot = dict(elements=0, code_mismatch=0, group_scale_zero_diff=0)
+    for h in range(cfg.Hkv):
+        st = compare_codes_at_ties(xr[:, h], R[h], tuple(a[:, h] for a in gpu),
+                                   tuple(a[:, h] for a in ora))
+        for k in tot:
+            tot[k] += st[k]
+    assert tot["code_mismatch"] <= 1e-5 * tot["elements"]
+    _report("quantize_dense c4 slice", **tot)
+
+
 def test_quantize_both_sides_one_call():
     cfg = W.small_config(W.config(2), T=300, Hkv=4, Hq=4)
     K = W.kv_tokens(cfg, "K").to(DEV)
@@ -250,6 +293,26 @@ def test_decode_fp16_tokens_only():
 
 
 # ---------------------------------------------------------- end to end
+def test_end_to_end_dense_gqa():
+    """Dense rotation, GQA group 4: GPU quantize (MFMA) -> GPU decode, against
+    the oracle decode on the GPU's own codes."""
+    cfg = W.small_config(W.config(4), B=2, T=1500, Hkv=2, Hq=8, t_new=0)
+    R = W.dense_rotations(cfg)
+    Rg = torch.as_tensor(R, device=DEV).contiguous()
+    K = W.kv_tokens(cfg, "K").to(DEV)
+    V = W.kv_tokens(cfg, "V").to(DEV)
+    ck, cv = empty_cache(cfg.B, cfg.Hkv, cfg.T), empty_cache(cfg.B, cfg.Hkv, cfg.T)
+    kvq.kvq_quantize(K, V, ck, cv, rot="dense", R=Rg)
+    q = W.queries(cfg).to(DEV)
+    out = kvq.kvq_decode_attention(q, ck, cv, 0, cfg.T, rot="dense", R=Rg)
+    torch.cuda.synchronize()
+    gk, gv = cache_to_numpy(ck), cache_to_numpy(cv)
+    ref = O.decode_attention(q.cpu().numpy(), gk, gv, 0, cfg.T, R)
+    err = normwise_rel_err(out.float().cpu().numpy(), ref)
+    _report("end_to_end dense G=4", normwise=err)
+    assert err <= ATTN_TOL
+
+
 @pytest.mark.parametrize("cid", [1, 2])
 def test_end_to_end_gpu_codes(cid):
     """GPU quantize -> GPU decode, against the oracle decode on the GPU's own
