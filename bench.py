@@ -181,9 +181,9 @@ def main():
     csrc = os.path.join(ROOT, "int2_rotated_kv_amd", "csrc")
     roof_q = {"bound": "hbm", "achieved": round(q_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
               "frac": round(q_gbs / PEAK_HBM_GBS, 4),
-              "traffic": traffic_from_profile("kv_rotate_quant_rows",
+              "traffic": traffic_from_profile("kv_rotate_quant_fwht_f16",
                                               os.path.join(csrc, "kv_rotate_quant.hip"), B * T * H),
-              "kernel": "kv_rotate_quant_rows", "algorithmic_bytes_per_launch": q_bytes,
+              "kernel": "kv_rotate_quant_fwht_f16", "algorithmic_bytes_per_launch": q_bytes,
               "bytes_per_unit": QUANT_BYTES_PER_TOKEN_HEAD, "unit_of_work": "(token, kv head)",
               "units_per_launch": B * T * H, "avg_ms": round(q_ms, 4)}
     roof_d = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
