@@ -37,11 +37,22 @@ constexpr uint32_t magic_pack_bias() {
 }
 constexpr uint32_t kPackBias = magic_pack_bias();
 
-// (x << s) + acc in one instruction (v_lshl_add_u32).
-__device__ __forceinline__ uint32_t shl_add(uint32_t x, uint32_t sh, uint32_t acc) {
+// (x << SH) + acc in one instruction (v_lshl_add_u32, SH an inline constant).
+template <int SH>
+__device__ __forceinline__ uint32_t shl_add(uint32_t x, uint32_t acc) {
   uint32_t r;
-  asm("v_lshl_add_u32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(sh), "v"(acc));
+  asm("v_lshl_add_u32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "I"(SH), "v"(acc));
   return r;
+}
+
+// Pack 16 magic-biased code words: sum_i f(i) << 2i (mod 2^32).
+template <typename F, int I = 0>
+__device__ __forceinline__ uint32_t pack16(F &&f, uint32_t acc) {
+  if constexpr (I == 16) {
+    return acc;
+  } else {
+    return pack16<F, I + 1>(static_cast<F &&>(f), shl_add<2 * I>(f(I), acc));
+  }
 }
 
 __device__ __forceinline__ uint32_t code_bits(float u) {
@@ -86,12 +97,8 @@ __device__ __forceinline__ void quantize_group32_exact(const float (&v)[32], uin
   scale_zero(mn, mx, sbits, zbits, sf, zf);
   const bool degenerate = (sf == 0.0f);
   const float inv = 1.0f / (degenerate ? 1.0f : sf);
-  uint32_t a = 0, b = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    a = shl_add(code_bits((v[i] - zf) * inv), 2 * i, a);
-    b = shl_add(code_bits((v[16 + i] - zf) * inv), 2 * i, b);
-  }
+  const uint32_t a = pack16([&](int i) { return code_bits((v[i] - zf) * inv); }, 0u);
+  const uint32_t b = pack16([&](int i) { return code_bits((v[16 + i] - zf) * inv); }, 0u);
   w0 = degenerate ? 0u : a - kPackBias;
   w1 = degenerate ? 0u : b - kPackBias;
 }
@@ -114,14 +121,12 @@ __device__ __forceinline__ void quantize_group32_fwht(const float (&z)[32], uint
   const bool degenerate = (sf == 0.0f);
   const float inv = 1.0f / (degenerate ? 1.0f : sf);
   const float top = 3.0f * sf;                      // exact: sf has 11 significant bits
-  uint32_t a = 0, b = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float da = __builtin_amdgcn_fmed3f(__builtin_fmaf(z[i], c, -zf), 0.0f, top);
-    const float db = __builtin_amdgcn_fmed3f(__builtin_fmaf(z[16 + i], c, -zf), 0.0f, top);
-    a = shl_add(float_as_bits(__builtin_fmaf(da, inv, kRoundMagic)), 2 * i, a);
-    b = shl_add(float_as_bits(__builtin_fmaf(db, inv, kRoundMagic)), 2 * i, b);
-  }
+  auto code = [&](float zz) {
+    const float d = __builtin_amdgcn_fmed3f(__builtin_fmaf(zz, c, -zf), 0.0f, top);
+    return float_as_bits(__builtin_fmaf(d, inv, kRoundMagic));
+  };
+  const uint32_t a = pack16([&](int i) { return code(z[i]); }, 0u);
+  const uint32_t b = pack16([&](int i) { return code(z[16 + i]); }, 0u);
   w0 = degenerate ? 0u : a - kPackBias;
   w1 = degenerate ? 0u : b - kPackBias;
 }
