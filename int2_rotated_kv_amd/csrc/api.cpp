@@ -82,7 +82,8 @@ kvq_status kvq_quantize(const void *K, const void *V, kvq_dtype in_dtype, int64_
     q.zeros = cs[s]->zeros;
     q.T_cap = cs[s]->T_cap;
   }
-  if (B * a.n_sides > 65535 || Hkv > 65535 || (T_new + 63) / 64 > 0x7FFFFFFF) return KVQ_ERR_UNSUPPORTED;
+  if (B * a.n_sides > 65535 || Hkv > 65535 || (T_new + 63) / 64 * Hkv > 0x7FFFFFFF)
+    return KVQ_ERR_UNSUPPORTED;
   if (B == 0 || T_new == 0) return KVQ_OK;
 
   a.in_f32 = in_dtype == KVQ_F32;
