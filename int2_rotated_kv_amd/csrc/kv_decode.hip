@@ -12,9 +12,12 @@
 //                        by softmax_scale*log2(e), turned into a per-group
 //                        19-bit fixed-point vector split into five signed
 //                        4-bit limbs.
-//   2. kv_int2_decode_attn  one wave per (b, kv head, token split): flash-
-//                        decoding over its tokens with an online softmax; every
-//                        loaded K/V row serves all G query heads of the group.
+//   2. kv_int2_decode_attn  one wave per (b, query head, split): flash-
+//                        decoding over every S-th 64-token tile of the head with
+//                        an online softmax.  The G query heads of a KV group are
+//                        sibling waves of one workgroup that stream the same
+//                        tiles together, so HBM serves each tile once and the
+//                        copies for the other heads come from the cache.
 //   3. kv_combine_unrotate  per (b, query head): log-sum-exp merge of the wave
 //                        partials staged through LDS, un-rotation by R^T
 //                        (linear, so applied once after the merge), fp16
@@ -104,16 +107,21 @@ __global__ __launch_bounds__(128) void kv_prep_query(PrepArgs a) {
   else if (a.rot == 2) x = block_matvec128(x, a.R + (int64_t)hkv * kD * kD, false, buf);
   x *= a.qscale;
 
-  // per-group (32 lanes) maximum magnitude -> exponent of the fixed point
+  // maximum magnitude over the head -> exponent of the fixed point (one step
+  // for all four groups, so the step can be applied once per token score)
+  __shared__ float wmax[2];
   float amax = fabsf(x);
 #pragma unroll
-  for (int m = 1; m < 32; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 32));
+  for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+  if ((c & 63) == 0) wmax[c >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(wmax[0], wmax[1]);
   int e = 0;
   (void)frexpf(amax, &e);                    // amax < 2^e
-  const bool zero_group = !(amax > 0.0f);
+  const bool zero_head = !(amax > 0.0f);
   const int E = 18 - e;                      // |x| * 2^E < 2^18
-  const int qi = zero_group ? 0 : (int)__builtin_rintf(ldexpf(x, E));
-  const float step = zero_group ? 0.0f : ldexpf(1.0f, -E);
+  const int qi = zero_head ? 0 : (int)__builtin_rintf(ldexpf(x, E));
+  const float step = zero_head ? 0.0f : ldexpf(1.0f, -E);
   int isum = qi;
 #pragma unroll
   for (int m = 1; m < 32; m <<= 1) isum += __shfl_xor(isum, m, 32);
@@ -150,6 +158,7 @@ __global__ __launch_bounds__(128) void kv_prep_query(PrepArgs a) {
     float *fb = reinterpret_cast<float *>(base);
     fb[24] = (float)isum * step;             // sum of the group's fixed-point q
     fb[25] = step;
+    fb[26] = (float)isum;                    // the same sum in steps (exact: |isum| < 2^23)
   }
 }
 
@@ -160,9 +169,9 @@ struct AttnArgs {
   const uint8_t *kcodes; const uint16_t *kscales; const uint16_t *kzeros; int64_t kT_cap;
   const uint8_t *vcodes; const uint16_t *vscales; const uint16_t *vzeros; int64_t vT_cap;
   int64_t t_begin, n_int2;
-  int64_t n_splits, tps;
-  int64_t total_waves;
-  int Hkv, Hq, G, g0;   // heads [g0, g0 + GC) of each group
+  int64_t n_splits;
+  int64_t total_waves;  // B * Hq * n_splits
+  int Hkv, Hq, G;
   const uint32_t *qprep;
   float *partials;
 };
@@ -189,14 +198,40 @@ struct AttnState {
   float m[GC], l[GC], zacc[GC][2], wsum[GC][2], acc[GC][64];
 };
 
+// Lazy rescaling: the running reference m is moved only when a score
+// exceeds it by more than kSlack (log2 units), so p = 2^(s - m) stays below
+// 2^kSlack and w = p * s_v stays far inside the fp16 range.  The partial
+// (m, l, o') is exact for any reference m, so the merge is unchanged.
+constexpr float kSlack = 4.0f;
+
 constexpr uint32_t kHalf2Ones = 0x3C003C00u;   // (1.0, 1.0) in fp16
 
 // Per-lane query data for the lane's two channel groups of GC heads.
 template <int GC>
 struct QueryLimbs {
   uint32_t limb[GC][2][20];   // [head][group in half][L*4 + w*2 + parity]
-  float qsum[GC][2], qstep[GC][2];
+  float isum[GC][2];          // group sums of the fixed-point query, in steps
+  float qstep[GC];            // fixed-point step of the head (log2 units)
 };
+
+// Sum / max over the two 16-lane rows of each 32-lane half (xor 16) and over
+// the two halves (xor 32) with the gfx950 lane-swap instructions.
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(float_as_bits(v), float_as_bits(v), false, false);
+  return bits_as_float(r[0]) + bits_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(float_as_bits(v), float_as_bits(v), false, false);
+  return bits_as_float(r[0]) + bits_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(float_as_bits(v), float_as_bits(v), false, false);
+  return fmaxf(bits_as_float(r[0]), bits_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(float_as_bits(v), float_as_bits(v), false, false);
+  return fmaxf(bits_as_float(r[0]), bits_as_float(r[1]));
+}
 
 __device__ __forceinline__ float lo_half(uint32_t w) { return half_bits_to_float((uint16_t)(w & 0xFFFFu)); }
 __device__ __forceinline__ float hi_half(uint32_t w) { return half_bits_to_float((uint16_t)(w >> 16)); }
@@ -221,34 +256,36 @@ __device__ __forceinline__ void attn_tile(AttnState<GC> &st, const QueryLimbs<GC
                                           const TileRegs &r, bool va, bool vb) {
   const uint32_t kAw[4] = {r.kA.x, r.kA.y, r.kA.z, r.kA.w};
   const uint32_t kBw[4] = {r.kB.x, r.kB.y, r.kB.z, r.kB.w};
+  const half2_t ksA = __builtin_bit_cast(half2_t, r.ksA), kzA = __builtin_bit_cast(half2_t, r.kzA);
+  const half2_t ksB = __builtin_bit_cast(half2_t, r.ksB), kzB = __builtin_bit_cast(half2_t, r.kzB);
+  const half2_t vsA = __builtin_bit_cast(half2_t, r.vsA), vzA = __builtin_bit_cast(half2_t, r.vzA);
+  const half2_t vsB = __builtin_bit_cast(half2_t, r.vsB), vzB = __builtin_bit_cast(half2_t, r.vzB);
   half2_t wp[GC][2];
 #pragma unroll
   for (int g = 0; g < GC; ++g) {
-    float sa = 0.0f, sb = 0.0f;
+    // score in units of the query step: sum_j s_j * dot_j + z_j * isum_j
+    float ra = 0.0f, rb = 0.0f;
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
       const int ia = group_dot(q.limb[g][gi], kAw[2 * gi], kAw[2 * gi + 1]);
       const int ib = group_dot(q.limb[g][gi], kBw[2 * gi], kBw[2 * gi + 1]);
-      const float skA = gi ? hi_half(r.ksA) : lo_half(r.ksA);
-      const float zkA = gi ? hi_half(r.kzA) : lo_half(r.kzA);
-      const float skB = gi ? hi_half(r.ksB) : lo_half(r.ksB);
-      const float zkB = gi ? hi_half(r.kzB) : lo_half(r.kzB);
-      sa += __builtin_fmaf((float)ia, skA * q.qstep[g][gi], zkA * q.qsum[g][gi]);
-      sb += __builtin_fmaf((float)ib, skB * q.qstep[g][gi], zkB * q.qsum[g][gi]);
+      ra = __builtin_fmaf((float)ia, (float)ksA[gi], __builtin_fmaf((float)kzA[gi], q.isum[g][gi], ra));
+      rb = __builtin_fmaf((float)ib, (float)ksB[gi], __builtin_fmaf((float)kzB[gi], q.isum[g][gi], rb));
     }
-    sa += quad_swap<kQuadXor1>(sa);          // the other half of the row
-    sb += quad_swap<kQuadXor1>(sb);
-    sa = va ? sa : kNegInf;
-    sb = vb ? sb : kNegInf;
-
-    // online softmax (log2 domain); the tile max is wave-uniform
-    float mx = fmaxf(sa, sb);
-    mx = fmaxf(mx, row_ror<2>(mx));
-    mx = fmaxf(mx, row_ror<4>(mx));
-    mx = fmaxf(mx, row_ror<8>(mx));
-    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    if (mx > st.m[g]) {
+    ra += quad_swap<kQuadXor1>(ra);          // the other half of the row
+    rb += quad_swap<kQuadXor1>(rb);
+    // log2-domain score minus the running reference
+    float xa = va ? __builtin_fmaf(q.qstep[g], ra, -st.m[g]) : kNegInf;
+    float xb = vb ? __builtin_fmaf(q.qstep[g], rb, -st.m[g]) : kNegInf;
+    if (__builtin_amdgcn_ballot_w64(fmaxf(xa, xb) > kSlack)) {     // wave-uniform
+      const float ya = va ? q.qstep[g] * ra : kNegInf;
+      const float yb = vb ? q.qstep[g] * rb : kNegInf;
+      float mx = fmaxf(ya, yb);
+      mx = fmaxf(mx, row_ror<2>(mx));
+      mx = fmaxf(mx, row_ror<4>(mx));
+      mx = fmaxf(mx, row_ror<8>(mx));
+      mx = max_xor16(mx);
+      mx = max_xor32(mx);                    // > m: some score passed m + kSlack
       const float alpha = __builtin_amdgcn_exp2f(st.m[g] - mx);
       st.l[g] *= alpha;
       st.zacc[g][0] *= alpha;
@@ -258,18 +295,18 @@ __device__ __forceinline__ void attn_tile(AttnState<GC> &st, const QueryLimbs<GC
 #pragma unroll
       for (int i = 0; i < 64; ++i) st.acc[g][i] *= alpha;
       st.m[g] = mx;
+      xa = ya - mx;
+      xb = yb - mx;
     }
-    const float pA = __builtin_amdgcn_exp2f(sa - st.m[g]);   // 0 for masked tokens
-    const float pB = __builtin_amdgcn_exp2f(sb - st.m[g]);
+    const float pA = __builtin_amdgcn_exp2f(xa);   // 0 for masked tokens
+    const float pB = __builtin_amdgcn_exp2f(xb);
     st.l[g] += pA + pB;
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
-      const float svA = gi ? hi_half(r.vsA) : lo_half(r.vsA);
-      const float zvA = gi ? hi_half(r.vzA) : lo_half(r.vzA);
-      const float svB = gi ? hi_half(r.vsB) : lo_half(r.vsB);
-      const float zvB = gi ? hi_half(r.vzB) : lo_half(r.vzB);
-      st.zacc[g][gi] = __builtin_fmaf(pA, __builtin_fmaf(1.5f, svA, zvA),
-                                      __builtin_fmaf(pB, __builtin_fmaf(1.5f, svB, zvB), st.zacc[g][gi]));
+      const float svA = (float)vsA[gi], svB = (float)vsB[gi];
+      st.zacc[g][gi] = __builtin_fmaf(pA, __builtin_fmaf(1.5f, svA, (float)vzA[gi]),
+                                      __builtin_fmaf(pB, __builtin_fmaf(1.5f, svB, (float)vzB[gi]),
+                                                     st.zacc[g][gi]));
       wp[g][gi].x = (_Float16)(pA * svA);
       wp[g][gi].y = (_Float16)(pB * svB);
       st.wsum[g][gi] = __builtin_amdgcn_fdot2(wp[g][gi], __builtin_bit_cast(half2_t, kHalf2Ones),
@@ -303,33 +340,43 @@ __device__ __forceinline__ void attn_tile(AttnState<GC> &st, const QueryLimbs<GC
   }
 }
 
-template <int GC>
-__global__ __launch_bounds__(256) void kv_int2_decode_attn(AttnArgs a) {
+// WPB waves per workgroup; wave index gw = ((b*Hkv + hkv)*S + split)*G + g,
+// so the G heads of a group (same tiles) are neighbours in one workgroup.
+template <int WPB>
+__global__ __launch_bounds__(64 * WPB) void kv_int2_decode_attn(AttnArgs a) {
+  constexpr int GC = 1;
   const int lane = threadIdx.x & 63;
   // wave index made explicitly uniform so every per-wave quantity is scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t gw = (int64_t)blockIdx.x * WPB + wave;
   if (gw >= a.total_waves) return;           // whole wave leaves together
-  const int64_t split = gw % a.n_splits;
-  const int64_t bh = gw / a.n_splits;        // b*Hkv + hkv
+  const int gq = (int)(gw % a.G);
+  const int64_t gs = gw / a.G;
+  const int64_t split = gs % a.n_splits;
+  const int64_t bh = gs / a.n_splits;        // b*Hkv + hkv
   const int hkv = (int)(bh % a.Hkv);
   const int64_t b = bh / a.Hkv;
   const int ts = lane >> 1;                  // token slot 0..31
   const int h = lane & 1;                    // channel half: groups 2h, 2h+1
-  const int64_t s0 = split * a.tps;
-  const int64_t s1 = (s0 + a.tps < a.n_int2) ? s0 + a.tps : a.n_int2;
+  // The head's INT2 tokens are cut into 64-token tiles; wave `split` takes
+  // tiles split, split + S, split + 2S, ... (S waves per head), so the waves
+  // of a head stream through adjacent tiles together rather than each
+  // through a region of its own.
+  const int64_t S = a.n_splits;
+  const int64_t n_full_tiles = a.n_int2 >> 6;
+  const int64_t mine = split < n_full_tiles ? (n_full_tiles - 1 - split) / S + 1 : 0;
 
   QueryLimbs<GC> q;
 #pragma unroll
   for (int g = 0; g < GC; ++g) {
-    const int hq = hkv * a.G + a.g0 + g;
+    const int hq = hkv * a.G + gq + g;
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
       const uint32_t *p = a.qprep + (b * a.Hq + hq) * kQprepDwordsPerHead + (2 * h + gi) * 32;
 #pragma unroll
       for (int i = 0; i < 20; ++i) q.limb[g][gi][i] = p[i];
-      q.qsum[g][gi] = bits_as_float(p[24]);
-      q.qstep[g][gi] = bits_as_float(p[25]);
+      q.isum[g][gi] = bits_as_float(p[26]);
+      if (gi == 0) q.qstep[g] = bits_as_float(p[25]);   // the same for every group
     }
   }
 
@@ -342,16 +389,14 @@ __global__ __launch_bounds__(256) void kv_int2_decode_attn(AttnArgs a) {
     for (int i = 0; i < 64; ++i) st.acc[g][i] = 0.0f;
   }
 
-  // Row r of the split: codes at *c + r*32 bytes, scales/zeros at *s + r*4
-  // halves.  Lane offsets are 32-bit; tile bases are wave-uniform.
-  const int64_t krow0 = bh * a.kT_cap + a.t_begin + s0;
-  const int64_t vrow0 = bh * a.vT_cap + a.t_begin + s0;
+  // Row r of the head's INT2 range: codes at *c + r*32 bytes, scales/zeros
+  // at *s + r*4 halves.  Lane offsets are 32-bit; tile bases are wave-uniform.
+  const int64_t krow0 = bh * a.kT_cap + a.t_begin;
+  const int64_t vrow0 = bh * a.vT_cap + a.t_begin;
   const uint8_t *kc = a.kcodes + krow0 * kCodeBytes;
   const uint8_t *vc = a.vcodes + vrow0 * kCodeBytes;
   const uint16_t *ks = a.kscales + krow0 * kNGroups, *kz = a.kzeros + krow0 * kNGroups;
   const uint16_t *vs = a.vscales + vrow0 * kNGroups, *vz = a.vzeros + vrow0 * kNGroups;
-  const int64_t n = s1 - s0;
-  const int64_t nfull = n & ~(int64_t)63;
 
   // Loads of one lane: codes at tile base + oc (+1 KB for token B), scales
   // and zeros at tile base + os halves (+64 halves for token B).  Tile bases
@@ -378,26 +423,29 @@ __global__ __launch_bounds__(256) void kv_int2_decode_attn(AttnArgs a) {
     return r;
   };
 
-  // Full tiles, software-pipelined two deep: while tile i is computed the
-  // loads of tile i+1 are in flight.  A prefetch past the last full tile is
-  // clamped to it (a re-read of valid rows, result unused).
-  const int64_t ntiles = nfull >> 6;
-  if (ntiles > 0) {
-    const int64_t last = ntiles - 1;
-    TileRegs r0 = load_tile(0), r1;
+  // This wave's full tiles, software-pipelined three deep: while tile i is
+  // computed the loads of tiles i+1 and i+2 are in flight.  A prefetch past
+  // the wave's last tile is clamped to it (a re-read of valid rows, unused).
+  if (mine > 0) {
+    auto at = [&](int64_t i) { return 64 * (split + (i < mine - 1 ? i : mine - 1) * S); };
+    TileRegs r0 = load_tile(at(0)), r1 = load_tile(at(1)), r2;
     int64_t i = 0;
-    for (; i + 2 <= ntiles; i += 2) {
-      r1 = load_tile(64 * (i + 1));
+    for (; i + 3 <= mine; i += 3) {
+      r2 = load_tile(at(i + 2));
       attn_tile<GC>(st, q, r0, true, true);
-      r0 = load_tile(64 * (i + 2 < last ? i + 2 : last));
+      r0 = load_tile(at(i + 3));
       attn_tile<GC>(st, q, r1, true, true);
+      r1 = load_tile(at(i + 4));
+      attn_tile<GC>(st, q, r2, true, true);
     }
-    if (i < ntiles) attn_tile<GC>(st, q, r0, true, true);
+    if (i < mine) attn_tile<GC>(st, q, r0, true, true);
+    if (i + 1 < mine) attn_tile<GC>(st, q, r1, true, true);
   }
-  if (nfull < n) {                          // tail tile: clamp rows into the split
-    const int64_t ta = nfull + ts, tb = nfull + 32 + ts;
-    const bool va = ta < n, vb = tb < n;
-    const int64_t ra = va ? ta : 0, rb = vb ? tb : 0;
+  const int64_t rem = a.n_int2 & 63;
+  if (rem != 0 && n_full_tiles % S == split) {   // the partial last tile: clamp rows into it
+    const int64_t t0 = 64 * n_full_tiles;
+    const bool va = ts < rem, vb = 32 + ts < rem;
+    const int64_t ra = t0 + (va ? ts : 0), rb = t0 + (vb ? 32 + ts : 0);
     TileRegs r;
     r.kA = *reinterpret_cast<const u32x4_t *>(kc + ra * kCodeBytes + 16 * h);
     r.kB = *reinterpret_cast<const u32x4_t *>(kc + rb * kCodeBytes + 16 * h);
@@ -420,16 +468,21 @@ __global__ __launch_bounds__(256) void kv_int2_decode_attn(AttnArgs a) {
     float l = st.l[g];
     float z0 = __builtin_fmaf(-1.5f, st.wsum[g][0], st.zacc[g][0]);
     float z1 = __builtin_fmaf(-1.5f, st.wsum[g][1], st.zacc[g][1]);
+    // sum over the 32 token slots sharing h: lane bits 1..3 inside the row
+    // (DPP), then the rows (xor 16, xor 32)
+    auto reduce = [](float v) {
+      v += quad_swap<kQuadXor2>(v);
+      v += row_ror<4>(v);
+      v += row_ror<8>(v);
+      return sum_xor32(sum_xor16(v));
+    };
+    l = reduce(l);
+    z0 = reduce(z0);
+    z1 = reduce(z1);
 #pragma unroll
-    for (int msk = 2; msk < 64; msk <<= 1) {
-      l += shfl_xor_f(l, msk);
-      z0 += shfl_xor_f(z0, msk);
-      z1 += shfl_xor_f(z1, msk);
-#pragma unroll
-      for (int i = 0; i < 64; ++i) st.acc[g][i] += shfl_xor_f(st.acc[g][i], msk);
-    }
+    for (int i = 0; i < 64; ++i) st.acc[g][i] = reduce(st.acc[g][i]);
     if (ts == 0) {
-      const int hq = hkv * a.G + a.g0 + g;
+      const int hq = hkv * a.G + gq + g;
       float *dst = a.partials + ((b * a.Hq + hq) * a.n_splits + split) * kPartialStride;
 #pragma unroll
       for (int i = 0; i < 64; ++i) {
@@ -439,203 +492,6 @@ __global__ __launch_bounds__(256) void kv_int2_decode_attn(AttnArgs a) {
       if (h == 0) {
         dst[128] = st.m[g];
         dst[129] = l;
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// GQA variant: lane (ts, j) = (l/4, l%4) handles tokens ts and 16 + ts of a
-// 32-token tile on channel group j for GC query heads at once, so each
-// loaded K/V code serves GC heads.  Registers allow GC = 2 with a three-deep
-// load pipeline.
-// ---------------------------------------------------------------------------
-struct QuadTileRegs {
-  uint2 kA, kB, vA, vB;
-  uint16_t h[8];   // kscale A, kzero A, kscale B, kzero B, vscale A, vzero A, vscale B, vzero B
-};
-
-template <int GC>
-struct QuadState {
-  float m[GC], l[GC], zacc[GC], wsum[GC], acc[GC][32];
-};
-
-template <int GC>
-struct QuadQuery {
-  uint32_t limb[GC][20];
-  float qsum[GC], qstep[GC];
-};
-
-template <int GC>
-__device__ __forceinline__ void quad_tile(QuadState<GC> &st, const QuadQuery<GC> &q,
-                                          const QuadTileRegs &r, bool va, bool vb) {
-  const float skA = half_bits_to_float(r.h[0]), zkA = half_bits_to_float(r.h[1]);
-  const float skB = half_bits_to_float(r.h[2]), zkB = half_bits_to_float(r.h[3]);
-  const float svA = half_bits_to_float(r.h[4]), zvA = half_bits_to_float(r.h[5]);
-  const float svB = half_bits_to_float(r.h[6]), zvB = half_bits_to_float(r.h[7]);
-  half2_t wp[GC];
-#pragma unroll
-  for (int g = 0; g < GC; ++g) {
-    const int ia = group_dot(q.limb[g], r.kA.x, r.kA.y);
-    const int ib = group_dot(q.limb[g], r.kB.x, r.kB.y);
-    float sa = __builtin_fmaf((float)ia, skA * q.qstep[g], zkA * q.qsum[g]);
-    float sb = __builtin_fmaf((float)ib, skB * q.qstep[g], zkB * q.qsum[g]);
-    sa += quad_swap<kQuadXor1>(sa);
-    sb += quad_swap<kQuadXor1>(sb);
-    sa += quad_swap<kQuadXor2>(sa);
-    sb += quad_swap<kQuadXor2>(sb);
-    sa = va ? sa : kNegInf;
-    sb = vb ? sb : kNegInf;
-    float mx = fmaxf(sa, sb);
-    mx = fmaxf(mx, row_ror<4>(mx));
-    mx = fmaxf(mx, row_ror<8>(mx));
-    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    if (mx > st.m[g]) {
-      const float alpha = __builtin_amdgcn_exp2f(st.m[g] - mx);
-      st.l[g] *= alpha;
-      st.zacc[g] *= alpha;
-      st.wsum[g] *= alpha;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) st.acc[g][i] *= alpha;
-      st.m[g] = mx;
-    }
-    const float pA = __builtin_amdgcn_exp2f(sa - st.m[g]);
-    const float pB = __builtin_amdgcn_exp2f(sb - st.m[g]);
-    st.l[g] += pA + pB;
-    st.zacc[g] = __builtin_fmaf(pA, __builtin_fmaf(1.5f, svA, zvA),
-                                __builtin_fmaf(pB, __builtin_fmaf(1.5f, svB, zvB), st.zacc[g]));
-    wp[g].x = (_Float16)(pA * svA);
-    wp[g].y = (_Float16)(pB * svB);
-    st.wsum[g] = __builtin_amdgcn_fdot2(wp[g], __builtin_bit_cast(half2_t, kHalf2Ones), st.wsum[g], false);
-  }
-#pragma unroll
-  for (int w = 0; w < 2; ++w) {
-    const uint32_t a32 = w ? r.vA.y : r.vA.x;
-    const uint32_t b32 = w ? r.vB.y : r.vB.x;
-    const uint32_t X = __builtin_amdgcn_perm(b32, a32, 0x05040100u);
-    const uint32_t Y = __builtin_amdgcn_perm(b32, a32, 0x07060302u);
-    const uint32_t X6 = X >> 6, Y6 = Y >> 6;
-#pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      const uint32_t px = x <= 4 ? (X & (0x00030003u << (2 * x))) : (X6 & (0x00030003u << (2 * x - 6)));
-      const uint32_t py = x <= 4 ? (Y & (0x00030003u << (2 * x))) : (Y6 & (0x00030003u << (2 * x - 6)));
-      const half2_t hx = __builtin_bit_cast(half2_t, px);
-      const half2_t hy = __builtin_bit_cast(half2_t, py);
-#pragma unroll
-      for (int g = 0; g < GC; ++g) {
-        st.acc[g][16 * w + x] = __builtin_amdgcn_fdot2(hx, wp[g], st.acc[g][16 * w + x], false);
-        st.acc[g][16 * w + 8 + x] = __builtin_amdgcn_fdot2(hy, wp[g], st.acc[g][16 * w + 8 + x], false);
-      }
-    }
-  }
-}
-
-template <int GC>
-__global__ __launch_bounds__(256) void kv_int2_decode_attn_gqa(AttnArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
-  if (gw >= a.total_waves) return;
-  const int64_t split = gw % a.n_splits;
-  const int64_t bh = gw / a.n_splits;
-  const int hkv = (int)(bh % a.Hkv);
-  const int64_t b = bh / a.Hkv;
-  const int ts = lane >> 2;
-  const int j = lane & 3;
-  const int64_t s0 = split * a.tps;
-  const int64_t s1 = (s0 + a.tps < a.n_int2) ? s0 + a.tps : a.n_int2;
-
-  QuadQuery<GC> q;
-#pragma unroll
-  for (int g = 0; g < GC; ++g) {
-    const int hq = hkv * a.G + a.g0 + g;
-    const uint32_t *p = a.qprep + (b * a.Hq + hq) * kQprepDwordsPerHead + j * 32;
-#pragma unroll
-    for (int i = 0; i < 20; ++i) q.limb[g][i] = p[i];
-    q.qsum[g] = bits_as_float(p[24]);
-    q.qstep[g] = bits_as_float(p[25]);
-  }
-  QuadState<GC> st;
-#pragma unroll
-  for (int g = 0; g < GC; ++g) {
-    st.m[g] = kNegInf; st.l[g] = 0.0f; st.zacc[g] = 0.0f; st.wsum[g] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) st.acc[g][i] = 0.0f;
-  }
-  const int64_t krow0 = bh * a.kT_cap + a.t_begin + s0;
-  const int64_t vrow0 = bh * a.vT_cap + a.t_begin + s0;
-  const uint8_t *kc = a.kcodes + krow0 * kCodeBytes, *vc = a.vcodes + vrow0 * kCodeBytes;
-  const uint16_t *ks = a.kscales + krow0 * kNGroups, *kz = a.kzeros + krow0 * kNGroups;
-  const uint16_t *vs = a.vscales + vrow0 * kNGroups, *vz = a.vzeros + vrow0 * kNGroups;
-  const uint32_t oc = (uint32_t)(ts * kCodeBytes + 8 * j);
-  const uint32_t os = (uint32_t)(ts * kNGroups + j);
-  const int64_t n = s1 - s0;
-  const int64_t nfull = n & ~(int64_t)31;
-  auto load_tile = [&](int64_t first_row) {
-    QuadTileRegs r;
-    const uint8_t *kct = kc + first_row * kCodeBytes, *vct = vc + first_row * kCodeBytes;
-    const uint16_t *kst = ks + first_row * kNGroups, *kzt = kz + first_row * kNGroups;
-    const uint16_t *vst = vs + first_row * kNGroups, *vzt = vz + first_row * kNGroups;
-    r.kA = *reinterpret_cast<const uint2 *>(kct + oc);
-    r.kB = *reinterpret_cast<const uint2 *>(kct + oc + 16 * kCodeBytes);
-    r.vA = *reinterpret_cast<const uint2 *>(vct + oc);
-    r.vB = *reinterpret_cast<const uint2 *>(vct + oc + 16 * kCodeBytes);
-    r.h[0] = kst[os]; r.h[1] = kzt[os];
-    r.h[2] = kst[os + 16 * kNGroups]; r.h[3] = kzt[os + 16 * kNGroups];
-    r.h[4] = vst[os]; r.h[5] = vzt[os];
-    r.h[6] = vst[os + 16 * kNGroups]; r.h[7] = vzt[os + 16 * kNGroups];
-    return r;
-  };
-  const int64_t ntiles = nfull >> 5;
-  if (ntiles > 0) {
-    const int64_t last = ntiles - 1;
-    QuadTileRegs r0 = load_tile(0), r1 = load_tile(32 * (last < 1 ? last : 1)), r2;
-    int64_t i = 0;
-    for (; i + 3 <= ntiles; i += 3) {
-      r2 = load_tile(32 * (i + 2 < last ? i + 2 : last));
-      quad_tile<GC>(st, q, r0, true, true);
-      r0 = load_tile(32 * (i + 3 < last ? i + 3 : last));
-      quad_tile<GC>(st, q, r1, true, true);
-      r1 = load_tile(32 * (i + 4 < last ? i + 4 : last));
-      quad_tile<GC>(st, q, r2, true, true);
-    }
-    if (i < ntiles) quad_tile<GC>(st, q, r0, true, true);
-    if (i + 1 < ntiles) quad_tile<GC>(st, q, r1, true, true);
-  }
-  if (nfull < n) {
-    const int64_t ta = nfull + ts, tb = nfull + 16 + ts;
-    const bool va = ta < n, vb = tb < n;
-    const int64_t ra = va ? ta : 0, rb = vb ? tb : 0;
-    QuadTileRegs r;
-    r.kA = *reinterpret_cast<const uint2 *>(kc + ra * kCodeBytes + 8 * j);
-    r.kB = *reinterpret_cast<const uint2 *>(kc + rb * kCodeBytes + 8 * j);
-    r.vA = *reinterpret_cast<const uint2 *>(vc + ra * kCodeBytes + 8 * j);
-    r.vB = *reinterpret_cast<const uint2 *>(vc + rb * kCodeBytes + 8 * j);
-    r.h[0] = ks[ra * kNGroups + j]; r.h[1] = kz[ra * kNGroups + j];
-    r.h[2] = ks[rb * kNGroups + j]; r.h[3] = kz[rb * kNGroups + j];
-    r.h[4] = vs[ra * kNGroups + j]; r.h[5] = vz[ra * kNGroups + j];
-    r.h[6] = vs[rb * kNGroups + j]; r.h[7] = vz[rb * kNGroups + j];
-    quad_tile<GC>(st, q, r, va, vb);
-  }
-#pragma unroll
-  for (int g = 0; g < GC; ++g) {
-    st.zacc[g] = __builtin_fmaf(-1.5f, st.wsum[g], st.zacc[g]);
-#pragma unroll
-    for (int msk = 4; msk < 64; msk <<= 1) {
-      st.l[g] += shfl_xor_f(st.l[g], msk);
-      st.zacc[g] += shfl_xor_f(st.zacc[g], msk);
-#pragma unroll
-      for (int i = 0; i < 32; ++i) st.acc[g][i] += shfl_xor_f(st.acc[g][i], msk);
-    }
-    if (ts == 0) {
-      const int hq = hkv * a.G + a.g0 + g;
-      float *dst = a.partials + ((b * a.Hq + hq) * a.n_splits + split) * kPartialStride;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) dst[32 * j + i] = __builtin_fmaf(st.acc[g][i], chan_unscale(i & 7), st.zacc[g]);
-      if (j == 0) {
-        dst[128] = st.m[g];
-        dst[129] = st.l[g];
       }
     }
   }
@@ -710,25 +566,59 @@ __global__ __launch_bounds__(128) void kv_combine_unrotate(CombineArgs a) {
   if (a.rot == 1) o = block_fwht128(o, buf);
   else if (a.rot == 2) o = block_matvec128(o, a.R + (int64_t)hkv * kD * kD, true, buf);
 
-  // fp16 tokens in the original basis
+  // fp16 tokens in the original basis.  Scores: a 16-lane row per token,
+  // 8 channels per lane (one 16-byte load), reduced over the row with DPP;
+  // eight tokens per step across the block.
   const int64_t nf = a.n_sink + a.n_res;
   float Mf = kNegInf, Lf = 0.0f, of = 0.0f;
   if (nf > 0) {
-    float qv = a.q_f32 ? reinterpret_cast<const float *>(a.q)[bh * kD + c]
-                       : (float)reinterpret_cast<const _Float16 *>(a.q)[bh * kD + c];
-    buf[c] = qv * a.qscale;
-    __syncthreads();
     const int64_t bkv = b * a.Hkv + hkv;
-    float sl = kNegInf;
-    for (int64_t t = c; t < nf; t += 128) {
-      const uint16_t *row = t < a.n_sink ? a.sink_k + (bkv * a.n_sink + t) * kD
-                                         : a.res_k + (bkv * a.n_res + (t - a.n_sink)) * kD;
-      float s = 0.0f;
-      for (int k = 0; k < kD; ++k) s = __builtin_fmaf(buf[k], half_bits_to_float(row[k]), s);
-      pf[t] = s;
-      sl = fmaxf(sl, s);
+    const int cl = c & 15;                    // channels 8cl .. 8cl+7
+    float q8[8];
+    {
+      const int64_t qoff = bh * kD + 8 * cl;
+      if (a.q_f32) {
+        const float4_t *qp = reinterpret_cast<const float4_t *>(reinterpret_cast<const float *>(a.q) + qoff);
+        const float4_t x0 = qp[0], x1 = qp[1];
+        q8[0] = x0.x; q8[1] = x0.y; q8[2] = x0.z; q8[3] = x0.w;
+        q8[4] = x1.x; q8[5] = x1.y; q8[6] = x1.z; q8[7] = x1.w;
+      } else {
+        const u32x4_t u = *reinterpret_cast<const u32x4_t *>(reinterpret_cast<const _Float16 *>(a.q) + qoff);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const half2_t hq2 = __builtin_bit_cast(half2_t, w[i]);
+          q8[2 * i] = (float)hq2.x;
+          q8[2 * i + 1] = (float)hq2.y;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q8[i] *= a.qscale;
     }
-    Mf = block_max128(sl, red);
+    float sl = kNegInf;
+    for (int64_t t0 = 0; t0 < nf; t0 += 8) {
+      const int64_t t = t0 + (c >> 4);
+      const bool valid = t < nf;
+      const int64_t tt = valid ? t : 0;
+      const uint16_t *row = tt < a.n_sink ? a.sink_k + (bkv * a.n_sink + tt) * kD
+                                          : a.res_k + (bkv * a.n_res + (tt - a.n_sink)) * kD;
+      const u32x4_t u = *reinterpret_cast<const u32x4_t *>(row + 8 * cl);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+      float sacc = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const half2_t k2 = __builtin_bit_cast(half2_t, w[i]);
+        sacc = __builtin_fmaf(q8[2 * i], (float)k2.x, sacc);
+        sacc = __builtin_fmaf(q8[2 * i + 1], (float)k2.y, sacc);
+      }
+      sacc += quad_swap<kQuadXor1>(sacc);
+      sacc += quad_swap<kQuadXor2>(sacc);
+      sacc += row_ror<4>(sacc);
+      sacc += row_ror<8>(sacc);
+      if (valid && cl == 0) pf[t] = sacc;
+      if (valid) sl = fmaxf(sl, sacc);
+    }
+    Mf = block_max128(sl, red);              // its barrier also publishes pf
   }
   const float M = fmaxf(M2, Mf);
   if (nf > 0) {
@@ -741,11 +631,23 @@ __global__ __launch_bounds__(128) void kv_combine_unrotate(CombineArgs a) {
     __syncthreads();
     Lf = block_sum128(ll, red);
     const int64_t bkv = b * a.Hkv + hkv;
-    for (int64_t t = 0; t < nf; ++t) {
-      const uint16_t *row = t < a.n_sink ? a.sink_v + (bkv * a.n_sink + t) * kD
-                                         : a.res_v + (bkv * a.n_res + (t - a.n_sink)) * kD;
-      of = __builtin_fmaf(pf[t], half_bits_to_float(row[c]), of);
+    const uint16_t *vs_rows = a.sink_v + bkv * a.n_sink * kD + c;
+    const uint16_t *vr_rows = a.res_v + bkv * a.n_res * kD + c;
+    float o4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    int64_t t = 0;
+    for (; t + 4 <= nf; t += 4) {             // four independent loads in flight
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t tu = t + u;
+        const uint16_t hv = tu < a.n_sink ? vs_rows[tu * kD] : vr_rows[(tu - a.n_sink) * kD];
+        o4[u] = __builtin_fmaf(pf[tu], half_bits_to_float(hv), o4[u]);
+      }
     }
+    for (; t < nf; ++t) {
+      const uint16_t hv = t < a.n_sink ? vs_rows[t * kD] : vr_rows[(t - a.n_sink) * kD];
+      o4[0] = __builtin_fmaf(pf[t], half_bits_to_float(hv), o4[0]);
+    }
+    of = (o4[0] + o4[1]) + (o4[2] + o4[3]);
   }
   const float wint = (M2 == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(M2 - M);
   const float res = (o * wint + of) / (L2 * wint + Lf);
@@ -756,20 +658,22 @@ __global__ __launch_bounds__(128) void kv_combine_unrotate(CombineArgs a) {
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-SplitPlan plan_splits(int64_t B, int64_t Hkv, int64_t n_int2) {
-  SplitPlan p{0, 0};
-  if (n_int2 <= 0 || B <= 0 || Hkv <= 0) return p;
-  const int64_t pairs = B * Hkv;
-  const int64_t target_waves = 8192;
-  int64_t s = (target_waves + pairs - 1) / pairs;
+// Enough waves to fill the chip once: 256 CUs x 4 SIMDs x 2 resident waves
+// of the attention kernel (its register budget allows two per SIMD).  One
+// round of resident waves, each streaming every S-th tile of its head,
+// measured faster than more, shorter waves.
+constexpr int64_t kTargetWaves = 2048;
+
+SplitPlan plan_splits(int64_t B, int64_t Hq, int64_t n_int2) {
+  SplitPlan p{0};
+  if (n_int2 <= 0 || B <= 0 || Hq <= 0) return p;
+  const int64_t heads = B * Hq;
+  int64_t s = kTargetWaves / heads;              // stay within one round of resident waves
   const int64_t by_len = (n_int2 + 255) / 256;   // at least ~256 tokens per wave
   if (s > by_len) s = by_len;
   if (s > 4096) s = 4096;
   if (s < 1) s = 1;
-  int64_t tps = (n_int2 + s - 1) / s;
-  tps = (tps + 31) / 32 * 32;
-  p.tokens_per_split = tps;
-  p.n_splits = (n_int2 + tps - 1) / tps;
+  p.n_splits = s;
   return p;
 }
 
@@ -789,27 +693,20 @@ hipError_t launch_decode(const DecodeArgs &d, hipStream_t stream) {
     a.kcodes = d.kcodes; a.kscales = d.kscales; a.kzeros = d.kzeros; a.kT_cap = d.kT_cap;
     a.vcodes = d.vcodes; a.vscales = d.vscales; a.vzeros = d.vzeros; a.vT_cap = d.vT_cap;
     a.t_begin = d.t_begin; a.n_int2 = d.n_int2;
-    a.n_splits = d.n_splits; a.tps = d.tokens_per_split;
-    a.total_waves = d.B * d.Hkv * d.n_splits;
+    a.n_splits = d.n_splits;
+    a.total_waves = d.B * d.Hq * d.n_splits;
     a.Hkv = (int)d.Hkv; a.Hq = (int)d.Hq; a.G = G;
     a.qprep = reinterpret_cast<const uint32_t *>(d.qprep);
     a.partials = d.partials;
-    const dim3 grid((unsigned)((a.total_waves + 3) / 4));
-    if (G == 1) {
-      a.g0 = 0;
-      hipLaunchKernelGGL(kv_int2_decode_attn<1>, grid, dim3(256), 0, stream, a);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
+    if (G <= 4) {
+      hipLaunchKernelGGL(kv_int2_decode_attn<4>, dim3((unsigned)((a.total_waves + 3) / 4)), dim3(256), 0,
+                         stream, a);
     } else {
-      const int GC = (G % 2 == 0) ? 2 : 1;
-      for (int g0 = 0; g0 < G; g0 += GC) {
-        a.g0 = g0;
-        if (GC == 2) hipLaunchKernelGGL(kv_int2_decode_attn_gqa<2>, grid, dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL(kv_int2_decode_attn_gqa<1>, grid, dim3(256), 0, stream, a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-      }
+      hipLaunchKernelGGL(kv_int2_decode_attn<8>, dim3((unsigned)((a.total_waves + 7) / 8)), dim3(512), 0,
+                         stream, a);
     }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
   {
     CombineArgs c;

@@ -47,16 +47,14 @@ struct DecodeArgs {
   // workspace carve-up (device pointers)
   int32_t *qprep;       // [B][Hq][128] dwords
   float *partials;      // [B][Hq][n_splits][kPartialStride]
-  int64_t n_splits;     // wave-splits per (b, kv head)
-  int64_t tokens_per_split;
+  int64_t n_splits;     // waves per (b, query head), each taking every n_splits-th tile
 };
 
 // Split plan shared by the workspace query and the attention call.
 struct SplitPlan {
   int64_t n_splits;
-  int64_t tokens_per_split;
 };
-SplitPlan plan_splits(int64_t B, int64_t Hkv, int64_t n_int2);
+SplitPlan plan_splits(int64_t B, int64_t Hq, int64_t n_int2);
 
 constexpr int kQprepDwordsPerHead = 128;
 constexpr int kPartialStride = 132;   // o'[128], m, l, 2 pad (16-byte rows)
