@@ -13,9 +13,12 @@
 // the fp16 inputs and the fp16 x fp16 products are exact.
 //
 // A workgroup owns one (batch, KV head) and a range of 32-token tiles of
-// both sides.  It converts R_h into A-operand fragments in LDS once (64 KiB)
-// and then streams its tiles; each wave loads the next tile's inputs while
-// the current tile's 64 MFMAs and its quantization run.
+// both sides.  Wave w computes quantization group w, so its 16 A fragments
+// (R_h columns 32w .. 32w+31, hi and lo) stay in registers for the whole
+// kernel.  The workgroup stages the inputs of four tiles at a time in LDS
+// with fully coalesced loads (16 lanes per 256-byte row), XOR-swizzled so
+// that the B-operand reads (one token per lane) hit distinct banks; the next
+// four tiles are loaded while the current ones compute.
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
@@ -23,8 +26,10 @@ namespace kvq {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 
-constexpr int kDenseWaves = 4;
-constexpr int64_t kDenseTargetBlocks = 512;   // 256 CUs x 2 workgroups (64 KiB LDS each)
+constexpr int kDenseTiles = 4;                 // 32-token tiles per iteration
+constexpr int kDenseSlots = kDenseTiles * 32 * 16;        // 16-byte input chunks per iteration
+constexpr int kDenseLoadsPerThread = kDenseSlots / 256;
+constexpr int64_t kDenseTargetBlocks = 512;   // 256 CUs x 2 workgroups
 constexpr int64_t kDenseMinItemsPerBlock = 16;
 
 // K-slot (k-step s of 8, lane half h, element i) <-> input channel: lane
@@ -34,10 +39,9 @@ constexpr int64_t kDenseMinItemsPerBlock = 16;
 // contiguous bytes.
 __device__ __forceinline__ constexpr int dense_in_channel(int s, int h, int i) { return 64 * h + 8 * s + i; }
 
-// LDS slot of the A operand (group g, k-step s, hi/lo part, lane): 16 bytes.
-__device__ __forceinline__ constexpr int dense_frag(int g, int s, int part, int lane) {
-  return ((g * 8 + s) * 2 + part) * 64 + lane;
-}
+// LDS slot (16-byte units) of position p of row r of tile u; the slot holds
+// input chunk p ^ (r & 15) of that row (bytes 16c .. 16c+15 for chunk c).
+__device__ __forceinline__ constexpr int dense_slot(int u, int r, int p) { return (u * 32 + r) * 16 + p; }
 
 struct DenseKernelArgs {
   QuantSide side[2];
@@ -118,132 +122,130 @@ __device__ __forceinline__ void dense_group_codes(const float16_t &y, uint32_t &
   w1 = __builtin_amdgcn_perm(o, e, 0x07030602u);   // e2 o2 e3 o3
 }
 
-// grid: x = chunk of items, y = KV head, z = batch; 256 threads, two
-// workgroups per CU (LDS), so at most 256 registers per lane.
+// grid: x = chunk of items, y = KV head, z = batch; 256 threads = four
+// waves, one per quantization group.
 __global__ __launch_bounds__(256, 2) void kv_rotate_quant_dense(DenseKernelArgs a) {
-  __shared__ half8_t frag[4 * 8 * 2 * 64];      // 64 KiB of A fragments
+  __shared__ u32x4_t xs[2][kDenseSlots];      // 2 x 32 KiB of staged inputs
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = __builtin_amdgcn_readfirstlane(tid >> 6);   // this wave's group
   const int h = blockIdx.y;
   const int64_t b = blockIdx.z;
-
-  // Stage R_h^T as fp16 hi / lo A fragments: slot (g, s, lane = (m, kh))
-  // holds R[dense_in_channel(s, kh, i)][32g + m] for i = 0..7.
-  {
-    const float *R = a.R + (int64_t)h * kD * kD;
-    for (int f = tid; f < 4 * 8 * 64; f += 256) {
-      const int ln = f & 63, s = (f >> 6) & 7, g = f >> 9;
-      const int m = ln & 31, kh = ln >> 5;
-      half8_t hi, lo;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float r = R[dense_in_channel(s, kh, i) * kD + 32 * g + m];
-        hi[i] = (_Float16)r;
-        lo[i] = (_Float16)(r - (float)hi[i]);
-      }
-      frag[dense_frag(g, s, 0, ln)] = hi;
-      frag[dense_frag(g, s, 1, ln)] = lo;
-    }
-  }
-  __syncthreads();
-
-  const int j = lane & 31;            // token column of the tile
+  const int j = lane & 31;            // token column of a tile
   const int half = lane >> 5;
-  const int64_t i0 = (int64_t)blockIdx.x * a.items_per_block;
-  const int64_t i1 = (i0 + a.items_per_block < a.n_items) ? i0 + a.items_per_block : a.n_items;
 
-  // this lane's 64 input channels of its token in the tile of item `it`
-  const int side_shift = a.n_sides - 1;                   // n_sides is 1 or 2
-  auto load_item = [&](int64_t it, uint32_t (&xw)[32]) {
-    const int sidx = (int)(it & side_shift);
-    const int64_t t0 = (it >> side_shift) * 32;
-    const QuantSide s = sidx ? a.side[1] : a.side[0];       // by value: scalar selects
-    const int64_t t = (t0 + j < a.T_new) ? t0 + j : a.T_new - 1;
-    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(
-        reinterpret_cast<const _Float16 *>(s.x) + b * a.stride_b + t * a.stride_t +
-        (int64_t)h * a.stride_h + 64 * half);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const u32x4_t u = __builtin_nontemporal_load(src + k);
-      xw[4 * k] = u.x; xw[4 * k + 1] = u.y; xw[4 * k + 2] = u.z; xw[4 * k + 3] = u.w;
-    }
-  };
-
-  // rotate-quantize-store one tile from the lane's inputs xw
-  auto tile = [&](int64_t it, const uint32_t (&xw)[32]) {
-    // four independent accumulators (one per group) keep the matrix pipe
-    // busy; acc[g][r] = y[token j][32g + 8(r/4) + 4*half + r%4].  The eight
-    // A fragments of k-step s+1 are read from LDS while the eight MFMAs of
-    // step s run (scheduling barriers pin that order).
-    float16_t acc[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) acc[g] = float16_t{};
-    half8_t fr[2][8];
-    auto read_frags = [&](int s, half8_t (&f)[8]) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f[2 * g] = frag[dense_frag(g, s, 0, lane)];
-        f[2 * g + 1] = frag[dense_frag(g, s, 1, lane)];
-      }
-    };
-    read_frags(0, fr[0]);
+  // A fragments of group g: rf[s][part] of lane (m = j, kh = half) holds
+  // R[dense_in_channel(s, half, i)][32g + j], i = 0..7, as fp16 hi / lo.
+  half8_t rf[8][2];
+  {
+    const float *R = a.R + (int64_t)h * kD * kD + 32 * g + j;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      if (s + 1 < 8) read_frags(s + 1, fr[(s + 1) & 1]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float r = R[dense_in_channel(s, half, i) * kD];
+        rf[s][0][i] = (_Float16)r;
+        rf[s][1][i] = (_Float16)(r - (float)rf[s][0][i]);
+      }
+    }
+  }
+
+  const int64_t i0 = (int64_t)blockIdx.x * a.items_per_block;
+  const int64_t i1 = (i0 + a.items_per_block < a.n_items) ? i0 + a.items_per_block : a.n_items;
+  const int64_t n_iter = (i1 - i0 + kDenseTiles - 1) / kDenseTiles;
+  const int side_shift = a.n_sides - 1;                   // n_sides is 1 or 2
+
+  // Loads of iteration k: thread tid fetches slots q = c*256 + tid.  Items
+  // past the block's range re-read its last item (results unused).
+  auto load_iter = [&](int64_t k, u32x4_t (&P)[kDenseLoadsPerThread]) {
+#pragma unroll
+    for (int c = 0; c < kDenseLoadsPerThread; ++c) {
+      const int q = c * 256 + tid;
+      const int u = q >> 9, r = (q >> 4) & 31, p = q & 15;
+      int64_t it = i0 + k * kDenseTiles + u;
+      it = it < i1 ? it : i1 - 1;
+      const QuantSide sd = (it & side_shift) ? a.side[1] : a.side[0];
+      const int64_t t0 = (it >> side_shift) * 32;
+      const int64_t t = (t0 + r < a.T_new) ? t0 + r : a.T_new - 1;
+      const u32x4_t *src = reinterpret_cast<const u32x4_t *>(
+          reinterpret_cast<const _Float16 *>(sd.x) + b * a.stride_b + t * a.stride_t +
+          (int64_t)h * a.stride_h) + (p ^ (r & 15));
+      P[c] = __builtin_nontemporal_load(src);
+    }
+  };
+  auto stage = [&](int buf, const u32x4_t (&P)[kDenseLoadsPerThread]) {
+#pragma unroll
+    for (int c = 0; c < kDenseLoadsPerThread; ++c) xs[buf][c * 256 + tid] = P[c];
+  };
+
+  // MFMAs and quantization of the iteration's tiles for group g; stage_next
+  // runs between the quantization and the stores.
+  auto compute = [&](int64_t k, int buf, auto &&stage_next) {
+    float16_t acc[kDenseTiles];
+#pragma unroll
+    for (int u = 0; u < kDenseTiles; ++u) acc[u] = float16_t{};
+    half8_t bx[2][kDenseTiles];
+    auto read_b = [&](int s, half8_t (&dst)[kDenseTiles]) {
+      const int pos = (8 * half + s) ^ (j & 15);
+#pragma unroll
+      for (int u = 0; u < kDenseTiles; ++u) dst[u] = __builtin_bit_cast(half8_t, xs[buf][dense_slot(u, j, pos)]);
+    };
+    read_b(0, bx[0]);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      if (s + 1 < 8) read_b(s + 1, bx[(s + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
-      const half8_t bx = __builtin_bit_cast(
-          half8_t, u32x4_t{xw[4 * s], xw[4 * s + 1], xw[4 * s + 2], xw[4 * s + 3]});
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fr[s & 1][2 * g], bx, acc[g], 0, 0, 0);
+      for (int u = 0; u < kDenseTiles; ++u)
+        acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(rf[s][0], bx[s & 1][u], acc[u], 0, 0, 0);
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fr[s & 1][2 * g + 1], bx, acc[g], 0, 0, 0);
+      for (int u = 0; u < kDenseTiles; ++u)
+        acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(rf[s][1], bx[s & 1][u], acc[u], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    uint32_t w0[4], w1[4];
-    uint16_t sb[4], zb[4];
+    // acc[u][r] = y[token j of tile u][32g + 8(r/4) + 4*half + r%4]
+    uint32_t cw[kDenseTiles];
+    uint16_t sz[kDenseTiles];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) dense_group_codes(acc[g], w0[g], w1[g], sb[g], zb[g]);
-    const int sidx = (int)(it & side_shift);
-    const int64_t t = (it >> side_shift) * 32 + j;
-    const QuantSide s = sidx ? a.side[1] : a.side[0];
-    if (t < a.T_new) {
-      const int64_t row = (b * a.Hkv + h) * s.T_cap + a.t_offset + t;
-      // lane half h stores code bytes [16h, 16h + 16) of the row (groups 2h,
-      // 2h+1): one instruction covers 32 consecutive rows; half 0 stores the
-      // four scales, half 1 the four zeros
-      const u32x4_t cw = half ? u32x4_t{w0[2], w1[2], w0[3], w1[3]} : u32x4_t{w0[0], w1[0], w0[1], w1[1]};
-      __builtin_nontemporal_store(cw, reinterpret_cast<u32x4_t *>(s.codes + row * kCodeBytes) + half);
-      const uint16_t *v4 = half ? zb : sb;
-      const u32x2_t sv = {(uint32_t)v4[0] | ((uint32_t)v4[1] << 16), (uint32_t)v4[2] | ((uint32_t)v4[3] << 16)};
-      uint16_t *dst = half ? s.zeros : s.scales;
-      __builtin_nontemporal_store(sv, reinterpret_cast<u32x2_t *>(dst + row * kNGroups));
+    for (int u = 0; u < kDenseTiles; ++u) {
+      uint32_t w0, w1;
+      uint16_t sb, zb;
+      dense_group_codes(acc[u], w0, w1, sb, zb);
+      cw[u] = half ? w1 : w0;
+      sz[u] = half ? zb : sb;
+    }
+    // The next inputs go to LDS before this iteration's stores are issued:
+    // waits for loads count every earlier memory operation, stores included.
+    stage_next();
+#pragma unroll
+    for (int u = 0; u < kDenseTiles; ++u) {
+      const int64_t it = i0 + k * kDenseTiles + u;
+      if (it >= i1) break;                              // wave-uniform
+      const QuantSide sd = (it & side_shift) ? a.side[1] : a.side[0];
+      const int64_t t = (it >> side_shift) * 32 + j;
+      if (t < a.T_new) {
+        const int64_t row = (b * a.Hkv + h) * sd.T_cap + a.t_offset + t;
+        // half 0 stores group bytes 0..3 and the scale, half 1 bytes 4..7
+        // and the zero; the four waves fill the rest of each row
+        *reinterpret_cast<uint32_t *>(sd.codes + row * kCodeBytes + 8 * g + 4 * half) = cw[u];
+        uint16_t *dst = half ? sd.zeros : sd.scales;
+        dst[row * kNGroups + g] = sz[u];
+      }
     }
   };
 
-  // The wave's items are it0, it0 + 4, it0 + 8, ... < i1.  The next tile's
-  // inputs are loaded while the current one computes (two register buffers
-  // used in turn); a prefetch past the block's items re-reads its last item
-  // (unused), which keeps every path's load count the same.
-  constexpr int64_t W = kDenseWaves;
-  int64_t it = i0 + wave;
-  if (it >= i1) return;               // wave-uniform; no barrier follows
-  auto clampi = [&](int64_t i) { return i < i1 ? i : i1 - 1; };
-  uint32_t xa[32], xb[32];
-  load_item(it, xa);
-  for (;;) {
-    load_item(clampi(it + W), xb);
-    __builtin_amdgcn_sched_barrier(0);    // keep the prefetch ahead of the tile's work
-    tile(it, xa);
-    it += W;
-    if (it >= i1) break;
-    load_item(clampi(it + W), xa);
+  u32x4_t P[kDenseLoadsPerThread];
+  load_iter(0, P);
+  stage(0, P);
+  __syncthreads();
+  for (int64_t k = 0; k < n_iter; ++k) {              // block-uniform trip count
+    const bool more = k + 1 < n_iter;
+    if (more) load_iter(k + 1, P);
     __builtin_amdgcn_sched_barrier(0);
-    tile(it, xb);
-    it += W;
-    if (it >= i1) break;
+    compute(k, (int)(k & 1), [&] {
+      if (more) stage((int)((k + 1) & 1), P);          // that buffer was last read before the previous barrier
+    });
+    __syncthreads();
   }
 }
 
