@@ -1,23 +1,26 @@
 #!/usr/bin/env python3
 """Benchmark of the rotated INT2 KV-cache hot path on one MI355X.
 
-One step = the whole path over one batch of the throughput workload
-(B=16, T=32768, 32 heads, d=128, fp16 K/V, Hadamard rotation, group 32):
-  1. kvq_quantize: rotate + quantize + pack all K and V rows into the cache;
-  2. kvq_decode_attention: one decode query per (batch, head) over the
-     whole INT2 cache (query rotation, split-K attention, merge,
-     un-rotation).
-The workload times the quantize kernel and the decode attention
-separately, so the timed region runs the K quantize calls back to back and
-then the K decode calls back to back (each call bracketed by events);
-ms_per_step is the sum per step.  Inputs are generated on the GPU before
-timing (seeded, synthetic) and are resident in HBM when the timed region
-starts.
+One step = the whole path over one batch of the workload (default: the
+throughput case B=16, T=32768, 32 heads, d=128, fp16 K/V, Hadamard rotation,
+group 32):
+  1. kvq_quantize: rotate + quantize + pack the K and V rows of the timed
+     token range into the cache;
+  2. kvq_decode_attention: one decode query per (batch, query head) over the
+     cache (query rotation, split-K attention, merge, un-rotation, fp16
+     sink / residual tokens when the workload has them).
+The quantize and the decode calls are timed separately: the timed region
+runs the K quantize calls back to back and then the K decode calls back to
+back (each call bracketed by events); ms_per_step is the wall time per
+step.  Inputs are generated on the GPU before timing (seeded, synthetic)
+and are resident in HBM when the timed region starts.
 
 Prints ONE JSON line.  `value` is the decode attention's effective HBM
 bandwidth (algorithmic bytes / time of the decode call); the quantize
 throughput, per-kernel rooflines and the oracle's CPU throughput on a
-bounded sample are extra fields.
+bounded sample are extra fields.  --config 4 (GQA, dense rotation, prefill
+slice) and --config 5 (13B-shaped, fp16 sinks and residual) give the same
+line for those workloads.
 """
 import argparse
 import hashlib
@@ -36,6 +39,7 @@ METRIC = "INT2 decode attention effective HBM GB/s (% of peak) + quantize tokens
 # algorithmic bytes (fp16 K/V input)
 QUANT_BYTES_PER_TOKEN_HEAD = 2 * 256 + 2 * 48     # read K and V rows, write 2 INT2 rows
 DECODE_BYTES_PER_TOKEN_HEAD = 2 * 48              # read one INT2 K row and one V row
+FP16_BYTES_PER_TOKEN_HEAD = 2 * 256               # read one fp16 K row and one V row
 
 
 def parse():
@@ -43,7 +47,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--config", type=int, default=3, help="workload id (3 = throughput case)")
+    p.add_argument("--config", type=int, default=3, choices=(3, 4, 5),
+                   help="workload id (3 = throughput case, 4 = GQA dense rotation, 5 = sinks)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a 1 GiB elementwise device copy (counter calibration)")
@@ -55,10 +60,10 @@ def file_sha(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profile(kernel, src_file, n_launch_units):
+def traffic_from_profile(kernel, workload, src_file):
     """HBM bytes per launch from a committed counter summary, or None when
     no summary exists or the kernel source changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -120,31 +125,42 @@ def main():
 
     kvq.load_library()
     cfg = W.config(args.config)
-    if cfg.rot != "hadamard" or cfg.n_sink or cfg.n_res or cfg.Hq != cfg.Hkv:
-        print("bench.py times the Hadamard, no-sink workloads", file=sys.stderr)
-        sys.exit(2)
     dev = "cuda"
     B, T, H, d = cfg.B, cfg.T, cfg.Hkv, cfg.d
+    rot = cfg.rot
     print(f"[bench] generating {cfg.name} on the GPU", file=sys.stderr, flush=True)
     t0 = time.time()
     K = W.kv_tokens(cfg, "K", device=dev)
     V = W.kv_tokens(cfg, "V", device=dev)
     q = W.queries(cfg, device=dev)
+    R = (torch.as_tensor(W.dense_rotations(cfg), device=dev).contiguous()
+         if rot == "dense" else None)
     ck = kvq.Int2Cache.empty(B, H, T, device=dev)
     cv = kvq.Int2Cache.empty(B, H, T, device=dev)
-    ws_bytes = kvq.kvq_decode_workspace_bytes(B, cfg.Hq, H, d, T)
+    tb, te = cfg.int2_range                    # INT2 tokens of the cache
+    q0, q1 = cfg.quant_range                   # tokens written by the timed quantize call
+    fp16 = {}
+    if cfg.n_sink or cfg.n_res:                # fp16 segments, [B, Hkv, n, d]
+        fp16 = dict(sink_k=K[:, :tb].permute(0, 2, 1, 3).contiguous(),
+                    sink_v=V[:, :tb].permute(0, 2, 1, 3).contiguous(),
+                    res_k=K[:, te:].permute(0, 2, 1, 3).contiguous(),
+                    res_v=V[:, te:].permute(0, 2, 1, 3).contiguous())
+    ws_bytes = kvq.kvq_decode_workspace_bytes(B, cfg.Hq, H, d, te - tb, cfg.n_sink, cfg.n_res)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
+    Kq, Vq = K[:, q0:q1], V[:, q0:q1]
+    if q0 > tb:                                # rest of the INT2 range, written once (untimed)
+        kvq.kvq_quantize(K[:, tb:q0], V[:, tb:q0], ck, cv, rot=rot, R=R, t_offset=tb)
     torch.cuda.synchronize()
     print(f"[bench] inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
 
     def quant():
-        kvq.kvq_quantize(K, V, ck, cv, rot="hadamard")
+        kvq.kvq_quantize(Kq, Vq, ck, cv, rot=rot, R=R, t_offset=q0)
 
     def decode():
-        kvq.kvq_decode_attention(q, ck, cv, 0, T, rot="hadamard", out=out, workspace=ws)
+        kvq.kvq_decode_attention(q, ck, cv, tb, te, rot=rot, R=R, out=out, workspace=ws, **fp16)
 
     for _ in range(args.warmup):
         quant()
@@ -171,29 +187,33 @@ def main():
     dec_ms = np.array([a.elapsed_time(b) for a, b in d_evs])
     ms_per_step = wall * 1e3 / args.steps
 
-    q_bytes = B * T * H * QUANT_BYTES_PER_TOKEN_HEAD
-    d_bytes = B * T * H * DECODE_BYTES_PER_TOKEN_HEAD + 2 * B * cfg.Hq * d * 2
+    n_q, n_int2, n_f16 = q1 - q0, te - tb, cfg.n_sink + cfg.n_res
+    r_bytes = H * d * d * 4 if rot == "dense" else 0
+    q_bytes = B * n_q * H * QUANT_BYTES_PER_TOKEN_HEAD + r_bytes
+    d_bytes = (B * n_int2 * H * DECODE_BYTES_PER_TOKEN_HEAD + B * n_f16 * H * FP16_BYTES_PER_TOKEN_HEAD
+               + 2 * B * cfg.Hq * d * 2 + r_bytes)
     q_ms, d_ms = float(np.median(quant_ms)), float(np.median(dec_ms))
     dec_gbs = d_bytes / (d_ms * 1e-3) / 1e9
     q_gbs = q_bytes / (q_ms * 1e-3) / 1e9
-    q_tok_s = B * T / (q_ms * 1e-3)
+    q_tok_s = B * n_q / (q_ms * 1e-3)
 
     csrc = os.path.join(ROOT, "int2_rotated_kv_amd", "csrc")
+    q_kernel, q_src = (("kv_rotate_quant_dense", "kv_rotate_quant_dense.hip") if rot == "dense"
+                       else ("kv_rotate_quant_fwht_f16", "kv_rotate_quant.hip"))
     roof_q = {"bound": "hbm", "achieved": round(q_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
               "frac": round(q_gbs / PEAK_HBM_GBS, 4),
-              "traffic": traffic_from_profile("kv_rotate_quant_fwht_f16",
-                                              os.path.join(csrc, "kv_rotate_quant.hip"), B * T * H),
-              "kernel": "kv_rotate_quant_fwht_f16", "algorithmic_bytes_per_launch": q_bytes,
+              "traffic": traffic_from_profile(q_kernel, cfg.name, os.path.join(csrc, q_src)),
+              "kernel": q_kernel, "algorithmic_bytes_per_launch": q_bytes,
               "bytes_per_unit": QUANT_BYTES_PER_TOKEN_HEAD, "unit_of_work": "(token, kv head)",
-              "units_per_launch": B * T * H, "avg_ms": round(q_ms, 4)}
+              "units_per_launch": B * n_q * H, "avg_ms": round(q_ms, 4)}
     roof_d = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
               "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
-              "traffic": traffic_from_profile("kv_int2_decode_attn",
-                                              os.path.join(csrc, "kv_decode.hip"), B * T * H),
+              "traffic": traffic_from_profile("kv_int2_decode_attn", cfg.name,
+                                              os.path.join(csrc, "kv_decode.hip")),
               "kernel": "decode call (kv_prep_query + kv_int2_decode_attn + kv_combine_unrotate)",
               "algorithmic_bytes_per_launch": d_bytes,
               "bytes_per_unit": DECODE_BYTES_PER_TOKEN_HEAD, "unit_of_work": "(INT2 token, kv head)",
-              "units_per_launch": B * T * H, "avg_ms": round(d_ms, 4)}
+              "units_per_launch": B * n_int2 * H, "avg_ms": round(d_ms, 4)}
     dominant, other = (roof_q, roof_d) if q_ms >= d_ms else (roof_d, roof_q)
 
     rec = {
@@ -203,7 +223,8 @@ def main():
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": cfg.name, "B": B, "T": T, "Hkv": H, "Hq": cfg.Hq, "d": d,
                    "kv_input": "f16", "cache": "int2 codes + f16 scale/zero, group 32",
-                   "rotation": "hadamard"},
+                   "rotation": rot, "int2_tokens": [tb, te], "quantize_tokens": [q0, q1],
+                   "fp16_tokens": n_f16},
         "decode_pct_of_peak": round(100 * dec_gbs / PEAK_HBM_GBS, 2),
         "decode_ms": round(d_ms, 4), "quantize_ms": round(q_ms, 4),
         "quantize_tokens_per_s": round(q_tok_s, 1),
@@ -216,36 +237,41 @@ def main():
     }
     rec["copy_reference_gbs"] = copy_bandwidth()
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(cfg, K, V, q)
+        rec["cpu_baseline"] = cpu_baseline(cfg, K, V, q, R, fp16)
     print(json.dumps(rec), flush=True)
 
 
-def cpu_baseline(cfg, K, V, q):
+def cpu_baseline(cfg, K, V, q, R, fp16):
     """The oracle, untouched, on a bounded sample of the same workload:
-    batch 0, all KV heads, all tokens (1/B of the job).  The sample's
-    inputs are the generator's values (copied from the device)."""
+    batch 0, all KV heads, all tokens of the INT2 range (1/B of the job).
+    The sample's inputs are the generator's values (copied from the
+    device)."""
     import numpy as np
     from oracle import kvq_oracle as O
     from threadpoolctl import threadpool_info
 
-    H = O.hadamard_rotation(cfg.d)
-    kh = K[0:1].permute(0, 2, 1, 3).contiguous().cpu().numpy()
-    vh = V[0:1].permute(0, 2, 1, 3).contiguous().cpu().numpy()
+    tb, te = cfg.int2_range
+    Rm = R.cpu().numpy() if R is not None else O.hadamard_rotation(cfg.d)
+    kh = K[0:1, tb:te].permute(0, 2, 1, 3).contiguous().cpu().numpy()
+    vh = V[0:1, tb:te].permute(0, 2, 1, 3).contiguous().cpu().numpy()
     qs = q[0:1].cpu().numpy()
+    kw = {k: v[0:1].cpu().numpy() for k, v in fp16.items()}
     t0 = time.perf_counter()
-    kc = O.quantize_cache(kh, H)
-    vc = O.quantize_cache(vh, H)
+    kc = O.quantize_cache(kh, Rm)
+    vc = O.quantize_cache(vh, Rm)
     t1 = time.perf_counter()
-    O.decode_attention(qs, kc, vc, 0, cfg.T, H)
+    O.decode_attention(qs, kc, vc, 0, te - tb, Rm, **kw)
     t2 = time.perf_counter()
-    d_bytes = cfg.T * cfg.Hkv * DECODE_BYTES_PER_TOKEN_HEAD + 2 * cfg.Hq * cfg.d * 2
+    n_f16 = cfg.n_sink + cfg.n_res
+    d_bytes = ((te - tb) * cfg.Hkv * DECODE_BYTES_PER_TOKEN_HEAD + n_f16 * cfg.Hkv * FP16_BYTES_PER_TOKEN_HEAD
+               + 2 * cfg.Hq * cfg.d * 2)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": round(d_bytes / (t2 - t1) / 1e9, 4), "unit": "GB/s",
             "cores": threads, "kind": "oracle",
-            "sample": f"batch 0 of {cfg.B} (all {cfg.Hkv} heads, {cfg.T} tokens): oracle "
+            "sample": f"batch 0 of {cfg.B} (all {cfg.Hkv} KV heads, {te - tb} INT2 tokens): oracle "
                       "rotate+quantize+pack of K and V, then oracle decode of the "
                       f"{cfg.Hq} queries; value = decode GB/s over the sample's bytes",
-            "quantize_tokens_per_s": round(cfg.T / (t1 - t0), 1),
+            "quantize_tokens_per_s": round((te - tb) / (t1 - t0), 1),
             "quantize_s": round(t1 - t0, 3), "decode_s": round(t2 - t1, 3),
             "host_cpus": len(os.sched_getaffinity(0))}
 

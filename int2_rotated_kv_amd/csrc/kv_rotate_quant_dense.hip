@@ -18,7 +18,10 @@
 // kernel.  The workgroup stages the inputs of four tiles at a time in LDS
 // with fully coalesced loads (16 lanes per 256-byte row), XOR-swizzled so
 // that the B-operand reads (one token per lane) hit distinct banks; the next
-// four tiles are loaded while the current ones compute.
+// four tiles are loaded while the current ones compute.  Output rows are
+// assembled in LDS and written with whole-line stores one iteration later
+// (per-wave 4-byte pieces left partial lines in the cache and cost extra
+// HBM traffic).
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
@@ -29,6 +32,10 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 constexpr int kDenseTiles = 4;                 // 32-token tiles per iteration
 constexpr int kDenseSlots = kDenseTiles * 32 * 16;        // 16-byte input chunks per iteration
 constexpr int kDenseLoadsPerThread = kDenseSlots / 256;
+// output staging per iteration: codes [tile][32 rows][32 B], then scales and
+// zeros [tile][32 rows][8 B] each
+constexpr int kDenseOutCodes = kDenseTiles * 32 * kCodeBytes;
+constexpr int kDenseOutBytes = kDenseOutCodes + 2 * kDenseTiles * 32 * 8;
 constexpr int64_t kDenseTargetBlocks = 512;   // 256 CUs x 2 workgroups
 constexpr int64_t kDenseMinItemsPerBlock = 16;
 
@@ -126,6 +133,7 @@ __device__ __forceinline__ void dense_group_codes(const float16_t &y, uint32_t &
 // waves, one per quantization group.
 __global__ __launch_bounds__(256, 2) void kv_rotate_quant_dense(DenseKernelArgs a) {
   __shared__ u32x4_t xs[2][kDenseSlots];      // 2 x 32 KiB of staged inputs
+  __shared__ __attribute__((aligned(16))) uint8_t out[2][kDenseOutBytes];   // 2 x 6 KiB of output rows
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int g = __builtin_amdgcn_readfirstlane(tid >> 6);   // this wave's group
@@ -178,9 +186,39 @@ __global__ __launch_bounds__(256, 2) void kv_rotate_quant_dense(DenseKernelArgs 
     for (int c = 0; c < kDenseLoadsPerThread; ++c) xs[buf][c * 256 + tid] = P[c];
   };
 
-  // MFMAs and quantization of the iteration's tiles for group g; stage_next
-  // runs between the quantization and the stores.
-  auto compute = [&](int64_t k, int buf, auto &&stage_next) {
+  // Output rows of iteration k (from LDS buffer ob) go to the cache: thread
+  // tid stores 16 code bytes (64 threads per tile = 32 rows x 32 bytes) and 8
+  // bytes of scales (tid < 128) or zeros.
+  auto store_out = [&](int64_t k, const uint8_t *ob) {
+    {
+      const int u = tid >> 6, r = (tid & 63) >> 1;
+      const int64_t it = i0 + k * kDenseTiles + u;
+      const QuantSide sd = (it & side_shift) ? a.side[1] : a.side[0];
+      const int64_t t = (it >> side_shift) * 32 + r;
+      if (it < i1 && t < a.T_new) {
+        const int64_t row = (b * a.Hkv + h) * sd.T_cap + a.t_offset + t;
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t *>(ob + 16 * tid),
+                                    reinterpret_cast<u32x4_t *>(sd.codes + row * kCodeBytes) + (tid & 1));
+      }
+    }
+    {
+      const int zs = tid >> 7, u = (tid >> 5) & 3, r = tid & 31;
+      const int64_t it = i0 + k * kDenseTiles + u;
+      const QuantSide sd = (it & side_shift) ? a.side[1] : a.side[0];
+      const int64_t t = (it >> side_shift) * 32 + r;
+      if (it < i1 && t < a.T_new) {
+        const int64_t row = (b * a.Hkv + h) * sd.T_cap + a.t_offset + t;
+        uint16_t *dst = zs ? sd.zeros : sd.scales;
+        __builtin_nontemporal_store(
+            *reinterpret_cast<const u32x2_t *>(ob + kDenseOutCodes + zs * kDenseTiles * 256 + (u * 32 + r) * 8),
+            reinterpret_cast<u32x2_t *>(dst + row * kNGroups));
+      }
+    }
+  };
+
+  // MFMAs and quantization of the iteration's tiles for group g into the
+  // output staging buffer ob; stage_next runs after that, then store_prev.
+  auto compute = [&](int buf, uint8_t *ob, auto &&stage_next, auto &&store_prev) {
     float16_t acc[kDenseTiles];
 #pragma unroll
     for (int u = 0; u < kDenseTiles; ++u) acc[u] = float16_t{};
@@ -203,35 +241,22 @@ __global__ __launch_bounds__(256, 2) void kv_rotate_quant_dense(DenseKernelArgs 
         acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(rf[s][1], bx[s & 1][u], acc[u], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // acc[u][r] = y[token j of tile u][32g + 8(r/4) + 4*half + r%4]
-    uint32_t cw[kDenseTiles];
-    uint16_t sz[kDenseTiles];
+    // acc[u][r] = y[token j of tile u][32g + 8(r/4) + 4*half + r%4]; half 0
+    // puts group bytes 0..3 and the scale in the row, half 1 bytes 4..7 and
+    // the zero
 #pragma unroll
     for (int u = 0; u < kDenseTiles; ++u) {
       uint32_t w0, w1;
       uint16_t sb, zb;
       dense_group_codes(acc[u], w0, w1, sb, zb);
-      cw[u] = half ? w1 : w0;
-      sz[u] = half ? zb : sb;
+      *reinterpret_cast<uint32_t *>(ob + (u * 32 + j) * kCodeBytes + 8 * g + 4 * half) = half ? w1 : w0;
+      *reinterpret_cast<uint16_t *>(ob + kDenseOutCodes + half * kDenseTiles * 256 + (u * 32 + j) * 8 + 2 * g) =
+          half ? zb : sb;
     }
-    // The next inputs go to LDS before this iteration's stores are issued:
-    // waits for loads count every earlier memory operation, stores included.
+    // Loads are waited for before the stores are issued: those waits also
+    // cover every earlier memory operation, stores included.
     stage_next();
-#pragma unroll
-    for (int u = 0; u < kDenseTiles; ++u) {
-      const int64_t it = i0 + k * kDenseTiles + u;
-      if (it >= i1) break;                              // wave-uniform
-      const QuantSide sd = (it & side_shift) ? a.side[1] : a.side[0];
-      const int64_t t = (it >> side_shift) * 32 + j;
-      if (t < a.T_new) {
-        const int64_t row = (b * a.Hkv + h) * sd.T_cap + a.t_offset + t;
-        // half 0 stores group bytes 0..3 and the scale, half 1 bytes 4..7
-        // and the zero; the four waves fill the rest of each row
-        *reinterpret_cast<uint32_t *>(sd.codes + row * kCodeBytes + 8 * g + 4 * half) = cw[u];
-        uint16_t *dst = half ? sd.zeros : sd.scales;
-        dst[row * kNGroups + g] = sz[u];
-      }
-    }
+    store_prev();
   };
 
   u32x4_t P[kDenseLoadsPerThread];
@@ -242,11 +267,13 @@ __global__ __launch_bounds__(256, 2) void kv_rotate_quant_dense(DenseKernelArgs 
     const bool more = k + 1 < n_iter;
     if (more) load_iter(k + 1, P);
     __builtin_amdgcn_sched_barrier(0);
-    compute(k, (int)(k & 1), [&] {
-      if (more) stage((int)((k + 1) & 1), P);          // that buffer was last read before the previous barrier
-    });
+    // buffers last read before the previous barrier: input (k+1)&1, output k&1
+    compute((int)(k & 1), out[k & 1],
+            [&] { if (more) stage((int)((k + 1) & 1), P); },
+            [&] { if (k > 0) store_out(k - 1, out[(k - 1) & 1]); });
     __syncthreads();
   }
+  store_out(n_iter - 1, out[(n_iter - 1) & 1]);      // published by the last barrier
 }
 
 hipError_t launch_quantize_dense(const QuantArgs &q, hipStream_t stream) {
