@@ -103,7 +103,7 @@ size_t kvq_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
                                   int64_t n_int2_tokens, int64_t n_sink, int64_t n_res) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || d != 128) return 0;
   if (n_int2_tokens < 0 || n_sink < 0 || n_res < 0) return 0;
-  const kvq::SplitPlan p = kvq::plan_splits(B, Hq, n_int2_tokens);
+  const kvq::SplitPlan p = kvq::plan_splits(B, Hq, Hkv, n_int2_tokens);
   return workspace_bytes(B, Hq, p.n_splits);
 }
 
@@ -137,7 +137,7 @@ kvq_status kvq_decode_attention(const void *q, kvq_dtype q_dtype, int64_t B, int
   if (n_sink + n_res > kMaxFp16Tokens) return KVQ_ERR_UNSUPPORTED;
   if (B * Hq > 0x7FFFFFFF) return KVQ_ERR_UNSUPPORTED;
   if (!(softmax_scale == softmax_scale)) return KVQ_ERR_INVALID_ARG;   // NaN
-  const kvq::SplitPlan plan = kvq::plan_splits(B, Hq, n_int2);
+  const kvq::SplitPlan plan = kvq::plan_splits(B, Hq, Hkv, n_int2);
   const size_t need = workspace_bytes(B, Hq, plan.n_splits);
   if (workspace == nullptr || ((uintptr_t)workspace & 255u) != 0) return KVQ_ERR_INVALID_ARG;
   if (workspace_bytes_given < need) return KVQ_ERR_WORKSPACE_TOO_SMALL;

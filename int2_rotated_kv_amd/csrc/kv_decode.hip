@@ -33,12 +33,10 @@
 // codes on 1.5 makes the fp16 rounding of w multiply code - 1.5 in
 // [-1.5, 1.5], so it does not get amplified by the cancellation between the
 // code and zero-point terms.
-#include "kvq_device.h"
-#include "kvq_launch.h"
+#include "kv_decode_common.h"
 
 namespace kvq {
 
-constexpr float kNegInf = -__builtin_huge_valf();
 
 // ---------------------------------------------------------------------------
 // 128-point normalized FWHT / dense rotation across a 128-thread block (LDS)
@@ -154,6 +152,8 @@ __global__ __launch_bounds__(128) void kv_prep_query(PrepArgs a) {
     part |= __shfl_xor(part, 8, 32);
     if (k == 0) base[L * 4 + w * 2 + par] = part;
   }
+  // the fixed-point query itself, for the matrix-core GQA kernel
+  reinterpret_cast<int32_t *>(a.qprep)[bh * kQprepDwordsPerHead + kQprepFixedOffset + c] = qi;
   if (cg == 0) {
     float *fb = reinterpret_cast<float *>(base);
     fb[24] = (float)isum * step;             // sum of the group's fixed-point q
@@ -165,23 +165,6 @@ __global__ __launch_bounds__(128) void kv_prep_query(PrepArgs a) {
 // ---------------------------------------------------------------------------
 // 2. split-K attention over INT2 tokens
 // ---------------------------------------------------------------------------
-struct AttnArgs {
-  const uint8_t *kcodes; const uint16_t *kscales; const uint16_t *kzeros; int64_t kT_cap;
-  const uint8_t *vcodes; const uint16_t *vscales; const uint16_t *vzeros; int64_t vT_cap;
-  int64_t t_begin, n_int2;
-  int64_t n_splits;
-  int64_t total_waves;  // B * Hq * n_splits
-  int Hkv, Hq, G;
-  const uint32_t *qprep;
-  float *partials;
-};
-
-// Reassemble the fp16 subnormal channel factor: code at position x of a
-// 16-bit half is read with weight 2^(2x-24) (x <= 4) or 2^(2x-30) (x >= 5).
-__device__ __forceinline__ constexpr float chan_unscale(int x) {
-  return x <= 4 ? (float)(1u << (24 - 2 * x)) : (float)(1u << (30 - 2 * x));
-}
-
 // Lane layout of the attention kernel: lane l handles token slot ts = l/2 of
 // a 64-token tile (tokens ts and 32 + ts) on channel half h = l%2, i.e. the
 // two groups 2h and 2h+1 (64 channels).  Codes arrive as one 16-byte load
@@ -198,14 +181,6 @@ struct AttnState {
   float m[GC], l[GC], zacc[GC][2], wsum[GC][2], acc[GC][64];
 };
 
-// Lazy rescaling: the running reference m is moved only when a score
-// exceeds it by more than kSlack (log2 units), so p = 2^(s - m) stays below
-// 2^kSlack and w = p * s_v stays far inside the fp16 range.  The partial
-// (m, l, o') is exact for any reference m, so the merge is unchanged.
-constexpr float kSlack = 4.0f;
-
-constexpr uint32_t kHalf2Ones = 0x3C003C00u;   // (1.0, 1.0) in fp16
-
 // Per-lane query data for the lane's two channel groups of GC heads.
 template <int GC>
 struct QueryLimbs {
@@ -213,28 +188,6 @@ struct QueryLimbs {
   float isum[GC][2];          // group sums of the fixed-point query, in steps
   float qstep[GC];            // fixed-point step of the head (log2 units)
 };
-
-// Sum / max over the two 16-lane rows of each 32-lane half (xor 16) and over
-// the two halves (xor 32) with the gfx950 lane-swap instructions.
-__device__ __forceinline__ float sum_xor16(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(float_as_bits(v), float_as_bits(v), false, false);
-  return bits_as_float(r[0]) + bits_as_float(r[1]);
-}
-__device__ __forceinline__ float sum_xor32(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(float_as_bits(v), float_as_bits(v), false, false);
-  return bits_as_float(r[0]) + bits_as_float(r[1]);
-}
-__device__ __forceinline__ float max_xor16(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(float_as_bits(v), float_as_bits(v), false, false);
-  return fmaxf(bits_as_float(r[0]), bits_as_float(r[1]));
-}
-__device__ __forceinline__ float max_xor32(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(float_as_bits(v), float_as_bits(v), false, false);
-  return fmaxf(bits_as_float(r[0]), bits_as_float(r[1]));
-}
-
-__device__ __forceinline__ float lo_half(uint32_t w) { return half_bits_to_float((uint16_t)(w & 0xFFFFu)); }
-__device__ __forceinline__ float hi_half(uint32_t w) { return half_bits_to_float((uint16_t)(w >> 16)); }
 
 // exact int32 dot product of one group's 32 codes (two code dwords) with the
 // five 4-bit limbs of the fixed-point query
@@ -664,11 +617,18 @@ __global__ __launch_bounds__(128) void kv_combine_unrotate(CombineArgs a) {
 // measured faster than more, shorter waves.
 constexpr int64_t kTargetWaves = 2048;
 
-SplitPlan plan_splits(int64_t B, int64_t Hq, int64_t n_int2) {
+// Waves per split unit: one per query head for G = 1, one per four query
+// heads of a KV head for G >= 2 (the matrix-core GQA kernel).
+static int64_t split_units(int64_t B, int64_t Hq, int64_t Hkv) {
+  const int64_t G = Hq / Hkv;
+  return G == 1 ? B * Hq : B * Hkv * ((G + 3) / 4);
+}
+
+SplitPlan plan_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_int2) {
   SplitPlan p{0};
-  if (n_int2 <= 0 || B <= 0 || Hq <= 0) return p;
-  const int64_t heads = B * Hq;
-  int64_t s = kTargetWaves / heads;              // stay within one round of resident waves
+  if (n_int2 <= 0 || B <= 0 || Hq <= 0 || Hkv <= 0) return p;
+  const int64_t units = split_units(B, Hq, Hkv);
+  int64_t s = kTargetWaves / units;              // stay within one round of resident waves
   const int64_t by_len = (n_int2 + 255) / 256;   // at least ~256 tokens per wave
   if (s > by_len) s = by_len;
   if (s > 4096) s = 4096;
@@ -694,16 +654,16 @@ hipError_t launch_decode(const DecodeArgs &d, hipStream_t stream) {
     a.vcodes = d.vcodes; a.vscales = d.vscales; a.vzeros = d.vzeros; a.vT_cap = d.vT_cap;
     a.t_begin = d.t_begin; a.n_int2 = d.n_int2;
     a.n_splits = d.n_splits;
-    a.total_waves = d.B * d.Hq * d.n_splits;
+    a.total_waves = split_units(d.B, d.Hq, d.Hkv) * d.n_splits;
     a.Hkv = (int)d.Hkv; a.Hq = (int)d.Hq; a.G = G;
     a.qprep = reinterpret_cast<const uint32_t *>(d.qprep);
     a.partials = d.partials;
-    if (G <= 4) {
+    if (G == 1) {
       hipLaunchKernelGGL(kv_int2_decode_attn<4>, dim3((unsigned)((a.total_waves + 3) / 4)), dim3(256), 0,
                          stream, a);
     } else {
-      hipLaunchKernelGGL(kv_int2_decode_attn<8>, dim3((unsigned)((a.total_waves + 7) / 8)), dim3(512), 0,
-                         stream, a);
+      hipError_t e = launch_attn_gqa(a, stream);
+      if (e != hipSuccess) return e;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

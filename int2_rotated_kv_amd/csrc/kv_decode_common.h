@@ -1,0 +1,68 @@
+// Declarations shared by the decode kernels of the kvq library.
+#pragma once
+
+#include "kvq_device.h"
+#include "kvq_launch.h"
+
+namespace kvq {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+struct AttnArgs {
+  const uint8_t *kcodes; const uint16_t *kscales; const uint16_t *kzeros; int64_t kT_cap;
+  const uint8_t *vcodes; const uint16_t *vscales; const uint16_t *vzeros; int64_t vT_cap;
+  int64_t t_begin, n_int2;
+  int64_t n_splits;
+  int64_t total_waves;  // B * Hq * n_splits
+  int Hkv, Hq, G;
+  const uint32_t *qprep;
+  float *partials;
+};
+
+// Reassemble the fp16 subnormal channel factor: code at position x of a
+// 16-bit half is read with weight 2^(2x-24) (x <= 4) or 2^(2x-30) (x >= 5).
+__device__ __forceinline__ constexpr float chan_unscale(int x) {
+  return x <= 4 ? (float)(1u << (24 - 2 * x)) : (float)(1u << (30 - 2 * x));
+}
+
+// Lazy rescaling: the running reference m is moved only when a score
+// exceeds it by more than kSlack (log2 units), so p = 2^(s - m) stays below
+// 2^kSlack and w = p * s_v stays far inside the fp16 range.  The partial
+// (m, l, o') is exact for any reference m, so the merge is unchanged.
+constexpr float kSlack = 4.0f;
+
+constexpr uint32_t kHalf2Ones = 0x3C003C00u;   // (1.0, 1.0) in fp16
+
+// Sum / max over the two 16-lane rows of each 32-lane half (xor 16) and over
+// the two halves (xor 32) with the gfx950 lane-swap instructions.
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(float_as_bits(v), float_as_bits(v), false, false);
+  return bits_as_float(r[0]) + bits_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(float_as_bits(v), float_as_bits(v), false, false);
+  return bits_as_float(r[0]) + bits_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(float_as_bits(v), float_as_bits(v), false, false);
+  return fmaxf(bits_as_float(r[0]), bits_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(float_as_bits(v), float_as_bits(v), false, false);
+  return fmaxf(bits_as_float(r[0]), bits_as_float(r[1]));
+}
+
+__device__ __forceinline__ float lo_half(uint32_t w) { return half_bits_to_float((uint16_t)(w & 0xFFFFu)); }
+__device__ __forceinline__ float hi_half(uint32_t w) { return half_bits_to_float((uint16_t)(w >> 16)); }
+
+// A wave's tiles: the head's INT2 tokens are cut into 64-token tiles and
+// wave `split` of S takes tiles split, split + S, ...; mine = how many full
+// tiles that is.
+__device__ __forceinline__ int64_t tiles_of_split(int64_t n_int2, int64_t split, int64_t S) {
+  const int64_t n_full = n_int2 >> 6;
+  return split < n_full ? (n_full - 1 - split) / S + 1 : 0;
+}
+
+hipError_t launch_attn_gqa(const AttnArgs &a, hipStream_t stream);
+
+}  // namespace kvq

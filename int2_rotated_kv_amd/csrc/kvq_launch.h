@@ -45,7 +45,7 @@ struct DecodeArgs {
   float qscale;         // softmax_scale * log2(e)
   void *out;
   // workspace carve-up (device pointers)
-  int32_t *qprep;       // [B][Hq][128] dwords
+  int32_t *qprep;       // [B][Hq][kQprepDwordsPerHead] dwords
   float *partials;      // [B][Hq][n_splits][kPartialStride]
   int64_t n_splits;     // waves per (b, query head), each taking every n_splits-th tile
 };
@@ -54,9 +54,12 @@ struct DecodeArgs {
 struct SplitPlan {
   int64_t n_splits;
 };
-SplitPlan plan_splits(int64_t B, int64_t Hq, int64_t n_int2);
+SplitPlan plan_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_int2);
 
-constexpr int kQprepDwordsPerHead = 128;
+// Per query head: 128 dwords of nibble limbs and group sums, then the 128
+// fixed-point query values (int32).
+constexpr int kQprepDwordsPerHead = 256;
+constexpr int kQprepFixedOffset = 128;
 constexpr int kPartialStride = 132;   // o'[128], m, l, 2 pad (16-byte rows)
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);

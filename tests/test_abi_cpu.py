@@ -155,14 +155,14 @@ def test_workspace_bytes():
     assert K.kvq_decode_workspace_bytes(0, 4, 2, 128, 10) == 0
     assert K.kvq_decode_workspace_bytes(1, 3, 2, 128, 10) == 0
     assert K.kvq_decode_workspace_bytes(1, 4, 2, 64, 10) == 0
-    # query block (512 B per head, 256-aligned) + 132 floats per (head, split)
-    qprep = 16 * 32 * 512
+    # query block (1 KiB per head, 256-aligned) + 132 floats per (head, split)
+    qprep = 16 * 32 * 1024
     ws = K.kvq_decode_workspace_bytes(16, 32, 32, 128, 32768)
     assert ws > qprep and (ws - qprep) % (16 * 32 * 132 * 4) == 0
     n_splits = (ws - qprep) // (16 * 32 * 132 * 4)
     assert 1 <= n_splits <= 32768 // 256
     # no INT2 tokens: only the query block
-    assert K.kvq_decode_workspace_bytes(1, 4, 2, 128, 0, 4, 8) == 4 * 512
+    assert K.kvq_decode_workspace_bytes(1, 4, 2, 128, 0, 4, 8) == 4 * 1024
     # more tokens never need fewer splits
     prev = 0
     for n in (1, 100, 1000, 10000, 100000, 1000000):
