@@ -71,8 +71,17 @@ __device__ __forceinline__ float block_matvec128(float x, const float *__restric
 #pragma unroll 8
     for (int k = 0; k < 128; ++k) acc = __builtin_fmaf(buf[k], M[k * 128 + c], acc);
   } else {
-#pragma unroll 8
-    for (int k = 0; k < 128; ++k) acc = __builtin_fmaf(buf[k], M[c * 128 + k], acc);
+    // thread c walks row c of M with 16-byte loads (a row is 4 cache lines,
+    // reused across the iterations)
+    const float4_t *row = reinterpret_cast<const float4_t *>(M + c * 128);
+#pragma unroll 4
+    for (int k4 = 0; k4 < 32; ++k4) {
+      const float4_t m4 = row[k4];
+      acc = __builtin_fmaf(buf[4 * k4], m4.x, acc);
+      acc = __builtin_fmaf(buf[4 * k4 + 1], m4.y, acc);
+      acc = __builtin_fmaf(buf[4 * k4 + 2], m4.z, acc);
+      acc = __builtin_fmaf(buf[4 * k4 + 3], m4.w, acc);
+    }
   }
   __syncthreads();
   return acc;

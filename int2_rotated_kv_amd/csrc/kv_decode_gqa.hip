@@ -190,7 +190,29 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
   const int tk = lane & 15, kgrp = lane >> 4;      // K side
   const int tp = lane >> 3, c4 = lane & 7;          // V side
 
-  // rows are relative to the head's INT2 start; clamped to rmax (tail tile)
+  // Full tile at row r0 (relative to the head's INT2 start): wave-uniform
+  // tile bases plus 32-bit lane offsets.
+  const uint32_t o_kc = (uint32_t)(tk * kCodeBytes + 8 * kgrp);
+  const uint32_t o_sz = (uint32_t)(lane * kNGroups);
+  const uint32_t o_va = (uint32_t)(tp * kCodeBytes + 4 * c4);
+  auto load_full = [&](int64_t r0) {
+    MqTile t;
+    const uint8_t *kct = kc + r0 * kCodeBytes, *vct = vc + r0 * kCodeBytes;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      t.kc[k] = *reinterpret_cast<const u32x2_t *>(kct + o_kc + 16 * k * kCodeBytes);
+    t.ks = *reinterpret_cast<const u32x2_t *>(ks + r0 * kNGroups + o_sz);
+    t.kz = *reinterpret_cast<const u32x2_t *>(kz + r0 * kNGroups + o_sz);
+    t.vs = *reinterpret_cast<const u32x2_t *>(vs + r0 * kNGroups + o_sz);
+    t.vz = *reinterpret_cast<const u32x2_t *>(vz + r0 * kNGroups + o_sz);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      t.va[k] = *reinterpret_cast<const uint32_t *>(vct + o_va + 16 * k * kCodeBytes);
+      t.vb[k] = *reinterpret_cast<const uint32_t *>(vct + o_va + (16 * k + 8) * kCodeBytes);
+    }
+    return t;
+  };
+  // Any tile: rows clamped to rmax (the partial last tile).
   auto load_tile = [&](int64_t r0, int64_t rmax) {
     MqTile t;
 #pragma unroll
@@ -346,14 +368,13 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
   // this wave's full tiles, loads one tile ahead
   const int64_t mine = tiles_of_split(a.n_int2, split, S);
   if (mine > 0) {
-    const int64_t rmax = a.n_int2 - 1;
     auto row_of = [&](int64_t i) { return 64 * (split + (i < mine - 1 ? i : mine - 1) * S); };
-    MqTile t0 = load_tile(row_of(0), rmax), t1;
+    MqTile t0 = load_full(row_of(0)), t1;
     int64_t i = 0;
     for (; i + 2 <= mine; i += 2) {
-      t1 = load_tile(row_of(i + 1), rmax);
+      t1 = load_full(row_of(i + 1));
       process(t0, 64);
-      t0 = load_tile(row_of(i + 2), rmax);
+      t0 = load_full(row_of(i + 2));
       process(t1, 64);
     }
     if (i < mine) process(t0, 64);
