@@ -12,12 +12,13 @@
 //                        by softmax_scale*log2(e), turned into a per-group
 //                        19-bit fixed-point vector split into five signed
 //                        4-bit limbs.
-//   2. kv_int2_decode_attn  one wave per (b, query head, split): flash-
-//                        decoding over every S-th 64-token tile of the head with
-//                        an online softmax.  The G query heads of a KV group are
-//                        sibling waves of one workgroup that stream the same
-//                        tiles together, so HBM serves each tile once and the
-//                        copies for the other heads come from the cache.
+//   2. kv_int2_decode_attn  (one query head per KV head) one wave per
+//                        (b, head, split): flash-decoding over every S-th
+//                        64-token tile of the head with an online softmax.
+//                        Grouped-query attention (several query heads per KV
+//                        head) takes the matrix-core kernel of
+//                        kv_decode_gqa.hip instead, which writes the same
+//                        partials.
 //   3. kv_combine_unrotate  per (b, query head): log-sum-exp merge of the wave
 //                        partials staged through LDS, un-rotation by R^T
 //                        (linear, so applied once after the merge), fp16
