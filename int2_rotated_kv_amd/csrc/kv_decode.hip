@@ -40,11 +40,12 @@ namespace kvq {
 
 
 // ---------------------------------------------------------------------------
-// 128-point normalized FWHT / dense rotation across a 128-thread block (LDS)
+// 128-point normalized FWHT / dense rotation across a block of >= 128 threads (LDS)
 // ---------------------------------------------------------------------------
+// Threads 0..127 own channel c; wider blocks pass through the barriers.
 __device__ __forceinline__ float block_fwht128(float x, float *buf) {
   const int c = threadIdx.x;
-  buf[c] = x;
+  if (c < 128) buf[c] = x;
   __syncthreads();
 #pragma unroll
   for (int h = 1; h < 128; h <<= 1) {
@@ -56,7 +57,7 @@ __device__ __forceinline__ float block_fwht128(float x, float *buf) {
     }
     __syncthreads();
   }
-  const float y = buf[c] * 0.08838834764831845f;
+  const float y = c < 128 ? buf[c] * 0.08838834764831845f : 0.0f;
   __syncthreads();
   return y;
 }
@@ -65,17 +66,17 @@ __device__ __forceinline__ float block_fwht128(float x, float *buf) {
 __device__ __forceinline__ float block_matvec128(float x, const float *__restrict__ M,
                                                  bool transpose, float *buf) {
   const int c = threadIdx.x;
-  buf[c] = x;
+  if (c < 128) buf[c] = x;
   __syncthreads();
   float acc = 0.0f;
-  if (!transpose) {
+  if (c < 128 && !transpose) {
 #pragma unroll 8
     for (int k = 0; k < 128; ++k) acc = __builtin_fmaf(buf[k], M[k * 128 + c], acc);
-  } else {
+  } else if (c < 128) {
     // thread c walks row c of M with 16-byte loads (a row is 4 cache lines,
     // reused across the iterations)
     const float4_t *row = reinterpret_cast<const float4_t *>(M + c * 128);
-#pragma unroll 4
+#pragma unroll 8
     for (int k4 = 0; k4 < 32; ++k4) {
       const float4_t m4 = row[k4];
       acc = __builtin_fmaf(buf[4 * k4], m4.x, acc);
@@ -477,66 +478,67 @@ struct CombineArgs {
   void *out;
 };
 
-__device__ __forceinline__ float block_max128(float v, float *red) {
+constexpr int kCombineThreads = 256;
+constexpr int kCombineWaves = kCombineThreads / 64;
+// fp16 tokens: a 16-lane row per token (8 channels per lane, one 16-byte
+// load), kFpRows tokens per step across the block, kFpUnroll steps whose loads
+// are issued together.
+constexpr int kFpRows = kCombineThreads / 16;
+constexpr int kFpUnroll = 4;
+
+__device__ __forceinline__ float block_max(float v, float *red) {
   for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  const float r = fmaxf(red[0], red[1]);
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < kCombineWaves; ++i) r = fmaxf(r, red[i]);
   __syncthreads();
   return r;
 }
 
-__device__ __forceinline__ float block_sum128(float v, float *red) {
+__device__ __forceinline__ float block_sum(float v, float *red) {
   for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  const float r = red[0] + red[1];
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < kCombineWaves; ++i) r += red[i];
   __syncthreads();
   return r;
 }
 
-// grid: B*Hq blocks of 128 threads.  Dynamic LDS: n_splits + n_sink + n_res floats.
-__global__ __launch_bounds__(128) void kv_combine_unrotate(CombineArgs a) {
+// Row t of the fp16 segment: sinks first, then residual tokens.
+__device__ __forceinline__ const uint16_t *fp16_row(const uint16_t *sink, const uint16_t *res, int64_t bkv,
+                                                    int64_t n_sink, int64_t n_res, int64_t t) {
+  return t < n_sink ? sink + (bkv * n_sink + t) * kD : res + (bkv * n_res + (t - n_sink)) * kD;
+}
+
+// grid: B*Hq blocks of kCombineThreads threads; threads c < 128 own channel c
+// in the merge and the un-rotation.  Dynamic LDS: n_splits + n_sink + n_res
+// floats.
+__global__ __launch_bounds__(kCombineThreads) void kv_combine_unrotate(CombineArgs a) {
   extern __shared__ float lds[];
-  __shared__ float buf[128];
-  __shared__ float red[2];
+  __shared__ float buf[kD];
+  __shared__ float red[kCombineWaves];
+  __shared__ float vred[kFpRows * kD];
   const int c = threadIdx.x;
+  const bool own = c < kD;
   const int64_t bh = blockIdx.x;             // b*Hq + hq
   const int hq = (int)(bh % a.Hq);
   const int64_t b = bh / a.Hq;
   const int hkv = hq / (a.Hq / a.Hkv);
+  const int64_t bkv = b * a.Hkv + hkv;
   float *wsplit = lds;
   float *pf = lds + a.n_splits;
-
-  // INT2 partials: M = max m_i, weights 2^(m_i - M)
-  const float *part = a.partials + bh * a.n_splits * kPartialStride;
-  float mloc = kNegInf;
-  for (int64_t i = c; i < a.n_splits; i += 128) mloc = fmaxf(mloc, part[i * kPartialStride + 128]);
-  const float M2 = block_max128(mloc, red);
-  float lloc = 0.0f;
-  for (int64_t i = c; i < a.n_splits; i += 128) {
-    const float mi = part[i * kPartialStride + 128];
-    const float wi = (mi == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(mi - M2);
-    wsplit[i] = wi;
-    lloc += wi * part[i * kPartialStride + 129];
-  }
-  __syncthreads();
-  const float L2 = block_sum128(lloc, red);
-  float o = 0.0f;
-  for (int64_t i = 0; i < a.n_splits; ++i) o = __builtin_fmaf(wsplit[i], part[i * kPartialStride + c], o);
-
-  // un-rotate the INT2 part (linear, so once after the merge)
-  if (a.rot == 1) o = block_fwht128(o, buf);
-  else if (a.rot == 2) o = block_matvec128(o, a.R + (int64_t)hkv * kD * kD, true, buf);
-
-  // fp16 tokens in the original basis.  Scores: a 16-lane row per token,
-  // 8 channels per lane (one 16-byte load), reduced over the row with DPP;
-  // eight tokens per step across the block.
   const int64_t nf = a.n_sink + a.n_res;
-  float Mf = kNegInf, Lf = 0.0f, of = 0.0f;
+  const int rs = c >> 4;                     // token row slot of the fp16 phases
+  const int cl = c & 15;                     // channels 8cl .. 8cl+7
+
+  // fp16 token scores in the original basis (independent of the partials,
+  // so they go first): scale * q . k, log2 units
+  float Mf = kNegInf;
   if (nf > 0) {
-    const int64_t bkv = b * a.Hkv + hkv;
-    const int cl = c & 15;                    // channels 8cl .. 8cl+7
     float q8[8];
     {
       const int64_t qoff = bh * kD + 8 * cl;
@@ -559,63 +561,121 @@ __global__ __launch_bounds__(128) void kv_combine_unrotate(CombineArgs a) {
       for (int i = 0; i < 8; ++i) q8[i] *= a.qscale;
     }
     float sl = kNegInf;
-    for (int64_t t0 = 0; t0 < nf; t0 += 8) {
-      const int64_t t = t0 + (c >> 4);
-      const bool valid = t < nf;
-      const int64_t tt = valid ? t : 0;
-      const uint16_t *row = tt < a.n_sink ? a.sink_k + (bkv * a.n_sink + tt) * kD
-                                          : a.res_k + (bkv * a.n_res + (tt - a.n_sink)) * kD;
-      const u32x4_t u = *reinterpret_cast<const u32x4_t *>(row + 8 * cl);
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-      float sacc = 0.0f;
+    for (int64_t t0 = 0; t0 < nf; t0 += kFpRows * kFpUnroll) {
+      u32x4_t u[kFpUnroll];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const half2_t k2 = __builtin_bit_cast(half2_t, w[i]);
-        sacc = __builtin_fmaf(q8[2 * i], (float)k2.x, sacc);
-        sacc = __builtin_fmaf(q8[2 * i + 1], (float)k2.y, sacc);
+      for (int k = 0; k < kFpUnroll; ++k) {
+        const int64_t t = t0 + k * kFpRows + rs;
+        const int64_t tt = t < nf ? t : 0;
+        u[k] = *reinterpret_cast<const u32x4_t *>(fp16_row(a.sink_k, a.res_k, bkv, a.n_sink, a.n_res, tt) + 8 * cl);
       }
-      sacc += quad_swap<kQuadXor1>(sacc);
-      sacc += quad_swap<kQuadXor2>(sacc);
-      sacc += row_ror<4>(sacc);
-      sacc += row_ror<8>(sacc);
-      if (valid && cl == 0) pf[t] = sacc;
-      if (valid) sl = fmaxf(sl, sacc);
+#pragma unroll
+      for (int k = 0; k < kFpUnroll; ++k) {
+        const uint32_t w[4] = {u[k].x, u[k].y, u[k].z, u[k].w};
+        float sacc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const half2_t k2 = __builtin_bit_cast(half2_t, w[i]);
+          sacc = __builtin_fmaf(q8[2 * i], (float)k2.x, sacc);
+          sacc = __builtin_fmaf(q8[2 * i + 1], (float)k2.y, sacc);
+        }
+        sacc += quad_swap<kQuadXor1>(sacc);
+        sacc += quad_swap<kQuadXor2>(sacc);
+        sacc += row_ror<4>(sacc);
+        sacc += row_ror<8>(sacc);
+        const int64_t t = t0 + k * kFpRows + rs;
+        if (t < nf) {
+          if (cl == 0) pf[t] = sacc;
+          sl = fmaxf(sl, sacc);
+        }
+      }
     }
-    Mf = block_max128(sl, red);              // its barrier also publishes pf
+    Mf = block_max(sl, red);                 // its barrier also publishes pf
   }
+
+  // INT2 partials: M2 = max m_i, weights 2^(m_i - M2)
+  const float *part = a.partials + bh * a.n_splits * kPartialStride;
+  float mloc = kNegInf;
+  for (int64_t i = c; i < a.n_splits; i += kCombineThreads) mloc = fmaxf(mloc, part[i * kPartialStride + 128]);
+  const float M2 = block_max(mloc, red);
+  float lloc = 0.0f;
+  for (int64_t i = c; i < a.n_splits; i += kCombineThreads) {
+    const float mi = part[i * kPartialStride + 128];
+    const float wi = (mi == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(mi - M2);
+    wsplit[i] = wi;
+    lloc += wi * part[i * kPartialStride + 129];
+  }
+  const float L2 = block_sum(lloc, red);     // its barrier also publishes wsplit
+  float o = 0.0f;
+  if (own) {
+    float o4[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // four loads in flight
+    int64_t i = 0;
+    for (; i + 4 <= a.n_splits; i += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) o4[u] = __builtin_fmaf(wsplit[i + u], part[(i + u) * kPartialStride + c], o4[u]);
+    }
+    for (; i < a.n_splits; ++i) o4[0] = __builtin_fmaf(wsplit[i], part[i * kPartialStride + c], o4[0]);
+    o = (o4[0] + o4[1]) + (o4[2] + o4[3]);
+  }
+
+  // un-rotate the INT2 part (linear, so once after the merge)
+  if (a.rot == 1) o = block_fwht128(o, buf);
+  else if (a.rot == 2) o = block_matvec128(o, a.R + (int64_t)hkv * kD * kD, true, buf);
+
+  // fp16 token weights and values, all in the original basis
   const float M = fmaxf(M2, Mf);
+  float Lf = 0.0f, of = 0.0f;
   if (nf > 0) {
     float ll = 0.0f;
-    for (int64_t t = c; t < nf; t += 128) {
+    for (int64_t t = c; t < nf; t += kCombineThreads) {
       const float p = __builtin_amdgcn_exp2f(pf[t] - M);
       pf[t] = p;
       ll += p;
     }
-    __syncthreads();
-    Lf = block_sum128(ll, red);
-    const int64_t bkv = b * a.Hkv + hkv;
-    const uint16_t *vs_rows = a.sink_v + bkv * a.n_sink * kD + c;
-    const uint16_t *vr_rows = a.res_v + bkv * a.n_res * kD + c;
-    float o4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    int64_t t = 0;
-    for (; t + 4 <= nf; t += 4) {             // four independent loads in flight
+    Lf = block_sum(ll, red);                 // its barrier also publishes the weights
+    float acc[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t tu = t + u;
-        const uint16_t hv = tu < a.n_sink ? vs_rows[tu * kD] : vr_rows[(tu - a.n_sink) * kD];
-        o4[u] = __builtin_fmaf(pf[tu], half_bits_to_float(hv), o4[u]);
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    for (int64_t t0 = 0; t0 < nf; t0 += kFpRows * kFpUnroll) {
+      u32x4_t u[kFpUnroll];
+#pragma unroll
+      for (int k = 0; k < kFpUnroll; ++k) {
+        const int64_t t = t0 + k * kFpRows + rs;
+        const int64_t tt = t < nf ? t : 0;
+        u[k] = *reinterpret_cast<const u32x4_t *>(fp16_row(a.sink_v, a.res_v, bkv, a.n_sink, a.n_res, tt) + 8 * cl);
+      }
+#pragma unroll
+      for (int k = 0; k < kFpUnroll; ++k) {
+        const int64_t t = t0 + k * kFpRows + rs;
+        const float p = t < nf ? pf[t] : 0.0f;
+        const uint32_t w[4] = {u[k].x, u[k].y, u[k].z, u[k].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const half2_t v2 = __builtin_bit_cast(half2_t, w[i]);
+          acc[2 * i] = __builtin_fmaf(p, (float)v2.x, acc[2 * i]);
+          acc[2 * i + 1] = __builtin_fmaf(p, (float)v2.y, acc[2 * i + 1]);
+        }
       }
     }
-    for (; t < nf; ++t) {
-      const uint16_t hv = t < a.n_sink ? vs_rows[t * kD] : vr_rows[(t - a.n_sink) * kD];
-      o4[0] = __builtin_fmaf(pf[t], half_bits_to_float(hv), o4[0]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vred[rs * kD + 8 * cl + i] = acc[i];
+    __syncthreads();
+    if (own) {
+      float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+      for (int r = 0; r < kFpRows; r += 2) {
+        s0 += vred[r * kD + c];
+        s1 += vred[(r + 1) * kD + c];
+      }
+      of = s0 + s1;
     }
-    of = (o4[0] + o4[1]) + (o4[2] + o4[3]);
   }
-  const float wint = (M2 == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(M2 - M);
-  const float res = (o * wint + of) / (L2 * wint + Lf);
-  if (a.out_f32) reinterpret_cast<float *>(a.out)[bh * kD + c] = res;
-  else reinterpret_cast<_Float16 *>(a.out)[bh * kD + c] = (_Float16)res;
+  if (own) {
+    const float wint = (M2 == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(M2 - M);
+    const float res = (o * wint + of) / (L2 * wint + Lf);
+    if (a.out_f32) reinterpret_cast<float *>(a.out)[bh * kD + c] = res;
+    else reinterpret_cast<_Float16 *>(a.out)[bh * kD + c] = (_Float16)res;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -687,7 +747,7 @@ hipError_t launch_decode(const DecodeArgs &d, hipStream_t stream) {
     c.res_k = d.res_k; c.res_v = d.res_v; c.n_res = d.n_res;
     c.out = d.out;
     const size_t lds = (size_t)(d.n_splits + d.n_sink + d.n_res) * sizeof(float);
-    hipLaunchKernelGGL(kv_combine_unrotate, dim3((unsigned)(d.B * d.Hq)), dim3(128), lds, stream, c);
+    hipLaunchKernelGGL(kv_combine_unrotate, dim3((unsigned)(d.B * d.Hq)), dim3(kCombineThreads), lds, stream, c);
     return hipGetLastError();
   }
 }

@@ -292,6 +292,18 @@ def test_decode_fp16_tokens_only():
     _decode_case(cfg, t_begin=4, t_end=4, n_sink=4, n_res=60, name="fp16 only")
 
 
+def test_decode_fp16_tokens_dense_gqa():
+    """Sinks and a ragged residual segment (73 fp16 tokens: more than one
+    batch of rows in flight) with a dense rotation and four query heads per
+    KV head."""
+    cfg = W.small_config(W.config(4), T=700, B=2, Hkv=2, Hq=8, t_new=0)
+    R = W.dense_rotations(cfg)
+    _decode_case(cfg, rot="dense", R=R, t_begin=3, t_end=630, n_sink=3, n_res=70,
+                 name="dense G=4 sinks+res")
+    _decode_case(cfg, rot="dense", R=R, t_begin=0, t_end=700, n_sink=0, n_res=1,
+                 name="dense G=4 one residual token")
+
+
 # ---------------------------------------------------------- end to end
 def test_end_to_end_dense_gqa():
     """Dense rotation, GQA group 4: GPU quantize (MFMA) -> GPU decode, against
