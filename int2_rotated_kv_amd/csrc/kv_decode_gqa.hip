@@ -23,19 +23,40 @@
 // lane (head g = lane/16, token lane%16) holding the four groups.
 //
 // Softmax runs per head on a 16-lane row (lazy reference as for G = 1).  The
-// value weights w = fp16(p * scale_v) go through LDS to a second lane layout
-// (token pair x 16 channels) where the V codes are accumulated for the four
-// heads with v_dot2 on fp16-subnormal code encodings, as for G = 1.
+// weights are rounded once to fp16, p~ = fp16(p), and used everywhere: in
+// the normalizer l = sum p~, the zero-point term and the value product, so
+// the partial is an exact softmax-weighted sum with weights p~.
+//
+// Values, also on the matrix cores (v_mfma_f32_16x16x32_f16), per 8 tokens
+// and 16 code bytes:
+//   A (16 x 32): row (head h, position e of a channel in its byte), column
+//                (token t, position e'): p~[h][t] when e' = e, else 0;
+//   B (32 x 16): column = code byte; (t, e') holds code * s - fp16(1.5 s)
+//                of channel 4 byte + e' (one fp4 -> fp16 conversion and one
+//                packed fp16 FMA per two values).
+// The accumulator row (h, e), column byte b, is channel 4b + e of head h;
+// with the two byte blocks (2n, 2n+1) a lane ends up owning channels
+// 8n .. 8n+7 of its head, summed over every token of the split.  The
+// zero-point term sum p~ (z + fp16(1.5 s)) is accumulated per group in the
+// softmax layout.
 #include "kv_decode_common.h"
 
 namespace kvq {
 
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef float float4v_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef half8_t v8h_t;
 
 constexpr int kMqHeads = 4;          // query heads per wave
 constexpr int kMqWaves = 4;          // waves per workgroup
-constexpr int kMqLdsDwords = 64 * 8 + 4 * 8 * 4 * 4;   // token scales + value weights
+// LDS per wave, in dwords: per-token records, the tile's value codes and the
+// fp16 weights of the four heads.
+constexpr int kMqRecDwords = 12;     // ks, kz (4) | (s_j, -fp16(1.5 s_j)) (4) | z_j + fp16(1.5 s_j) fp32 (4)
+constexpr int kMqRecOff = 0;
+constexpr int kMqCodeOff = kMqRecOff + 64 * kMqRecDwords;          // 64 tokens x 32 bytes
+constexpr int kMqPwOff = kMqCodeOff + 64 * kCodeBytes / 4;          // [head][64 tokens] fp16
+constexpr int kMqLdsDwords = kMqPwOff + kMqHeads * 64 / 2;
 
 // Score slot k <-> channel of the head: slot 32 kb + 8 u + e holds nibble e
 // of unpacked code dword u of group kb (mq_unpack).
@@ -72,18 +93,18 @@ __device__ __forceinline__ int mq_digit(int q, int L) {
 __device__ __forceinline__ constexpr int mq_scale(int L) { return 127 + 15 - 5 * L; }
 
 // Loads of one 64-token tile.  K side: lane (token slot lane%16, group
-// lane/16); tokens 16k + lane%16 for block k.  Token scales: lane = token.
-// V side: lane (pair slot tp = lane/8, code dword lane%8); tokens 16k + tp
-// and 16k + tp + 8.
+// lane/16); tokens 16k + lane%16 for block k.  Token scales and zeros: lane =
+// token.  Value codes: the tile's 2 KB as two 1 KB halves, 16 bytes per lane,
+// staged to LDS in token-major order.
 struct MqTile {
   u32x2_t kc[4];
   u32x2_t ks, kz, vs, vz;
-  uint32_t va[4], vb[4];
+  u32x4_t vc[2];
 };
 
 struct MqState {
-  float m, l, zacc[4], wsum[4];     // K side: the lane's head
-  float acc[kMqHeads][16];          // V side: four heads x the lane's 16 channels
+  float m, l, zacc[4];     // softmax layout: the lane's head (lane / 16)
+  float4v_t o[2];          // value layout: rows (head lane/16, e = 0..3), byte 2 (lane%16) + blk
 };
 
 // Sums / maxima over the 16 lanes of a row.
@@ -101,11 +122,27 @@ __device__ __forceinline__ float row_max16(float v) {
   v = fmaxf(v, row_ror<8>(v));
   return v;
 }
-__device__ __forceinline__ uint32_t row_ror8_u(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x120 + 8, 0xF, 0xF, false);
-}
 __device__ __forceinline__ float lane_read(float v, int l) {
   return bits_as_float((uint32_t)__builtin_amdgcn_readlane((int)float_as_bits(v), l));
+}
+
+// Value operand of code byte block BLK: in y (nibble form, positions
+// (0, 2) in y02 and (1, 3) in y13), byte BLK is token t0's and byte 2 + BLK
+// token t0 + 1's.  Each pair of codes (exact in fp16 after the fp4
+// conversion) becomes code * s - nb with (s, nb) the fp16 halves of sv.
+template <int BLK>
+__device__ __forceinline__ half8_t mq_bvals(uint32_t y02, uint32_t y13, uint32_t sv0, uint32_t sv1) {
+  const half2_t c0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y02, 2.0f, BLK);
+  const half2_t c1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y13, 2.0f, BLK);
+  const half2_t c2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y02, 2.0f, 2 + BLK);
+  const half2_t c3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y13, 2.0f, 2 + BLK);
+  const half2_t p0 = __builtin_bit_cast(half2_t, sv0), p1 = __builtin_bit_cast(half2_t, sv1);
+  const _Float16 s0 = p0.x, n0 = p0.y, s1 = p1.x, n1 = p1.y;
+  const half2_t a = __builtin_elementwise_fma(c0, half2_t{s0, s0}, half2_t{n0, n0});
+  const half2_t b = __builtin_elementwise_fma(c1, half2_t{s0, s0}, half2_t{n0, n0});
+  const half2_t c = __builtin_elementwise_fma(c2, half2_t{s1, s1}, half2_t{n1, n1});
+  const half2_t d = __builtin_elementwise_fma(c3, half2_t{s1, s1}, half2_t{n1, n1});
+  return half8_t{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
 // grid: ceil(total_waves / 4) workgroups of 4 waves; wave index
@@ -116,8 +153,9 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t gw = (int64_t)blockIdx.x * kMqWaves + wave;
   if (gw >= a.total_waves) return;                  // whole wave leaves; no barrier follows
-  uint32_t *tsz = lds_all[wave];                    // [64 tokens][8 dwords]: ks kz vs vz
-  uint32_t *wl = lds_all[wave] + 64 * 8;            // [group][pair slot][block][head] half2
+  uint32_t *rec = lds_all[wave] + kMqRecOff;        // [64 tokens][kMqRecDwords]
+  uint8_t *vcl = reinterpret_cast<uint8_t *>(lds_all[wave] + kMqCodeOff);   // [64 tokens][32 bytes]
+  _Float16 *pw = reinterpret_cast<_Float16 *>(lds_all[wave] + kMqPwOff);     // [head][64 tokens]
   const int quads = (a.G + kMqHeads - 1) / kMqHeads;
   const int quad = (int)(gw % quads);
   const int64_t gs = gw / quads;
@@ -172,14 +210,26 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
     }
   }
 
+  // ---- value side: lane (byte pair n = lane%16, token pair kb = lane/16) of
+  // B; lane (head ha = (lane%16)/4, position e = lane%4, kb) of A.  The A
+  // dword d holds token kb*2 + d/2, positions (d%2, d%2 + 2); v_perm
+  // selectors pick p~ of that token into the half of position e, or zero.
+  const int vn = lane & 15, vkb = lane >> 4;
+  const int ha = vn >> 2, ve = vn & 3;
+  uint32_t selA[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t src = (d >> 1) ? 0x0706u : 0x0504u;       // p~ of token 2 kb + d/2 in P
+    const bool on = (d & 1) == (ve & 1);
+    selA[d] = !on ? 0x0C0C0C0Cu : (ve >> 1) ? ((src << 16) | 0x0C0Cu) : (0x0C0C0000u | src);
+  }
+
   MqState st;
   st.m = kNegInf; st.l = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) { st.zacc[j] = 0.0f; st.wsum[j] = 0.0f; }
-#pragma unroll
-  for (int g = 0; g < kMqHeads; ++g)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) st.acc[g][i] = 0.0f;
+  for (int j = 0; j < 4; ++j) st.zacc[j] = 0.0f;
+  st.o[0] = float4v_t{0.0f, 0.0f, 0.0f, 0.0f};
+  st.o[1] = float4v_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int64_t krow0 = bh * a.kT_cap + a.t_begin;
   const int64_t vrow0 = bh * a.vT_cap + a.t_begin;
@@ -188,13 +238,12 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
   const uint16_t *ks = a.kscales + krow0 * kNGroups, *kz = a.kzeros + krow0 * kNGroups;
   const uint16_t *vs = a.vscales + vrow0 * kNGroups, *vz = a.vzeros + vrow0 * kNGroups;
   const int tk = lane & 15, kgrp = lane >> 4;      // K side
-  const int tp = lane >> 3, c4 = lane & 7;          // V side
 
   // Full tile at row r0 (relative to the head's INT2 start): wave-uniform
   // tile bases plus 32-bit lane offsets.
   const uint32_t o_kc = (uint32_t)(tk * kCodeBytes + 8 * kgrp);
   const uint32_t o_sz = (uint32_t)(lane * kNGroups);
-  const uint32_t o_va = (uint32_t)(tp * kCodeBytes + 4 * c4);
+  const uint32_t o_vc = (uint32_t)(16 * lane);
   auto load_full = [&](int64_t r0) {
     MqTile t;
     const uint8_t *kct = kc + r0 * kCodeBytes, *vct = vc + r0 * kCodeBytes;
@@ -205,11 +254,8 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
     t.kz = *reinterpret_cast<const u32x2_t *>(kz + r0 * kNGroups + o_sz);
     t.vs = *reinterpret_cast<const u32x2_t *>(vs + r0 * kNGroups + o_sz);
     t.vz = *reinterpret_cast<const u32x2_t *>(vz + r0 * kNGroups + o_sz);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      t.va[k] = *reinterpret_cast<const uint32_t *>(vct + o_va + 16 * k * kCodeBytes);
-      t.vb[k] = *reinterpret_cast<const uint32_t *>(vct + o_va + (16 * k + 8) * kCodeBytes);
-    }
+    t.vc[0] = *reinterpret_cast<const u32x4_t *>(vct + o_vc);
+    t.vc[1] = *reinterpret_cast<const u32x4_t *>(vct + 1024 + o_vc);
     return t;
   };
   // Any tile: rows clamped to rmax (the partial last tile).
@@ -230,20 +276,35 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
       t.vz = *reinterpret_cast<const u32x2_t *>(vz + r * kNGroups);
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      int64_t ra = r0 + 16 * k + tp, rb = ra + 8;
-      ra = ra < rmax ? ra : rmax;
-      rb = rb < rmax ? rb : rmax;
-      t.va[k] = *reinterpret_cast<const uint32_t *>(vc + ra * kCodeBytes + 4 * c4);
-      t.vb[k] = *reinterpret_cast<const uint32_t *>(vc + rb * kCodeBytes + 4 * c4);
+    for (int hh = 0; hh < 2; ++hh) {
+      int64_t r = r0 + 32 * hh + (lane >> 1);
+      r = r < rmax ? r : rmax;
+      t.vc[hh] = *reinterpret_cast<const u32x4_t *>(vc + r * kCodeBytes + 16 * (lane & 1));
     }
     return t;
   };
 
   // One tile with nvalid (<= 64) valid tokens.
   auto process = [&](const MqTile &t, int nvalid) {
-    reinterpret_cast<u32x4_t *>(tsz)[2 * lane] = u32x4_t{t.ks.x, t.ks.y, t.kz.x, t.kz.y};
-    reinterpret_cast<u32x4_t *>(tsz)[2 * lane + 1] = u32x4_t{t.vs.x, t.vs.y, t.vz.x, t.vz.y};
+    {
+      // per-token record (lane = token) and the value codes
+      uint32_t *rl = rec + lane * kMqRecDwords;
+      const uint32_t vs0 = t.vs.x, vs1 = t.vs.y, vz0 = t.vz.x, vz1 = t.vz.y;
+      const half2_t s01 = __builtin_bit_cast(half2_t, vs0), s23 = __builtin_bit_cast(half2_t, vs1);
+      const half2_t z01 = __builtin_bit_cast(half2_t, vz0), z23 = __builtin_bit_cast(half2_t, vz1);
+      const half2_t n01 = s01 * half2_t{(_Float16)-1.5f, (_Float16)-1.5f};   // -fp16(1.5 s)
+      const half2_t n23 = s23 * half2_t{(_Float16)-1.5f, (_Float16)-1.5f};
+      const uint32_t un01 = __builtin_bit_cast(uint32_t, n01), un23 = __builtin_bit_cast(uint32_t, n23);
+      reinterpret_cast<u32x4_t *>(rl)[0] = u32x4_t{t.ks.x, t.ks.y, t.kz.x, t.kz.y};
+      reinterpret_cast<u32x4_t *>(rl)[1] =
+          u32x4_t{__builtin_amdgcn_perm(un01, vs0, 0x05040100u), __builtin_amdgcn_perm(un01, vs0, 0x07060302u),
+                  __builtin_amdgcn_perm(un23, vs1, 0x05040100u), __builtin_amdgcn_perm(un23, vs1, 0x07060302u)};
+      reinterpret_cast<float4v_t *>(rl)[2] =
+          float4v_t{(float)z01.x - (float)n01.x, (float)z01.y - (float)n01.y,
+                    (float)z23.x - (float)n23.x, (float)z23.y - (float)n23.y};
+      reinterpret_cast<u32x4_t *>(vcl)[lane] = t.vc[0];
+      reinterpret_cast<u32x4_t *>(vcl)[64 + lane] = t.vc[1];
+    }
     asm volatile("" ::: "memory");     // LDS of one wave is ordered; keep the program order
     // scores of the four 16-token blocks (lane: head gk, token 16k + tk)
     float raw[4];
@@ -255,7 +316,7 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
 #pragma unroll
       for (int L = 0; L < 4; ++L)
         d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[L], Bop, d, 0, 4, 0, mq_scale(L), 0, 127);
-      const u32x4_t kq = reinterpret_cast<const u32x4_t *>(tsz)[2 * tt];
+      const u32x4_t kq = reinterpret_cast<const u32x4_t *>(rec + tt * kMqRecDwords)[0];
       // vector elements go through scalars: a bit_cast of an element
       // expression reads element 0 with this compiler
       const uint32_t kq0 = kq.x, kq1 = kq.y, kq2 = kq.z, kq3 = kq.w;
@@ -289,78 +350,53 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
         ymax = fmaxf(ymax, y[k]);
       }
       const float mnew = fmaxf(st.m, row_max16(ymax));
-      const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);
+      const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);   // the row's head = the lane's value rows
       st.l *= alpha;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) { st.zacc[j] *= alpha; st.wsum[j] *= alpha; }
-#pragma unroll
-      for (int g = 0; g < kMqHeads; ++g) {
-        const float ag = lane_read(alpha, 16 * g);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) st.acc[g][i] *= ag;
-      }
+      for (int j = 0; j < 4; ++j) st.zacc[j] *= alpha;
+      st.o[0] *= alpha;
+      st.o[1] *= alpha;
       st.m = mnew;
 #pragma unroll
       for (int k = 0; k < 4; ++k) x[k] = y[k] - mnew;
     }
-    // weights of the value side: w = fp16(p * scale_v) per group
+    // weights p~ = fp16(p), the normalizer and the zero-point term
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int tt = 16 * k + tk;
-      const float p = __builtin_amdgcn_exp2f(x[k]);          // 0 for masked tokens
-      st.l += p;
-      const u32x4_t vq = reinterpret_cast<const u32x4_t *>(tsz)[2 * tt + 1];
-      const uint32_t vq0 = vq.x, vq1 = vq.y, vq2 = vq.z, vq3 = vq.w;
-      const half2_t vs01 = __builtin_bit_cast(half2_t, vq0), vs23 = __builtin_bit_cast(half2_t, vq1);
-      const half2_t vz01 = __builtin_bit_cast(half2_t, vq2), vz23 = __builtin_bit_cast(half2_t, vq3);
-      const float svj[4] = {(float)vs01.x, (float)vs01.y, (float)vs23.x, (float)vs23.y};
-      const float zvj[4] = {(float)vz01.x, (float)vz01.y, (float)vz23.x, (float)vz23.y};
-      _Float16 wh[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        wh[j] = (_Float16)(p * svj[j]);
-        st.zacc[j] = __builtin_fmaf(p, __builtin_fmaf(1.5f, svj[j], zvj[j]), st.zacc[j]);
-        st.wsum[j] += (float)wh[j];
-      }
-      // token tt + 8's weights from lane tk + 8 of the row; lanes tk < 8
-      // store the pairs (token 16k + tk, token 16k + tk + 8) per group
-      const uint32_t w01 = __builtin_bit_cast(uint32_t, half2_t{wh[0], wh[1]});
-      const uint32_t w23 = __builtin_bit_cast(uint32_t, half2_t{wh[2], wh[3]});
-      const uint32_t o01 = row_ror8_u(w01), o23 = row_ror8_u(w23);
-      if (tk < 8) {
-        const uint32_t pr[4] = {__builtin_amdgcn_perm(o01, w01, 0x05040100u),   // (w0 mine, w0 partner)
-                                __builtin_amdgcn_perm(o01, w01, 0x07060302u),
-                                __builtin_amdgcn_perm(o23, w23, 0x05040100u),
-                                __builtin_amdgcn_perm(o23, w23, 0x07060302u)};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) wl[((j * 8 + tk) * 4 + k) * 4 + kgrp] = pr[j];
-      }
+      const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(x[k]);   // 0 for masked tokens
+      const float pf = (float)ph;
+      st.l += pf;
+      const float4v_t zb = reinterpret_cast<const float4v_t *>(rec + tt * kMqRecDwords)[2];
+      st.zacc[0] = __builtin_fmaf(pf, zb[0], st.zacc[0]);
+      st.zacc[1] = __builtin_fmaf(pf, zb[1], st.zacc[1]);
+      st.zacc[2] = __builtin_fmaf(pf, zb[2], st.zacc[2]);
+      st.zacc[3] = __builtin_fmaf(pf, zb[3], st.zacc[3]);
+      pw[gk * 64 + tt] = ph;
     }
     asm volatile("" ::: "memory");
-    // V side: pairs (16k + tp, 16k + tp + 8) x channels 16 c4 .. 16 c4 + 15
-    const int jv = c4 >> 1;
-    u32x4_t wq[4];
+    // values: 8 blocks of 8 tokens; lane's tokens t0 = 8 tb + 2 kb and t0 + 1
+    const int jv = vn >> 2;                        // group of bytes 2 vn, 2 vn + 1
 #pragma unroll
-    for (int k = 0; k < 4; ++k) wq[k] = reinterpret_cast<const u32x4_t *>(wl)[(jv * 8 + tp) * 4 + k];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t X = __builtin_amdgcn_perm(t.vb[k], t.va[k], 0x05040100u);
-      const uint32_t Y = __builtin_amdgcn_perm(t.vb[k], t.va[k], 0x07060302u);
-      const uint32_t X6 = X >> 6, Y6 = Y >> 6;
-      const uint32_t wk[4] = {wq[k].x, wq[k].y, wq[k].z, wq[k].w};
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        const uint32_t px = x <= 4 ? (X & (0x00030003u << (2 * x))) : (X6 & (0x00030003u << (2 * x - 6)));
-        const uint32_t py = x <= 4 ? (Y & (0x00030003u << (2 * x))) : (Y6 & (0x00030003u << (2 * x - 6)));
-        const half2_t hx = __builtin_bit_cast(half2_t, px);
-        const half2_t hy = __builtin_bit_cast(half2_t, py);
-#pragma unroll
-        for (int g = 0; g < kMqHeads; ++g) {
-          const half2_t wg = __builtin_bit_cast(half2_t, wk[g]);
-          st.acc[g][x] = __builtin_amdgcn_fdot2(hx, wg, st.acc[g][x], false);
-          st.acc[g][8 + x] = __builtin_amdgcn_fdot2(hy, wg, st.acc[g][8 + x], false);
-        }
+    for (int tb = 0; tb < 8; ++tb) {
+      const int t0 = 8 * tb + 2 * vkb;
+      const uint32_t y = (uint32_t)*reinterpret_cast<const uint16_t *>(vcl + t0 * kCodeBytes + 2 * vn) |
+                         ((uint32_t)*reinterpret_cast<const uint16_t *>(vcl + (t0 + 1) * kCodeBytes + 2 * vn) << 16);
+      const uint32_t sv0 = rec[t0 * kMqRecDwords + 4 + jv];
+      const uint32_t sv1 = rec[(t0 + 1) * kMqRecDwords + 4 + jv];
+      const uint32_t P = *reinterpret_cast<const uint32_t *>(pw + ha * 64 + t0);
+      v8h_t Aop;
+      {
+        const uint32_t a0 = __builtin_amdgcn_perm(P, P, selA[0]), a1 = __builtin_amdgcn_perm(P, P, selA[1]);
+        const uint32_t a2 = __builtin_amdgcn_perm(P, P, selA[2]), a3 = __builtin_amdgcn_perm(P, P, selA[3]);
+        const half2_t h0 = __builtin_bit_cast(half2_t, a0), h1 = __builtin_bit_cast(half2_t, a1);
+        const half2_t h2 = __builtin_bit_cast(half2_t, a2), h3 = __builtin_bit_cast(half2_t, a3);
+        Aop = half8_t{h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
       }
+      // nibble bytes: positions (0, 2) and (1, 3) of every code byte
+      const uint32_t y02 = y & 0x33333333u, y13 = (y >> 2) & 0x33333333u;
+      st.o[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aop, mq_bvals<0>(y02, y13, sv0, sv1), st.o[0], 0, 0, 0);
+      st.o[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aop, mq_bvals<1>(y02, y13, sv0, sv1), st.o[1], 0, 0, 0);
     }
     asm volatile("" ::: "memory");
   };
@@ -386,37 +422,24 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
     process(t, rem);
   }
 
-  // ---- reduce and write the partials of the wave's heads
+  // ---- write the partials of the wave's heads.  Softmax rows: head = lane/16;
+  // value lanes: head lane/16, channels 8 (lane%16) .. + 7 (group (lane%16)/4).
   st.l = row_sum16(st.l);
   float corr[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) corr[j] = row_sum16(__builtin_fmaf(-1.5f, st.wsum[j], st.zacc[j]));
-#pragma unroll
-  for (int g = 0; g < kMqHeads; ++g)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float v = st.acc[g][i];
-      v += row_ror<8>(v);                  // pair slots tp and tp ^ 1 (lanes l, l + 8)
-      st.acc[g][i] = sum_xor32(sum_xor16(v));
-    }
-  const int jv = c4 >> 1;
-#pragma unroll
-  for (int g = 0; g < kMqHeads; ++g) {
-    if (kMqHeads * quad + g >= a.G) break;          // wave-uniform
+  for (int j = 0; j < 4; ++j) corr[j] = row_sum16(st.zacc[j]);
+  const int g = lane >> 4;
+  if (kMqHeads * quad + g < a.G) {
     const int hq = hkv * a.G + kMqHeads * quad + g;
     float *dst = a.partials + ((b * a.Hq + hq) * S + split) * kPartialStride;
-    const float c0 = lane_read(corr[0], 16 * g), c1 = lane_read(corr[1], 16 * g);
-    const float c2 = lane_read(corr[2], 16 * g), c3 = lane_read(corr[3], 16 * g);
-    const float cj = jv == 0 ? c0 : jv == 1 ? c1 : jv == 2 ? c2 : c3;
-    if (tp == 0) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        dst[16 * c4 + i] = __builtin_fmaf(st.acc[g][i], chan_unscale(i & 7), cj);
-    }
-    const float mg = lane_read(st.m, 16 * g), lg = lane_read(st.l, 16 * g);
-    if (lane == 0) {
-      dst[128] = mg;
-      dst[129] = lg;
+    const int jo = vn >> 2;
+    const float cj = jo == 0 ? corr[0] : jo == 1 ? corr[1] : jo == 2 ? corr[2] : corr[3];
+    const float4v_t c4v = {cj, cj, cj, cj};
+    reinterpret_cast<float4v_t *>(dst + 8 * vn)[0] = st.o[0] + c4v;
+    reinterpret_cast<float4v_t *>(dst + 8 * vn)[1] = st.o[1] + c4v;
+    if (vn == 0) {
+      dst[128] = st.m;
+      dst[129] = st.l;
     }
   }
 }
