@@ -62,31 +62,63 @@ __device__ __forceinline__ float block_fwht128(float x, float *buf) {
   return y;
 }
 
-// y_c = sum_k x_k M[k][c]  (transpose=false)  or  sum_k x_k M[c][k] (true)
+// y_c = sum_k x_k M[k][c]  (transpose=false)  or  sum_k x_k M[c][k] (true),
+// spread over a block of kMatThreads threads so that every thread has 16
+// independent 16-byte loads in flight:
+//   M[k][c]: thread t owns columns 4 (t%32) .. +3 over rows 16 (t/32) .. +15;
+//   M[c][k]: thread t owns row c = t%128 over columns 64 (t/128) .. +63.
+// Partial sums meet in `red` (8 x 128 floats).
+constexpr int kMatThreads = 256;
 __device__ __forceinline__ float block_matvec128(float x, const float *__restrict__ M,
-                                                 bool transpose, float *buf) {
-  const int c = threadIdx.x;
-  if (c < 128) buf[c] = x;
+                                                 bool transpose, float *buf, float *red) {
+  const int t = threadIdx.x;
+  if (t < 128) buf[t] = x;
   __syncthreads();
-  float acc = 0.0f;
-  if (c < 128 && !transpose) {
-#pragma unroll 8
-    for (int k = 0; k < 128; ++k) acc = __builtin_fmaf(buf[k], M[k * 128 + c], acc);
-  } else if (c < 128) {
-    // thread c walks row c of M with 16-byte loads (a row is 4 cache lines,
-    // reused across the iterations)
-    const float4_t *row = reinterpret_cast<const float4_t *>(M + c * 128);
-#pragma unroll 8
-    for (int k4 = 0; k4 < 32; ++k4) {
-      const float4_t m4 = row[k4];
-      acc = __builtin_fmaf(buf[4 * k4], m4.x, acc);
-      acc = __builtin_fmaf(buf[4 * k4 + 1], m4.y, acc);
-      acc = __builtin_fmaf(buf[4 * k4 + 2], m4.z, acc);
-      acc = __builtin_fmaf(buf[4 * k4 + 3], m4.w, acc);
+  if (!transpose) {
+    const int cg = t & 31, sl = t >> 5;
+    const float4_t *col = reinterpret_cast<const float4_t *>(M + 16 * sl * 128) + cg;
+    float4_t m[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m[i] = col[32 * i];
+    float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float xk = buf[16 * sl + i];
+      acc.x = __builtin_fmaf(xk, m[i].x, acc.x);
+      acc.y = __builtin_fmaf(xk, m[i].y, acc.y);
+      acc.z = __builtin_fmaf(xk, m[i].z, acc.z);
+      acc.w = __builtin_fmaf(xk, m[i].w, acc.w);
+    }
+    reinterpret_cast<float4_t *>(red + 128 * sl)[cg] = acc;
+  } else {
+    const int c = t & 127, hh = t >> 7;
+    const float4_t *row = reinterpret_cast<const float4_t *>(M + c * 128 + 64 * hh);
+    float4_t m[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m[i] = row[i];
+    float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float *xb = buf + 64 * hh + 4 * i;
+      acc0 = __builtin_fmaf(xb[0], m[i].x, acc0);
+      acc1 = __builtin_fmaf(xb[1], m[i].y, acc1);
+      acc0 = __builtin_fmaf(xb[2], m[i].z, acc0);
+      acc1 = __builtin_fmaf(xb[3], m[i].w, acc1);
+    }
+    red[128 * hh + c] = acc0 + acc1;
+  }
+  __syncthreads();
+  float y = 0.0f;
+  if (t < 128) {
+    if (!transpose) {
+#pragma unroll
+      for (int sl = 0; sl < kMatThreads / 32; ++sl) y += red[128 * sl + t];
+    } else {
+      y = red[t] + red[128 + t];
     }
   }
   __syncthreads();
-  return acc;
+  return y;
 }
 
 // ---------------------------------------------------------------------------
@@ -103,22 +135,26 @@ struct PrepArgs {
 };
 
 
-// grid: B*Hq blocks of 128 threads; thread c owns channel c.
-__global__ __launch_bounds__(128) void kv_prep_query(PrepArgs a) {
+// grid: B*Hq blocks of kMatThreads threads; thread c < 128 owns channel c,
+// the others only help with a dense rotation.
+__global__ __launch_bounds__(kMatThreads) void kv_prep_query(PrepArgs a) {
   __shared__ float buf[128];
+  __shared__ float red[8 * 128];
   const int c = threadIdx.x;
+  const bool own = c < kD;
   const int64_t bh = blockIdx.x;            // b*Hq + hq
   const int hq = (int)(bh % a.Hq);
   const int hkv = hq / (a.Hq / a.Hkv);
-  float x = a.q_f32 ? reinterpret_cast<const float *>(a.q)[bh * kD + c]
-                    : (float)reinterpret_cast<const _Float16 *>(a.q)[bh * kD + c];
+  float x = 0.0f;
+  if (own) x = a.q_f32 ? reinterpret_cast<const float *>(a.q)[bh * kD + c]
+                       : (float)reinterpret_cast<const _Float16 *>(a.q)[bh * kD + c];
   if (a.rot == 1) x = block_fwht128(x, buf);
-  else if (a.rot == 2) x = block_matvec128(x, a.R + (int64_t)hkv * kD * kD, false, buf);
+  else if (a.rot == 2) x = block_matvec128(x, a.R + (int64_t)hkv * kD * kD, false, buf, red);
   x *= a.qscale;
 
   // maximum magnitude over the head -> exponent of the fixed point (one step
   // for all four groups, so the step can be applied once per token score)
-  __shared__ float wmax[2];
+  __shared__ float wmax[kMatThreads / 64];
   float amax = fabsf(x);
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
@@ -161,11 +197,11 @@ __global__ __launch_bounds__(128) void kv_prep_query(PrepArgs a) {
     part |= __shfl_xor(part, 2, 32);
     part |= __shfl_xor(part, 4, 32);
     part |= __shfl_xor(part, 8, 32);
-    if (k == 0) base[L * 4 + w * 2 + par] = part;
+    if (own && k == 0) base[L * 4 + w * 2 + par] = part;
   }
   // the fixed-point query itself, for the matrix-core GQA kernel
-  reinterpret_cast<int32_t *>(a.qprep)[bh * kQprepDwordsPerHead + kQprepFixedOffset + c] = qi;
-  if (cg == 0) {
+  if (own) reinterpret_cast<int32_t *>(a.qprep)[bh * kQprepDwordsPerHead + kQprepFixedOffset + c] = qi;
+  if (own && cg == 0) {
     float *fb = reinterpret_cast<float *>(base);
     fb[24] = (float)isum * step;             // sum of the group's fixed-point q
     fb[25] = step;
@@ -479,6 +515,7 @@ struct CombineArgs {
 };
 
 constexpr int kCombineThreads = 256;
+static_assert(kCombineThreads == kMatThreads, "the combine block runs the block-wide matvec");
 constexpr int kCombineWaves = kCombineThreads / 64;
 // fp16 tokens: a 16-lane row per token (8 channels per lane, one 16-byte
 // load), kFpRows tokens per step across the block, kFpUnroll steps whose loads
@@ -606,21 +643,28 @@ __global__ __launch_bounds__(kCombineThreads) void kv_combine_unrotate(CombineAr
     lloc += wi * part[i * kPartialStride + 129];
   }
   const float L2 = block_sum(lloc, red);     // its barrier also publishes wsplit
+  // weighted sum of the partial outputs: thread t takes channel t%128 of the
+  // splits with parity t/128, eight loads in flight
   float o = 0.0f;
-  if (own) {
-    float o4[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // four loads in flight
-    int64_t i = 0;
-    for (; i + 4 <= a.n_splits; i += 4) {
+  {
+    const int ch = c & 127;
+    float o8[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    int64_t i = c >> 7;
+    for (; i + 14 < a.n_splits; i += 16) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) o4[u] = __builtin_fmaf(wsplit[i + u], part[(i + u) * kPartialStride + c], o4[u]);
+      for (int u = 0; u < 8; ++u)
+        o8[u] = __builtin_fmaf(wsplit[i + 2 * u], part[(i + 2 * u) * kPartialStride + ch], o8[u]);
     }
-    for (; i < a.n_splits; ++i) o4[0] = __builtin_fmaf(wsplit[i], part[i * kPartialStride + c], o4[0]);
-    o = (o4[0] + o4[1]) + (o4[2] + o4[3]);
+    for (; i < a.n_splits; i += 2) o8[0] = __builtin_fmaf(wsplit[i], part[i * kPartialStride + ch], o8[0]);
+    vred[c] = ((o8[0] + o8[1]) + (o8[2] + o8[3])) + ((o8[4] + o8[5]) + (o8[6] + o8[7]));
+    __syncthreads();
+    if (own) o = vred[c] + vred[128 + c];
+    __syncthreads();
   }
 
   // un-rotate the INT2 part (linear, so once after the merge)
   if (a.rot == 1) o = block_fwht128(o, buf);
-  else if (a.rot == 2) o = block_matvec128(o, a.R + (int64_t)hkv * kD * kD, true, buf);
+  else if (a.rot == 2) o = block_matvec128(o, a.R + (int64_t)hkv * kD * kD, true, buf, vred);
 
   // fp16 token weights and values, all in the original basis
   const float M = fmaxf(M2, Mf);
@@ -714,7 +758,7 @@ hipError_t launch_decode(const DecodeArgs &d, hipStream_t stream) {
     p.q = d.q; p.q_f32 = d.q_f32; p.Hq = (int)d.Hq; p.Hkv = (int)d.Hkv;
     p.rot = d.rot; p.R = d.R; p.qscale = d.qscale;
     p.qprep = reinterpret_cast<uint8_t *>(d.qprep);
-    hipLaunchKernelGGL(kv_prep_query, dim3((unsigned)(d.B * d.Hq)), dim3(128), 0, stream, p);
+    hipLaunchKernelGGL(kv_prep_query, dim3((unsigned)(d.B * d.Hq)), dim3(kMatThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
