@@ -340,6 +340,73 @@ __device__ __forceinline__ void attn_tile(AttnState<GC> &st, const QueryLimbs<GC
   }
 }
 
+// The query preparation of kv_prep_query done by one wave for its own head
+// (no rotation or the Hadamard rotation): lane l holds channels 2l, 2l+1.
+// The butterfly stages, the fixed-point exponent and the digits are the same
+// operations in the same order as in kv_prep_query, so the results are
+// bitwise identical.  The limb dwords of the four groups (20 each) and the
+// group sums go to `lds` (84 dwords); returns the fixed-point step.
+__device__ __forceinline__ float wave_prep_query(const void *q, bool q_f32, int64_t qoff, int rot,
+                                                 float qscale, uint32_t *lds) {
+  const int lane = threadIdx.x & 63;
+  float x0, x1;
+  if (q_f32) {
+    const float *qp = reinterpret_cast<const float *>(q) + qoff + 2 * lane;
+    x0 = qp[0]; x1 = qp[1];
+  } else {
+    const uint32_t u = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const _Float16 *>(q) + qoff + 2 * lane);
+    const half2_t hq = __builtin_bit_cast(half2_t, u);
+    x0 = (float)hq.x; x1 = (float)hq.y;
+  }
+  if (rot == 1) {
+    float y0 = x0 + x1, y1 = x0 - x1;                      // distance 1: inside the lane
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {                    // distance 2m: lane partner l ^ m
+      const float p0 = __shfl_xor(y0, m, 64), p1 = __shfl_xor(y1, m, 64);
+      const bool hi = (lane & m) != 0;
+      y0 = hi ? p0 - y0 : y0 + p0;
+      y1 = hi ? p1 - y1 : y1 + p1;
+    }
+    x0 = y0 * 0.08838834764831845f;
+    x1 = y1 * 0.08838834764831845f;
+  }
+  x0 *= qscale;
+  x1 *= qscale;
+  float amax = fmaxf(fabsf(x0), fabsf(x1));
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+  int e = 0;
+  (void)frexpf(amax, &e);
+  const bool zero_head = !(amax > 0.0f);
+  const int E = 18 - e;
+  const int qi0 = zero_head ? 0 : (int)__builtin_rintf(ldexpf(x0, E));
+  const int qi1 = zero_head ? 0 : (int)__builtin_rintf(ldexpf(x1, E));
+  const float step = zero_head ? 0.0f : ldexpf(1.0f, -E);
+  int isum = qi0 + qi1;                                   // group j = lane / 16
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) isum += __shfl_xor(isum, m, 64);
+  // limb dword (L, w, parity) of group j: nibble k holds digit L of channel
+  // 32 j + 16 w + 2 k + parity, i.e. lane 16 j + 8 w + k, element `parity`
+  const int j = lane >> 4, w = (lane >> 3) & 1, k = lane & 7;
+  int r0 = qi0, r1 = qi1;
+#pragma unroll
+  for (int L = 4; L >= 0; --L) {
+    const int d0 = ((r0 + 8) & 15) - 8, d1 = ((r1 + 8) & 15) - 8;
+    r0 = (r0 - d0) >> 4;
+    r1 = (r1 - d1) >> 4;
+    uint32_t p0 = ((uint32_t)d0 & 15u) << (4 * k), p1 = ((uint32_t)d1 & 15u) << (4 * k);
+    p0 |= __shfl_xor(p0, 1, 64); p1 |= __shfl_xor(p1, 1, 64);
+    p0 |= __shfl_xor(p0, 2, 64); p1 |= __shfl_xor(p1, 2, 64);
+    p0 |= __shfl_xor(p0, 4, 64); p1 |= __shfl_xor(p1, 4, 64);
+    if (k == 0) {
+      lds[20 * j + 4 * L + 2 * w] = p0;
+      lds[20 * j + 4 * L + 2 * w + 1] = p1;
+    }
+  }
+  if ((lane & 15) == 0) lds[80 + j] = float_as_bits((float)isum);
+  return step;
+}
+
 // WPB waves per workgroup; wave index gw = ((b*Hkv + hkv)*S + split)*G + g,
 // so the G heads of a group (same tiles) are neighbours in one workgroup.
 template <int WPB>
@@ -367,6 +434,18 @@ __global__ __launch_bounds__(64 * WPB) void kv_int2_decode_attn(AttnArgs a) {
   const int64_t mine = split < n_full_tiles ? (n_full_tiles - 1 - split) / S + 1 : 0;
 
   QueryLimbs<GC> q;
+  __shared__ uint32_t qlds[WPB][84];
+  if (a.fused_prep) {                        // one head per KV head: hq = b*Hq + hkv
+    q.qstep[0] = wave_prep_query(a.q, a.q_f32, (b * a.Hq + hkv) * kD, a.rot, a.qscale, qlds[wave]);
+    asm volatile("" ::: "memory");           // LDS of one wave is ordered; keep the program order
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const uint32_t *p = qlds[wave] + 20 * (2 * h + gi);
+#pragma unroll
+      for (int i = 0; i < 20; ++i) q.limb[0][gi][i] = p[i];
+      q.isum[0][gi] = bits_as_float(qlds[wave][80 + 2 * h + gi]);
+    }
+  } else {
 #pragma unroll
   for (int g = 0; g < GC; ++g) {
     const int hq = hkv * a.G + gq + g;
@@ -378,6 +457,7 @@ __global__ __launch_bounds__(64 * WPB) void kv_int2_decode_attn(AttnArgs a) {
       q.isum[g][gi] = bits_as_float(p[26]);
       if (gi == 0) q.qstep[g] = bits_as_float(p[25]);   // the same for every group
     }
+  }
   }
 
   AttnState<GC> st;
@@ -753,7 +833,10 @@ SplitPlan plan_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_int2) {
 
 hipError_t launch_decode(const DecodeArgs &d, hipStream_t stream) {
   const int G = (int)(d.Hq / d.Hkv);
-  {
+  // one query head per KV head without a dense rotation: the attention waves
+  // prepare the query themselves
+  const bool fused_prep = G == 1 && d.rot != 2;
+  if (!fused_prep && d.n_splits > 0) {
     PrepArgs p;
     p.q = d.q; p.q_f32 = d.q_f32; p.Hq = (int)d.Hq; p.Hkv = (int)d.Hkv;
     p.rot = d.rot; p.R = d.R; p.qscale = d.qscale;
@@ -772,6 +855,8 @@ hipError_t launch_decode(const DecodeArgs &d, hipStream_t stream) {
     a.Hkv = (int)d.Hkv; a.Hq = (int)d.Hq; a.G = G;
     a.qprep = reinterpret_cast<const uint32_t *>(d.qprep);
     a.partials = d.partials;
+    a.fused_prep = fused_prep;
+    a.q = d.q; a.q_f32 = d.q_f32; a.rot = d.rot; a.qscale = d.qscale;
     if (G == 1) {
       hipLaunchKernelGGL(kv_int2_decode_attn<4>, dim3((unsigned)((a.total_waves + 3) / 4)), dim3(256), 0,
                          stream, a);

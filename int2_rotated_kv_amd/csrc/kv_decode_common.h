@@ -17,6 +17,12 @@ struct AttnArgs {
   int Hkv, Hq, G;
   const uint32_t *qprep;
   float *partials;
+  // In-wave query preparation (one query head per KV head, Hadamard or no
+  // rotation): the attention waves transform q themselves and qprep is unused.
+  bool fused_prep;
+  const void *q; bool q_f32;
+  int rot;
+  float qscale;
 };
 
 // Reassemble the fp16 subnormal channel factor: code at position x of a
