@@ -173,6 +173,26 @@ def test_quantize_dense_rotation_ties(T, toff):
         _report(f"quantize_dense T={T} {which}", **st)
 
 
+@pytest.mark.parametrize("T,toff", [(100, 5), (64, 0), (1, 63)])
+def test_quantize_hadamard_fp16_ragged_offset(T, toff):
+    """The fp16 Hadamard kernel on a ragged token count (a partial 64-token
+    tile) written at a token offset into a larger cache; slots outside the
+    range keep their sentinel bytes."""
+    cfg = W.small_config(W.config(2), B=2, T=T, Hkv=3, Hq=3)
+    for which in ("K", "V"):
+        x = W.kv_tokens(cfg, which)
+        gp, gs, gz = _gpu_quantize(x, "hadamard", T_cap=T + toff + 5, t_offset=toff, side=which)
+        sl = slice(toff, toff + T)
+        for arr in (gp, gs.view(np.uint8), gz.view(np.uint8)):
+            assert np.all(arr[:, :, :toff] == SENTINEL)
+            assert np.all(arr[:, :, toff + T:] == SENTINEL)
+        gpu = (gp[:, :, sl], gs[:, :, sl], gz[:, :, sl])
+        ora = _oracle_quantize(x, "hadamard")
+        xr = x.permute(0, 2, 1, 3).contiguous().numpy()
+        st = compare_codes_at_ties(xr, rot_matrix("hadamard"), gpu, ora)
+        _report(f"quantize_hadamard ragged T={T} toff={toff} {which}", **st)
+
+
 def test_quantize_dense_config4_slice():
     """Config 4 shapes on the prefill slice (32768 new tokens of one
     sequence, all 8 heads)."""
@@ -302,6 +322,33 @@ def test_decode_fp16_tokens_dense_gqa():
                  name="dense G=4 sinks+res")
     _decode_case(cfg, rot="dense", R=R, t_begin=0, t_end=700, n_sink=0, n_res=1,
                  name="dense G=4 one residual token")
+
+
+def test_decode_max_fp16_tokens():
+    """The largest fp16 segment the library accepts (8192 sink + residual
+    tokens) next to a short INT2 range."""
+    cfg = W.small_config(W.config(5), T=8400, B=1, Hkv=2, Hq=2)
+    _decode_case(cfg, t_begin=4, t_end=208, n_sink=4, n_res=8188, name="8192 fp16 tokens")
+
+
+@pytest.mark.parametrize("Hq", [1, 2])
+def test_decode_many_splits(Hq):
+    """One KV head over a long range: about 500 splits per head, so
+    the merge runs over many partials (one and two query heads)."""
+    cfg = W.small_config(W.config(3), T=131072 + 37, B=1, Hkv=1, Hq=Hq)
+    _decode_case(cfg, name=f"many splits Hq={Hq}")
+
+
+@pytest.mark.parametrize("G", [2, 8])
+def test_decode_gqa_hadamard(G):
+    cfg = W.small_config(W.config(2), T=777, B=2, Hkv=2, Hq=2 * G)
+    _decode_case(cfg, name=f"hadamard G={G}")
+
+
+def test_decode_gqa_fp32_query():
+    """fp32 queries (and fp32 output) with four query heads per KV head."""
+    cfg = W.small_config(W.config(1), T=500, B=2, Hkv=2, Hq=8)
+    _decode_case(cfg, name="fp32 q G=4")
 
 
 # ---------------------------------------------------------- end to end
