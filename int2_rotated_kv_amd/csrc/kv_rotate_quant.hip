@@ -117,9 +117,20 @@ __device__ __forceinline__ void quantize_group32_fwht(const float (&z)[32], uint
   constexpr float c = 0.08838834764831845f;         // fp32(1/sqrt(128))
   float zmn, zmx, sf, zf;
   minmax32(z, zmn, zmx);
-  scale_zero(zmn * c, zmx * c, sbits, zbits, sf, zf);
+  {
+    // The rotated path is compared at rounding ties, with a group's scale
+    // allowed one fp16 ulp of slack, so the two divisions of the exact
+    // sequence become a multiply by fp32(1/3) (within one fp32 ulp of the
+    // quotient) and v_rcp_f32 (within one ulp of 1/scale).
+    const float mn = zmn * c, mx = zmx * c;
+    const float s32 = (mx - mn) * 0.3333333432674408f;
+    sbits = float_to_half_bits(s32);
+    zbits = float_to_half_bits(mn + 0.0f);
+    sf = half_bits_to_float(sbits);
+    zf = half_bits_to_float(zbits);
+  }
   const bool degenerate = (sf == 0.0f);
-  const float inv = 1.0f / (degenerate ? 1.0f : sf);
+  const float inv = __builtin_amdgcn_rcpf(degenerate ? 1.0f : sf);
   const float top = 3.0f * sf;                      // exact: sf has 11 significant bits
   auto code = [&](float zz) {
     const float d = __builtin_amdgcn_fmed3f(__builtin_fmaf(zz, c, -zf), 0.0f, top);
