@@ -131,15 +131,38 @@ __device__ __forceinline__ void quantize_group32_fwht(const float (&z)[32], uint
   }
   const bool degenerate = (sf == 0.0f);
   const float inv = __builtin_amdgcn_rcpf(degenerate ? 1.0f : sf);
-  const float top = 3.0f * sf;                      // exact: sf has 11 significant bits
-  auto code = [&](float zz) {
-    const float d = __builtin_amdgcn_fmed3f(__builtin_fmaf(zz, c, -zf), 0.0f, top);
-    return float_as_bits(__builtin_fmaf(d, inv, kRoundMagic));
-  };
-  const uint32_t a = pack16([&](int i) { return code(z[i]); }, 0u);
-  const uint32_t b = pack16([&](int i) { return code(z[16 + i]); }, 0u);
-  w0 = degenerate ? 0u : a - kPackBias;
-  w1 = degenerate ? 0u : b - kPackBias;
+  // Fast form: x = z * (c/scale) - zero/scale in one FMA, clamped to [0, 3],
+  // then v_cvt_pk_u8_f32 rounds half to even and drops the code into byte
+  // i/4 of word i%4; the four words merge into the 2-bit layout.  Folding
+  // 1/scale into the constants adds an error of about (|y| + |zero|)/scale
+  // ulps, so the wave takes it only while every group has |zero| <= 8 scale
+  // (then the argument is within ~1e-6 of the exact one); otherwise the
+  // sequence below keeps y - zero to one rounding.
+  const float ci = c * inv, nzi = -zf * inv;
+  uint32_t a, b;
+  if (!__builtin_amdgcn_ballot_w64(fabsf(nzi) > 8.0f)) {
+    auto pk = [&](int base) {
+      uint32_t D[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float x = __builtin_amdgcn_fmed3f(__builtin_fmaf(z[base + i], ci, nzi), 0.0f, 3.0f);
+        D[i & 3] = __builtin_amdgcn_cvt_pk_u8_f32(x, (uint32_t)(i >> 2), D[i & 3]);
+      }
+      return D[0] | (D[1] << 2) | (D[2] << 4) | (D[3] << 6);
+    };
+    a = pk(0);
+    b = pk(16);
+  } else {
+    const float top = 3.0f * sf;                      // exact: sf has 11 significant bits
+    auto code = [&](float zz) {
+      const float d = __builtin_amdgcn_fmed3f(__builtin_fmaf(zz, c, -zf), 0.0f, top);
+      return float_as_bits(__builtin_fmaf(d, inv, kRoundMagic));
+    };
+    a = pack16([&](int i) { return code(z[i]); }, 0u) - kPackBias;
+    b = pack16([&](int i) { return code(z[16 + i]); }, 0u) - kPackBias;
+  }
+  w0 = degenerate ? 0u : a;
+  w1 = degenerate ? 0u : b;
 }
 
 // lo + hi and lo - hi of the two fp16 halves of a dword, in fp32 with one

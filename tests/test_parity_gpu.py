@@ -193,6 +193,29 @@ def test_quantize_hadamard_fp16_ragged_offset(T, toff):
         _report(f"quantize_hadamard ragged T={T} toff={toff} {which}", **st)
 
 
+def test_quantize_hadamard_offset_groups():
+    """Rows whose rotated groups sit far from zero relative to their spread
+    (zero about 12 scales away in half of the groups), so waves take both
+    forms of the rotated quantizer (the one that folds 1/scale into the
+    first FMA is only used while every group has |zero| <= 8 scale)."""
+    rng = np.random.default_rng(11)
+    B, T, H, d = 2, 130, 2, 128
+    y = 0.3 * rng.standard_normal((B, T, H, d))
+    off = np.zeros(d)
+    off[0:32] = 6.0
+    off[64:96] = -6.0
+    y[:, 1::2] += off                                  # odd tokens: offset groups 0 and 2
+    Hn = rot_matrix("hadamard")                        # symmetric and orthogonal: its own inverse
+    x = torch.from_numpy((y @ Hn).astype(np.float16))
+    gpu = _gpu_quantize(x, "hadamard")
+    ora = _oracle_quantize(x, "hadamard")
+    xr = x.permute(0, 2, 1, 3).contiguous().numpy()
+    zs = ora[2].astype(np.float64) / np.maximum(ora[1].astype(np.float64), 1e-30)
+    assert (np.abs(zs) > 8).any() and (np.abs(zs) <= 8).any()
+    st = compare_codes_at_ties(xr, Hn, gpu, ora)
+    _report("quantize_hadamard offset groups", **st)
+
+
 def test_quantize_dense_config4_slice():
     """Config 4 shapes on the prefill slice (32768 new tokens of one
     sequence, all 8 heads)."""
