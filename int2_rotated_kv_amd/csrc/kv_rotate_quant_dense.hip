@@ -108,21 +108,38 @@ __device__ __forceinline__ void dense_group_codes(const float16_t &y, uint32_t &
   }
   mn = pair_min(mn);
   mx = pair_max(mx);
-  const float s32 = (mx - mn) / 3.0f;                         // correctly rounded
+  // The rotated path is compared at rounding ties with one fp16 ulp of slack
+  // on a group's scale, so s = range * fp32(1/3) and 1/scale = v_rcp_f32.
+  const float s32 = (mx - mn) * 0.3333333432674408f;
   sbits = float_to_half_bits(s32);
   zbits = float_to_half_bits(mn + 0.0f);
   const float sf = half_bits_to_float(sbits);
   const float zf = half_bits_to_float(zbits);
   // scale 0: every code is 0 (inv = 1 and the clamp to [0, 0] give that)
-  const float inv = 1.0f / (sf == 0.0f ? 1.0f : sf);
-  const float top = 3.0f * sf;
-  // code = rint((y - zero) / scale) clamped to [0, 3]: clamp the difference to
-  // [0, 3 scale], then one fma with the magic constant rounds to an integer
-  auto code = [&](int r) {
-    const float d = __builtin_amdgcn_fmed3f(y[r] - zf, 0.0f, top);
-    return float_as_bits(__builtin_fmaf(d, inv, kDenseRoundMagic));
-  };
-  const uint32_t mine = dense_pack16(code, 0u) - kDensePackBias;   // byte q = group byte 2q + half
+  const float inv = __builtin_amdgcn_rcpf(sf == 0.0f ? 1.0f : sf);
+  const float nzi = -zf * inv;
+  // Three instructions per code while every group of the wave has
+  // |zero| <= 8 scale: x = y/scale - zero/scale in one FMA, clamp to [0, 3],
+  // v_cvt_pk_u8_f32 (round half to even) into byte r/4 of word r%4; the
+  // words merge into the 2-bit layout.  Otherwise (or for a zero scale) the
+  // sequence below keeps y - zero to one rounding.
+  uint32_t mine;
+  if (!__builtin_amdgcn_ballot_w64(fabsf(nzi) > 8.0f || sf == 0.0f)) {
+    uint32_t D[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float x = __builtin_amdgcn_fmed3f(__builtin_fmaf(y[r], inv, nzi), 0.0f, 3.0f);
+      D[r & 3] = __builtin_amdgcn_cvt_pk_u8_f32(x, (uint32_t)(r >> 2), D[r & 3]);
+    }
+    mine = D[0] | (D[1] << 2) | (D[2] << 4) | (D[3] << 6);
+  } else {
+    const float top = 3.0f * sf;
+    auto code = [&](int r) {
+      const float d = __builtin_amdgcn_fmed3f(y[r] - zf, 0.0f, top);
+      return float_as_bits(__builtin_fmaf(d, inv, kDenseRoundMagic));
+    };
+    mine = dense_pack16(code, 0u) - kDensePackBias;   // byte q = group byte 2q + half
+  }
   const auto ex = __builtin_amdgcn_permlane32_swap(mine, mine, false, false);
   const uint32_t e = ex[0], o = ex[1];          // bytes of the lower / upper half
   w0 = __builtin_amdgcn_perm(o, e, 0x05010400u);   // e0 o0 e1 o1

@@ -193,7 +193,8 @@ def test_quantize_hadamard_fp16_ragged_offset(T, toff):
         _report(f"quantize_hadamard ragged T={T} toff={toff} {which}", **st)
 
 
-def test_quantize_hadamard_offset_groups():
+@pytest.mark.parametrize("rot", ["hadamard", "dense"])
+def test_quantize_offset_groups(rot):
     """Rows whose rotated groups sit far from zero relative to their spread
     (zero about 12 scales away in half of the groups), so waves take both
     forms of the rotated quantizer (the one that folds 1/scale into the
@@ -205,15 +206,24 @@ def test_quantize_hadamard_offset_groups():
     off[0:32] = 6.0
     off[64:96] = -6.0
     y[:, 1::2] += off                                  # odd tokens: offset groups 0 and 2
-    Hn = rot_matrix("hadamard")                        # symmetric and orthogonal: its own inverse
-    x = torch.from_numpy((y @ Hn).astype(np.float16))
-    gpu = _gpu_quantize(x, "hadamard")
-    ora = _oracle_quantize(x, "hadamard")
+    if rot == "hadamard":
+        R = None
+        Rh = [rot_matrix("hadamard")] * H              # symmetric and orthogonal: its own inverse
+    else:
+        R = W.dense_rotations(W.small_config(W.config(4), B=B, T=T, Hkv=H, Hq=H, t_new=0))
+        Rh = [R[h].astype(np.float64) for h in range(H)]
+    # rows x with x R = y (R orthogonal: x = y R^T)
+    x = np.stack([y[:, :, h] @ Rh[h].T for h in range(H)], axis=2)
+    x = torch.from_numpy(x.astype(np.float16))
+    gpu = _gpu_quantize(x, rot, R=R)
+    ora = _oracle_quantize(x, rot, R)
     xr = x.permute(0, 2, 1, 3).contiguous().numpy()
     zs = ora[2].astype(np.float64) / np.maximum(ora[1].astype(np.float64), 1e-30)
     assert (np.abs(zs) > 8).any() and (np.abs(zs) <= 8).any()
-    st = compare_codes_at_ties(xr, Hn, gpu, ora)
-    _report("quantize_hadamard offset groups", **st)
+    for h in range(H):
+        st = compare_codes_at_ties(xr[:, h], Rh[h] if rot == "dense" else rot_matrix("hadamard"),
+                                   tuple(a[:, h] for a in gpu), tuple(a[:, h] for a in ora))
+        _report(f"quantize offset groups {rot} h={h}", **st)
 
 
 def test_quantize_dense_config4_slice():
