@@ -430,8 +430,8 @@ __global__ __launch_bounds__(64 * WPB) void kv_int2_decode_attn(AttnArgs a) {
   // of a head stream through adjacent tiles together rather than each
   // through a region of its own.
   const int64_t S = a.n_splits;
-  const int64_t n_full_tiles = a.n_int2 >> 6;
-  const int64_t mine = split < n_full_tiles ? (n_full_tiles - 1 - split) / S + 1 : 0;
+  const HeadTiles ht(a.n_int2, a.skip, split, S);
+  const int64_t mine = ht.mine;
 
   QueryLimbs<GC> q;
   __shared__ uint32_t qlds[WPB][84];
@@ -471,8 +471,8 @@ __global__ __launch_bounds__(64 * WPB) void kv_int2_decode_attn(AttnArgs a) {
 
   // Row r of the head's INT2 range: codes at *c + r*32 bytes, scales/zeros
   // at *s + r*4 halves.  Lane offsets are 32-bit; tile bases are wave-uniform.
-  const int64_t krow0 = bh * a.kT_cap + a.t_begin;
-  const int64_t vrow0 = bh * a.vT_cap + a.t_begin;
+  const int64_t krow0 = bh * a.kT_cap + a.t_begin - a.skip;   // row 0 of the shifted grid
+  const int64_t vrow0 = bh * a.vT_cap + a.t_begin - a.skip;
   const uint8_t *kc = a.kcodes + krow0 * kCodeBytes;
   const uint8_t *vc = a.vcodes + vrow0 * kCodeBytes;
   const uint16_t *ks = a.kscales + krow0 * kNGroups, *kz = a.kzeros + krow0 * kNGroups;
@@ -507,7 +507,7 @@ __global__ __launch_bounds__(64 * WPB) void kv_int2_decode_attn(AttnArgs a) {
   // computed the loads of tiles i+1 and i+2 are in flight.  A prefetch past
   // the wave's last tile is clamped to it (a re-read of valid rows, unused).
   if (mine > 0) {
-    auto at = [&](int64_t i) { return 64 * (split + (i < mine - 1 ? i : mine - 1) * S); };
+    auto at = [&](int64_t i) { return ht.full_row(i, split, S); };
     TileRegs r0 = load_tile(at(0)), r1 = load_tile(at(1)), r2;
     int64_t i = 0;
     for (; i + 3 <= mine; i += 3) {
@@ -521,11 +521,13 @@ __global__ __launch_bounds__(64 * WPB) void kv_int2_decode_attn(AttnArgs a) {
     if (i < mine) attn_tile<GC>(st, q, r0, true, true);
     if (i + 1 < mine) attn_tile<GC>(st, q, r1, true, true);
   }
-  const int64_t rem = a.n_int2 & 63;
-  if (rem != 0 && n_full_tiles % S == split) {   // the partial last tile: clamp rows into it
-    const int64_t t0 = 64 * n_full_tiles;
-    const bool va = ts < rem, vb = 32 + ts < rem;
-    const int64_t ra = t0 + (va ? ts : 0), rb = t0 + (vb ? 32 + ts : 0);
+  // partial tiles: masked rows are loaded from the tile's first valid row
+  auto masked_tile = [&](int64_t t) {
+    const int64_t base = 64 * t;
+    const int64_t lo = a.skip > base ? a.skip - base : 0;
+    const int64_t hi = ht.n_tok - base < 64 ? ht.n_tok - base : 64;
+    const bool va = ts >= lo && ts < hi, vb = 32 + ts >= lo && 32 + ts < hi;
+    const int64_t ra = base + (va ? ts : lo), rb = base + (vb ? 32 + ts : lo);
     TileRegs r;
     r.kA = *reinterpret_cast<const u32x4_t *>(kc + ra * kCodeBytes + 16 * h);
     r.kB = *reinterpret_cast<const u32x4_t *>(kc + rb * kCodeBytes + 16 * h);
@@ -540,6 +542,12 @@ __global__ __launch_bounds__(64 * WPB) void kv_int2_decode_attn(AttnArgs a) {
     r.vsB = *reinterpret_cast<const uint32_t *>(vs + rb * kNGroups + 2 * h);
     r.vzB = *reinterpret_cast<const uint32_t *>(vz + rb * kNGroups + 2 * h);
     attn_tile<GC>(st, q, r, va, vb);
+  };
+  {
+    int64_t p0, p1;
+    ht.partial(a.skip, split, S, p0, p1);
+    if (p0 >= 0) masked_tile(p0);
+    if (p1 >= 0) masked_tile(p1);
   }
 
   // reduce over the 32 token slots (lanes sharing h), then write the partial
@@ -856,6 +864,9 @@ hipError_t launch_decode(const DecodeArgs &d, hipStream_t stream) {
     a.qprep = reinterpret_cast<const uint32_t *>(d.qprep);
     a.partials = d.partials;
     a.fused_prep = fused_prep;
+    // shift the tile grid onto 16-row boundaries when both caches keep rows
+    // of a head on them
+    a.skip = (d.kT_cap % 16 == 0 && d.vT_cap % 16 == 0) ? (int)(d.t_begin % 16) : 0;
     a.q = d.q; a.q_f32 = d.q_f32; a.rot = d.rot; a.qscale = d.qscale;
     if (G == 1) {
       hipLaunchKernelGGL(kv_int2_decode_attn<4>, dim3((unsigned)((a.total_waves + 3) / 4)), dim3(256), 0,

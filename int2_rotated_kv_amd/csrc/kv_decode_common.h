@@ -23,6 +23,8 @@ struct AttnArgs {
   const void *q; bool q_f32;
   int rot;
   float qscale;
+  // Tile grid shift: tiles start `skip` rows before t_begin (0 <= skip < 16).
+  int skip;
 };
 
 // Reassemble the fp16 subnormal channel factor: code at position x of a
@@ -64,10 +66,35 @@ __device__ __forceinline__ float hi_half(uint32_t w) { return half_bits_to_float
 // A wave's tiles: the head's INT2 tokens are cut into 64-token tiles and
 // wave `split` of S takes tiles split, split + S, ...; mine = how many full
 // tiles that is.
-__device__ __forceinline__ int64_t tiles_of_split(int64_t n_int2, int64_t split, int64_t S) {
-  const int64_t n_full = n_int2 >> 6;
-  return split < n_full ? (n_full - 1 - split) / S + 1 : 0;
-}
+// The tiles of a head.  The 64-token tile grid starts `skip` rows before
+// the INT2 range, chosen on the host so that tile starts sit on 16-row
+// boundaries of the cache arrays: then every 512-byte run of a tile's scales
+// or zeros is four whole 128-byte lines.  In the shifted row coordinates the
+// valid rows are [skip, n_tok).  Tile t is full when none of its rows is
+// masked; wave `split` of S owns tiles split, split + S, ...  Its full tiles
+// are split + (i0 + i) S for i < mine; the partial tiles (the first one when
+// skip > 0, the last one when n_tok is not a multiple of 64) are processed
+// with masks by the wave that owns them.
+struct HeadTiles {
+  int64_t n_tok, n_full_end, i0, mine;
+  __device__ __forceinline__ HeadTiles(int64_t n_int2, int skip, int64_t split, int64_t S) {
+    n_tok = n_int2 + skip;
+    n_full_end = n_tok >> 6;
+    i0 = (skip > 0 && split == 0) ? 1 : 0;
+    const int64_t t_first = split + i0 * S;
+    mine = t_first < n_full_end ? (n_full_end - 1 - t_first) / S + 1 : 0;
+  }
+  // first row of the wave's i-th full tile (i clamped to the last one)
+  __device__ __forceinline__ int64_t full_row(int64_t i, int64_t split, int64_t S) const {
+    return 64 * (split + (i0 + (i < mine - 1 ? i : mine - 1)) * S);
+  }
+  // the partial tiles this wave owns: t0 (first) and t1 (last), or -1
+  __device__ __forceinline__ void partial(int skip, int64_t split, int64_t S, int64_t &t0, int64_t &t1) const {
+    t0 = (skip > 0 && split == 0) ? 0 : -1;
+    t1 = ((n_tok & 63) != 0 && n_full_end % S == split) ? n_full_end : -1;
+    if (t1 == t0) t1 = -1;                         // one tile that is both
+  }
+};
 
 hipError_t launch_attn_gqa(const AttnArgs &a, hipStream_t stream);
 

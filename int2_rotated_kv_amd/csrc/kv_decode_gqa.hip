@@ -231,8 +231,8 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
   st.o[0] = float4v_t{0.0f, 0.0f, 0.0f, 0.0f};
   st.o[1] = float4v_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int64_t krow0 = bh * a.kT_cap + a.t_begin;
-  const int64_t vrow0 = bh * a.vT_cap + a.t_begin;
+  const int64_t krow0 = bh * a.kT_cap + a.t_begin - a.skip;   // row 0 of the shifted grid
+  const int64_t vrow0 = bh * a.vT_cap + a.t_begin - a.skip;
   const uint8_t *kc = a.kcodes + krow0 * kCodeBytes;
   const uint8_t *vc = a.vcodes + vrow0 * kCodeBytes;
   const uint16_t *ks = a.kscales + krow0 * kNGroups, *kz = a.kzeros + krow0 * kNGroups;
@@ -258,18 +258,17 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
     t.vc[1] = *reinterpret_cast<const u32x4_t *>(vct + 1024 + o_vc);
     return t;
   };
-  // Any tile: rows clamped to rmax (the partial last tile).
-  auto load_tile = [&](int64_t r0, int64_t rmax) {
+  // Any tile: rows clamped into [rmin, rmax] (a partial tile).
+  auto load_tile = [&](int64_t r0, int64_t rmin, int64_t rmax) {
+    auto clampr = [&](int64_t r) { return r < rmax ? (r > rmin ? r : rmin) : rmax; };
     MqTile t;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      int64_t r = r0 + 16 * k + tk;
-      r = r < rmax ? r : rmax;
+      const int64_t r = clampr(r0 + 16 * k + tk);
       t.kc[k] = *reinterpret_cast<const u32x2_t *>(kc + r * kCodeBytes + 8 * kgrp);
     }
     {
-      int64_t r = r0 + lane;
-      r = r < rmax ? r : rmax;
+      const int64_t r = clampr(r0 + lane);
       t.ks = *reinterpret_cast<const u32x2_t *>(ks + r * kNGroups);
       t.kz = *reinterpret_cast<const u32x2_t *>(kz + r * kNGroups);
       t.vs = *reinterpret_cast<const u32x2_t *>(vs + r * kNGroups);
@@ -277,15 +276,14 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
     }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      int64_t r = r0 + 32 * hh + (lane >> 1);
-      r = r < rmax ? r : rmax;
+      const int64_t r = clampr(r0 + 32 * hh + (lane >> 1));
       t.vc[hh] = *reinterpret_cast<const u32x4_t *>(vc + r * kCodeBytes + 16 * (lane & 1));
     }
     return t;
   };
 
-  // One tile with nvalid (<= 64) valid tokens.
-  auto process = [&](const MqTile &t, int nvalid) {
+  // One tile whose tokens [lo, hi) are valid.
+  auto process = [&](const MqTile &t, int lo, int hi) {
     {
       // per-token record (lane = token) and the value codes
       uint32_t *rl = rec + lane * kMqRecDwords;
@@ -338,7 +336,7 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
     float xmax = kNegInf;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      x[k] = (16 * k + tk < nvalid) ? __builtin_fmaf(qstep, raw[k], -st.m) : kNegInf;
+      x[k] = (16 * k + tk >= lo && 16 * k + tk < hi) ? __builtin_fmaf(qstep, raw[k], -st.m) : kNegInf;
       xmax = fmaxf(xmax, x[k]);
     }
     if (__builtin_amdgcn_ballot_w64(xmax > kSlack)) {              // wave-uniform
@@ -346,7 +344,7 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
       float ymax = kNegInf;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        y[k] = (16 * k + tk < nvalid) ? qstep * raw[k] : kNegInf;
+        y[k] = (16 * k + tk >= lo && 16 * k + tk < hi) ? qstep * raw[k] : kNegInf;
         ymax = fmaxf(ymax, y[k]);
       }
       const float mnew = fmaxf(st.m, row_max16(ymax));
@@ -402,24 +400,32 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
   };
 
   // this wave's full tiles, loads one tile ahead
-  const int64_t mine = tiles_of_split(a.n_int2, split, S);
+  const HeadTiles ht(a.n_int2, a.skip, split, S);
+  const int64_t mine = ht.mine;
   if (mine > 0) {
-    auto row_of = [&](int64_t i) { return 64 * (split + (i < mine - 1 ? i : mine - 1) * S); };
+    auto row_of = [&](int64_t i) { return ht.full_row(i, split, S); };
     MqTile t0 = load_full(row_of(0)), t1;
     int64_t i = 0;
     for (; i + 2 <= mine; i += 2) {
       t1 = load_full(row_of(i + 1));
-      process(t0, 64);
+      process(t0, 0, 64);
       t0 = load_full(row_of(i + 2));
-      process(t1, 64);
+      process(t1, 0, 64);
     }
-    if (i < mine) process(t0, 64);
+    if (i < mine) process(t0, 0, 64);
   }
-  const int64_t n_full = a.n_int2 >> 6;
-  const int rem = (int)(a.n_int2 & 63);
-  if (rem != 0 && n_full % S == split) {
-    const MqTile t = load_tile(64 * n_full, a.n_int2 - 1);
-    process(t, rem);
+  {
+    // partial tiles: masked rows are loaded from the nearest valid row
+    int64_t p[2];
+    ht.partial(a.skip, split, S, p[0], p[1]);
+    for (int e = 0; e < 2; ++e) {
+      if (p[e] < 0) continue;
+      const int64_t base = 64 * p[e];
+      const int lo = a.skip > base ? (int)(a.skip - base) : 0;
+      const int hi = ht.n_tok - base < 64 ? (int)(ht.n_tok - base) : 64;
+      const MqTile t = load_tile(base, base + lo, base + hi - 1);
+      process(t, lo, hi);
+    }
   }
 
   // ---- write the partials of the wave's heads.  Softmax rows: head = lane/16;
