@@ -208,10 +208,13 @@ def main():
               "units_per_launch": B * n_q * H, "avg_ms": round(q_ms, 4)}
     d_kernel, d_src = (("kv_int2_decode_attn", "kv_decode.hip") if cfg.G == 1
                        else ("kv_int2_decode_attn_gqa", "kv_decode_gqa.hip"))
+    # the query preparation is its own launch only for a dense rotation or
+    # grouped-query attention; otherwise the attention waves do it
+    prep_kernel = cfg.G > 1 or rot == "dense"
     roof_d = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
               "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
               "traffic": traffic_from_profile(d_kernel, cfg.name, os.path.join(csrc, d_src)),
-              "kernel": f"decode call (kv_prep_query + {d_kernel} + kv_combine_unrotate)",
+              "kernel": f"decode call ({'kv_prep_query + ' if prep_kernel else ''}{d_kernel} + kv_combine_unrotate)",
               "algorithmic_bytes_per_launch": d_bytes,
               "bytes_per_unit": DECODE_BYTES_PER_TOKEN_HEAD, "unit_of_work": "(INT2 token, kv head)",
               "units_per_launch": B * n_int2 * H, "avg_ms": round(d_ms, 4)}
