@@ -7,11 +7,13 @@
 // KV-Cache Quantization", woor.ai page, "What You Need to Know" and "Key
 // Details"); sinks stay unquantized (RotateKV abstract, item (iii)).
 //
-// Three launches on the caller's stream:
+// Launches on the caller's stream:
 //   1. kv_prep_query     per (b, query head): q' = q R (FWHT or dense), scaled
 //                        by softmax_scale*log2(e), turned into a per-group
 //                        19-bit fixed-point vector split into five signed
-//                        4-bit limbs.
+//                        4-bit limbs.  Only for a dense rotation or grouped-
+//                        query attention: otherwise every attention wave
+//                        does the same steps for its head (wave_prep_query).
 //   2. kv_int2_decode_attn  (one query head per KV head) one wave per
 //                        (b, head, split): flash-decoding over every S-th
 //                        64-token tile of the head with an online softmax.

@@ -357,6 +357,23 @@ def test_decode_fp16_tokens_dense_gqa():
                  name="dense G=4 one residual token")
 
 
+@pytest.mark.parametrize("Hq,t_begin,t_end", [(2, 9, 60), (2, 5, 1000), (8, 7, 40), (8, 5, 1000),
+                                             (8, 16, 1000), (2, 13, 77)])
+def test_decode_shifted_tile_grid(Hq, t_begin, t_end):
+    """A cache whose T_cap is a multiple of 16 with an INT2 range starting
+    off a 16-row boundary: the tile grid starts t_begin mod 16 rows early and
+    the first tile is masked below t_begin (for one and four query heads per
+    KV head, a range inside a single tile masked at both ends, and ranges over
+    many tiles)."""
+    cfg = W.small_config(W.config(4), T=1024, B=2, Hkv=2, Hq=Hq, t_new=0)
+    R = W.dense_rotations(cfg)
+    _decode_case(cfg, rot="dense", R=R, t_begin=t_begin, t_end=t_end, n_sink=0, n_res=0,
+                 name=f"shifted grid Hq={Hq} [{t_begin},{t_end})")
+    cfg2 = W.small_config(W.config(2), T=1024, B=1, Hkv=2, Hq=Hq)
+    _decode_case(cfg2, t_begin=t_begin, t_end=t_end, n_sink=0, n_res=0,
+                 name=f"shifted grid hadamard Hq={Hq} [{t_begin},{t_end})")
+
+
 def test_decode_max_fp16_tokens():
     """The largest fp16 segment the library accepts (8192 sink + residual
     tokens) next to a short INT2 range."""
