@@ -11,9 +11,10 @@ group 32):
      sink / residual tokens when the workload has them).
 The quantize and the decode calls are timed separately: the K quantize
 calls run back to back, then the K decode calls (each call bracketed by
-events).  Each timed phase follows about 30 ms of untimed calls of the same
-kind, so it is measured in its own steady state.  ms_per_step is the wall
-time of the two timed phases per step.  Inputs are generated on the GPU before timing (seeded, synthetic)
+events, with an untimed 1 GiB read before each call to evict the caches).
+Each timed phase follows about 30 ms of untimed calls of the same kind, so
+it is measured in its own steady state.  ms_per_step is the time of one
+timed quantize call plus one timed decode call (mean over the steps).  Inputs are generated on the GPU before timing (seeded, synthetic)
 and are resident in HBM when the timed region starts.
 
 Prints ONE JSON line.  `value` is the decode attention's effective HBM
@@ -57,6 +58,7 @@ def parse():
 
 
 PREROLL_MS = 30.0        # untimed calls before each timed phase
+FLUSH_BYTES = 1 << 30    # read between timed calls
 
 
 def file_sha(path):
@@ -187,25 +189,34 @@ def main():
             fn()
         torch.cuda.synchronize()
 
+    # Between timed calls a 1 GiB read evicts the caches (the 256 MB MALL
+    # included), so no call is served by data the previous one left behind.
+    # A read: a copy would leave dirty lines whose write-back lands in the
+    # next call (measured ~12% on the decode).
+    flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    flush_out = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def flush():
+        torch.sum(flush_buf, dim=0, out=flush_out)
+
     def phase(fn, n):
         preroll(fn)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(n)]
-        t0 = time.perf_counter()
         for a, b in evs:
+            flush()
             a.record(stream)
             fn()
             b.record(stream)
         torch.cuda.synchronize()
-        return evs, time.perf_counter() - t0
+        return evs
 
     torch.cuda.synchronize()
-    q_evs, q_wall = phase(quant, args.steps)
-    d_evs, d_wall = phase(decode, args.steps)
-    wall = q_wall + d_wall
+    q_evs = phase(quant, args.steps)
+    d_evs = phase(decode, args.steps)
     quant_ms = np.array([a.elapsed_time(b) for a, b in q_evs])
     dec_ms = np.array([a.elapsed_time(b) for a, b in d_evs])
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step = float(quant_ms.sum() + dec_ms.sum()) / args.steps   # the timed calls, flushes excluded
 
     n_q, n_int2, n_f16 = q1 - q0, te - tb, cfg.n_sink + cfg.n_res
     r_bytes = H * d * d * 4 if rot == "dense" else 0
