@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--perm", action="store_true",
+                   help="reordered Hadamard rotation (each head's channels sorted by outlier "
+                        "magnitude ahead of the transform) on a Hadamard workload")
     p.add_argument("--config", type=int, default=3, choices=(3, 4, 5),
                    help="workload id (3 = throughput case, 4 = GQA dense rotation, 5 = sinks)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -134,13 +137,21 @@ def main():
     dev = "cuda"
     B, T, H, d = cfg.B, cfg.T, cfg.Hkv, cfg.d
     rot = cfg.rot
-    print(f"[bench] generating {cfg.name} on the GPU", file=sys.stderr, flush=True)
+    workload = cfg.name
+    if args.perm:
+        if rot != "hadamard":
+            sys.exit("--perm applies to the Hadamard workloads (--config 3 or 5)")
+        rot, workload = "perm", cfg.name + "_perm"
+    print(f"[bench] generating {workload} on the GPU", file=sys.stderr, flush=True)
     t0 = time.time()
     K = W.kv_tokens(cfg, "K", device=dev)
     V = W.kv_tokens(cfg, "V", device=dev)
     q = W.queries(cfg, device=dev)
-    R = (torch.as_tensor(W.dense_rotations(cfg), device=dev).contiguous()
-         if rot == "dense" else None)
+    R = None
+    if rot == "dense":
+        R = torch.as_tensor(W.dense_rotations(cfg), device=dev).contiguous()
+    elif rot == "perm":
+        R = torch.as_tensor(W.channel_orders(cfg), dtype=torch.int32, device=dev).contiguous()
     ck = kvq.Int2Cache.empty(B, H, T, device=dev)
     cv = kvq.Int2Cache.empty(B, H, T, device=dev)
     tb, te = cfg.int2_range                    # INT2 tokens of the cache
@@ -219,7 +230,7 @@ def main():
     ms_per_step = float(quant_ms.sum() + dec_ms.sum()) / args.steps   # the timed calls, flushes excluded
 
     n_q, n_int2, n_f16 = q1 - q0, te - tb, cfg.n_sink + cfg.n_res
-    r_bytes = H * d * d * 4 if rot == "dense" else 0
+    r_bytes = {"dense": H * d * d * 4, "perm": H * d * 4}.get(rot, 0)   # R / channel orders, read once
     q_bytes = B * n_q * H * QUANT_BYTES_PER_TOKEN_HEAD + r_bytes
     d_bytes = (B * n_int2 * H * DECODE_BYTES_PER_TOKEN_HEAD + B * n_f16 * H * FP16_BYTES_PER_TOKEN_HEAD
                + 2 * B * cfg.Hq * d * 2 + r_bytes)
@@ -230,11 +241,12 @@ def main():
     q_tok_s = B * n_q / (q_ms * 1e-3)
 
     csrc = os.path.join(ROOT, "int2_rotated_kv_amd", "csrc")
-    q_kernel, q_src = (("kv_rotate_quant_dense", "kv_rotate_quant_dense.hip") if rot == "dense"
-                       else ("kv_rotate_quant_fwht_f16", "kv_rotate_quant.hip"))
+    q_kernel, q_src = {"dense": ("kv_rotate_quant_dense", "kv_rotate_quant_dense.hip"),
+                       "perm": ("kv_rotate_quant_fwht_perm_f16", "kv_rotate_quant.hip")}.get(
+                           rot, ("kv_rotate_quant_fwht_f16", "kv_rotate_quant.hip"))
     roof_q = {"bound": "hbm", "achieved": round(q_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
               "frac": round(q_gbs / PEAK_HBM_GBS, 4),
-              "traffic": traffic_from_profile(q_kernel, cfg.name, os.path.join(csrc, q_src)),
+              "traffic": traffic_from_profile(q_kernel, workload, os.path.join(csrc, q_src)),
               "kernel": q_kernel, "algorithmic_bytes_per_launch": q_bytes,
               "bytes_per_unit": QUANT_BYTES_PER_TOKEN_HEAD, "unit_of_work": "(token, kv head)",
               "units_per_launch": B * n_q * H, "avg_ms": round(q_ms, 4)}
@@ -242,10 +254,10 @@ def main():
                        else ("kv_int2_decode_attn_gqa", "kv_decode_gqa.hip"))
     # the query preparation is its own launch only for a dense rotation or
     # grouped-query attention; otherwise the attention waves do it
-    prep_kernel = cfg.G > 1 or rot == "dense"
+    prep_kernel = cfg.G > 1 or rot in ("dense", "perm")
     roof_d = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
               "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
-              "traffic": traffic_from_profile(d_kernel, cfg.name, os.path.join(csrc, d_src)),
+              "traffic": traffic_from_profile(d_kernel, workload, os.path.join(csrc, d_src)),
               "kernel": f"decode call ({'kv_prep_query + ' if prep_kernel else ''}{d_kernel} + kv_combine_unrotate)",
               "algorithmic_bytes_per_launch": d_bytes,
               "bytes_per_unit": DECODE_BYTES_PER_TOKEN_HEAD, "unit_of_work": "(INT2 token, kv head)",
@@ -257,7 +269,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
-        "config": {"workload": cfg.name, "B": B, "T": T, "Hkv": H, "Hq": cfg.Hq, "d": d,
+        "config": {"workload": workload, "B": B, "T": T, "Hkv": H, "Hq": cfg.Hq, "d": d,
                    "kv_input": "f16", "cache": "int2 codes + f16 scale/zero, group 32",
                    "rotation": rot, "int2_tokens": [tb, te], "quantize_tokens": [q0, q1],
                    "fp16_tokens": n_f16},
@@ -275,11 +287,11 @@ def main():
     }
     rec["copy_reference_gbs"] = copy_bandwidth()
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(cfg, K, V, q, R, fp16)
+        rec["cpu_baseline"] = cpu_baseline(cfg, rot, K, V, q, R, fp16)
     print(json.dumps(rec), flush=True)
 
 
-def cpu_baseline(cfg, K, V, q, R, fp16):
+def cpu_baseline(cfg, rot, K, V, q, R, fp16):
     """The oracle, untouched, on a bounded sample of the same workload:
     batch 0, all KV heads, all tokens of the INT2 range (1/B of the job).
     The sample's inputs are the generator's values (copied from the
@@ -289,7 +301,12 @@ def cpu_baseline(cfg, K, V, q, R, fp16):
     from threadpoolctl import threadpool_info
 
     tb, te = cfg.int2_range
-    Rm = R.cpu().numpy() if R is not None else O.hadamard_rotation(cfg.d)
+    if rot == "dense":
+        Rm = R.cpu().numpy()
+    elif rot == "perm":
+        Rm = O.permuted_hadamard_rotation(R.cpu().numpy())
+    else:
+        Rm = O.hadamard_rotation(cfg.d)
     kh = K[0:1, tb:te].permute(0, 2, 1, 3).contiguous().cpu().numpy()
     vh = V[0:1, tb:te].permute(0, 2, 1, 3).contiguous().cpu().numpy()
     qs = q[0:1].cpu().numpy()

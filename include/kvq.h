@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 1
+#define KVQ_ABI_VERSION 2
 
 typedef enum {
   KVQ_OK = 0,
@@ -71,7 +71,14 @@ typedef enum { KVQ_F16 = 0, KVQ_F32 = 1 } kvq_dtype;
 typedef enum {
   KVQ_ROT_NONE = 0,      /* identity: rows are quantized as given            */
   KVQ_ROT_HADAMARD = 1,  /* R = H_d / sqrt(d), H[i][j] = (-1)^popcount(i&j)  */
-  KVQ_ROT_DENSE = 2      /* R = caller's fp32 [Hkv][d][d] row-major, y = x R */
+  KVQ_ROT_DENSE = 2,     /* R = caller's fp32 [Hkv][d][d] row-major, y = x R */
+  KVQ_ROT_PERM_HADAMARD = 3  /* R = P_h H_d / sqrt(d): channels reordered by a
+                              * per-head permutation pi_h, then the Hadamard
+                              * transform, y_j = (H x_pi / sqrt(d))_j with
+                              * (x_pi)_j = x[pi_h(j)]; the outlier-aware
+                              * rotation of RotateKV (IJCAI 2025 record,
+                              * abstract item (i): channel reordering ahead of
+                              * the fast Walsh-Hadamard transform) */
 } kvq_rot;
 
 /* One side (K or V) of an INT2 cache; all three arrays are device memory
@@ -92,9 +99,13 @@ typedef struct {
  *             [B][T_new][Hkv][d]: stride_b = T_new*Hkv*d, stride_t = Hkv*d,
  *             stride_h = d.  Either side may be skipped by passing NULL for
  *             both its input and its cache; not both.
- *  rot, R     KVQ_ROT_NONE / KVQ_ROT_HADAMARD with R == NULL, or
- *             KVQ_ROT_DENSE with R = fp32 [Hkv][d][d] (device), y = x R_h.
- *             The dense path needs in_dtype == KVQ_F16.
+ *  rot, R     KVQ_ROT_NONE / KVQ_ROT_HADAMARD with R == NULL;
+ *             KVQ_ROT_DENSE with R = fp32 [Hkv][d][d] (device), y = x R_h;
+ *             KVQ_ROT_PERM_HADAMARD with R = int32 [Hkv][d] (device), row h
+ *             a permutation pi_h of 0..d-1 (entries are used modulo d; a
+ *             row that is not a permutation gives unspecified codes, never
+ *             an out-of-bounds access).  The dense and permuted paths need
+ *             in_dtype == KVQ_F16.
  *  group      channels per scale/zero group; must be 32.
  *  t_offset   the rows land in cache slots [t_offset, t_offset + T_new) of
  *             every (b, h); must satisfy 0 <= t_offset, t_offset + T_new <=
@@ -105,7 +116,7 @@ typedef struct {
 kvq_status kvq_quantize(const void *K, const void *V, kvq_dtype in_dtype,
                         int64_t B, int64_t T_new, int64_t Hkv, int64_t d,
                         int64_t stride_b, int64_t stride_t, int64_t stride_h,
-                        kvq_rot rot, const float *R, int group,
+                        kvq_rot rot, const void *R, int group,
                         int64_t t_offset, const kvq_int2_cache *kc,
                         const kvq_int2_cache *vc, void *stream);
 
@@ -142,7 +153,7 @@ kvq_status kvq_decode_attention(const void *q, kvq_dtype q_dtype,
                                 const kvq_int2_cache *kc,
                                 const kvq_int2_cache *vc,
                                 int64_t t_begin, int64_t t_end,
-                                kvq_rot rot, const float *R, int group,
+                                kvq_rot rot, const void *R, int group,
                                 const uint16_t *sink_k, const uint16_t *sink_v,
                                 int64_t n_sink,
                                 const uint16_t *res_k, const uint16_t *res_v,

@@ -15,12 +15,13 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool valid_dtype(kvq_dtype t) { return t == KVQ_F16 || t == KVQ_F32; }
 bool valid_rot(kvq_rot r) {
-  return r == KVQ_ROT_NONE || r == KVQ_ROT_HADAMARD || r == KVQ_ROT_DENSE;
+  return r == KVQ_ROT_NONE || r == KVQ_ROT_HADAMARD || r == KVQ_ROT_DENSE ||
+         r == KVQ_ROT_PERM_HADAMARD;
 }
 
-kvq_status check_rotation(kvq_rot rot, const float *R) {
+kvq_status check_rotation(kvq_rot rot, const void *R) {
   if (!valid_rot(rot)) return KVQ_ERR_INVALID_ARG;
-  if (rot == KVQ_ROT_DENSE) {
+  if (rot == KVQ_ROT_DENSE || rot == KVQ_ROT_PERM_HADAMARD) {
     if (R == nullptr || !aligned16(R)) return KVQ_ERR_INVALID_ARG;
   } else if (R != nullptr) {
     return KVQ_ERR_INVALID_ARG;
@@ -50,7 +51,7 @@ extern "C" {
 
 kvq_status kvq_quantize(const void *K, const void *V, kvq_dtype in_dtype, int64_t B,
                         int64_t T_new, int64_t Hkv, int64_t d, int64_t stride_b,
-                        int64_t stride_t, int64_t stride_h, kvq_rot rot, const float *R,
+                        int64_t stride_t, int64_t stride_h, kvq_rot rot, const void *R,
                         int group, int64_t t_offset, const kvq_int2_cache *kc,
                         const kvq_int2_cache *vc, void *stream) {
   if (!valid_dtype(in_dtype)) return KVQ_ERR_INVALID_ARG;
@@ -59,7 +60,8 @@ kvq_status kvq_quantize(const void *K, const void *V, kvq_dtype in_dtype, int64_
   if (d != 128 || group != 32) return KVQ_ERR_UNSUPPORTED;
   kvq_status st = check_rotation(rot, R);
   if (st != KVQ_OK) return st;
-  if (rot == KVQ_ROT_DENSE && in_dtype != KVQ_F16) return KVQ_ERR_UNSUPPORTED;
+  if ((rot == KVQ_ROT_DENSE || rot == KVQ_ROT_PERM_HADAMARD) && in_dtype != KVQ_F16)
+    return KVQ_ERR_UNSUPPORTED;
   if ((K == nullptr) != (kc == nullptr) || (V == nullptr) != (vc == nullptr)) return KVQ_ERR_INVALID_ARG;
   if (K == nullptr && V == nullptr) return KVQ_ERR_INVALID_ARG;
   const int64_t esize = in_dtype == KVQ_F32 ? 4 : 2;
@@ -91,7 +93,8 @@ kvq_status kvq_quantize(const void *K, const void *V, kvq_dtype in_dtype, int64_
   a.stride_b = stride_b; a.stride_t = stride_t; a.stride_h = stride_h;
   a.t_offset = t_offset;
   a.rot = (int)rot;
-  a.R = R;
+  a.R = rot == KVQ_ROT_DENSE ? static_cast<const float *>(R) : nullptr;
+  a.perm = rot == KVQ_ROT_PERM_HADAMARD ? static_cast<const int32_t *>(R) : nullptr;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = (rot == KVQ_ROT_DENSE) ? kvq::launch_quantize_dense(a, s)
                                         : kvq::launch_quantize_rows(a, s);
@@ -110,7 +113,7 @@ size_t kvq_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
 kvq_status kvq_decode_attention(const void *q, kvq_dtype q_dtype, int64_t B, int64_t Hq,
                                 int64_t Hkv, int64_t d, const kvq_int2_cache *kc,
                                 const kvq_int2_cache *vc, int64_t t_begin, int64_t t_end,
-                                kvq_rot rot, const float *R, int group,
+                                kvq_rot rot, const void *R, int group,
                                 const uint16_t *sink_k, const uint16_t *sink_v, int64_t n_sink,
                                 const uint16_t *res_k, const uint16_t *res_v, int64_t n_res,
                                 float softmax_scale, void *out, kvq_dtype out_dtype,
@@ -154,7 +157,8 @@ kvq_status kvq_decode_attention(const void *q, kvq_dtype q_dtype, int64_t B, int
   a.t_begin = t_begin;
   a.n_int2 = n_int2;
   a.rot = (int)rot;
-  a.R = R;
+  a.R = rot == KVQ_ROT_DENSE ? static_cast<const float *>(R) : nullptr;
+  a.perm = rot == KVQ_ROT_PERM_HADAMARD ? static_cast<const int32_t *>(R) : nullptr;
   a.sink_k = sink_k; a.sink_v = sink_v; a.n_sink = n_sink;
   a.res_k = res_k; a.res_v = res_v; a.n_res = n_res;
   const double scale = softmax_scale > 0.0f ? (double)softmax_scale : 1.0 / sqrt(128.0);

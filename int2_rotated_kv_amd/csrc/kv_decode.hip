@@ -132,6 +132,7 @@ struct PrepArgs {
   int Hq, Hkv;
   int rot;
   const float *R;
+  const int32_t *perm;   // permuted Hadamard: [Hkv][128]
   float qscale;
   uint8_t *qprep;    // [B][Hq][128 dwords]
 };
@@ -148,9 +149,11 @@ __global__ __launch_bounds__(kMatThreads) void kv_prep_query(PrepArgs a) {
   const int hq = (int)(bh % a.Hq);
   const int hkv = hq / (a.Hq / a.Hkv);
   float x = 0.0f;
-  if (own) x = a.q_f32 ? reinterpret_cast<const float *>(a.q)[bh * kD + c]
-                       : (float)reinterpret_cast<const _Float16 *>(a.q)[bh * kD + c];
-  if (a.rot == 1) x = block_fwht128(x, buf);
+  // permuted Hadamard: thread c takes channel pi[c] of q (q_pi), then the transform
+  const int cin = a.rot == 3 ? (a.perm[(int64_t)hkv * kD + (c & (kD - 1))] & (kD - 1)) : c;
+  if (own) x = a.q_f32 ? reinterpret_cast<const float *>(a.q)[bh * kD + cin]
+                       : (float)reinterpret_cast<const _Float16 *>(a.q)[bh * kD + cin];
+  if (a.rot == 1 || a.rot == 3) x = block_fwht128(x, buf);
   else if (a.rot == 2) x = block_matvec128(x, a.R + (int64_t)hkv * kD * kD, false, buf, red);
   x *= a.qscale;
 
@@ -596,6 +599,7 @@ struct CombineArgs {
   int Hq, Hkv;
   int rot;
   const float *R;
+  const int32_t *perm;   // permuted Hadamard: [Hkv][128]
   float qscale;
   const float *partials;
   int64_t n_splits;
@@ -755,6 +759,14 @@ __global__ __launch_bounds__(kCombineThreads) void kv_combine_unrotate(CombineAr
   // un-rotate the INT2 part (linear, so once after the merge)
   if (a.rot == 1) o = block_fwht128(o, buf);
   else if (a.rot == 2) o = block_matvec128(o, a.R + (int64_t)hkv * kD * kD, true, buf, vred);
+  else if (a.rot == 3) {
+    // o' R^T = (o' H / sqrt(d)) P^T: transform, then output j goes to channel pi[j]
+    o = block_fwht128(o, buf);
+    if (own) buf[a.perm[(int64_t)hkv * kD + c] & (kD - 1)] = o;
+    __syncthreads();
+    o = own ? buf[c] : 0.0f;
+    __syncthreads();
+  }
 
   // fp16 token weights and values, all in the original basis
   const float M = fmaxf(M2, Mf);
@@ -845,11 +857,11 @@ hipError_t launch_decode(const DecodeArgs &d, hipStream_t stream) {
   const int G = (int)(d.Hq / d.Hkv);
   // one query head per KV head without a dense rotation: the attention waves
   // prepare the query themselves
-  const bool fused_prep = G == 1 && d.rot != 2;
+  const bool fused_prep = G == 1 && (d.rot == 0 || d.rot == 1);
   if (!fused_prep && d.n_splits > 0) {
     PrepArgs p;
     p.q = d.q; p.q_f32 = d.q_f32; p.Hq = (int)d.Hq; p.Hkv = (int)d.Hkv;
-    p.rot = d.rot; p.R = d.R; p.qscale = d.qscale;
+    p.rot = d.rot; p.R = d.R; p.perm = d.perm; p.qscale = d.qscale;
     p.qprep = reinterpret_cast<uint8_t *>(d.qprep);
     hipLaunchKernelGGL(kv_prep_query, dim3((unsigned)(d.B * d.Hq)), dim3(kMatThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
@@ -883,7 +895,7 @@ hipError_t launch_decode(const DecodeArgs &d, hipStream_t stream) {
   {
     CombineArgs c;
     c.q = d.q; c.q_f32 = d.q_f32; c.out_f32 = d.out_f32;
-    c.Hq = (int)d.Hq; c.Hkv = (int)d.Hkv; c.rot = d.rot; c.R = d.R; c.qscale = d.qscale;
+    c.Hq = (int)d.Hq; c.Hkv = (int)d.Hkv; c.rot = d.rot; c.R = d.R; c.perm = d.perm; c.qscale = d.qscale;
     c.partials = d.partials; c.n_splits = d.n_splits;
     c.sink_k = d.sink_k; c.sink_v = d.sink_v; c.n_sink = d.n_sink;
     c.res_k = d.res_k; c.res_v = d.res_v; c.n_res = d.n_res;

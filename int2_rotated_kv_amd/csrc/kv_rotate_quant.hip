@@ -265,6 +265,7 @@ struct RowsKernelArgs {
   int64_t T_new, t_offset;
   int Hkv;
   int n_sides;
+  const int32_t *perm;   // permuted Hadamard: [Hkv][128] channel order, else unused
 };
 
 // grid: x = token blocks of 64, y = KV head, z = batch * n_sides + side
@@ -319,8 +320,12 @@ __global__ __launch_bounds__(256) void kv_rotate_quant_rows(RowsKernelArgs a) {
 constexpr int kStageRowDwords = 64 + 4;     // 128 fp16 + 16-byte pad
 
 // grid: x = token block * Hkv + KV head, z = batch * n_sides + side;
-// block = one wave.
-__global__ __launch_bounds__(64) void kv_rotate_quant_fwht_f16(RowsKernelArgs a) {
+// block = one wave.  PERM: the row is read from LDS in the head's channel
+// order pi (x_pi[j] = x[pi[j]], RotateKV's channel reordering ahead of the
+// transform), one fp16 value per read; pi[j] is wave-uniform (scalar loads)
+// and taken modulo 128, so any index stays inside the row.
+template <bool PERM>
+__device__ __forceinline__ void fwht_f16_body(const RowsKernelArgs &a) {
   __shared__ uint32_t stage[64 * kStageRowDwords];
   const int lane = threadIdx.x;
   const int h = (int)(blockIdx.x % (unsigned)a.Hkv);
@@ -357,14 +362,27 @@ __global__ __launch_bounds__(64) void kv_rotate_quant_fwht_f16(RowsKernelArgs a)
   __syncthreads();
 
   float v[128];
+  if constexpr (PERM) {
+    const int32_t *pi = a.perm + (int64_t)h * kD;
+    const uint8_t *row = reinterpret_cast<const uint8_t *>(&stage[lane * kStageRowDwords]);
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const u32x4_t u = *reinterpret_cast<const u32x4_t *>(&stage[lane * kStageRowDwords + 4 * k]);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    for (int k = 0; k < 64; ++k) {
+      const uint32_t lo = *reinterpret_cast<const uint16_t *>(row + 2 * (pi[2 * k] & (kD - 1)));
+      const uint32_t hi = *reinterpret_cast<const uint16_t *>(row + 2 * (pi[2 * k + 1] & (kD - 1)));
+      const uint32_t w = lo | (hi << 16);
+      v[2 * k] = mix_sum(w);                     // FWHT stage 1 on the way in
+      v[2 * k + 1] = mix_diff(w);
+    }
+  } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[8 * k + 2 * e] = mix_sum(w[e]);          // FWHT stage 1 on the way in
-      v[8 * k + 2 * e + 1] = mix_diff(w[e]);
+    for (int k = 0; k < 16; ++k) {
+      const u32x4_t u = *reinterpret_cast<const u32x4_t *>(&stage[lane * kStageRowDwords + 4 * k]);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[8 * k + 2 * e] = mix_sum(w[e]);          // FWHT stage 1 on the way in
+        v[8 * k + 2 * e + 1] = mix_diff(w[e]);
+      }
     }
   }
 #pragma unroll
@@ -408,6 +426,13 @@ __global__ __launch_bounds__(64) void kv_rotate_quant_fwht_f16(RowsKernelArgs a)
   }
 }
 
+__global__ __launch_bounds__(64) void kv_rotate_quant_fwht_f16(RowsKernelArgs a) {
+  fwht_f16_body<false>(a);
+}
+__global__ __launch_bounds__(64) void kv_rotate_quant_fwht_perm_f16(RowsKernelArgs a) {
+  fwht_f16_body<true>(a);
+}
+
 hipError_t launch_quantize_rows(const QuantArgs &q, hipStream_t stream) {
   RowsKernelArgs a;
   a.side[0] = q.side[0];
@@ -419,14 +444,17 @@ hipError_t launch_quantize_rows(const QuantArgs &q, hipStream_t stream) {
   a.t_offset = q.t_offset;
   a.Hkv = (int)q.Hkv;
   a.n_sides = q.n_sides;
+  a.perm = q.perm;
   const int64_t n_tb = (q.T_new + 63) / 64;
   dim3 grid((unsigned)n_tb, (unsigned)q.Hkv, (unsigned)(q.B * q.n_sides));
   const bool rot = (q.rot == 1);
-  if (rot && !q.in_f32) {
+  if ((rot || q.rot == 3) && !q.in_f32) {
     dim3 grid_hf((unsigned)(n_tb * q.Hkv), 1, (unsigned)(q.B * q.n_sides));
-    hipLaunchKernelGGL(kv_rotate_quant_fwht_f16, grid_hf, dim3(64), 0, stream, a);
+    if (q.rot == 3) hipLaunchKernelGGL(kv_rotate_quant_fwht_perm_f16, grid_hf, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL(kv_rotate_quant_fwht_f16, grid_hf, dim3(64), 0, stream, a);
     return hipGetLastError();
   }
+  if (q.rot == 3) return hipErrorNotSupported;     // fp32 input: the caller has rejected it
   dim3 block(256);
   if (q.in_f32) {
     if (rot) hipLaunchKernelGGL((kv_rotate_quant_rows<float, true>), grid, block, 0, stream, a);

@@ -22,8 +22,9 @@ KVQ_ERR_WORKSPACE_TOO_SMALL = 3
 KVQ_ERR_HIP = 4
 
 KVQ_F16, KVQ_F32 = 0, 1
-KVQ_ROT_NONE, KVQ_ROT_HADAMARD, KVQ_ROT_DENSE = 0, 1, 2
-_ROT = {"none": KVQ_ROT_NONE, "hadamard": KVQ_ROT_HADAMARD, "dense": KVQ_ROT_DENSE}
+KVQ_ROT_NONE, KVQ_ROT_HADAMARD, KVQ_ROT_DENSE, KVQ_ROT_PERM_HADAMARD = 0, 1, 2, 3
+_ROT = {"none": KVQ_ROT_NONE, "hadamard": KVQ_ROT_HADAMARD, "dense": KVQ_ROT_DENSE,
+        "perm": KVQ_ROT_PERM_HADAMARD}
 
 EXPORTED_SYMBOLS = ("kvq_quantize", "kvq_decode_workspace_bytes",
                     "kvq_decode_attention", "kvq_status_str", "kvq_abi_version")
@@ -138,7 +139,9 @@ def kvq_quantize(K, V, cache_k: Int2Cache | None, cache_v: Int2Cache | None,
                  rot: str = "hadamard", R: torch.Tensor | None = None,
                  group: int = GROUP, t_offset: int = 0, stream=None):
     """Rotate, quantize and pack K/V rows [B, T_new, Hkv, d] (channel stride 1)
-    into cache slots [t_offset, t_offset + T_new).  Either side may be None."""
+    into cache slots [t_offset, t_offset + T_new).  Either side may be None.
+    R: fp32 [Hkv, d, d] for rot="dense"; int32 [Hkv, d] channel permutations
+    for rot="perm" (reorder, then the Hadamard transform); None otherwise."""
     x = K if K is not None else V
     for t in (K, V):
         if t is not None and (t.dim() != 4 or t.stride(3) != 1):

@@ -66,6 +66,31 @@ def hadamard_rotation(d: int = D_HEAD) -> np.ndarray:
     return np.where(parity == 1, -1.0, 1.0) / np.sqrt(float(d))
 
 
+def permuted_hadamard_rotation(perm) -> np.ndarray:
+    """Per-head rotation R_h = P_h . H for channel orders perm [H, d], fp64.
+
+    Channel reordering ahead of the fast Walsh-Hadamard transform (RotateKV,
+    IJCAI 2025 record, abstract item (i): the reordering adapts the rotation
+    to where the outlier channels are while the transform stays the FWHT).
+    The pages do not say how the order is applied; the reading here: the
+    row is gathered first, (x P)_j = x[perm[j]], then rotated by H, so
+    y = x P H and P[i, j] = 1 exactly when i == perm[j].
+    """
+    perm = np.asarray(perm)
+    if perm.ndim != 2:
+        raise ValueError("perm must be [heads, d]")
+    n_heads, d = perm.shape
+    H = hadamard_rotation(d)
+    out = np.empty((n_heads, d, d))
+    for h in range(n_heads):
+        if sorted(perm[h].tolist()) != list(range(d)):
+            raise ValueError("each row of perm must be a permutation of 0..d-1")
+        P = np.zeros((d, d))
+        P[perm[h], np.arange(d)] = 1.0
+        out[h] = P @ H
+    return out
+
+
 def rotate_rows(x: np.ndarray, R: np.ndarray | None) -> np.ndarray:
     """y = x . R for row vectors x, in fp64, rounded once to fp32.
 

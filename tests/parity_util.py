@@ -38,6 +38,8 @@ def rot_matrix(rot, R=None):
         return None
     if rot == "hadamard":
         return O.hadamard_rotation(128)
+    if rot == "perm":
+        return O.permuted_hadamard_rotation(R)
     return np.asarray(R, dtype=np.float32)
 
 

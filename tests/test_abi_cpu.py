@@ -46,7 +46,8 @@ def test_library_exports_every_header_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert K.kvq_abi_version() == 1
+    hdr = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    assert K.kvq_abi_version() == int(re.search(r"#define KVQ_ABI_VERSION (\d+)", hdr).group(1))
     names = [K.kvq_status_str(s) for s in range(5)]
     assert names == ["KVQ_OK", "KVQ_ERR_INVALID_ARG", "KVQ_ERR_UNSUPPORTED",
                      "KVQ_ERR_WORKSPACE_TOO_SMALL", "KVQ_ERR_HIP"]
@@ -93,6 +94,10 @@ QUANT_ERRORS = [
     (dict(rot=K.KVQ_ROT_DENSE, R=FAKE, dt=K.KVQ_F32, sb=8 * 2 * 128, st=256, sh=128),
      K.KVQ_ERR_UNSUPPORTED),
     (dict(B=70000), K.KVQ_ERR_UNSUPPORTED),                # grid z limit
+    (dict(rot=K.KVQ_ROT_PERM_HADAMARD, R=None), K.KVQ_ERR_INVALID_ARG),
+    (dict(rot=K.KVQ_ROT_PERM_HADAMARD, R=FAKE_MISALIGNED), K.KVQ_ERR_INVALID_ARG),
+    (dict(rot=K.KVQ_ROT_PERM_HADAMARD, R=FAKE, dt=K.KVQ_F32, sb=8 * 2 * 128, st=256, sh=128),
+     K.KVQ_ERR_UNSUPPORTED),
 ]
 
 
@@ -138,6 +143,8 @@ DECODE_ERRORS = [
     (dict(nr=9000, rk=FAKE, rv=FAKE), K.KVQ_ERR_UNSUPPORTED),
     (dict(tb=0, te=0), K.KVQ_ERR_INVALID_ARG),             # no tokens at all
     (dict(rot=K.KVQ_ROT_DENSE), K.KVQ_ERR_INVALID_ARG),    # dense without R
+    (dict(rot=K.KVQ_ROT_PERM_HADAMARD), K.KVQ_ERR_INVALID_ARG),   # permutation missing
+    (dict(rot=K.KVQ_ROT_NONE, R=FAKE), K.KVQ_ERR_INVALID_ARG),
     (dict(ws=None), K.KVQ_ERR_INVALID_ARG),
     (dict(ws=FAKE + 16), K.KVQ_ERR_INVALID_ARG),           # workspace not 256-aligned
     (dict(wsb=100), K.KVQ_ERR_WORKSPACE_TOO_SMALL),

@@ -54,6 +54,29 @@ def pin_hadamard_orthogonal(orc):
     assert np.abs(H @ H.T - np.eye(128)).max() < 1e-14
 
 
+def pin_perm_hadamard_gather(orc):
+    """Channel reordering ahead of the transform (RotateKV (i)): x R_h equals
+    gathering x in the head's channel order, then scipy's Sylvester Hadamard
+    (normalized); one-hot rows give the Hadamard row of the inverse position;
+    the identity order gives the plain Hadamard rotation."""
+    rng = np.random.default_rng(17)
+    d = 128
+    perm = np.stack([rng.permutation(d) for _ in range(3)])
+    R = orc.permuted_hadamard_rotation(perm)
+    Hs = scipy.linalg.hadamard(d).astype(np.float64) / math.sqrt(d)
+    x = rng.standard_normal((5, d))
+    for h in range(3):
+        assert np.allclose(x @ R[h], x[:, perm[h]] @ Hs, atol=1e-12)
+        inv = np.argsort(perm[h])
+        for k in (0, 1, 77):
+            e = np.zeros(d)
+            e[k] = 1.0
+            assert np.allclose(e @ R[h], Hs[inv[k]], atol=1e-15)
+        assert np.abs(R[h] @ R[h].T - np.eye(d)).max() < 1e-14
+    ident = orc.permuted_hadamard_rotation(np.arange(d)[None])
+    assert np.allclose(ident[0], orc.hadamard_rotation(d), atol=0)
+
+
 def pin_rotate_onehot_dense(orc):
     """Row-vector convention: e_k R is row k of R (a non-symmetric R)."""
     rng = np.random.default_rng(7)
@@ -266,7 +289,7 @@ def pin_decode_large_scores(orc):
 
 PINS = [
     pin_hadamard_scipy, pin_hadamard_golden4, pin_hadamard_orthogonal,
-    pin_rotate_onehot_dense, pin_parseval_and_dot_invariance,
+    pin_perm_hadamard_gather, pin_rotate_onehot_dense, pin_parseval_and_dot_invariance,
     pin_quant_golden, pin_quant_grid_random, pin_quant_nearest_level,
     pin_pack_golden, pin_pack_roundtrip,
     pin_decode_vs_sdpa, pin_decode_bruteforce, pin_decode_large_scores,
@@ -333,6 +356,9 @@ MUTATIONS = [
     ("no clamp", "np.clip(np.rint(u), 0, QMAX)", "np.rint(u)"),
     ("rotation transposed", "x64 @ np.asarray(R, dtype=np.float64)",
      "x64 @ np.asarray(R, dtype=np.float64).T"),
+    ("channel order applied inverted", "P[perm[h], np.arange(d)] = 1.0",
+     "P[np.arange(d), perm[h]] = 1.0"),
+    ("channel order after the transform", "out[h] = P @ H", "out[h] = H @ P"),
 ]
 
 

@@ -36,13 +36,23 @@ def _report(name, **kw):
     print(f"[parity] {name} " + json.dumps(kw), flush=True)
 
 
+def _rot_arg(rot, R):
+    """The R argument of the library for a rotation: fp32 matrices (dense),
+    int32 channel orders (perm) or None."""
+    if rot == "dense":
+        return torch.as_tensor(R, dtype=torch.float32, device=DEV).contiguous()
+    if rot == "perm":
+        return torch.as_tensor(R, dtype=torch.int32, device=DEV).contiguous()
+    return None
+
+
 # ------------------------------------------------------------ quantize
 def _gpu_quantize(x_tok, rot, R=None, T_cap=None, t_offset=0, side="K"):
     B, T, H, d = x_tok.shape
     T_cap = T_cap or (T + t_offset)
     c = empty_cache(B, H, T_cap)
     xg = x_tok.to(DEV)
-    Rg = None if R is None else torch.as_tensor(R, dtype=torch.float32, device=DEV).contiguous()
+    Rg = _rot_arg(rot, R)
     if side == "K":
         kvq.kvq_quantize(xg, None, c, None, rot=rot, R=Rg, t_offset=t_offset)
     else:
@@ -226,6 +236,34 @@ def test_quantize_offset_groups(rot):
         _report(f"quantize offset groups {rot} h={h}", **st)
 
 
+@pytest.mark.parametrize("order", ["outliers", "random"])
+def test_quantize_perm_hadamard_ties(order):
+    """Channel reordering ahead of the Hadamard transform (per-head orders:
+    sorted by outlier magnitude, or random), ragged token count, offset."""
+    cfg = W.small_config(W.config(2), B=2, T=1000, Hkv=3, Hq=3)
+    if order == "outliers":
+        perm = W.channel_orders(cfg)
+    else:
+        rng = np.random.default_rng(5)
+        perm = np.stack([rng.permutation(128) for _ in range(cfg.Hkv)]).astype(np.int32)
+    Rh = O.permuted_hadamard_rotation(perm)
+    tot = dict(elements=0, code_mismatch=0, group_scale_zero_diff=0)
+    for which in ("K", "V"):
+        x = W.kv_tokens(cfg, which)
+        gp, gs, gz = _gpu_quantize(x, "perm", R=perm, T_cap=cfg.T + 9, t_offset=9, side=which)
+        gpu = (gp[:, :, 9:], gs[:, :, 9:], gz[:, :, 9:])
+        ora = _oracle_quantize(x, "perm", perm)
+        xr = x.permute(0, 2, 1, 3).contiguous().numpy()
+        for h in range(cfg.Hkv):
+            # per head: every mismatch at a tie; the fraction is checked over the whole call
+            st = compare_codes_at_ties(xr[:, h], Rh[h], tuple(a[:, h] for a in gpu),
+                                       tuple(a[:, h] for a in ora), max_frac=1.0)
+            for k in tot:
+                tot[k] += st[k]
+    assert tot["code_mismatch"] <= 1e-5 * tot["elements"]
+    _report(f"quantize_perm {order}", **tot)
+
+
 def test_quantize_dense_config4_slice():
     """Config 4 shapes on the prefill slice (32768 new tokens of one
     sequence, all 8 heads)."""
@@ -284,7 +322,7 @@ def _decode_case(cfg, rot="hadamard", R=None, t_begin=None, t_end=None, n_sink=N
                              sink_k=sk, sink_v=sv, res_k=rk, res_v=rv,
                              softmax_scale=scale if scale > 0 else None)
     up = lambda a: None if a is None else torch.from_numpy(a).to(DEV)
-    Rg = None if rot != "dense" else torch.as_tensor(R, device=DEV).contiguous()
+    Rg = _rot_arg(rot, R)
     out = kvq.kvq_decode_attention(q.to(DEV), cache_from_numpy(*kcache),
                                    cache_from_numpy(*vcache), t_begin, t_end, rot=rot,
                                    R=Rg, sink_k=up(sk), sink_v=up(sv), res_k=up(rk),
@@ -372,6 +410,19 @@ def test_decode_shifted_tile_grid(Hq, t_begin, t_end):
     cfg2 = W.small_config(W.config(2), T=1024, B=1, Hkv=2, Hq=Hq)
     _decode_case(cfg2, t_begin=t_begin, t_end=t_end, n_sink=0, n_res=0,
                  name=f"shifted grid hadamard Hq={Hq} [{t_begin},{t_end})")
+
+
+@pytest.mark.parametrize("Hq", [3, 12])
+def test_decode_perm_hadamard(Hq):
+    """Reordered Hadamard rotation on the read path: q gathered in the
+    head's order before the transform, the output scattered back after it;
+    with sinks and residual tokens (original basis) and an INT2 range off a
+    16-row boundary; one and four query heads per KV head."""
+    cfg = W.small_config(W.config(5), T=1024, B=2, Hkv=3, Hq=Hq)
+    rng = np.random.default_rng(23)
+    perm = np.stack([rng.permutation(128) for _ in range(cfg.Hkv)]).astype(np.int32)
+    _decode_case(cfg, rot="perm", R=perm, name=f"perm Hq={Hq}")
+    _decode_case(cfg, rot="perm", R=perm, n_sink=0, n_res=0, name=f"perm Hq={Hq} INT2 only")
 
 
 def test_decode_max_fp16_tokens():

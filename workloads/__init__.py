@@ -2,5 +2,5 @@
 the oracle's callers.  Holds no arithmetic of the method itself."""
 from .synth import (  # noqa: F401
     Config, CONFIGS, config, small_config, normal_at, channel_sigma,
-    dense_rotations, kv_tokens, queries, head_major,
+    dense_rotations, channel_orders, kv_tokens, queries, head_major,
 )

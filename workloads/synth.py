@@ -194,6 +194,15 @@ def dense_rotations(cfg: Config) -> np.ndarray:
     return out
 
 
+def channel_orders(cfg: Config) -> np.ndarray:
+    """Per-KV-head channel orders for the reordered Hadamard rotation: the
+    channels of each head sorted by their K standard deviation, largest
+    first (ties by channel index), i.e. ordered by outlier magnitude.
+    Returns int32 [Hkv, d], each row a permutation of 0..d-1."""
+    sig = channel_sigma(cfg, "K")
+    return np.stack([np.argsort(-sig[h], kind="stable") for h in range(cfg.Hkv)]).astype(np.int32)
+
+
 # --------------------------------------------------------------------------
 # tensors
 # --------------------------------------------------------------------------
