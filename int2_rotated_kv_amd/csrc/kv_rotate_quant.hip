@@ -320,10 +320,12 @@ __global__ __launch_bounds__(256) void kv_rotate_quant_rows(RowsKernelArgs a) {
 constexpr int kStageRowDwords = 64 + 4;     // 128 fp16 + 16-byte pad
 
 // grid: x = token block * Hkv + KV head, z = batch * n_sides + side;
-// block = one wave.  PERM: the row is read from LDS in the head's channel
+// block = one wave.  PERM: the rows are reordered to the head's channel
 // order pi (x_pi[j] = x[pi[j]], RotateKV's channel reordering ahead of the
-// transform), one fp16 value per read; pi[j] is wave-uniform (scalar loads)
-// and taken modulo 128, so any index stays inside the row.
+// transform) while they are staged: channel c goes to position pinv[c] of
+// its LDS row (one 2-byte store each, the row offset in the store's
+// immediate), and the rows are read back as in the plain kernel.  Indices
+// are taken modulo 128, so any order array stays inside the rows.
 template <bool PERM>
 __device__ __forceinline__ void fwht_f16_body(const RowsKernelArgs &a) {
   __shared__ uint32_t stage[64 * kStageRowDwords];
@@ -340,49 +342,55 @@ __device__ __forceinline__ void fwht_f16_body(const RowsKernelArgs &a) {
   // coalesced staging: instruction i covers rows 4i..4i+3, 16 lanes per row
   const int chunk = lane & 15;
   const int r0 = lane >> 4;
+  // PERM: channel c is staged at position pinv[c] of its row (pinv = the
+  // inverse of the head's order, built in LDS), so the rows are read back
+  // already reordered.  pos[e]: byte offset of channel 8 chunk + e in row r0.
+  uint32_t pos[8];
+  if constexpr (PERM) {
+    __shared__ uint8_t pinv[kD];
+    const int32_t *pi = a.perm + (int64_t)h * kD;
+    pinv[pi[2 * lane] & (kD - 1)] = (uint8_t)(2 * lane);
+    pinv[pi[2 * lane + 1] & (kD - 1)] = (uint8_t)(2 * lane + 1);
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      pos[e] = (uint32_t)(r0 * kStageRowDwords * 4 + 2 * (pinv[8 * chunk + e] & (kD - 1)));
+  }
+  auto stage_row = [&](int i, const u32x4_t &u) {
+    if constexpr (PERM) {
+      uint8_t *rb = reinterpret_cast<uint8_t *>(stage) + 4 * i * kStageRowDwords * 4;
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<uint16_t *>(rb + pos[e]) = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+    } else {
+      *reinterpret_cast<u32x4_t *>(&stage[(4 * i + r0) * kStageRowDwords + 4 * chunk]) = u;
+    }
+  };
   if (t0 + 64 <= a.T_new) {
     const u32x4_t *src = reinterpret_cast<const u32x4_t *>(base + (t0 + r0) * a.stride_t) + chunk;
     const int64_t step = 4 * a.stride_t / 8;        // 4 rows, in 16-byte units
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const u32x4_t u = __builtin_nontemporal_load(src + i * step);
-      *reinterpret_cast<u32x4_t *>(&stage[(4 * i + r0) * kStageRowDwords + 4 * chunk]) = u;
-    }
+    for (int i = 0; i < 16; ++i) stage_row(i, __builtin_nontemporal_load(src + i * step));
   } else {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int row = 4 * i + r0;
-      const int64_t t = t0 + row;
+      const int64_t t = t0 + 4 * i + r0;
       const int64_t tl = t < a.T_new ? t : 0;
-      const u32x4_t u = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4_t *>(base + tl * a.stride_t) + chunk);
-      *reinterpret_cast<u32x4_t *>(&stage[row * kStageRowDwords + 4 * chunk]) = u;
+      stage_row(i, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(base + tl * a.stride_t) + chunk));
     }
   }
   __syncthreads();
 
   float v[128];
-  if constexpr (PERM) {
-    const int32_t *pi = a.perm + (int64_t)h * kD;
-    const uint8_t *row = reinterpret_cast<const uint8_t *>(&stage[lane * kStageRowDwords]);
 #pragma unroll
-    for (int k = 0; k < 64; ++k) {
-      const uint32_t lo = *reinterpret_cast<const uint16_t *>(row + 2 * (pi[2 * k] & (kD - 1)));
-      const uint32_t hi = *reinterpret_cast<const uint16_t *>(row + 2 * (pi[2 * k + 1] & (kD - 1)));
-      const uint32_t w = lo | (hi << 16);
-      v[2 * k] = mix_sum(w);                     // FWHT stage 1 on the way in
-      v[2 * k + 1] = mix_diff(w);
-    }
-  } else {
+  for (int k = 0; k < 16; ++k) {
+    const u32x4_t u = *reinterpret_cast<const u32x4_t *>(&stage[lane * kStageRowDwords + 4 * k]);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const u32x4_t u = *reinterpret_cast<const u32x4_t *>(&stage[lane * kStageRowDwords + 4 * k]);
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[8 * k + 2 * e] = mix_sum(w[e]);          // FWHT stage 1 on the way in
-        v[8 * k + 2 * e + 1] = mix_diff(w[e]);
-      }
+    for (int e = 0; e < 4; ++e) {
+      v[8 * k + 2 * e] = mix_sum(w[e]);          // FWHT stage 1 on the way in
+      v[8 * k + 2 * e + 1] = mix_diff(w[e]);
     }
   }
 #pragma unroll
