@@ -318,6 +318,28 @@ def test_hadamard_reduces_int2_error_on_outliers():
         assert errs[1] < 0.6 * errs[0]
 
 
+def test_outlier_order_reduces_int2_error():
+    """Reordering each head's channels by outlier magnitude ahead of the
+    Hadamard transform lowers the INT2 reconstruction error further on
+    outlier data (RotateKV abstract, item (i): the reordering adapts the
+    rotation to the channel-wise outliers).  Property, not parity."""
+    from workloads import config, small_config, kv_tokens, channel_orders
+    cfg = small_config(config(2), B=1, T=256, Hkv=4, Hq=4)
+    x = kv_tokens(cfg, "K").numpy()[0].transpose(1, 0, 2)          # [H, T, d]
+    H = kvq_oracle.hadamard_rotation(128)
+    Rp = kvq_oracle.permuted_hadamard_rotation(channel_orders(cfg))
+
+    def mse(R, h):
+        y = kvq_oracle.rotate_rows(x[h], R)
+        c, s, z = kvq_oracle.quantize_rows(y)
+        back = kvq_oracle.dequantize(c, s, z) @ np.asarray(R, np.float64).T
+        return np.mean((back - x[h].astype(np.float64)) ** 2)
+
+    plain = np.mean([mse(H, h) for h in range(cfg.Hkv)])
+    ordered = np.mean([mse(Rp[h], h) for h in range(cfg.Hkv)])
+    assert ordered < 0.9 * plain
+
+
 def test_format_bits_per_element():
     """2-bit codes + fp16 scale and zero per 32 channels = 3 bits/element,
     18.75% of fp16 (the OptR page quotes roughly 75% savings, Key Details)."""
