@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 2
+#define KVQ_ABI_VERSION 3
 
 typedef enum {
   KVQ_OK = 0,
@@ -121,6 +121,27 @@ kvq_status kvq_quantize(const void *K, const void *V, kvq_dtype in_dtype,
                         const kvq_int2_cache *vc, void *stream);
 
 /*
+ * kvq_quantize_at -- kvq_quantize with a cache slot per sequence: the T_new
+ * rows of sequence b land in slots [t_offsets[b], t_offsets[b] + T_new) of
+ * every (b, h) (a decode-step append with sequences of different lengths
+ * writes T_new = 1 row per sequence at its current length).
+ *
+ *  t_offsets  int32 [B], device, 4-byte aligned.  Read by the kernels, so
+ *             not checked on the host: a row whose slot falls outside
+ *             [0, T_cap) is not written.  T_new <= T_cap is checked.
+ *  Every other argument as for kvq_quantize.
+ * Serving stacks need this alongside variable-length decode (the survey's
+ * next step after the hot path; the pages name serving stacks as the
+ * setting, OptR page, "Why It Matters").
+ */
+kvq_status kvq_quantize_at(const void *K, const void *V, kvq_dtype in_dtype,
+                           int64_t B, int64_t T_new, int64_t Hkv, int64_t d,
+                           int64_t stride_b, int64_t stride_t, int64_t stride_h,
+                           kvq_rot rot, const void *R, int group,
+                           const int32_t *t_offsets, const kvq_int2_cache *kc,
+                           const kvq_int2_cache *vc, void *stream);
+
+/*
  * kvq_decode_workspace_bytes -- bytes of device workspace that
  * kvq_decode_attention needs for these sizes (0 on invalid sizes).  Pure
  * host arithmetic; calls nothing in HIP.
@@ -161,6 +182,33 @@ kvq_status kvq_decode_attention(const void *q, kvq_dtype q_dtype,
                                 void *out, kvq_dtype out_dtype,
                                 void *workspace, size_t workspace_bytes,
                                 void *stream);
+
+/*
+ * kvq_decode_attention_varlen -- kvq_decode_attention over a batch of
+ * sequences of different lengths: sequence b attends to INT2 tokens
+ * [t_begin, t_ends[b]) (plus the fp16 tokens, common to the batch).
+ *
+ *  t_ends     int32 [B], device, 4-byte aligned.  Read by the kernels and
+ *             clamped to [t_begin, t_end_max].  A sequence left with no
+ *             token at all (no INT2 and no fp16 token) gets a zero output.
+ *  t_end_max  host upper bound of every t_ends[b]: sizes the split plan
+ *             and the workspace (kvq_decode_workspace_bytes with
+ *             n_int2_tokens = t_end_max - t_begin); t_end_max <= T_cap.
+ *  Every other argument as for kvq_decode_attention.
+ */
+kvq_status kvq_decode_attention_varlen(const void *q, kvq_dtype q_dtype,
+                                       int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
+                                       const kvq_int2_cache *kc,
+                                       const kvq_int2_cache *vc, int64_t t_begin,
+                                       const int32_t *t_ends, int64_t t_end_max,
+                                       kvq_rot rot, const void *R, int group,
+                                       const uint16_t *sink_k, const uint16_t *sink_v,
+                                       int64_t n_sink,
+                                       const uint16_t *res_k, const uint16_t *res_v,
+                                       int64_t n_res, float softmax_scale,
+                                       void *out, kvq_dtype out_dtype,
+                                       void *workspace, size_t workspace_bytes,
+                                       void *stream);
 
 /* Human-readable name of a status code (static storage). */
 const char *kvq_status_str(kvq_status s);

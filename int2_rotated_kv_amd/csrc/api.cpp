@@ -45,15 +45,16 @@ size_t workspace_bytes(int64_t B, int64_t Hq, int64_t n_splits) {
   return qprep + parts;
 }
 
-}  // namespace
 
-extern "C" {
-
-kvq_status kvq_quantize(const void *K, const void *V, kvq_dtype in_dtype, int64_t B,
-                        int64_t T_new, int64_t Hkv, int64_t d, int64_t stride_b,
-                        int64_t stride_t, int64_t stride_h, kvq_rot rot, const void *R,
-                        int group, int64_t t_offset, const kvq_int2_cache *kc,
-                        const kvq_int2_cache *vc, void *stream) {
+// Shared by the common-offset and the per-sequence-offset entry points.
+// offsets == NULL: every sequence's rows start at t_offset (checked against
+// T_cap here); otherwise at offsets[b] (device), where a row whose slot falls
+// outside [0, T_cap) is skipped by the kernels.
+kvq_status quantize_impl(const void *K, const void *V, kvq_dtype in_dtype, int64_t B,
+                         int64_t T_new, int64_t Hkv, int64_t d, int64_t stride_b,
+                         int64_t stride_t, int64_t stride_h, kvq_rot rot, const void *R,
+                         int group, int64_t t_offset, const int32_t *offsets,
+                         const kvq_int2_cache *kc, const kvq_int2_cache *vc, void *stream) {
   if (!valid_dtype(in_dtype)) return KVQ_ERR_INVALID_ARG;
   if (B < 0 || T_new < 0 || Hkv <= 0 || t_offset < 0) return KVQ_ERR_INVALID_ARG;
   if (stride_b < 0 || stride_t < 0 || stride_h < 0) return KVQ_ERR_INVALID_ARG;
@@ -76,7 +77,9 @@ kvq_status kvq_quantize(const void *K, const void *V, kvq_dtype in_dtype, int64_
     if (!aligned16(xs[s])) return KVQ_ERR_INVALID_ARG;
     st = check_cache(cs[s]);
     if (st != KVQ_OK) return st;
-    if (t_offset > cs[s]->T_cap || T_new > cs[s]->T_cap - t_offset) return KVQ_ERR_INVALID_ARG;
+    if (offsets == nullptr && (t_offset > cs[s]->T_cap || T_new > cs[s]->T_cap - t_offset))
+      return KVQ_ERR_INVALID_ARG;
+    if (offsets != nullptr && T_new > cs[s]->T_cap) return KVQ_ERR_INVALID_ARG;
     kvq::QuantSide &q = a.side[a.n_sides++];
     q.x = xs[s];
     q.codes = cs[s]->codes;
@@ -92,6 +95,7 @@ kvq_status kvq_quantize(const void *K, const void *V, kvq_dtype in_dtype, int64_
   a.B = B; a.T_new = T_new; a.Hkv = Hkv;
   a.stride_b = stride_b; a.stride_t = stride_t; a.stride_h = stride_h;
   a.t_offset = t_offset;
+  a.offsets = offsets;
   a.rot = (int)rot;
   a.R = rot == KVQ_ROT_DENSE ? static_cast<const float *>(R) : nullptr;
   a.perm = rot == KVQ_ROT_PERM_HADAMARD ? static_cast<const int32_t *>(R) : nullptr;
@@ -102,6 +106,29 @@ kvq_status kvq_quantize(const void *K, const void *V, kvq_dtype in_dtype, int64_
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_quantize(const void *K, const void *V, kvq_dtype in_dtype, int64_t B,
+                        int64_t T_new, int64_t Hkv, int64_t d, int64_t stride_b,
+                        int64_t stride_t, int64_t stride_h, kvq_rot rot, const void *R,
+                        int group, int64_t t_offset, const kvq_int2_cache *kc,
+                        const kvq_int2_cache *vc, void *stream) {
+  return quantize_impl(K, V, in_dtype, B, T_new, Hkv, d, stride_b, stride_t, stride_h, rot, R,
+                       group, t_offset, nullptr, kc, vc, stream);
+}
+
+kvq_status kvq_quantize_at(const void *K, const void *V, kvq_dtype in_dtype, int64_t B,
+                           int64_t T_new, int64_t Hkv, int64_t d, int64_t stride_b,
+                           int64_t stride_t, int64_t stride_h, kvq_rot rot, const void *R,
+                           int group, const int32_t *t_offsets, const kvq_int2_cache *kc,
+                           const kvq_int2_cache *vc, void *stream) {
+  if (t_offsets == nullptr || ((uintptr_t)t_offsets & 3u) != 0) return KVQ_ERR_INVALID_ARG;
+  return quantize_impl(K, V, in_dtype, B, T_new, Hkv, d, stride_b, stride_t, stride_h, rot, R,
+                       group, 0, t_offsets, kc, vc, stream);
+}
+
 size_t kvq_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
                                   int64_t n_int2_tokens, int64_t n_sink, int64_t n_res) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || d != 128) return 0;
@@ -110,14 +137,21 @@ size_t kvq_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
   return workspace_bytes(B, Hq, p.n_splits);
 }
 
-kvq_status kvq_decode_attention(const void *q, kvq_dtype q_dtype, int64_t B, int64_t Hq,
-                                int64_t Hkv, int64_t d, const kvq_int2_cache *kc,
-                                const kvq_int2_cache *vc, int64_t t_begin, int64_t t_end,
-                                kvq_rot rot, const void *R, int group,
-                                const uint16_t *sink_k, const uint16_t *sink_v, int64_t n_sink,
-                                const uint16_t *res_k, const uint16_t *res_v, int64_t n_res,
-                                float softmax_scale, void *out, kvq_dtype out_dtype,
-                                void *workspace, size_t workspace_bytes_given, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by the fixed-length and the variable-length entry points: t_end is
+// the (upper bound of the) end of every sequence's INT2 range; t_ends, when
+// not NULL, holds each sequence's own end (device).
+kvq_status decode_impl(const void *q, kvq_dtype q_dtype, int64_t B, int64_t Hq,
+                       int64_t Hkv, int64_t d, const kvq_int2_cache *kc,
+                       const kvq_int2_cache *vc, int64_t t_begin, int64_t t_end,
+                       const int32_t *t_ends, kvq_rot rot, const void *R, int group,
+                       const uint16_t *sink_k, const uint16_t *sink_v, int64_t n_sink,
+                       const uint16_t *res_k, const uint16_t *res_v, int64_t n_res,
+                       float softmax_scale, void *out, kvq_dtype out_dtype,
+                       void *workspace, size_t workspace_bytes_given, void *stream) {
   if (!valid_dtype(q_dtype) || !valid_dtype(out_dtype)) return KVQ_ERR_INVALID_ARG;
   if (q == nullptr || out == nullptr || !aligned16(q) || !aligned16(out)) return KVQ_ERR_INVALID_ARG;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return KVQ_ERR_INVALID_ARG;
@@ -156,6 +190,7 @@ kvq_status kvq_decode_attention(const void *q, kvq_dtype q_dtype, int64_t B, int
   }
   a.t_begin = t_begin;
   a.n_int2 = n_int2;
+  a.t_ends = n_int2 > 0 ? t_ends : nullptr;
   a.rot = (int)rot;
   a.R = rot == KVQ_ROT_DENSE ? static_cast<const float *>(R) : nullptr;
   a.perm = rot == KVQ_ROT_PERM_HADAMARD ? static_cast<const int32_t *>(R) : nullptr;
@@ -170,6 +205,38 @@ kvq_status kvq_decode_attention(const void *q, kvq_dtype q_dtype, int64_t B, int
   a.n_splits = plan.n_splits;
   hipError_t e = kvq::launch_decode(a, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_decode_attention(const void *q, kvq_dtype q_dtype, int64_t B, int64_t Hq,
+                                int64_t Hkv, int64_t d, const kvq_int2_cache *kc,
+                                const kvq_int2_cache *vc, int64_t t_begin, int64_t t_end,
+                                kvq_rot rot, const void *R, int group,
+                                const uint16_t *sink_k, const uint16_t *sink_v, int64_t n_sink,
+                                const uint16_t *res_k, const uint16_t *res_v, int64_t n_res,
+                                float softmax_scale, void *out, kvq_dtype out_dtype,
+                                void *workspace, size_t workspace_bytes_given, void *stream) {
+  return decode_impl(q, q_dtype, B, Hq, Hkv, d, kc, vc, t_begin, t_end, nullptr, rot, R, group,
+                     sink_k, sink_v, n_sink, res_k, res_v, n_res, softmax_scale, out, out_dtype,
+                     workspace, workspace_bytes_given, stream);
+}
+
+kvq_status kvq_decode_attention_varlen(const void *q, kvq_dtype q_dtype, int64_t B, int64_t Hq,
+                                       int64_t Hkv, int64_t d, const kvq_int2_cache *kc,
+                                       const kvq_int2_cache *vc, int64_t t_begin,
+                                       const int32_t *t_ends, int64_t t_end_max,
+                                       kvq_rot rot, const void *R, int group,
+                                       const uint16_t *sink_k, const uint16_t *sink_v, int64_t n_sink,
+                                       const uint16_t *res_k, const uint16_t *res_v, int64_t n_res,
+                                       float softmax_scale, void *out, kvq_dtype out_dtype,
+                                       void *workspace, size_t workspace_bytes_given, void *stream) {
+  if (t_ends == nullptr || ((uintptr_t)t_ends & 3u) != 0) return KVQ_ERR_INVALID_ARG;
+  return decode_impl(q, q_dtype, B, Hq, Hkv, d, kc, vc, t_begin, t_end_max, t_ends, rot, R, group,
+                     sink_k, sink_v, n_sink, res_k, res_v, n_res, softmax_scale, out, out_dtype,
+                     workspace, workspace_bytes_given, stream);
 }
 
 const char *kvq_status_str(kvq_status s) {

@@ -435,7 +435,7 @@ __global__ __launch_bounds__(64 * WPB) void kv_int2_decode_attn(AttnArgs a) {
   // of a head stream through adjacent tiles together rather than each
   // through a region of its own.
   const int64_t S = a.n_splits;
-  const HeadTiles ht(a.n_int2, a.skip, split, S);
+  const HeadTiles ht(seq_int2(a, b), a.skip, split, S);
   const int64_t mine = ht.mine;
 
   QueryLimbs<GC> q;
@@ -818,7 +818,8 @@ __global__ __launch_bounds__(kCombineThreads) void kv_combine_unrotate(CombineAr
   }
   if (own) {
     const float wint = (M2 == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(M2 - M);
-    const float res = (o * wint + of) / (L2 * wint + Lf);
+    const float den = L2 * wint + Lf;
+    const float res = den > 0.0f ? (o * wint + of) / den : 0.0f;   // no token at all: 0
     if (a.out_f32) reinterpret_cast<float *>(a.out)[bh * kD + c] = res;
     else reinterpret_cast<_Float16 *>(a.out)[bh * kD + c] = (_Float16)res;
   }
@@ -871,7 +872,7 @@ hipError_t launch_decode(const DecodeArgs &d, hipStream_t stream) {
     AttnArgs a;
     a.kcodes = d.kcodes; a.kscales = d.kscales; a.kzeros = d.kzeros; a.kT_cap = d.kT_cap;
     a.vcodes = d.vcodes; a.vscales = d.vscales; a.vzeros = d.vzeros; a.vT_cap = d.vT_cap;
-    a.t_begin = d.t_begin; a.n_int2 = d.n_int2;
+    a.t_begin = d.t_begin; a.n_int2 = d.n_int2; a.t_ends = d.t_ends;
     a.n_splits = d.n_splits;
     a.total_waves = split_units(d.B, d.Hq, d.Hkv) * d.n_splits;
     a.Hkv = (int)d.Hkv; a.Hq = (int)d.Hq; a.G = G;

@@ -25,7 +25,17 @@ struct AttnArgs {
   float qscale;
   // Tile grid shift: tiles start `skip` rows before t_begin (0 <= skip < 16).
   int skip;
+  // Variable-length batch: sequence b's INT2 range ends at t_ends[b] (device
+  // [B]; clamped to [t_begin, t_begin + n_int2]); NULL: every range is n_int2.
+  const int32_t *t_ends;
 };
+
+// INT2 tokens of sequence b.
+__device__ __forceinline__ int64_t seq_int2(const AttnArgs &a, int64_t b) {
+  if (a.t_ends == nullptr) return a.n_int2;
+  const int64_t e = (int64_t)a.t_ends[b] - a.t_begin;
+  return e < 0 ? 0 : (e > a.n_int2 ? a.n_int2 : e);
+}
 
 // Reassemble the fp16 subnormal channel factor: code at position x of a
 // 16-bit half is read with weight 2^(2x-24) (x <= 4) or 2^(2x-30) (x >= 5).

@@ -400,7 +400,7 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
   };
 
   // this wave's full tiles, loads one tile ahead
-  const HeadTiles ht(a.n_int2, a.skip, split, S);
+  const HeadTiles ht(seq_int2(a, b), a.skip, split, S);
   const int64_t mine = ht.mine;
   if (mine > 0) {
     auto row_of = [&](int64_t i) { return ht.full_row(i, split, S); };

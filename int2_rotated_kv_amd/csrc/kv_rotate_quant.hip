@@ -266,6 +266,7 @@ struct RowsKernelArgs {
   int Hkv;
   int n_sides;
   const int32_t *perm;   // permuted Hadamard: [Hkv][128] channel order, else unused
+  const int32_t *offsets;   // per-sequence first slot (device [B]) or NULL: t_offset
 };
 
 // grid: x = token blocks of 64, y = KV head, z = batch * n_sides + side
@@ -294,8 +295,9 @@ __global__ __launch_bounds__(256) void kv_rotate_quant_rows(RowsKernelArgs a) {
   } else {
     quantize_group32_exact(v, w0, w1, sb, zb);
   }
-  if (valid) {
-    const int64_t row = (b * a.Hkv + h) * s.T_cap + a.t_offset + t;
+  const int64_t slot = seq_offset(a.offsets, a.t_offset, b) + t;
+  if (valid && slot >= 0 && slot < s.T_cap) {       // a per-sequence slot outside the cache is skipped
+    const int64_t row = (b * a.Hkv + h) * s.T_cap + slot;
     *reinterpret_cast<uint2 *>(s.codes + row * kCodeBytes + 8 * j) = make_uint2(w0, w1);
     s.scales[row * kNGroups + j] = sb;
     s.zeros[row * kNGroups + j] = zb;
@@ -418,15 +420,21 @@ __device__ __forceinline__ void fwht_f16_body(const RowsKernelArgs &a) {
   rows[2 * lane] = u32x4_t{w[0], w[1], w[2], w[3]};
   rows[2 * lane + 1] = u32x4_t{w[4], w[5], w[6], w[7]};
   __syncthreads();
+  // rows [lo, hi) of the tile are written: below T_new, and inside the cache
+  // (a per-sequence slot outside [0, T_cap) is skipped)
+  const int64_t slot0 = seq_offset(a.offsets, a.t_offset, b) + t0;
   const int64_t n_valid = a.T_new - t0;              // >= 1; rows past it are not ours
-  const int64_t row0 = (b * a.Hkv + h) * s.T_cap + a.t_offset + t0;
+  const int64_t lo = slot0 < 0 ? -slot0 : 0;
+  const int64_t hi = s.T_cap - slot0 < n_valid ? s.T_cap - slot0 : n_valid;
+  const int64_t row0 = (b * a.Hkv + h) * s.T_cap + slot0;
   u32x4_t *cdst = reinterpret_cast<u32x4_t *>(s.codes + row0 * kCodeBytes);
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    if (32 * k + (lane >> 1) < n_valid)
+    const int r = 32 * k + (lane >> 1);
+    if (r >= lo && r < hi)
       __builtin_nontemporal_store(rows[64 * k + lane], cdst + 64 * k + lane);
   }
-  if (lane < n_valid) {
+  if (lane >= lo && lane < hi) {
     const u32x2_t sv = {(uint32_t)sb[0] | ((uint32_t)sb[1] << 16), (uint32_t)sb[2] | ((uint32_t)sb[3] << 16)};
     const u32x2_t zv = {(uint32_t)zb[0] | ((uint32_t)zb[1] << 16), (uint32_t)zb[2] | ((uint32_t)zb[3] << 16)};
     __builtin_nontemporal_store(sv, reinterpret_cast<u32x2_t *>(s.scales + row0 * kNGroups) + lane);
@@ -450,6 +458,7 @@ hipError_t launch_quantize_rows(const QuantArgs &q, hipStream_t stream) {
   a.stride_h = q.stride_h;
   a.T_new = q.T_new;
   a.t_offset = q.t_offset;
+  a.offsets = q.offsets;
   a.Hkv = (int)q.Hkv;
   a.n_sides = q.n_sides;
   a.perm = q.perm;

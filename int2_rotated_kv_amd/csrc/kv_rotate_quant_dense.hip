@@ -59,6 +59,7 @@ struct DenseKernelArgs {
   int64_t n_items;          // n_sides * 32-token tiles; item i = (side i % n_sides, tile i / n_sides)
   int64_t items_per_block;
   const float *R;           // [Hkv][128][128], y = x R
+  const int32_t *offsets;   // per-sequence first slot (device [B]) or NULL: t_offset
 };
 
 // (x << SH) + acc in one instruction (v_lshl_add_u32, SH an inline constant).
@@ -212,8 +213,9 @@ __global__ __launch_bounds__(256, 2) void kv_rotate_quant_dense(DenseKernelArgs 
       const int64_t it = i0 + k * kDenseTiles + u;
       const QuantSide sd = (it & side_shift) ? a.side[1] : a.side[0];
       const int64_t t = (it >> side_shift) * 32 + r;
-      if (it < i1 && t < a.T_new) {
-        const int64_t row = (b * a.Hkv + h) * sd.T_cap + a.t_offset + t;
+      const int64_t slot = seq_offset(a.offsets, a.t_offset, b) + t;
+      if (it < i1 && t < a.T_new && slot >= 0 && slot < sd.T_cap) {   // per-sequence slot inside the cache
+        const int64_t row = (b * a.Hkv + h) * sd.T_cap + slot;
         __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t *>(ob + 16 * tid),
                                     reinterpret_cast<u32x4_t *>(sd.codes + row * kCodeBytes) + (tid & 1));
       }
@@ -223,8 +225,9 @@ __global__ __launch_bounds__(256, 2) void kv_rotate_quant_dense(DenseKernelArgs 
       const int64_t it = i0 + k * kDenseTiles + u;
       const QuantSide sd = (it & side_shift) ? a.side[1] : a.side[0];
       const int64_t t = (it >> side_shift) * 32 + r;
-      if (it < i1 && t < a.T_new) {
-        const int64_t row = (b * a.Hkv + h) * sd.T_cap + a.t_offset + t;
+      const int64_t slot = seq_offset(a.offsets, a.t_offset, b) + t;
+      if (it < i1 && t < a.T_new && slot >= 0 && slot < sd.T_cap) {   // per-sequence slot inside the cache
+        const int64_t row = (b * a.Hkv + h) * sd.T_cap + slot;
         uint16_t *dst = zs ? sd.zeros : sd.scales;
         __builtin_nontemporal_store(
             *reinterpret_cast<const u32x2_t *>(ob + kDenseOutCodes + zs * kDenseTiles * 256 + (u * 32 + r) * 8),
@@ -302,6 +305,7 @@ hipError_t launch_quantize_dense(const QuantArgs &q, hipStream_t stream) {
   a.stride_h = q.stride_h;
   a.T_new = q.T_new;
   a.t_offset = q.t_offset;
+  a.offsets = q.offsets;
   a.Hkv = (int)q.Hkv;
   a.n_sides = q.n_sides;
   a.R = q.R;

@@ -30,6 +30,12 @@ __device__ __forceinline__ uint16_t float_to_half_bits(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
+// First cache slot of sequence b's new rows: the call's t_offset, or
+// offsets[b] for a per-sequence append.
+__device__ __forceinline__ int64_t seq_offset(const int32_t *offsets, int64_t t_offset, int64_t b) {
+  return offsets != nullptr ? (int64_t)offsets[b] : t_offset;
+}
+
 // Cross-lane moves inside a quad of four lanes (DPP quad_perm).
 // kQuadXor1: lane i reads lane i^1; kQuadXor2: lane i reads lane i^2.
 constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]

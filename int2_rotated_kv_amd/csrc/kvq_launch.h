@@ -24,6 +24,7 @@ struct QuantArgs {
   int64_t B, T_new, Hkv;
   int64_t stride_b, stride_t, stride_h;
   int64_t t_offset;
+  const int32_t *offsets;   // per-sequence append: sequence b's rows start at slot offsets[b] (device [B]) or NULL
   int rot;              // 0 none, 1 Hadamard, 2 dense, 3 permuted Hadamard
   const float *R;       // dense: [Hkv][128][128]
   const int32_t *perm;  // permuted Hadamard: [Hkv][128]
@@ -40,6 +41,7 @@ struct DecodeArgs {
   const uint8_t *kcodes; const uint16_t *kscales; const uint16_t *kzeros; int64_t kT_cap;
   const uint8_t *vcodes; const uint16_t *vscales; const uint16_t *vzeros; int64_t vT_cap;
   int64_t t_begin, n_int2;
+  const int32_t *t_ends;   // variable-length batch: per-sequence end (device [B]) or NULL
   int rot; const float *R; const int32_t *perm;
   const uint16_t *sink_k, *sink_v; int64_t n_sink;
   const uint16_t *res_k, *res_v; int64_t n_res;

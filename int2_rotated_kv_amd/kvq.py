@@ -26,8 +26,9 @@ KVQ_ROT_NONE, KVQ_ROT_HADAMARD, KVQ_ROT_DENSE, KVQ_ROT_PERM_HADAMARD = 0, 1, 2, 
 _ROT = {"none": KVQ_ROT_NONE, "hadamard": KVQ_ROT_HADAMARD, "dense": KVQ_ROT_DENSE,
         "perm": KVQ_ROT_PERM_HADAMARD}
 
-EXPORTED_SYMBOLS = ("kvq_quantize", "kvq_decode_workspace_bytes",
-                    "kvq_decode_attention", "kvq_status_str", "kvq_abi_version")
+EXPORTED_SYMBOLS = ("kvq_quantize", "kvq_quantize_at", "kvq_decode_workspace_bytes",
+                    "kvq_decode_attention", "kvq_decode_attention_varlen", "kvq_status_str",
+                    "kvq_abi_version")
 
 D_HEAD = 128
 GROUP = 32
@@ -65,6 +66,13 @@ def load_library() -> ctypes.CDLL:
     lib.kvq_quantize.restype = i32
     lib.kvq_quantize.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, i64, i64,
                                  i32, vp, i32, i64, cp, cp, vp]
+    lib.kvq_quantize_at.restype = i32
+    lib.kvq_quantize_at.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, i64, i64,
+                                    i32, vp, i32, vp, cp, cp, vp]
+    lib.kvq_decode_attention_varlen.restype = i32
+    lib.kvq_decode_attention_varlen.argtypes = [vp, i32, i64, i64, i64, i64, cp, cp, i64, vp, i64,
+                                                i32, vp, i32, vp, vp, i64, vp, vp, i64, f32,
+                                                vp, i32, vp, ctypes.c_size_t, vp]
     lib.kvq_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.kvq_decode_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, i64]
     lib.kvq_decode_attention.restype = i32
@@ -137,11 +145,15 @@ class Int2Cache:
 
 def kvq_quantize(K, V, cache_k: Int2Cache | None, cache_v: Int2Cache | None,
                  rot: str = "hadamard", R: torch.Tensor | None = None,
-                 group: int = GROUP, t_offset: int = 0, stream=None):
+                 group: int = GROUP, t_offset: int = 0, stream=None,
+                 t_offsets: torch.Tensor | None = None):
     """Rotate, quantize and pack K/V rows [B, T_new, Hkv, d] (channel stride 1)
     into cache slots [t_offset, t_offset + T_new).  Either side may be None.
     R: fp32 [Hkv, d, d] for rot="dense"; int32 [Hkv, d] channel permutations
-    for rot="perm" (reorder, then the Hadamard transform); None otherwise."""
+    for rot="perm" (reorder, then the Hadamard transform); None otherwise.
+    t_offsets: int32 [B] on the device: sequence b's rows land at slots
+    [t_offsets[b], t_offsets[b] + T_new) (kvq_quantize_at); t_offset is then
+    unused."""
     x = K if K is not None else V
     for t in (K, V):
         if t is not None and (t.dim() != 4 or t.stride(3) != 1):
@@ -152,7 +164,18 @@ def kvq_quantize(K, V, cache_k: Int2Cache | None, cache_v: Int2Cache | None,
     B, T_new, Hkv, d = x.shape
     kc = cache_k.c_struct() if cache_k is not None else None
     vc = cache_v.c_struct() if cache_v is not None else None
-    st = load_library().kvq_quantize(
+    lib = load_library()
+    if t_offsets is not None:
+        if t_offsets.dtype != torch.int32 or t_offsets.numel() != B:
+            raise ValueError("t_offsets must be int32 [B]")
+        st = lib.kvq_quantize_at(
+            _ptr(K), _ptr(V), _dtype_code(x), B, T_new, Hkv, d,
+            x.stride(0), x.stride(1), x.stride(2), _ROT[rot], _ptr(R), group, _ptr(t_offsets),
+            ctypes.byref(kc) if kc is not None else None,
+            ctypes.byref(vc) if vc is not None else None, _stream(stream))
+        _check(st, "kvq_quantize_at")
+        return
+    st = lib.kvq_quantize(
         _ptr(K), _ptr(V), _dtype_code(x), B, T_new, Hkv, d,
         x.stride(0), x.stride(1), x.stride(2), _ROT[rot], _ptr(R), group, t_offset,
         ctypes.byref(kc) if kc is not None else None,
@@ -171,10 +194,13 @@ def kvq_decode_attention(q: torch.Tensor, cache_k: Int2Cache | None,
                          group: int = GROUP, sink_k=None, sink_v=None, res_k=None,
                          res_v=None, softmax_scale: float = 0.0,
                          out: torch.Tensor | None = None,
-                         workspace: torch.Tensor | None = None, stream=None):
+                         workspace: torch.Tensor | None = None, stream=None,
+                         t_ends: torch.Tensor | None = None):
     """Decode attention for q [B, Hq, d] over INT2 tokens [t_begin, t_end)
     plus optional fp16 sink / residual tokens [B, Hkv, n, d].  Returns out
-    [B, Hq, d] in q's dtype (or writes `out`)."""
+    [B, Hq, d] in q's dtype (or writes `out`).  t_ends: int32 [B] on the
+    device, sequence b's own end (kvq_decode_attention_varlen); t_end is
+    then the upper bound of every t_ends[b]."""
     if not q.is_contiguous():
         raise ValueError("q must be contiguous [B, Hq, d]")
     B, Hq, d = q.shape
@@ -192,7 +218,21 @@ def kvq_decode_attention(q: torch.Tensor, cache_k: Int2Cache | None,
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     kc = cache_k.c_struct() if cache_k is not None else None
     vc = cache_v.c_struct() if cache_v is not None else None
-    st = load_library().kvq_decode_attention(
+    lib = load_library()
+    if t_ends is not None:
+        if t_ends.dtype != torch.int32 or t_ends.numel() != B:
+            raise ValueError("t_ends must be int32 [B]")
+        st = lib.kvq_decode_attention_varlen(
+            _ptr(q), _dtype_code(q), B, Hq, Hkv, d,
+            ctypes.byref(kc) if kc is not None else None,
+            ctypes.byref(vc) if vc is not None else None,
+            t_begin, _ptr(t_ends), t_end, _ROT[rot], _ptr(R), group,
+            _ptr(sink_k), _ptr(sink_v), n_sink, _ptr(res_k), _ptr(res_v), n_res,
+            float(softmax_scale), _ptr(out), _dtype_code(out),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+        _check(st, "kvq_decode_attention_varlen")
+        return out
+    st = lib.kvq_decode_attention(
         _ptr(q), _dtype_code(q), B, Hq, Hkv, d,
         ctypes.byref(kc) if kc is not None else None,
         ctypes.byref(vc) if vc is not None else None,

@@ -157,6 +157,37 @@ def test_decode_rejects(lib, kw, want):
     assert _decode(lib, **kw) == want
 
 
+def test_quantize_at_rejects(lib):
+    a = dict(K=FAKE, V=FAKE, dt=K.KVQ_F16, B=1, T=8, H=2, d=128, sb=8 * 2 * 128,
+             st=2 * 128, sh=128, rot=K.KVQ_ROT_HADAMARD, R=None, group=32)
+    kc, vc = _cache(), _cache()
+
+    def call(offs, T=8, kcache=kc):
+        return lib.kvq_quantize_at(a["K"], a["V"], a["dt"], a["B"], T, a["H"], a["d"], a["sb"],
+                                   a["st"], a["sh"], a["rot"], a["R"], a["group"], offs,
+                                   ctypes.byref(kcache), ctypes.byref(vc), None)
+    assert call(None) == K.KVQ_ERR_INVALID_ARG                 # offsets missing
+    assert call(FAKE + 2) == K.KVQ_ERR_INVALID_ARG             # not 4-byte aligned
+    assert call(FAKE, T=65) == K.KVQ_ERR_INVALID_ARG           # T_new > T_cap
+    assert call(FAKE, T=0) == K.KVQ_OK                         # nothing to write
+
+
+def test_decode_varlen_rejects(lib):
+    def call(t_ends, te_max=64, **kw):
+        a = dict(q=FAKE, qdt=K.KVQ_F16, B=2, Hq=4, Hkv=2, d=128, kc=_cache(), vc=_cache(),
+                 tb=0, rot=K.KVQ_ROT_HADAMARD, R=None, group=32, out=FAKE, odt=K.KVQ_F16,
+                 ws=FAKE * 16, wsb=1 << 30)
+        a.update(kw)
+        return lib.kvq_decode_attention_varlen(
+            a["q"], a["qdt"], a["B"], a["Hq"], a["Hkv"], a["d"], ctypes.byref(a["kc"]),
+            ctypes.byref(a["vc"]), a["tb"], t_ends, te_max, a["rot"], a["R"], a["group"],
+            None, None, 0, None, None, 0, 0.0, a["out"], a["odt"], a["ws"], a["wsb"], None)
+    assert call(None) == K.KVQ_ERR_INVALID_ARG                 # ends missing
+    assert call(FAKE + 2) == K.KVQ_ERR_INVALID_ARG             # not 4-byte aligned
+    assert call(FAKE, te_max=65) == K.KVQ_ERR_INVALID_ARG      # bound beyond T_cap
+    assert call(FAKE, wsb=100) == K.KVQ_ERR_WORKSPACE_TOO_SMALL
+
+
 def test_workspace_bytes():
     # invalid sizes give 0
     assert K.kvq_decode_workspace_bytes(0, 4, 2, 128, 10) == 0

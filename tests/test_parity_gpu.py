@@ -452,6 +452,96 @@ def test_decode_gqa_fp32_query():
     _decode_case(cfg, name="fp32 q G=4")
 
 
+@pytest.mark.parametrize("cid,Hkv,Hq,rot", [(5, 3, 3, "hadamard"), (4, 2, 8, "dense"), (2, 2, 2, "perm")])
+def test_decode_varlen(cid, Hkv, Hq, rot):
+    """Variable-length batch (kvq_decode_attention_varlen): sequence b
+    attends to INT2 tokens [t_begin, t_ends[b]) of its own cache rows, plus
+    the batch's fp16 tokens when the workload has them.  Ends include an
+    empty range, a single token, ranges inside one tile and a full range."""
+    T = 1024
+    extra = dict(t_new=0) if cid == 4 else {}
+    cfg = W.small_config(W.config(cid), T=T, B=5, Hkv=Hkv, Hq=Hq, **extra)
+    tb = cfg.n_sink if cfg.n_sink else 3
+    te_max = T - cfg.n_res
+    ends = np.array([tb, tb + 1, tb + 40, tb + 333, te_max], np.int32)
+    R = W.dense_rotations(cfg) if rot == "dense" else (
+        np.stack([np.random.default_rng(9).permutation(128) for _ in range(cfg.Hkv)]).astype(np.int32)
+        if rot == "perm" else None)
+    Rm = rot_matrix(rot, R)
+    K = W.kv_tokens(cfg, "K")
+    V = W.kv_tokens(cfg, "V")
+    kh = K.permute(0, 2, 1, 3).contiguous().numpy()
+    vh = V.permute(0, 2, 1, 3).contiguous().numpy()
+    kcache = O.quantize_cache(kh, Rm)
+    vcache = O.quantize_cache(vh, Rm)
+    q = W.queries(cfg)
+    fp16 = {}
+    if cfg.n_sink or cfg.n_res:
+        fp16 = dict(sink_k=np.ascontiguousarray(kh[:, :, :cfg.n_sink]).astype(np.float16),
+                    sink_v=np.ascontiguousarray(vh[:, :, :cfg.n_sink]).astype(np.float16),
+                    res_k=np.ascontiguousarray(kh[:, :, T - cfg.n_res:]).astype(np.float16),
+                    res_v=np.ascontiguousarray(vh[:, :, T - cfg.n_res:]).astype(np.float16))
+    up = {k: torch.from_numpy(v).to(DEV) for k, v in fp16.items()}
+    out = kvq.kvq_decode_attention(q.to(DEV), cache_from_numpy(*kcache), cache_from_numpy(*vcache),
+                                   tb, te_max, rot=rot, R=_rot_arg(rot, R),
+                                   t_ends=torch.from_numpy(ends).to(DEV), **up)
+    torch.cuda.synchronize()
+    out = out.float().cpu().numpy()
+    for b in range(cfg.B):
+        sl = lambda c: tuple(a[b:b + 1] for a in c)
+        kwb = {k: v[b:b + 1] for k, v in fp16.items()}
+        if ends[b] == tb and not fp16:
+            assert np.all(out[b] == 0.0)                   # no token at all: zero output
+            continue
+        ref = O.decode_attention(q.numpy()[b:b + 1], sl(kcache), sl(vcache), tb, int(ends[b]), Rm, **kwb)
+        err = normwise_rel_err(out[b:b + 1], ref)
+        _report(f"decode varlen {rot} c{cid} b={b} [{tb},{ends[b]})", normwise=err)
+        assert err <= ATTN_TOL
+
+
+@pytest.mark.parametrize("rot", ["none", "hadamard", "perm", "dense"])
+def test_quantize_at_per_sequence_slots(rot):
+    """kvq_quantize_at: each sequence's new rows land at its own slot;
+    rows whose slot falls outside [0, T_cap) are skipped and every other slot
+    keeps its sentinel bytes.  T_new = 1 (a decode-step append) and T_new = 5."""
+    T_cap = 40
+    cfg = W.small_config(W.config(2), B=4, T=5, Hkv=2, Hq=2)
+    R = W.dense_rotations(cfg) if rot == "dense" else (
+        np.stack([np.random.default_rng(4).permutation(128) for _ in range(cfg.Hkv)]).astype(np.int32)
+        if rot == "perm" else None)
+    Rm = rot_matrix(rot, R)
+    for T_new, offs in ((1, [0, 17, 39, 25]), (5, [3, 37, -2, 20])):
+        x = W.kv_tokens(cfg, "K")[:, :T_new]                      # [B, T_new, H, d] fp16
+        c = empty_cache(cfg.B, cfg.Hkv, T_cap)
+        offsets = torch.tensor(offs, dtype=torch.int32, device=DEV)
+        kvq.kvq_quantize(x.to(DEV), None, c, None, rot=rot, R=_rot_arg(rot, R), t_offsets=offsets)
+        torch.cuda.synchronize()
+        gp, gs, gz = cache_to_numpy(c)
+        op, os_, oz = _oracle_quantize(x, rot, R)                 # [B, H, T_new, ...]
+        xr = x.permute(0, 2, 1, 3).contiguous().numpy()
+        for b in range(cfg.B):
+            written = np.zeros(T_cap, bool)
+            for t in range(T_new):
+                slot = offs[b] + t
+                if not 0 <= slot < T_cap:
+                    continue
+                written[slot] = True
+                g = (gp[b, :, slot:slot + 1], gs[b, :, slot:slot + 1], gz[b, :, slot:slot + 1])
+                o = (op[b, :, t:t + 1], os_[b, :, t:t + 1], oz[b, :, t:t + 1])
+                if rot == "none":
+                    assert np.array_equal(g[0], o[0])
+                    assert np.array_equal(g[1].view(np.uint16), o[1].view(np.uint16))
+                    assert np.array_equal(g[2].view(np.uint16), o[2].view(np.uint16))
+                else:
+                    for h in range(cfg.Hkv):
+                        Rh = Rm[h] if (rot != "hadamard" and np.asarray(Rm).ndim == 3) else Rm
+                        compare_codes_at_ties(xr[b, h, t:t + 1], Rh, tuple(a[h] for a in g),
+                                              tuple(a[h] for a in o), max_frac=1.0)
+            for arr in (gp, gs.view(np.uint8), gz.view(np.uint8)):
+                assert np.all(arr[b][:, ~written] == SENTINEL)
+        _report(f"quantize_at {rot} T_new={T_new}", offsets=offs)
+
+
 # ---------------------------------------------------------- end to end
 def test_end_to_end_dense_gqa():
     """Dense rotation, GQA group 4: GPU quantize (MFMA) -> GPU decode, against
