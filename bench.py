@@ -52,6 +52,10 @@ def parse():
     p.add_argument("--perm", action="store_true",
                    help="reordered Hadamard rotation (each head's channels sorted by outlier "
                         "magnitude ahead of the transform) on a Hadamard workload")
+    p.add_argument("--varlen", action="store_true",
+                   help="serving form: per-sequence lengths drawn in [T/2, T] (seeded); the decode "
+                        "is kvq_decode_attention_varlen and the write phase a decode-step append "
+                        "of one row per sequence (kvq_quantize_at)")
     p.add_argument("--config", type=int, default=3, choices=(3, 4, 5),
                    help="workload id (3 = throughput case, 4 = GQA dense rotation, 5 = sinks)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -142,6 +146,8 @@ def main():
         if rot != "hadamard":
             sys.exit("--perm applies to the Hadamard workloads (--config 3 or 5)")
         rot, workload = "perm", cfg.name + "_perm"
+    if args.varlen:
+        workload += "_varlen"
     print(f"[bench] generating {workload} on the GPU", file=sys.stderr, flush=True)
     t0 = time.time()
     K = W.kv_tokens(cfg, "K", device=dev)
@@ -168,16 +174,31 @@ def main():
     Kq, Vq = K[:, q0:q1], V[:, q0:q1]
     if q0 > tb:                                # rest of the INT2 range, written once (untimed)
         kvq.kvq_quantize(K[:, tb:q0], V[:, tb:q0], ck, cv, rot=rot, R=R, t_offset=tb)
+    ends = None
+    if args.varlen:
+        # the whole INT2 range is written once (untimed); sequence b then holds
+        # INT2 tokens [tb, ends[b]), and a decode step appends one row at its end
+        kvq.kvq_quantize(K[:, q0:q1], V[:, q0:q1], ck, cv, rot=rot, R=R, t_offset=q0)
+        rng = np.random.default_rng(np.random.SeedSequence([1000 + cfg.cid, 77]))
+        n_full = te - tb
+        ends_h = (tb + rng.integers(n_full // 2, n_full + 1, size=B)).astype(np.int32)
+        ends = torch.from_numpy(ends_h).to(dev)
+        slots = ends - 1                         # the append rewrites each sequence's last row
+        Kq, Vq = K[:, tb:tb + 1], V[:, tb:tb + 1]
     torch.cuda.synchronize()
     print(f"[bench] inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
 
     def quant():
-        kvq.kvq_quantize(Kq, Vq, ck, cv, rot=rot, R=R, t_offset=q0)
+        if ends is None:
+            kvq.kvq_quantize(Kq, Vq, ck, cv, rot=rot, R=R, t_offset=q0)
+        else:
+            kvq.kvq_quantize(Kq, Vq, ck, cv, rot=rot, R=R, t_offsets=slots)
 
     def decode():
-        kvq.kvq_decode_attention(q, ck, cv, tb, te, rot=rot, R=R, out=out, workspace=ws, **fp16)
+        kvq.kvq_decode_attention(q, ck, cv, tb, te, rot=rot, R=R, out=out, workspace=ws,
+                                 t_ends=ends, **fp16)
 
     for _ in range(args.warmup):
         quant()
@@ -229,10 +250,13 @@ def main():
     dec_ms = np.array([a.elapsed_time(b) for a, b in d_evs])
     ms_per_step = float(quant_ms.sum() + dec_ms.sum()) / args.steps   # the timed calls, flushes excluded
 
-    n_q, n_int2, n_f16 = q1 - q0, te - tb, cfg.n_sink + cfg.n_res
+    n_q = 1 if ends is not None else q1 - q0
+    n_f16 = cfg.n_sink + cfg.n_res
+    # INT2 (token, head) units the decode reads: every sequence's own range
+    int2_tokens = int((ends_h - tb).sum()) if ends is not None else B * (te - tb)
     r_bytes = {"dense": H * d * d * 4, "perm": H * d * 4}.get(rot, 0)   # R / channel orders, read once
     q_bytes = B * n_q * H * QUANT_BYTES_PER_TOKEN_HEAD + r_bytes
-    d_bytes = (B * n_int2 * H * DECODE_BYTES_PER_TOKEN_HEAD + B * n_f16 * H * FP16_BYTES_PER_TOKEN_HEAD
+    d_bytes = (int2_tokens * H * DECODE_BYTES_PER_TOKEN_HEAD + B * n_f16 * H * FP16_BYTES_PER_TOKEN_HEAD
                + 2 * B * cfg.Hq * d * 2 + r_bytes)
     # mean call time over the timed calls (whole-phase throughput)
     q_ms, d_ms = float(np.mean(quant_ms)), float(np.mean(dec_ms))
@@ -261,7 +285,7 @@ def main():
               "kernel": f"decode call ({'kv_prep_query + ' if prep_kernel else ''}{d_kernel} + kv_combine_unrotate)",
               "algorithmic_bytes_per_launch": d_bytes,
               "bytes_per_unit": DECODE_BYTES_PER_TOKEN_HEAD, "unit_of_work": "(INT2 token, kv head)",
-              "units_per_launch": B * n_int2 * H, "avg_ms": round(d_ms, 4)}
+              "units_per_launch": int2_tokens * H, "avg_ms": round(d_ms, 4)}
     dominant, other = (roof_q, roof_d) if q_ms >= d_ms else (roof_d, roof_q)
 
     rec = {
@@ -271,8 +295,12 @@ def main():
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": workload, "B": B, "T": T, "Hkv": H, "Hq": cfg.Hq, "d": d,
                    "kv_input": "f16", "cache": "int2 codes + f16 scale/zero, group 32",
-                   "rotation": rot, "int2_tokens": [tb, te], "quantize_tokens": [q0, q1],
-                   "fp16_tokens": n_f16},
+                   "rotation": rot, "int2_tokens": [tb, te],
+                   "quantize_tokens": ("one appended row per sequence, at its own end" if ends is not None
+                                       else [q0, q1]),
+                   "fp16_tokens": n_f16,
+                   **({"int2_ends": {"min": int(ends_h.min()), "max": int(ends_h.max()),
+                                     "mean": round(float(ends_h.mean()), 1)}} if ends is not None else {})},
         "decode_pct_of_peak": round(100 * dec_gbs / PEAK_HBM_GBS, 2),
         "decode_ms": round(d_ms, 4), "quantize_ms": round(q_ms, 4),
         "quantize_tokens_per_s": round(q_tok_s, 1),
