@@ -143,8 +143,10 @@ kvq_status kvq_quantize_at(const void *K, const void *V, kvq_dtype in_dtype,
 
 /*
  * kvq_decode_workspace_bytes -- bytes of device workspace that
- * kvq_decode_attention needs for these sizes (0 on invalid sizes).  Pure
- * host arithmetic; calls nothing in HIP.
+ * kvq_decode_attention and kvq_decode_attention_varlen need for these sizes
+ * (0 on invalid sizes; n_int2_tokens = t_end - t_begin, or t_end_max -
+ * t_begin for the variable-length call).  Pure host arithmetic; calls
+ * nothing in HIP.
  */
 size_t kvq_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
                                   int64_t n_int2_tokens, int64_t n_sink,
@@ -186,7 +188,9 @@ kvq_status kvq_decode_attention(const void *q, kvq_dtype q_dtype,
 /*
  * kvq_decode_attention_varlen -- kvq_decode_attention over a batch of
  * sequences of different lengths: sequence b attends to INT2 tokens
- * [t_begin, t_ends[b]) (plus the fp16 tokens, common to the batch).
+ * [t_begin, t_ends[b]) (plus the fp16 tokens, common to the batch).  The
+ * attention waves are shared among the sequences in proportion to their
+ * lengths, so a mixed batch costs about what its tokens cost.
  *
  *  t_ends     int32 [B], device, 4-byte aligned.  Read by the kernels and
  *             clamped to [t_begin, t_end_max].  A sequence left with no

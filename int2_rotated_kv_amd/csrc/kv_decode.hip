@@ -412,8 +412,9 @@ __device__ __forceinline__ float wave_prep_query(const void *q, bool q_f32, int6
   return step;
 }
 
-// WPB waves per workgroup; wave index gw = ((b*Hkv + hkv)*S + split)*G + g,
-// so the G heads of a group (same tiles) are neighbours in one workgroup.
+// WPB waves per workgroup; wave index gw = ((b*Hkv + hkv)*S + split)*G + g
+// for one length (the variable-length map of wave_place otherwise), so the
+// G heads of a group (same tiles) are neighbours in one workgroup.
 template <int WPB>
 __global__ __launch_bounds__(64 * WPB) void kv_int2_decode_attn(AttnArgs a) {
   constexpr int GC = 1;
@@ -421,20 +422,21 @@ __global__ __launch_bounds__(64 * WPB) void kv_int2_decode_attn(AttnArgs a) {
   // wave index made explicitly uniform so every per-wave quantity is scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t gw = (int64_t)blockIdx.x * WPB + wave;
-  if (gw >= a.total_waves) return;           // whole wave leaves together
-  const int gq = (int)(gw % a.G);
-  const int64_t gs = gw / a.G;
-  const int64_t split = gs % a.n_splits;
-  const int64_t bh = gs / a.n_splits;        // b*Hkv + hkv
-  const int hkv = (int)(bh % a.Hkv);
-  const int64_t b = bh / a.Hkv;
+  WavePlace wp;
+  if (!wave_place(a, gw, a.G, wp)) return;   // whole wave leaves together
+  const int gq = wp.sub;
+  const int64_t split = wp.split;
+  const int hkv = wp.hkv;
+  const int64_t b = wp.b;
+  const int64_t bh = b * a.Hkv + hkv;
   const int ts = lane >> 1;                  // token slot 0..31
   const int h = lane & 1;                    // channel half: groups 2h, 2h+1
   // The head's INT2 tokens are cut into 64-token tiles; wave `split` takes
-  // tiles split, split + S, split + 2S, ... (S waves per head), so the waves
+  // tiles split, split + S, split + 2S, ... (S waves per head: the call's
+  // split count, or the sequence's own in a variable-length batch), so the waves
   // of a head stream through adjacent tiles together rather than each
   // through a region of its own.
-  const int64_t S = a.n_splits;
+  const int64_t S = wp.S;
   const HeadTiles ht(seq_int2(a, b), a.skip, split, S);
   const int64_t mine = ht.mine;
 
@@ -576,7 +578,7 @@ __global__ __launch_bounds__(64 * WPB) void kv_int2_decode_attn(AttnArgs a) {
     for (int i = 0; i < 64; ++i) st.acc[g][i] = reduce(st.acc[g][i]);
     if (ts == 0) {
       const int hq = hkv * a.G + gq + g;
-      float *dst = a.partials + ((b * a.Hq + hq) * a.n_splits + split) * kPartialStride;
+      float *dst = a.partials + partial_row(a, wp, hq) * kPartialStride;
 #pragma unroll
       for (int i = 0; i < 64; ++i) {
         const int x = i & 7;
@@ -603,6 +605,8 @@ struct CombineArgs {
   float qscale;
   const float *partials;
   int64_t n_splits;
+  // variable-length batch (t_ends != NULL): the split map of the attention call
+  const int32_t *t_ends; int64_t B, t_begin, n_int2; int skip;
   const uint16_t *sink_k, *sink_v; int64_t n_sink;
   const uint16_t *res_k, *res_v; int64_t n_res;
   void *out;
@@ -646,8 +650,8 @@ __device__ __forceinline__ const uint16_t *fp16_row(const uint16_t *sink, const 
 }
 
 // grid: B*Hq blocks of kCombineThreads threads; threads c < 128 own channel c
-// in the merge and the un-rotation.  Dynamic LDS: n_splits + n_sink + n_res
-// floats.
+// in the merge and the un-rotation.  Dynamic LDS: (most splits of one head)
+// + n_sink + n_res floats.
 __global__ __launch_bounds__(kCombineThreads) void kv_combine_unrotate(CombineArgs a) {
   extern __shared__ float lds[];
   __shared__ float buf[kD];
@@ -660,8 +664,25 @@ __global__ __launch_bounds__(kCombineThreads) void kv_combine_unrotate(CombineAr
   const int64_t b = bh / a.Hq;
   const int hkv = hq / (a.Hq / a.Hkv);
   const int64_t bkv = b * a.Hkv + hkv;
+  // the head's partial rows: S splits, or its sequence's own count
+  int64_t first, ns;
+  int64_t lds_splits = a.n_splits;
+  if (a.t_ends == nullptr) {
+    first = b * a.n_splits;
+    ns = a.n_splits;
+  } else {
+    const SplitMap m = make_split_map(a.t_ends, a.B, a.t_begin, a.n_int2, a.n_splits, a.skip);
+    const int64_t wt = sm_wave_tiles(m);
+    if (wt > 0) {
+      sm_of_seq(m, wt, b, first, ns);
+    } else {
+      first = 0;
+      ns = 0;
+    }
+    lds_splits = varlen_lds_splits(a.B, a.n_splits);
+  }
   float *wsplit = lds;
-  float *pf = lds + a.n_splits;
+  float *pf = lds + lds_splits;
   const int64_t nf = a.n_sink + a.n_res;
   const int rs = c >> 4;                     // token row slot of the fp16 phases
   const int cl = c & 15;                     // channels 8cl .. 8cl+7
@@ -725,12 +746,12 @@ __global__ __launch_bounds__(kCombineThreads) void kv_combine_unrotate(CombineAr
   }
 
   // INT2 partials: M2 = max m_i, weights 2^(m_i - M2)
-  const float *part = a.partials + bh * a.n_splits * kPartialStride;
+  const float *part = a.partials + (first * a.Hq + hq * ns) * kPartialStride;
   float mloc = kNegInf;
-  for (int64_t i = c; i < a.n_splits; i += kCombineThreads) mloc = fmaxf(mloc, part[i * kPartialStride + 128]);
+  for (int64_t i = c; i < ns; i += kCombineThreads) mloc = fmaxf(mloc, part[i * kPartialStride + 128]);
   const float M2 = block_max(mloc, red);
   float lloc = 0.0f;
-  for (int64_t i = c; i < a.n_splits; i += kCombineThreads) {
+  for (int64_t i = c; i < ns; i += kCombineThreads) {
     const float mi = part[i * kPartialStride + 128];
     const float wi = (mi == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(mi - M2);
     wsplit[i] = wi;
@@ -744,12 +765,12 @@ __global__ __launch_bounds__(kCombineThreads) void kv_combine_unrotate(CombineAr
     const int ch = c & 127;
     float o8[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
     int64_t i = c >> 7;
-    for (; i + 14 < a.n_splits; i += 16) {
+    for (; i + 14 < ns; i += 16) {
 #pragma unroll
       for (int u = 0; u < 8; ++u)
         o8[u] = __builtin_fmaf(wsplit[i + 2 * u], part[(i + 2 * u) * kPartialStride + ch], o8[u]);
     }
-    for (; i < a.n_splits; i += 2) o8[0] = __builtin_fmaf(wsplit[i], part[i * kPartialStride + ch], o8[0]);
+    for (; i < ns; i += 2) o8[0] = __builtin_fmaf(wsplit[i], part[i * kPartialStride + ch], o8[0]);
     vred[c] = ((o8[0] + o8[1]) + (o8[2] + o8[3])) + ((o8[4] + o8[5]) + (o8[6] + o8[7]));
     __syncthreads();
     if (own) o = vred[c] + vred[128 + c];
@@ -841,6 +862,12 @@ static int64_t split_units(int64_t B, int64_t Hq, int64_t Hkv) {
   return G == 1 ? B * Hq : B * Hkv * ((G + 3) / 4);
 }
 
+// Tile grid shift: start the grid t_begin mod 16 rows early when both caches
+// keep the rows of a head on 16-row boundaries.
+static int grid_skip(const DecodeArgs &d) {
+  return (d.kT_cap % 16 == 0 && d.vT_cap % 16 == 0) ? (int)(d.t_begin % 16) : 0;
+}
+
 SplitPlan plan_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_int2) {
   SplitPlan p{0};
   if (n_int2 <= 0 || B <= 0 || Hq <= 0 || Hkv <= 0) return p;
@@ -874,14 +901,13 @@ hipError_t launch_decode(const DecodeArgs &d, hipStream_t stream) {
     a.vcodes = d.vcodes; a.vscales = d.vscales; a.vzeros = d.vzeros; a.vT_cap = d.vT_cap;
     a.t_begin = d.t_begin; a.n_int2 = d.n_int2; a.t_ends = d.t_ends;
     a.n_splits = d.n_splits;
-    a.total_waves = split_units(d.B, d.Hq, d.Hkv) * d.n_splits;
+    a.B = d.B;
+    a.total_waves = split_units(d.B, d.Hq, d.Hkv) * d.n_splits;   // B*S split rows
     a.Hkv = (int)d.Hkv; a.Hq = (int)d.Hq; a.G = G;
     a.qprep = reinterpret_cast<const uint32_t *>(d.qprep);
     a.partials = d.partials;
     a.fused_prep = fused_prep;
-    // shift the tile grid onto 16-row boundaries when both caches keep rows
-    // of a head on them
-    a.skip = (d.kT_cap % 16 == 0 && d.vT_cap % 16 == 0) ? (int)(d.t_begin % 16) : 0;
+    a.skip = grid_skip(d);
     a.q = d.q; a.q_f32 = d.q_f32; a.rot = d.rot; a.qscale = d.qscale;
     if (G == 1) {
       hipLaunchKernelGGL(kv_int2_decode_attn<4>, dim3((unsigned)((a.total_waves + 3) / 4)), dim3(256), 0,
@@ -898,10 +924,13 @@ hipError_t launch_decode(const DecodeArgs &d, hipStream_t stream) {
     c.q = d.q; c.q_f32 = d.q_f32; c.out_f32 = d.out_f32;
     c.Hq = (int)d.Hq; c.Hkv = (int)d.Hkv; c.rot = d.rot; c.R = d.R; c.perm = d.perm; c.qscale = d.qscale;
     c.partials = d.partials; c.n_splits = d.n_splits;
+    c.t_ends = d.n_splits > 0 ? d.t_ends : nullptr;
+    c.B = d.B; c.t_begin = d.t_begin; c.n_int2 = d.n_int2; c.skip = grid_skip(d);
     c.sink_k = d.sink_k; c.sink_v = d.sink_v; c.n_sink = d.n_sink;
     c.res_k = d.res_k; c.res_v = d.res_v; c.n_res = d.n_res;
     c.out = d.out;
-    const size_t lds = (size_t)(d.n_splits + d.n_sink + d.n_res) * sizeof(float);
+    const int64_t lds_splits = c.t_ends != nullptr ? varlen_lds_splits(d.B, d.n_splits) : d.n_splits;
+    const size_t lds = (size_t)(lds_splits + d.n_sink + d.n_res) * sizeof(float);
     hipLaunchKernelGGL(kv_combine_unrotate, dim3((unsigned)(d.B * d.Hq)), dim3(kCombineThreads), lds, stream, c);
     return hipGetLastError();
   }

@@ -12,8 +12,9 @@ struct AttnArgs {
   const uint8_t *kcodes; const uint16_t *kscales; const uint16_t *kzeros; int64_t kT_cap;
   const uint8_t *vcodes; const uint16_t *vscales; const uint16_t *vzeros; int64_t vT_cap;
   int64_t t_begin, n_int2;
-  int64_t n_splits;
-  int64_t total_waves;  // B * Hq * n_splits
+  int64_t n_splits;     // splits per head planned for the longest sequence
+  int64_t total_waves;  // grid size in waves
+  int64_t B;
   int Hkv, Hq, G;
   const uint32_t *qprep;
   float *partials;
@@ -35,6 +36,247 @@ __device__ __forceinline__ int64_t seq_int2(const AttnArgs &a, int64_t b) {
   if (a.t_ends == nullptr) return a.n_int2;
   const int64_t e = (int64_t)a.t_ends[b] - a.t_begin;
   return e < 0 ? 0 : (e > a.n_int2 ? a.n_int2 : e);
+}
+
+// ---------------------------------------------------------------------------
+// Splits of a variable-length batch.
+//
+// With one length for the whole batch every head of every sequence gets S
+// waves (splits), planned on the host so that one round of resident waves
+// covers the call.  With per-sequence lengths that plan would leave the waves
+// of short sequences idle once they finish, so the B*S split rows of a head
+// index are instead shared among the sequences by tile count: with w tiles
+// per wave, sequence b gets count_b = ceil(tiles_b / w) rows, and w is the
+// least value (at least 4 tiles, i.e. 256 tokens, and at most kMaxSplits rows
+// per sequence) whose counts fit in B*S rows.  That minimises the longest
+// wave.  Sequence b's rows are first_b .. first_b + count_b - 1, first_b the
+// sum of the earlier counts.  With every sequence as long as the longest,
+// count_b is S or a smaller count whose longest wave is no longer.
+//
+// Waves of sequence b sit at [first_b U, (first_b + count_b) U) with U the
+// waves of one split row (Hkv per-head waves, or Hkv head quads), ordered
+// (KV head, split, sub-wave); partial rows of sequence b sit at
+// [first_b Hq, (first_b + count_b) Hq), ordered (query head, split).
+// Both the attention kernels and the combine derive the same counts from
+// t_ends, so nothing passes between them.  The functions below are
+// wave-level: every lane of the wave calls them with the same arguments,
+// and their results are wave-uniform.
+// ---------------------------------------------------------------------------
+constexpr int64_t kMaxSplits = 4096;
+
+// Most split rows one head of a variable-length batch can take.
+__host__ __device__ __forceinline__ int64_t varlen_lds_splits(int64_t B, int64_t S) {
+  return B * S < kMaxSplits ? B * S : kMaxSplits;
+}
+
+struct SplitMap {
+  const int32_t *t_ends;
+  int64_t B, t_begin, n_int2, S;
+  int skip;
+  uint32_t t_lane;   // B <= 64: tiles of sequence `lane` (0 past B), loaded once
+};
+
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
+  for (int k = 1; k < 64; k <<= 1) v += __shfl_xor(v, k, 64);
+  return uniform64(v);
+}
+
+// Sum / max of a 32-bit value over the wave with DPP and the lane-swap
+// instructions (no LDS round trips); the result is wave-uniform.
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kQuadXor1, 0xF, 0xF, true);
+  v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kQuadXor2, 0xF, 0xF, true);
+  v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false);   // row_ror 4
+  v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);   // row_ror 8
+  const auto r16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = r16[0] + r16[1];
+  const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __builtin_amdgcn_readfirstlane(r32[0] + r32[1]);
+}
+__device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = umax32(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kQuadXor1, 0xF, 0xF, true));
+  v = umax32(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kQuadXor2, 0xF, 0xF, true));
+  v = umax32(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false));
+  v = umax32(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false));
+  const auto r16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = umax32(r16[0], r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __builtin_amdgcn_readfirstlane(umax32(r32[0], r32[1]));
+}
+
+// tiles of sequence b (its INT2 tokens in the shifted 64-row grid); below
+// 2^26 since t_ends are int32
+__device__ __forceinline__ uint32_t sm_tiles(const SplitMap &m, int64_t b) {
+  const int64_t e = (int64_t)m.t_ends[b] - m.t_begin;
+  const int64_t n = e < 0 ? 0 : (e > m.n_int2 ? m.n_int2 : e);
+  return n > 0 ? (uint32_t)((n + m.skip + 63) >> 6) : 0u;
+}
+
+__device__ __forceinline__ SplitMap make_split_map(const int32_t *t_ends, int64_t B, int64_t t_begin,
+                                                   int64_t n_int2, int64_t S, int skip) {
+  SplitMap m{t_ends, B, t_begin, n_int2, S, skip, 0u};
+  const int lane = threadIdx.x & 63;
+  if (B <= 64 && lane < B) m.t_lane = sm_tiles(m, lane);
+  return m;
+}
+
+__device__ __forceinline__ int64_t ceil_div(int64_t x, int64_t w) { return (x + w - 1) / w; }
+// ceil(tiles / tiles-per-wave), both below 2^26
+__device__ __forceinline__ uint32_t tiles_div(uint32_t t, uint32_t w) { return (t + w - 1u) / w; }
+
+// split rows the batch takes at w tiles per wave
+__device__ __forceinline__ int64_t sm_rows(const SplitMap &m, uint32_t w) {
+  if (m.B <= 64) return wave_sum_u32(tiles_div(m.t_lane, w));   // <= 64 * 2^24
+  int64_t r = 0;
+  for (int64_t b = threadIdx.x & 63; b < m.B; b += 64) r += tiles_div(sm_tiles(m, b), w);
+  return wave_sum64(r);
+}
+
+// Tiles per wave; 0 when the batch has no INT2 token.
+__device__ __forceinline__ int64_t sm_wave_tiles(const SplitMap &m) {
+  int64_t tot, tmax, nb;
+  if (m.B <= 64) {
+    tot = wave_sum_u32(m.t_lane);                 // <= 64 * 2^26
+    tmax = wave_max_u32(m.t_lane);
+    nb = wave_sum_u32(m.t_lane > 0u ? 1u : 0u);
+  } else {
+    int64_t t0 = 0, n0 = 0;
+    uint32_t x0 = 0;
+    for (int64_t b = threadIdx.x & 63; b < m.B; b += 64) {
+      const uint32_t t = sm_tiles(m, b);
+      t0 += t;
+      x0 = umax32(x0, t);
+      n0 += t > 0u;
+    }
+    tot = wave_sum64(t0);
+    tmax = wave_max_u32(x0);
+    nb = wave_sum64(n0);
+  }
+  if (tmax == 0) return 0;
+  const int64_t rows = m.B * m.S;
+  // rows(w) >= tot / w, and rows(w) <= tot / w + nb: the least feasible w
+  // lies in [lo, hi], and rows(hi) <= B*S
+  int64_t lo = ceil_div(tot, rows);
+  const int64_t lo_cap = ceil_div(tmax, kMaxSplits);
+  lo = lo > 4 ? lo : 4;
+  lo = lo > lo_cap ? lo : lo_cap;
+  int64_t hi = rows > nb ? ceil_div(tot, rows - nb) : tmax;
+  hi = hi > lo ? hi : lo;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (sm_rows(m, (uint32_t)mid) <= rows) hi = mid;
+    else lo = mid + 1;
+  }
+  return lo;
+}
+
+// Sequence b's first split row and split count, w tiles per wave.
+__device__ __forceinline__ void sm_of_seq(const SplitMap &m, int64_t w, int64_t b, int64_t &first,
+                                          int64_t &count) {
+  if (m.B <= 64) {
+    const uint32_t c = tiles_div(m.t_lane, (uint32_t)w);
+    uint32_t f = 0;
+    for (int i = 0; i < (int)b; ++i) f += __builtin_amdgcn_readlane(c, i);
+    first = f;
+    count = __builtin_amdgcn_readlane(c, (int)b);
+    return;
+  }
+  int64_t f = 0;
+  for (int64_t i = threadIdx.x & 63; i < b; i += 64) f += tiles_div(sm_tiles(m, i), (uint32_t)w);
+  first = wave_sum64(f);
+  count = __builtin_amdgcn_readfirstlane(tiles_div(sm_tiles(m, b), (uint32_t)w));
+}
+
+// The sequence that owns split row r, with its first row and count; false
+// when r lies past the last row.
+__device__ __forceinline__ bool sm_find_row(const SplitMap &m, int64_t w, int64_t r, int64_t &b,
+                                            int64_t &first, int64_t &count) {
+  if (m.B <= 64) {
+    // one sequence per lane: walk the counts in the scalar unit
+    const uint32_t c = tiles_div(m.t_lane, (uint32_t)w);
+    int64_t f = 0;
+    for (int i = 0; i < (int)m.B; ++i) {
+      const int64_t ci = __builtin_amdgcn_readlane(c, i);
+      if (r < f + ci) {
+        b = i;
+        first = f;
+        count = ci;
+        return true;
+      }
+      f += ci;
+    }
+    return false;
+  }
+  const int lane = threadIdx.x & 63;
+  int64_t carry = 0;
+  for (int64_t base = 0; base < m.B; base += 64) {
+    const int64_t bb = base + lane;
+    const int64_t c = bb < m.B ? tiles_div(sm_tiles(m, bb), (uint32_t)w) : 0;
+    int64_t incl = c;                           // inclusive prefix over the chunk
+    for (int k = 1; k < 64; k <<= 1) {
+      const int64_t y = __shfl_up(incl, (unsigned)k, 64);
+      if (lane >= k) incl += y;
+    }
+    incl += carry;
+    // the prefix is non-decreasing, so the sequences ending at or before row
+    // r are the first k lanes, and lane k (if any) holds row r
+    const int k = __popcll(__ballot(bb < m.B && incl <= r));
+    if (k < 64 && base + k < m.B) {
+      b = base + k;
+      count = uniform64(__shfl(c, k, 64));
+      first = uniform64(__shfl(incl, k, 64)) - count;
+      return true;
+    }
+    carry = uniform64(__shfl(incl, 63, 64));
+  }
+  return false;
+}
+
+// A wave's place in the grid: sequence, KV head, split, sub-wave (query head
+// of a group, or head quad; `per` of them per split), and its sequence's
+// split count and first split row.  False for a wave with nothing to do.
+struct WavePlace {
+  int64_t b, split, S, first;
+  int hkv, sub;
+};
+
+__device__ __forceinline__ bool wave_place(const AttnArgs &a, int64_t gw, int per, WavePlace &w) {
+  if (gw >= a.total_waves) return false;
+  if (a.t_ends == nullptr) {
+    w.sub = (int)(gw % per);
+    const int64_t gs = gw / per;
+    w.split = gs % a.n_splits;
+    const int64_t bh = gs / a.n_splits;
+    w.hkv = (int)(bh % a.Hkv);
+    w.b = bh / a.Hkv;
+    w.S = a.n_splits;
+    w.first = w.b * a.n_splits;
+    return true;
+  }
+  const SplitMap m = make_split_map(a.t_ends, a.B, a.t_begin, a.n_int2, a.n_splits, a.skip);
+  const int64_t wt = sm_wave_tiles(m);
+  if (wt == 0) return false;
+  const int64_t U = (int64_t)a.Hkv * per;
+  if (!sm_find_row(m, wt, gw / U, w.b, w.first, w.S)) return false;
+  const int64_t local = gw - w.first * U;
+  const int64_t per_head = w.S * per;
+  w.hkv = (int)(local / per_head);
+  const int64_t rem = local - (int64_t)w.hkv * per_head;
+  w.split = rem / per;
+  w.sub = (int)(rem - w.split * per);
+  return true;
+}
+
+// Partial row of query head hq for a wave at place w.
+__device__ __forceinline__ int64_t partial_row(const AttnArgs &a, const WavePlace &w, int hq) {
+  return w.first * a.Hq + (int64_t)hq * w.S + w.split;
 }
 
 // Reassemble the fp16 subnormal channel factor: code at position x of a

@@ -146,24 +146,25 @@ __device__ __forceinline__ half8_t mq_bvals(uint32_t y02, uint32_t y13, uint32_t
 }
 
 // grid: ceil(total_waves / 4) workgroups of 4 waves; wave index
-// gw = ((b*Hkv + hkv)*S + split)*quads + quad.
+// gw = ((b*Hkv + hkv)*S + split)*quads + quad for one length, the
+// variable-length map of wave_place otherwise.
 __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArgs a) {
   __shared__ uint32_t lds_all[kMqWaves][kMqLdsDwords];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t gw = (int64_t)blockIdx.x * kMqWaves + wave;
-  if (gw >= a.total_waves) return;                  // whole wave leaves; no barrier follows
+  const int quads = (a.G + kMqHeads - 1) / kMqHeads;
+  WavePlace wp;
+  if (!wave_place(a, gw, quads, wp)) return;        // whole wave leaves; no barrier follows
   uint32_t *rec = lds_all[wave] + kMqRecOff;        // [64 tokens][kMqRecDwords]
   uint8_t *vcl = reinterpret_cast<uint8_t *>(lds_all[wave] + kMqCodeOff);   // [64 tokens][32 bytes]
   _Float16 *pw = reinterpret_cast<_Float16 *>(lds_all[wave] + kMqPwOff);     // [head][64 tokens]
-  const int quads = (a.G + kMqHeads - 1) / kMqHeads;
-  const int quad = (int)(gw % quads);
-  const int64_t gs = gw / quads;
-  const int64_t split = gs % a.n_splits;
-  const int64_t bh = gs / a.n_splits;
-  const int hkv = (int)(bh % a.Hkv);
-  const int64_t b = bh / a.Hkv;
-  const int64_t S = a.n_splits;
+  const int quad = wp.sub;
+  const int64_t split = wp.split;
+  const int hkv = wp.hkv;
+  const int64_t b = wp.b;
+  const int64_t bh = b * a.Hkv + hkv;
+  const int64_t S = wp.S;
 
   // ---- query: K-side data of head g = lane/16, A operands of row lane%16
   const int gk = lane >> 4;
@@ -437,7 +438,7 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
   const int g = lane >> 4;
   if (kMqHeads * quad + g < a.G) {
     const int hq = hkv * a.G + kMqHeads * quad + g;
-    float *dst = a.partials + ((b * a.Hq + hq) * S + split) * kPartialStride;
+    float *dst = a.partials + partial_row(a, wp, hq) * kPartialStride;
     const int jo = vn >> 2;
     const float cj = jo == 0 ? corr[0] : jo == 1 ? corr[1] : jo == 2 ? corr[2] : corr[3];
     const float4v_t c4v = {cj, cj, cj, cj};

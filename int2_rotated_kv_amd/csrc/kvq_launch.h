@@ -49,8 +49,10 @@ struct DecodeArgs {
   void *out;
   // workspace carve-up (device pointers)
   int32_t *qprep;       // [B][Hq][kQprepDwordsPerHead] dwords
-  float *partials;      // [B][Hq][n_splits][kPartialStride]
+  float *partials;      // [B][Hq][n_splits][kPartialStride]; variable length: the same
+                        // B*Hq*n_splits rows, shared by sequence
   int64_t n_splits;     // waves per (b, query head), each taking every n_splits-th tile
+                        // (variable length: planned for the longest sequence)
 };
 
 // Split plan shared by the workspace query and the attention call.

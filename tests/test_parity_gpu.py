@@ -499,6 +499,59 @@ def test_decode_varlen(cid, Hkv, Hq, rot):
         assert err <= ATTN_TOL
 
 
+@pytest.mark.parametrize("B,Hq", [(64, 1), (70, 1), (67, 4), (130, 1)])
+def test_decode_varlen_many_sequences(B, Hq):
+    """Variable-length batches of many sequences with a skewed length mix:
+    one sequence spans the whole range, the rest are short or empty.  The
+    attention waves are shared among the sequences by tile count, so this
+    covers batches of one wave's width (64) and wider ones, for one query
+    head per KV head and for a query group.
+
+    Checks: (1) each sequence's output matches a one-sequence call over the
+    same range (which other tests hold to the oracle), so every sequence
+    got exactly its own tiles; (2) against the oracle, the error relative to
+    the largest attended value row.  A short range's output can be far
+    smaller than the rows it averages (they cancel), so the per-row
+    normwise reading would measure the cancellation, not the arithmetic,
+    whose error scales with the value rows."""
+    T = 1300
+    cfg = W.small_config(W.config(1), T=T, B=B, Hkv=1, Hq=Hq)
+    tb, te_max = 5, T
+    rng = np.random.default_rng(1000 + B)
+    ends = (tb + rng.integers(0, 200, B)).astype(np.int32)
+    ends[rng.random(B) < 0.2] = tb                         # empty sequences
+    ends[B // 3] = te_max                                  # one long sequence
+    K = W.kv_tokens(cfg, "K")
+    V = W.kv_tokens(cfg, "V")
+    kh = K.permute(0, 2, 1, 3).contiguous().numpy()
+    vh = V.permute(0, 2, 1, 3).contiguous().numpy()
+    Rm = rot_matrix("hadamard", None)
+    kcache = O.quantize_cache(kh, Rm)
+    vcache = O.quantize_cache(vh, Rm)
+    q = W.queries(cfg)
+    out = kvq.kvq_decode_attention(q.to(DEV), cache_from_numpy(*kcache), cache_from_numpy(*vcache),
+                                   tb, te_max, rot="hadamard", t_ends=torch.from_numpy(ends).to(DEV))
+    torch.cuda.synchronize()
+    out = out.float().cpu().numpy()
+    worst_single, worst_oracle = 0.0, 0.0
+    for b in range(B):
+        if ends[b] == tb:
+            assert np.all(out[b] == 0.0)                   # no token at all: zero output
+            continue
+        sl = lambda c: tuple(a[b:b + 1] for a in c)
+        one = kvq.kvq_decode_attention(q[b:b + 1].to(DEV), cache_from_numpy(*sl(kcache)),
+                                       cache_from_numpy(*sl(vcache)), tb, int(ends[b]), rot="hadamard")
+        torch.cuda.synchronize()
+        worst_single = max(worst_single, normwise_rel_err(out[b:b + 1], one.float().cpu().numpy()))
+        ref = O.decode_attention(q.numpy()[b:b + 1], sl(kcache), sl(vcache), tb, int(ends[b]), Rm)
+        vrows = O.dequantize(O.unpack_codes(vcache[0][b, 0, tb:ends[b]]), vcache[1][b, 0, tb:ends[b]],
+                             vcache[2][b, 0, tb:ends[b]]) @ Rm.T          # attended rows, original basis
+        worst_oracle = max(worst_oracle, float(np.abs(out[b] - ref[0]).max() / np.abs(vrows).max()))
+    _report(f"decode varlen B={B} Hq={Hq}", vs_single=worst_single, vs_oracle_value_scale=worst_oracle)
+    assert worst_single <= 1e-4
+    assert worst_oracle <= ATTN_TOL
+
+
 @pytest.mark.parametrize("rot", ["none", "hadamard", "perm", "dense"])
 def test_quantize_at_per_sequence_slots(rot):
     """kvq_quantize_at: each sequence's new rows land at its own slot;
