@@ -131,21 +131,25 @@ __device__ __forceinline__ void quantize_group32_fwht(const float (&z)[32], uint
   }
   const bool degenerate = (sf == 0.0f);
   const float inv = __builtin_amdgcn_rcpf(degenerate ? 1.0f : sf);
-  // Fast form: x = z * (c/scale) - zero/scale in one FMA, clamped to [0, 3],
-  // then v_cvt_pk_u8_f32 rounds half to even and drops the code into byte
-  // i/4 of word i%4; the four words merge into the 2-bit layout.  Folding
-  // 1/scale into the constants adds an error of about (|y| + |zero|)/scale
-  // ulps, so the wave takes it only while every group has |zero| <= 8 scale
-  // (then the argument is within ~1e-6 of the exact one); otherwise the
-  // sequence below keeps y - zero to one rounding.
+  // Fast form: x = z * (c/scale) - zero/scale in one FMA, then
+  // v_cvt_pk_u8_f32 rounds half to even, saturates below 0 and drops the
+  // code into byte i/4 of word i%4; the four words merge into the 2-bit
+  // layout.  Folding 1/scale into the constants adds an error of about
+  // (|y| + |zero|)/scale ulps, so the wave takes it only while every group
+  // has |zero| <= 8 scale and a normal fp16 scale.  Then x is within 0.006 of
+  // (y - min)/(range/3), which lies in [0, 3]: the fp16 roundings of the
+  // scale and the zero move it by at most 3 * 2^-11 and 8 * 2^-11.  So x
+  // rounds to a code in [0, 3] with no clamp, and the codes are those of the
+  // clamped argument.  Otherwise the sequence below keeps y - zero to one
+  // rounding.
   const float ci = c * inv, nzi = -zf * inv;
   uint32_t a, b;
-  if (!__builtin_amdgcn_ballot_w64(fabsf(nzi) > 8.0f)) {
+  if (!__builtin_amdgcn_ballot_w64(fabsf(nzi) > 8.0f || sf < kMinNormalHalf)) {
     auto pk = [&](int base) {
       uint32_t D[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float x = __builtin_amdgcn_fmed3f(__builtin_fmaf(z[base + i], ci, nzi), 0.0f, 3.0f);
+        const float x = __builtin_fmaf(z[base + i], ci, nzi);
         D[i & 3] = __builtin_amdgcn_cvt_pk_u8_f32(x, (uint32_t)(i >> 2), D[i & 3]);
       }
       return D[0] | (D[1] << 2) | (D[2] << 4) | (D[3] << 6);
@@ -305,12 +309,13 @@ __global__ __launch_bounds__(256) void kv_rotate_quant_rows(RowsKernelArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// fp16 input + Hadamard: one row per lane, all seven butterfly stages in
-// registers (no cross-lane traffic).  A wave handles 64 consecutive tokens
-// of one (batch, head, side).  Rows are first brought into LDS with fully
-// coalesced 16-byte loads (16 lanes per 256-byte row) and read back one row
-// per lane; rows are padded by 16 bytes so the row-per-lane reads hit
-// distinct banks.
+// fp16 input + Hadamard.  A wave handles 64 consecutive tokens of one
+// (batch, head, side).  Rows are first brought into LDS with fully coalesced
+// 16-byte loads (16 lanes per 256-byte row); rows are padded by 16 bytes so
+// that 16 lanes reading 16 bytes each from 16 different rows hit distinct
+// banks.  The transform then takes part of the butterfly onto the matrix
+// cores (below), each quantization group is quantized by the lane that
+// holds it, and the codes go back through LDS to whole-row stores.
 //
 // Block order puts the head index fastest, so the waves resident at one
 // time read whole token records (all heads of a token are adjacent in the
@@ -333,11 +338,10 @@ __device__ __forceinline__ void fwht_f16_body(const RowsKernelArgs &a) {
   __shared__ uint32_t stage[64 * kStageRowDwords];
   const int lane = threadIdx.x;
   const int h = (int)(blockIdx.x % (unsigned)a.Hkv);
-  const int64_t tb = blockIdx.x / (unsigned)a.Hkv;
+  const int64_t t0 = (int64_t)(blockIdx.x / (unsigned)a.Hkv) * 64;
   const int sidx = (int)(blockIdx.z % (unsigned)a.n_sides);
   const int64_t b = blockIdx.z / (unsigned)a.n_sides;
   const QuantSide s = sidx ? a.side[1] : a.side[0];
-  const int64_t t0 = tb * 64;
   const _Float16 *base = reinterpret_cast<const _Float16 *>(s.x) + b * a.stride_b +
                          (int64_t)h * a.stride_h;
 
@@ -369,76 +373,118 @@ __device__ __forceinline__ void fwht_f16_body(const RowsKernelArgs &a) {
       *reinterpret_cast<u32x4_t *>(&stage[(4 * i + r0) * kStageRowDwords + 4 * chunk]) = u;
     }
   };
+  // all 16 loads of the tile first, then the LDS writes
+  u32x4_t ld[16];
   if (t0 + 64 <= a.T_new) {
     const u32x4_t *src = reinterpret_cast<const u32x4_t *>(base + (t0 + r0) * a.stride_t) + chunk;
     const int64_t step = 4 * a.stride_t / 8;        // 4 rows, in 16-byte units
 #pragma unroll
-    for (int i = 0; i < 16; ++i) stage_row(i, __builtin_nontemporal_load(src + i * step));
-  } else {
+    for (int i = 0; i < 16; ++i) ld[i] = __builtin_nontemporal_load(src + i * step);
+  } else {                                          // rows past T_new re-read row 0
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int64_t t = t0 + 4 * i + r0;
       const int64_t tl = t < a.T_new ? t : 0;
-      stage_row(i, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(base + tl * a.stride_t) + chunk));
+      ld[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(base + tl * a.stride_t) + chunk);
     }
   }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) stage_row(i, ld[i]);
   __syncthreads();
 
-  float v[128];
+  // Transform.  H128 = H16 (channel bits 3..6) x H8 (bits 0..2), and the
+  // factors commute.  The H16 part runs on the matrix cores straight from the
+  // fp16 rows: for each low index c0 = 0..7, D = H16 * X_c0 with
+  // X_c0[k][n] = x[token n][c0 + 8k] (16 tokens per product, fp32
+  // accumulation of exact +-x products).  v_mfma_f32_16x16x16_f16 leaves
+  // D[4q + r][n] in lane 16q + n, so after the eight products lane (n, q)
+  // holds channels c0 + 8(4q + r) of token n: exactly quantization group q.
+  // The H8 part (three butterfly stages over c0) then runs in registers, and
+  // the group is quantized and stored by the lane that holds it.
+  const int n = lane & 15;                 // token within a group of 16
+  const int q = lane >> 4;                 // quantization group
+  // A operand: H16[m = lane%16][k = 4(lane/16) + i] = (-1)^popcount(m & k)
+  half4_t hA;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const u32x4_t u = *reinterpret_cast<const u32x4_t *>(&stage[lane * kStageRowDwords + 4 * k]);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[8 * k + 2 * e] = mix_sum(w[e]);          // FWHT stage 1 on the way in
-      v[8 * k + 2 * e + 1] = mix_diff(w[e]);
-    }
-  }
-#pragma unroll
-  for (int hs = 2; hs < 128; hs <<= 1) {
-#pragma unroll
-    for (int i = 0; i < 128; ++i) {
-      if ((i & hs) == 0) {
-        const float x = v[i], y = v[i + hs];
-        v[i] = x + y;
-        v[i + hs] = x - y;
-      }
-    }
-  }
-  uint32_t w[8];
-  uint16_t sb[4], zb[4];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const float(&z)[32] = *reinterpret_cast<const float(*)[32]>(&v[32 * g]);
-    quantize_group32_fwht(z, w[2 * g], w[2 * g + 1], sb[g], zb[g]);
-  }
-  // code rows through LDS: entry 2r + k holds 16 bytes k of row r, so
-  // entries [64k, 64k + 64) are rows 32k .. 32k + 31 in cache order
-  u32x4_t *rows = reinterpret_cast<u32x4_t *>(stage);
-  __syncthreads();                                   // row reads of the stage are done
-  rows[2 * lane] = u32x4_t{w[0], w[1], w[2], w[3]};
-  rows[2 * lane + 1] = u32x4_t{w[4], w[5], w[6], w[7]};
-  __syncthreads();
-  // rows [lo, hi) of the tile are written: below T_new, and inside the cache
-  // (a per-sequence slot outside [0, T_cap) is skipped)
+  for (int i = 0; i < 4; ++i)
+    hA[i] = (__builtin_popcount((unsigned)(n & (4 * q + i))) & 1) ? (_Float16)-1.0f : (_Float16)1.0f;
   const int64_t slot0 = seq_offset(a.offsets, a.t_offset, b) + t0;
   const int64_t n_valid = a.T_new - t0;              // >= 1; rows past it are not ours
-  const int64_t lo = slot0 < 0 ? -slot0 : 0;
+  const int64_t lo = slot0 < 0 ? -slot0 : 0;         // rows [lo, hi) of the tile are written
   const int64_t hi = s.T_cap - slot0 < n_valid ? s.T_cap - slot0 : n_valid;
   const int64_t row0 = (b * a.Hkv + h) * s.T_cap + slot0;
-  u32x4_t *cdst = reinterpret_cast<u32x4_t *>(s.codes + row0 * kCodeBytes);
+
+  uint32_t cw[4][2], csz[4];                         // codes and scale | zero << 16 of row 16g + n
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int r = 32 * k + (lane >> 1);
-    if (r >= lo && r < hi)
-      __builtin_nontemporal_store(rows[64 * k + lane], cdst + 64 * k + lane);
+  for (int g = 0; g < 4; ++g) {
+    const int r = 16 * g + n;                        // the lane's token row in the tile
+    // channels 8(4q + i) .. 8(4q + i) + 7 of row r, i = 0..3
+    u32x4_t u[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      u[i] = *reinterpret_cast<const u32x4_t *>(&stage[r * kStageRowDwords + 4 * (4 * q + i)]);
+    float z[32];                                     // z[c0 + 8r'] = channel c0 + 8(4q + r') after H16
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t w0 = u[0][e], w1 = u[1][e], w2 = u[2][e], w3 = u[3][e];
+      // B operands for c0 = 2e (low halves) and 2e + 1 (high halves)
+      const uint32_t lo01 = __builtin_amdgcn_perm(w1, w0, 0x05040100u), lo23 = __builtin_amdgcn_perm(w3, w2, 0x05040100u);
+      const uint32_t hi01 = __builtin_amdgcn_perm(w1, w0, 0x07060302u), hi23 = __builtin_amdgcn_perm(w3, w2, 0x07060302u);
+      const half4_t bl = __builtin_bit_cast(half4_t, u32x2_t{lo01, lo23});
+      const half4_t bh = __builtin_bit_cast(half4_t, u32x2_t{hi01, hi23});
+      const float4_t dl = __builtin_amdgcn_mfma_f32_16x16x16f16(hA, bl, float4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+      const float4_t dh = __builtin_amdgcn_mfma_f32_16x16x16f16(hA, bh, float4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        z[2 * e + 8 * rr] = dl[rr];
+        z[2 * e + 1 + 8 * rr] = dh[rr];
+      }
+    }
+    // H8 over c0 for each r': three butterfly stages in registers
+#pragma unroll
+    for (int hs = 1; hs < 8; hs <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if ((i & hs) == 0) {
+          const float x = z[i], y = z[i + hs];
+          z[i] = x + y;
+          z[i + hs] = x - y;
+        }
+      }
+    }
+    uint16_t sb, zb;
+    quantize_group32_fwht(z, cw[g][0], cw[g][1], sb, zb);
+    csz[g] = (uint32_t)sb | ((uint32_t)zb << 16);
   }
-  if (lane >= lo && lane < hi) {
-    const u32x2_t sv = {(uint32_t)sb[0] | ((uint32_t)sb[1] << 16), (uint32_t)sb[2] | ((uint32_t)sb[3] << 16)};
-    const u32x2_t zv = {(uint32_t)zb[0] | ((uint32_t)zb[1] << 16), (uint32_t)zb[2] | ((uint32_t)zb[3] << 16)};
-    __builtin_nontemporal_store(sv, reinterpret_cast<u32x2_t *>(s.scales + row0 * kNGroups) + lane);
-    __builtin_nontemporal_store(zv, reinterpret_cast<u32x2_t *>(s.zeros + row0 * kNGroups) + lane);
+  // Back through LDS to one row per lane (codes: entry 2r + k holds bytes
+  // 16k .. 16k + 15 of row r; then scale | zero << 16 of each group), so
+  // each code store writes 1 KiB of consecutive cache rows and each lane
+  // writes its row's scales and zeros as 8 bytes; storing the 8-byte and
+  // 2-byte pieces straight from the transform layout measured slower.
+  __syncthreads();                                   // the stage is read
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int r = 16 * g + n;
+    *reinterpret_cast<u32x2_t *>(&stage[r * 8 + 2 * q]) = u32x2_t{cw[g][0], cw[g][1]};
+    stage[512 + r * 4 + q] = csz[g];
+  }
+  __syncthreads();
+  {
+    u32x4_t *rows = reinterpret_cast<u32x4_t *>(stage);
+    u32x4_t *cdst = reinterpret_cast<u32x4_t *>(s.codes + row0 * kCodeBytes);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int r = 32 * kk + (lane >> 1);
+      if (r >= lo && r < hi)
+        __builtin_nontemporal_store(rows[64 * kk + lane], cdst + 64 * kk + lane);
+    }
+    if (lane >= lo && lane < hi) {
+      const u32x4_t e = *reinterpret_cast<const u32x4_t *>(&stage[512 + lane * 4]);
+      const u32x2_t sv = {__builtin_amdgcn_perm(e.y, e.x, 0x05040100u), __builtin_amdgcn_perm(e.w, e.z, 0x05040100u)};
+      const u32x2_t zv = {__builtin_amdgcn_perm(e.y, e.x, 0x07060302u), __builtin_amdgcn_perm(e.w, e.z, 0x07060302u)};
+      __builtin_nontemporal_store(sv, reinterpret_cast<u32x2_t *>(s.scales + row0 * kNGroups) + lane);
+      __builtin_nontemporal_store(zv, reinterpret_cast<u32x2_t *>(s.zeros + row0 * kNGroups) + lane);
+    }
   }
 }
 

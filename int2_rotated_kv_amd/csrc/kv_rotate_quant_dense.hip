@@ -119,17 +119,19 @@ __device__ __forceinline__ void dense_group_codes(const float16_t &y, uint32_t &
   // scale 0: every code is 0 (inv = 1 and the clamp to [0, 0] give that)
   const float inv = __builtin_amdgcn_rcpf(sf == 0.0f ? 1.0f : sf);
   const float nzi = -zf * inv;
-  // Three instructions per code while every group of the wave has
-  // |zero| <= 8 scale: x = y/scale - zero/scale in one FMA, clamp to [0, 3],
-  // v_cvt_pk_u8_f32 (round half to even) into byte r/4 of word r%4; the
-  // words merge into the 2-bit layout.  Otherwise (or for a zero scale) the
-  // sequence below keeps y - zero to one rounding.
+  // Two instructions per code while every group of the wave has
+  // |zero| <= 8 scale and a normal fp16 scale: x = y/scale - zero/scale in
+  // one FMA, then v_cvt_pk_u8_f32 (round half to even, saturating below 0)
+  // into byte r/4 of word r%4; the words merge into the 2-bit layout.  x is
+  // then within 0.006 of (y - min)/(range/3), which lies in [0, 3], so it
+  // rounds to a code in [0, 3] with no clamp.  Otherwise (or for a zero
+  // scale) the sequence below keeps y - zero to one rounding.
   uint32_t mine;
-  if (!__builtin_amdgcn_ballot_w64(fabsf(nzi) > 8.0f || sf == 0.0f)) {
+  if (!__builtin_amdgcn_ballot_w64(fabsf(nzi) > 8.0f || sf < kMinNormalHalf)) {
     uint32_t D[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float x = __builtin_amdgcn_fmed3f(__builtin_fmaf(y[r], inv, nzi), 0.0f, 3.0f);
+      const float x = __builtin_fmaf(y[r], inv, nzi);
       D[r & 3] = __builtin_amdgcn_cvt_pk_u8_f32(x, (uint32_t)(r >> 2), D[r & 3]);
     }
     mine = D[0] | (D[1] << 2) | (D[2] << 4) | (D[3] << 6);

@@ -10,6 +10,7 @@ constexpr int kD = 128;        // head dimension
 constexpr int kGroup = 32;     // channels per scale/zero group
 constexpr int kNGroups = kD / kGroup;
 constexpr int kCodeBytes = kD / 4;   // packed bytes per row
+constexpr float kMinNormalHalf = 6.103515625e-05f;   // 2^-14, least normal fp16
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
