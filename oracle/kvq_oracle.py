@@ -23,6 +23,12 @@ What it computes, and where that comes from:
   The pages name INT2 but fix none of these parameters; they are this
   library's format, and every step below that the pages leave open is a
   stated reading (listed in the design notes).
+* Other bit widths: the same codec with b = 1 or 4 bits per code
+  (2**b - 1 levels above the zero-point, 8/b codes per byte), so that keys
+  and values can be kept at different widths.  The pages name mixed-bit
+  schemes and binary codes as directions only (OptR page, the future-work
+  paragraph and "Why It Matters"; the mixed-precision entries of the
+  related-work list) and fix nothing about them; b = 2 is the INT2 codec.
 
 Precision: the rotation and the attention are evaluated in fp64.  The
 quantizer is a fixed sequence of IEEE binary32 operations (subtract,
@@ -32,6 +38,8 @@ written in float32 here.  No fused multiply-add is used anywhere.
 
 Cache layout (the library's boundary format, [B][Hkv][T_cap][...]):
     codes  uint8   [..., d/4]  channel 4*b+i in bits 2i..2i+1 of byte b
+                   (b-bit codes: [..., d*b/8], channel (8/b)*j+i in bits
+                   b*i .. b*i+b-1 of byte j)
     scales float16 [..., d/group]
     zeros  float16 [..., d/group]   (the fp16 group minimum)
 """
@@ -42,6 +50,14 @@ import numpy as np
 D_HEAD = 128
 GROUP = 32
 QMAX = 3  # 2**2 - 1 levels above the zero-point
+BITS = (1, 2, 4)  # code widths of the codec
+
+
+def levels(bits: int) -> int:
+    """Levels above the zero-point of b-bit codes: 2**b - 1."""
+    if bits not in BITS:
+        raise ValueError(f"code width must be one of {BITS}")
+    return (1 << bits) - 1
 
 
 # --------------------------------------------------------------------------
@@ -109,17 +125,18 @@ def rotate_rows(x: np.ndarray, R: np.ndarray | None) -> np.ndarray:
 # --------------------------------------------------------------------------
 # O2-O4: group statistics, scale/zero, codes
 # --------------------------------------------------------------------------
-def quantize_rows(y32: np.ndarray, group: int = GROUP):
-    """Asymmetric 2-bit quantization of fp32 rows in channel groups.
+def quantize_rows(y32: np.ndarray, group: int = GROUP, bits: int = 2):
+    """Asymmetric b-bit quantization of fp32 rows in channel groups
+    (b = 2: INT2; L = 2**b - 1 levels above the zero-point).
 
     Per row and per group of `group` contiguous channels:
         mn, mx = min, max                       (exact)
-        s32    = fp32( fp32(mx - mn) / 3 )      (IEEE fp32 ops)
+        s32    = fp32( fp32(mx - mn) / L )      (IEEE fp32 ops)
         scale  = fp16_rne(s32);  zero = fp16_rne(mn + 0.0)
         if scale == 0: every code is 0
         else:  inv  = fp32(1 / fp32(scale))
                u    = fp32( fp32(y - fp32(zero)) * inv )
-               code = clamp(rint_half_even(u), 0, 3)
+               code = clamp(rint_half_even(u), 0, L)
     Codes are taken against the stored fp16 scale and zero so that
     dequantization code*scale + zero is self-consistent.  Adding +0.0 to the
     minimum makes a zero minimum +0 whatever the signs of the group's zeros
@@ -135,11 +152,12 @@ def quantize_rows(y32: np.ndarray, group: int = GROUP):
     if d % group:
         raise ValueError("row length must be a multiple of the group size")
     ng = d // group
+    qmax = levels(bits)
     yg = y32.reshape(*y32.shape[:-1], ng, group)
     mn = yg.min(axis=-1)
     mx = yg.max(axis=-1)
     rng32 = np.subtract(mx, mn, dtype=np.float32)
-    s32 = np.divide(rng32, np.float32(QMAX), dtype=np.float32)
+    s32 = np.divide(rng32, np.float32(qmax), dtype=np.float32)
     scale_h = s32.astype(np.float16)
     zero_h = np.add(mn, np.float32(0), dtype=np.float32).astype(np.float16)
 
@@ -149,7 +167,7 @@ def quantize_rows(y32: np.ndarray, group: int = GROUP):
     inv = np.divide(np.float32(1), safe, dtype=np.float32)
     diff = np.subtract(yg, zero32[..., None], dtype=np.float32)
     u = np.multiply(diff, inv[..., None], dtype=np.float32)
-    code = np.clip(np.rint(u), 0, QMAX)
+    code = np.clip(np.rint(u), 0, qmax)
     code = np.where((scale32 == 0)[..., None], 0, code)
     codes = code.astype(np.uint8).reshape(y32.shape)
     return codes, scale_h, zero_h
@@ -158,26 +176,33 @@ def quantize_rows(y32: np.ndarray, group: int = GROUP):
 # --------------------------------------------------------------------------
 # O5: packing
 # --------------------------------------------------------------------------
-def pack_codes(codes: np.ndarray) -> np.ndarray:
-    """Four 2-bit codes per byte, first channel in the lowest bits.
+def pack_codes(codes: np.ndarray, bits: int = 2) -> np.ndarray:
+    """8/b codes of b bits per byte, first channel in the lowest bits.
 
-    byte b = c[4b] | c[4b+1] << 2 | c[4b+2] << 4 | c[4b+3] << 6
+    b = 2: byte j = c[4j] | c[4j+1] << 2 | c[4j+2] << 4 | c[4j+3] << 6
+    b-bit: byte j = sum over i < 8/b of c[(8/b) j + i] << (b i)
     """
+    qmax = levels(bits)
+    per = 8 // bits
     codes = np.asarray(codes, dtype=np.uint8)
-    if codes.shape[-1] % 4:
-        raise ValueError("row length must be a multiple of 4")
-    if np.any(codes > QMAX):
-        raise ValueError("codes must be in [0, 3]")
-    c = codes.reshape(*codes.shape[:-1], codes.shape[-1] // 4, 4).astype(np.uint32)
-    packed = c[..., 0] | (c[..., 1] << 2) | (c[..., 2] << 4) | (c[..., 3] << 6)
+    if codes.shape[-1] % per:
+        raise ValueError(f"row length must be a multiple of {per}")
+    if np.any(codes > qmax):
+        raise ValueError(f"codes must be in [0, {qmax}]")
+    c = codes.reshape(*codes.shape[:-1], codes.shape[-1] // per, per).astype(np.uint32)
+    packed = np.zeros(c.shape[:-1], np.uint32)
+    for i in range(per):
+        packed |= c[..., i] << (bits * i)
     return packed.astype(np.uint8)
 
 
-def unpack_codes(packed: np.ndarray) -> np.ndarray:
-    """Inverse of pack_codes: uint8 [..., d/4] -> uint8 codes [..., d]."""
+def unpack_codes(packed: np.ndarray, bits: int = 2) -> np.ndarray:
+    """Inverse of pack_codes: uint8 [..., d*b/8] -> uint8 codes [..., d]."""
+    qmax = levels(bits)
+    per = 8 // bits
     p = np.asarray(packed, dtype=np.uint8)
-    parts = [(p >> (2 * i)) & 3 for i in range(4)]
-    return np.stack(parts, axis=-1).reshape(*p.shape[:-1], p.shape[-1] * 4)
+    parts = [(p >> (bits * i)) & qmax for i in range(per)]
+    return np.stack(parts, axis=-1).reshape(*p.shape[:-1], p.shape[-1] * per)
 
 
 # --------------------------------------------------------------------------
@@ -198,23 +223,23 @@ def dequantize(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
 # --------------------------------------------------------------------------
 # Write path: rotate -> quantize -> pack, for whole caches
 # --------------------------------------------------------------------------
-def quantize_cache(x: np.ndarray, R_heads=None, group: int = GROUP):
+def quantize_cache(x: np.ndarray, R_heads=None, group: int = GROUP, bits: int = 2):
     """Quantize K or V given head-major rows x [B, H, T, d].
 
     R_heads: None (no rotation), a single [d, d] matrix used for every head,
-    or [H, d, d] (one per head).  Returns (packed [B,H,T,d/4] uint8,
+    or [H, d, d] (one per head).  Returns (packed [B,H,T,d*bits/8] uint8,
     scales [B,H,T,d/group] fp16, zeros [B,H,T,d/group] fp16).
     """
     x = np.asarray(x)
     B, H, T, d = x.shape
-    packed = np.empty((B, H, T, d // 4), np.uint8)
+    packed = np.empty((B, H, T, d * bits // 8), np.uint8)
     scales = np.empty((B, H, T, d // group), np.float16)
     zeros = np.empty((B, H, T, d // group), np.float16)
     for h in range(H):
         R = _head_matrix(R_heads, h)
         y = rotate_rows(x[:, h], R)
-        codes, s, z = quantize_rows(y, group)
-        packed[:, h] = pack_codes(codes)
+        codes, s, z = quantize_rows(y, group, bits)
+        packed[:, h] = pack_codes(codes, bits)
         scales[:, h] = s
         zeros[:, h] = z
     return packed, scales, zeros
@@ -238,8 +263,9 @@ def decode_attention(q, kcache, vcache, t_begin, t_end, R_heads=None,
     """One decode query per (batch, query head) against the cached tokens.
 
     q       [B, Hq, d]  (any float dtype; promoted to fp64)
-    kcache  (codes [B,Hkv,T_cap,d/4], scales, zeros) in the rotated basis
-    vcache  same for V
+    kcache  (codes [B,Hkv,T_cap,d*b/8], scales, zeros) in the rotated basis;
+            the code width b (1, 2 or 4) follows from the codes' row length
+    vcache  same for V (its width may differ from the keys')
     INT2 tokens are [t_begin, t_end).  sink_* / res_* are optional fp16
     [B, Hkv, n, d] tokens kept unquantized in the ORIGINAL basis.
 
@@ -262,6 +288,7 @@ def decode_attention(q, kcache, vcache, t_begin, t_end, R_heads=None,
     if Hq % Hkv:
         raise ValueError("Hq must be a multiple of Hkv")
     G = Hq // Hkv
+    kbits, vbits = 8 * kc.shape[-1] // d, 8 * vc.shape[-1] // d
     if softmax_scale is None or softmax_scale <= 0:
         softmax_scale = 1.0 / np.sqrt(float(d))
     n_int2 = t_end - t_begin
@@ -271,10 +298,10 @@ def decode_attention(q, kcache, vcache, t_begin, t_end, R_heads=None,
             R = _head_matrix(R_heads, hk)
             R64 = None if R is None else np.asarray(R, dtype=np.float64)
             if n_int2 > 0:
-                khat = dequantize(unpack_codes(kc[b, hk, t_begin:t_end]),
+                khat = dequantize(unpack_codes(kc[b, hk, t_begin:t_end], kbits),
                                   ks[b, hk, t_begin:t_end],
                                   kz[b, hk, t_begin:t_end], group)
-                vhat = dequantize(unpack_codes(vc[b, hk, t_begin:t_end]),
+                vhat = dequantize(unpack_codes(vc[b, hk, t_begin:t_end], vbits),
                                   vs[b, hk, t_begin:t_end],
                                   vz[b, hk, t_begin:t_end], group)
             else:

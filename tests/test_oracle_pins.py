@@ -195,6 +195,113 @@ def pin_pack_roundtrip(orc):
         assert sum(int(c[i]) << (2 * i) for i in range(4)) == b
 
 
+# ------------------------------------------------------ other code widths
+def pin_quant_bits_grid(orc):
+    """1- and 4-bit codes: grid data z + j*s, j in [0, 2**b - 1] with every
+    level present, is recovered exactly (scale = s, zero = z, codes = j)."""
+    rng = np.random.default_rng(13)
+    for bits, L in ((1, 1), (4, 15)):
+        done = 0
+        for _ in range(400):
+            z = np.float16(rng.uniform(-4, 4))
+            s = np.float16(2.0 ** rng.uniform(-4, 0))
+            j = rng.integers(0, L + 1, size=(4, 32))
+            j[:, 0], j[:, 1] = 0, L
+            y64 = float(z) + j * float(s)
+            y = y64.astype(np.float32)
+            if not np.array_equal(y.astype(np.float64), y64):
+                continue
+            codes, sc, zz = orc.quantize_rows(y.reshape(1, 128), bits=bits)
+            assert np.all(sc == s) and np.all(zz == z), bits
+            assert np.array_equal(codes.reshape(4, 32), j.astype(np.uint8)), bits
+            assert np.array_equal(orc.dequantize(codes, sc, zz).reshape(4, 32), y64)
+            done += 1
+        assert done > 50
+
+
+def pin_quant_bits_ramp(orc):
+    """Hand-derived groups.  Ramp y_i = i, i = 0..31:
+    4 bits: range 31, scale = fp16(31/15): 31/15 = 2.0666.., the fp16 step
+    in [2, 4) is 2^-9, 2.0666../2^-9 = 1058.13, so scale = 1058 * 2^-9 =
+    2.06640625; code_i = round(i / scale) in exact rationals (no i sits
+    within 0.01 of a half).  1 bit: scale = 31, code = 1 exactly for
+    i >= 16 (15/31 < 1/2 < 16/31)."""
+    from fractions import Fraction
+    y = np.tile(np.arange(32, dtype=np.float32), 4)[None]
+    codes, s, z = orc.quantize_rows(y, bits=4)
+    assert float(s[0, 0]) == 2.06640625 and float(z[0, 0]) == 0.0
+    sc = Fraction(1058, 512)
+    want = []
+    for i in range(32):
+        u = Fraction(i) / sc
+        k = math.floor(u)
+        assert abs(u - k - Fraction(1, 2)) > Fraction(1, 100)
+        want.append(k + (1 if u - k > Fraction(1, 2) else 0))
+    assert list(codes[0, :32]) == want
+    assert want[-1] == 15 and want[1] == 0 and want[2] == 1
+    codes1, s1, _ = orc.quantize_rows(y, bits=1)
+    assert float(s1[0, 0]) == 31.0
+    assert list(codes1[0, :32]) == [0] * 16 + [1] * 16
+
+
+def pin_quant_bits_nearest(orc):
+    """Every 1- and 4-bit code picks the nearest level of its group (fp32
+    slop only), for random outlier data in both bases."""
+    rng = np.random.default_rng(15)
+    x = rng.standard_normal((32, 128)) * np.where(np.arange(128) % 29 == 5, 20, 1)
+    for bits in (1, 4):
+        L = (1 << bits) - 1
+        for R in (None, orc.hadamard_rotation(128)):
+            y = orc.rotate_rows(x, R)
+            codes, s, z = orc.quantize_rows(y, bits=bits)
+            lv = (np.arange(L + 1)[None, None, :] * s.astype(np.float64)[..., None]
+                  + z.astype(np.float64)[..., None])
+            yg = y.astype(np.float64).reshape(32, 4, 32)
+            err = np.abs(yg[..., None] - lv[:, :, None, :])
+            chosen = np.take_along_axis(err, codes.reshape(32, 4, 32, 1).astype(np.int64), -1)[..., 0]
+            assert np.all(chosen <= err.min(-1) + 1e-6 * (np.abs(yg) + 1)), bits
+
+
+def pin_pack_bits(orc):
+    """Hand-packed bytes: 1 bit, codes 1,0,1,1,0,0,0,1 -> 1+4+8+128 = 141;
+    4 bits, codes 3,12 -> 3 + 12*16 = 195, codes 15,0 -> 15.  Every byte
+    value round-trips at each width."""
+    c1 = np.array([[1, 0, 1, 1, 0, 0, 0, 1] * 2], np.uint8)
+    assert list(orc.pack_codes(c1, bits=1)[0]) == [141, 141]
+    c4 = np.array([[3, 12, 15, 0]], np.uint8)
+    assert list(orc.pack_codes(c4, bits=4)[0]) == [195, 15]
+    allb = np.arange(256, dtype=np.uint8)[None]
+    for bits in (1, 4):
+        c = orc.unpack_codes(allb, bits=bits)
+        assert c.shape == (1, 256 * 8 // bits) and c.max() == (1 << bits) - 1
+        assert np.array_equal(orc.pack_codes(c, bits=bits), allb)
+    assert list(orc.unpack_codes(np.array([[141]], np.uint8), bits=1)[0]) == [1, 0, 1, 1, 0, 0, 0, 1]
+    assert list(orc.unpack_codes(np.array([[195]], np.uint8), bits=4)[0]) == [3, 12]
+
+
+def pin_decode_mixed_widths(orc):
+    """Decode reads each cache at its own width: 2-bit caches re-encoded as
+    4-bit codes (same levels, scales and zeros) give the same output; keys
+    at 4 bits with values at 2 bits, and keys at 1 bit (codes 0/1 written at
+    1 and at 2 bits) likewise."""
+    rng = np.random.default_rng(17)
+    B, H, T, d = 1, 2, 40, 128
+    q = rng.standard_normal((B, 2 * H, d))
+    kc, ks, kz, kp = _random_cache(rng, B, H, T)
+    vc, vs, vz, vp = _random_cache(rng, B, H, T)
+    ref = orc.decode_attention(q, (kp, ks, kz), (vp, vs, vz), 3, T)
+    k4 = orc.pack_codes(orc.unpack_codes(kp), bits=4)
+    v4 = orc.pack_codes(orc.unpack_codes(vp), bits=4)
+    assert k4.shape[-1] == 64
+    for kk, vv in (((k4, ks, kz), (vp, vs, vz)), ((k4, ks, kz), (v4, vs, vz)), ((kp, ks, kz), (v4, vs, vz))):
+        assert np.allclose(orc.decode_attention(q, kk, vv, 3, T), ref, rtol=0, atol=1e-12)
+    kb = orc.unpack_codes(kp) & 1                           # codes in {0, 1}
+    r2 = orc.decode_attention(q, (orc.pack_codes(kb), ks, kz), (vp, vs, vz), 3, T)
+    r1 = orc.decode_attention(q, (orc.pack_codes(kb, bits=1), ks, kz), (vp, vs, vz), 3, T)
+    assert orc.pack_codes(kb, bits=1).shape[-1] == 16
+    assert np.allclose(r1, r2, rtol=0, atol=1e-12)
+
+
 # ------------------------------------------------------------------ decode
 def _random_cache(rng, B, H, T, d=128):
     codes = rng.integers(0, 4, size=(B, H, T, d)).astype(np.uint8)
@@ -293,6 +400,8 @@ PINS = [
     pin_quant_golden, pin_quant_grid_random, pin_quant_nearest_level,
     pin_pack_golden, pin_pack_roundtrip,
     pin_decode_vs_sdpa, pin_decode_bruteforce, pin_decode_large_scores,
+    pin_quant_bits_grid, pin_quant_bits_ramp, pin_quant_bits_nearest, pin_pack_bits,
+    pin_decode_mixed_widths,
 ]
 
 
@@ -364,23 +473,29 @@ MUTATIONS = [
     ("un-rotation with R instead of R^T", "o_rot @ R64.T", "o_rot @ R64"),
     ("query rotated by R^T", "qv @ R64\n", "qv @ R64.T\n"),
     ("zero-point dropped in dequantization", "(c * s + z)", "(c * s)"),
-    ("round half up instead of half even", "np.clip(np.rint(u), 0, QMAX)",
-     "np.clip(np.floor(u + 0.5), 0, QMAX)"),
+    ("round half up instead of half even", "np.clip(np.rint(u), 0, qmax)",
+     "np.clip(np.floor(u + 0.5), 0, qmax)"),
     ("softmax scale 1/d", "1.0 / np.sqrt(float(d))", "1.0 / float(d)"),
-    ("divisor 4 instead of 3", "np.float32(QMAX), dtype", "np.float32(4), dtype"),
-    ("packing order swapped", "c[..., 0] | (c[..., 1] << 2)", "c[..., 1] | (c[..., 0] << 2)"),
+    ("divisor 4 instead of 3", "np.float32(qmax), dtype", "np.float32(qmax + 1), dtype"),
+    ("packing order swapped", "packed |= c[..., i] << (bits * i)",
+     "packed |= c[..., per - 1 - i] << (bits * i)"),
     ("fp16 values taken from keys", "p_f16 @ fv", "p_f16 @ fk"),
     ("Hadamard parity or-ed", "parity ^= bits & 1", "parity |= bits & 1"),
     ("GQA head mapping interleaved", "hq = hk * G + g", "hq = g * Hkv + hk"),
     ("no max subtraction", "np.exp(s_int2 - m)", "np.exp(s_int2)"),
     ("zero from the max", "np.add(mn, np.float32(0)", "np.add(mx, np.float32(0)"),
     ("signed zero kept", "np.add(mn, np.float32(0), dtype=np.float32)", "mn"),
-    ("no clamp", "np.clip(np.rint(u), 0, QMAX)", "np.rint(u)"),
+    ("no clamp", "np.clip(np.rint(u), 0, qmax)", "np.rint(u)"),
     ("rotation transposed", "x64 @ np.asarray(R, dtype=np.float64)",
      "x64 @ np.asarray(R, dtype=np.float64).T"),
     ("channel order applied inverted", "P[perm[h], np.arange(d)] = 1.0",
      "P[np.arange(d), perm[h]] = 1.0"),
     ("channel order after the transform", "out[h] = P @ H", "out[h] = H @ P"),
+    ("2**b levels instead of 2**b - 1", "return (1 << bits) - 1", "return 1 << bits"),
+    ("key width taken from the values", "kbits, vbits = 8 * kc.shape[-1] // d",
+     "kbits, vbits = 8 * vc.shape[-1] // d"),
+    ("unpack mask fixed at 2 bits", "& qmax for i in range(per)", "& 3 for i in range(per)"),
+    ("1-bit divisor 2", "qmax = levels(bits)\n    yg", "qmax = max(levels(bits), 2)\n    yg"),
 ]
 
 
