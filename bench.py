@@ -41,6 +41,12 @@ METRIC = "INT2 decode attention effective HBM GB/s (% of peak) + quantize tokens
 # algorithmic bytes (fp16 K/V input)
 QUANT_BYTES_PER_TOKEN_HEAD = 2 * 256 + 2 * 48     # read K and V rows, write 2 INT2 rows
 DECODE_BYTES_PER_TOKEN_HEAD = 2 * 48              # read one INT2 K row and one V row
+
+
+def row_bytes(bits):
+    """Bytes of one cached row at `bits` per code: 16*bits code bytes plus
+    four fp16 scales and four fp16 zeros (48 for INT2)."""
+    return 16 * bits + 16
 FP16_BYTES_PER_TOKEN_HEAD = 2 * 256               # read one fp16 K row and one V row
 
 
@@ -56,6 +62,9 @@ def parse():
                    help="serving form: per-sequence lengths drawn in [T/2, T] (seeded); the decode "
                         "is kvq_decode_attention_varlen and the write phase a decode-step append "
                         "of one row per sequence (kvq_quantize_at)")
+    p.add_argument("--kbits", type=int, default=2, choices=(1, 2, 4),
+                   help="key code width (1 and 4: the b-bit write and decode kernels)")
+    p.add_argument("--vbits", type=int, default=2, choices=(1, 2, 4), help="value code width")
     p.add_argument("--config", type=int, default=3, choices=(3, 4, 5),
                    help="workload id (3 = throughput case, 4 = GQA dense rotation, 5 = sinks)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -148,6 +157,12 @@ def main():
         rot, workload = "perm", cfg.name + "_perm"
     if args.varlen:
         workload += "_varlen"
+    kbits, vbits = args.kbits, args.vbits
+    if (kbits, vbits) != (2, 2):
+        if rot == "dense" or args.varlen:
+            sys.exit("--kbits/--vbits other than 2 need a Hadamard workload (--config 3 or 5) "
+                     "without --varlen")
+        workload += f"_k{kbits}v{vbits}"
     print(f"[bench] generating {workload} on the GPU", file=sys.stderr, flush=True)
     t0 = time.time()
     K = W.kv_tokens(cfg, "K", device=dev)
@@ -158,8 +173,8 @@ def main():
         R = torch.as_tensor(W.dense_rotations(cfg), device=dev).contiguous()
     elif rot == "perm":
         R = torch.as_tensor(W.channel_orders(cfg), dtype=torch.int32, device=dev).contiguous()
-    ck = kvq.Int2Cache.empty(B, H, T, device=dev)
-    cv = kvq.Int2Cache.empty(B, H, T, device=dev)
+    ck = kvq.Int2Cache.empty(B, H, T, device=dev, bits=kbits)
+    cv = kvq.Int2Cache.empty(B, H, T, device=dev, bits=vbits)
     tb, te = cfg.int2_range                    # INT2 tokens of the cache
     q0, q1 = cfg.quant_range                   # tokens written by the timed quantize call
     fp16 = {}
@@ -255,8 +270,10 @@ def main():
     # INT2 (token, head) units the decode reads: every sequence's own range
     int2_tokens = int((ends_h - tb).sum()) if ends is not None else B * (te - tb)
     r_bytes = {"dense": H * d * d * 4, "perm": H * d * 4}.get(rot, 0)   # R / channel orders, read once
-    q_bytes = B * n_q * H * QUANT_BYTES_PER_TOKEN_HEAD + r_bytes
-    d_bytes = (int2_tokens * H * DECODE_BYTES_PER_TOKEN_HEAD + B * n_f16 * H * FP16_BYTES_PER_TOKEN_HEAD
+    q_unit = 2 * 256 + row_bytes(kbits) + row_bytes(vbits)     # QUANT_BYTES_PER_TOKEN_HEAD at 2/2
+    d_unit = row_bytes(kbits) + row_bytes(vbits)               # DECODE_BYTES_PER_TOKEN_HEAD at 2/2
+    q_bytes = B * n_q * H * q_unit + r_bytes
+    d_bytes = (int2_tokens * H * d_unit + B * n_f16 * H * FP16_BYTES_PER_TOKEN_HEAD
                + 2 * B * cfg.Hq * d * 2 + r_bytes)
     # mean call time over the timed calls (whole-phase throughput)
     q_ms, d_ms = float(np.mean(quant_ms)), float(np.mean(dec_ms))
@@ -268,23 +285,30 @@ def main():
     q_kernel, q_src = {"dense": ("kv_rotate_quant_dense", "kv_rotate_quant_dense.hip"),
                        "perm": ("kv_rotate_quant_fwht_perm_f16", "kv_rotate_quant.hip")}.get(
                            rot, ("kv_rotate_quant_fwht_f16", "kv_rotate_quant.hip"))
+    if (kbits, vbits) != (2, 2):
+        stem = "kv_rotate_quant_fwht_perm" if rot == "perm" else "kv_rotate_quant_fwht"
+        names = [f"{stem}_f16" if b == 2 else f"{stem}_b{b}_f16" for b in (kbits, vbits)]
+        q_kernel = names[0] if kbits == vbits else " + ".join(names)
     roof_q = {"bound": "hbm", "achieved": round(q_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
               "frac": round(q_gbs / PEAK_HBM_GBS, 4),
               "traffic": traffic_from_profile(q_kernel, workload, os.path.join(csrc, q_src)),
               "kernel": q_kernel, "algorithmic_bytes_per_launch": q_bytes,
-              "bytes_per_unit": QUANT_BYTES_PER_TOKEN_HEAD, "unit_of_work": "(token, kv head)",
+              "bytes_per_unit": q_unit, "unit_of_work": "(token, kv head)",
               "units_per_launch": B * n_q * H, "avg_ms": round(q_ms, 4)}
     d_kernel, d_src = (("kv_int2_decode_attn", "kv_decode.hip") if cfg.G == 1
                        else ("kv_int2_decode_attn_gqa", "kv_decode_gqa.hip"))
     # the query preparation is its own launch only for a dense rotation or
     # grouped-query attention; otherwise the attention waves do it
     prep_kernel = cfg.G > 1 or rot in ("dense", "perm")
+    if (kbits, vbits) != (2, 2):                   # the b-bit kernel prepares its query itself
+        d_kernel, d_src = f"kv_quant_decode_attn<{kbits},{vbits}>", "kv_decode_generic.hip"
+        prep_kernel = False
     roof_d = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
               "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
               "traffic": traffic_from_profile(d_kernel, workload, os.path.join(csrc, d_src)),
               "kernel": f"decode call ({'kv_prep_query + ' if prep_kernel else ''}{d_kernel} + kv_combine_unrotate)",
               "algorithmic_bytes_per_launch": d_bytes,
-              "bytes_per_unit": DECODE_BYTES_PER_TOKEN_HEAD, "unit_of_work": "(INT2 token, kv head)",
+              "bytes_per_unit": d_unit, "unit_of_work": "(INT2 token, kv head)",
               "units_per_launch": int2_tokens * H, "avg_ms": round(d_ms, 4)}
     dominant, other = (roof_q, roof_d) if q_ms >= d_ms else (roof_d, roof_q)
 
@@ -294,7 +318,9 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": workload, "B": B, "T": T, "Hkv": H, "Hq": cfg.Hq, "d": d,
-                   "kv_input": "f16", "cache": "int2 codes + f16 scale/zero, group 32",
+                   "kv_input": "f16",
+                   "cache": ("int2 codes + f16 scale/zero, group 32" if (kbits, vbits) == (2, 2) else
+                             f"{kbits}-bit key / {vbits}-bit value codes + f16 scale/zero, group 32"),
                    "rotation": rot, "int2_tokens": [tb, te],
                    "quantize_tokens": ("one appended row per sequence, at its own end" if ends is not None
                                        else [q0, q1]),
@@ -315,11 +341,11 @@ def main():
     }
     rec["copy_reference_gbs"] = copy_bandwidth()
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(cfg, rot, K, V, q, R, fp16)
+        rec["cpu_baseline"] = cpu_baseline(cfg, rot, K, V, q, R, fp16, kbits, vbits)
     print(json.dumps(rec), flush=True)
 
 
-def cpu_baseline(cfg, rot, K, V, q, R, fp16):
+def cpu_baseline(cfg, rot, K, V, q, R, fp16, kbits=2, vbits=2):
     """The oracle, untouched, on a bounded sample of the same workload:
     batch 0, all KV heads, all tokens of the INT2 range (1/B of the job).
     The sample's inputs are the generator's values (copied from the
@@ -340,13 +366,14 @@ def cpu_baseline(cfg, rot, K, V, q, R, fp16):
     qs = q[0:1].cpu().numpy()
     kw = {k: v[0:1].cpu().numpy() for k, v in fp16.items()}
     t0 = time.perf_counter()
-    kc = O.quantize_cache(kh, Rm)
-    vc = O.quantize_cache(vh, Rm)
+    kc = O.quantize_cache(kh, Rm, bits=kbits)
+    vc = O.quantize_cache(vh, Rm, bits=vbits)
     t1 = time.perf_counter()
     O.decode_attention(qs, kc, vc, 0, te - tb, Rm, **kw)
     t2 = time.perf_counter()
     n_f16 = cfg.n_sink + cfg.n_res
-    d_bytes = ((te - tb) * cfg.Hkv * DECODE_BYTES_PER_TOKEN_HEAD + n_f16 * cfg.Hkv * FP16_BYTES_PER_TOKEN_HEAD
+    d_bytes = ((te - tb) * cfg.Hkv * (row_bytes(kbits) + row_bytes(vbits))
+               + n_f16 * cfg.Hkv * FP16_BYTES_PER_TOKEN_HEAD
                + 2 * cfg.Hq * cfg.d * 2)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": round(d_bytes / (t2 - t1) / 1e9, 4), "unit": "GB/s",

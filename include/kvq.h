@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 3
+#define KVQ_ABI_VERSION 4
 
 typedef enum {
   KVQ_OK = 0,
@@ -89,6 +89,26 @@ typedef struct {
   uint16_t *zeros;
   int64_t T_cap;
 } kvq_int2_cache;
+
+/* One side of a cache whose codes are `bits` wide (1, 2 or 4; 2 is the INT2
+ * format above, kvq_int2_cache's).  b-bit codes use L = 2^b - 1 levels
+ * above the zero-point and pack 8/b codes per byte:
+ *    codes  uint8  [B][Hkv][T_cap][d*b/8]  channel (8/b)j+i in bits
+ *                                           b*i .. b*i+b-1 of byte j
+ *    scales fp16   [B][Hkv][T_cap][d/32]   fp32(max-min)/L rounded to fp16
+ *    zeros  fp16   [B][Hkv][T_cap][d/32]   group minimum rounded to fp16
+ *    code = clamp(rint_half_even((y - zero) * fp32(1/scale)), 0, L).
+ * Keys and values may be kept at different widths (for example 4-bit keys
+ * with 2-bit values).  The pages name mixed-bit schemes and binary codes as
+ * directions without fixing them (OptR page, the future-work paragraph and
+ * "Why It Matters"); these widths are this library's. */
+typedef struct {
+  uint8_t *codes;
+  uint16_t *scales;
+  uint16_t *zeros;
+  int64_t T_cap;
+  int32_t bits;
+} kvq_quant_cache;
 
 /*
  * kvq_quantize -- rotate, quantize and pack T_new new tokens of K and V.
@@ -130,9 +150,8 @@ kvq_status kvq_quantize(const void *K, const void *V, kvq_dtype in_dtype,
  *             not checked on the host: a row whose slot falls outside
  *             [0, T_cap) is not written.  T_new <= T_cap is checked.
  *  Every other argument as for kvq_quantize.
- * Serving stacks need this alongside variable-length decode (the survey's
- * next step after the hot path; the pages name serving stacks as the
- * setting, OptR page, "Why It Matters").
+ * Serving stacks need this alongside variable-length decode (the pages
+ * name serving stacks as the setting, OptR page, "Why It Matters").
  */
 kvq_status kvq_quantize_at(const void *K, const void *V, kvq_dtype in_dtype,
                            int64_t B, int64_t T_new, int64_t Hkv, int64_t d,
@@ -213,6 +232,43 @@ kvq_status kvq_decode_attention_varlen(const void *q, kvq_dtype q_dtype,
                                        void *out, kvq_dtype out_dtype,
                                        void *workspace, size_t workspace_bytes,
                                        void *stream);
+
+/*
+ * kvq_quantize_bits -- kvq_quantize into caches of any supported code width
+ * (kvq_quant_cache; keys and values may differ).  With both sides at 2 bits
+ * it is kvq_quantize.  A side at 1 or 4 bits needs in_dtype == KVQ_F16 and
+ * rot KVQ_ROT_HADAMARD or KVQ_ROT_PERM_HADAMARD (else KVQ_ERR_UNSUPPORTED);
+ * bits outside {1, 2, 4} give KVQ_ERR_INVALID_ARG.  Every other argument
+ * as for kvq_quantize.  Mixed-bit caches: OptR page, future-work paragraph.
+ */
+kvq_status kvq_quantize_bits(const void *K, const void *V, kvq_dtype in_dtype,
+                             int64_t B, int64_t T_new, int64_t Hkv, int64_t d,
+                             int64_t stride_b, int64_t stride_t, int64_t stride_h,
+                             kvq_rot rot, const void *R, int group,
+                             int64_t t_offset, const kvq_quant_cache *kc,
+                             const kvq_quant_cache *vc, void *stream);
+
+/*
+ * kvq_decode_attention_bits -- kvq_decode_attention over caches of any
+ * supported code width (kvq_quant_cache; keys and values may differ).  With
+ * both sides at 2 bits it is kvq_decode_attention.  Otherwise rot must be
+ * KVQ_ROT_NONE, KVQ_ROT_HADAMARD or KVQ_ROT_PERM_HADAMARD (KVQ_ROT_DENSE
+ * gives KVQ_ERR_UNSUPPORTED).  Workspace as for kvq_decode_attention
+ * (kvq_decode_workspace_bytes); every other argument likewise.
+ */
+kvq_status kvq_decode_attention_bits(const void *q, kvq_dtype q_dtype,
+                                     int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
+                                     const kvq_quant_cache *kc,
+                                     const kvq_quant_cache *vc,
+                                     int64_t t_begin, int64_t t_end,
+                                     kvq_rot rot, const void *R, int group,
+                                     const uint16_t *sink_k, const uint16_t *sink_v,
+                                     int64_t n_sink,
+                                     const uint16_t *res_k, const uint16_t *res_v,
+                                     int64_t n_res, float softmax_scale,
+                                     void *out, kvq_dtype out_dtype,
+                                     void *workspace, size_t workspace_bytes,
+                                     void *stream);
 
 /* Human-readable name of a status code (static storage). */
 const char *kvq_status_str(kvq_status s);

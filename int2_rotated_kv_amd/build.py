@@ -9,7 +9,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvq.so")
 
-SOURCES = ["api.cpp", "kv_rotate_quant.hip", "kv_rotate_quant_dense.hip", "kv_decode.hip", "kv_decode_gqa.hip"]
+SOURCES = ["api.cpp", "kv_rotate_quant.hip", "kv_rotate_quant_dense.hip", "kv_decode.hip", "kv_decode_gqa.hip",
+           "kv_decode_generic.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -29,13 +29,26 @@ kvq_status check_rotation(kvq_rot rot, const void *R) {
   return KVQ_OK;
 }
 
-kvq_status check_cache(const kvq_int2_cache *c) {
+kvq_status check_cache(const kvq_quant_cache *c) {
   if (c == nullptr) return KVQ_ERR_INVALID_ARG;
   if (c->codes == nullptr || c->scales == nullptr || c->zeros == nullptr) return KVQ_ERR_INVALID_ARG;
   if (!aligned16(c->codes) || !aligned16(c->scales) || !aligned16(c->zeros)) return KVQ_ERR_INVALID_ARG;
   if (c->T_cap <= 0) return KVQ_ERR_INVALID_ARG;
+  if (c->bits != 1 && c->bits != 2 && c->bits != 4) return KVQ_ERR_INVALID_ARG;
   return KVQ_OK;
 }
+
+// An INT2 cache side as a 2-bit cache side (NULL stays NULL).
+struct AsQuant {
+  kvq_quant_cache c;
+  const kvq_quant_cache *p;
+  explicit AsQuant(const kvq_int2_cache *x) : c{}, p(nullptr) {
+    if (x != nullptr) {
+      c.codes = x->codes; c.scales = x->scales; c.zeros = x->zeros; c.T_cap = x->T_cap; c.bits = 2;
+      p = &c;
+    }
+  }
+};
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
@@ -54,7 +67,7 @@ kvq_status quantize_impl(const void *K, const void *V, kvq_dtype in_dtype, int64
                          int64_t T_new, int64_t Hkv, int64_t d, int64_t stride_b,
                          int64_t stride_t, int64_t stride_h, kvq_rot rot, const void *R,
                          int group, int64_t t_offset, const int32_t *offsets,
-                         const kvq_int2_cache *kc, const kvq_int2_cache *vc, void *stream) {
+                         const kvq_quant_cache *kc, const kvq_quant_cache *vc, void *stream) {
   if (!valid_dtype(in_dtype)) return KVQ_ERR_INVALID_ARG;
   if (B < 0 || T_new < 0 || Hkv <= 0 || t_offset < 0) return KVQ_ERR_INVALID_ARG;
   if (stride_b < 0 || stride_t < 0 || stride_h < 0) return KVQ_ERR_INVALID_ARG;
@@ -71,7 +84,7 @@ kvq_status quantize_impl(const void *K, const void *V, kvq_dtype in_dtype, int64
   kvq::QuantArgs a{};
   a.n_sides = 0;
   const void *xs[2] = {K, V};
-  const kvq_int2_cache *cs[2] = {kc, vc};
+  const kvq_quant_cache *cs[2] = {kc, vc};
   for (int s = 0; s < 2; ++s) {
     if (xs[s] == nullptr) continue;
     if (!aligned16(xs[s])) return KVQ_ERR_INVALID_ARG;
@@ -86,6 +99,10 @@ kvq_status quantize_impl(const void *K, const void *V, kvq_dtype in_dtype, int64
     q.scales = cs[s]->scales;
     q.zeros = cs[s]->zeros;
     q.T_cap = cs[s]->T_cap;
+    q.bits = cs[s]->bits;
+    // 1- and 4-bit codes: fp16 rows with the (reordered) Hadamard rotation
+    if (q.bits != 2 && (in_dtype != KVQ_F16 || !(rot == KVQ_ROT_HADAMARD || rot == KVQ_ROT_PERM_HADAMARD)))
+      return KVQ_ERR_UNSUPPORTED;
   }
   if (B * a.n_sides > 65535 || Hkv > 65535 || (T_new + 63) / 64 * Hkv > 0x7FFFFFFF)
     return KVQ_ERR_UNSUPPORTED;
@@ -115,6 +132,16 @@ kvq_status kvq_quantize(const void *K, const void *V, kvq_dtype in_dtype, int64_
                         int64_t stride_t, int64_t stride_h, kvq_rot rot, const void *R,
                         int group, int64_t t_offset, const kvq_int2_cache *kc,
                         const kvq_int2_cache *vc, void *stream) {
+  const AsQuant k2(kc), v2(vc);
+  return quantize_impl(K, V, in_dtype, B, T_new, Hkv, d, stride_b, stride_t, stride_h, rot, R,
+                       group, t_offset, nullptr, k2.p, v2.p, stream);
+}
+
+kvq_status kvq_quantize_bits(const void *K, const void *V, kvq_dtype in_dtype, int64_t B,
+                             int64_t T_new, int64_t Hkv, int64_t d, int64_t stride_b,
+                             int64_t stride_t, int64_t stride_h, kvq_rot rot, const void *R,
+                             int group, int64_t t_offset, const kvq_quant_cache *kc,
+                             const kvq_quant_cache *vc, void *stream) {
   return quantize_impl(K, V, in_dtype, B, T_new, Hkv, d, stride_b, stride_t, stride_h, rot, R,
                        group, t_offset, nullptr, kc, vc, stream);
 }
@@ -125,8 +152,9 @@ kvq_status kvq_quantize_at(const void *K, const void *V, kvq_dtype in_dtype, int
                            int group, const int32_t *t_offsets, const kvq_int2_cache *kc,
                            const kvq_int2_cache *vc, void *stream) {
   if (t_offsets == nullptr || ((uintptr_t)t_offsets & 3u) != 0) return KVQ_ERR_INVALID_ARG;
+  const AsQuant k2(kc), v2(vc);
   return quantize_impl(K, V, in_dtype, B, T_new, Hkv, d, stride_b, stride_t, stride_h, rot, R,
-                       group, 0, t_offsets, kc, vc, stream);
+                       group, 0, t_offsets, k2.p, v2.p, stream);
 }
 
 size_t kvq_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
@@ -145,8 +173,8 @@ namespace {
 // the (upper bound of the) end of every sequence's INT2 range; t_ends, when
 // not NULL, holds each sequence's own end (device).
 kvq_status decode_impl(const void *q, kvq_dtype q_dtype, int64_t B, int64_t Hq,
-                       int64_t Hkv, int64_t d, const kvq_int2_cache *kc,
-                       const kvq_int2_cache *vc, int64_t t_begin, int64_t t_end,
+                       int64_t Hkv, int64_t d, const kvq_quant_cache *kc,
+                       const kvq_quant_cache *vc, int64_t t_begin, int64_t t_end,
                        const int32_t *t_ends, kvq_rot rot, const void *R, int group,
                        const uint16_t *sink_k, const uint16_t *sink_v, int64_t n_sink,
                        const uint16_t *res_k, const uint16_t *res_v, int64_t n_res,
@@ -164,6 +192,8 @@ kvq_status decode_impl(const void *q, kvq_dtype q_dtype, int64_t B, int64_t Hq,
     if ((st = check_cache(kc)) != KVQ_OK) return st;
     if ((st = check_cache(vc)) != KVQ_OK) return st;
     if (t_end > kc->T_cap || t_end > vc->T_cap) return KVQ_ERR_INVALID_ARG;
+    // 1- and 4-bit caches: the b-bit kernel, which has no dense rotation
+    if ((kc->bits != 2 || vc->bits != 2) && rot == KVQ_ROT_DENSE) return KVQ_ERR_UNSUPPORTED;
   }
   if (n_sink < 0 || n_res < 0) return KVQ_ERR_INVALID_ARG;
   if (n_sink > 0 && (sink_k == nullptr || sink_v == nullptr || !aligned16(sink_k) || !aligned16(sink_v)))
@@ -188,6 +218,8 @@ kvq_status decode_impl(const void *q, kvq_dtype q_dtype, int64_t B, int64_t Hq,
     a.kcodes = kc->codes; a.kscales = kc->scales; a.kzeros = kc->zeros; a.kT_cap = kc->T_cap;
     a.vcodes = vc->codes; a.vscales = vc->scales; a.vzeros = vc->zeros; a.vT_cap = vc->T_cap;
   }
+  a.kbits = n_int2 > 0 ? kc->bits : 2;
+  a.vbits = n_int2 > 0 ? vc->bits : 2;
   a.t_begin = t_begin;
   a.n_int2 = n_int2;
   a.t_ends = n_int2 > 0 ? t_ends : nullptr;
@@ -219,6 +251,20 @@ kvq_status kvq_decode_attention(const void *q, kvq_dtype q_dtype, int64_t B, int
                                 const uint16_t *res_k, const uint16_t *res_v, int64_t n_res,
                                 float softmax_scale, void *out, kvq_dtype out_dtype,
                                 void *workspace, size_t workspace_bytes_given, void *stream) {
+  const AsQuant k2(kc), v2(vc);
+  return decode_impl(q, q_dtype, B, Hq, Hkv, d, k2.p, v2.p, t_begin, t_end, nullptr, rot, R, group,
+                     sink_k, sink_v, n_sink, res_k, res_v, n_res, softmax_scale, out, out_dtype,
+                     workspace, workspace_bytes_given, stream);
+}
+
+kvq_status kvq_decode_attention_bits(const void *q, kvq_dtype q_dtype, int64_t B, int64_t Hq,
+                                     int64_t Hkv, int64_t d, const kvq_quant_cache *kc,
+                                     const kvq_quant_cache *vc, int64_t t_begin, int64_t t_end,
+                                     kvq_rot rot, const void *R, int group,
+                                     const uint16_t *sink_k, const uint16_t *sink_v, int64_t n_sink,
+                                     const uint16_t *res_k, const uint16_t *res_v, int64_t n_res,
+                                     float softmax_scale, void *out, kvq_dtype out_dtype,
+                                     void *workspace, size_t workspace_bytes_given, void *stream) {
   return decode_impl(q, q_dtype, B, Hq, Hkv, d, kc, vc, t_begin, t_end, nullptr, rot, R, group,
                      sink_k, sink_v, n_sink, res_k, res_v, n_res, softmax_scale, out, out_dtype,
                      workspace, workspace_bytes_given, stream);
@@ -234,7 +280,8 @@ kvq_status kvq_decode_attention_varlen(const void *q, kvq_dtype q_dtype, int64_t
                                        float softmax_scale, void *out, kvq_dtype out_dtype,
                                        void *workspace, size_t workspace_bytes_given, void *stream) {
   if (t_ends == nullptr || ((uintptr_t)t_ends & 3u) != 0) return KVQ_ERR_INVALID_ARG;
-  return decode_impl(q, q_dtype, B, Hq, Hkv, d, kc, vc, t_begin, t_end_max, t_ends, rot, R, group,
+  const AsQuant k2(kc), v2(vc);
+  return decode_impl(q, q_dtype, B, Hq, Hkv, d, k2.p, v2.p, t_begin, t_end_max, t_ends, rot, R, group,
                      sink_k, sink_v, n_sink, res_k, res_v, n_res, softmax_scale, out, out_dtype,
                      workspace, workspace_bytes_given, stream);
 }

@@ -886,7 +886,9 @@ hipError_t launch_decode(const DecodeArgs &d, hipStream_t stream) {
   // one query head per KV head without a dense rotation: the attention waves
   // prepare the query themselves
   const bool fused_prep = G == 1 && (d.rot == 0 || d.rot == 1);
-  if (!fused_prep && d.n_splits > 0) {
+  // other code widths: the b-bit kernel, which prepares its query itself
+  const bool generic = d.kbits != 2 || d.vbits != 2;
+  if (!generic && !fused_prep && d.n_splits > 0) {
     PrepArgs p;
     p.q = d.q; p.q_f32 = d.q_f32; p.Hq = (int)d.Hq; p.Hkv = (int)d.Hkv;
     p.rot = d.rot; p.R = d.R; p.perm = d.perm; p.qscale = d.qscale;
@@ -902,14 +904,18 @@ hipError_t launch_decode(const DecodeArgs &d, hipStream_t stream) {
     a.t_begin = d.t_begin; a.n_int2 = d.n_int2; a.t_ends = d.t_ends;
     a.n_splits = d.n_splits;
     a.B = d.B;
-    a.total_waves = split_units(d.B, d.Hq, d.Hkv) * d.n_splits;   // B*S split rows
+    // B*S split rows; the b-bit kernel runs one wave per query head
+    a.total_waves = (generic ? d.B * d.Hq : split_units(d.B, d.Hq, d.Hkv)) * d.n_splits;
     a.Hkv = (int)d.Hkv; a.Hq = (int)d.Hq; a.G = G;
     a.qprep = reinterpret_cast<const uint32_t *>(d.qprep);
     a.partials = d.partials;
     a.fused_prep = fused_prep;
     a.skip = grid_skip(d);
-    a.q = d.q; a.q_f32 = d.q_f32; a.rot = d.rot; a.qscale = d.qscale;
-    if (G == 1) {
+    a.q = d.q; a.q_f32 = d.q_f32; a.rot = d.rot; a.perm = d.perm; a.qscale = d.qscale;
+    if (generic) {
+      hipError_t e = launch_attn_generic(a, d.kbits, d.vbits, stream);
+      if (e != hipSuccess) return e;
+    } else if (G == 1) {
       hipLaunchKernelGGL(kv_int2_decode_attn<4>, dim3((unsigned)((a.total_waves + 3) / 4)), dim3(256), 0,
                          stream, a);
     } else {

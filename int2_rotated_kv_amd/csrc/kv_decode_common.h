@@ -23,6 +23,7 @@ struct AttnArgs {
   bool fused_prep;
   const void *q; bool q_f32;
   int rot;
+  const int32_t *perm;  // reordered Hadamard: [Hkv][128] (read by the b-bit kernel)
   float qscale;
   // Tile grid shift: tiles start `skip` rows before t_begin (0 <= skip < 16).
   int skip;
@@ -349,5 +350,6 @@ struct HeadTiles {
 };
 
 hipError_t launch_attn_gqa(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_attn_generic(const AttnArgs &a, int kbits, int vbits, hipStream_t stream);
 
 }  // namespace kvq

@@ -107,23 +107,30 @@ __device__ __forceinline__ void quantize_group32_exact(const float (&v)[32], uin
 // c = fp32(1/sqrt(128))).  min/max of y are taken as c * min/max of z (the
 // rounding of a positive scaling is monotonic, so they equal the min/max of
 // the rounded y).  Per element: d = fp32(fma(z, c, -zero)) (y - zero with one
-// rounding), clamped to [0, 3*scale], then fma(d, 1/scale, magic) rounds
+// rounding), clamped to [0, L*scale] (L = 2^b - 1 levels above the zero for
+// b-bit codes), then fma(d, 1/scale, magic) rounds
 // d/scale to the nearest code with a single rounding.  This differs from the
 // three-rounding reference sequence only for arguments within a few ulps of
 // a half-integer.
-__device__ __forceinline__ void quantize_group32_fwht(const float (&z)[32], uint32_t &w0,
-                                                      uint32_t &w1, uint16_t &sbits,
-                                                      uint16_t &zbits) {
+template <int BITS>
+__device__ __forceinline__ void quantize_group32_fwht(const float (&z)[32], uint32_t (&w)[BITS],
+                                                      uint16_t &sbits, uint16_t &zbits) {
+  // b-bit codes: L = 2^b - 1 levels above the zero; word k holds codes
+  // 32k/b .. 32(k+1)/b - 1, code i of a word at bits b*i.
+  constexpr int L = (1 << BITS) - 1;
+  constexpr int CPW = 32 / BITS;                    // codes per word
+  constexpr int P = 8 / BITS;                       // codes per byte
+  constexpr float inv_levels = BITS == 1 ? 1.0f : BITS == 2 ? 0.3333333432674408f : 0.06666667014360428f;
   constexpr float c = 0.08838834764831845f;         // fp32(1/sqrt(128))
   float zmn, zmx, sf, zf;
   minmax32(z, zmn, zmx);
   {
     // The rotated path is compared at rounding ties, with a group's scale
     // allowed one fp16 ulp of slack, so the two divisions of the exact
-    // sequence become a multiply by fp32(1/3) (within one fp32 ulp of the
+    // sequence become a multiply by fp32(1/L) (within one fp32 ulp of the
     // quotient) and v_rcp_f32 (within one ulp of 1/scale).
     const float mn = zmn * c, mx = zmx * c;
-    const float s32 = (mx - mn) * 0.3333333432674408f;
+    const float s32 = (mx - mn) * inv_levels;
     sbits = float_to_half_bits(s32);
     zbits = float_to_half_bits(mn + 0.0f);
     sf = half_bits_to_float(sbits);
@@ -133,40 +140,54 @@ __device__ __forceinline__ void quantize_group32_fwht(const float (&z)[32], uint
   const float inv = __builtin_amdgcn_rcpf(degenerate ? 1.0f : sf);
   // Fast form: x = z * (c/scale) - zero/scale in one FMA, then
   // v_cvt_pk_u8_f32 rounds half to even, saturates below 0 and drops the
-  // code into byte i/4 of word i%4; the four words merge into the 2-bit
+  // code into byte i/P of word i%P; the P words merge into the b-bit
   // layout.  Folding 1/scale into the constants adds an error of about
   // (|y| + |zero|)/scale ulps, so the wave takes it only while every group
-  // has |zero| <= 8 scale and a normal fp16 scale.  Then x is within 0.006 of
-  // (y - min)/(range/3), which lies in [0, 3]: the fp16 roundings of the
-  // scale and the zero move it by at most 3 * 2^-11 and 8 * 2^-11.  So x
-  // rounds to a code in [0, 3] with no clamp, and the codes are those of the
-  // clamped argument.  Otherwise the sequence below keeps y - zero to one
-  // rounding.
+  // has |zero| <= 8 scale and a normal fp16 scale.  Then x is within
+  // (L + 8) 2^-11 <= 0.012 of (y - min)/(range/L), which lies in [0, L]:
+  // the fp16 roundings of the scale and the zero move it by at most
+  // L 2^-11 and 8 2^-11.  So x rounds to a code in [0, L] with no clamp,
+  // and the codes are those of the clamped argument.  Otherwise the
+  // sequence below keeps y - zero to one rounding.
   const float ci = c * inv, nzi = -zf * inv;
-  uint32_t a, b;
+  uint32_t r[BITS];
   if (!__builtin_amdgcn_ballot_w64(fabsf(nzi) > 8.0f || sf < kMinNormalHalf)) {
-    auto pk = [&](int base) {
-      uint32_t D[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float x = __builtin_fmaf(z[base + i], ci, nzi);
-        D[i & 3] = __builtin_amdgcn_cvt_pk_u8_f32(x, (uint32_t)(i >> 2), D[i & 3]);
+    for (int k = 0; k < BITS; ++k) {
+      uint32_t D[P];
+#pragma unroll
+      for (int m = 0; m < P; ++m) D[m] = 0u;
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) {
+        const float x = __builtin_fmaf(z[k * CPW + i], ci, nzi);
+        D[i % P] = __builtin_amdgcn_cvt_pk_u8_f32(x, (uint32_t)(i / P), D[i % P]);
       }
-      return D[0] | (D[1] << 2) | (D[2] << 4) | (D[3] << 6);
-    };
-    a = pk(0);
-    b = pk(16);
+      uint32_t word = D[0];
+#pragma unroll
+      for (int m = 1; m < P; ++m) word |= D[m] << (BITS * m);
+      r[k] = word;
+    }
   } else {
-    const float top = 3.0f * sf;                      // exact: sf has 11 significant bits
+    const float top = (float)L * sf;                  // exact: sf has 11 significant bits
     auto code = [&](float zz) {
       const float d = __builtin_amdgcn_fmed3f(__builtin_fmaf(zz, c, -zf), 0.0f, top);
       return float_as_bits(__builtin_fmaf(d, inv, kRoundMagic));
     };
-    a = pack16([&](int i) { return code(z[i]); }, 0u) - kPackBias;
-    b = pack16([&](int i) { return code(z[16 + i]); }, 0u) - kPackBias;
+    if constexpr (BITS == 2) {
+      r[0] = pack16([&](int i) { return code(z[i]); }, 0u) - kPackBias;
+      r[1] = pack16([&](int i) { return code(z[16 + i]); }, 0u) - kPackBias;
+    } else {
+#pragma unroll
+      for (int k = 0; k < BITS; ++k) {
+        uint32_t word = 0u;
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) word |= (code(z[k * CPW + i]) - kRoundMagicBits) << (BITS * i);
+        r[k] = word;
+      }
+    }
   }
-  w0 = degenerate ? 0u : a;
-  w1 = degenerate ? 0u : b;
+#pragma unroll
+  for (int k = 0; k < BITS; ++k) w[k] = degenerate ? 0u : r[k];
 }
 
 // lo + hi and lo - hi of the two fp16 halves of a dword, in fp32 with one
@@ -295,7 +316,10 @@ __global__ __launch_bounds__(256) void kv_rotate_quant_rows(RowsKernelArgs a) {
   uint16_t sb, zb;
   if (ROT) {
     fwht128_quad_rest(v, j);
-    quantize_group32_fwht(v, w0, w1, sb, zb);
+    uint32_t w2[2];
+    quantize_group32_fwht<2>(v, w2, sb, zb);
+    w0 = w2[0];
+    w1 = w2[1];
   } else {
     quantize_group32_exact(v, w0, w1, sb, zb);
   }
@@ -333,7 +357,7 @@ constexpr int kStageRowDwords = 64 + 4;     // 128 fp16 + 16-byte pad
 // its LDS row (one 2-byte store each, the row offset in the store's
 // immediate), and the rows are read back as in the plain kernel.  Indices
 // are taken modulo 128, so any order array stays inside the rows.
-template <bool PERM>
+template <bool PERM, int BITS>
 __device__ __forceinline__ void fwht_f16_body(const RowsKernelArgs &a) {
   __shared__ uint32_t stage[64 * kStageRowDwords];
   const int lane = threadIdx.x;
@@ -414,7 +438,7 @@ __device__ __forceinline__ void fwht_f16_body(const RowsKernelArgs &a) {
   const int64_t hi = s.T_cap - slot0 < n_valid ? s.T_cap - slot0 : n_valid;
   const int64_t row0 = (b * a.Hkv + h) * s.T_cap + slot0;
 
-  uint32_t cw[4][2], csz[4];                         // codes and scale | zero << 16 of row 16g + n
+  uint32_t cw[4][BITS], csz[4];                      // codes and scale | zero << 16 of row 16g + n
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int r = 16 * g + n;                        // the lane's token row in the tile
@@ -453,33 +477,38 @@ __device__ __forceinline__ void fwht_f16_body(const RowsKernelArgs &a) {
       }
     }
     uint16_t sb, zb;
-    quantize_group32_fwht(z, cw[g][0], cw[g][1], sb, zb);
+    quantize_group32_fwht<BITS>(z, cw[g], sb, zb);
     csz[g] = (uint32_t)sb | ((uint32_t)zb << 16);
   }
-  // Back through LDS to one row per lane (codes: entry 2r + k holds bytes
-  // 16k .. 16k + 15 of row r; then scale | zero << 16 of each group), so
-  // each code store writes 1 KiB of consecutive cache rows and each lane
-  // writes its row's scales and zeros as 8 bytes; storing the 8-byte and
-  // 2-byte pieces straight from the transform layout measured slower.
+  // Back through LDS to one row per lane (codes: the row's 16 b bytes,
+  // 16-byte chunk k of row r at entry b r + k; then scale | zero << 16 of
+  // each group), so each code store writes 1 KiB of consecutive cache rows
+  // and each lane writes its row's scales and zeros as 8 bytes; storing the
+  // code pieces and 2-byte scales straight from the transform layout
+  // measured slower.
+  constexpr int kRowDwords = 4 * BITS;               // code dwords per row
+  constexpr int kSzOff = 64 * kRowDwords;            // scale | zero entries
+  const int64_t row_bytes = 16 * BITS;
   __syncthreads();                                   // the stage is read
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int r = 16 * g + n;
-    *reinterpret_cast<u32x2_t *>(&stage[r * 8 + 2 * q]) = u32x2_t{cw[g][0], cw[g][1]};
-    stage[512 + r * 4 + q] = csz[g];
+#pragma unroll
+    for (int k = 0; k < BITS; ++k) stage[r * kRowDwords + BITS * q + k] = cw[g][k];
+    stage[kSzOff + r * 4 + q] = csz[g];
   }
   __syncthreads();
   {
     u32x4_t *rows = reinterpret_cast<u32x4_t *>(stage);
-    u32x4_t *cdst = reinterpret_cast<u32x4_t *>(s.codes + row0 * kCodeBytes);
+    u32x4_t *cdst = reinterpret_cast<u32x4_t *>(s.codes + row0 * row_bytes);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int r = 32 * kk + (lane >> 1);
+    for (int kk = 0; kk < BITS; ++kk) {
+      const int r = (64 * kk + lane) / BITS;
       if (r >= lo && r < hi)
         __builtin_nontemporal_store(rows[64 * kk + lane], cdst + 64 * kk + lane);
     }
     if (lane >= lo && lane < hi) {
-      const u32x4_t e = *reinterpret_cast<const u32x4_t *>(&stage[512 + lane * 4]);
+      const u32x4_t e = *reinterpret_cast<const u32x4_t *>(&stage[kSzOff + lane * 4]);
       const u32x2_t sv = {__builtin_amdgcn_perm(e.y, e.x, 0x05040100u), __builtin_amdgcn_perm(e.w, e.z, 0x05040100u)};
       const u32x2_t zv = {__builtin_amdgcn_perm(e.y, e.x, 0x07060302u), __builtin_amdgcn_perm(e.w, e.z, 0x07060302u)};
       __builtin_nontemporal_store(sv, reinterpret_cast<u32x2_t *>(s.scales + row0 * kNGroups) + lane);
@@ -489,10 +518,23 @@ __device__ __forceinline__ void fwht_f16_body(const RowsKernelArgs &a) {
 }
 
 __global__ __launch_bounds__(64) void kv_rotate_quant_fwht_f16(RowsKernelArgs a) {
-  fwht_f16_body<false>(a);
+  fwht_f16_body<false, 2>(a);
 }
 __global__ __launch_bounds__(64) void kv_rotate_quant_fwht_perm_f16(RowsKernelArgs a) {
-  fwht_f16_body<true>(a);
+  fwht_f16_body<true, 2>(a);
+}
+// 1- and 4-bit codes (keys and values may be kept at different widths)
+__global__ __launch_bounds__(64) void kv_rotate_quant_fwht_b1_f16(RowsKernelArgs a) {
+  fwht_f16_body<false, 1>(a);
+}
+__global__ __launch_bounds__(64) void kv_rotate_quant_fwht_b4_f16(RowsKernelArgs a) {
+  fwht_f16_body<false, 4>(a);
+}
+__global__ __launch_bounds__(64) void kv_rotate_quant_fwht_perm_b1_f16(RowsKernelArgs a) {
+  fwht_f16_body<true, 1>(a);
+}
+__global__ __launch_bounds__(64) void kv_rotate_quant_fwht_perm_b4_f16(RowsKernelArgs a) {
+  fwht_f16_body<true, 4>(a);
 }
 
 hipError_t launch_quantize_rows(const QuantArgs &q, hipStream_t stream) {
@@ -509,6 +551,39 @@ hipError_t launch_quantize_rows(const QuantArgs &q, hipStream_t stream) {
   a.n_sides = q.n_sides;
   a.perm = q.perm;
   const int64_t n_tb = (q.T_new + 63) / 64;
+  const int kbits = q.side[0].bits, vbits = q.n_sides > 1 ? q.side[1].bits : kbits;
+  if (kbits != 2 || vbits != 2) {
+    // 1- and 4-bit codes: fp16 rows with the (reordered) Hadamard rotation;
+    // one launch per side when the two widths differ
+    if (q.in_f32 || !(q.rot == 1 || q.rot == 3)) return hipErrorNotSupported;   // rejected by the caller
+    const bool perm = q.rot == 3;
+    for (int sd = 0; sd < q.n_sides; ++sd) {
+      if (sd == 1 && kbits == vbits) break;          // both sides in the first launch
+      RowsKernelArgs a1 = a;
+      int n_sides = q.n_sides;
+      if (kbits != vbits) {
+        a1.side[0] = q.side[sd];
+        a1.side[1] = q.side[sd];
+        a1.n_sides = 1;
+        n_sides = 1;
+      }
+      const int bits = q.side[sd].bits;
+      dim3 g1((unsigned)(n_tb * q.Hkv), 1, (unsigned)(q.B * n_sides));
+      if (bits == 1) {
+        if (perm) hipLaunchKernelGGL(kv_rotate_quant_fwht_perm_b1_f16, g1, dim3(64), 0, stream, a1);
+        else hipLaunchKernelGGL(kv_rotate_quant_fwht_b1_f16, g1, dim3(64), 0, stream, a1);
+      } else if (bits == 4) {
+        if (perm) hipLaunchKernelGGL(kv_rotate_quant_fwht_perm_b4_f16, g1, dim3(64), 0, stream, a1);
+        else hipLaunchKernelGGL(kv_rotate_quant_fwht_b4_f16, g1, dim3(64), 0, stream, a1);
+      } else {
+        if (perm) hipLaunchKernelGGL(kv_rotate_quant_fwht_perm_f16, g1, dim3(64), 0, stream, a1);
+        else hipLaunchKernelGGL(kv_rotate_quant_fwht_f16, g1, dim3(64), 0, stream, a1);
+      }
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   dim3 grid((unsigned)n_tb, (unsigned)q.Hkv, (unsigned)(q.B * q.n_sides));
   const bool rot = (q.rot == 1);
   if ((rot || q.rot == 3) && !q.in_f32) {

@@ -15,6 +15,7 @@ struct QuantSide {
   uint16_t *scales;
   uint16_t *zeros;
   int64_t T_cap;
+  int bits;             // code width: 1, 2 or 4 (codes per row: 16 * bits bytes)
 };
 
 struct QuantArgs {
@@ -40,6 +41,7 @@ struct DecodeArgs {
   int64_t B, Hq, Hkv;
   const uint8_t *kcodes; const uint16_t *kscales; const uint16_t *kzeros; int64_t kT_cap;
   const uint8_t *vcodes; const uint16_t *vscales; const uint16_t *vzeros; int64_t vT_cap;
+  int kbits, vbits;        // code widths (2: the INT2 kernels; else the b-bit kernel)
   int64_t t_begin, n_int2;
   const int32_t *t_ends;   // variable-length batch: per-sequence end (device [B]) or NULL
   int rot; const float *R; const int32_t *perm;

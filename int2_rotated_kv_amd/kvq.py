@@ -26,8 +26,9 @@ KVQ_ROT_NONE, KVQ_ROT_HADAMARD, KVQ_ROT_DENSE, KVQ_ROT_PERM_HADAMARD = 0, 1, 2, 
 _ROT = {"none": KVQ_ROT_NONE, "hadamard": KVQ_ROT_HADAMARD, "dense": KVQ_ROT_DENSE,
         "perm": KVQ_ROT_PERM_HADAMARD}
 
-EXPORTED_SYMBOLS = ("kvq_quantize", "kvq_quantize_at", "kvq_decode_workspace_bytes",
-                    "kvq_decode_attention", "kvq_decode_attention_varlen", "kvq_status_str",
+EXPORTED_SYMBOLS = ("kvq_quantize", "kvq_quantize_at", "kvq_quantize_bits",
+                    "kvq_decode_workspace_bytes", "kvq_decode_attention",
+                    "kvq_decode_attention_varlen", "kvq_decode_attention_bits", "kvq_status_str",
                     "kvq_abi_version")
 
 D_HEAD = 128
@@ -43,6 +44,11 @@ class KvqError(RuntimeError):
 class kvq_int2_cache(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("zeros", ctypes.c_void_p), ("T_cap", ctypes.c_int64)]
+
+
+class kvq_quant_cache(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("zeros", ctypes.c_void_p), ("T_cap", ctypes.c_int64), ("bits", ctypes.c_int32)]
 
 
 _lib = None
@@ -79,6 +85,14 @@ def load_library() -> ctypes.CDLL:
     lib.kvq_decode_attention.argtypes = [vp, i32, i64, i64, i64, i64, cp, cp, i64, i64,
                                          i32, vp, i32, vp, vp, i64, vp, vp, i64, f32,
                                          vp, i32, vp, ctypes.c_size_t, vp]
+    qp = ctypes.POINTER(kvq_quant_cache)
+    lib.kvq_quantize_bits.restype = i32
+    lib.kvq_quantize_bits.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, i64, i64,
+                                      i32, vp, i32, i64, qp, qp, vp]
+    lib.kvq_decode_attention_bits.restype = i32
+    lib.kvq_decode_attention_bits.argtypes = [vp, i32, i64, i64, i64, i64, qp, qp, i64, i64,
+                                              i32, vp, i32, vp, vp, i64, vp, vp, i64, f32,
+                                              vp, i32, vp, ctypes.c_size_t, vp]
     lib.kvq_status_str.restype = ctypes.c_char_p
     lib.kvq_status_str.argtypes = [i32]
     lib.kvq_abi_version.restype = i32
@@ -119,25 +133,37 @@ def _stream(stream):
 
 
 class Int2Cache:
-    """Device buffers of one side (K or V) of an INT2 cache.
+    """Device buffers of one side (K or V) of a quantized cache.
 
-    codes  uint8 [B, Hkv, T_cap, d/4]; scales / zeros fp16 [B, Hkv, T_cap, d/32]
+    codes  uint8 [B, Hkv, T_cap, d*bits/8]; scales / zeros fp16 [B, Hkv, T_cap, d/32].
+    bits = 2 (the INT2 format) unless given; 1 and 4 are the other widths.
     """
 
-    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor):
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+                 bits: int | None = None):
         self.codes, self.scales, self.zeros = codes, scales, zeros
         self.T_cap = codes.shape[2]
+        d = scales.shape[3] * GROUP
+        self.bits = bits if bits is not None else 8 * codes.shape[3] // d
+        if codes.shape[3] * 8 != d * self.bits:
+            raise ValueError("codes row length does not match the code width")
 
     @classmethod
-    def empty(cls, B: int, Hkv: int, T_cap: int, device="cuda", d: int = D_HEAD):
-        codes = torch.empty((B, Hkv, T_cap, d // 4), dtype=torch.uint8, device=device)
+    def empty(cls, B: int, Hkv: int, T_cap: int, device="cuda", d: int = D_HEAD, bits: int = 2):
+        codes = torch.empty((B, Hkv, T_cap, d * bits // 8), dtype=torch.uint8, device=device)
         scales = torch.empty((B, Hkv, T_cap, d // GROUP), dtype=torch.float16, device=device)
         zeros = torch.empty((B, Hkv, T_cap, d // GROUP), dtype=torch.float16, device=device)
-        return cls(codes, scales, zeros)
+        return cls(codes, scales, zeros, bits)
 
     def c_struct(self) -> kvq_int2_cache:
+        if self.bits != 2:
+            raise ValueError("not a 2-bit cache")
         return kvq_int2_cache(self.codes.data_ptr(), self.scales.data_ptr(),
                               self.zeros.data_ptr(), self.T_cap)
+
+    def c_quant_struct(self) -> kvq_quant_cache:
+        return kvq_quant_cache(self.codes.data_ptr(), self.scales.data_ptr(),
+                               self.zeros.data_ptr(), self.T_cap, self.bits)
 
     def nbytes(self) -> int:
         return self.codes.nbytes + self.scales.nbytes + self.zeros.nbytes
@@ -162,9 +188,21 @@ def kvq_quantize(K, V, cache_k: Int2Cache | None, cache_v: Int2Cache | None,
                                             or K.dtype != V.dtype):
         raise ValueError("K and V must share shape, strides and dtype")
     B, T_new, Hkv, d = x.shape
+    lib = load_library()
+    if any(c is not None and c.bits != 2 for c in (cache_k, cache_v)):
+        if t_offsets is not None:
+            raise ValueError("per-sequence slots are for 2-bit caches")
+        kq = cache_k.c_quant_struct() if cache_k is not None else None
+        vq = cache_v.c_quant_struct() if cache_v is not None else None
+        st = lib.kvq_quantize_bits(
+            _ptr(K), _ptr(V), _dtype_code(x), B, T_new, Hkv, d,
+            x.stride(0), x.stride(1), x.stride(2), _ROT[rot], _ptr(R), group, t_offset,
+            ctypes.byref(kq) if kq is not None else None,
+            ctypes.byref(vq) if vq is not None else None, _stream(stream))
+        _check(st, "kvq_quantize_bits")
+        return
     kc = cache_k.c_struct() if cache_k is not None else None
     vc = cache_v.c_struct() if cache_v is not None else None
-    lib = load_library()
     if t_offsets is not None:
         if t_offsets.dtype != torch.int32 or t_offsets.numel() != B:
             raise ValueError("t_offsets must be int32 [B]")
@@ -216,9 +254,24 @@ def kvq_decode_attention(q: torch.Tensor, cache_k: Int2Cache | None,
     need = kvq_decode_workspace_bytes(B, Hq, Hkv, d, t_end - t_begin, n_sink, n_res)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    lib = load_library()
+    if any(c is not None and c.bits != 2 for c in (cache_k, cache_v)):
+        if t_ends is not None:
+            raise ValueError("per-sequence ends are for 2-bit caches")
+        kq = cache_k.c_quant_struct() if cache_k is not None else None
+        vq = cache_v.c_quant_struct() if cache_v is not None else None
+        st = lib.kvq_decode_attention_bits(
+            _ptr(q), _dtype_code(q), B, Hq, Hkv, d,
+            ctypes.byref(kq) if kq is not None else None,
+            ctypes.byref(vq) if vq is not None else None,
+            t_begin, t_end, _ROT[rot], _ptr(R), group,
+            _ptr(sink_k), _ptr(sink_v), n_sink, _ptr(res_k), _ptr(res_v), n_res,
+            float(softmax_scale), _ptr(out), _dtype_code(out),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+        _check(st, "kvq_decode_attention_bits")
+        return out
     kc = cache_k.c_struct() if cache_k is not None else None
     vc = cache_v.c_struct() if cache_v is not None else None
-    lib = load_library()
     if t_ends is not None:
         if t_ends.dtype != torch.int32 or t_ends.numel() != B:
             raise ValueError("t_ends must be int32 [B]")

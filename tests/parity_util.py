@@ -15,8 +15,8 @@ def require_gpu():
     kvq.load_library()
 
 
-def empty_cache(B, H, T_cap, device="cuda"):
-    c = kvq.Int2Cache.empty(B, H, T_cap, device=device)
+def empty_cache(B, H, T_cap, device="cuda", bits=2):
+    c = kvq.Int2Cache.empty(B, H, T_cap, device=device, bits=bits)
     c.codes.fill_(SENTINEL)
     c.scales.view(torch.uint8).fill_(SENTINEL)
     c.zeros.view(torch.uint8).fill_(SENTINEL)
@@ -43,9 +43,10 @@ def rot_matrix(rot, R=None):
     return np.asarray(R, dtype=np.float32)
 
 
-def compare_codes_at_ties(x_rows, R, gpu, ora, tau=1e-4, max_frac=1e-5):
+def compare_codes_at_ties(x_rows, R, gpu, ora, tau=1e-4, max_frac=1e-5, bits=2):
     """Rotated-path code check.  x_rows: [..., d] inputs (numpy), gpu/ora:
-    (packed, scales, zeros) with matching leading shapes.  Returns stats.
+    (packed, scales, zeros) with matching leading shapes, codes `bits` wide.
+    Returns stats.
 
     Every differing code must differ by one and sit at a rounding tie of the
     exact quantizer argument (within tau of k + 1/2), unless its group's
@@ -53,8 +54,8 @@ def compare_codes_at_ties(x_rows, R, gpu, ora, tau=1e-4, max_frac=1e-5):
     """
     gp, gs, gz = gpu
     op, os_, oz = ora
-    gc = O.unpack_codes(gp).astype(np.int16)
-    oc = O.unpack_codes(op).astype(np.int16)
+    gc = O.unpack_codes(gp, bits).astype(np.int16)
+    oc = O.unpack_codes(op, bits).astype(np.int16)
     diff = gc != oc
     n = gc.size
     sz_diff = (gs.view(np.uint16) != os_.view(np.uint16)) | (gz.view(np.uint16) != oz.view(np.uint16))

@@ -207,3 +207,34 @@ def test_workspace_bytes():
         w = K.kvq_decode_workspace_bytes(1, 8, 8, 128, n)
         assert w >= prev
         prev = w
+
+
+def _qcache(bits, T_cap=64):
+    return K.kvq_quant_cache(FAKE, FAKE, FAKE, T_cap, bits)
+
+
+def test_quantize_bits_rejects(lib):
+    """Code widths: 1, 2 or 4 bits per side; 1 and 4 need fp16 rows with
+    the (reordered) Hadamard rotation."""
+    def call(kb, vb, dt=K.KVQ_F16, rot=K.KVQ_ROT_HADAMARD, R=None):
+        return lib.kvq_quantize_bits(FAKE, FAKE, dt, 1, 8, 2, 128, 8 * 2 * 128, 2 * 128, 128,
+                                     rot, R, 32, 0, ctypes.byref(_qcache(kb)),
+                                     ctypes.byref(_qcache(vb)), None)
+    assert call(3, 2) == K.KVQ_ERR_INVALID_ARG                  # no 3-bit codes
+    assert call(2, 8) == K.KVQ_ERR_INVALID_ARG
+    assert call(4, 2, dt=K.KVQ_F32) == K.KVQ_ERR_UNSUPPORTED    # fp32 rows at 4 bits
+    assert call(2, 1, rot=K.KVQ_ROT_NONE) == K.KVQ_ERR_UNSUPPORTED
+    assert call(4, 4, rot=K.KVQ_ROT_DENSE, R=FAKE) == K.KVQ_ERR_UNSUPPORTED
+    assert call(4, 2, rot=K.KVQ_ROT_PERM_HADAMARD) == K.KVQ_ERR_INVALID_ARG   # no channel order
+
+
+def test_decode_bits_rejects(lib):
+    def call(kb, vb, rot=K.KVQ_ROT_HADAMARD, R=None, wsb=1 << 30):
+        return lib.kvq_decode_attention_bits(
+            FAKE, K.KVQ_F16, 2, 4, 2, 128, ctypes.byref(_qcache(kb)), ctypes.byref(_qcache(vb)),
+            0, 64, rot, R, 32, None, None, 0, None, None, 0, 0.0, FAKE, K.KVQ_F16,
+            FAKE * 16, wsb, None)
+    assert call(3, 2) == K.KVQ_ERR_INVALID_ARG
+    assert call(4, 0) == K.KVQ_ERR_INVALID_ARG
+    assert call(4, 2, rot=K.KVQ_ROT_DENSE, R=FAKE) == K.KVQ_ERR_UNSUPPORTED   # no dense R at 4 bits
+    assert call(1, 4, wsb=100) == K.KVQ_ERR_WORKSPACE_TOO_SMALL

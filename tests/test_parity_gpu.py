@@ -499,6 +499,80 @@ def test_decode_varlen(cid, Hkv, Hq, rot):
         assert err <= ATTN_TOL
 
 
+# ------------------------------------------------ other code widths (1, 4 bits)
+@pytest.mark.parametrize("kbits,vbits,rot", [(4, 2, "hadamard"), (1, 4, "hadamard"), (4, 4, "perm"),
+                                             (1, 1, "perm")])
+def test_quantize_bits_ties(kbits, vbits, rot):
+    """b-bit write path (keys and values at their own widths): codes, fp16
+    scales and zeros against the oracle's b-bit codec, compared at rounding
+    ties as for 2 bits; a ragged token count at an offset, so the first 9
+    slots and the rows past T_new keep their sentinel bytes."""
+    cfg = W.small_config(W.config(2), B=2, T=700, Hkv=3, Hq=3)
+    perm = W.channel_orders(cfg) if rot == "perm" else None
+    Rm = rot_matrix(rot, perm)
+    K = W.kv_tokens(cfg, "K")
+    V = W.kv_tokens(cfg, "V")
+    T_cap = cfg.T + 20
+    kc = empty_cache(cfg.B, cfg.Hkv, T_cap, bits=kbits)
+    vc = empty_cache(cfg.B, cfg.Hkv, T_cap, bits=vbits)
+    kvq.kvq_quantize(K.to(DEV), V.to(DEV), kc, vc, rot=rot, R=_rot_arg(rot, perm), t_offset=9)
+    torch.cuda.synchronize()
+    tot = dict(elements=0, code_mismatch=0, group_scale_zero_diff=0)
+    for x, c, bits in ((K, kc, kbits), (V, vc, vbits)):
+        gp, gs, gz = cache_to_numpy(c)
+        assert gp.shape[-1] == 16 * bits
+        for arr in (gp, gs.view(np.uint8), gz.view(np.uint8)):       # untouched slots
+            assert np.all(arr[:, :, :9] == SENTINEL) and np.all(arr[:, :, 9 + cfg.T:] == SENTINEL)
+        xh = x.permute(0, 2, 1, 3).contiguous().numpy()
+        ora = O.quantize_cache(xh, Rm, bits=bits)
+        for h in range(cfg.Hkv):
+            Rh = Rm if rot != "perm" else Rm[h]
+            st = compare_codes_at_ties(xh[:, h], Rh, tuple(a[:, h, 9:9 + cfg.T] for a in (gp, gs, gz)),
+                                       tuple(a[:, h] for a in ora), max_frac=1.0, bits=bits)
+            for k in tot:
+                tot[k] += st[k]
+    _report(f"quantize bits K{kbits}V{vbits} {rot}", **tot)
+    assert tot["code_mismatch"] <= 1e-5 * tot["elements"]
+
+
+@pytest.mark.parametrize("kbits,vbits,rot,cid,G", [
+    (4, 2, "hadamard", 2, 1), (2, 4, "hadamard", 2, 1), (1, 1, "hadamard", 2, 1),
+    (4, 4, "hadamard", 2, 1), (1, 2, "none", 1, 1), (4, 2, "perm", 2, 1),
+    (4, 2, "hadamard", 2, 4), (4, 2, "hadamard", 5, 1), (2, 1, "hadamard", 1, 2)])
+def test_decode_bits(kbits, vbits, rot, cid, G):
+    """b-bit decode (the kernel for widths other than 2/2) against the
+    oracle on the same cache bytes: keys and values at their own widths,
+    none / Hadamard / reordered Hadamard, a query group, fp16 sinks and
+    residual tokens (LLaMA-2-13B recipe), a ragged INT2 range that starts
+    inside a tile and spans several tiles and splits."""
+    T = 900
+    cfg = W.small_config(W.config(cid), T=T, B=2, Hkv=2, Hq=2 * G)
+    perm = W.channel_orders(cfg) if rot == "perm" else None
+    Rm = rot_matrix(rot, perm)
+    K = W.kv_tokens(cfg, "K")
+    V = W.kv_tokens(cfg, "V")
+    kh = K.permute(0, 2, 1, 3).contiguous().numpy()
+    vh = V.permute(0, 2, 1, 3).contiguous().numpy()
+    kcache = O.quantize_cache(kh, Rm, bits=kbits)
+    vcache = O.quantize_cache(vh, Rm, bits=vbits)
+    q = W.queries(cfg)
+    fp16 = {}
+    tb, te = (cfg.n_sink, T - cfg.n_res) if (cfg.n_sink or cfg.n_res) else (7, T - 5)
+    if cfg.n_sink or cfg.n_res:
+        fp16 = dict(sink_k=np.ascontiguousarray(kh[:, :, :cfg.n_sink]).astype(np.float16),
+                    sink_v=np.ascontiguousarray(vh[:, :, :cfg.n_sink]).astype(np.float16),
+                    res_k=np.ascontiguousarray(kh[:, :, T - cfg.n_res:]).astype(np.float16),
+                    res_v=np.ascontiguousarray(vh[:, :, T - cfg.n_res:]).astype(np.float16))
+    up = {k: torch.from_numpy(v).to(DEV) for k, v in fp16.items()}
+    out = kvq.kvq_decode_attention(q.to(DEV), cache_from_numpy(*kcache), cache_from_numpy(*vcache),
+                                   tb, te, rot=rot, R=_rot_arg(rot, perm), **up)
+    torch.cuda.synchronize()
+    ref = O.decode_attention(q.numpy(), kcache, vcache, tb, te, Rm, **fp16)
+    err = normwise_rel_err(out.float().cpu().numpy(), ref)
+    _report(f"decode bits K{kbits}V{vbits} {rot} c{cid} G={G}", normwise=err)
+    assert err <= ATTN_TOL
+
+
 @pytest.mark.parametrize("B,Hq", [(64, 1), (70, 1), (67, 4), (130, 1)])
 def test_decode_varlen_many_sequences(B, Hq):
     """Variable-length batches of many sequences with a skewed length mix:
