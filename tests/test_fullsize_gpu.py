@@ -41,9 +41,11 @@ def _head_slice_cpu(cfg, which, b, h, t0=0, t1=None):
 
 
 def _check_head(cfg, Kd, Vd, ck, cv, out, q, b, hk, rot, R, t_begin, t_end,
-                sink=None, res=None):
-    """Codes of head (b, hk) vs oracle at ties; decode of its query heads vs
-    the oracle on the GPU codes."""
+                sink=None, res=None, code_end=None):
+    """Codes of head (b, hk) vs oracle at ties (rows [t_begin, code_end),
+    default t_end); decode of its query heads over [t_begin, t_end) vs the
+    oracle on the GPU codes.  Each cache side is read at its own width."""
+    code_end = t_end if code_end is None else code_end
     Rm = rot_matrix(rot, R)
     Rh = Rm if rot != "dense" else Rm[hk]
     stats = {}
@@ -51,12 +53,12 @@ def _check_head(cfg, Kd, Vd, ck, cv, out, q, b, hk, rot, R, t_begin, t_end,
         x_cpu = _head_slice_cpu(cfg, which, b, hk)
         x_dev = xd[b, :, hk].cpu()
         assert torch.equal(x_cpu, x_dev), "generator differs between CPU and GPU"
-        xr = x_cpu[t_begin:t_end].numpy()[None]                # [1, T, d]
-        gpu = tuple(a[b, hk, t_begin:t_end].cpu().numpy()[None]
+        xr = x_cpu[t_begin:code_end].numpy()[None]             # [1, T, d]
+        gpu = tuple(a[b, hk, t_begin:code_end].cpu().numpy()[None]
                     for a in (c.codes, c.scales, c.zeros))
-        ora = O.quantize_cache(xr[:, None], Rh)
+        ora = O.quantize_cache(xr[:, None], Rh, bits=c.bits)
         ora = tuple(a[:, 0] for a in ora)
-        stats[which] = compare_codes_at_ties(xr, Rh, gpu, ora)
+        stats[which] = compare_codes_at_ties(xr, Rh, gpu, ora, bits=c.bits)
     G = cfg.G
     hq = slice(hk * G, hk * G + G)
     kc = tuple(a[b:b + 1, hk:hk + 1].cpu().numpy() for a in (ck.codes, ck.scales, ck.zeros))
@@ -135,3 +137,45 @@ def test_fullsize_config5_sinks_residual():
         _report(f"c5 b={b} h={hk}", normwise_full=err, normwise_int2_only=err2,
                 K=stats["K"], V=stats["V"])
         assert err <= ATTN_TOL and err2 <= ATTN_TOL
+
+
+def test_fullsize_config3_key4_value2():
+    """Throughput shapes with 4-bit keys and 2-bit values (the b-bit write
+    and decode kernels, as bench.py --kbits 4 --vbits 2 runs them)."""
+    cfg = W.config(3)
+    B, T, H, d = cfg.B, cfg.T, cfg.Hkv, cfg.d
+    K = W.kv_tokens(cfg, "K", device=DEV)
+    V = W.kv_tokens(cfg, "V", device=DEV)
+    q = W.queries(cfg, device=DEV)
+    ck, cv = kvq.Int2Cache.empty(B, H, T, bits=4), kvq.Int2Cache.empty(B, H, T, bits=2)
+    kvq.kvq_quantize(K, V, ck, cv, rot="hadamard")
+    out = kvq.kvq_decode_attention(q, ck, cv, 0, T, rot="hadamard")
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    for b, hk in ((0, 0), (9, 17)):
+        stats, err = _check_head(cfg, K, V, ck, cv, out, q, b, hk, "hadamard", None, 0, T)
+        _report(f"c3 K4V2 b={b} h={hk}", normwise=err, K=stats["K"], V=stats["V"])
+        assert err <= ATTN_TOL
+
+
+def test_fullsize_config3_varlen():
+    """Throughput shapes as a mixed-length batch (the ends bench.py --varlen
+    draws): sampled sequences against the oracle over their own ranges."""
+    cfg = W.config(3)
+    B, T, H, d = cfg.B, cfg.T, cfg.Hkv, cfg.d
+    K = W.kv_tokens(cfg, "K", device=DEV)
+    V = W.kv_tokens(cfg, "V", device=DEV)
+    q = W.queries(cfg, device=DEV)
+    ck, cv = kvq.Int2Cache.empty(B, H, T), kvq.Int2Cache.empty(B, H, T)
+    kvq.kvq_quantize(K, V, ck, cv, rot="hadamard")
+    rng = np.random.default_rng(np.random.SeedSequence([1000 + cfg.cid, 77]))
+    ends = rng.integers(T // 2, T + 1, size=B).astype(np.int32)
+    out = kvq.kvq_decode_attention(q, ck, cv, 0, T, rot="hadamard",
+                                   t_ends=torch.from_numpy(ends).to(DEV))
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    for b, hk in ((int(np.argmin(ends)), 3), (int(np.argmax(ends)), 30), (5, 11)):
+        _, err = _check_head(cfg, K, V, ck, cv, out, q, b, hk, "hadamard", None, 0, int(ends[b]),
+                             code_end=64)
+        _report(f"c3 varlen b={b} end={int(ends[b])} h={hk}", normwise=err)
+        assert err <= ATTN_TOL
