@@ -357,31 +357,51 @@ constexpr int kStageRowDwords = 64 + 4;     // 128 fp16 + 16-byte pad
 // its LDS row (one 2-byte store each, the row offset in the store's
 // immediate), and the rows are read back as in the plain kernel.  Indices
 // are taken modulo 128, so any order array stays inside the rows.
-template <bool PERM, int BITS>
+// HG = 4: a wave takes 16 consecutive tokens of 4 consecutive heads (64 rows),
+// so each staging load reads the 4 heads' rows of one token, 1 KiB of
+// contiguous input when heads are adjacent, and each store writes runs of
+// 16 rows per head.  HG = 1: 64 consecutive tokens of one head.
+template <bool PERM, int BITS, int HG>
 __device__ __forceinline__ void fwht_f16_body(const RowsKernelArgs &a) {
+  constexpr int TPW = 64 / HG;                       // tokens per wave
   __shared__ uint32_t stage[64 * kStageRowDwords];
   const int lane = threadIdx.x;
-  const int h = (int)(blockIdx.x % (unsigned)a.Hkv);
-  const int64_t t0 = (int64_t)(blockIdx.x / (unsigned)a.Hkv) * 64;
+  const int hgroups = a.Hkv / HG;
+  const int h0 = (int)(blockIdx.x % (unsigned)hgroups) * HG;
   const int sidx = (int)(blockIdx.z % (unsigned)a.n_sides);
   const int64_t b = blockIdx.z / (unsigned)a.n_sides;
   const QuantSide s = sidx ? a.side[1] : a.side[0];
+  // HG = 4: the 16-token tiles are laid on 16-slot boundaries of the cache
+  // (the first tile starts `shift` tokens early, those tokens masked), so
+  // each 16-row run of scales or zeros is one whole 128-byte line when T_cap
+  // is a multiple of 16; a per-sequence slot gives a per-sequence shift.
+  const int64_t slot_base = seq_offset(a.offsets, a.t_offset, b);
+  const int64_t shift = HG == 1 ? 0 : ((slot_base % 16) + 16) % 16;
+  const int64_t t0 = (int64_t)(blockIdx.x / (unsigned)hgroups) * TPW - shift;
+  if (t0 >= a.T_new) return;                         // the extra tile of a shift of 0: no token
   const _Float16 *base = reinterpret_cast<const _Float16 *>(s.x) + b * a.stride_b +
-                         (int64_t)h * a.stride_h;
+                         (int64_t)h0 * a.stride_h;
 
-  // coalesced staging: instruction i covers rows 4i..4i+3, 16 lanes per row
+  // Coalesced staging: instruction i covers stage rows 4i..4i+3, 16 lanes
+  // per row.  Stage row r holds token t0 + r / HG of head h0 + r % HG (HG = 4:
+  // instruction i reads token i of the 4 heads; HG = 1: tokens 4i..4i+3).
   const int chunk = lane & 15;
   const int r0 = lane >> 4;
+  const int hr = HG == 1 ? 0 : r0;                   // head of this lane's staged rows
+  auto tok_of_load = [&](int i) { return HG == 1 ? 4 * i + r0 : i; };
   // PERM: channel c is staged at position pinv[c] of its row (pinv = the
   // inverse of the head's order, built in LDS), so the rows are read back
   // already reordered.  pos[e]: byte offset of channel 8 chunk + e in row r0.
   uint32_t pos[8];
   if constexpr (PERM) {
-    __shared__ uint8_t pinv[kD];
-    const int32_t *pi = a.perm + (int64_t)h * kD;
-    pinv[pi[2 * lane] & (kD - 1)] = (uint8_t)(2 * lane);
-    pinv[pi[2 * lane + 1] & (kD - 1)] = (uint8_t)(2 * lane + 1);
+    __shared__ uint8_t pinv_all[HG][kD];
+    for (int g = 0; g < HG; ++g) {
+      const int32_t *pi = a.perm + (int64_t)(h0 + g) * kD;
+      pinv_all[g][pi[2 * lane] & (kD - 1)] = (uint8_t)(2 * lane);
+      pinv_all[g][pi[2 * lane + 1] & (kD - 1)] = (uint8_t)(2 * lane + 1);
+    }
     __syncthreads();
+    const uint8_t *pinv = pinv_all[hr];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       pos[e] = (uint32_t)(r0 * kStageRowDwords * 4 + 2 * (pinv[8 * chunk + e] & (kD - 1)));
@@ -399,17 +419,20 @@ __device__ __forceinline__ void fwht_f16_body(const RowsKernelArgs &a) {
   };
   // all 16 loads of the tile first, then the LDS writes
   u32x4_t ld[16];
-  if (t0 + 64 <= a.T_new) {
-    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(base + (t0 + r0) * a.stride_t) + chunk;
-    const int64_t step = 4 * a.stride_t / 8;        // 4 rows, in 16-byte units
+  {
+    const _Float16 *hb = base + (int64_t)hr * a.stride_h;
+    if (t0 >= 0 && t0 + TPW <= a.T_new) {
+      const u32x4_t *src = reinterpret_cast<const u32x4_t *>(hb + (t0 + tok_of_load(0)) * a.stride_t) + chunk;
+      const int64_t step = (HG == 1 ? 4 : 1) * a.stride_t / 8;   // in 16-byte units
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ld[i] = __builtin_nontemporal_load(src + i * step);
-  } else {                                          // rows past T_new re-read row 0
+      for (int i = 0; i < 16; ++i) ld[i] = __builtin_nontemporal_load(src + i * step);
+    } else {                                        // tokens past T_new re-read the first
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int64_t t = t0 + 4 * i + r0;
-      const int64_t tl = t < a.T_new ? t : 0;
-      ld[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(base + tl * a.stride_t) + chunk);
+      for (int i = 0; i < 16; ++i) {
+        const int64_t t = t0 + tok_of_load(i);
+        const int64_t tl = (t >= 0 && t < a.T_new) ? t : (t0 > 0 ? t0 : 0);   // t0 < T_new here
+        ld[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(hb + tl * a.stride_t) + chunk);
+      }
     }
   }
 #pragma unroll
@@ -432,16 +455,20 @@ __device__ __forceinline__ void fwht_f16_body(const RowsKernelArgs &a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     hA[i] = (__builtin_popcount((unsigned)(n & (4 * q + i))) & 1) ? (_Float16)-1.0f : (_Float16)1.0f;
-  const int64_t slot0 = seq_offset(a.offsets, a.t_offset, b) + t0;
-  const int64_t n_valid = a.T_new - t0;              // >= 1; rows past it are not ours
-  const int64_t lo = slot0 < 0 ? -slot0 : 0;         // rows [lo, hi) of the tile are written
+  const int64_t slot0 = slot_base + t0;
+  const int64_t n_valid = a.T_new - t0;              // >= 1; tokens past it are not ours
+  // tokens [lo, hi) of the tile are written: at or after token 0 and slot 0
+  const int64_t lo = (slot0 < 0 ? -slot0 : 0) > -t0 ? (slot0 < 0 ? -slot0 : 0) : -t0;
   const int64_t hi = s.T_cap - slot0 < n_valid ? s.T_cap - slot0 : n_valid;
-  const int64_t row0 = (b * a.Hkv + h) * s.T_cap + slot0;
+  // first cache row of (token 0 of the tile, head h0 + g)
+  auto row_of = [&](int g) { return (b * a.Hkv + h0 + g) * s.T_cap + slot0; };
 
-  uint32_t cw[4][BITS], csz[4];                      // codes and scale | zero << 16 of row 16g + n
+  // lane (n, q): stage row r(g) = 16g + n for HG = 1, 4n + g for HG = 4
+  auto srow = [&](int g) { return HG == 1 ? 16 * g + n : 4 * n + g; };
+  uint32_t cw[4][BITS], csz[4];                      // codes and scale | zero << 16 of stage row srow(g)
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    const int r = 16 * g + n;                        // the lane's token row in the tile
+    const int r = srow(g);                           // the lane's stage row
     // channels 8(4q + i) .. 8(4q + i) + 7 of row r, i = 0..3
     u32x4_t u[4];
 #pragma unroll
@@ -492,49 +519,85 @@ __device__ __forceinline__ void fwht_f16_body(const RowsKernelArgs &a) {
   __syncthreads();                                   // the stage is read
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    const int r = 16 * g + n;
+    const int r = srow(g);
 #pragma unroll
     for (int k = 0; k < BITS; ++k) stage[r * kRowDwords + BITS * q + k] = cw[g][k];
     stage[kSzOff + r * 4 + q] = csz[g];
   }
   __syncthreads();
   {
-    u32x4_t *rows = reinterpret_cast<u32x4_t *>(stage);
-    u32x4_t *cdst = reinterpret_cast<u32x4_t *>(s.codes + row0 * row_bytes);
+    // stage row r = token r / HG of head h0 + r % HG (HG = 1: token r)
+    const u32x4_t *rows = reinterpret_cast<const u32x4_t *>(stage);
 #pragma unroll
     for (int kk = 0; kk < BITS; ++kk) {
-      const int r = (64 * kk + lane) / BITS;
-      if (r >= lo && r < hi)
-        __builtin_nontemporal_store(rows[64 * kk + lane], cdst + 64 * kk + lane);
+      const int c = 64 * kk + lane;                  // 16-byte chunk c % BITS of stage row c / BITS
+      const int r = c / BITS, tk = r / HG;
+      if (tk >= lo && tk < hi)
+        __builtin_nontemporal_store(rows[c], reinterpret_cast<u32x4_t *>(s.codes + (row_of(r % HG) + tk) * row_bytes) + c % BITS);
     }
-    if (lane >= lo && lane < hi) {
+    const int tk = lane / HG;
+    if (tk >= lo && tk < hi) {
+      const int64_t row = row_of(lane % HG) + tk;
       const u32x4_t e = *reinterpret_cast<const u32x4_t *>(&stage[kSzOff + lane * 4]);
       const u32x2_t sv = {__builtin_amdgcn_perm(e.y, e.x, 0x05040100u), __builtin_amdgcn_perm(e.w, e.z, 0x05040100u)};
       const u32x2_t zv = {__builtin_amdgcn_perm(e.y, e.x, 0x07060302u), __builtin_amdgcn_perm(e.w, e.z, 0x07060302u)};
-      __builtin_nontemporal_store(sv, reinterpret_cast<u32x2_t *>(s.scales + row0 * kNGroups) + lane);
-      __builtin_nontemporal_store(zv, reinterpret_cast<u32x2_t *>(s.zeros + row0 * kNGroups) + lane);
+      __builtin_nontemporal_store(sv, reinterpret_cast<u32x2_t *>(s.scales + row * kNGroups));
+      __builtin_nontemporal_store(zv, reinterpret_cast<u32x2_t *>(s.zeros + row * kNGroups));
     }
   }
 }
 
+template <int HG>
 __global__ __launch_bounds__(64) void kv_rotate_quant_fwht_f16(RowsKernelArgs a) {
-  fwht_f16_body<false, 2>(a);
+  fwht_f16_body<false, 2, HG>(a);
 }
+template <int HG>
 __global__ __launch_bounds__(64) void kv_rotate_quant_fwht_perm_f16(RowsKernelArgs a) {
-  fwht_f16_body<true, 2>(a);
+  fwht_f16_body<true, 2, HG>(a);
 }
 // 1- and 4-bit codes (keys and values may be kept at different widths)
+template <int HG>
 __global__ __launch_bounds__(64) void kv_rotate_quant_fwht_b1_f16(RowsKernelArgs a) {
-  fwht_f16_body<false, 1>(a);
+  fwht_f16_body<false, 1, HG>(a);
 }
+template <int HG>
 __global__ __launch_bounds__(64) void kv_rotate_quant_fwht_b4_f16(RowsKernelArgs a) {
-  fwht_f16_body<false, 4>(a);
+  fwht_f16_body<false, 4, HG>(a);
 }
+template <int HG>
 __global__ __launch_bounds__(64) void kv_rotate_quant_fwht_perm_b1_f16(RowsKernelArgs a) {
-  fwht_f16_body<true, 1>(a);
+  fwht_f16_body<true, 1, HG>(a);
 }
+template <int HG>
 __global__ __launch_bounds__(64) void kv_rotate_quant_fwht_perm_b4_f16(RowsKernelArgs a) {
-  fwht_f16_body<true, 4>(a);
+  fwht_f16_body<true, 4, HG>(a);
+}
+
+// The fp16 Hadamard write kernels: a wave takes 16 tokens of 4 heads when
+// the head count allows, else 64 tokens of one head.
+template <int HG>
+static hipError_t launch_fwht_hg(const RowsKernelArgs &a, int64_t T_new, int64_t Hkv, int64_t zdim,
+                                 bool perm, int bits, hipStream_t stream) {
+  // HG = 4: one more tile for the shift onto 16-slot boundaries
+  const int64_t tiles = HG == 1 ? (T_new + 63) / 64 : (T_new + 15) / 16 + 1;
+  const dim3 grid((unsigned)(tiles * (Hkv / HG)), 1, (unsigned)zdim), block(64);
+  if (bits == 1) {
+    if (perm) hipLaunchKernelGGL(kv_rotate_quant_fwht_perm_b1_f16<HG>, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(kv_rotate_quant_fwht_b1_f16<HG>, grid, block, 0, stream, a);
+  } else if (bits == 4) {
+    if (perm) hipLaunchKernelGGL(kv_rotate_quant_fwht_perm_b4_f16<HG>, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(kv_rotate_quant_fwht_b4_f16<HG>, grid, block, 0, stream, a);
+  } else {
+    if (perm) hipLaunchKernelGGL(kv_rotate_quant_fwht_perm_f16<HG>, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(kv_rotate_quant_fwht_f16<HG>, grid, block, 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+static hipError_t launch_fwht_f16(const RowsKernelArgs &a, int64_t T_new, int64_t Hkv, int64_t zdim,
+                                  bool perm, int bits, hipStream_t stream) {
+  if (Hkv % 4 == 0) return launch_fwht_hg<4>(a, T_new, Hkv, zdim, perm, bits, stream);
+  return launch_fwht_hg<1>(a, T_new, Hkv, zdim, perm, bits, stream);
 }
 
 hipError_t launch_quantize_rows(const QuantArgs &q, hipStream_t stream) {
@@ -568,30 +631,15 @@ hipError_t launch_quantize_rows(const QuantArgs &q, hipStream_t stream) {
         n_sides = 1;
       }
       const int bits = q.side[sd].bits;
-      dim3 g1((unsigned)(n_tb * q.Hkv), 1, (unsigned)(q.B * n_sides));
-      if (bits == 1) {
-        if (perm) hipLaunchKernelGGL(kv_rotate_quant_fwht_perm_b1_f16, g1, dim3(64), 0, stream, a1);
-        else hipLaunchKernelGGL(kv_rotate_quant_fwht_b1_f16, g1, dim3(64), 0, stream, a1);
-      } else if (bits == 4) {
-        if (perm) hipLaunchKernelGGL(kv_rotate_quant_fwht_perm_b4_f16, g1, dim3(64), 0, stream, a1);
-        else hipLaunchKernelGGL(kv_rotate_quant_fwht_b4_f16, g1, dim3(64), 0, stream, a1);
-      } else {
-        if (perm) hipLaunchKernelGGL(kv_rotate_quant_fwht_perm_f16, g1, dim3(64), 0, stream, a1);
-        else hipLaunchKernelGGL(kv_rotate_quant_fwht_f16, g1, dim3(64), 0, stream, a1);
-      }
-      const hipError_t e = hipGetLastError();
+      const hipError_t e = launch_fwht_f16(a1, q.T_new, q.Hkv, q.B * n_sides, perm, bits, stream);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;
   }
   dim3 grid((unsigned)n_tb, (unsigned)q.Hkv, (unsigned)(q.B * q.n_sides));
   const bool rot = (q.rot == 1);
-  if ((rot || q.rot == 3) && !q.in_f32) {
-    dim3 grid_hf((unsigned)(n_tb * q.Hkv), 1, (unsigned)(q.B * q.n_sides));
-    if (q.rot == 3) hipLaunchKernelGGL(kv_rotate_quant_fwht_perm_f16, grid_hf, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL(kv_rotate_quant_fwht_f16, grid_hf, dim3(64), 0, stream, a);
-    return hipGetLastError();
-  }
+  if ((rot || q.rot == 3) && !q.in_f32)
+    return launch_fwht_f16(a, q.T_new, q.Hkv, q.B * q.n_sides, q.rot == 3, 2, stream);
   if (q.rot == 3) return hipErrorNotSupported;     // fp32 input: the caller has rejected it
   dim3 block(256);
   if (q.in_f32) {
