@@ -38,6 +38,42 @@ kvq_status check_cache(const kvq_quant_cache *c) {
   return KVQ_OK;
 }
 
+// Block table of a paged cache (both sides share it).
+struct Paging {
+  const int32_t *block_table;
+  int64_t max_pages, n_pages, page_tokens;
+};
+
+// Checks a paged side pair and the table; on success fills the 2-bit cache
+// views (T_cap = the logical capacity max_pages * page_tokens) and pg.
+kvq_status check_paged(const kvq_paged_cache *kc, const kvq_paged_cache *vc, const int32_t *block_table,
+                       int64_t B, int64_t max_pages, kvq_quant_cache &kq, kvq_quant_cache &vq, Paging &pg) {
+  if (block_table == nullptr || ((uintptr_t)block_table & 3u) != 0) return KVQ_ERR_INVALID_ARG;
+  if (max_pages <= 0 || B < 0 || B * max_pages > 0x7FFFFFFF) return KVQ_ERR_INVALID_ARG;
+  const kvq_paged_cache *cs[2] = {kc, vc};
+  kvq_quant_cache *qs[2] = {&kq, &vq};
+  int64_t np = -1, pt = -1;
+  for (int i = 0; i < 2; ++i) {
+    const kvq_paged_cache *c = cs[i];
+    if (c == nullptr) continue;
+    if (c->codes == nullptr || c->scales == nullptr || c->zeros == nullptr) return KVQ_ERR_INVALID_ARG;
+    if (!aligned16(c->codes) || !aligned16(c->scales) || !aligned16(c->zeros)) return KVQ_ERR_INVALID_ARG;
+    if (c->n_pages <= 0 || c->page_tokens < 64 || c->page_tokens % 64 != 0) return KVQ_ERR_INVALID_ARG;
+    if (np >= 0 && (c->n_pages != np || c->page_tokens != pt)) return KVQ_ERR_INVALID_ARG;
+    np = c->n_pages;
+    pt = c->page_tokens;
+    if (max_pages > ((int64_t)1 << 40) / pt) return KVQ_ERR_INVALID_ARG;
+    qs[i]->codes = c->codes; qs[i]->scales = c->scales; qs[i]->zeros = c->zeros;
+    qs[i]->T_cap = max_pages * c->page_tokens;
+    qs[i]->bits = 2;
+  }
+  pg.block_table = block_table;
+  pg.max_pages = max_pages;
+  pg.n_pages = np;
+  pg.page_tokens = pt;
+  return KVQ_OK;
+}
+
 // An INT2 cache side as a 2-bit cache side (NULL stays NULL).
 struct AsQuant {
   kvq_quant_cache c;
@@ -67,7 +103,8 @@ kvq_status quantize_impl(const void *K, const void *V, kvq_dtype in_dtype, int64
                          int64_t T_new, int64_t Hkv, int64_t d, int64_t stride_b,
                          int64_t stride_t, int64_t stride_h, kvq_rot rot, const void *R,
                          int group, int64_t t_offset, const int32_t *offsets,
-                         const kvq_quant_cache *kc, const kvq_quant_cache *vc, void *stream) {
+                         const kvq_quant_cache *kc, const kvq_quant_cache *vc, void *stream,
+                         const Paging *pg = nullptr) {
   if (!valid_dtype(in_dtype)) return KVQ_ERR_INVALID_ARG;
   if (B < 0 || T_new < 0 || Hkv <= 0 || t_offset < 0) return KVQ_ERR_INVALID_ARG;
   if (stride_b < 0 || stride_t < 0 || stride_h < 0) return KVQ_ERR_INVALID_ARG;
@@ -116,6 +153,13 @@ kvq_status quantize_impl(const void *K, const void *V, kvq_dtype in_dtype, int64
   a.rot = (int)rot;
   a.R = rot == KVQ_ROT_DENSE ? static_cast<const float *>(R) : nullptr;
   a.perm = rot == KVQ_ROT_PERM_HADAMARD ? static_cast<const int32_t *>(R) : nullptr;
+  if (pg != nullptr) {
+    // paged writes run the fp16 Hadamard kernels only
+    if (in_dtype != KVQ_F16 || !(rot == KVQ_ROT_HADAMARD || rot == KVQ_ROT_PERM_HADAMARD))
+      return KVQ_ERR_UNSUPPORTED;
+    a.block_table = pg->block_table;
+    a.max_pages = pg->max_pages; a.n_pages = pg->n_pages; a.page_tokens = pg->page_tokens;
+  }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = (rot == KVQ_ROT_DENSE) ? kvq::launch_quantize_dense(a, s)
                                         : kvq::launch_quantize_rows(a, s);
@@ -179,7 +223,8 @@ kvq_status decode_impl(const void *q, kvq_dtype q_dtype, int64_t B, int64_t Hq,
                        const uint16_t *sink_k, const uint16_t *sink_v, int64_t n_sink,
                        const uint16_t *res_k, const uint16_t *res_v, int64_t n_res,
                        float softmax_scale, void *out, kvq_dtype out_dtype,
-                       void *workspace, size_t workspace_bytes_given, void *stream) {
+                       void *workspace, size_t workspace_bytes_given, void *stream,
+                       const Paging *pg = nullptr) {
   if (!valid_dtype(q_dtype) || !valid_dtype(out_dtype)) return KVQ_ERR_INVALID_ARG;
   if (q == nullptr || out == nullptr || !aligned16(q) || !aligned16(out)) return KVQ_ERR_INVALID_ARG;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return KVQ_ERR_INVALID_ARG;
@@ -220,6 +265,12 @@ kvq_status decode_impl(const void *q, kvq_dtype q_dtype, int64_t B, int64_t Hq,
   }
   a.kbits = n_int2 > 0 ? kc->bits : 2;
   a.vbits = n_int2 > 0 ? vc->bits : 2;
+  if (pg != nullptr && n_int2 > 0) {
+    // paged caches: rows per page instead of per (b, head)
+    a.block_table = pg->block_table;
+    a.max_pages = pg->max_pages; a.n_pages = pg->n_pages; a.page_tokens = pg->page_tokens;
+    a.kT_cap = a.vT_cap = pg->page_tokens;
+  }
   a.t_begin = t_begin;
   a.n_int2 = n_int2;
   a.t_ends = n_int2 > 0 ? t_ends : nullptr;
@@ -284,6 +335,42 @@ kvq_status kvq_decode_attention_varlen(const void *q, kvq_dtype q_dtype, int64_t
   return decode_impl(q, q_dtype, B, Hq, Hkv, d, k2.p, v2.p, t_begin, t_end_max, t_ends, rot, R, group,
                      sink_k, sink_v, n_sink, res_k, res_v, n_res, softmax_scale, out, out_dtype,
                      workspace, workspace_bytes_given, stream);
+}
+
+kvq_status kvq_quantize_paged(const void *K, const void *V, kvq_dtype in_dtype, int64_t B,
+                              int64_t T_new, int64_t Hkv, int64_t d, int64_t stride_b,
+                              int64_t stride_t, int64_t stride_h, kvq_rot rot, const void *R,
+                              int group, const int32_t *t_offsets, const int32_t *block_table,
+                              int64_t max_pages, const kvq_paged_cache *kc,
+                              const kvq_paged_cache *vc, void *stream) {
+  if (t_offsets == nullptr || ((uintptr_t)t_offsets & 3u) != 0) return KVQ_ERR_INVALID_ARG;
+  kvq_quant_cache kq{}, vq{};
+  Paging pg{};
+  const kvq_status st = check_paged(kc, vc, block_table, B, max_pages, kq, vq, pg);
+  if (st != KVQ_OK) return st;
+  return quantize_impl(K, V, in_dtype, B, T_new, Hkv, d, stride_b, stride_t, stride_h, rot, R,
+                       group, 0, t_offsets, kc ? &kq : nullptr, vc ? &vq : nullptr, stream, &pg);
+}
+
+kvq_status kvq_decode_attention_paged(const void *q, kvq_dtype q_dtype, int64_t B, int64_t Hq,
+                                      int64_t Hkv, int64_t d, const kvq_paged_cache *kc,
+                                      const kvq_paged_cache *vc, int64_t t_begin,
+                                      const int32_t *t_ends, int64_t t_end_max,
+                                      const int32_t *block_table, int64_t max_pages,
+                                      kvq_rot rot, const void *R, int group,
+                                      const uint16_t *sink_k, const uint16_t *sink_v, int64_t n_sink,
+                                      const uint16_t *res_k, const uint16_t *res_v, int64_t n_res,
+                                      float softmax_scale, void *out, kvq_dtype out_dtype,
+                                      void *workspace, size_t workspace_bytes_given, void *stream) {
+  if (t_ends == nullptr || ((uintptr_t)t_ends & 3u) != 0) return KVQ_ERR_INVALID_ARG;
+  if (kc == nullptr || vc == nullptr) return KVQ_ERR_INVALID_ARG;
+  kvq_quant_cache kq{}, vq{};
+  Paging pg{};
+  const kvq_status st = check_paged(kc, vc, block_table, B, max_pages, kq, vq, pg);
+  if (st != KVQ_OK) return st;
+  return decode_impl(q, q_dtype, B, Hq, Hkv, d, &kq, &vq, t_begin, t_end_max, t_ends, rot, R, group,
+                     sink_k, sink_v, n_sink, res_k, res_v, n_res, softmax_scale, out, out_dtype,
+                     workspace, workspace_bytes_given, stream, &pg);
 }
 
 const char *kvq_status_str(kvq_status s) {

@@ -480,10 +480,6 @@ __global__ __launch_bounds__(64 * WPB) void kv_int2_decode_attn(AttnArgs a) {
   // at *s + r*4 halves.  Lane offsets are 32-bit; tile bases are wave-uniform.
   const int64_t krow0 = bh * a.kT_cap + a.t_begin - a.skip;   // row 0 of the shifted grid
   const int64_t vrow0 = bh * a.vT_cap + a.t_begin - a.skip;
-  const uint8_t *kc = a.kcodes + krow0 * kCodeBytes;
-  const uint8_t *vc = a.vcodes + vrow0 * kCodeBytes;
-  const uint16_t *ks = a.kscales + krow0 * kNGroups, *kz = a.kzeros + krow0 * kNGroups;
-  const uint16_t *vs = a.vscales + vrow0 * kNGroups, *vz = a.vzeros + vrow0 * kNGroups;
 
   // Loads of one lane: codes at tile base + oc (+1 KB for token B), scales
   // and zeros at tile base + os halves (+64 halves for token B).  Tile bases
@@ -492,9 +488,10 @@ __global__ __launch_bounds__(64 * WPB) void kv_int2_decode_attn(AttnArgs a) {
   const uint32_t os = (uint32_t)(ts * kNGroups + 2 * h);
   auto load_tile = [&](int64_t first_row) {
     TileRegs r;
-    const uint8_t *kct = kc + first_row * kCodeBytes, *vct = vc + first_row * kCodeBytes;
-    const uint16_t *kst = ks + first_row * kNGroups, *kzt = kz + first_row * kNGroups;
-    const uint16_t *vst = vs + first_row * kNGroups, *vzt = vz + first_row * kNGroups;
+    const TileRows tr = tile_rows(a, b, hkv, krow0, vrow0, first_row);
+    const uint8_t *kct = a.kcodes + tr.k * kCodeBytes, *vct = a.vcodes + tr.v * kCodeBytes;
+    const uint16_t *kst = a.kscales + tr.k * kNGroups, *kzt = a.kzeros + tr.k * kNGroups;
+    const uint16_t *vst = a.vscales + tr.v * kNGroups, *vzt = a.vzeros + tr.v * kNGroups;
     r.kA = *reinterpret_cast<const u32x4_t *>(kct + oc);
     r.kB = *reinterpret_cast<const u32x4_t *>(kct + oc + 32 * kCodeBytes);
     r.vA = *reinterpret_cast<const u32x4_t *>(vct + oc);
@@ -534,7 +531,11 @@ __global__ __launch_bounds__(64 * WPB) void kv_int2_decode_attn(AttnArgs a) {
     const int64_t lo = a.skip > base ? a.skip - base : 0;
     const int64_t hi = ht.n_tok - base < 64 ? ht.n_tok - base : 64;
     const bool va = ts >= lo && ts < hi, vb = 32 + ts >= lo && 32 + ts < hi;
-    const int64_t ra = base + (va ? ts : lo), rb = base + (vb ? 32 + ts : lo);
+    const TileRows tr = tile_rows(a, b, hkv, krow0, vrow0, base);
+    const uint8_t *kc = a.kcodes + tr.k * kCodeBytes, *vc = a.vcodes + tr.v * kCodeBytes;
+    const uint16_t *ks = a.kscales + tr.k * kNGroups, *kz = a.kzeros + tr.k * kNGroups;
+    const uint16_t *vs = a.vscales + tr.v * kNGroups, *vz = a.vzeros + tr.v * kNGroups;
+    const int64_t ra = va ? ts : lo, rb = vb ? 32 + ts : lo;   // rows inside the tile
     TileRegs r;
     r.kA = *reinterpret_cast<const u32x4_t *>(kc + ra * kCodeBytes + 16 * h);
     r.kB = *reinterpret_cast<const u32x4_t *>(kc + rb * kCodeBytes + 16 * h);
@@ -864,7 +865,10 @@ static int64_t split_units(int64_t B, int64_t Hq, int64_t Hkv) {
 
 // Tile grid shift: start the grid t_begin mod 16 rows early when both caches
 // keep the rows of a head on 16-row boundaries.
+// A paged cache starts the grid on a 64-token boundary instead, so that no
+// tile crosses a page.
 static int grid_skip(const DecodeArgs &d) {
+  if (d.block_table != nullptr) return (int)(d.t_begin % 64);
   return (d.kT_cap % 16 == 0 && d.vT_cap % 16 == 0) ? (int)(d.t_begin % 16) : 0;
 }
 
@@ -911,6 +915,8 @@ hipError_t launch_decode(const DecodeArgs &d, hipStream_t stream) {
     a.partials = d.partials;
     a.fused_prep = fused_prep;
     a.skip = grid_skip(d);
+    a.block_table = d.block_table;
+    a.max_pages = d.max_pages; a.n_pages = d.n_pages; a.page_tokens = d.page_tokens;
     a.q = d.q; a.q_f32 = d.q_f32; a.rot = d.rot; a.perm = d.perm; a.qscale = d.qscale;
     if (generic) {
       hipError_t e = launch_attn_generic(a, d.kbits, d.vbits, stream);

@@ -30,7 +30,30 @@ struct AttnArgs {
   // Variable-length batch: sequence b's INT2 range ends at t_ends[b] (device
   // [B]; clamped to [t_begin, t_begin + n_int2]); NULL: every range is n_int2.
   const int32_t *t_ends;
+  // Paged cache: token t of sequence b is row t % page_tokens of page
+  // block_table[b * max_pages + t / page_tokens] ([n_pages][Hkv][page_tokens]
+  // rows per side); NULL: rows (b*Hkv + h)*T_cap + t.
+  const int32_t *block_table;
+  int64_t max_pages, n_pages, page_tokens;
 };
+
+// First K and V cache rows of the tile that starts at row r0 of a head's
+// shifted grid (row 0 = token t_begin - skip).  A paged cache's tiles start on
+// 64-token boundaries and pages hold a multiple of 64 tokens, so a tile never
+// crosses a page; an out-of-range page index reads page 0 (an unspecified
+// result, never an access outside the cache).
+struct TileRows {
+  int64_t k, v;
+};
+__device__ __forceinline__ TileRows tile_rows(const AttnArgs &a, int64_t b, int hkv, int64_t krow0,
+                                              int64_t vrow0, int64_t r0) {
+  if (a.block_table == nullptr) return TileRows{krow0 + r0, vrow0 + r0};
+  const int64_t t = a.t_begin - a.skip + r0;
+  int64_t page = a.block_table[b * a.max_pages + t / a.page_tokens];
+  page = (page >= 0 && page < a.n_pages) ? page : 0;
+  const int64_t row = (page * a.Hkv + hkv) * a.page_tokens + t % a.page_tokens;
+  return TileRows{row, row};
+}
 
 // INT2 tokens of sequence b.
 __device__ __forceinline__ int64_t seq_int2(const AttnArgs &a, int64_t b) {

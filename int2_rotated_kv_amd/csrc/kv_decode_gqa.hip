@@ -234,10 +234,6 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
 
   const int64_t krow0 = bh * a.kT_cap + a.t_begin - a.skip;   // row 0 of the shifted grid
   const int64_t vrow0 = bh * a.vT_cap + a.t_begin - a.skip;
-  const uint8_t *kc = a.kcodes + krow0 * kCodeBytes;
-  const uint8_t *vc = a.vcodes + vrow0 * kCodeBytes;
-  const uint16_t *ks = a.kscales + krow0 * kNGroups, *kz = a.kzeros + krow0 * kNGroups;
-  const uint16_t *vs = a.vscales + vrow0 * kNGroups, *vz = a.vzeros + vrow0 * kNGroups;
   const int tk = lane & 15, kgrp = lane >> 4;      // K side
 
   // Full tile at row r0 (relative to the head's INT2 start): wave-uniform
@@ -247,20 +243,26 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
   const uint32_t o_vc = (uint32_t)(16 * lane);
   auto load_full = [&](int64_t r0) {
     MqTile t;
-    const uint8_t *kct = kc + r0 * kCodeBytes, *vct = vc + r0 * kCodeBytes;
+    const TileRows tr = tile_rows(a, b, hkv, krow0, vrow0, r0);
+    const uint8_t *kct = a.kcodes + tr.k * kCodeBytes, *vct = a.vcodes + tr.v * kCodeBytes;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       t.kc[k] = *reinterpret_cast<const u32x2_t *>(kct + o_kc + 16 * k * kCodeBytes);
-    t.ks = *reinterpret_cast<const u32x2_t *>(ks + r0 * kNGroups + o_sz);
-    t.kz = *reinterpret_cast<const u32x2_t *>(kz + r0 * kNGroups + o_sz);
-    t.vs = *reinterpret_cast<const u32x2_t *>(vs + r0 * kNGroups + o_sz);
-    t.vz = *reinterpret_cast<const u32x2_t *>(vz + r0 * kNGroups + o_sz);
+    t.ks = *reinterpret_cast<const u32x2_t *>(a.kscales + tr.k * kNGroups + o_sz);
+    t.kz = *reinterpret_cast<const u32x2_t *>(a.kzeros + tr.k * kNGroups + o_sz);
+    t.vs = *reinterpret_cast<const u32x2_t *>(a.vscales + tr.v * kNGroups + o_sz);
+    t.vz = *reinterpret_cast<const u32x2_t *>(a.vzeros + tr.v * kNGroups + o_sz);
     t.vc[0] = *reinterpret_cast<const u32x4_t *>(vct + o_vc);
     t.vc[1] = *reinterpret_cast<const u32x4_t *>(vct + 1024 + o_vc);
     return t;
   };
-  // Any tile: rows clamped into [rmin, rmax] (a partial tile).
+  // Any tile: rows clamped into [rmin, rmax] (a partial tile), then taken
+  // relative to the tile's first cache row.
   auto load_tile = [&](int64_t r0, int64_t rmin, int64_t rmax) {
+    const TileRows tr = tile_rows(a, b, hkv, krow0, vrow0, r0);
+    const uint8_t *kc = a.kcodes + (tr.k - r0) * kCodeBytes, *vc = a.vcodes + (tr.v - r0) * kCodeBytes;
+    const uint16_t *ks = a.kscales + (tr.k - r0) * kNGroups, *kz = a.kzeros + (tr.k - r0) * kNGroups;
+    const uint16_t *vs = a.vscales + (tr.v - r0) * kNGroups, *vz = a.vzeros + (tr.v - r0) * kNGroups;
     auto clampr = [&](int64_t r) { return r < rmax ? (r > rmin ? r : rmin) : rmax; };
     MqTile t;
 #pragma unroll

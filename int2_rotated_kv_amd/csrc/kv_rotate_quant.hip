@@ -292,6 +292,10 @@ struct RowsKernelArgs {
   int n_sides;
   const int32_t *perm;   // permuted Hadamard: [Hkv][128] channel order, else unused
   const int32_t *offsets;   // per-sequence first slot (device [B]) or NULL: t_offset
+  // paged cache: slot t of sequence b is row t % page_tokens of page
+  // block_table[b * max_pages + t / page_tokens]; NULL: row (b*Hkv + h)*T_cap + t
+  const int32_t *block_table;
+  int64_t max_pages, n_pages, page_tokens;
 };
 
 // grid: x = token blocks of 64, y = KV head, z = batch * n_sides + side
@@ -460,8 +464,15 @@ __device__ __forceinline__ void fwht_f16_body(const RowsKernelArgs &a) {
   // tokens [lo, hi) of the tile are written: at or after token 0 and slot 0
   const int64_t lo = (slot0 < 0 ? -slot0 : 0) > -t0 ? (slot0 < 0 ? -slot0 : 0) : -t0;
   const int64_t hi = s.T_cap - slot0 < n_valid ? s.T_cap - slot0 : n_valid;
-  // first cache row of (token 0 of the tile, head h0 + g)
-  auto row_of = [&](int g) { return (b * a.Hkv + h0 + g) * s.T_cap + slot0; };
+  // cache row of token tk of the tile, head h0 + g; -1 when a paged slot's
+  // page index is outside the cache (the row is not written)
+  auto row_of = [&](int g, int64_t tk) -> int64_t {
+    const int64_t slot = slot0 + tk;
+    if (a.block_table == nullptr) return (b * a.Hkv + h0 + g) * s.T_cap + slot;
+    const int64_t page = a.block_table[b * a.max_pages + slot / a.page_tokens];
+    if (page < 0 || page >= a.n_pages) return -1;
+    return (page * a.Hkv + h0 + g) * a.page_tokens + slot % a.page_tokens;
+  };
 
   // lane (n, q): stage row r(g) = 16g + n for HG = 1, 4n + g for HG = 4
   auto srow = [&](int g) { return HG == 1 ? 16 * g + n : 4 * n + g; };
@@ -532,12 +543,15 @@ __device__ __forceinline__ void fwht_f16_body(const RowsKernelArgs &a) {
     for (int kk = 0; kk < BITS; ++kk) {
       const int c = 64 * kk + lane;                  // 16-byte chunk c % BITS of stage row c / BITS
       const int r = c / BITS, tk = r / HG;
-      if (tk >= lo && tk < hi)
-        __builtin_nontemporal_store(rows[c], reinterpret_cast<u32x4_t *>(s.codes + (row_of(r % HG) + tk) * row_bytes) + c % BITS);
+      if (tk >= lo && tk < hi) {
+        const int64_t row = row_of(r % HG, tk);
+        if (row >= 0)
+          __builtin_nontemporal_store(rows[c], reinterpret_cast<u32x4_t *>(s.codes + row * row_bytes) + c % BITS);
+      }
     }
     const int tk = lane / HG;
-    if (tk >= lo && tk < hi) {
-      const int64_t row = row_of(lane % HG) + tk;
+    const int64_t row = (tk >= lo && tk < hi) ? row_of(lane % HG, tk) : -1;
+    if (row >= 0) {
       const u32x4_t e = *reinterpret_cast<const u32x4_t *>(&stage[kSzOff + lane * 4]);
       const u32x2_t sv = {__builtin_amdgcn_perm(e.y, e.x, 0x05040100u), __builtin_amdgcn_perm(e.w, e.z, 0x05040100u)};
       const u32x2_t zv = {__builtin_amdgcn_perm(e.y, e.x, 0x07060302u), __builtin_amdgcn_perm(e.w, e.z, 0x07060302u)};
@@ -613,6 +627,10 @@ hipError_t launch_quantize_rows(const QuantArgs &q, hipStream_t stream) {
   a.Hkv = (int)q.Hkv;
   a.n_sides = q.n_sides;
   a.perm = q.perm;
+  a.block_table = q.block_table;
+  a.max_pages = q.max_pages;
+  a.n_pages = q.n_pages;
+  a.page_tokens = q.page_tokens;
   const int64_t n_tb = (q.T_new + 63) / 64;
   const int kbits = q.side[0].bits, vbits = q.n_sides > 1 ? q.side[1].bits : kbits;
   if (kbits != 2 || vbits != 2) {

@@ -29,6 +29,10 @@ struct QuantArgs {
   int rot;              // 0 none, 1 Hadamard, 2 dense, 3 permuted Hadamard
   const float *R;       // dense: [Hkv][128][128]
   const int32_t *perm;  // permuted Hadamard: [Hkv][128]
+  // paged cache (rows kernels for fp16 + Hadamard only): side T_cap is then
+  // max_pages * page_tokens, the logical capacity of a sequence
+  const int32_t *block_table;
+  int64_t max_pages, n_pages, page_tokens;
 };
 
 hipError_t launch_quantize_rows(const QuantArgs &a, hipStream_t stream);
@@ -45,6 +49,10 @@ struct DecodeArgs {
   int64_t t_begin, n_int2;
   const int32_t *t_ends;   // variable-length batch: per-sequence end (device [B]) or NULL
   int rot; const float *R; const int32_t *perm;
+  // paged cache: [n_pages][Hkv][page_tokens] rows per side, block_table
+  // [B][max_pages] (device); NULL: contiguous [B][Hkv][T_cap]
+  const int32_t *block_table;
+  int64_t max_pages, n_pages, page_tokens;
   const uint16_t *sink_k, *sink_v; int64_t n_sink;
   const uint16_t *res_k, *res_v; int64_t n_res;
   float qscale;         // softmax_scale * log2(e)

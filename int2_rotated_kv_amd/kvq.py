@@ -26,10 +26,10 @@ KVQ_ROT_NONE, KVQ_ROT_HADAMARD, KVQ_ROT_DENSE, KVQ_ROT_PERM_HADAMARD = 0, 1, 2, 
 _ROT = {"none": KVQ_ROT_NONE, "hadamard": KVQ_ROT_HADAMARD, "dense": KVQ_ROT_DENSE,
         "perm": KVQ_ROT_PERM_HADAMARD}
 
-EXPORTED_SYMBOLS = ("kvq_quantize", "kvq_quantize_at", "kvq_quantize_bits",
+EXPORTED_SYMBOLS = ("kvq_quantize", "kvq_quantize_at", "kvq_quantize_bits", "kvq_quantize_paged",
                     "kvq_decode_workspace_bytes", "kvq_decode_attention",
-                    "kvq_decode_attention_varlen", "kvq_decode_attention_bits", "kvq_status_str",
-                    "kvq_abi_version")
+                    "kvq_decode_attention_varlen", "kvq_decode_attention_bits",
+                    "kvq_decode_attention_paged", "kvq_status_str", "kvq_abi_version")
 
 D_HEAD = 128
 GROUP = 32
@@ -44,6 +44,12 @@ class KvqError(RuntimeError):
 class kvq_int2_cache(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("zeros", ctypes.c_void_p), ("T_cap", ctypes.c_int64)]
+
+
+class kvq_paged_cache(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("zeros", ctypes.c_void_p), ("n_pages", ctypes.c_int64),
+                ("page_tokens", ctypes.c_int64)]
 
 
 class kvq_quant_cache(ctypes.Structure):
@@ -93,6 +99,14 @@ def load_library() -> ctypes.CDLL:
     lib.kvq_decode_attention_bits.argtypes = [vp, i32, i64, i64, i64, i64, qp, qp, i64, i64,
                                               i32, vp, i32, vp, vp, i64, vp, vp, i64, f32,
                                               vp, i32, vp, ctypes.c_size_t, vp]
+    pp = ctypes.POINTER(kvq_paged_cache)
+    lib.kvq_quantize_paged.restype = i32
+    lib.kvq_quantize_paged.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, i64, i64,
+                                       i32, vp, i32, vp, vp, i64, pp, pp, vp]
+    lib.kvq_decode_attention_paged.restype = i32
+    lib.kvq_decode_attention_paged.argtypes = [vp, i32, i64, i64, i64, i64, pp, pp, i64, vp, i64,
+                                               vp, i64, i32, vp, i32, vp, vp, i64, vp, vp, i64, f32,
+                                               vp, i32, vp, ctypes.c_size_t, vp]
     lib.kvq_status_str.restype = ctypes.c_char_p
     lib.kvq_status_str.argtypes = [i32]
     lib.kvq_abi_version.restype = i32
@@ -299,3 +313,90 @@ def kvq_decode_attention(q: torch.Tensor, cache_k: Int2Cache | None,
 
 def default_softmax_scale(d: int = D_HEAD) -> float:
     return 1.0 / math.sqrt(d)
+
+
+class PagedCache:
+    """Device buffers of one side (K or V) of a paged INT2 cache:
+    codes uint8 [n_pages, Hkv, page_tokens, d/4]; scales / zeros fp16
+    [n_pages, Hkv, page_tokens, d/32].  A block table int32 [B, max_pages]
+    maps sequence b's token t to row t % page_tokens of page table[b, t // page_tokens]."""
+
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor):
+        self.codes, self.scales, self.zeros = codes, scales, zeros
+        self.n_pages, self.page_tokens = codes.shape[0], codes.shape[2]
+
+    @classmethod
+    def empty(cls, n_pages: int, Hkv: int, page_tokens: int, device="cuda", d: int = D_HEAD):
+        codes = torch.empty((n_pages, Hkv, page_tokens, d // 4), dtype=torch.uint8, device=device)
+        scales = torch.empty((n_pages, Hkv, page_tokens, d // GROUP), dtype=torch.float16, device=device)
+        zeros = torch.empty((n_pages, Hkv, page_tokens, d // GROUP), dtype=torch.float16, device=device)
+        return cls(codes, scales, zeros)
+
+    def c_struct(self) -> kvq_paged_cache:
+        return kvq_paged_cache(self.codes.data_ptr(), self.scales.data_ptr(), self.zeros.data_ptr(),
+                               self.n_pages, self.page_tokens)
+
+
+def _table(block_table, B):
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B \
+            or not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous int32 [B, max_pages]")
+    return block_table.shape[1]
+
+
+def kvq_quantize_paged(K, V, cache_k: PagedCache | None, cache_v: PagedCache | None,
+                       t_offsets: torch.Tensor, block_table: torch.Tensor,
+                       rot: str = "hadamard", R: torch.Tensor | None = None,
+                       group: int = GROUP, stream=None):
+    """Rotate, quantize and pack K/V rows [B, T_new, Hkv, d] of fp16 into a
+    paged cache: sequence b's rows are its tokens t_offsets[b] + i, placed
+    through block_table [B, max_pages] (kvq_quantize_paged)."""
+    x = K if K is not None else V
+    B, T_new, Hkv, d = x.shape
+    if t_offsets.dtype != torch.int32 or t_offsets.numel() != B:
+        raise ValueError("t_offsets must be int32 [B]")
+    max_pages = _table(block_table, B)
+    kc = cache_k.c_struct() if cache_k is not None else None
+    vc = cache_v.c_struct() if cache_v is not None else None
+    st = load_library().kvq_quantize_paged(
+        _ptr(K), _ptr(V), _dtype_code(x), B, T_new, Hkv, d,
+        x.stride(0), x.stride(1), x.stride(2), _ROT[rot], _ptr(R), group, _ptr(t_offsets),
+        _ptr(block_table), max_pages,
+        ctypes.byref(kc) if kc is not None else None,
+        ctypes.byref(vc) if vc is not None else None, _stream(stream))
+    _check(st, "kvq_quantize_paged")
+
+
+def kvq_decode_attention_paged(q: torch.Tensor, cache_k: PagedCache, cache_v: PagedCache,
+                               t_begin: int, t_ends: torch.Tensor, t_end_max: int,
+                               block_table: torch.Tensor, rot: str = "hadamard",
+                               R: torch.Tensor | None = None, group: int = GROUP,
+                               sink_k=None, sink_v=None, res_k=None, res_v=None,
+                               softmax_scale: float = 0.0, out: torch.Tensor | None = None,
+                               workspace: torch.Tensor | None = None, stream=None):
+    """Decode attention for q [B, Hq, d] over a paged cache: sequence b
+    attends to its tokens [t_begin, t_ends[b]) (kvq_decode_attention_paged)."""
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous [B, Hq, d]")
+    B, Hq, d = q.shape
+    Hkv = cache_k.codes.shape[1]
+    if t_ends.dtype != torch.int32 or t_ends.numel() != B:
+        raise ValueError("t_ends must be int32 [B]")
+    max_pages = _table(block_table, B)
+    n_sink = 0 if sink_k is None else sink_k.shape[2]
+    n_res = 0 if res_k is None else res_k.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    need = kvq_decode_workspace_bytes(B, Hq, Hkv, d, t_end_max - t_begin, n_sink, n_res)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    kc, vc = cache_k.c_struct(), cache_v.c_struct()
+    st = load_library().kvq_decode_attention_paged(
+        _ptr(q), _dtype_code(q), B, Hq, Hkv, d, ctypes.byref(kc), ctypes.byref(vc),
+        t_begin, _ptr(t_ends), t_end_max, _ptr(block_table), max_pages,
+        _ROT[rot], _ptr(R), group,
+        _ptr(sink_k), _ptr(sink_v), n_sink, _ptr(res_k), _ptr(res_v), n_res,
+        float(softmax_scale), _ptr(out), _dtype_code(out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "kvq_decode_attention_paged")
+    return out

@@ -238,3 +238,35 @@ def test_decode_bits_rejects(lib):
     assert call(4, 0) == K.KVQ_ERR_INVALID_ARG
     assert call(4, 2, rot=K.KVQ_ROT_DENSE, R=FAKE) == K.KVQ_ERR_UNSUPPORTED   # no dense R at 4 bits
     assert call(1, 4, wsb=100) == K.KVQ_ERR_WORKSPACE_TOO_SMALL
+
+
+def _pcache(n_pages=4, page_tokens=128):
+    return K.kvq_paged_cache(FAKE, FAKE, FAKE, n_pages, page_tokens)
+
+
+def test_paged_rejects(lib):
+    """Paged caches: pages of a multiple of 64 tokens, both sides alike, a
+    4-byte aligned table; the write needs fp16 rows and a Hadamard rotation."""
+    def dec(kc=None, vc=None, table=FAKE, maxp=4, te_max=512, tends=FAKE, wsb=1 << 30):
+        kc = kc or _pcache()
+        vc = vc or _pcache()
+        return lib.kvq_decode_attention_paged(
+            FAKE, K.KVQ_F16, 2, 4, 2, 128, ctypes.byref(kc), ctypes.byref(vc), 0, tends, te_max,
+            table, maxp, K.KVQ_ROT_HADAMARD, None, 32, None, None, 0, None, None, 0, 0.0,
+            FAKE, K.KVQ_F16, FAKE * 16, wsb, None)
+    assert dec(kc=_pcache(page_tokens=96), vc=_pcache(page_tokens=96)) == K.KVQ_ERR_INVALID_ARG
+    assert dec(vc=_pcache(n_pages=5)) == K.KVQ_ERR_INVALID_ARG          # sides differ
+    assert dec(table=None) == K.KVQ_ERR_INVALID_ARG
+    assert dec(table=FAKE + 2) == K.KVQ_ERR_INVALID_ARG
+    assert dec(tends=None) == K.KVQ_ERR_INVALID_ARG
+    assert dec(te_max=513) == K.KVQ_ERR_INVALID_ARG                      # beyond 4 pages x 128
+    assert dec(wsb=100) == K.KVQ_ERR_WORKSPACE_TOO_SMALL
+
+    def quant(dt=K.KVQ_F16, rot=K.KVQ_ROT_HADAMARD, offs=FAKE, R=None):
+        return lib.kvq_quantize_paged(FAKE, FAKE, dt, 1, 8, 2, 128, 8 * 2 * 128, 2 * 128, 128,
+                                      rot, R, 32, offs, FAKE, 4, ctypes.byref(_pcache()),
+                                      ctypes.byref(_pcache()), None)
+    assert quant(offs=None) == K.KVQ_ERR_INVALID_ARG
+    assert quant(dt=K.KVQ_F32) == K.KVQ_ERR_UNSUPPORTED
+    assert quant(rot=K.KVQ_ROT_NONE) == K.KVQ_ERR_UNSUPPORTED
+    assert quant(rot=K.KVQ_ROT_DENSE, R=FAKE) == K.KVQ_ERR_UNSUPPORTED

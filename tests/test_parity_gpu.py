@@ -499,6 +499,121 @@ def test_decode_varlen(cid, Hkv, Hq, rot):
         assert err <= ATTN_TOL
 
 
+# ------------------------------------------------------------- paged caches
+def _page_layout(rng, B, T_cap, P, spare=3):
+    """A block table [B, T_cap/P] over a shuffled pool of pages (plus a few
+    unused ones), and the pool size."""
+    per = T_cap // P
+    n_pages = B * per + spare
+    pool = rng.permutation(n_pages)[:B * per]
+    return pool.reshape(B, per).astype(np.int32), n_pages
+
+
+def _to_pages(cache, table, n_pages, P):
+    """Contiguous (codes, scales, zeros) [B, H, T, ...] -> paged arrays
+    [n_pages, H, P, ...] (unused pages hold the sentinel)."""
+    out = []
+    for arr in cache:
+        B, H, T = arr.shape[:3]
+        pg = np.zeros((n_pages, H, P) + arr.shape[3:], arr.dtype)
+        for b in range(B):
+            for j in range(T // P):
+                pg[table[b, j]] = arr[b, :, j * P:(j + 1) * P]
+        out.append(pg)
+    return out
+
+
+@pytest.mark.parametrize("cid,Hkv,Hq,rot,P,tb", [(2, 2, 2, "hadamard", 128, 5), (4, 2, 8, "dense", 64, 0),
+                                                 (5, 2, 2, "hadamard", 192, 4), (2, 3, 3, "perm", 64, 70)])
+def test_decode_paged(cid, Hkv, Hq, rot, P, tb):
+    """Paged decode (block table over a shuffled page pool, per-sequence
+    ends): each sequence against the oracle on the same rows, and against
+    the contiguous variable-length call over the same bytes."""
+    T = 768
+    extra = dict(t_new=0) if cid == 4 else {}
+    cfg = W.small_config(W.config(cid), T=T, B=3, Hkv=Hkv, Hq=Hq, **extra)
+    rng = np.random.default_rng(100 + cid)
+    R = W.dense_rotations(cfg) if rot == "dense" else (W.channel_orders(cfg) if rot == "perm" else None)
+    Rm = rot_matrix(rot, R)
+    K = W.kv_tokens(cfg, "K")
+    V = W.kv_tokens(cfg, "V")
+    kh = K.permute(0, 2, 1, 3).contiguous().numpy()
+    vh = V.permute(0, 2, 1, 3).contiguous().numpy()
+    kcache = O.quantize_cache(kh, Rm)
+    vcache = O.quantize_cache(vh, Rm)
+    table, n_pages = _page_layout(rng, cfg.B, T, P)
+    te_max = T - cfg.n_res
+    tb = cfg.n_sink if cfg.n_sink else tb
+    ends = np.array([te_max, tb + 1 + int(rng.integers(0, te_max - tb - 1)), tb + 64 + 3], np.int32)
+    fp16 = {}
+    if cfg.n_sink or cfg.n_res:
+        fp16 = dict(sink_k=np.ascontiguousarray(kh[:, :, :cfg.n_sink]).astype(np.float16),
+                    sink_v=np.ascontiguousarray(vh[:, :, :cfg.n_sink]).astype(np.float16),
+                    res_k=np.ascontiguousarray(kh[:, :, T - cfg.n_res:]).astype(np.float16),
+                    res_v=np.ascontiguousarray(vh[:, :, T - cfg.n_res:]).astype(np.float16))
+    up = {k: torch.from_numpy(v).to(DEV) for k, v in fp16.items()}
+    kp = kvq.PagedCache(*[torch.from_numpy(a).to(DEV) for a in _to_pages(kcache, table, n_pages, P)])
+    vp = kvq.PagedCache(*[torch.from_numpy(a).to(DEV) for a in _to_pages(vcache, table, n_pages, P)])
+    q = W.queries(cfg)
+    tends = torch.from_numpy(ends).to(DEV)
+    out = kvq.kvq_decode_attention_paged(q.to(DEV), kp, vp, tb, tends, te_max,
+                                         torch.from_numpy(table).to(DEV), rot=rot, R=_rot_arg(rot, R), **up)
+    flat = kvq.kvq_decode_attention(q.to(DEV), cache_from_numpy(*kcache), cache_from_numpy(*vcache),
+                                    tb, te_max, rot=rot, R=_rot_arg(rot, R), t_ends=tends, **up)
+    torch.cuda.synchronize()
+    out, flat = out.float().cpu().numpy(), flat.float().cpu().numpy()
+    worst = 0.0
+    for b in range(cfg.B):
+        sl = lambda c: tuple(a[b:b + 1] for a in c)
+        kwb = {k: v[b:b + 1] for k, v in fp16.items()}
+        ref = O.decode_attention(q.numpy()[b:b + 1], sl(kcache), sl(vcache), tb, int(ends[b]), Rm, **kwb)
+        worst = max(worst, normwise_rel_err(out[b:b + 1], ref))
+    err_flat = normwise_rel_err(out, flat)
+    _report(f"decode paged {rot} c{cid} P={P} tb={tb}", normwise=worst, vs_contiguous=err_flat)
+    assert worst <= ATTN_TOL and err_flat <= 1e-3
+
+
+@pytest.mark.parametrize("rot,Hkv,P", [("hadamard", 4, 128), ("perm", 3, 64)])
+def test_quantize_paged(rot, Hkv, P):
+    """Paged decode-step appends and prefills: sequence b's rows at its own
+    offset through the block table; pages not addressed keep their sentinel
+    bytes, a table entry outside the pool drops its rows, and the written
+    rows gathered back match the contiguous per-sequence write."""
+    cfg = W.small_config(W.config(2), B=3, T=150, Hkv=Hkv, Hq=Hkv)
+    perm = W.channel_orders(cfg) if rot == "perm" else None
+    rng = np.random.default_rng(7)
+    T_cap = 4 * P
+    table, n_pages = _page_layout(rng, cfg.B, T_cap, P)
+    table[2, 1] = n_pages + 5                       # out of the pool: those rows are dropped
+    offs = np.array([0, 37, P - 20], np.int32)      # the last crosses into page 1
+    K = W.kv_tokens(cfg, "K")
+    kp = kvq.PagedCache.empty(n_pages, Hkv, P)
+    for t in (kp.codes, kp.scales.view(torch.uint8), kp.zeros.view(torch.uint8)):
+        t.fill_(SENTINEL)
+    Rg = _rot_arg(rot, perm)
+    kvq.kvq_quantize_paged(K.to(DEV), None, kp, None, torch.from_numpy(offs).to(DEV),
+                           torch.from_numpy(table).to(DEV), rot=rot, R=Rg)
+    flat = empty_cache(cfg.B, Hkv, T_cap)
+    kvq.kvq_quantize(K.to(DEV), None, flat, None, rot=rot, R=Rg, t_offsets=torch.from_numpy(offs).to(DEV))
+    torch.cuda.synchronize()
+    pc = cache_to_numpy(kp)
+    fc = cache_to_numpy(flat)
+    written = np.zeros((n_pages, P), bool)
+    for b in range(cfg.B):
+        for t in range(cfg.T):
+            slot = int(offs[b]) + t
+            page = int(table[b, slot // P])
+            if page >= n_pages:
+                continue
+            written[page, slot % P] = True
+            for a_p, a_f in zip(pc, fc):
+                assert np.array_equal(a_p[page, :, slot % P].view(np.uint8), a_f[b, :, slot].view(np.uint8))
+    for a_p in pc:                                   # nothing else was touched
+        assert np.all(np.moveaxis(a_p.view(np.uint8), 1, 2)[~written] == SENTINEL)
+    _report(f"quantize paged {rot} P={P}", rows=int(written.sum()))
+    assert written.sum() < cfg.B * cfg.T             # the dropped page's rows are missing
+
+
 # ------------------------------------------------ other code widths (1, 4 bits)
 @pytest.mark.parametrize("kbits,vbits,rot", [(4, 2, "hadamard"), (1, 4, "hadamard"), (4, 4, "perm"),
                                              (1, 1, "perm")])
