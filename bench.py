@@ -62,6 +62,9 @@ def parse():
                    help="serving form: per-sequence lengths drawn in [T/2, T] (seeded); the decode "
                         "is kvq_decode_attention_varlen and the write phase a decode-step append "
                         "of one row per sequence (kvq_quantize_at)")
+    p.add_argument("--paged", type=int, default=0, metavar="P",
+                   help="keep the cache in pages of P tokens (a multiple of 64) behind a shuffled "
+                        "block table (kvq_quantize_paged / kvq_decode_attention_paged)")
     p.add_argument("--kbits", type=int, default=2, choices=(1, 2, 4),
                    help="key code width (1 and 4: the b-bit write and decode kernels)")
     p.add_argument("--vbits", type=int, default=2, choices=(1, 2, 4), help="value code width")
@@ -163,6 +166,11 @@ def main():
             sys.exit("--kbits/--vbits other than 2 need a Hadamard workload (--config 3 or 5) "
                      "without --varlen")
         workload += f"_k{kbits}v{vbits}"
+    P = args.paged
+    if P:
+        if P % 64 or rot == "dense" or (kbits, vbits) != (2, 2):
+            sys.exit("--paged P needs P a multiple of 64, a Hadamard workload and 2-bit codes")
+        workload += f"_paged{P}"
     print(f"[bench] generating {workload} on the GPU", file=sys.stderr, flush=True)
     t0 = time.time()
     K = W.kv_tokens(cfg, "K", device=dev)
@@ -173,9 +181,27 @@ def main():
         R = torch.as_tensor(W.dense_rotations(cfg), device=dev).contiguous()
     elif rot == "perm":
         R = torch.as_tensor(W.channel_orders(cfg), dtype=torch.int32, device=dev).contiguous()
-    ck = kvq.Int2Cache.empty(B, H, T, device=dev, bits=kbits)
-    cv = kvq.Int2Cache.empty(B, H, T, device=dev, bits=vbits)
     tb, te = cfg.int2_range                    # INT2 tokens of the cache
+    if P:
+        # every sequence's pages drawn from one shuffled pool (seeded)
+        per = (T + P - 1) // P
+        pool = np.random.default_rng(np.random.SeedSequence([2000 + cfg.cid, P])).permutation(B * per)
+        table = torch.from_numpy(pool.reshape(B, per).astype(np.int32)).to(dev)
+        ck = kvq.PagedCache.empty(B * per, H, P, device=dev)
+        cv = kvq.PagedCache.empty(B * per, H, P, device=dev)
+    else:
+        ck = kvq.Int2Cache.empty(B, H, T, device=dev, bits=kbits)
+        cv = kvq.Int2Cache.empty(B, H, T, device=dev, bits=vbits)
+
+    def write(Kx, Vx, first=None, offsets=None):
+        """Rows of every sequence from token `first`, or from offsets[b]."""
+        if P:
+            offs = offsets if offsets is not None else torch.full((B,), first, dtype=torch.int32, device=dev)
+            kvq.kvq_quantize_paged(Kx, Vx, ck, cv, offs, table, rot=rot, R=R)
+        elif offsets is not None:
+            kvq.kvq_quantize(Kx, Vx, ck, cv, rot=rot, R=R, t_offsets=offsets)
+        else:
+            kvq.kvq_quantize(Kx, Vx, ck, cv, rot=rot, R=R, t_offset=first)
     q0, q1 = cfg.quant_range                   # tokens written by the timed quantize call
     fp16 = {}
     if cfg.n_sink or cfg.n_res:                # fp16 segments, [B, Hkv, n, d]
@@ -188,12 +214,15 @@ def main():
     out = torch.empty_like(q)
     Kq, Vq = K[:, q0:q1], V[:, q0:q1]
     if q0 > tb:                                # rest of the INT2 range, written once (untimed)
-        kvq.kvq_quantize(K[:, tb:q0], V[:, tb:q0], ck, cv, rot=rot, R=R, t_offset=tb)
+        write(K[:, tb:q0], V[:, tb:q0], first=tb)
     ends = None
+    if P and not args.varlen:                  # the paged decode takes per-sequence ends
+        ends_h = np.full(B, te, np.int32)
+        ends = torch.from_numpy(ends_h).to(dev)
     if args.varlen:
         # the whole INT2 range is written once (untimed); sequence b then holds
         # INT2 tokens [tb, ends[b]), and a decode step appends one row at its end
-        kvq.kvq_quantize(K[:, q0:q1], V[:, q0:q1], ck, cv, rot=rot, R=R, t_offset=q0)
+        write(K[:, q0:q1], V[:, q0:q1], first=q0)
         rng = np.random.default_rng(np.random.SeedSequence([1000 + cfg.cid, 77]))
         n_full = te - tb
         ends_h = (tb + rng.integers(n_full // 2, n_full + 1, size=B)).astype(np.int32)
@@ -206,14 +235,18 @@ def main():
     stream = torch.cuda.current_stream()
 
     def quant():
-        if ends is None:
-            kvq.kvq_quantize(Kq, Vq, ck, cv, rot=rot, R=R, t_offset=q0)
+        if args.varlen:
+            write(Kq, Vq, offsets=slots)
         else:
-            kvq.kvq_quantize(Kq, Vq, ck, cv, rot=rot, R=R, t_offsets=slots)
+            write(Kq, Vq, first=q0)
 
     def decode():
-        kvq.kvq_decode_attention(q, ck, cv, tb, te, rot=rot, R=R, out=out, workspace=ws,
-                                 t_ends=ends, **fp16)
+        if P:
+            kvq.kvq_decode_attention_paged(q, ck, cv, tb, ends, te, table, rot=rot, R=R, out=out,
+                                           workspace=ws, **fp16)
+        else:
+            kvq.kvq_decode_attention(q, ck, cv, tb, te, rot=rot, R=R, out=out, workspace=ws,
+                                     t_ends=ends, **fp16)
 
     for _ in range(args.warmup):
         quant()
@@ -265,10 +298,10 @@ def main():
     dec_ms = np.array([a.elapsed_time(b) for a, b in d_evs])
     ms_per_step = float(quant_ms.sum() + dec_ms.sum()) / args.steps   # the timed calls, flushes excluded
 
-    n_q = 1 if ends is not None else q1 - q0
+    n_q = 1 if args.varlen else q1 - q0
     n_f16 = cfg.n_sink + cfg.n_res
     # INT2 (token, head) units the decode reads: every sequence's own range
-    int2_tokens = int((ends_h - tb).sum()) if ends is not None else B * (te - tb)
+    int2_tokens = int((ends_h - tb).sum()) if args.varlen else B * (te - tb)
     r_bytes = {"dense": H * d * d * 4, "perm": H * d * 4}.get(rot, 0)   # R / channel orders, read once
     q_unit = 2 * 256 + row_bytes(kbits) + row_bytes(vbits)     # QUANT_BYTES_PER_TOKEN_HEAD at 2/2
     d_unit = row_bytes(kbits) + row_bytes(vbits)               # DECODE_BYTES_PER_TOKEN_HEAD at 2/2
@@ -322,11 +355,12 @@ def main():
                    "cache": ("int2 codes + f16 scale/zero, group 32" if (kbits, vbits) == (2, 2) else
                              f"{kbits}-bit key / {vbits}-bit value codes + f16 scale/zero, group 32"),
                    "rotation": rot, "int2_tokens": [tb, te],
-                   "quantize_tokens": ("one appended row per sequence, at its own end" if ends is not None
+                   "quantize_tokens": ("one appended row per sequence, at its own end" if args.varlen
                                        else [q0, q1]),
                    "fp16_tokens": n_f16,
                    **({"int2_ends": {"min": int(ends_h.min()), "max": int(ends_h.max()),
-                                     "mean": round(float(ends_h.mean()), 1)}} if ends is not None else {})},
+                                     "mean": round(float(ends_h.mean()), 1)}} if args.varlen else {}),
+                   **({"page_tokens": P, "pages": int(ck.n_pages)} if P else {})},
         "decode_pct_of_peak": round(100 * dec_gbs / PEAK_HBM_GBS, 2),
         "decode_ms": round(d_ms, 4), "quantize_ms": round(q_ms, 4),
         "quantize_tokens_per_s": round(q_tok_s, 1),
