@@ -464,12 +464,20 @@ __device__ __forceinline__ void fwht_f16_body(const RowsKernelArgs &a) {
   // tokens [lo, hi) of the tile are written: at or after token 0 and slot 0
   const int64_t lo = (slot0 < 0 ? -slot0 : 0) > -t0 ? (slot0 < 0 ? -slot0 : 0) : -t0;
   const int64_t hi = s.T_cap - slot0 < n_valid ? s.T_cap - slot0 : n_valid;
+  // Paged cache, HG = 4: the tile's 16 slots start on a 16-slot boundary and
+  // pages hold a multiple of 64 tokens, so one page (looked up once, wave-
+  // uniform) holds every written row of the tile.
+  int64_t tile_page = -1;
+  if (HG == 4 && a.block_table != nullptr) {
+    const int64_t first = slot0 + lo;                // the tile's first written slot
+    if (lo < hi) tile_page = a.block_table[b * a.max_pages + first / a.page_tokens];
+  }
   // cache row of token tk of the tile, head h0 + g; -1 when a paged slot's
   // page index is outside the cache (the row is not written)
   auto row_of = [&](int g, int64_t tk) -> int64_t {
     const int64_t slot = slot0 + tk;
     if (a.block_table == nullptr) return (b * a.Hkv + h0 + g) * s.T_cap + slot;
-    const int64_t page = a.block_table[b * a.max_pages + slot / a.page_tokens];
+    const int64_t page = HG == 4 ? tile_page : a.block_table[b * a.max_pages + slot / a.page_tokens];
     if (page < 0 || page >= a.n_pages) return -1;
     return (page * a.Hkv + h0 + g) * a.page_tokens + slot % a.page_tokens;
   };
