@@ -39,14 +39,19 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "INT2 decode attention effective HBM GB/s (% of peak) + quantize tokens/s"
 
 # algorithmic bytes (fp16 K/V input)
-QUANT_BYTES_PER_TOKEN_HEAD = 2 * 256 + 2 * 48     # read K and V rows, write 2 INT2 rows
-DECODE_BYTES_PER_TOKEN_HEAD = 2 * 48              # read one INT2 K row and one V row
 
 
 def row_bytes(bits):
     """Bytes of one cached row at `bits` per code: 16*bits code bytes plus
     four fp16 scales and four fp16 zeros (48 for INT2)."""
     return 16 * bits + 16
+
+
+# Algorithmic bytes per (token, KV head): the write reads the fp16 K and V
+# rows and writes two cache rows (608 at 2 bits); the decode reads one K and
+# one V cache row (96 at 2 bits).
+QUANT_BYTES_PER_TOKEN_HEAD = 2 * 256 + 2 * row_bytes(2)
+DECODE_BYTES_PER_TOKEN_HEAD = 2 * row_bytes(2)
 FP16_BYTES_PER_TOKEN_HEAD = 2 * 256               # read one fp16 K row and one V row
 
 
@@ -303,8 +308,10 @@ def main():
     # INT2 (token, head) units the decode reads: every sequence's own range
     int2_tokens = int((ends_h - tb).sum()) if args.varlen else B * (te - tb)
     r_bytes = {"dense": H * d * d * 4, "perm": H * d * 4}.get(rot, 0)   # R / channel orders, read once
-    q_unit = 2 * 256 + row_bytes(kbits) + row_bytes(vbits)     # QUANT_BYTES_PER_TOKEN_HEAD at 2/2
-    d_unit = row_bytes(kbits) + row_bytes(vbits)               # DECODE_BYTES_PER_TOKEN_HEAD at 2/2
+    q_unit = 2 * 256 + row_bytes(kbits) + row_bytes(vbits)
+    d_unit = row_bytes(kbits) + row_bytes(vbits)
+    assert (kbits, vbits) != (2, 2) or (q_unit, d_unit) == (QUANT_BYTES_PER_TOKEN_HEAD,
+                                                             DECODE_BYTES_PER_TOKEN_HEAD)
     q_bytes = B * n_q * H * q_unit + r_bytes
     d_bytes = (int2_tokens * H * d_unit + B * n_f16 * H * FP16_BYTES_PER_TOKEN_HEAD
                + 2 * B * cfg.Hq * d * 2 + r_bytes)
