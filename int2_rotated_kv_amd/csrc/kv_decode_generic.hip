@@ -94,6 +94,9 @@ __device__ __forceinline__ float gen_half(const u32x2_t &v, int g) {
 template <int KB, int VB>
 __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float qs_all[kGenWaves][kD + 4];
+  // 4-bit keys: the query as 19-bit fixed point in five signed 4-bit limbs,
+  // limb L of channels 8j .. 8j+7 in dword j (nibble order of the key codes)
+  __shared__ __attribute__((aligned(16))) uint32_t ql_all[kGenWaves][5][16];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t gw = (int64_t)blockIdx.x * kGenWaves + wave;
@@ -104,6 +107,7 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
   const int hq = hkv * a.G + wp.sub;
   const int64_t bh = b * a.Hkv + hkv;
   float *qs = qs_all[wave];
+  float qstep = 1.0f;                                 // 4-bit keys: weight of one qi unit
 
   // ---- query: q' = qscale * q R, lane l holding channels 2l and 2l + 1,
   // stored in the key codes' order; qs[128 + g] = sum of group g
@@ -140,8 +144,31 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
     }
     x0 *= scale;
     x1 *= scale;
-    qs[idx_of<KB>(2 * lane)] = x0;
-    qs[idx_of<KB>(2 * lane + 1)] = x1;
+    if constexpr (KB == 4) {
+      // qi = rint(q' 2^E) with |qi| < 2^18 for the head's largest |q'|; the
+      // scores are then exact integer dot products of qi with the codes,
+      // and the fixed-point rounding (below 2^-18 of the largest |q'|) is
+      // their only approximation
+      const float amax = gen_wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+      // amax = m 2^e with m in [0.5, 1): E = 18 - e puts amax 2^E in [2^17, 2^18)
+      const int E = amax > 0.0f ? 18 - __builtin_amdgcn_frexp_expf(amax) : 0;
+      qstep = __builtin_amdgcn_ldexpf(1.0f, -E);
+      int q0i = (int)__builtin_rintf(__builtin_amdgcn_ldexpf(x0, E));
+      int q1i = (int)__builtin_rintf(__builtin_amdgcn_ldexpf(x1, E));
+      x0 = (float)q0i;                                // group sums below, in qi units
+      x1 = (float)q1i;
+      uint8_t *lb = reinterpret_cast<uint8_t *>(ql_all[wave]);
+#pragma unroll
+      for (int L = 0; L < 5; ++L) {                   // balanced base-16 digits
+        const int d0 = ((q0i + 8) & 15) - 8, d1 = ((q1i + 8) & 15) - 8;
+        q0i = (q0i - d0) >> 4;
+        q1i = (q1i - d1) >> 4;
+        lb[64 * L + lane] = (uint8_t)((d0 & 15) | ((d1 & 15) << 4));
+      }
+    } else {
+      qs[idx_of<KB>(2 * lane)] = x0;
+      qs[idx_of<KB>(2 * lane + 1)] = x1;
+    }
     float gs = x0 + x1;                               // group g = lane / 16
     gs += quad_swap<kQuadXor1>(gs);
     gs += quad_swap<kQuadXor2>(gs);
@@ -169,16 +196,39 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
     // slower than the re-read).
     asm volatile("" ::: "memory");
     float s = 0.0f;
+    if constexpr (KB == 4) {
+      // per group: sum qi (c - 8) from v_dot8_i32_i4 on the codes with their
+      // top bits flipped (c ^ 8 read as a signed nibble is c - 8), one
+      // accumulator per limb, then + 8 sum qi
+      const uint32_t *ql = &ql_all[wave][0][0];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      float dot = 0.0f;
+      for (int g = 0; g < 4; ++g) {
+        int acc[5] = {0, 0, 0, 0, 0};
+        const u32x4_t w = kr.w[g];                    // dwords 4g .. 4g+3: channels 32g .. 32g+31
 #pragma unroll
-      for (int i4 = 0; i4 < 8; ++i4) {
-        const float4_t q4 = *reinterpret_cast<const float4_t *>(&qs[32 * g + 4 * i4]);
+        for (int L = 0; L < 5; ++L) {
+          const u32x4_t l4 = *reinterpret_cast<const u32x4_t *>(&ql[16 * L + 4 * g]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dot = __builtin_fmaf(q4[e], gen_code<KB>(kr, 32 * g + 4 * i4 + e), dot);
+          for (int e = 0; e < 4; ++e)
+            acc[L] = __builtin_amdgcn_sdot8((int)l4[e], (int)(w[e] ^ 0x88888888u), acc[L], false);
+        }
+        const int v = acc[0] + (acc[1] << 4) + (acc[2] << 8) + (acc[3] << 12) + (acc[4] << 16);
+        const float dot = (float)v + 8.0f * qsum[g];  // sum qi c, exact in fp32 (< 2^24)
+        s = __builtin_fmaf(gen_half(kr.s, g), dot, __builtin_fmaf(gen_half(kr.z, g), qsum[g], s));
       }
-      s = __builtin_fmaf(gen_half(kr.s, g), dot, __builtin_fmaf(gen_half(kr.z, g), qsum[g], s));
+      s *= qstep;
+    } else {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float dot = 0.0f;
+#pragma unroll
+        for (int i4 = 0; i4 < 8; ++i4) {
+          const float4_t q4 = *reinterpret_cast<const float4_t *>(&qs[32 * g + 4 * i4]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dot = __builtin_fmaf(q4[e], gen_code<KB>(kr, 32 * g + 4 * i4 + e), dot);
+        }
+        s = __builtin_fmaf(gen_half(kr.s, g), dot, __builtin_fmaf(gen_half(kr.z, g), qsum[g], s));
+      }
     }
     s = valid ? s : kNegInf;
     const float mt = gen_wave_max(s);
