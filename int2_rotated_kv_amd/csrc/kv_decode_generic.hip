@@ -9,9 +9,10 @@
 // query rotated by R and the output un-rotated by R^T in the combine).
 //
 // One wave per (batch, query head, split).  The wave rotates and scales its
-// query itself (none, Hadamard or reordered Hadamard) and keeps it in LDS in
-// the key codes' order.  Every 64-token tile gives one token to each lane:
-// the lane unpacks its token's key codes into a score, the wave shares a
+// query itself (none, Hadamard or reordered Hadamard) and keeps it in LDS as
+// a 19-bit fixed point in five 4-bit limbs, laid out in the nibble order of
+// the key codes.  Every 64-token tile gives one token to each lane: the lane
+// scores its token with v_dot8_i32_i4 on the key codes, the wave shares a
 // running maximum, and the lane adds its token's weighted value codes into
 // 128 accumulators of its own.  At the end the 64 lanes' accumulators are
 // summed by a reduce-scatter that leaves two channels in each lane, and the
@@ -42,16 +43,11 @@ __device__ __forceinline__ float gen_wave_max(float v) {
 // Code order of a b-bit row: dword j holds channels (32/b) j .. (32/b)(j+1) - 1,
 // channel (32/b) j + P k + m (P = 8/b codes per byte) in byte k, field m.
 // Reading the dword field by field, k fastest, gives index
-// (32/b) j + 4 m + k; the channel of index i, and the index of channel c:
+// (32/b) j + 4 m + k; the channel of index i:
 template <int BITS>
 __host__ __device__ __forceinline__ constexpr int chan_of(int i) {
   constexpr int CPW = 32 / BITS, P = 8 / BITS;
   return CPW * (i / CPW) + P * (i % 4) + (i % CPW) / 4;
-}
-template <int BITS>
-__host__ __device__ __forceinline__ constexpr int idx_of(int c) {
-  constexpr int CPW = 32 / BITS, P = 8 / BITS;
-  return CPW * (c / CPW) + 4 * ((c % CPW) % P) + (c % CPW) / P;
 }
 
 // One token's row of one side: 16*BITS code bytes, then the four fp16
@@ -74,6 +70,26 @@ __device__ __forceinline__ GenRow<BITS> gen_load(const uint8_t *codes, const uin
   return r;
 }
 
+// Key codes as signed nibbles for v_dot8_i32_i4.  Limb dword u (0..15) of a
+// b-bit row is code dword j = u / (4/b), shifted right by b (u mod 4/b) and
+// masked to b bits per nibble: nibble h then holds the code of channel
+// (32/b) j + (4/b) h + (u mod 4/b).  4-bit codes are flipped in their top bit,
+// so that the signed nibble reads c - 8.
+template <int BITS>
+__host__ __device__ __forceinline__ constexpr int nib_pos(int c) {   // 8 u + h of channel c
+  constexpr int CPW = 32 / BITS, SUB = 4 / BITS;
+  return 8 * ((c / CPW) * SUB + (c % CPW) % SUB) + (c % CPW) / SUB;
+}
+template <int BITS>
+__device__ __forceinline__ uint32_t key_nibbles(const GenRow<BITS> &r, int u) {
+  constexpr int SUB = 4 / BITS;
+  const int j = u / SUB;
+  const uint32_t w = r.w[j >> 2][j & 3];
+  if constexpr (BITS == 4) return w ^ 0x88888888u;
+  else if constexpr (BITS == 2) return (w >> (2 * (u % SUB))) & 0x33333333u;
+  else return (w >> (u % SUB)) & 0x11111111u;
+}
+
 // Code of index i (code order) of a row held as BITS x 4 dwords.
 template <int BITS>
 __device__ __forceinline__ float gen_code(const GenRow<BITS> &r, int i) {
@@ -93,10 +109,12 @@ __device__ __forceinline__ float gen_half(const u32x2_t &v, int g) {
 // wave_place with one wave per query head (`per` = G).
 template <int KB, int VB>
 __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) float qs_all[kGenWaves][kD + 4];
-  // 4-bit keys: the query as 19-bit fixed point in five signed 4-bit limbs,
-  // limb L of channels 8j .. 8j+7 in dword j (nibble order of the key codes)
+  // the query as a 19-bit fixed point in five signed 4-bit limbs: limb L,
+  // nibble 8u + h at the position of the key nibble it multiplies (nib_pos);
+  // nibbles staged one per byte first, then packed; group sums of qi last
   __shared__ __attribute__((aligned(16))) uint32_t ql_all[kGenWaves][5][16];
+  __shared__ uint8_t qn_all[kGenWaves][5][kD];
+  __shared__ float qsum_all[kGenWaves][4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t gw = (int64_t)blockIdx.x * kGenWaves + wave;
@@ -106,11 +124,9 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
   const int hkv = wp.hkv;
   const int hq = hkv * a.G + wp.sub;
   const int64_t bh = b * a.Hkv + hkv;
-  float *qs = qs_all[wave];
-  float qstep = 1.0f;                                 // 4-bit keys: weight of one qi unit
+  float qstep;                                        // weight of one qi unit
 
-  // ---- query: q' = qscale * q R, lane l holding channels 2l and 2l + 1,
-  // stored in the key codes' order; qs[128 + g] = sum of group g
+  // ---- query: q' = qscale * q R, lane l holding channels 2l and 2l + 1
   {
     const int64_t qoff = (b * a.Hq + hq) * kD;
     int c0 = 2 * lane, c1 = 2 * lane + 1;
@@ -144,42 +160,40 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
     }
     x0 *= scale;
     x1 *= scale;
-    if constexpr (KB == 4) {
-      // qi = rint(q' 2^E) with |qi| < 2^18 for the head's largest |q'|; the
-      // scores are then exact integer dot products of qi with the codes,
-      // and the fixed-point rounding (below 2^-18 of the largest |q'|) is
-      // their only approximation
-      const float amax = gen_wave_max(fmaxf(fabsf(x0), fabsf(x1)));
-      // amax = m 2^e with m in [0.5, 1): E = 18 - e puts amax 2^E in [2^17, 2^18)
-      const int E = amax > 0.0f ? 18 - __builtin_amdgcn_frexp_expf(amax) : 0;
-      qstep = __builtin_amdgcn_ldexpf(1.0f, -E);
-      int q0i = (int)__builtin_rintf(__builtin_amdgcn_ldexpf(x0, E));
-      int q1i = (int)__builtin_rintf(__builtin_amdgcn_ldexpf(x1, E));
-      x0 = (float)q0i;                                // group sums below, in qi units
-      x1 = (float)q1i;
-      uint8_t *lb = reinterpret_cast<uint8_t *>(ql_all[wave]);
+    // qi = rint(q' 2^E) with |qi| < 2^18 for the head's largest |q'|; the
+    // scores are then exact integer dot products of qi with the codes, and
+    // the fixed-point rounding (below 2^-18 of the largest |q'|) is their
+    // only approximation
+    const float amax = gen_wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+    // amax = m 2^e with m in [0.5, 1): E = 18 - e puts amax 2^E in [2^17, 2^18)
+    const int E = amax > 0.0f ? 18 - __builtin_amdgcn_frexp_expf(amax) : 0;
+    qstep = __builtin_amdgcn_ldexpf(1.0f, -E);
+    int q0i = (int)__builtin_rintf(__builtin_amdgcn_ldexpf(x0, E));
+    int q1i = (int)__builtin_rintf(__builtin_amdgcn_ldexpf(x1, E));
+    float gs = (float)q0i + (float)q1i;               // group g = lane / 16, exact
+    uint8_t(*qn)[kD] = qn_all[wave];
 #pragma unroll
-      for (int L = 0; L < 5; ++L) {                   // balanced base-16 digits
-        const int d0 = ((q0i + 8) & 15) - 8, d1 = ((q1i + 8) & 15) - 8;
-        q0i = (q0i - d0) >> 4;
-        q1i = (q1i - d1) >> 4;
-        lb[64 * L + lane] = (uint8_t)((d0 & 15) | ((d1 & 15) << 4));
-      }
-    } else {
-      qs[idx_of<KB>(2 * lane)] = x0;
-      qs[idx_of<KB>(2 * lane + 1)] = x1;
+    for (int L = 0; L < 5; ++L) {                     // balanced base-16 digits
+      const int d0 = ((q0i + 8) & 15) - 8, d1 = ((q1i + 8) & 15) - 8;
+      q0i = (q0i - d0) >> 4;
+      q1i = (q1i - d1) >> 4;
+      qn[L][nib_pos<KB>(2 * lane)] = (uint8_t)(d0 & 15);
+      qn[L][nib_pos<KB>(2 * lane + 1)] = (uint8_t)(d1 & 15);
     }
-    float gs = x0 + x1;                               // group g = lane / 16
     gs += quad_swap<kQuadXor1>(gs);
     gs += quad_swap<kQuadXor2>(gs);
     gs += row_ror<4>(gs);
     gs += row_ror<8>(gs);
-    if ((lane & 15) == 0) qs[kD + (lane >> 4)] = gs;
-  }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's LDS writes are done
-  float qsum[4];
+    if ((lane & 15) == 0) qsum_all[wave][lane >> 4] = gs;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's LDS writes are done
+    uint8_t *lb = reinterpret_cast<uint8_t *>(ql_all[wave]);
 #pragma unroll
-  for (int g = 0; g < 4; ++g) qsum[g] = qs[kD + g];
+    for (int L = 0; L < 5; ++L) lb[64 * L + lane] = (uint8_t)(qn[L][2 * lane] | (qn[L][2 * lane + 1] << 4));
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  float qsum[4];                                      // sum of qi over each group
+#pragma unroll
+  for (int g = 0; g < 4; ++g) qsum[g] = qsum_all[wave][g];
 
   float acc[kD];                                      // value accumulators, value-code order
 #pragma unroll
@@ -191,45 +205,27 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
   const int64_t vrow0 = bh * a.vT_cap + a.t_begin - a.skip;
 
   auto token = [&](const GenRow<KB> &kr, const GenRow<VB> &vr, bool valid) {
-    // The query is re-read from LDS for every token: kept in registers it
-    // would take 128 of them and leave one wave per SIMD (measured 12-19%
-    // slower than the re-read).
+    // The query limbs are re-read from LDS for every token: a query held
+    // in registers leaves one wave per SIMD (measured 12-19% slower).
     asm volatile("" ::: "memory");
+    // per group: sum qi c from v_dot8_i32_i4, one accumulator per limb
+    // (4-bit codes read as c - 8, so + 8 sum qi restores sum qi c)
     float s = 0.0f;
-    if constexpr (KB == 4) {
-      // per group: sum qi (c - 8) from v_dot8_i32_i4 on the codes with their
-      // top bits flipped (c ^ 8 read as a signed nibble is c - 8), one
-      // accumulator per limb, then + 8 sum qi
-      const uint32_t *ql = &ql_all[wave][0][0];
+    const uint32_t *ql = &ql_all[wave][0][0];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        int acc[5] = {0, 0, 0, 0, 0};
-        const u32x4_t w = kr.w[g];                    // dwords 4g .. 4g+3: channels 32g .. 32g+31
+    for (int g = 0; g < 4; ++g) {
+      int acc5[5] = {0, 0, 0, 0, 0};
 #pragma unroll
-        for (int L = 0; L < 5; ++L) {
-          const u32x4_t l4 = *reinterpret_cast<const u32x4_t *>(&ql[16 * L + 4 * g]);
+      for (int e = 0; e < 4; ++e) {
+        const int kn = (int)key_nibbles<KB>(kr, 4 * g + e);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            acc[L] = __builtin_amdgcn_sdot8((int)l4[e], (int)(w[e] ^ 0x88888888u), acc[L], false);
-        }
-        const int v = acc[0] + (acc[1] << 4) + (acc[2] << 8) + (acc[3] << 12) + (acc[4] << 16);
-        const float dot = (float)v + 8.0f * qsum[g];  // sum qi c, exact in fp32 (< 2^24)
-        s = __builtin_fmaf(gen_half(kr.s, g), dot, __builtin_fmaf(gen_half(kr.z, g), qsum[g], s));
+        for (int L = 0; L < 5; ++L) acc5[L] = __builtin_amdgcn_sdot8((int)ql[16 * L + 4 * g + e], kn, acc5[L], false);
       }
-      s *= qstep;
-    } else {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float dot = 0.0f;
-#pragma unroll
-        for (int i4 = 0; i4 < 8; ++i4) {
-          const float4_t q4 = *reinterpret_cast<const float4_t *>(&qs[32 * g + 4 * i4]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dot = __builtin_fmaf(q4[e], gen_code<KB>(kr, 32 * g + 4 * i4 + e), dot);
-        }
-        s = __builtin_fmaf(gen_half(kr.s, g), dot, __builtin_fmaf(gen_half(kr.z, g), qsum[g], s));
-      }
+      const int v = acc5[0] + (acc5[1] << 4) + (acc5[2] << 8) + (acc5[3] << 12) + (acc5[4] << 16);
+      const float dot = KB == 4 ? (float)v + 8.0f * qsum[g] : (float)v;   // exact in fp32 (< 2^24)
+      s = __builtin_fmaf(gen_half(kr.s, g), dot, __builtin_fmaf(gen_half(kr.z, g), qsum[g], s));
     }
+    s *= qstep;
     s = valid ? s : kNegInf;
     const float mt = gen_wave_max(s);
     if (mt > m_run + kSlack) {                         // wave-uniform
