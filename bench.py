@@ -167,14 +167,13 @@ def main():
         workload += "_varlen"
     kbits, vbits = args.kbits, args.vbits
     if (kbits, vbits) != (2, 2):
-        if rot == "dense" or args.varlen:
-            sys.exit("--kbits/--vbits other than 2 need a Hadamard workload (--config 3 or 5) "
-                     "without --varlen")
+        if rot == "dense":
+            sys.exit("--kbits/--vbits other than 2 need a Hadamard workload (--config 3 or 5)")
         workload += f"_k{kbits}v{vbits}"
     P = args.paged
     if P:
-        if P % 64 or rot == "dense" or (kbits, vbits) != (2, 2):
-            sys.exit("--paged P needs P a multiple of 64, a Hadamard workload and 2-bit codes")
+        if P % 64 or rot == "dense":
+            sys.exit("--paged P needs P a multiple of 64 and a Hadamard workload")
         workload += f"_paged{P}"
     print(f"[bench] generating {workload} on the GPU", file=sys.stderr, flush=True)
     t0 = time.time()
@@ -192,8 +191,8 @@ def main():
         per = (T + P - 1) // P
         pool = np.random.default_rng(np.random.SeedSequence([2000 + cfg.cid, P])).permutation(B * per)
         table = torch.from_numpy(pool.reshape(B, per).astype(np.int32)).to(dev)
-        ck = kvq.PagedCache.empty(B * per, H, P, device=dev)
-        cv = kvq.PagedCache.empty(B * per, H, P, device=dev)
+        ck = kvq.PagedCache.empty(B * per, H, P, device=dev, bits=kbits)
+        cv = kvq.PagedCache.empty(B * per, H, P, device=dev, bits=vbits)
     else:
         ck = kvq.Int2Cache.empty(B, H, T, device=dev, bits=kbits)
         cv = kvq.Int2Cache.empty(B, H, T, device=dev, bits=vbits)

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 5
+#define KVQ_ABI_VERSION 6
 
 typedef enum {
   KVQ_OK = 0,
@@ -110,19 +110,20 @@ typedef struct {
   int32_t bits;
 } kvq_quant_cache;
 
-/* One side (K or V) of a paged INT2 cache: fixed-size pages of page_tokens
+/* One side (K or V) of a paged cache: fixed-size pages of page_tokens
  * token rows each, [n_pages][Hkv][page_tokens][...] per array, row formats as
- * above.  A block table int32 [B][max_pages] (device) maps sequence b's
- * token t to row t % page_tokens of page table[b][t / page_tokens];
- * page_tokens must be a multiple of 64.  Serving stacks keep caches in such
- * pages (the pages name serving stacks as the setting: OptR page, "Why It
- * Matters"). */
+ * above for codes `bits` wide (1, 2 or 4; 2 is the INT2 format).  A block
+ * table int32 [B][max_pages] (device) maps sequence b's token t to row
+ * t % page_tokens of page table[b][t / page_tokens]; page_tokens must be a
+ * multiple of 64.  Serving stacks keep caches in such pages (the pages name
+ * serving stacks as the setting: OptR page, "Why It Matters"). */
 typedef struct {
   uint8_t *codes;
   uint16_t *scales;
   uint16_t *zeros;
   int64_t n_pages;
   int64_t page_tokens;
+  int32_t bits;
 } kvq_paged_cache;
 
 /*
@@ -286,13 +287,46 @@ kvq_status kvq_decode_attention_bits(const void *q, kvq_dtype q_dtype,
                                      void *stream);
 
 /*
+ * kvq_quantize_at_bits -- kvq_quantize_at into caches of any supported code
+ * width: the per-sequence slots of kvq_quantize_at with the caches and
+ * width rules of kvq_quantize_bits.
+ */
+kvq_status kvq_quantize_at_bits(const void *K, const void *V, kvq_dtype in_dtype,
+                                int64_t B, int64_t T_new, int64_t Hkv, int64_t d,
+                                int64_t stride_b, int64_t stride_t, int64_t stride_h,
+                                kvq_rot rot, const void *R, int group,
+                                const int32_t *t_offsets, const kvq_quant_cache *kc,
+                                const kvq_quant_cache *vc, void *stream);
+
+/*
+ * kvq_decode_attention_varlen_bits -- kvq_decode_attention_varlen over
+ * caches of any supported code width: the per-sequence ends of
+ * kvq_decode_attention_varlen with the caches and rotation rules of
+ * kvq_decode_attention_bits.  Workspace as for kvq_decode_attention_varlen.
+ */
+kvq_status kvq_decode_attention_varlen_bits(const void *q, kvq_dtype q_dtype,
+                                            int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
+                                            const kvq_quant_cache *kc,
+                                            const kvq_quant_cache *vc, int64_t t_begin,
+                                            const int32_t *t_ends, int64_t t_end_max,
+                                            kvq_rot rot, const void *R, int group,
+                                            const uint16_t *sink_k, const uint16_t *sink_v,
+                                            int64_t n_sink,
+                                            const uint16_t *res_k, const uint16_t *res_v,
+                                            int64_t n_res, float softmax_scale,
+                                            void *out, kvq_dtype out_dtype,
+                                            void *workspace, size_t workspace_bytes,
+                                            void *stream);
+
+/*
  * kvq_quantize_paged -- kvq_quantize_at into a paged cache: sequence b's
  * T_new rows are its tokens t_offsets[b] .. t_offsets[b] + T_new - 1, each
  * written to its page through block_table.  A token outside
  * [0, max_pages * page_tokens), or whose page index is outside [0, n_pages),
  * is not written.  Needs in_dtype == KVQ_F16 and rot KVQ_ROT_HADAMARD or
  * KVQ_ROT_PERM_HADAMARD (else KVQ_ERR_UNSUPPORTED).  kc and vc (either may
- * be NULL with its input) must agree on n_pages and page_tokens.
+ * be NULL with its input) must agree on n_pages and page_tokens; each has
+ * its own bits (1, 2 or 4, else KVQ_ERR_INVALID_ARG).
  */
 kvq_status kvq_quantize_paged(const void *K, const void *V, kvq_dtype in_dtype,
                               int64_t B, int64_t T_new, int64_t Hkv, int64_t d,
@@ -309,7 +343,9 @@ kvq_status kvq_quantize_paged(const void *K, const void *V, kvq_dtype in_dtype,
  * max_pages * page_tokens.  A page index outside [0, n_pages) reads page 0
  * (an unspecified result, never an access outside the cache).  Workspace:
  * kvq_decode_workspace_bytes with n_int2_tokens = t_end_max - t_begin.
- * Every other argument as for kvq_decode_attention_varlen.
+ * With either side at 1 or 4 bits the rotation rules of
+ * kvq_decode_attention_bits apply.  Every other argument as for
+ * kvq_decode_attention_varlen.
  */
 kvq_status kvq_decode_attention_paged(const void *q, kvq_dtype q_dtype,
                                       int64_t B, int64_t Hq, int64_t Hkv, int64_t d,

@@ -44,8 +44,9 @@ struct Paging {
   int64_t max_pages, n_pages, page_tokens;
 };
 
-// Checks a paged side pair and the table; on success fills the 2-bit cache
-// views (T_cap = the logical capacity max_pages * page_tokens) and pg.
+// Checks a paged side pair and the table; on success fills the cache views
+// (T_cap = the logical capacity max_pages * page_tokens) and pg.  The widths
+// are checked with the views.
 kvq_status check_paged(const kvq_paged_cache *kc, const kvq_paged_cache *vc, const int32_t *block_table,
                        int64_t B, int64_t max_pages, kvq_quant_cache &kq, kvq_quant_cache &vq, Paging &pg) {
   if (block_table == nullptr || ((uintptr_t)block_table & 3u) != 0) return KVQ_ERR_INVALID_ARG;
@@ -65,7 +66,7 @@ kvq_status check_paged(const kvq_paged_cache *kc, const kvq_paged_cache *vc, con
     if (max_pages > ((int64_t)1 << 40) / pt) return KVQ_ERR_INVALID_ARG;
     qs[i]->codes = c->codes; qs[i]->scales = c->scales; qs[i]->zeros = c->zeros;
     qs[i]->T_cap = max_pages * c->page_tokens;
-    qs[i]->bits = 2;
+    qs[i]->bits = c->bits;
   }
   pg.block_table = block_table;
   pg.max_pages = max_pages;
@@ -333,6 +334,33 @@ kvq_status kvq_decode_attention_varlen(const void *q, kvq_dtype q_dtype, int64_t
   if (t_ends == nullptr || ((uintptr_t)t_ends & 3u) != 0) return KVQ_ERR_INVALID_ARG;
   const AsQuant k2(kc), v2(vc);
   return decode_impl(q, q_dtype, B, Hq, Hkv, d, k2.p, v2.p, t_begin, t_end_max, t_ends, rot, R, group,
+                     sink_k, sink_v, n_sink, res_k, res_v, n_res, softmax_scale, out, out_dtype,
+                     workspace, workspace_bytes_given, stream);
+}
+
+kvq_status kvq_quantize_at_bits(const void *K, const void *V, kvq_dtype in_dtype, int64_t B,
+                                int64_t T_new, int64_t Hkv, int64_t d, int64_t stride_b,
+                                int64_t stride_t, int64_t stride_h, kvq_rot rot, const void *R,
+                                int group, const int32_t *t_offsets, const kvq_quant_cache *kc,
+                                const kvq_quant_cache *vc, void *stream) {
+  if (t_offsets == nullptr || ((uintptr_t)t_offsets & 3u) != 0) return KVQ_ERR_INVALID_ARG;
+  return quantize_impl(K, V, in_dtype, B, T_new, Hkv, d, stride_b, stride_t, stride_h, rot, R,
+                       group, 0, t_offsets, kc, vc, stream);
+}
+
+kvq_status kvq_decode_attention_varlen_bits(const void *q, kvq_dtype q_dtype, int64_t B, int64_t Hq,
+                                            int64_t Hkv, int64_t d, const kvq_quant_cache *kc,
+                                            const kvq_quant_cache *vc, int64_t t_begin,
+                                            const int32_t *t_ends, int64_t t_end_max,
+                                            kvq_rot rot, const void *R, int group,
+                                            const uint16_t *sink_k, const uint16_t *sink_v,
+                                            int64_t n_sink,
+                                            const uint16_t *res_k, const uint16_t *res_v,
+                                            int64_t n_res, float softmax_scale, void *out,
+                                            kvq_dtype out_dtype, void *workspace,
+                                            size_t workspace_bytes_given, void *stream) {
+  if (t_ends == nullptr || ((uintptr_t)t_ends & 3u) != 0) return KVQ_ERR_INVALID_ARG;
+  return decode_impl(q, q_dtype, B, Hq, Hkv, d, kc, vc, t_begin, t_end_max, t_ends, rot, R, group,
                      sink_k, sink_v, n_sink, res_k, res_v, n_res, softmax_scale, out, out_dtype,
                      workspace, workspace_bytes_given, stream);
 }

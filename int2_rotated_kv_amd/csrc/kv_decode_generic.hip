@@ -250,15 +250,16 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
 
   const HeadTiles ht(seq_int2(a, b), a.skip, split, S);
   if (ht.mine > 0) {
-    int64_t r = ht.full_row(0, split, S) + lane;
-    GenRow<KB> kr = gen_load<KB>(a.kcodes, a.kscales, a.kzeros, krow0 + r);
-    GenRow<VB> vr = gen_load<VB>(a.vcodes, a.vscales, a.vzeros, vrow0 + r);
+    // a tile's rows follow its first row (one page holds the whole tile)
+    const TileRows t0 = tile_rows(a, b, hkv, krow0, vrow0, ht.full_row(0, split, S));
+    GenRow<KB> kr = gen_load<KB>(a.kcodes, a.kscales, a.kzeros, t0.k + lane);
+    GenRow<VB> vr = gen_load<VB>(a.vcodes, a.vscales, a.vzeros, t0.v + lane);
     for (int64_t i = 0; i < ht.mine; ++i) {
       // the next tile's rows are loaded while this one is computed (the
       // last prefetch re-reads the wave's last tile)
-      const int64_t rn = ht.full_row(i + 1, split, S) + lane;
-      const GenRow<KB> kn = gen_load<KB>(a.kcodes, a.kscales, a.kzeros, krow0 + rn);
-      const GenRow<VB> vn = gen_load<VB>(a.vcodes, a.vscales, a.vzeros, vrow0 + rn);
+      const TileRows tn = tile_rows(a, b, hkv, krow0, vrow0, ht.full_row(i + 1, split, S));
+      const GenRow<KB> kn = gen_load<KB>(a.kcodes, a.kscales, a.kzeros, tn.k + lane);
+      const GenRow<VB> vn = gen_load<VB>(a.vcodes, a.vscales, a.vzeros, tn.v + lane);
       token(kr, vr, true);
       kr = kn;
       vr = vn;
@@ -274,9 +275,10 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
       const int64_t lo = a.skip > base ? a.skip - base : 0;
       const int64_t hi = ht.n_tok - base < 64 ? ht.n_tok - base : 64;
       const bool valid = lane >= lo && lane < hi;
-      const int64_t r = base + (valid ? lane : lo);
-      token(gen_load<KB>(a.kcodes, a.kscales, a.kzeros, krow0 + r),
-            gen_load<VB>(a.vcodes, a.vscales, a.vzeros, vrow0 + r), valid);
+      const int64_t r = valid ? lane : lo;
+      const TileRows tr = tile_rows(a, b, hkv, krow0, vrow0, base);
+      token(gen_load<KB>(a.kcodes, a.kscales, a.kzeros, tr.k + r),
+            gen_load<VB>(a.vcodes, a.vscales, a.vzeros, tr.v + r), valid);
     }
   }
 

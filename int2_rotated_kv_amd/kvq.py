@@ -26,10 +26,11 @@ KVQ_ROT_NONE, KVQ_ROT_HADAMARD, KVQ_ROT_DENSE, KVQ_ROT_PERM_HADAMARD = 0, 1, 2, 
 _ROT = {"none": KVQ_ROT_NONE, "hadamard": KVQ_ROT_HADAMARD, "dense": KVQ_ROT_DENSE,
         "perm": KVQ_ROT_PERM_HADAMARD}
 
-EXPORTED_SYMBOLS = ("kvq_quantize", "kvq_quantize_at", "kvq_quantize_bits", "kvq_quantize_paged",
-                    "kvq_decode_workspace_bytes", "kvq_decode_attention",
+EXPORTED_SYMBOLS = ("kvq_quantize", "kvq_quantize_at", "kvq_quantize_bits", "kvq_quantize_at_bits",
+                    "kvq_quantize_paged", "kvq_decode_workspace_bytes", "kvq_decode_attention",
                     "kvq_decode_attention_varlen", "kvq_decode_attention_bits",
-                    "kvq_decode_attention_paged", "kvq_status_str", "kvq_abi_version")
+                    "kvq_decode_attention_varlen_bits", "kvq_decode_attention_paged",
+                    "kvq_status_str", "kvq_abi_version")
 
 D_HEAD = 128
 GROUP = 32
@@ -49,7 +50,7 @@ class kvq_int2_cache(ctypes.Structure):
 class kvq_paged_cache(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("zeros", ctypes.c_void_p), ("n_pages", ctypes.c_int64),
-                ("page_tokens", ctypes.c_int64)]
+                ("page_tokens", ctypes.c_int64), ("bits", ctypes.c_int32)]
 
 
 class kvq_quant_cache(ctypes.Structure):
@@ -99,6 +100,13 @@ def load_library() -> ctypes.CDLL:
     lib.kvq_decode_attention_bits.argtypes = [vp, i32, i64, i64, i64, i64, qp, qp, i64, i64,
                                               i32, vp, i32, vp, vp, i64, vp, vp, i64, f32,
                                               vp, i32, vp, ctypes.c_size_t, vp]
+    lib.kvq_quantize_at_bits.restype = i32
+    lib.kvq_quantize_at_bits.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, i64, i64,
+                                         i32, vp, i32, vp, qp, qp, vp]
+    lib.kvq_decode_attention_varlen_bits.restype = i32
+    lib.kvq_decode_attention_varlen_bits.argtypes = [vp, i32, i64, i64, i64, i64, qp, qp, i64, vp,
+                                                     i64, i32, vp, i32, vp, vp, i64, vp, vp, i64,
+                                                     f32, vp, i32, vp, ctypes.c_size_t, vp]
     pp = ctypes.POINTER(kvq_paged_cache)
     lib.kvq_quantize_paged.restype = i32
     lib.kvq_quantize_paged.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, i64, i64,
@@ -203,11 +211,20 @@ def kvq_quantize(K, V, cache_k: Int2Cache | None, cache_v: Int2Cache | None,
         raise ValueError("K and V must share shape, strides and dtype")
     B, T_new, Hkv, d = x.shape
     lib = load_library()
+    if t_offsets is not None and (t_offsets.dtype != torch.int32 or t_offsets.numel() != B):
+        raise ValueError("t_offsets must be int32 [B]")
     if any(c is not None and c.bits != 2 for c in (cache_k, cache_v)):
-        if t_offsets is not None:
-            raise ValueError("per-sequence slots are for 2-bit caches")
         kq = cache_k.c_quant_struct() if cache_k is not None else None
         vq = cache_v.c_quant_struct() if cache_v is not None else None
+        if t_offsets is not None:
+            st = lib.kvq_quantize_at_bits(
+                _ptr(K), _ptr(V), _dtype_code(x), B, T_new, Hkv, d,
+                x.stride(0), x.stride(1), x.stride(2), _ROT[rot], _ptr(R), group,
+                _ptr(t_offsets),
+                ctypes.byref(kq) if kq is not None else None,
+                ctypes.byref(vq) if vq is not None else None, _stream(stream))
+            _check(st, "kvq_quantize_at_bits")
+            return
         st = lib.kvq_quantize_bits(
             _ptr(K), _ptr(V), _dtype_code(x), B, T_new, Hkv, d,
             x.stride(0), x.stride(1), x.stride(2), _ROT[rot], _ptr(R), group, t_offset,
@@ -218,8 +235,6 @@ def kvq_quantize(K, V, cache_k: Int2Cache | None, cache_v: Int2Cache | None,
     kc = cache_k.c_struct() if cache_k is not None else None
     vc = cache_v.c_struct() if cache_v is not None else None
     if t_offsets is not None:
-        if t_offsets.dtype != torch.int32 or t_offsets.numel() != B:
-            raise ValueError("t_offsets must be int32 [B]")
         st = lib.kvq_quantize_at(
             _ptr(K), _ptr(V), _dtype_code(x), B, T_new, Hkv, d,
             x.stride(0), x.stride(1), x.stride(2), _ROT[rot], _ptr(R), group, _ptr(t_offsets),
@@ -269,11 +284,22 @@ def kvq_decode_attention(q: torch.Tensor, cache_k: Int2Cache | None,
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     lib = load_library()
+    if t_ends is not None and (t_ends.dtype != torch.int32 or t_ends.numel() != B):
+        raise ValueError("t_ends must be int32 [B]")
     if any(c is not None and c.bits != 2 for c in (cache_k, cache_v)):
-        if t_ends is not None:
-            raise ValueError("per-sequence ends are for 2-bit caches")
         kq = cache_k.c_quant_struct() if cache_k is not None else None
         vq = cache_v.c_quant_struct() if cache_v is not None else None
+        if t_ends is not None:
+            st = lib.kvq_decode_attention_varlen_bits(
+                _ptr(q), _dtype_code(q), B, Hq, Hkv, d,
+                ctypes.byref(kq) if kq is not None else None,
+                ctypes.byref(vq) if vq is not None else None,
+                t_begin, _ptr(t_ends), t_end, _ROT[rot], _ptr(R), group,
+                _ptr(sink_k), _ptr(sink_v), n_sink, _ptr(res_k), _ptr(res_v), n_res,
+                float(softmax_scale), _ptr(out), _dtype_code(out),
+                _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+            _check(st, "kvq_decode_attention_varlen_bits")
+            return out
         st = lib.kvq_decode_attention_bits(
             _ptr(q), _dtype_code(q), B, Hq, Hkv, d,
             ctypes.byref(kq) if kq is not None else None,
@@ -287,8 +313,6 @@ def kvq_decode_attention(q: torch.Tensor, cache_k: Int2Cache | None,
     kc = cache_k.c_struct() if cache_k is not None else None
     vc = cache_v.c_struct() if cache_v is not None else None
     if t_ends is not None:
-        if t_ends.dtype != torch.int32 or t_ends.numel() != B:
-            raise ValueError("t_ends must be int32 [B]")
         st = lib.kvq_decode_attention_varlen(
             _ptr(q), _dtype_code(q), B, Hq, Hkv, d,
             ctypes.byref(kc) if kc is not None else None,
@@ -316,25 +340,33 @@ def default_softmax_scale(d: int = D_HEAD) -> float:
 
 
 class PagedCache:
-    """Device buffers of one side (K or V) of a paged INT2 cache:
-    codes uint8 [n_pages, Hkv, page_tokens, d/4]; scales / zeros fp16
+    """Device buffers of one side (K or V) of a paged cache:
+    codes uint8 [n_pages, Hkv, page_tokens, d*bits/8]; scales / zeros fp16
     [n_pages, Hkv, page_tokens, d/32].  A block table int32 [B, max_pages]
-    maps sequence b's token t to row t % page_tokens of page table[b, t // page_tokens]."""
+    maps sequence b's token t to row t % page_tokens of page table[b, t // page_tokens].
+    bits = 2 (the INT2 format) unless given; 1 and 4 are the other widths."""
 
-    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor):
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+                 bits: int | None = None):
         self.codes, self.scales, self.zeros = codes, scales, zeros
         self.n_pages, self.page_tokens = codes.shape[0], codes.shape[2]
+        d = scales.shape[3] * GROUP
+        self.bits = bits if bits is not None else 8 * codes.shape[3] // d
+        if codes.shape[3] * 8 != d * self.bits:
+            raise ValueError("codes row width does not match bits")
 
     @classmethod
-    def empty(cls, n_pages: int, Hkv: int, page_tokens: int, device="cuda", d: int = D_HEAD):
-        codes = torch.empty((n_pages, Hkv, page_tokens, d // 4), dtype=torch.uint8, device=device)
+    def empty(cls, n_pages: int, Hkv: int, page_tokens: int, device="cuda", d: int = D_HEAD,
+              bits: int = 2):
+        codes = torch.empty((n_pages, Hkv, page_tokens, d * bits // 8), dtype=torch.uint8,
+                            device=device)
         scales = torch.empty((n_pages, Hkv, page_tokens, d // GROUP), dtype=torch.float16, device=device)
         zeros = torch.empty((n_pages, Hkv, page_tokens, d // GROUP), dtype=torch.float16, device=device)
-        return cls(codes, scales, zeros)
+        return cls(codes, scales, zeros, bits)
 
     def c_struct(self) -> kvq_paged_cache:
         return kvq_paged_cache(self.codes.data_ptr(), self.scales.data_ptr(), self.zeros.data_ptr(),
-                               self.n_pages, self.page_tokens)
+                               self.n_pages, self.page_tokens, self.bits)
 
 
 def _table(block_table, B):

@@ -240,8 +240,35 @@ def test_decode_bits_rejects(lib):
     assert call(1, 4, wsb=100) == K.KVQ_ERR_WORKSPACE_TOO_SMALL
 
 
-def _pcache(n_pages=4, page_tokens=128):
-    return K.kvq_paged_cache(FAKE, FAKE, FAKE, n_pages, page_tokens)
+def test_varlen_bits_rejects(lib):
+    """Per-sequence slots and ends at other code widths: the per-sequence
+    arrays are required and 4-byte aligned; the width rules are those of
+    the common-range calls."""
+    def quant(kb, vb, offs=FAKE, dt=K.KVQ_F16, rot=K.KVQ_ROT_HADAMARD):
+        return lib.kvq_quantize_at_bits(FAKE, FAKE, dt, 1, 8, 2, 128, 8 * 2 * 128, 2 * 128, 128,
+                                        rot, None, 32, offs, ctypes.byref(_qcache(kb)),
+                                        ctypes.byref(_qcache(vb)), None)
+    assert quant(4, 2, offs=None) == K.KVQ_ERR_INVALID_ARG
+    assert quant(4, 2, offs=FAKE + 2) == K.KVQ_ERR_INVALID_ARG
+    assert quant(3, 2) == K.KVQ_ERR_INVALID_ARG
+    assert quant(1, 1, dt=K.KVQ_F32) == K.KVQ_ERR_UNSUPPORTED
+    assert quant(4, 2, rot=K.KVQ_ROT_NONE) == K.KVQ_ERR_UNSUPPORTED
+
+    def dec(kb, vb, tends=FAKE, te_max=64, rot=K.KVQ_ROT_HADAMARD, R=None, wsb=1 << 30):
+        return lib.kvq_decode_attention_varlen_bits(
+            FAKE, K.KVQ_F16, 2, 4, 2, 128, ctypes.byref(_qcache(kb)), ctypes.byref(_qcache(vb)),
+            0, tends, te_max, rot, R, 32, None, None, 0, None, None, 0, 0.0, FAKE, K.KVQ_F16,
+            FAKE * 16, wsb, None)
+    assert dec(4, 2, tends=None) == K.KVQ_ERR_INVALID_ARG
+    assert dec(4, 2, tends=FAKE + 1) == K.KVQ_ERR_INVALID_ARG
+    assert dec(2, 3) == K.KVQ_ERR_INVALID_ARG
+    assert dec(4, 2, te_max=65) == K.KVQ_ERR_INVALID_ARG                 # beyond T_cap
+    assert dec(1, 2, rot=K.KVQ_ROT_DENSE, R=FAKE) == K.KVQ_ERR_UNSUPPORTED
+    assert dec(4, 4, wsb=100) == K.KVQ_ERR_WORKSPACE_TOO_SMALL
+
+
+def _pcache(n_pages=4, page_tokens=128, bits=2):
+    return K.kvq_paged_cache(FAKE, FAKE, FAKE, n_pages, page_tokens, bits)
 
 
 def test_paged_rejects(lib):
@@ -261,11 +288,15 @@ def test_paged_rejects(lib):
     assert dec(tends=None) == K.KVQ_ERR_INVALID_ARG
     assert dec(te_max=513) == K.KVQ_ERR_INVALID_ARG                      # beyond 4 pages x 128
     assert dec(wsb=100) == K.KVQ_ERR_WORKSPACE_TOO_SMALL
+    assert dec(kc=_pcache(bits=3)) == K.KVQ_ERR_INVALID_ARG              # no 3-bit codes
+    assert dec(vc=_pcache(bits=0)) == K.KVQ_ERR_INVALID_ARG
 
-    def quant(dt=K.KVQ_F16, rot=K.KVQ_ROT_HADAMARD, offs=FAKE, R=None):
+    def quant(dt=K.KVQ_F16, rot=K.KVQ_ROT_HADAMARD, offs=FAKE, R=None, kb=2, vb=2):
         return lib.kvq_quantize_paged(FAKE, FAKE, dt, 1, 8, 2, 128, 8 * 2 * 128, 2 * 128, 128,
-                                      rot, R, 32, offs, FAKE, 4, ctypes.byref(_pcache()),
-                                      ctypes.byref(_pcache()), None)
+                                      rot, R, 32, offs, FAKE, 4, ctypes.byref(_pcache(bits=kb)),
+                                      ctypes.byref(_pcache(bits=vb)), None)
+    assert quant(kb=4, vb=8) == K.KVQ_ERR_INVALID_ARG
+    assert quant(kb=1, dt=K.KVQ_F32) == K.KVQ_ERR_UNSUPPORTED
     assert quant(offs=None) == K.KVQ_ERR_INVALID_ARG
     assert quant(dt=K.KVQ_F32) == K.KVQ_ERR_UNSUPPORTED
     assert quant(rot=K.KVQ_ROT_NONE) == K.KVQ_ERR_UNSUPPORTED

@@ -688,6 +688,117 @@ def test_decode_bits(kbits, vbits, rot, cid, G):
     assert err <= ATTN_TOL
 
 
+@pytest.mark.parametrize("kbits,vbits,rot,cid,G,P", [
+    (4, 2, "hadamard", 2, 1, 128), (1, 4, "perm", 2, 2, 64), (2, 1, "hadamard", 5, 1, 64)])
+def test_decode_bits_varlen_paged(kbits, vbits, rot, cid, G, P):
+    """b-bit decode with per-sequence ends, over a contiguous cache
+    (kvq_decode_attention_varlen_bits) and over a paged one (block table
+    over a shuffled pool): each sequence against the oracle on the same
+    rows, and the two layouts against each other.  Ends: the full range,
+    a ragged one and one just past the first tile."""
+    T = 768
+    cfg = W.small_config(W.config(cid), T=T, B=3, Hkv=2, Hq=2 * G)
+    rng = np.random.default_rng(300 + kbits * 10 + vbits)
+    perm = W.channel_orders(cfg) if rot == "perm" else None
+    Rm = rot_matrix(rot, perm)
+    kh = W.kv_tokens(cfg, "K").permute(0, 2, 1, 3).contiguous().numpy()
+    vh = W.kv_tokens(cfg, "V").permute(0, 2, 1, 3).contiguous().numpy()
+    kcache = O.quantize_cache(kh, Rm, bits=kbits)
+    vcache = O.quantize_cache(vh, Rm, bits=vbits)
+    table, n_pages = _page_layout(rng, cfg.B, T, P)
+    te_max = T - cfg.n_res
+    tb = cfg.n_sink if cfg.n_sink else 5
+    ends = np.array([te_max, tb + 1 + int(rng.integers(0, te_max - tb - 1)), tb + 64 + 3], np.int32)
+    fp16 = {}
+    if cfg.n_sink or cfg.n_res:
+        fp16 = dict(sink_k=np.ascontiguousarray(kh[:, :, :cfg.n_sink]).astype(np.float16),
+                    sink_v=np.ascontiguousarray(vh[:, :, :cfg.n_sink]).astype(np.float16),
+                    res_k=np.ascontiguousarray(kh[:, :, T - cfg.n_res:]).astype(np.float16),
+                    res_v=np.ascontiguousarray(vh[:, :, T - cfg.n_res:]).astype(np.float16))
+    up = {k: torch.from_numpy(v).to(DEV) for k, v in fp16.items()}
+    kp = kvq.PagedCache(*[torch.from_numpy(a).to(DEV) for a in _to_pages(kcache, table, n_pages, P)])
+    vp = kvq.PagedCache(*[torch.from_numpy(a).to(DEV) for a in _to_pages(vcache, table, n_pages, P)])
+    assert (kp.bits, vp.bits) == (kbits, vbits)
+    q = W.queries(cfg)
+    tends = torch.from_numpy(ends).to(DEV)
+    Rg = _rot_arg(rot, perm)
+    out = kvq.kvq_decode_attention_paged(q.to(DEV), kp, vp, tb, tends, te_max,
+                                         torch.from_numpy(table).to(DEV), rot=rot, R=Rg, **up)
+    flat = kvq.kvq_decode_attention(q.to(DEV), cache_from_numpy(*kcache), cache_from_numpy(*vcache),
+                                    tb, te_max, rot=rot, R=Rg, t_ends=tends, **up)
+    torch.cuda.synchronize()
+    out, flat = out.float().cpu().numpy(), flat.float().cpu().numpy()
+    worst = worst_flat = 0.0
+    for b in range(cfg.B):
+        sl = lambda c: tuple(a[b:b + 1] for a in c)
+        kwb = {k: v[b:b + 1] for k, v in fp16.items()}
+        ref = O.decode_attention(q.numpy()[b:b + 1], sl(kcache), sl(vcache), tb, int(ends[b]), Rm, **kwb)
+        worst = max(worst, normwise_rel_err(out[b:b + 1], ref))
+        worst_flat = max(worst_flat, normwise_rel_err(flat[b:b + 1], ref))
+    err = normwise_rel_err(out, flat)
+    _report(f"decode bits varlen/paged K{kbits}V{vbits} {rot} c{cid} G={G} P={P}",
+            paged=worst, contiguous=worst_flat, paged_vs_contiguous=err)
+    assert worst <= ATTN_TOL and worst_flat <= ATTN_TOL and err <= 1e-3
+
+
+@pytest.mark.parametrize("kbits,vbits,rot,Hkv,P", [(4, 2, "hadamard", 4, 128), (1, 4, "perm", 3, 64)])
+def test_quantize_bits_varlen_paged(kbits, vbits, rot, Hkv, P):
+    """b-bit writes at per-sequence slots: the contiguous write
+    (kvq_quantize_at_bits) against the oracle's codec at rounding ties, with
+    the slots outside each sequence's rows left untouched; the paged write
+    of the same rows bit for bit equal to it, and nothing else in the pool
+    touched."""
+    cfg = W.small_config(W.config(2), B=3, T=150, Hkv=Hkv, Hq=Hkv)
+    perm = W.channel_orders(cfg) if rot == "perm" else None
+    Rm = rot_matrix(rot, perm)
+    Rg = _rot_arg(rot, perm)
+    rng = np.random.default_rng(9)
+    T_cap = 4 * P
+    table, n_pages = _page_layout(rng, cfg.B, T_cap, P)
+    offs = np.array([0, 37, P - 20], np.int32)
+    toffs = torch.from_numpy(offs).to(DEV)
+    K, V = W.kv_tokens(cfg, "K"), W.kv_tokens(cfg, "V")
+    kc = empty_cache(cfg.B, Hkv, T_cap, bits=kbits)
+    vc = empty_cache(cfg.B, Hkv, T_cap, bits=vbits)
+    kvq.kvq_quantize(K.to(DEV), V.to(DEV), kc, vc, rot=rot, R=Rg, t_offsets=toffs)
+    pk = kvq.PagedCache.empty(n_pages, Hkv, P, bits=kbits)
+    pv = kvq.PagedCache.empty(n_pages, Hkv, P, bits=vbits)
+    for c in (pk, pv):
+        for t in (c.codes, c.scales.view(torch.uint8), c.zeros.view(torch.uint8)):
+            t.fill_(SENTINEL)
+    kvq.kvq_quantize_paged(K.to(DEV), V.to(DEV), pk, pv, toffs, torch.from_numpy(table).to(DEV),
+                           rot=rot, R=Rg)
+    torch.cuda.synchronize()
+    tot = dict(elements=0, code_mismatch=0, group_scale_zero_diff=0)
+    for x, c, p_c, bits in ((K, kc, pk, kbits), (V, vc, pv, vbits)):
+        fc, pc = cache_to_numpy(c), cache_to_numpy(p_c)
+        xh = x.permute(0, 2, 1, 3).contiguous().numpy()
+        ora = O.quantize_cache(xh, Rm, bits=bits)
+        written = np.zeros((n_pages, P), bool)
+        for b in range(cfg.B):
+            o = int(offs[b])
+            for arr in (fc[0], fc[1].view(np.uint8), fc[2].view(np.uint8)):
+                assert np.all(arr[b, :, :o] == SENTINEL) and np.all(arr[b, :, o + cfg.T:] == SENTINEL)
+            for h in range(Hkv):
+                Rh = Rm if rot != "perm" else Rm[h]
+                st = compare_codes_at_ties(xh[b:b + 1, h], Rh,
+                                           tuple(a[b:b + 1, h, o:o + cfg.T] for a in fc),
+                                           tuple(a[b:b + 1, h] for a in ora), max_frac=1.0, bits=bits)
+                for k in tot:
+                    tot[k] += st[k]
+            for t in range(cfg.T):
+                slot = o + t
+                page = int(table[b, slot // P])
+                written[page, slot % P] = True
+                for a_p, a_f in zip(pc, fc):
+                    assert np.array_equal(a_p[page, :, slot % P].view(np.uint8),
+                                          a_f[b, :, slot].view(np.uint8))
+        for a_p in pc:
+            assert np.all(np.moveaxis(a_p.view(np.uint8), 1, 2)[~written] == SENTINEL)
+    _report(f"quantize bits varlen/paged K{kbits}V{vbits} {rot} P={P}", **tot)
+    assert tot["code_mismatch"] <= 1e-5 * tot["elements"]
+
+
 @pytest.mark.parametrize("B,Hq", [(64, 1), (70, 1), (67, 4), (130, 1)])
 def test_decode_varlen_many_sequences(B, Hq):
     """Variable-length batches of many sequences with a skewed length mix:
