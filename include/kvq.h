@@ -115,7 +115,7 @@ typedef struct {
  * above for codes `bits` wide (1, 2 or 4; 2 is the INT2 format).  A block
  * table int32 [B][max_pages] (device) maps sequence b's token t to row
  * t % page_tokens of page table[b][t / page_tokens]; page_tokens must be a
- * multiple of 64.  Serving stacks keep caches in such pages (the pages name
+ * multiple of 64, and max_pages * page_tokens below 2^31.  Serving stacks keep caches in such pages (the pages name
  * serving stacks as the setting: OptR page, "Why It Matters"). */
 typedef struct {
   uint8_t *codes;

@@ -63,7 +63,7 @@ kvq_status check_paged(const kvq_paged_cache *kc, const kvq_paged_cache *vc, con
     if (np >= 0 && (c->n_pages != np || c->page_tokens != pt)) return KVQ_ERR_INVALID_ARG;
     np = c->n_pages;
     pt = c->page_tokens;
-    if (max_pages > ((int64_t)1 << 40) / pt) return KVQ_ERR_INVALID_ARG;
+    if (max_pages > (int64_t)0x7FFFFFFF / pt) return KVQ_ERR_INVALID_ARG;   // < 2^31 tokens per sequence
     qs[i]->codes = c->codes; qs[i]->scales = c->scales; qs[i]->zeros = c->zeros;
     qs[i]->T_cap = max_pages * c->page_tokens;
     qs[i]->bits = c->bits;

@@ -486,9 +486,8 @@ __global__ __launch_bounds__(64 * WPB) void kv_int2_decode_attn(AttnArgs a) {
   // are wave-uniform, lane offsets 32-bit.
   const uint32_t oc = (uint32_t)(ts * kCodeBytes + 16 * h);
   const uint32_t os = (uint32_t)(ts * kNGroups + 2 * h);
-  auto load_tile = [&](int64_t first_row) {
+  auto load_tile = [&](const TileRows &tr) {
     TileRegs r;
-    const TileRows tr = tile_rows(a, b, hkv, krow0, vrow0, first_row);
     const uint8_t *kct = a.kcodes + tr.k * kCodeBytes, *vct = a.vcodes + tr.v * kCodeBytes;
     const uint16_t *kst = a.kscales + tr.k * kNGroups, *kzt = a.kzeros + tr.k * kNGroups;
     const uint16_t *vst = a.vscales + tr.v * kNGroups, *vzt = a.vzeros + tr.v * kNGroups;
@@ -511,7 +510,15 @@ __global__ __launch_bounds__(64 * WPB) void kv_int2_decode_attn(AttnArgs a) {
   // computed the loads of tiles i+1 and i+2 are in flight.  A prefetch past
   // the wave's last tile is clamped to it (a re-read of valid rows, unused).
   if (mine > 0) {
-    auto at = [&](int64_t i) { return ht.full_row(i, split, S); };
+    PagedTileRows pages;
+    auto at = [&](int64_t i) {
+      if (a.block_table == nullptr) {
+        const int64_t r = ht.full_row(i, split, S);
+        return TileRows{krow0 + r, vrow0 + r};
+      }
+      const int64_t r = pages.row(a, b, hkv, ht, split, S, i);
+      return TileRows{r, r};
+    };
     TileRegs r0 = load_tile(at(0)), r1 = load_tile(at(1)), r2;
     int64_t i = 0;
     for (; i + 3 <= mine; i += 3) {

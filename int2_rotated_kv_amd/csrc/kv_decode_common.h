@@ -48,10 +48,12 @@ struct TileRows {
 __device__ __forceinline__ TileRows tile_rows(const AttnArgs &a, int64_t b, int hkv, int64_t krow0,
                                               int64_t vrow0, int64_t r0) {
   if (a.block_table == nullptr) return TileRows{krow0 + r0, vrow0 + r0};
-  const int64_t t = a.t_begin - a.skip + r0;
-  int64_t page = a.block_table[b * a.max_pages + t / a.page_tokens];
+  // a sequence holds fewer than 2^31 tokens (max_pages * page_tokens)
+  const uint32_t t = (uint32_t)(a.t_begin - a.skip + r0), P = (uint32_t)a.page_tokens;
+  const uint32_t pi = t / P;
+  int64_t page = a.block_table[b * a.max_pages + pi];
   page = (page >= 0 && page < a.n_pages) ? page : 0;
-  const int64_t row = (page * a.Hkv + hkv) * a.page_tokens + t % a.page_tokens;
+  const int64_t row = (page * a.Hkv + hkv) * a.page_tokens + (t - pi * P);
   return TileRows{row, row};
 }
 
@@ -369,6 +371,31 @@ struct HeadTiles {
     t0 = (skip > 0 && split == 0) ? 0 : -1;
     t1 = ((n_tok & 63) != 0 && n_full_end % S == split) ? n_full_end : -1;
     if (t1 == t0) t1 = -1;                         // one tile that is both
+  }
+};
+
+// First rows of a wave's full tiles in a paged cache, fetched 64 tiles at a
+// time: lane j holds the row of full tile 64 blk + j (low and high dwords),
+// so a tile's row is two lane reads instead of a table load and a division
+// in front of the tile's loads.  row(i) takes wave-uniform i, clamped to the
+// wave's last full tile as HeadTiles::full_row does.
+struct PagedTileRows {
+  int64_t blk = -1;
+  uint32_t lo = 0, hi = 0;
+  __device__ __forceinline__ int64_t row(const AttnArgs &a, int64_t b, int hkv, const HeadTiles &ht,
+                                         int64_t split, int64_t S, int64_t i) {
+    const int64_t ic = i < ht.mine - 1 ? i : ht.mine - 1;
+    if ((ic >> 6) != blk) {                          // wave-uniform
+      blk = ic >> 6;
+      const int64_t j = (blk << 6) + (threadIdx.x & 63);
+      const int64_t r = j < ht.mine ? tile_rows(a, b, hkv, 0, 0, ht.full_row(j, split, S)).k : 0;
+      lo = (uint32_t)r;
+      hi = (uint32_t)((uint64_t)r >> 32);
+    }
+    const int l = (int)(ic & 63);
+    const uint32_t rl = (uint32_t)__builtin_amdgcn_readlane((int)lo, l);
+    const uint32_t rh = (uint32_t)__builtin_amdgcn_readlane((int)hi, l);
+    return (int64_t)(((uint64_t)rh << 32) | rl);
   }
 };
 

@@ -251,13 +251,22 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
   const HeadTiles ht(seq_int2(a, b), a.skip, split, S);
   if (ht.mine > 0) {
     // a tile's rows follow its first row (one page holds the whole tile)
-    const TileRows t0 = tile_rows(a, b, hkv, krow0, vrow0, ht.full_row(0, split, S));
+    PagedTileRows pages;
+    auto full_rows = [&](int64_t i) {
+      if (a.block_table == nullptr) {
+        const int64_t r = ht.full_row(i, split, S);
+        return TileRows{krow0 + r, vrow0 + r};
+      }
+      const int64_t r = pages.row(a, b, hkv, ht, split, S, i);
+      return TileRows{r, r};
+    };
+    const TileRows t0 = full_rows(0);
     GenRow<KB> kr = gen_load<KB>(a.kcodes, a.kscales, a.kzeros, t0.k + lane);
     GenRow<VB> vr = gen_load<VB>(a.vcodes, a.vscales, a.vzeros, t0.v + lane);
     for (int64_t i = 0; i < ht.mine; ++i) {
       // the next tile's rows are loaded while this one is computed (the
       // last prefetch re-reads the wave's last tile)
-      const TileRows tn = tile_rows(a, b, hkv, krow0, vrow0, ht.full_row(i + 1, split, S));
+      const TileRows tn = full_rows(i + 1);
       const GenRow<KB> kn = gen_load<KB>(a.kcodes, a.kscales, a.kzeros, tn.k + lane);
       const GenRow<VB> vn = gen_load<VB>(a.vcodes, a.vscales, a.vzeros, tn.v + lane);
       token(kr, vr, true);

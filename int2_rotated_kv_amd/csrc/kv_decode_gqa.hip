@@ -241,9 +241,8 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
   const uint32_t o_kc = (uint32_t)(tk * kCodeBytes + 8 * kgrp);
   const uint32_t o_sz = (uint32_t)(lane * kNGroups);
   const uint32_t o_vc = (uint32_t)(16 * lane);
-  auto load_full = [&](int64_t r0) {
+  auto load_full = [&](const TileRows &tr) {
     MqTile t;
-    const TileRows tr = tile_rows(a, b, hkv, krow0, vrow0, r0);
     const uint8_t *kct = a.kcodes + tr.k * kCodeBytes, *vct = a.vcodes + tr.v * kCodeBytes;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
@@ -406,7 +405,15 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
   const HeadTiles ht(seq_int2(a, b), a.skip, split, S);
   const int64_t mine = ht.mine;
   if (mine > 0) {
-    auto row_of = [&](int64_t i) { return ht.full_row(i, split, S); };
+    PagedTileRows pages;
+    auto row_of = [&](int64_t i) {
+      if (a.block_table == nullptr) {
+        const int64_t r = ht.full_row(i, split, S);
+        return TileRows{krow0 + r, vrow0 + r};
+      }
+      const int64_t r = pages.row(a, b, hkv, ht, split, S, i);
+      return TileRows{r, r};
+    };
     MqTile t0 = load_full(row_of(0)), t1;
     int64_t i = 0;
     for (; i + 2 <= mine; i += 2) {

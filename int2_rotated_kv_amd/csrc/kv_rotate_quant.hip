@@ -470,16 +470,18 @@ __device__ __forceinline__ void fwht_f16_body(const RowsKernelArgs &a) {
   int64_t tile_page = -1;
   if (HG == 4 && a.block_table != nullptr) {
     const int64_t first = slot0 + lo;                // the tile's first written slot
-    if (lo < hi) tile_page = a.block_table[b * a.max_pages + first / a.page_tokens];
+    if (lo < hi) tile_page = a.block_table[b * a.max_pages + (uint32_t)first / (uint32_t)a.page_tokens];
   }
-  // cache row of token tk of the tile, head h0 + g; -1 when a paged slot's
-  // page index is outside the cache (the row is not written)
+  // cache row of token tk in [lo, hi) of the tile, head h0 + g; -1 when a
+  // paged slot's page index is outside the cache (the row is not written).
+  // A paged slot is below max_pages * page_tokens < 2^31.
   auto row_of = [&](int g, int64_t tk) -> int64_t {
     const int64_t slot = slot0 + tk;
     if (a.block_table == nullptr) return (b * a.Hkv + h0 + g) * s.T_cap + slot;
-    const int64_t page = HG == 4 ? tile_page : a.block_table[b * a.max_pages + slot / a.page_tokens];
+    const uint32_t sl = (uint32_t)slot, P = (uint32_t)a.page_tokens, pi = sl / P;
+    const int64_t page = HG == 4 ? tile_page : a.block_table[b * a.max_pages + pi];
     if (page < 0 || page >= a.n_pages) return -1;
-    return (page * a.Hkv + h0 + g) * a.page_tokens + slot % a.page_tokens;
+    return (page * a.Hkv + h0 + g) * a.page_tokens + (sl - pi * P);
   };
 
   // lane (n, q): stage row r(g) = 16g + n for HG = 1, 4n + g for HG = 4
