@@ -40,29 +40,35 @@ def _head_slice_cpu(cfg, which, b, h, t0=0, t1=None):
     return W.kv_tokens(cfg, which, b0=b, b1=b + 1, h0=h, h1=h + 1, t0=t0, t1=t1)[0, :, 0]
 
 
+def _contiguous_head(c, b, hk):
+    """(codes, scales, zeros) of head (b, hk) of a contiguous cache side, [T, ...]."""
+    return tuple(a[b, hk] for a in (c.codes, c.scales, c.zeros))
+
+
 def _check_head(cfg, Kd, Vd, ck, cv, out, q, b, hk, rot, R, t_begin, t_end,
-                sink=None, res=None, code_end=None):
+                sink=None, res=None, code_end=None, head_rows=_contiguous_head):
     """Codes of head (b, hk) vs oracle at ties (rows [t_begin, code_end),
     default t_end); decode of its query heads over [t_begin, t_end) vs the
-    oracle on the GPU codes.  Each cache side is read at its own width."""
+    oracle on the GPU codes.  Each cache side is read at its own width;
+    head_rows(side, b, hk) gives the head's rows in token order."""
     code_end = t_end if code_end is None else code_end
+    kh, vh = head_rows(ck, b, hk), head_rows(cv, b, hk)
     Rm = rot_matrix(rot, R)
     Rh = Rm if rot != "dense" else Rm[hk]
     stats = {}
-    for which, xd, c in (("K", Kd, ck), ("V", Vd, cv)):
+    for which, xd, c, rows in (("K", Kd, ck, kh), ("V", Vd, cv, vh)):
         x_cpu = _head_slice_cpu(cfg, which, b, hk)
         x_dev = xd[b, :, hk].cpu()
         assert torch.equal(x_cpu, x_dev), "generator differs between CPU and GPU"
         xr = x_cpu[t_begin:code_end].numpy()[None]             # [1, T, d]
-        gpu = tuple(a[b, hk, t_begin:code_end].cpu().numpy()[None]
-                    for a in (c.codes, c.scales, c.zeros))
+        gpu = tuple(a[t_begin:code_end].cpu().numpy()[None] for a in rows)
         ora = O.quantize_cache(xr[:, None], Rh, bits=c.bits)
         ora = tuple(a[:, 0] for a in ora)
         stats[which] = compare_codes_at_ties(xr, Rh, gpu, ora, bits=c.bits)
     G = cfg.G
     hq = slice(hk * G, hk * G + G)
-    kc = tuple(a[b:b + 1, hk:hk + 1].cpu().numpy() for a in (ck.codes, ck.scales, ck.zeros))
-    vc = tuple(a[b:b + 1, hk:hk + 1].cpu().numpy() for a in (cv.codes, cv.scales, cv.zeros))
+    kc = tuple(a.cpu().numpy()[None, None] for a in kh)
+    vc = tuple(a.cpu().numpy()[None, None] for a in vh)
     kw = {}
     if sink is not None:
         kw.update(sink_k=sink[0][b:b + 1, hk:hk + 1].cpu().numpy(),
@@ -179,3 +185,48 @@ def test_fullsize_config3_varlen():
                              code_end=64)
         _report(f"c3 varlen b={b} end={int(ends[b])} h={hk}", normwise=err)
         assert err <= ATTN_TOL
+
+
+def test_fullsize_config5_paged():
+    """LLaMA-2-13B shapes in a paged cache of 128-token pages over a pool
+    shuffled per sequence (the table bench.py --config 5 --paged 128 draws):
+    the paged write, then the paged decode with sinks and residual tokens;
+    sampled heads gathered back through the table against the oracle."""
+    cfg = W.config(5)
+    B, T, H, d = cfg.B, cfg.T, cfg.Hkv, cfg.d
+    P = 128
+    tb, te = cfg.int2_range
+    per = (T + P - 1) // P
+    pool = np.random.default_rng(np.random.SeedSequence([2000 + cfg.cid, P])).permutation(B * per)
+    table_h = pool.reshape(B, per).astype(np.int32)
+    table = torch.from_numpy(table_h).to(DEV)
+    K = W.kv_tokens(cfg, "K", device=DEV)
+    V = W.kv_tokens(cfg, "V", device=DEV)
+    q = W.queries(cfg, device=DEV)
+    ck, cv = kvq.PagedCache.empty(B * per, H, P), kvq.PagedCache.empty(B * per, H, P)
+    offs = torch.full((B,), tb, dtype=torch.int32, device=DEV)
+    kvq.kvq_quantize_paged(K[:, tb:te], V[:, tb:te], ck, cv, offs, table, rot="hadamard")
+    sink = tuple(x[:, :tb].permute(0, 2, 1, 3).contiguous() for x in (K, V))
+    res = tuple(x[:, te:].permute(0, 2, 1, 3).contiguous() for x in (K, V))
+    ends = torch.full((B,), te, dtype=torch.int32, device=DEV)
+    out = kvq.kvq_decode_attention_paged(q, ck, cv, tb, ends, te, table, rot="hadamard",
+                                         sink_k=sink[0], sink_v=sink[1], res_k=res[0], res_v=res[1])
+    # the sinks take most of the weight on these inputs, so the INT2 rows
+    # are also checked on their own
+    out_int2 = kvq.kvq_decode_attention_paged(q, ck, cv, tb, ends, te, table, rot="hadamard")
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(out_int2.float()).all()
+    t = torch.arange(T, device=DEV)
+
+    def paged_head(c, b, hk):
+        pages = table[b][t // P].long()
+        return tuple(a[pages, hk, t % P] for a in (c.codes, c.scales, c.zeros))
+
+    for b, hk in ((0, 0), (6, 33)):
+        stats, err = _check_head(cfg, K, V, ck, cv, out, q, b, hk, "hadamard", None, tb, te,
+                                 sink=sink, res=res, head_rows=paged_head)
+        _, err2 = _check_head(cfg, K, V, ck, cv, out_int2, q, b, hk, "hadamard", None, tb, te,
+                              head_rows=paged_head)
+        _report(f"c5 paged P={P} b={b} h={hk}", normwise_full=err, normwise_int2_only=err2,
+                K=stats["K"], V=stats["V"])
+        assert err <= ATTN_TOL and err2 <= ATTN_TOL
