@@ -167,8 +167,6 @@ def main():
         workload += "_varlen"
     kbits, vbits = args.kbits, args.vbits
     if (kbits, vbits) != (2, 2):
-        if rot == "dense":
-            sys.exit("--kbits/--vbits other than 2 need a Hadamard workload (--config 3 or 5)")
         workload += f"_k{kbits}v{vbits}"
     P = args.paged
     if P:
@@ -324,7 +322,7 @@ def main():
     q_kernel, q_src = {"dense": ("kv_rotate_quant_dense", "kv_rotate_quant_dense.hip"),
                        "perm": ("kv_rotate_quant_fwht_perm_f16", "kv_rotate_quant.hip")}.get(
                            rot, ("kv_rotate_quant_fwht_f16", "kv_rotate_quant.hip"))
-    if (kbits, vbits) != (2, 2):
+    if (kbits, vbits) != (2, 2) and rot != "dense":
         stem = "kv_rotate_quant_fwht_perm" if rot == "perm" else "kv_rotate_quant_fwht"
         names = [f"{stem}_f16" if b == 2 else f"{stem}_b{b}_f16" for b in (kbits, vbits)]
         q_kernel = names[0] if kbits == vbits else " + ".join(names)
@@ -341,7 +339,7 @@ def main():
     prep_kernel = cfg.G > 1 or rot in ("dense", "perm")
     if (kbits, vbits) != (2, 2):                   # the b-bit kernel prepares its query itself
         d_kernel, d_src = f"kv_quant_decode_attn<{kbits},{vbits}>", "kv_decode_generic.hip"
-        prep_kernel = False
+        prep_kernel = rot == "dense"                 # except a dense R's
     roof_d = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
               "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
               "traffic": traffic_from_profile(d_kernel, workload, os.path.join(csrc, d_src)),

@@ -138,9 +138,8 @@ kvq_status quantize_impl(const void *K, const void *V, kvq_dtype in_dtype, int64
     q.zeros = cs[s]->zeros;
     q.T_cap = cs[s]->T_cap;
     q.bits = cs[s]->bits;
-    // 1- and 4-bit codes: fp16 rows with the (reordered) Hadamard rotation
-    if (q.bits != 2 && (in_dtype != KVQ_F16 || !(rot == KVQ_ROT_HADAMARD || rot == KVQ_ROT_PERM_HADAMARD)))
-      return KVQ_ERR_UNSUPPORTED;
+    // 1- and 4-bit codes: fp16 rows with a Hadamard (plain or reordered) or dense rotation
+    if (q.bits != 2 && (in_dtype != KVQ_F16 || rot == KVQ_ROT_NONE)) return KVQ_ERR_UNSUPPORTED;
   }
   if (B * a.n_sides > 65535 || Hkv > 65535 || (T_new + 63) / 64 * Hkv > 0x7FFFFFFF)
     return KVQ_ERR_UNSUPPORTED;
@@ -238,8 +237,6 @@ kvq_status decode_impl(const void *q, kvq_dtype q_dtype, int64_t B, int64_t Hq,
     if ((st = check_cache(kc)) != KVQ_OK) return st;
     if ((st = check_cache(vc)) != KVQ_OK) return st;
     if (t_end > kc->T_cap || t_end > vc->T_cap) return KVQ_ERR_INVALID_ARG;
-    // 1- and 4-bit caches: the b-bit kernel, which has no dense rotation
-    if ((kc->bits != 2 || vc->bits != 2) && rot == KVQ_ROT_DENSE) return KVQ_ERR_UNSUPPORTED;
   }
   if (n_sink < 0 || n_res < 0) return KVQ_ERR_INVALID_ARG;
   if (n_sink > 0 && (sink_k == nullptr || sink_v == nullptr || !aligned16(sink_k) || !aligned16(sink_v)))

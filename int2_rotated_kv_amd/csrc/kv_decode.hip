@@ -899,7 +899,8 @@ hipError_t launch_decode(const DecodeArgs &d, hipStream_t stream) {
   const bool fused_prep = G == 1 && (d.rot == 0 || d.rot == 1);
   // other code widths: the b-bit kernel, which prepares its query itself
   const bool generic = d.kbits != 2 || d.vbits != 2;
-  if (!generic && !fused_prep && d.n_splits > 0) {
+  // the b-bit kernel takes a dense R's query from the preparation launch
+  if (((!generic && !fused_prep) || (generic && d.rot == 2)) && d.n_splits > 0) {
     PrepArgs p;
     p.q = d.q; p.q_f32 = d.q_f32; p.Hq = (int)d.Hq; p.Hkv = (int)d.Hkv;
     p.rot = d.rot; p.R = d.R; p.perm = d.perm; p.qscale = d.qscale;

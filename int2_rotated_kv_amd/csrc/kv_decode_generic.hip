@@ -9,7 +9,8 @@
 // query rotated by R and the output un-rotated by R^T in the combine).
 //
 // One wave per (batch, query head, split).  The wave rotates and scales its
-// query itself (none, Hadamard or reordered Hadamard) and keeps it in LDS as
+// query itself (none, Hadamard or reordered Hadamard; a dense R comes from
+// the query preparation launch as a fixed point) and keeps it in LDS as
 // a 19-bit fixed point in five 4-bit limbs, laid out in the nibble order of
 // the key codes.  Every 64-token tile gives one token to each lane: the lane
 // scores its token with v_dot8_i32_i4 on the key codes, the wave shares a
@@ -128,6 +129,15 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
 
   // ---- query: q' = qscale * q R, lane l holding channels 2l and 2l + 1
   {
+    int q0i, q1i;
+    if (a.rot == 2) {
+      // dense R: the query preparation launch has written the fixed point
+      // (same exponent rule as below) and its step
+      const int32_t *qp = reinterpret_cast<const int32_t *>(a.qprep) + (b * a.Hq + hq) * kQprepDwordsPerHead;
+      q0i = qp[kQprepFixedOffset + 2 * lane];
+      q1i = qp[kQprepFixedOffset + 2 * lane + 1];
+      qstep = bits_as_float((uint32_t)qp[25]);
+    } else {
     const int64_t qoff = (b * a.Hq + hq) * kD;
     int c0 = 2 * lane, c1 = 2 * lane + 1;
     if (a.rot == 3) {                                // (q_pi)_j = q[pi(j)]
@@ -168,8 +178,9 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
     // amax = m 2^e with m in [0.5, 1): E = 18 - e puts amax 2^E in [2^17, 2^18)
     const int E = amax > 0.0f ? 18 - __builtin_amdgcn_frexp_expf(amax) : 0;
     qstep = __builtin_amdgcn_ldexpf(1.0f, -E);
-    int q0i = (int)__builtin_rintf(__builtin_amdgcn_ldexpf(x0, E));
-    int q1i = (int)__builtin_rintf(__builtin_amdgcn_ldexpf(x1, E));
+    q0i = (int)__builtin_rintf(__builtin_amdgcn_ldexpf(x0, E));
+    q1i = (int)__builtin_rintf(__builtin_amdgcn_ldexpf(x1, E));
+    }
     float gs = (float)q0i + (float)q1i;               // group g = lane / 16, exact
     uint8_t(*qn)[kD] = qn_all[wave];
 #pragma unroll

@@ -1,7 +1,8 @@
 // Write path with a dense per-head rotation (OptR style: one learned
 // orthogonal matrix per head, "Output-Aware Rotation for INT2 KV-Cache
 // Quantization", woor.ai page, "Key Details"): y = x R_h, then the same
-// 2-bit group quantizer as the Hadamard path.
+// group quantizer as the Hadamard path, at 2 bits per code or at the
+// library's other widths (1 and 4 bits).
 //
 // The 128x128 contraction over many tokens runs on the matrix cores.
 // Computing y^T = R^T x^T with v_mfma_f32_32x32x16_f16 puts one token per
@@ -32,10 +33,10 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 constexpr int kDenseTiles = 4;                 // 32-token tiles per iteration
 constexpr int kDenseSlots = kDenseTiles * 32 * 16;        // 16-byte input chunks per iteration
 constexpr int kDenseLoadsPerThread = kDenseSlots / 256;
-// output staging per iteration: codes [tile][32 rows][32 B], then scales and
-// zeros [tile][32 rows][8 B] each
-constexpr int kDenseOutCodes = kDenseTiles * 32 * kCodeBytes;
-constexpr int kDenseOutBytes = kDenseOutCodes + 2 * kDenseTiles * 32 * 8;
+// output staging per iteration: codes [tile][32 rows][16 b B], then scales
+// and zeros [tile][32 rows][8 B] each
+constexpr int dense_out_codes(int bits) { return kDenseTiles * 32 * 16 * bits; }
+constexpr int dense_out_bytes(int bits) { return dense_out_codes(bits) + 2 * kDenseTiles * 32 * 8; }
 constexpr int64_t kDenseTargetBlocks = 512;   // 256 CUs x 2 workgroups
 constexpr int64_t kDenseMinItemsPerBlock = 16;
 
@@ -95,12 +96,15 @@ __device__ __forceinline__ float pair_max(float v) {
 
 // Quantize the 16 values this lane holds of one group; the partner lane
 // (lane ^ 32) holds the other 16.  y[r] is channel 8(r/4) + 4*half + r%4 of
-// the group, so y[4q .. 4q+3] are the four codes of group byte 2q + half.
-// Returns the group's 8 code bytes (w0: bytes 0..3, w1: bytes 4..7) and its
-// scale / zero bits, identical in both lanes of the pair.
-__device__ __forceinline__ void dense_group_codes(const float16_t &y, uint32_t &w0, uint32_t &w1,
+// the group.  Returns the group's 4 BITS code bytes in w (dword k = bytes
+// 4k .. 4k+3) and its scale / zero bits, identical in both lanes of the pair.
+// At 2 bits y[4q .. 4q+3] are the four codes of group byte 2q + half.
+template <int BITS>
+__device__ __forceinline__ void dense_group_codes(const float16_t &y, uint32_t (&w)[BITS],
                                                   uint16_t &sbits, uint16_t &zbits) {
 #pragma clang fp contract(off)
+  constexpr int L = (1 << BITS) - 1;
+  constexpr float inv_levels = BITS == 1 ? 1.0f : BITS == 2 ? 0.3333333432674408f : 0.06666667014360428f;
   float mn = y[0], mx = y[0];
 #pragma unroll
   for (int r = 1; r < 16; ++r) {
@@ -110,8 +114,8 @@ __device__ __forceinline__ void dense_group_codes(const float16_t &y, uint32_t &
   mn = pair_min(mn);
   mx = pair_max(mx);
   // The rotated path is compared at rounding ties with one fp16 ulp of slack
-  // on a group's scale, so s = range * fp32(1/3) and 1/scale = v_rcp_f32.
-  const float s32 = (mx - mn) * 0.3333333432674408f;
+  // on a group's scale, so s = range * fp32(1/L) and 1/scale = v_rcp_f32.
+  const float s32 = (mx - mn) * inv_levels;
   sbits = float_to_half_bits(s32);
   zbits = float_to_half_bits(mn + 0.0f);
   const float sf = half_bits_to_float(sbits);
@@ -122,12 +126,48 @@ __device__ __forceinline__ void dense_group_codes(const float16_t &y, uint32_t &
   // Two instructions per code while every group of the wave has
   // |zero| <= 8 scale and a normal fp16 scale: x = y/scale - zero/scale in
   // one FMA, then v_cvt_pk_u8_f32 (round half to even, saturating below 0)
-  // into byte r/4 of word r%4; the words merge into the 2-bit layout.  x is
-  // then within 0.006 of (y - min)/(range/3), which lies in [0, 3], so it
-  // rounds to a code in [0, 3] with no clamp.  Otherwise (or for a zero
-  // scale) the sequence below keeps y - zero to one rounding.
+  // into byte r/4 of word r%4; the words merge into the b-bit layout.  x is
+  // then within (L + 8) 2^-11 of (y - min)/(range/L), which lies in [0, L],
+  // so it rounds to a code in [0, L] with no clamp.  Otherwise (or for a
+  // zero scale) the sequence below keeps y - zero to one rounding.
+  const bool fast = !__builtin_amdgcn_ballot_w64(fabsf(nzi) > 8.0f || sf < kMinNormalHalf);
+  if constexpr (BITS != 2) {
+    // D[e] byte q = code of the lane's channel 8q + 4 half + e
+    uint32_t D[4] = {0u, 0u, 0u, 0u};
+    if (fast) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        D[r & 3] = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(y[r], inv, nzi), (uint32_t)(r >> 2), D[r & 3]);
+    } else {
+      const float top = (float)L * sf;               // exact: sf has 11 significant bits
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float d = __builtin_amdgcn_fmed3f(y[r] - zf, 0.0f, top);
+        D[r & 3] |= (float_as_bits(__builtin_fmaf(d, inv, kDenseRoundMagic)) - 0x4B400000u) << (8 * (r >> 2));
+      }
+    }
+    if constexpr (BITS == 1) {
+      // channel 8q + 4 half + e is bit 4 half + e of group byte q
+      const uint32_t mine = D[0] | (D[1] << 1) | (D[2] << 2) | (D[3] << 3);
+      const auto ex = __builtin_amdgcn_permlane32_swap(mine, mine, false, false);
+      w[0] = ex[0] | (ex[1] << 4);
+    } else {
+      // channel 8q + 4 half + e is nibble e % 2 of group byte 4q + 2 half + e / 2
+      const uint32_t a = D[0] | (D[1] << 4), c = D[2] | (D[3] << 4);
+      const auto ea = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+      const auto ec = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // bytes 4q .. 4q+3: lower half's (a, c) byte q, then the upper half's
+        const uint32_t lo = __builtin_amdgcn_perm(ec[0], ea[0], (uint32_t)(q | (q + 4) << 8) | 0x0C0C0000u);
+        const uint32_t hi = __builtin_amdgcn_perm(ec[1], ea[1], 0x0C0Cu | (uint32_t)(q << 16 | (q + 4) << 24));
+        w[q] = lo | hi;
+      }
+    }
+    return;
+  }
   uint32_t mine;
-  if (!__builtin_amdgcn_ballot_w64(fabsf(nzi) > 8.0f || sf < kMinNormalHalf)) {
+  if (fast) {
     uint32_t D[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -145,15 +185,20 @@ __device__ __forceinline__ void dense_group_codes(const float16_t &y, uint32_t &
   }
   const auto ex = __builtin_amdgcn_permlane32_swap(mine, mine, false, false);
   const uint32_t e = ex[0], o = ex[1];          // bytes of the lower / upper half
-  w0 = __builtin_amdgcn_perm(o, e, 0x05010400u);   // e0 o0 e1 o1
-  w1 = __builtin_amdgcn_perm(o, e, 0x07030602u);   // e2 o2 e3 o3
+  w[0] = __builtin_amdgcn_perm(o, e, 0x05010400u);   // e0 o0 e1 o1
+  w[BITS - 1] = __builtin_amdgcn_perm(o, e, 0x07030602u);   // e2 o2 e3 o3
 }
 
 // grid: x = chunk of items, y = KV head, z = batch; 256 threads = four
 // waves, one per quantization group.
+// At 4 bits the output staging (2 x 10 KiB) leaves room for one workgroup
+// per CU instead of two.
+template <int BITS>
 __global__ __launch_bounds__(256, 2) void kv_rotate_quant_dense(DenseKernelArgs a) {
+  constexpr int kOutCodes = dense_out_codes(BITS);
+  constexpr int kRowBytes = 16 * BITS;
   __shared__ u32x4_t xs[2][kDenseSlots];      // 2 x 32 KiB of staged inputs
-  __shared__ __attribute__((aligned(16))) uint8_t out[2][kDenseOutBytes];   // 2 x 6 KiB of output rows
+  __shared__ __attribute__((aligned(16))) uint8_t out[2][dense_out_bytes(BITS)];   // 2 x (4 + 2 b) KiB of output rows
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int g = __builtin_amdgcn_readfirstlane(tid >> 6);   // this wave's group
@@ -206,20 +251,21 @@ __global__ __launch_bounds__(256, 2) void kv_rotate_quant_dense(DenseKernelArgs 
     for (int c = 0; c < kDenseLoadsPerThread; ++c) xs[buf][c * 256 + tid] = P[c];
   };
 
-  // Output rows of iteration k (from LDS buffer ob) go to the cache: thread
-  // tid stores 16 code bytes (64 threads per tile = 32 rows x 32 bytes) and 8
-  // bytes of scales (tid < 128) or zeros.
+  // Output rows of iteration k (from LDS buffer ob) go to the cache: 16-byte
+  // code chunk c (piece c % BITS of row (c / BITS) % 32 of tile c / (32 BITS))
+  // from thread c % 256, and 8 bytes of scales (tid < 128) or zeros.
   auto store_out = [&](int64_t k, const uint8_t *ob) {
-    {
-      const int u = tid >> 6, r = (tid & 63) >> 1;
+#pragma unroll
+    for (int c = tid; c < kOutCodes / 16; c += 256) {
+      const int u = c / (32 * BITS), r = (c % (32 * BITS)) / BITS, piece = c % BITS;
       const int64_t it = i0 + k * kDenseTiles + u;
       const QuantSide sd = (it & side_shift) ? a.side[1] : a.side[0];
       const int64_t t = (it >> side_shift) * 32 + r;
       const int64_t slot = seq_offset(a.offsets, a.t_offset, b) + t;
       if (it < i1 && t < a.T_new && slot >= 0 && slot < sd.T_cap) {   // per-sequence slot inside the cache
         const int64_t row = (b * a.Hkv + h) * sd.T_cap + slot;
-        __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t *>(ob + 16 * tid),
-                                    reinterpret_cast<u32x4_t *>(sd.codes + row * kCodeBytes) + (tid & 1));
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t *>(ob + 16 * c),
+                                    reinterpret_cast<u32x4_t *>(sd.codes + row * kRowBytes) + piece);
       }
     }
     {
@@ -232,7 +278,7 @@ __global__ __launch_bounds__(256, 2) void kv_rotate_quant_dense(DenseKernelArgs 
         const int64_t row = (b * a.Hkv + h) * sd.T_cap + slot;
         uint16_t *dst = zs ? sd.zeros : sd.scales;
         __builtin_nontemporal_store(
-            *reinterpret_cast<const u32x2_t *>(ob + kDenseOutCodes + zs * kDenseTiles * 256 + (u * 32 + r) * 8),
+            *reinterpret_cast<const u32x2_t *>(ob + kOutCodes + zs * kDenseTiles * 256 + (u * 32 + r) * 8),
             reinterpret_cast<u32x2_t *>(dst + row * kNGroups));
       }
     }
@@ -268,11 +314,20 @@ __global__ __launch_bounds__(256, 2) void kv_rotate_quant_dense(DenseKernelArgs 
     // the zero
 #pragma unroll
     for (int u = 0; u < kDenseTiles; ++u) {
-      uint32_t w0, w1;
+      uint32_t w[BITS];
       uint16_t sb, zb;
-      dense_group_codes(acc[u], w0, w1, sb, zb);
-      *reinterpret_cast<uint32_t *>(ob + (u * 32 + j) * kCodeBytes + 8 * g + 4 * half) = half ? w1 : w0;
-      *reinterpret_cast<uint16_t *>(ob + kDenseOutCodes + half * kDenseTiles * 256 + (u * 32 + j) * 8 + 2 * g) =
+      dense_group_codes<BITS>(acc[u], w, sb, zb);
+      // group g's 4 BITS code bytes: each half of the lane pair writes half
+      // of them (at 1 bit, the lower half writes the one dword)
+      uint8_t *gc = ob + (u * 32 + j) * kRowBytes + 4 * BITS * g;
+      if constexpr (BITS == 4) {
+        *reinterpret_cast<u32x2_t *>(gc + 8 * half) = half ? u32x2_t{w[2], w[3]} : u32x2_t{w[0], w[1]};
+      } else if constexpr (BITS == 2) {
+        *reinterpret_cast<uint32_t *>(gc + 4 * half) = half ? w[1] : w[0];
+      } else {
+        if (half == 0) *reinterpret_cast<uint32_t *>(gc) = w[0];
+      }
+      *reinterpret_cast<uint16_t *>(ob + kOutCodes + half * kDenseTiles * 256 + (u * 32 + j) * 8 + 2 * g) =
           half ? zb : sb;
     }
     // Loads are waited for before the stores are issued: those waits also
@@ -298,7 +353,8 @@ __global__ __launch_bounds__(256, 2) void kv_rotate_quant_dense(DenseKernelArgs 
   store_out(n_iter - 1, out[(n_iter - 1) & 1]);      // published by the last barrier
 }
 
-hipError_t launch_quantize_dense(const QuantArgs &q, hipStream_t stream) {
+// Both sides at one code width.
+static hipError_t launch_quantize_dense_one(const QuantArgs &q, hipStream_t stream) {
   DenseKernelArgs a;
   a.side[0] = q.side[0];
   a.side[1] = q.n_sides > 1 ? q.side[1] : q.side[0];
@@ -321,8 +377,27 @@ hipError_t launch_quantize_dense(const QuantArgs &q, hipStream_t stream) {
   a.items_per_block = (a.n_items + chunks - 1) / chunks;
   chunks = (a.n_items + a.items_per_block - 1) / a.items_per_block;
   dim3 grid((unsigned)chunks, (unsigned)q.Hkv, (unsigned)q.B);
-  hipLaunchKernelGGL(kv_rotate_quant_dense, grid, dim3(256), 0, stream, a);
+  switch (a.side[0].bits) {
+    case 1: hipLaunchKernelGGL(kv_rotate_quant_dense<1>, grid, dim3(256), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(kv_rotate_quant_dense<4>, grid, dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL(kv_rotate_quant_dense<2>, grid, dim3(256), 0, stream, a); break;
+  }
   return hipGetLastError();
+}
+
+hipError_t launch_quantize_dense(const QuantArgs &q, hipStream_t stream) {
+  // sides of different code widths: one launch each
+  if (q.n_sides == 2 && q.side[0].bits != q.side[1].bits) {
+    for (int sd = 0; sd < 2; ++sd) {
+      QuantArgs q1 = q;
+      q1.side[0] = q.side[sd];
+      q1.n_sides = 1;
+      const hipError_t e = launch_quantize_dense_one(q1, stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  return launch_quantize_dense_one(q, stream);
 }
 
 }  // namespace kvq

@@ -224,7 +224,8 @@ def test_quantize_bits_rejects(lib):
     assert call(2, 8) == K.KVQ_ERR_INVALID_ARG
     assert call(4, 2, dt=K.KVQ_F32) == K.KVQ_ERR_UNSUPPORTED    # fp32 rows at 4 bits
     assert call(2, 1, rot=K.KVQ_ROT_NONE) == K.KVQ_ERR_UNSUPPORTED
-    assert call(4, 4, rot=K.KVQ_ROT_DENSE, R=FAKE) == K.KVQ_ERR_UNSUPPORTED
+    assert call(4, 4, dt=K.KVQ_F32, rot=K.KVQ_ROT_DENSE, R=FAKE) == K.KVQ_ERR_UNSUPPORTED
+    assert call(4, 4, rot=K.KVQ_ROT_DENSE, R=None) == K.KVQ_ERR_INVALID_ARG   # dense needs R
     assert call(4, 2, rot=K.KVQ_ROT_PERM_HADAMARD) == K.KVQ_ERR_INVALID_ARG   # no channel order
 
 
@@ -236,7 +237,7 @@ def test_decode_bits_rejects(lib):
             FAKE * 16, wsb, None)
     assert call(3, 2) == K.KVQ_ERR_INVALID_ARG
     assert call(4, 0) == K.KVQ_ERR_INVALID_ARG
-    assert call(4, 2, rot=K.KVQ_ROT_DENSE, R=FAKE) == K.KVQ_ERR_UNSUPPORTED   # no dense R at 4 bits
+    assert call(4, 2, rot=K.KVQ_ROT_DENSE, R=None) == K.KVQ_ERR_INVALID_ARG   # dense needs R
     assert call(1, 4, wsb=100) == K.KVQ_ERR_WORKSPACE_TOO_SMALL
 
 
@@ -263,7 +264,7 @@ def test_varlen_bits_rejects(lib):
     assert dec(4, 2, tends=FAKE + 1) == K.KVQ_ERR_INVALID_ARG
     assert dec(2, 3) == K.KVQ_ERR_INVALID_ARG
     assert dec(4, 2, te_max=65) == K.KVQ_ERR_INVALID_ARG                 # beyond T_cap
-    assert dec(1, 2, rot=K.KVQ_ROT_DENSE, R=FAKE) == K.KVQ_ERR_UNSUPPORTED
+    assert dec(1, 2, rot=K.KVQ_ROT_PERM_HADAMARD, R=None) == K.KVQ_ERR_INVALID_ARG   # no channel order
     assert dec(4, 4, wsb=100) == K.KVQ_ERR_WORKSPACE_TOO_SMALL
 
 

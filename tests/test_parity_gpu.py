@@ -616,14 +616,16 @@ def test_quantize_paged(rot, Hkv, P):
 
 # ------------------------------------------------ other code widths (1, 4 bits)
 @pytest.mark.parametrize("kbits,vbits,rot", [(4, 2, "hadamard"), (1, 4, "hadamard"), (4, 4, "perm"),
-                                             (1, 1, "perm")])
+                                             (1, 1, "perm"), (4, 2, "dense"), (1, 4, "dense"),
+                                             (4, 4, "dense")])
 def test_quantize_bits_ties(kbits, vbits, rot):
     """b-bit write path (keys and values at their own widths): codes, fp16
     scales and zeros against the oracle's b-bit codec, compared at rounding
     ties as for 2 bits; a ragged token count at an offset, so the first 9
     slots and the rows past T_new keep their sentinel bytes."""
     cfg = W.small_config(W.config(2), B=2, T=700, Hkv=3, Hq=3)
-    perm = W.channel_orders(cfg) if rot == "perm" else None
+    perm = (W.channel_orders(cfg) if rot == "perm" else
+            W.dense_rotations(cfg) if rot == "dense" else None)
     Rm = rot_matrix(rot, perm)
     K = W.kv_tokens(cfg, "K")
     V = W.kv_tokens(cfg, "V")
@@ -641,7 +643,7 @@ def test_quantize_bits_ties(kbits, vbits, rot):
         xh = x.permute(0, 2, 1, 3).contiguous().numpy()
         ora = O.quantize_cache(xh, Rm, bits=bits)
         for h in range(cfg.Hkv):
-            Rh = Rm if rot != "perm" else Rm[h]
+            Rh = Rm[h] if rot in ("perm", "dense") else Rm
             st = compare_codes_at_ties(xh[:, h], Rh, tuple(a[:, h, 9:9 + cfg.T] for a in (gp, gs, gz)),
                                        tuple(a[:, h] for a in ora), max_frac=1.0, bits=bits)
             for k in tot:
@@ -653,7 +655,8 @@ def test_quantize_bits_ties(kbits, vbits, rot):
 @pytest.mark.parametrize("kbits,vbits,rot,cid,G", [
     (4, 2, "hadamard", 2, 1), (2, 4, "hadamard", 2, 1), (1, 1, "hadamard", 2, 1),
     (4, 4, "hadamard", 2, 1), (1, 2, "none", 1, 1), (4, 2, "perm", 2, 1),
-    (4, 2, "hadamard", 2, 4), (4, 2, "hadamard", 5, 1), (2, 1, "hadamard", 1, 2)])
+    (4, 2, "hadamard", 2, 4), (4, 2, "hadamard", 5, 1), (2, 1, "hadamard", 1, 2),
+    (4, 2, "dense", 4, 4), (1, 4, "dense", 4, 1)])
 def test_decode_bits(kbits, vbits, rot, cid, G):
     """b-bit decode (the kernel for widths other than 2/2) against the
     oracle on the same cache bytes: keys and values at their own widths,
@@ -661,8 +664,10 @@ def test_decode_bits(kbits, vbits, rot, cid, G):
     residual tokens (LLaMA-2-13B recipe), a ragged INT2 range that starts
     inside a tile and spans several tiles and splits."""
     T = 900
-    cfg = W.small_config(W.config(cid), T=T, B=2, Hkv=2, Hq=2 * G)
-    perm = W.channel_orders(cfg) if rot == "perm" else None
+    extra = dict(t_new=0) if cid == 4 else {}
+    cfg = W.small_config(W.config(cid), T=T, B=2, Hkv=2, Hq=2 * G, **extra)
+    perm = (W.channel_orders(cfg) if rot == "perm" else
+            W.dense_rotations(cfg) if rot == "dense" else None)
     Rm = rot_matrix(rot, perm)
     K = W.kv_tokens(cfg, "K")
     V = W.kv_tokens(cfg, "V")
@@ -689,7 +694,8 @@ def test_decode_bits(kbits, vbits, rot, cid, G):
 
 
 @pytest.mark.parametrize("kbits,vbits,rot,cid,G,P", [
-    (4, 2, "hadamard", 2, 1, 128), (1, 4, "perm", 2, 2, 64), (2, 1, "hadamard", 5, 1, 64)])
+    (4, 2, "hadamard", 2, 1, 128), (1, 4, "perm", 2, 2, 64), (2, 1, "hadamard", 5, 1, 64),
+    (4, 1, "dense", 4, 4, 64)])
 def test_decode_bits_varlen_paged(kbits, vbits, rot, cid, G, P):
     """b-bit decode with per-sequence ends, over a contiguous cache
     (kvq_decode_attention_varlen_bits) and over a paged one (block table
@@ -697,9 +703,11 @@ def test_decode_bits_varlen_paged(kbits, vbits, rot, cid, G, P):
     rows, and the two layouts against each other.  Ends: the full range,
     a ragged one and one just past the first tile."""
     T = 768
-    cfg = W.small_config(W.config(cid), T=T, B=3, Hkv=2, Hq=2 * G)
+    extra = dict(t_new=0) if cid == 4 else {}
+    cfg = W.small_config(W.config(cid), T=T, B=3, Hkv=2, Hq=2 * G, **extra)
     rng = np.random.default_rng(300 + kbits * 10 + vbits)
-    perm = W.channel_orders(cfg) if rot == "perm" else None
+    perm = (W.channel_orders(cfg) if rot == "perm" else
+            W.dense_rotations(cfg) if rot == "dense" else None)
     Rm = rot_matrix(rot, perm)
     kh = W.kv_tokens(cfg, "K").permute(0, 2, 1, 3).contiguous().numpy()
     vh = W.kv_tokens(cfg, "V").permute(0, 2, 1, 3).contiguous().numpy()
