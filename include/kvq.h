@@ -253,9 +253,10 @@ kvq_status kvq_decode_attention_varlen(const void *q, kvq_dtype q_dtype,
  * kvq_quantize_bits -- kvq_quantize into caches of any supported code width
  * (kvq_quant_cache; keys and values may differ).  With both sides at 2 bits
  * it is kvq_quantize.  A side at 1 or 4 bits needs in_dtype == KVQ_F16 and
- * rot KVQ_ROT_HADAMARD or KVQ_ROT_PERM_HADAMARD (else KVQ_ERR_UNSUPPORTED);
- * bits outside {1, 2, 4} give KVQ_ERR_INVALID_ARG.  Every other argument
- * as for kvq_quantize.  Mixed-bit caches: OptR page, future-work paragraph.
+ * a rotation: KVQ_ROT_HADAMARD, KVQ_ROT_PERM_HADAMARD or KVQ_ROT_DENSE
+ * (KVQ_ROT_NONE gives KVQ_ERR_UNSUPPORTED); bits outside {1, 2, 4} give
+ * KVQ_ERR_INVALID_ARG.  Every other argument as for kvq_quantize.
+ * Mixed-bit caches: OptR page, future-work paragraph.
  */
 kvq_status kvq_quantize_bits(const void *K, const void *V, kvq_dtype in_dtype,
                              int64_t B, int64_t T_new, int64_t Hkv, int64_t d,
@@ -267,10 +268,10 @@ kvq_status kvq_quantize_bits(const void *K, const void *V, kvq_dtype in_dtype,
 /*
  * kvq_decode_attention_bits -- kvq_decode_attention over caches of any
  * supported code width (kvq_quant_cache; keys and values may differ).  With
- * both sides at 2 bits it is kvq_decode_attention.  Otherwise rot must be
- * KVQ_ROT_NONE, KVQ_ROT_HADAMARD or KVQ_ROT_PERM_HADAMARD (KVQ_ROT_DENSE
- * gives KVQ_ERR_UNSUPPORTED).  Workspace as for kvq_decode_attention
- * (kvq_decode_workspace_bytes); every other argument likewise.
+ * both sides at 2 bits it is kvq_decode_attention; otherwise a kernel for
+ * the other widths runs, with every rotation.  Workspace as for
+ * kvq_decode_attention (kvq_decode_workspace_bytes); every other argument
+ * likewise.
  */
 kvq_status kvq_decode_attention_bits(const void *q, kvq_dtype q_dtype,
                                      int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
