@@ -627,7 +627,7 @@ constexpr int kCombineWaves = kCombineThreads / 64;
 // load), kFpRows tokens per step across the block, kFpUnroll steps whose loads
 // are issued together.
 constexpr int kFpRows = kCombineThreads / 16;
-constexpr int kFpUnroll = 4;
+constexpr int kFpUnroll = 9;
 
 __device__ __forceinline__ float block_max(float v, float *red) {
   for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
