@@ -61,9 +61,9 @@ def _gpu_quantize(x_tok, rot, R=None, T_cap=None, t_offset=0, side="K"):
     return cache_to_numpy(c)
 
 
-def _oracle_quantize(x_tok, rot, R=None):
+def _oracle_quantize(x_tok, rot, R=None, bits=2):
     x = x_tok.permute(0, 2, 1, 3).contiguous().numpy()   # [B, H, T, d]
-    return O.quantize_cache(x, rot_matrix(rot, R))
+    return O.quantize_cache(x, rot_matrix(rot, R), bits=bits)
 
 
 def _outlier_rows(rng, shape, dtype):
@@ -860,11 +860,13 @@ def test_decode_varlen_many_sequences(B, Hq):
     assert worst_oracle <= ATTN_TOL
 
 
-@pytest.mark.parametrize("rot", ["none", "hadamard", "perm", "dense"])
-def test_quantize_at_per_sequence_slots(rot):
-    """kvq_quantize_at: each sequence's new rows land at its own slot;
-    rows whose slot falls outside [0, T_cap) are skipped and every other slot
-    keeps its sentinel bytes.  T_new = 1 (a decode-step append) and T_new = 5."""
+@pytest.mark.parametrize("rot,bits", [("none", 2), ("hadamard", 2), ("perm", 2), ("dense", 2),
+                                      ("dense", 1), ("dense", 4), ("perm", 4)])
+def test_quantize_at_per_sequence_slots(rot, bits):
+    """kvq_quantize_at (kvq_quantize_at_bits at 1 and 4 bits): each
+    sequence's new rows land at its own slot; rows whose slot falls outside
+    [0, T_cap) are skipped and every other slot keeps its sentinel bytes.
+    T_new = 1 (a decode-step append) and T_new = 5."""
     T_cap = 40
     cfg = W.small_config(W.config(2), B=4, T=5, Hkv=2, Hq=2)
     R = W.dense_rotations(cfg) if rot == "dense" else (
@@ -873,12 +875,12 @@ def test_quantize_at_per_sequence_slots(rot):
     Rm = rot_matrix(rot, R)
     for T_new, offs in ((1, [0, 17, 39, 25]), (5, [3, 37, -2, 20])):
         x = W.kv_tokens(cfg, "K")[:, :T_new]                      # [B, T_new, H, d] fp16
-        c = empty_cache(cfg.B, cfg.Hkv, T_cap)
+        c = empty_cache(cfg.B, cfg.Hkv, T_cap, bits=bits)
         offsets = torch.tensor(offs, dtype=torch.int32, device=DEV)
         kvq.kvq_quantize(x.to(DEV), None, c, None, rot=rot, R=_rot_arg(rot, R), t_offsets=offsets)
         torch.cuda.synchronize()
         gp, gs, gz = cache_to_numpy(c)
-        op, os_, oz = _oracle_quantize(x, rot, R)                 # [B, H, T_new, ...]
+        op, os_, oz = _oracle_quantize(x, rot, R, bits)           # [B, H, T_new, ...]
         xr = x.permute(0, 2, 1, 3).contiguous().numpy()
         for b in range(cfg.B):
             written = np.zeros(T_cap, bool)
@@ -897,10 +899,10 @@ def test_quantize_at_per_sequence_slots(rot):
                     for h in range(cfg.Hkv):
                         Rh = Rm[h] if (rot != "hadamard" and np.asarray(Rm).ndim == 3) else Rm
                         compare_codes_at_ties(xr[b, h, t:t + 1], Rh, tuple(a[h] for a in g),
-                                              tuple(a[h] for a in o), max_frac=1.0)
+                                              tuple(a[h] for a in o), max_frac=1.0, bits=bits)
             for arr in (gp, gs.view(np.uint8), gz.view(np.uint8)):
                 assert np.all(arr[b][:, ~written] == SENTINEL)
-        _report(f"quantize_at {rot} T_new={T_new}", offsets=offs)
+        _report(f"quantize_at {rot} bits={bits} T_new={T_new}", offsets=offs)
 
 
 # ---------------------------------------------------------- end to end
