@@ -230,3 +230,27 @@ def test_fullsize_config5_paged():
         _report(f"c5 paged P={P} b={b} h={hk}", normwise_full=err, normwise_int2_only=err2,
                 K=stats["K"], V=stats["V"])
         assert err <= ATTN_TOL and err2 <= ATTN_TOL
+
+
+def test_fullsize_config4_dense_gqa_key4_value2():
+    """GQA shapes with a dense R at 4-bit keys and 2-bit values (the dense
+    write kernel at two widths and the b-bit decode over the prepared dense
+    query, as bench.py --config 4 --kbits 4 --vbits 2 runs them)."""
+    cfg = W.config(4)
+    B, T, H, d = cfg.B, cfg.T, cfg.Hkv, cfg.d
+    R = W.dense_rotations(cfg)
+    Rg = torch.as_tensor(R, device=DEV).contiguous()
+    K = W.kv_tokens(cfg, "K", device=DEV)
+    V = W.kv_tokens(cfg, "V", device=DEV)
+    q = W.queries(cfg, device=DEV)
+    ck, cv = kvq.Int2Cache.empty(B, H, T, bits=4), kvq.Int2Cache.empty(B, H, T, bits=2)
+    p0, p1 = cfg.quant_range
+    kvq.kvq_quantize(K[:, :p0], V[:, :p0], ck, cv, rot="dense", R=Rg)
+    kvq.kvq_quantize(K[:, p0:p1], V[:, p0:p1], ck, cv, rot="dense", R=Rg, t_offset=p0)
+    out = kvq.kvq_decode_attention(q, ck, cv, 0, T, rot="dense", R=Rg)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    for b, hk in ((1, 2), (3, 7)):
+        stats, err = _check_head(cfg, K, V, ck, cv, out, q, b, hk, "dense", R, 0, T)
+        _report(f"c4 K4V2 b={b} h={hk}", normwise=err, K=stats["K"], V=stats["V"])
+        assert err <= ATTN_TOL
