@@ -807,13 +807,15 @@ def test_quantize_bits_varlen_paged(kbits, vbits, rot, Hkv, P):
     assert tot["code_mismatch"] <= 1e-5 * tot["elements"]
 
 
-@pytest.mark.parametrize("B,Hq", [(64, 1), (70, 1), (67, 4), (130, 1)])
-def test_decode_varlen_many_sequences(B, Hq):
+@pytest.mark.parametrize("B,Hq,kbits,vbits", [(64, 1, 2, 2), (70, 1, 2, 2), (67, 4, 2, 2), (130, 1, 2, 2),
+                                              (70, 1, 4, 2), (130, 2, 1, 4)])
+def test_decode_varlen_many_sequences(B, Hq, kbits, vbits):
     """Variable-length batches of many sequences with a skewed length mix:
     one sequence spans the whole range, the rest are short or empty.  The
     attention waves are shared among the sequences by tile count, so this
     covers batches of one wave's width (64) and wider ones, for one query
-    head per KV head and for a query group.
+    head per KV head and for a query group, and at other code widths (the
+    b-bit kernel takes the same wave map).
 
     Checks: (1) each sequence's output matches a one-sequence call over the
     same range (which other tests hold to the oracle), so every sequence
@@ -834,8 +836,8 @@ def test_decode_varlen_many_sequences(B, Hq):
     kh = K.permute(0, 2, 1, 3).contiguous().numpy()
     vh = V.permute(0, 2, 1, 3).contiguous().numpy()
     Rm = rot_matrix("hadamard", None)
-    kcache = O.quantize_cache(kh, Rm)
-    vcache = O.quantize_cache(vh, Rm)
+    kcache = O.quantize_cache(kh, Rm, bits=kbits)
+    vcache = O.quantize_cache(vh, Rm, bits=vbits)
     q = W.queries(cfg)
     out = kvq.kvq_decode_attention(q.to(DEV), cache_from_numpy(*kcache), cache_from_numpy(*vcache),
                                    tb, te_max, rot="hadamard", t_ends=torch.from_numpy(ends).to(DEV))
@@ -852,10 +854,11 @@ def test_decode_varlen_many_sequences(B, Hq):
         torch.cuda.synchronize()
         worst_single = max(worst_single, normwise_rel_err(out[b:b + 1], one.float().cpu().numpy()))
         ref = O.decode_attention(q.numpy()[b:b + 1], sl(kcache), sl(vcache), tb, int(ends[b]), Rm)
-        vrows = O.dequantize(O.unpack_codes(vcache[0][b, 0, tb:ends[b]]), vcache[1][b, 0, tb:ends[b]],
+        vrows = O.dequantize(O.unpack_codes(vcache[0][b, 0, tb:ends[b]], vbits), vcache[1][b, 0, tb:ends[b]],
                              vcache[2][b, 0, tb:ends[b]]) @ Rm.T          # attended rows, original basis
         worst_oracle = max(worst_oracle, float(np.abs(out[b] - ref[0]).max() / np.abs(vrows).max()))
-    _report(f"decode varlen B={B} Hq={Hq}", vs_single=worst_single, vs_oracle_value_scale=worst_oracle)
+    _report(f"decode varlen B={B} Hq={Hq} K{kbits}V{vbits}", vs_single=worst_single,
+            vs_oracle_value_scale=worst_oracle)
     assert worst_single <= 1e-4
     assert worst_oracle <= ATTN_TOL
 
