@@ -290,7 +290,9 @@ kvq_status kvq_decode_attention_bits(const void *q, kvq_dtype q_dtype,
 /*
  * kvq_quantize_at_bits -- kvq_quantize_at into caches of any supported code
  * width: the per-sequence slots of kvq_quantize_at with the caches and
- * width rules of kvq_quantize_bits.
+ * width rules of kvq_quantize_bits.  Mixed-bit caches (OptR page, the
+ * future-work paragraph) in the serving setting the pages name (OptR page,
+ * "Why It Matters").
  */
 kvq_status kvq_quantize_at_bits(const void *K, const void *V, kvq_dtype in_dtype,
                                 int64_t B, int64_t T_new, int64_t Hkv, int64_t d,
@@ -304,6 +306,7 @@ kvq_status kvq_quantize_at_bits(const void *K, const void *V, kvq_dtype in_dtype
  * caches of any supported code width: the per-sequence ends of
  * kvq_decode_attention_varlen with the caches and rotation rules of
  * kvq_decode_attention_bits.  Workspace as for kvq_decode_attention_varlen.
+ * Same sources as kvq_quantize_at_bits.
  */
 kvq_status kvq_decode_attention_varlen_bits(const void *q, kvq_dtype q_dtype,
                                             int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
