@@ -191,14 +191,16 @@ __device__ __forceinline__ void dense_group_codes(const float16_t &y, uint32_t (
 
 // grid: x = chunk of items, y = KV head, z = batch; 256 threads = four
 // waves, one per quantization group.
-// At 4 bits the output staging (2 x 10 KiB) leaves room for one workgroup
-// per CU instead of two.
+// At 4 bits two output buffers (2 x 10 KiB) would leave room for only one
+// workgroup per CU, so one buffer is used: an iteration's rows leave before
+// the next iteration's are staged, one barrier apart.
 template <int BITS>
 __global__ __launch_bounds__(256, 2) void kv_rotate_quant_dense(DenseKernelArgs a) {
   constexpr int kOutCodes = dense_out_codes(BITS);
   constexpr int kRowBytes = 16 * BITS;
+  constexpr int kOutBufs = BITS == 4 ? 1 : 2;
   __shared__ u32x4_t xs[2][kDenseSlots];      // 2 x 32 KiB of staged inputs
-  __shared__ __attribute__((aligned(16))) uint8_t out[2][dense_out_bytes(BITS)];   // 2 x (4 + 2 b) KiB of output rows
+  __shared__ __attribute__((aligned(16))) uint8_t out[kOutBufs][dense_out_bytes(BITS)];   // (4 + 2 b) KiB each
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int g = __builtin_amdgcn_readfirstlane(tid >> 6);   // this wave's group
@@ -343,14 +345,21 @@ __global__ __launch_bounds__(256, 2) void kv_rotate_quant_dense(DenseKernelArgs 
   for (int64_t k = 0; k < n_iter; ++k) {              // block-uniform trip count
     const bool more = k + 1 < n_iter;
     if (more) load_iter(k + 1, P);
+    if constexpr (kOutBufs == 1) {
+      // the previous iteration's rows leave before this one's are staged
+      if (k > 0) {
+        store_out(k - 1, out[0]);
+        __syncthreads();
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
     // buffers last read before the previous barrier: input (k+1)&1, output k&1
-    compute((int)(k & 1), out[k & 1],
+    compute((int)(k & 1), out[k & (kOutBufs - 1)],
             [&] { if (more) stage((int)((k + 1) & 1), P); },
-            [&] { if (k > 0) store_out(k - 1, out[(k - 1) & 1]); });
+            [&] { if (kOutBufs == 2 && k > 0) store_out(k - 1, out[(k - 1) & (kOutBufs - 1)]); });
     __syncthreads();
   }
-  store_out(n_iter - 1, out[(n_iter - 1) & 1]);      // published by the last barrier
+  store_out(n_iter - 1, out[(n_iter - 1) & (kOutBufs - 1)]);   // published by the last barrier
 }
 
 // Both sides at one code width.
