@@ -327,10 +327,10 @@ kvq_status kvq_decode_attention_varlen_bits(const void *q, kvq_dtype q_dtype,
  * T_new rows are its tokens t_offsets[b] .. t_offsets[b] + T_new - 1, each
  * written to its page through block_table.  A token outside
  * [0, max_pages * page_tokens), or whose page index is outside [0, n_pages),
- * is not written.  Needs in_dtype == KVQ_F16 and rot KVQ_ROT_HADAMARD or
- * KVQ_ROT_PERM_HADAMARD (else KVQ_ERR_UNSUPPORTED).  kc and vc (either may
- * be NULL with its input) must agree on n_pages and page_tokens; each has
- * its own bits (1, 2 or 4, else KVQ_ERR_INVALID_ARG).
+ * is not written.  Input rows, rotations and code widths follow the rules
+ * of kvq_quantize and kvq_quantize_bits.  kc and vc (either may be NULL with
+ * its input) must agree on n_pages and page_tokens; each has its own bits
+ * (1, 2 or 4, else KVQ_ERR_INVALID_ARG).
  */
 kvq_status kvq_quantize_paged(const void *K, const void *V, kvq_dtype in_dtype,
                               int64_t B, int64_t T_new, int64_t Hkv, int64_t d,

@@ -154,9 +154,6 @@ kvq_status quantize_impl(const void *K, const void *V, kvq_dtype in_dtype, int64
   a.R = rot == KVQ_ROT_DENSE ? static_cast<const float *>(R) : nullptr;
   a.perm = rot == KVQ_ROT_PERM_HADAMARD ? static_cast<const int32_t *>(R) : nullptr;
   if (pg != nullptr) {
-    // paged writes run the fp16 Hadamard kernels only
-    if (in_dtype != KVQ_F16 || !(rot == KVQ_ROT_HADAMARD || rot == KVQ_ROT_PERM_HADAMARD))
-      return KVQ_ERR_UNSUPPORTED;
     a.block_table = pg->block_table;
     a.max_pages = pg->max_pages; a.n_pages = pg->n_pages; a.page_tokens = pg->page_tokens;
   }

@@ -329,10 +329,12 @@ __global__ __launch_bounds__(256) void kv_rotate_quant_rows(RowsKernelArgs a) {
   }
   const int64_t slot = seq_offset(a.offsets, a.t_offset, b) + t;
   if (valid && slot >= 0 && slot < s.T_cap) {       // a per-sequence slot outside the cache is skipped
-    const int64_t row = (b * a.Hkv + h) * s.T_cap + slot;
-    *reinterpret_cast<uint2 *>(s.codes + row * kCodeBytes + 8 * j) = make_uint2(w0, w1);
-    s.scales[row * kNGroups + j] = sb;
-    s.zeros[row * kNGroups + j] = zb;
+    const int64_t row = write_row(a.block_table, a.max_pages, a.n_pages, a.page_tokens, a.Hkv, b, h, s.T_cap, slot);
+    if (row >= 0) {                                  // a page outside the pool is skipped
+      *reinterpret_cast<uint2 *>(s.codes + row * kCodeBytes + 8 * j) = make_uint2(w0, w1);
+      s.scales[row * kNGroups + j] = sb;
+      s.zeros[row * kNGroups + j] = zb;
+    }
   }
 }
 

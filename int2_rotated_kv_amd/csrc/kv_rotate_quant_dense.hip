@@ -61,6 +61,9 @@ struct DenseKernelArgs {
   int64_t items_per_block;
   const float *R;           // [Hkv][128][128], y = x R
   const int32_t *offsets;   // per-sequence first slot (device [B]) or NULL: t_offset
+  // paged cache: block_table[b * max_pages + t / page_tokens]; NULL: contiguous
+  const int32_t *block_table;
+  int64_t max_pages, n_pages, page_tokens;
 };
 
 // (x << SH) + acc in one instruction (v_lshl_add_u32, SH an inline constant).
@@ -265,9 +268,11 @@ __global__ __launch_bounds__(256, 2) void kv_rotate_quant_dense(DenseKernelArgs 
       const int64_t t = (it >> side_shift) * 32 + r;
       const int64_t slot = seq_offset(a.offsets, a.t_offset, b) + t;
       if (it < i1 && t < a.T_new && slot >= 0 && slot < sd.T_cap) {   // per-sequence slot inside the cache
-        const int64_t row = (b * a.Hkv + h) * sd.T_cap + slot;
-        __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t *>(ob + 16 * c),
-                                    reinterpret_cast<u32x4_t *>(sd.codes + row * kRowBytes) + piece);
+        const int64_t row = write_row(a.block_table, a.max_pages, a.n_pages, a.page_tokens, a.Hkv, b, h,
+                                      sd.T_cap, slot);
+        if (row >= 0)                                // a page outside the pool is skipped
+          __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t *>(ob + 16 * c),
+                                      reinterpret_cast<u32x4_t *>(sd.codes + row * kRowBytes) + piece);
       }
     }
     {
@@ -276,8 +281,11 @@ __global__ __launch_bounds__(256, 2) void kv_rotate_quant_dense(DenseKernelArgs 
       const QuantSide sd = (it & side_shift) ? a.side[1] : a.side[0];
       const int64_t t = (it >> side_shift) * 32 + r;
       const int64_t slot = seq_offset(a.offsets, a.t_offset, b) + t;
-      if (it < i1 && t < a.T_new && slot >= 0 && slot < sd.T_cap) {   // per-sequence slot inside the cache
-        const int64_t row = (b * a.Hkv + h) * sd.T_cap + slot;
+      const int64_t row = (it < i1 && t < a.T_new && slot >= 0 && slot < sd.T_cap)   // per-sequence slot inside the cache
+                              ? write_row(a.block_table, a.max_pages, a.n_pages, a.page_tokens, a.Hkv, b, h,
+                                          sd.T_cap, slot)
+                              : -1;
+      if (row >= 0) {
         uint16_t *dst = zs ? sd.zeros : sd.scales;
         __builtin_nontemporal_store(
             *reinterpret_cast<const u32x2_t *>(ob + kOutCodes + zs * kDenseTiles * 256 + (u * 32 + r) * 8),
@@ -373,6 +381,10 @@ static hipError_t launch_quantize_dense_one(const QuantArgs &q, hipStream_t stre
   a.T_new = q.T_new;
   a.t_offset = q.t_offset;
   a.offsets = q.offsets;
+  a.block_table = q.block_table;
+  a.max_pages = q.max_pages;
+  a.n_pages = q.n_pages;
+  a.page_tokens = q.page_tokens;
   a.Hkv = (int)q.Hkv;
   a.n_sides = q.n_sides;
   a.R = q.R;

@@ -37,6 +37,20 @@ __device__ __forceinline__ int64_t seq_offset(const int32_t *offsets, int64_t t_
   return offsets != nullptr ? (int64_t)offsets[b] : t_offset;
 }
 
+// Cache row of slot `slot` (in [0, T_cap)) of (batch b, KV head h) for a
+// write: (b*Hkv + h)*T_cap + slot, or through a block table (slot t of
+// sequence b is row t % P of page table[b*max_pages + t / P]; the slot is
+// below max_pages * P < 2^31), -1 when the page index is outside the pool.
+__device__ __forceinline__ int64_t write_row(const int32_t *table, int64_t max_pages, int64_t n_pages,
+                                             int64_t P, int Hkv, int64_t b, int h, int64_t T_cap,
+                                             int64_t slot) {
+  if (table == nullptr) return (b * Hkv + h) * T_cap + slot;
+  const uint32_t sl = (uint32_t)slot, p32 = (uint32_t)P, pi = sl / p32;
+  const int64_t page = table[b * max_pages + pi];
+  if (page < 0 || page >= n_pages) return -1;
+  return (page * Hkv + h) * P + (sl - pi * p32);
+}
+
 // Cross-lane moves inside a quad of four lanes (DPP quad_perm).
 // kQuadXor1: lane i reads lane i^1; kQuadXor2: lane i reads lane i^2.
 constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]

@@ -298,7 +298,9 @@ def test_paged_rejects(lib):
                                       ctypes.byref(_pcache(bits=vb)), None)
     assert quant(kb=4, vb=8) == K.KVQ_ERR_INVALID_ARG
     assert quant(kb=1, dt=K.KVQ_F32) == K.KVQ_ERR_UNSUPPORTED
+    assert quant(kb=4, rot=K.KVQ_ROT_NONE) == K.KVQ_ERR_UNSUPPORTED
     assert quant(offs=None) == K.KVQ_ERR_INVALID_ARG
-    assert quant(dt=K.KVQ_F32) == K.KVQ_ERR_UNSUPPORTED
-    assert quant(rot=K.KVQ_ROT_NONE) == K.KVQ_ERR_UNSUPPORTED
-    assert quant(rot=K.KVQ_ROT_DENSE, R=FAKE) == K.KVQ_ERR_UNSUPPORTED
+    # rows and rotations as for the contiguous caches
+    assert quant(dt=K.KVQ_F32, rot=K.KVQ_ROT_DENSE, R=FAKE) == K.KVQ_ERR_UNSUPPORTED
+    assert quant(dt=K.KVQ_F32, rot=K.KVQ_ROT_PERM_HADAMARD, R=FAKE) == K.KVQ_ERR_UNSUPPORTED
+    assert quant(rot=K.KVQ_ROT_DENSE, R=None) == K.KVQ_ERR_INVALID_ARG

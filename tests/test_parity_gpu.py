@@ -573,20 +573,26 @@ def test_decode_paged(cid, Hkv, Hq, rot, P, tb):
     assert worst <= ATTN_TOL and err_flat <= 1e-3
 
 
-@pytest.mark.parametrize("rot,Hkv,P", [("hadamard", 4, 128), ("perm", 3, 64)])
-def test_quantize_paged(rot, Hkv, P):
+@pytest.mark.parametrize("rot,Hkv,P,f32", [("hadamard", 4, 128, False), ("perm", 3, 64, False),
+                                           ("none", 2, 64, False), ("dense", 4, 128, False),
+                                           ("hadamard", 3, 64, True)])
+def test_quantize_paged(rot, Hkv, P, f32):
     """Paged decode-step appends and prefills: sequence b's rows at its own
     offset through the block table; pages not addressed keep their sentinel
     bytes, a table entry outside the pool drops its rows, and the written
-    rows gathered back match the contiguous per-sequence write."""
+    rows gathered back match the contiguous per-sequence write.  Every
+    write kernel: fp16 (reordered) Hadamard, no rotation, dense R, fp32 rows."""
     cfg = W.small_config(W.config(2), B=3, T=150, Hkv=Hkv, Hq=Hkv)
-    perm = W.channel_orders(cfg) if rot == "perm" else None
+    perm = (W.channel_orders(cfg) if rot == "perm" else
+            W.dense_rotations(cfg) if rot == "dense" else None)
     rng = np.random.default_rng(7)
     T_cap = 4 * P
     table, n_pages = _page_layout(rng, cfg.B, T_cap, P)
     table[2, 1] = n_pages + 5                       # out of the pool: those rows are dropped
     offs = np.array([0, 37, P - 20], np.int32)      # the last crosses into page 1
     K = W.kv_tokens(cfg, "K")
+    if f32:
+        K = K.float()
     kp = kvq.PagedCache.empty(n_pages, Hkv, P)
     for t in (kp.codes, kp.scales.view(torch.uint8), kp.zeros.view(torch.uint8)):
         t.fill_(SENTINEL)
@@ -610,7 +616,7 @@ def test_quantize_paged(rot, Hkv, P):
                 assert np.array_equal(a_p[page, :, slot % P].view(np.uint8), a_f[b, :, slot].view(np.uint8))
     for a_p in pc:                                   # nothing else was touched
         assert np.all(np.moveaxis(a_p.view(np.uint8), 1, 2)[~written] == SENTINEL)
-    _report(f"quantize paged {rot} P={P}", rows=int(written.sum()))
+    _report(f"quantize paged {rot}{' fp32' if f32 else ''} P={P}", rows=int(written.sum()))
     assert written.sum() < cfg.B * cfg.T             # the dropped page's rows are missing
 
 
@@ -749,7 +755,8 @@ def test_decode_bits_varlen_paged(kbits, vbits, rot, cid, G, P):
     assert worst <= ATTN_TOL and worst_flat <= ATTN_TOL and err <= 1e-3
 
 
-@pytest.mark.parametrize("kbits,vbits,rot,Hkv,P", [(4, 2, "hadamard", 4, 128), (1, 4, "perm", 3, 64)])
+@pytest.mark.parametrize("kbits,vbits,rot,Hkv,P", [(4, 2, "hadamard", 4, 128), (1, 4, "perm", 3, 64),
+                                                   (4, 1, "dense", 2, 64)])
 def test_quantize_bits_varlen_paged(kbits, vbits, rot, Hkv, P):
     """b-bit writes at per-sequence slots: the contiguous write
     (kvq_quantize_at_bits) against the oracle's codec at rounding ties, with
@@ -757,7 +764,8 @@ def test_quantize_bits_varlen_paged(kbits, vbits, rot, Hkv, P):
     of the same rows bit for bit equal to it, and nothing else in the pool
     touched."""
     cfg = W.small_config(W.config(2), B=3, T=150, Hkv=Hkv, Hq=Hkv)
-    perm = W.channel_orders(cfg) if rot == "perm" else None
+    perm = (W.channel_orders(cfg) if rot == "perm" else
+            W.dense_rotations(cfg) if rot == "dense" else None)
     Rm = rot_matrix(rot, perm)
     Rg = _rot_arg(rot, perm)
     rng = np.random.default_rng(9)
@@ -788,7 +796,7 @@ def test_quantize_bits_varlen_paged(kbits, vbits, rot, Hkv, P):
             for arr in (fc[0], fc[1].view(np.uint8), fc[2].view(np.uint8)):
                 assert np.all(arr[b, :, :o] == SENTINEL) and np.all(arr[b, :, o + cfg.T:] == SENTINEL)
             for h in range(Hkv):
-                Rh = Rm if rot != "perm" else Rm[h]
+                Rh = Rm[h] if rot in ("perm", "dense") else Rm
                 st = compare_codes_at_ties(xh[b:b + 1, h], Rh,
                                            tuple(a[b:b + 1, h, o:o + cfg.T] for a in fc),
                                            tuple(a[b:b + 1, h] for a in ora), max_frac=1.0, bits=bits)
