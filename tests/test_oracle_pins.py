@@ -195,6 +195,93 @@ def pin_pack_roundtrip(orc):
         assert sum(int(c[i]) << (2 * i) for i in range(4)) == b
 
 
+# ------------------------------------------------------- whole-cache write
+def _grid_rows(rng, shape):
+    """Grid data per group: z + j*s with j in 0..3 (levels 0 and 3 present
+    in every group), z and s fp16 with |z| >= 0.25 and s in [1/4, 1], so the
+    scale, zero and codes of such a row are z, s and j exactly, and a
+    perturbation of a few fp32 ulps changes none of them."""
+    *lead, d = shape
+    ng = d // 32
+    j = rng.integers(0, 4, size=(*lead, ng, 32))
+    j[..., 0], j[..., 1] = 0, 3
+    z = rng.choice([-1, 1], size=(*lead, ng)) * rng.uniform(0.25, 2.0, size=(*lead, ng))
+    z = z.astype(np.float16)
+    s = rng.uniform(0.25, 1.0, size=(*lead, ng)).astype(np.float16)
+    y = z.astype(np.float64)[..., None] + j * s.astype(np.float64)[..., None]
+    return y.reshape(*lead, d), j.reshape(*lead, d).astype(np.uint8), s, z
+
+
+def _pack_by_hand(codes):
+    """byte b = sum_i code[4b + i] << 2i, by explicit loops."""
+    *lead, d = codes.shape
+    flat = codes.reshape(-1, d)
+    out = np.zeros((flat.shape[0], d // 4), np.uint8)
+    for r in range(flat.shape[0]):
+        for b in range(d // 4):
+            out[r, b] = sum(int(flat[r, 4 * b + i]) << (2 * i) for i in range(4))
+    return out.reshape(*lead, d // 4)
+
+
+def pin_quantize_cache_per_head(orc):
+    """Whole-cache write with a different rotation per head (OptR page, Key
+    Details: one orthogonal rotation per head).  Rotated rows are chosen on
+    a grid per head, the inputs are x = y R_h^T, and the expected codes,
+    scales and zeros are the grid's own (codes packed by hand), for each of
+    three non-symmetric per-head rotations: a dense QR rotation, a reordered
+    Hadamard (permutation then scipy's Hadamard) and a signed permutation.
+    Using one head's rotation for another, the transposed rotation, or the
+    wrong head or batch slot gives different codes."""
+    rng = np.random.default_rng(41)
+    B, H, T, d = 2, 3, 5, 128
+    Hs = scipy.linalg.hadamard(d).astype(np.float64) / math.sqrt(d)
+    perm = rng.permutation(d)
+    Pm = np.zeros((d, d))
+    Pm[perm, np.arange(d)] = 1.0
+    sp = rng.permutation(d)
+    Sg = np.zeros((d, d))
+    Sg[sp, np.arange(d)] = rng.choice([-1.0, 1.0], size=d)
+    R = np.stack([_rand_orthogonal(rng, d), Pm @ Hs, Sg])
+    for h in range(H):
+        assert not np.allclose(R[h], R[h].T)
+    y, j, s, z = _grid_rows(rng, (B, H, T, d))
+    x = np.einsum("bhtc,hkc->bhtk", y, R).astype(np.float32)      # x = y R_h^T
+    packed, sc, zz = orc.quantize_cache(x, R)
+    assert packed.shape == (B, H, T, 32) and sc.shape == zz.shape == (B, H, T, 4)
+    assert np.array_equal(sc, s) and np.array_equal(zz, z)
+    assert np.array_equal(packed, _pack_by_hand(j))
+    # one shared [d, d] matrix is used for every head
+    y1, j1, s1, z1 = _grid_rows(rng, (1, H, 4, d))
+    x1 = (y1 @ R[1].T).astype(np.float32)
+    p1, sc1, zz1 = orc.quantize_cache(x1, R[1])
+    assert np.array_equal(p1, _pack_by_hand(j1)) and np.array_equal(sc1, s1) and np.array_equal(zz1, z1)
+
+
+def pin_tie_distance_dense(orc):
+    """tie_distance takes the exact argument (x R - zero)/scale with the
+    caller's R.  With a signed permutation R (non-symmetric) and rotated
+    values y = x R chosen by hand on one group with scale 1 and zero 0:
+    y = 0.5, 1.5, 2.5 sit at ties (distance 0), y = 0.75 and 2.25 at 0.25,
+    y = 1 and 3 at 0.5; a scale-0 group gives +inf."""
+    rng = np.random.default_rng(43)
+    d = 128
+    sp = rng.permutation(d)
+    R = np.zeros((d, d))
+    R[sp, np.arange(d)] = rng.choice([-1.0, 1.0], size=d)
+    assert not np.allclose(R, R.T)
+    y = np.zeros(d)
+    vals = [0.5, 1.5, 2.5, 0.75, 2.25, 1.0, 3.0]
+    want = [0.0, 0.0, 0.0, 0.25, 0.25, 0.5, 0.5]
+    y[:len(vals)] = vals
+    x = (y @ R.T)[None]                                  # exact: a signed permutation
+    scales = np.array([[1.0, 1.0, 0.0, 1.0]], np.float16)
+    zeros = np.zeros((1, 4), np.float16)
+    dist = orc.tie_distance(x, R, scales, zeros)
+    assert list(dist[0, :len(vals)]) == want
+    assert np.all(np.isinf(dist[0, 64:96]))
+    assert np.all(dist[0, 32:64] == 0.5)                 # y = 0 lies mid-way between ties
+
+
 # ------------------------------------------------------ other code widths
 def pin_quant_bits_grid(orc):
     """1- and 4-bit codes: grid data z + j*s, j in [0, 2**b - 1] with every
@@ -401,7 +488,7 @@ PINS = [
     pin_pack_golden, pin_pack_roundtrip,
     pin_decode_vs_sdpa, pin_decode_bruteforce, pin_decode_large_scores,
     pin_quant_bits_grid, pin_quant_bits_ramp, pin_quant_bits_nearest, pin_pack_bits,
-    pin_decode_mixed_widths,
+    pin_decode_mixed_widths, pin_quantize_cache_per_head, pin_tie_distance_dense,
 ]
 
 
@@ -496,6 +583,11 @@ MUTATIONS = [
      "kbits, vbits = 8 * vc.shape[-1] // d"),
     ("unpack mask fixed at 2 bits", "& qmax for i in range(per)", "& 3 for i in range(per)"),
     ("1-bit divisor 2", "qmax = levels(bits)\n    yg", "qmax = max(levels(bits), 2)\n    yg"),
+    ("head 0's rotation for every head", "R = _head_matrix(R_heads, h)\n        y = rotate_rows",
+     "R = _head_matrix(R_heads, 0)\n        y = rotate_rows"),
+    ("rows of the wrong head written", "y = rotate_rows(x[:, h], R)", "y = rotate_rows(x[:, H - 1 - h], R)"),
+    ("tie distance with R^T", "y64 = y64 @ np.asarray(R, dtype=np.float64)",
+     "y64 = y64 @ np.asarray(R, dtype=np.float64).T"),
 ]
 
 
