@@ -334,6 +334,149 @@ def decode_attention(q, kcache, vcache, t_begin, t_end, R_heads=None,
 
 
 # --------------------------------------------------------------------------
+# Pre-RoPE grouped-head rotation of the keys
+# --------------------------------------------------------------------------
+# RotateKV (IJCAI 2025 record, abstract item (ii)) rotates keys before the
+# rotary position embedding is applied and across a group of heads, to keep
+# RoPE from disturbing the outlier-aware rotation and to spread outliers
+# over heads.  The record fixes neither RoPE nor the grouping; the readings
+# used here:
+#   * RoPE is the rotate-half form: channel i pairs with i + d/2, pair i
+#     turns by the angle t * base**(-2i/d) at position t, base 10000;
+#   * an INT2 key's position is its cache slot t; the decode query comes in
+#     already position-embedded (post-RoPE), as a decode step produces it;
+#   * the grouped-head rotation concatenates the pre-RoPE key rows of g
+#     consecutive KV heads (head-major channels, head j of the group first
+#     at channels j*d .. j*d + d - 1) and applies the normalized Sylvester
+#     Hadamard matrix of size g*d; each head's d-channel slice of the result
+#     is one cache row, quantized like any other;
+#   * values carry no RoPE and keep the per-head Hadamard rotation;
+#   * fp16 sink / residual keys are kept as a plain fp16 cache would keep
+#     them: position-embedded, unrotated.
+ROPE_BASE = 10000.0
+
+
+def rope(x, positions, base: float = ROPE_BASE) -> np.ndarray:
+    """Rotary position embedding of rows x [..., T, d] at positions [T], in
+    fp64: for pair i (channels i and i + d/2) with angle a = t * base**(-2i/d),
+    (x_i, x_{i+d/2}) -> (x_i cos a - x_{i+d/2} sin a, x_{i+d/2} cos a + x_i sin a)."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    half = d // 2
+    theta = base ** (-2.0 * np.arange(half) / d)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * theta[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def grouped_hadamard_rotation(group_heads: int, d: int = D_HEAD) -> np.ndarray:
+    """The rotation over the channels of a group of g heads: the normalized
+    Sylvester Hadamard matrix of size g*d (fp64)."""
+    return hadamard_rotation(group_heads * d)
+
+
+def quantize_cache_grouped(x: np.ndarray, group_heads: int, group: int = GROUP, bits: int = 2):
+    """Quantize pre-RoPE keys x [B, H, T, d] with the grouped-head rotation:
+    the rows of heads g*k .. g*k + g - 1 are concatenated along channels,
+    rotated by grouped_hadamard_rotation(g) (fp64, rounded once to fp32), and
+    each head's d-channel slice is quantized and packed as a cache row.
+    Returns (packed, scales, zeros) laid out as quantize_cache's."""
+    x = np.asarray(x)
+    B, H, T, d = x.shape
+    g = group_heads
+    if H % g:
+        raise ValueError("the head count must be a multiple of the group size")
+    Rg = grouped_hadamard_rotation(g, d)
+    packed = np.empty((B, H, T, d * bits // 8), np.uint8)
+    scales = np.empty((B, H, T, d // group), np.float16)
+    zeros = np.empty((B, H, T, d // group), np.float16)
+    for k in range(H // g):
+        hs = range(g * k, g * k + g)
+        cat = np.concatenate([x[:, h] for h in hs], axis=-1)          # [B, T, g*d]
+        y = rotate_rows(cat, Rg)
+        for j, h in enumerate(hs):
+            codes, sc, z = quantize_rows(y[..., j * d:(j + 1) * d], group, bits)
+            packed[:, h] = pack_codes(codes, bits)
+            scales[:, h] = sc
+            zeros[:, h] = z
+    return packed, scales, zeros
+
+
+def decode_attention_prerope(q, kcache, vcache, t_begin, t_end, group_heads,
+                             rope_base: float = ROPE_BASE, group: int = GROUP,
+                             sink_k=None, sink_v=None, res_k=None, res_v=None,
+                             softmax_scale=None):
+    """Decode attention over a cache whose keys hold the grouped-head
+    rotation of pre-RoPE keys (quantize_cache_grouped) and whose values hold
+    the per-head Hadamard rotation (quantize_cache with the Hadamard matrix).
+
+    q [B, Hq, d] is post-RoPE.  For INT2 token t (cache slot t, position t)
+    of KV head h in group k = h // g, slot j = h % g:
+        k_t  = slice j of [k_hat_{g k, t}, ..., k_hat_{g k + g - 1, t}] R_g^T
+        s_t  = softmax_scale * q . rope(k_t, t)
+    fp16 sink / residual keys are post-RoPE already: s_t = softmax_scale q.k_t.
+        out  = (sum_INT2 p_t v_hat_t) H^T + sum_fp16 p_t v_t
+    Returns fp64 [B, Hq, d].
+    """
+    q64 = np.asarray(q, dtype=np.float64)
+    B, Hq, d = q64.shape
+    kc, ks, kz = kcache
+    vc, vs, vz = vcache
+    Hkv = kc.shape[1]
+    g = group_heads
+    if Hq % Hkv or Hkv % g:
+        raise ValueError("Hq must be a multiple of Hkv, and Hkv of the group size")
+    G = Hq // Hkv
+    kbits, vbits = 8 * kc.shape[-1] // d, 8 * vc.shape[-1] // d
+    if softmax_scale is None or softmax_scale <= 0:
+        softmax_scale = 1.0 / np.sqrt(float(d))
+    Rg = grouped_hadamard_rotation(g, d)
+    Hv = hadamard_rotation(d)
+    pos = np.arange(t_begin, t_end)
+    out = np.zeros((B, Hq, d), np.float64)
+    for b in range(B):
+        kpre = np.zeros((Hkv, t_end - t_begin, d))
+        if t_end > t_begin:
+            for k in range(Hkv // g):
+                hs = range(g * k, g * k + g)
+                cat = np.concatenate([dequantize(unpack_codes(kc[b, h, t_begin:t_end], kbits),
+                                                 ks[b, h, t_begin:t_end], kz[b, h, t_begin:t_end], group)
+                                      for h in hs], axis=-1)
+                un = cat @ Rg.T
+                for j, h in enumerate(hs):
+                    kpre[h] = un[:, j * d:(j + 1) * d]
+        for hk in range(Hkv):
+            khat = rope(kpre[hk], pos, rope_base)
+            if t_end > t_begin:
+                vhat = dequantize(unpack_codes(vc[b, hk, t_begin:t_end], vbits),
+                                  vs[b, hk, t_begin:t_end], vz[b, hk, t_begin:t_end], group)
+            else:
+                vhat = np.zeros((0, d))
+            fk, fv = [], []
+            for seg_k, seg_v in ((sink_k, sink_v), (res_k, res_v)):
+                if seg_k is not None and np.asarray(seg_k).shape[2] > 0:
+                    fk.append(np.asarray(seg_k[b, hk], dtype=np.float64))
+                    fv.append(np.asarray(seg_v[b, hk], dtype=np.float64))
+            fk = np.concatenate(fk, 0) if fk else np.zeros((0, d))
+            fv = np.concatenate(fv, 0) if fv else np.zeros((0, d))
+            if khat.shape[0] + fk.shape[0] == 0:
+                raise ValueError("decode over zero tokens is undefined")
+            for gg in range(G):
+                hq = hk * G + gg
+                qv = q64[b, hq]
+                s_int2 = (khat @ qv) * softmax_scale
+                s_f16 = (fk @ qv) * softmax_scale
+                m = max(s_int2.max(initial=-np.inf), s_f16.max(initial=-np.inf))
+                p_int2 = np.exp(s_int2 - m)
+                p_f16 = np.exp(s_f16 - m)
+                L = p_int2.sum() + p_f16.sum()
+                o = (p_int2 @ vhat) @ Hv.T + p_f16 @ fv
+                out[b, hq] = o / L
+    return out
+
+
+# --------------------------------------------------------------------------
 # Code-level tolerance helper for the rotated write path
 # --------------------------------------------------------------------------
 def tie_distance(x, R, scales, zeros, group: int = GROUP):

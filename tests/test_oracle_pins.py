@@ -282,6 +282,170 @@ def pin_tie_distance_dense(orc):
     assert np.all(dist[0, 32:64] == 0.5)                 # y = 0 lies mid-way between ties
 
 
+# ------------------------------------- pre-RoPE grouped-head rotation (keys)
+def _rope_complex(x, t, base=10000.0):
+    """Rotary embedding written with complex numbers: pair i of x (channels
+    i and i + d/2) is the complex number x_i + 1j x_{i+d/2}, multiplied by
+    exp(1j t theta_i), theta_i = exp(-ln(base) 2i/d)."""
+    d = x.shape[-1]
+    half = d // 2
+    z = x[..., :half] + 1j * x[..., half:]
+    theta = np.exp(-math.log(base) * 2.0 * np.arange(half) / d)
+    w = z * np.exp(1j * t * theta)
+    return np.concatenate([w.real, w.imag], axis=-1)
+
+
+def pin_rope_golden_and_complex(orc):
+    """Hand values for d = 4, base 10000 (theta = 1 and 0.01): e_0 at
+    position 1 goes to (cos 1, 0, sin 1, 0); e_1 at position 2 to
+    (0, cos 0.02, 0, sin 0.02); position 0 is the identity.  At d = 128 the
+    rotate-half form equals the complex-number form."""
+    r = orc.rope(np.array([[1.0, 0, 0, 0]]), [1])
+    assert np.allclose(r, [[math.cos(1), 0, math.sin(1), 0]], atol=1e-15)
+    r = orc.rope(np.array([[0.0, 1, 0, 0]]), [2])
+    assert np.allclose(r, [[0, math.cos(0.02), 0, math.sin(0.02)]], atol=1e-15)
+    rng = np.random.default_rng(51)
+    x = rng.standard_normal((6, 128))
+    assert np.array_equal(orc.rope(x, np.zeros(6)), x)
+    pos = np.array([0, 1, 7, 100, 4095, 131071])
+    want = np.stack([_rope_complex(x[i], pos[i]) for i in range(6)])
+    assert np.allclose(orc.rope(x, pos), want, atol=1e-12)
+
+
+def pin_rope_relative_position(orc):
+    """rope(q, m) . rope(k, n) depends on m - n only, and rope keeps norms."""
+    rng = np.random.default_rng(52)
+    q, k = rng.standard_normal(128), rng.standard_normal(128)
+    for m, n in ((5, 3), (1000, 998), (70000, 3), (3, 70000)):
+        a = orc.rope(q[None], [m])[0] @ orc.rope(k[None], [n])[0]
+        b = orc.rope(q[None], [m - n])[0] @ k
+        assert abs(a - b) < 1e-9 * (np.linalg.norm(q) * np.linalg.norm(k))
+        assert abs(np.linalg.norm(orc.rope(k[None], [n])[0]) - np.linalg.norm(k)) < 1e-12
+
+
+def pin_grouped_rotation(orc):
+    """The rotation over g heads' channels is scipy's Hadamard of size 128 g
+    (normalized), i.e. H_g kron H_128 with the head index as the high bits;
+    g = 1 is the per-head Hadamard rotation."""
+    for g in (1, 2, 4):
+        Rg = orc.grouped_hadamard_rotation(g)
+        n = 128 * g
+        assert np.allclose(Rg, scipy.linalg.hadamard(n) / math.sqrt(n), atol=1e-15)
+        assert np.allclose(Rg, np.kron(scipy.linalg.hadamard(g), scipy.linalg.hadamard(128)) / math.sqrt(n),
+                           atol=1e-15)
+        assert np.abs(Rg @ Rg.T - np.eye(n)).max() < 1e-13
+    assert np.array_equal(orc.grouped_hadamard_rotation(1), orc.hadamard_rotation(128))
+
+
+def pin_quantize_cache_grouped(orc):
+    """Grouped write: rotated group rows chosen on a grid (per 32-channel
+    group), inputs x = y R_g^T split into the g heads; the expected codes
+    (packed by hand), scales and zeros are the grid's, for g = 2 and 4 with
+    two head groups."""
+    rng = np.random.default_rng(53)
+    for g in (2, 4):
+        B, H, T = 2, 2 * g, 3
+        Rg = scipy.linalg.hadamard(128 * g) / math.sqrt(128 * g)
+        y, j, s, z = _grid_rows(rng, (B, H // g, T, 128 * g))           # per head group
+        xg = (y @ Rg.T).astype(np.float32)                               # [B, H/g, T, g*128]
+        x = np.concatenate([xg[:, k, :, 128 * i:128 * (i + 1)][:, None]
+                            for k in range(H // g) for i in range(g)], axis=1)
+        packed, sc, zz = orc.quantize_cache_grouped(x, g)
+        for k in range(H // g):
+            for i in range(g):
+                h = g * k + i
+                sl = slice(128 * i, 128 * (i + 1))
+                assert np.array_equal(packed[:, h], _pack_by_hand(j[:, k, :, sl]))
+                assert np.array_equal(sc[:, h], s[:, k, :, 4 * i:4 * i + 4])
+                assert np.array_equal(zz[:, h], z[:, k, :, 4 * i:4 * i + 4])
+
+
+def _prerope_reference(q, kcache, vcache, t_begin, t_end, g, scale, sinks=None):
+    """Plain loops: dequantized key rows of each head group concatenated,
+    un-rotated with scipy's Hadamard (explicit sums), rotary-embedded with
+    complex numbers at the cache slot, scores and softmax by loops, values
+    un-rotated per head."""
+    kp, ks, kz = kcache
+    vp, vs, vz = vcache
+    B, Hq, d = q.shape
+    Hkv = kp.shape[1]
+    G = Hq // Hkv
+    n = 128 * g
+    Hn = scipy.linalg.hadamard(n).astype(np.float64) / math.sqrt(n)
+    H1 = scipy.linalg.hadamard(d).astype(np.float64) / math.sqrt(d)
+    kc, vc = kvq_oracle.unpack_codes(kp), kvq_oracle.unpack_codes(vp)
+    out = np.zeros((B, Hq, d))
+    for b in range(B):
+        keys = {}
+        for t in range(t_begin, t_end):
+            for k in range(Hkv // g):
+                cat = [int(kc[b, g * k + i, t, c]) * float(ks[b, g * k + i, t, c // 32])
+                       + float(kz[b, g * k + i, t, c // 32]) for i in range(g) for c in range(d)]
+                un = [sum(cat[m] * Hn[r, m] for m in range(n)) for r in range(n)]   # cat R^T
+                for i in range(g):
+                    keys[(g * k + i, t)] = _rope_complex(np.array(un[i * d:(i + 1) * d]), t)
+        for hq in range(Hq):
+            hk = hq // G
+            sc, vals = [], []
+            for t in range(t_begin, t_end):
+                sc.append(scale * sum(float(q[b, hq, c]) * keys[(hk, t)][c] for c in range(d)))
+                rot = [int(vc[b, hk, t, c]) * float(vs[b, hk, t, c // 32]) + float(vz[b, hk, t, c // 32])
+                       for c in range(d)]
+                vals.append([sum(rot[m] * H1[c, m] for m in range(d)) for c in range(d)])
+            if sinks is not None:
+                for kk, vv in zip(sinks[0][b, hk], sinks[1][b, hk]):
+                    sc.append(scale * sum(float(q[b, hq, c]) * float(kk[c]) for c in range(d)))
+                    vals.append([float(v) for v in vv])
+            m = max(sc)
+            p = [math.exp(x - m) for x in sc]
+            L = sum(p)
+            out[b, hq] = [sum(p[t] * vals[t][c] for t in range(len(p))) / L for c in range(d)]
+    return out
+
+
+def pin_decode_prerope_bruteforce(orc):
+    """Decode over pre-RoPE grouped-rotated keys against plain loops, with
+    two query heads per KV head, g = 2, INT2 slots [3, 7) and two fp16
+    (post-RoPE) sink tokens."""
+    rng = np.random.default_rng(54)
+    B, Hkv, G, T, g = 1, 2, 2, 7, 2
+    _, ks, kz, kp = _random_cache(rng, B, Hkv, T)
+    _, vs, vz, vp = _random_cache(rng, B, Hkv, T)
+    q = rng.standard_normal((B, Hkv * G, 128)).astype(np.float16)
+    sk = rng.standard_normal((B, Hkv, 2, 128)).astype(np.float16)
+    sv = rng.standard_normal((B, Hkv, 2, 128)).astype(np.float16)
+    out = orc.decode_attention_prerope(q, (kp, ks, kz), (vp, vs, vz), 3, T, g, sink_k=sk, sink_v=sv)
+    ref = _prerope_reference(q.astype(np.float64), (kp, ks, kz), (vp, vs, vz), 3, T, g,
+                             1 / math.sqrt(128), sinks=(sk, sv))
+    assert np.abs(out - ref).max() <= 1e-11 * np.abs(ref).max()
+
+
+def pin_decode_prerope_vs_sdpa(orc):
+    """Against torch SDPA in fp64 on keys un-rotated (scipy's Hadamard of
+    size 128 g) and rotary-embedded (complex form) at their slots, values
+    un-rotated per head; g = 4, grouped-query heads, a softmax scale."""
+    rng = np.random.default_rng(55)
+    B, Hkv, G, T, g, tb = 2, 4, 2, 40, 4, 5
+    kcodes, ks, kz, kp = _random_cache(rng, B, Hkv, T)
+    vcodes, vs, vz, vp = _random_cache(rng, B, Hkv, T)
+    q = rng.standard_normal((B, Hkv * G, 128))
+    out = orc.decode_attention_prerope(q, (kp, ks, kz), (vp, vs, vz), tb, T, g, softmax_scale=0.05)
+    n = 128 * g
+    Hn = scipy.linalg.hadamard(n) / math.sqrt(n)
+    H1 = scipy.linalg.hadamard(128) / math.sqrt(128)
+    kr = _deq(kcodes, ks, kz)[:, :, tb:]                                  # [B, Hkv, T', 128]
+    cat = kr.transpose(0, 2, 1, 3).reshape(B, T - tb, Hkv // g, n)       # head groups
+    un = (cat @ Hn.T).reshape(B, T - tb, Hkv, 128).transpose(0, 2, 1, 3)
+    pos = np.arange(tb, T)
+    K = np.stack([np.stack([np.stack([_rope_complex(un[b, h, i], pos[i]) for i in range(T - tb)])
+                            for h in range(Hkv)]) for b in range(B)])
+    V = _deq(vcodes, vs, vz)[:, :, tb:] @ H1.T
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[:, :, None, :], torch.from_numpy(np.repeat(K, G, axis=1)),
+        torch.from_numpy(np.repeat(V, G, axis=1)), scale=0.05)[:, :, 0].numpy()
+    assert np.abs(out - ref).max() <= 1e-11 * np.abs(ref).max()
+
+
 # ------------------------------------------------------ other code widths
 def pin_quant_bits_grid(orc):
     """1- and 4-bit codes: grid data z + j*s, j in [0, 2**b - 1] with every
@@ -489,6 +653,8 @@ PINS = [
     pin_decode_vs_sdpa, pin_decode_bruteforce, pin_decode_large_scores,
     pin_quant_bits_grid, pin_quant_bits_ramp, pin_quant_bits_nearest, pin_pack_bits,
     pin_decode_mixed_widths, pin_quantize_cache_per_head, pin_tie_distance_dense,
+    pin_rope_golden_and_complex, pin_rope_relative_position, pin_grouped_rotation,
+    pin_quantize_cache_grouped, pin_decode_prerope_bruteforce, pin_decode_prerope_vs_sdpa,
 ]
 
 
@@ -588,6 +754,19 @@ MUTATIONS = [
     ("rows of the wrong head written", "y = rotate_rows(x[:, h], R)", "y = rotate_rows(x[:, H - 1 - h], R)"),
     ("tie distance with R^T", "y64 = y64 @ np.asarray(R, dtype=np.float64)",
      "y64 = y64 @ np.asarray(R, dtype=np.float64).T"),
+    ("rotary sine sign flipped", "x2 * c + x1 * s", "x2 * c - x1 * s"),
+    ("rotary pairs interleaved", "x1, x2 = x[..., :half], x[..., half:]",
+     "x1, x2 = x[..., 0::2], x[..., 1::2]"),
+    ("rotary frequencies base**(-i/d)", "base ** (-2.0 * np.arange(half) / d)",
+     "base ** (-1.0 * np.arange(half) / d)"),
+    ("key positions counted from the range start", "pos = np.arange(t_begin, t_end)",
+     "pos = np.arange(0, t_end - t_begin)"),
+    ("head order reversed in a group", "cat = np.concatenate([x[:, h] for h in hs], axis=-1)",
+     "cat = np.concatenate([x[:, h] for h in reversed(hs)], axis=-1)"),
+    ("grouped rotation over one head only", "return hadamard_rotation(group_heads * d)",
+     "return np.kron(np.eye(group_heads), hadamard_rotation(d))"),
+    ("values not un-rotated (pre-RoPE decode)", "o = (p_int2 @ vhat) @ Hv.T + p_f16 @ fv",
+     "o = (p_int2 @ vhat) + p_f16 @ fv"),
 ]
 
 
