@@ -12,12 +12,12 @@
  *                         by R, the output un-rotated by R^T.
  *
  * The method: "Output-Aware Rotation for INT2 KV-Cache Quantization"
- * (woor.ai page, section "Key Details": a per-head orthogonal rotation is
- * applied before INT2 quantization and removed after the attention
- * computation; section "What You Need to Know": the readout is scaled
- * dot-product attention).  The Hadamard form and its fast transform:
- * RotateKV (IJCAI 2025 record, abstract item (i)) and KVLinC (fugumt page,
- * abstract).  Sinks kept at higher precision: RotateKV abstract, item (iii).
+ * (woor.ai page, section "Key Details": K and V rows of each head are
+ * turned by that head's orthogonal matrix before the 2-bit quantizer sees
+ * them, and the attention output is turned back afterwards; section "What
+ * You Need to Know": the readout is scaled dot-product attention).  The
+ * Hadamard form and its fast transform: RotateKV (IJCAI 2025 record,
+ * abstract item (i)) and KVLinC (fugumt page, abstract).  Sinks kept at higher precision: RotateKV abstract, item (iii).
  * The pages fix no group size, scale format, rounding rule or bit layout;
  * the format below is this library's.
  *
@@ -30,9 +30,11 @@
  *    failed check returns an error status and enqueues nothing.  A failed
  *    kernel launch returns KVQ_ERR_HIP.  No C++ exception crosses the ABI.
  *  - Device pointers must be 16-byte aligned (checked).
- *  - Preconditions not checked: inputs are finite; every group's range
- *    (max - min) / 3 and its minimum are within the fp16 range; buffers are
- *    as large as the shapes say.
+ *  - Preconditions not checked: inputs are finite; on the write path every
+ *    rotated group's (max - min) / L and its minimum are within the fp16
+ *    range (else the stored scale or zero is infinite); buffers are as large
+ *    as the shapes say.  The decode handles every finite fp16 scale and
+ *    zero; an output beyond the range of the output dtype rounds to inf.
  *  - There is no mutable global state; calls on different streams may run
  *    concurrently as long as they do not write the same memory.
  *
@@ -115,8 +117,9 @@ typedef struct {
  * above for codes `bits` wide (1, 2 or 4; 2 is the INT2 format).  A block
  * table int32 [B][max_pages] (device) maps sequence b's token t to row
  * t % page_tokens of page table[b][t / page_tokens]; page_tokens must be a
- * multiple of 64, and max_pages * page_tokens below 2^31.  Serving stacks keep caches in such pages (the pages name
- * serving stacks as the setting: OptR page, "Why It Matters"). */
+ * multiple of 64, and max_pages * page_tokens below 2^31.  Serving stacks
+ * keep caches in such pages (the pages name serving stacks as the setting:
+ * OptR page, "Why It Matters"). */
 typedef struct {
   uint8_t *codes;
   uint16_t *scales;

@@ -154,6 +154,103 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+# ---------------------------------------------------------------- checks
+# The C ABI takes raw device pointers and trusts the buffer sizes its shape
+# arguments imply, so every tensor is checked here first: shape, dtype and
+# contiguity, then that everything sits on one GPU.  A failed check raises
+# ValueError before the library is loaded or called.
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _is_dense(t):
+    return t is not None and t.is_contiguous()
+
+
+def _check_device(tensors):
+    ts = [t for t in tensors if t is not None]
+    _need(all(t.is_cuda for t in ts), "every tensor must be on the GPU (device memory)")
+    _need(len({t.device for t in ts}) <= 1, "every tensor must be on the same GPU")
+
+
+def _cache_tensors(c):
+    return () if c is None else (c.codes, c.scales, c.zeros)
+
+
+def _check_cache(c, lead, what):
+    """A cache side: codes uint8 [*lead, rows, 16*bits], scales / zeros fp16
+    [*lead, rows, 4], all contiguous with the same row count."""
+    for t, dt, last in ((c.codes, torch.uint8, 16 * c.bits), (c.scales, torch.float16, D_HEAD // GROUP),
+                        (c.zeros, torch.float16, D_HEAD // GROUP)):
+        _need(_is_dense(t), f"{what}: cache arrays must be contiguous")
+        _need(t.dtype == dt and t.dim() == 4, f"{what}: cache arrays must be 4-D ({dt})")
+        _need(tuple(t.shape[:2]) == tuple(lead), f"{what}: cache leading dims {tuple(t.shape[:2])} "
+              f"do not match {tuple(lead)}")
+        _need(t.shape[2] == c.codes.shape[2] and t.shape[3] == last,
+              f"{what}: cache array of shape {tuple(t.shape)} does not fit the layout")
+
+
+def _check_rotation(rot, R, Hkv):
+    _need(rot in _ROT, f"unknown rotation {rot!r}")
+    if rot == "dense":
+        _need(R is not None and _is_dense(R) and R.dtype == torch.float32
+              and tuple(R.shape) == (Hkv, D_HEAD, D_HEAD), "rot='dense' needs R fp32 [Hkv, 128, 128] contiguous")
+    elif rot == "perm":
+        _need(R is not None and _is_dense(R) and R.dtype == torch.int32
+              and tuple(R.shape) == (Hkv, D_HEAD), "rot='perm' needs R int32 [Hkv, 128] contiguous")
+    else:
+        _need(R is None, f"rot={rot!r} takes no R")
+
+
+def _check_vec(t, B, name):
+    _need(t is not None and _is_dense(t) and t.dtype == torch.int32 and t.dim() == 1 and t.numel() == B,
+          f"{name} must be contiguous int32 [B]")
+
+
+def _check_rows(K, V):
+    """K/V token rows [B, T_new, Hkv, 128] with unit channel stride."""
+    x = K if K is not None else V
+    _need(x is not None, "K and V cannot both be None")
+    for t in (K, V):
+        if t is not None:
+            _need(t.dim() == 4 and t.shape[3] == D_HEAD and t.stride(3) == 1,
+                  "K/V must be [B, T_new, Hkv, 128] with unit channel stride")
+            _need(t.dtype in (torch.float16, torch.float32), "K/V must be fp16 or fp32")
+    if K is not None and V is not None:
+        _need(K.shape == V.shape and K.stride() == V.stride() and K.dtype == V.dtype,
+              "K and V must share shape, strides and dtype")
+    return x
+
+
+def _check_fp16_tokens(k, v, B, Hkv, what):
+    """fp16 sink / residual tokens [B, Hkv, n, 128]; returns n."""
+    _need((k is None) == (v is None), f"{what}: give both keys and values or neither")
+    if k is None:
+        return 0
+    for t in (k, v):
+        _need(_is_dense(t) and t.dtype == torch.float16 and t.dim() == 4
+              and tuple(t.shape[:2]) == (B, Hkv) and t.shape[3] == D_HEAD,
+              f"{what}: tokens must be contiguous fp16 [B, Hkv, n, 128]")
+    _need(k.shape == v.shape, f"{what}: keys and values must have the same shape")
+    return k.shape[2]
+
+
+def _check_query(q, out, Hkv):
+    _need(q.dim() == 3 and q.shape[2] == D_HEAD and q.is_contiguous(), "q must be contiguous [B, Hq, 128]")
+    _need(q.dtype in (torch.float16, torch.float32), "q must be fp16 or fp32")
+    _need(q.shape[1] % Hkv == 0, "the query heads must be a multiple of the KV heads")
+    if out is not None:
+        _need(_is_dense(out) and out.shape == q.shape and out.dtype in (torch.float16, torch.float32),
+              "out must be contiguous, shaped like q, fp16 or fp32")
+
+
+def _check_workspace(ws, need):
+    if ws is not None:
+        _need(_is_dense(ws) and ws.dim() == 1 and ws.dtype == torch.uint8, "workspace must be a 1-D uint8 tensor")
+        _need(ws.numel() >= need, f"workspace holds {ws.numel()} bytes, the call needs {need}")
+
+
 class Int2Cache:
     """Device buffers of one side (K or V) of a quantized cache.
 
@@ -202,17 +299,18 @@ def kvq_quantize(K, V, cache_k: Int2Cache | None, cache_v: Int2Cache | None,
     t_offsets: int32 [B] on the device: sequence b's rows land at slots
     [t_offsets[b], t_offsets[b] + T_new) (kvq_quantize_at); t_offset is then
     unused."""
-    x = K if K is not None else V
-    for t in (K, V):
-        if t is not None and (t.dim() != 4 or t.stride(3) != 1):
-            raise ValueError("K/V must be [B, T_new, Hkv, d] with unit channel stride")
-    if K is not None and V is not None and (K.shape != V.shape or K.stride() != V.stride()
-                                            or K.dtype != V.dtype):
-        raise ValueError("K and V must share shape, strides and dtype")
+    x = _check_rows(K, V)
     B, T_new, Hkv, d = x.shape
+    _need((K is None) == (cache_k is None) and (V is None) == (cache_v is None),
+          "each side needs both its rows and its cache, or neither")
+    for c, what in ((cache_k, "cache_k"), (cache_v, "cache_v")):
+        if c is not None:
+            _check_cache(c, (B, Hkv), what)
+    _check_rotation(rot, R, Hkv)
+    if t_offsets is not None:
+        _check_vec(t_offsets, B, "t_offsets")
+    _check_device((K, V, R, t_offsets, *_cache_tensors(cache_k), *_cache_tensors(cache_v)))
     lib = load_library()
-    if t_offsets is not None and (t_offsets.dtype != torch.int32 or t_offsets.numel() != B):
-        raise ValueError("t_offsets must be int32 [B]")
     if any(c is not None and c.bits != 2 for c in (cache_k, cache_v)):
         kq = cache_k.c_quant_struct() if cache_k is not None else None
         vq = cache_v.c_quant_struct() if cache_v is not None else None
@@ -268,24 +366,33 @@ def kvq_decode_attention(q: torch.Tensor, cache_k: Int2Cache | None,
     [B, Hq, d] in q's dtype (or writes `out`).  t_ends: int32 [B] on the
     device, sequence b's own end (kvq_decode_attention_varlen); t_end is
     then the upper bound of every t_ends[b]."""
-    if not q.is_contiguous():
-        raise ValueError("q must be contiguous [B, Hq, d]")
+    _need(q.dim() == 3, "q must be [B, Hq, 128]")
     B, Hq, d = q.shape
+    _need((cache_k is None) == (cache_v is None), "give both cache sides or neither")
     Hkv = (cache_k.codes.shape[1] if cache_k is not None
-           else (sink_k if sink_k is not None else res_k).shape[1])
-    n_sink = 0 if sink_k is None else sink_k.shape[2]
-    n_res = 0 if res_k is None else res_k.shape[2]
-    for t in (sink_k, sink_v, res_k, res_v):
-        if t is not None and (t.dtype != torch.float16 or not t.is_contiguous()):
-            raise ValueError("sink/residual tensors must be contiguous fp16 [B, Hkv, n, d]")
+           else (sink_k if sink_k is not None else res_k).shape[1] if (sink_k is not None or res_k is not None)
+           else 0)
+    _need(Hkv > 0, "no cache and no fp16 tokens")
+    _check_query(q, out, Hkv)
+    if cache_k is not None:
+        for c, what in ((cache_k, "cache_k"), (cache_v, "cache_v")):
+            _check_cache(c, (B, Hkv), what)
+            _need(0 <= t_begin <= t_end <= c.T_cap, f"{what}: token range [{t_begin}, {t_end}) "
+                  f"outside the cache's {c.T_cap} slots")
+    n_sink = _check_fp16_tokens(sink_k, sink_v, B, Hkv, "sink")
+    n_res = _check_fp16_tokens(res_k, res_v, B, Hkv, "residual")
+    _check_rotation(rot, R, Hkv)
+    if t_ends is not None:
+        _check_vec(t_ends, B, "t_ends")
+    _check_device((q, out, workspace, R, t_ends, sink_k, sink_v, res_k, res_v,
+                   *_cache_tensors(cache_k), *_cache_tensors(cache_v)))
+    need = kvq_decode_workspace_bytes(B, Hq, Hkv, d, t_end - t_begin, n_sink, n_res)
+    _check_workspace(workspace, need)
     if out is None:
         out = torch.empty_like(q)
-    need = kvq_decode_workspace_bytes(B, Hq, Hkv, d, t_end - t_begin, n_sink, n_res)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     lib = load_library()
-    if t_ends is not None and (t_ends.dtype != torch.int32 or t_ends.numel() != B):
-        raise ValueError("t_ends must be int32 [B]")
     if any(c is not None and c.bits != 2 for c in (cache_k, cache_v)):
         kq = cache_k.c_quant_struct() if cache_k is not None else None
         vq = cache_v.c_quant_struct() if cache_v is not None else None
@@ -369,6 +476,15 @@ class PagedCache:
                                self.n_pages, self.page_tokens, self.bits)
 
 
+def _check_paged_pair(cache_k, cache_v, Hkv):
+    """Paged sides: [n_pages, Hkv, page_tokens, row] arrays, one pool shape."""
+    cs = [c for c in (cache_k, cache_v) if c is not None]
+    for c in cs:
+        _check_cache(c, (c.n_pages, Hkv), "paged cache")
+        _need(c.page_tokens % 64 == 0, "page_tokens must be a multiple of 64")
+    _need(len({(c.n_pages, c.page_tokens) for c in cs}) <= 1, "both sides must share the page pool shape")
+
+
 def _table(block_table, B):
     if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B \
             or not block_table.is_contiguous():
@@ -383,11 +499,15 @@ def kvq_quantize_paged(K, V, cache_k: PagedCache | None, cache_v: PagedCache | N
     """Rotate, quantize and pack K/V rows [B, T_new, Hkv, d] of fp16 into a
     paged cache: sequence b's rows are its tokens t_offsets[b] + i, placed
     through block_table [B, max_pages] (kvq_quantize_paged)."""
-    x = K if K is not None else V
+    x = _check_rows(K, V)
     B, T_new, Hkv, d = x.shape
-    if t_offsets.dtype != torch.int32 or t_offsets.numel() != B:
-        raise ValueError("t_offsets must be int32 [B]")
+    _need((K is None) == (cache_k is None) and (V is None) == (cache_v is None),
+          "each side needs both its rows and its cache, or neither")
+    _check_vec(t_offsets, B, "t_offsets")
     max_pages = _table(block_table, B)
+    _check_paged_pair(cache_k, cache_v, Hkv)
+    _check_rotation(rot, R, Hkv)
+    _check_device((K, V, R, t_offsets, block_table, *_cache_tensors(cache_k), *_cache_tensors(cache_v)))
     kc = cache_k.c_struct() if cache_k is not None else None
     vc = cache_v.c_struct() if cache_v is not None else None
     st = load_library().kvq_quantize_paged(
@@ -408,18 +528,25 @@ def kvq_decode_attention_paged(q: torch.Tensor, cache_k: PagedCache, cache_v: Pa
                                workspace: torch.Tensor | None = None, stream=None):
     """Decode attention for q [B, Hq, d] over a paged cache: sequence b
     attends to its tokens [t_begin, t_ends[b]) (kvq_decode_attention_paged)."""
-    if not q.is_contiguous():
-        raise ValueError("q must be contiguous [B, Hq, d]")
+    _need(q.dim() == 3, "q must be [B, Hq, 128]")
     B, Hq, d = q.shape
+    _need(cache_k is not None and cache_v is not None, "a paged decode needs both cache sides")
     Hkv = cache_k.codes.shape[1]
-    if t_ends.dtype != torch.int32 or t_ends.numel() != B:
-        raise ValueError("t_ends must be int32 [B]")
+    _check_query(q, out, Hkv)
+    _check_vec(t_ends, B, "t_ends")
     max_pages = _table(block_table, B)
-    n_sink = 0 if sink_k is None else sink_k.shape[2]
-    n_res = 0 if res_k is None else res_k.shape[2]
+    _check_paged_pair(cache_k, cache_v, Hkv)
+    _need(0 <= t_begin <= t_end_max <= max_pages * cache_k.page_tokens,
+          "t_end_max is past the block table's capacity")
+    n_sink = _check_fp16_tokens(sink_k, sink_v, B, Hkv, "sink")
+    n_res = _check_fp16_tokens(res_k, res_v, B, Hkv, "residual")
+    _check_rotation(rot, R, Hkv)
+    _check_device((q, out, workspace, R, t_ends, block_table, sink_k, sink_v, res_k, res_v,
+                   *_cache_tensors(cache_k), *_cache_tensors(cache_v)))
+    need = kvq_decode_workspace_bytes(B, Hq, Hkv, d, t_end_max - t_begin, n_sink, n_res)
+    _check_workspace(workspace, need)
     if out is None:
         out = torch.empty_like(q)
-    need = kvq_decode_workspace_bytes(B, Hq, Hkv, d, t_end_max - t_begin, n_sink, n_res)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     kc, vc = cache_k.c_struct(), cache_v.c_struct()
