@@ -81,6 +81,22 @@ def parse():
     return p.parse_args()
 
 
+# What the path computes in (the JSON line's "arithmetic" field).
+ARITHMETIC_WRITE = "f32 transform of the f16 rows, f32 quantizer (IEEE steps), 2-bit codes + f16 scale/zero"
+ARITHMETIC_G1 = {"write": ARITHMETIC_WRITE,
+                 "scores": "int32 dot of the codes with a 19-bit fixed-point rotated query, f32 scale/zero terms",
+                 "values": "f16 weights p*s times the codes (f16 dot2), f32 accumulation",
+                 "combine": "f32 merge and un-rotation, output in the query dtype"}
+ARITHMETIC_GQA = {"write": ARITHMETIC_WRITE,
+                  "scores": "fp8 digits of a 19-bit fixed-point query x fp4 codes on the matrix cores (exact), "
+                            "f32 scale/zero terms",
+                  "values": "f16 weights x f16 (code*s - 1.5s) on the matrix cores, f32 accumulation",
+                  "combine": "f32 merge and un-rotation, output in the query dtype"}
+ARITHMETIC_BBIT = {"write": ARITHMETIC_WRITE.replace("2-bit", "b-bit"),
+                   "scores": "int32 dot of the codes with a 19-bit fixed-point rotated query, f32 scale/zero terms",
+                   "values": "f32 FMA per code, f32 accumulation",
+                   "combine": "f32 merge and un-rotation, output in the query dtype"}
+
 PREROLL_MS = 30.0        # untimed calls before each timed phase
 FLUSH_BYTES = 1 << 30    # read between timed calls
 
@@ -348,12 +364,15 @@ def main():
               "bytes_per_unit": d_unit, "unit_of_work": "(INT2 token, kv head)",
               "units_per_launch": int2_tokens * H, "avg_ms": round(d_ms, 4)}
     dominant, other = (roof_q, roof_d) if q_ms >= d_ms else (roof_d, roof_q)
+    cache_tag = "int2" if (kbits, vbits) == (2, 2) else f"k{kbits}v{vbits}-bit"
 
     rec = {
         "metric": METRIC, "value": round(dec_gbs, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32", "data": "synthetic",
+        "dtype": f"f16 in / {cache_tag} cache", "data": "synthetic",
+        "arithmetic": (ARITHMETIC_BBIT if (kbits, vbits) != (2, 2) else
+                       ARITHMETIC_G1 if cfg.G == 1 else ARITHMETIC_GQA),
         "config": {"workload": workload, "B": B, "T": T, "Hkv": H, "Hq": cfg.Hq, "d": d,
                    "kv_input": "f16",
                    "cache": ("int2 codes + f16 scale/zero, group 32" if (kbits, vbits) == (2, 2) else

@@ -231,7 +231,19 @@ struct TileRegs {
 template <int GC>
 struct AttnState {
   float m[GC], l[GC], zacc[GC][2], wsum[GC][2], acc[GC][64];
+  // Weights are kept below 2^slack (log2 units above the reference m):
+  // kSlack, or 0 once the wave has met a value scale of 2^11 or more, so
+  // that w = p * s stays inside the fp16 range for every finite fp16 scale.
+  float slack;
 };
+
+// Any of the four fp16 value scales (two per dword, all >= 0) at 2^11 or
+// above: with p < 2^kSlack, p * s could then round past the fp16 range.
+// Adding 0x1800 to each half sets its bit 15 exactly for 0x6800 (= 2048)
+// and above; finite halves stay below 0x10000, so nothing carries across.
+__device__ __forceinline__ bool big_value_scale(uint32_t s0, uint32_t s1) {
+  return (((s0 + 0x18001800u) | (s1 + 0x18001800u)) & 0x80008000u) != 0u;
+}
 
 // Per-lane query data for the lane's two channel groups of GC heads.
 template <int GC>
@@ -266,6 +278,8 @@ __device__ __forceinline__ void attn_tile(AttnState<GC> &st, const QueryLimbs<GC
   const half2_t vsA = __builtin_bit_cast(half2_t, r.vsA), vzA = __builtin_bit_cast(half2_t, r.vzA);
   const half2_t vsB = __builtin_bit_cast(half2_t, r.vsB), vzB = __builtin_bit_cast(half2_t, r.vzB);
   half2_t wp[GC][2];
+  // a value scale that could overflow w at the current slack: lower the slack
+  const bool big = st.slack > 0.0f && __builtin_amdgcn_ballot_w64(big_value_scale(r.vsA, r.vsB));
 #pragma unroll
   for (int g = 0; g < GC; ++g) {
     // score in units of the query step: sum_j s_j * dot_j + z_j * isum_j
@@ -282,7 +296,8 @@ __device__ __forceinline__ void attn_tile(AttnState<GC> &st, const QueryLimbs<GC
     // log2-domain score minus the running reference
     float xa = va ? __builtin_fmaf(q.qstep[g], ra, -st.m[g]) : kNegInf;
     float xb = vb ? __builtin_fmaf(q.qstep[g], rb, -st.m[g]) : kNegInf;
-    if (__builtin_amdgcn_ballot_w64(fmaxf(xa, xb) > kSlack)) {     // wave-uniform
+    if (__builtin_amdgcn_ballot_w64(fmaxf(xa, xb) > st.slack) || big) {     // wave-uniform
+      if (big) st.slack = 0.0f;              // from here on p <= 1
       const float ya = va ? q.qstep[g] * ra : kNegInf;
       const float yb = vb ? q.qstep[g] * rb : kNegInf;
       float mx = fmaxf(ya, yb);
@@ -290,18 +305,21 @@ __device__ __forceinline__ void attn_tile(AttnState<GC> &st, const QueryLimbs<GC
       mx = fmaxf(mx, row_ror<4>(mx));
       mx = fmaxf(mx, row_ror<8>(mx));
       mx = max_xor16(mx);
-      mx = max_xor32(mx);                    // > m: some score passed m + kSlack
-      const float alpha = __builtin_amdgcn_exp2f(st.m[g] - mx);
-      st.l[g] *= alpha;
-      st.zacc[g][0] *= alpha;
-      st.zacc[g][1] *= alpha;
-      st.wsum[g][0] *= alpha;
-      st.wsum[g][1] *= alpha;
+      mx = max_xor32(mx);
+      mx = fmaxf(mx, st.m[g]);               // the reference never moves down
+      if (mx != kNegInf) {                   // wave-uniform; else no token so far
+        const float alpha = __builtin_amdgcn_exp2f(st.m[g] - mx);
+        st.l[g] *= alpha;
+        st.zacc[g][0] *= alpha;
+        st.zacc[g][1] *= alpha;
+        st.wsum[g][0] *= alpha;
+        st.wsum[g][1] *= alpha;
 #pragma unroll
-      for (int i = 0; i < 64; ++i) st.acc[g][i] *= alpha;
-      st.m[g] = mx;
-      xa = ya - mx;
-      xb = yb - mx;
+        for (int i = 0; i < 64; ++i) st.acc[g][i] *= alpha;
+        st.m[g] = mx;
+        xa = ya - mx;
+        xb = yb - mx;
+      }
     }
     const float pA = __builtin_amdgcn_exp2f(xa);   // 0 for masked tokens
     const float pB = __builtin_amdgcn_exp2f(xb);
@@ -471,6 +489,7 @@ __global__ __launch_bounds__(64 * WPB) void kv_int2_decode_attn(AttnArgs a) {
 #pragma unroll
   for (int g = 0; g < GC; ++g) {
     st.m[g] = kNegInf; st.l[g] = 0.0f; st.zacc[g][0] = 0.0f; st.zacc[g][1] = 0.0f;
+    st.slack = kSlack;
     st.wsum[g][0] = 0.0f; st.wsum[g][1] = 0.0f;
 #pragma unroll
     for (int i = 0; i < 64; ++i) st.acc[g][i] = 0.0f;

@@ -39,6 +39,8 @@
 // 8n .. 8n+7 of its head, summed over every token of the split.  The
 // zero-point term sum p~ (z + fp16(1.5 s)) is accumulated per group in the
 // softmax layout.
+#include <type_traits>
+
 #include "kv_decode_common.h"
 
 namespace kvq {
@@ -284,13 +286,28 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
     return t;
   };
 
-  // One tile whose tokens [lo, hi) are valid.
-  auto process = [&](const MqTile &t, int lo, int hi) {
+  // One tile whose tokens [lo, hi) are valid.  BIG: the wave has met a value
+  // scale of 2^15 or more, for which fp16(1.5 s) and the B entries could
+  // overflow; the B entries are then built from s/2 and each weight in the A
+  // operand is doubled (2 p~ (code s/2 - fp16(0.75 s)) = p~ (code s - 2
+  // fp16(0.75 s)), exact power-of-two scalings), with the zero-point term
+  // z + 2 fp16(0.75 s) to match.  Either form may follow the other in one
+  // accumulator: each token's product is the same.
+  auto process = [&](const MqTile &t, int lo, int hi, auto big_c) {
+    constexpr bool BIG = decltype(big_c)::value;
+    constexpr float kB = BIG ? 2.0f : 1.0f;
     {
       // per-token record (lane = token) and the value codes
       uint32_t *rl = rec + lane * kMqRecDwords;
-      const uint32_t vs0 = t.vs.x, vs1 = t.vs.y, vz0 = t.vz.x, vz1 = t.vz.y;
-      const half2_t s01 = __builtin_bit_cast(half2_t, vs0), s23 = __builtin_bit_cast(half2_t, vs1);
+      uint32_t vs0 = t.vs.x, vs1 = t.vs.y;
+      const uint32_t vz0 = t.vz.x, vz1 = t.vz.y;
+      half2_t s01 = __builtin_bit_cast(half2_t, vs0), s23 = __builtin_bit_cast(half2_t, vs1);
+      if constexpr (BIG) {
+        s01 = s01 * half2_t{(_Float16)0.5f, (_Float16)0.5f};
+        s23 = s23 * half2_t{(_Float16)0.5f, (_Float16)0.5f};
+        vs0 = __builtin_bit_cast(uint32_t, s01);
+        vs1 = __builtin_bit_cast(uint32_t, s23);
+      }
       const half2_t z01 = __builtin_bit_cast(half2_t, vz0), z23 = __builtin_bit_cast(half2_t, vz1);
       const half2_t n01 = s01 * half2_t{(_Float16)-1.5f, (_Float16)-1.5f};   // -fp16(1.5 s)
       const half2_t n23 = s23 * half2_t{(_Float16)-1.5f, (_Float16)-1.5f};
@@ -300,8 +317,8 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
           u32x4_t{__builtin_amdgcn_perm(un01, vs0, 0x05040100u), __builtin_amdgcn_perm(un01, vs0, 0x07060302u),
                   __builtin_amdgcn_perm(un23, vs1, 0x05040100u), __builtin_amdgcn_perm(un23, vs1, 0x07060302u)};
       reinterpret_cast<float4v_t *>(rl)[2] =
-          float4v_t{(float)z01.x - (float)n01.x, (float)z01.y - (float)n01.y,
-                    (float)z23.x - (float)n23.x, (float)z23.y - (float)n23.y};
+          float4v_t{__builtin_fmaf(-kB, (float)n01.x, (float)z01.x), __builtin_fmaf(-kB, (float)n01.y, (float)z01.y),
+                    __builtin_fmaf(-kB, (float)n23.x, (float)z23.x), __builtin_fmaf(-kB, (float)n23.y, (float)z23.y)};
       reinterpret_cast<u32x4_t *>(vcl)[lane] = t.vc[0];
       reinterpret_cast<u32x4_t *>(vcl)[64 + lane] = t.vc[1];
     }
@@ -372,7 +389,7 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
       st.zacc[1] = __builtin_fmaf(pf, zb[1], st.zacc[1]);
       st.zacc[2] = __builtin_fmaf(pf, zb[2], st.zacc[2]);
       st.zacc[3] = __builtin_fmaf(pf, zb[3], st.zacc[3]);
-      pw[gk * 64 + tt] = ph;
+      pw[gk * 64 + tt] = BIG ? ph * (_Float16)2.0f : ph;
     }
     asm volatile("" ::: "memory");
     // values: 8 blocks of 8 tokens; lane's tokens t0 = 8 tb + 2 kb and t0 + 1
@@ -401,6 +418,18 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
     asm volatile("" ::: "memory");
   };
 
+  // Value scales of 2^15 or more (fp16 bits 0x7800 and up; adding 0x0800
+  // sets bit 15 of a half exactly then, with no carry for finite halves)
+  // switch the wave to the halved B entries for good.
+  bool big = false;
+  auto run = [&](const MqTile &t, int lo, int hi) {
+    if (!big && __builtin_amdgcn_ballot_w64(
+                    (((t.vs.x + 0x08000800u) | (t.vs.y + 0x08000800u)) & 0x80008000u) != 0u))
+      big = true;
+    if (big) process(t, lo, hi, std::true_type{});
+    else process(t, lo, hi, std::false_type{});
+  };
+
   // this wave's full tiles, loads one tile ahead
   const HeadTiles ht(seq_int2(a, b), a.skip, split, S);
   const int64_t mine = ht.mine;
@@ -418,11 +447,11 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
     int64_t i = 0;
     for (; i + 2 <= mine; i += 2) {
       t1 = load_full(row_of(i + 1));
-      process(t0, 0, 64);
+      run(t0, 0, 64);
       t0 = load_full(row_of(i + 2));
-      process(t1, 0, 64);
+      run(t1, 0, 64);
     }
-    if (i < mine) process(t0, 0, 64);
+    if (i < mine) run(t0, 0, 64);
   }
   {
     // partial tiles: masked rows are loaded from the nearest valid row
@@ -434,7 +463,7 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
       const int lo = a.skip > base ? (int)(a.skip - base) : 0;
       const int hi = ht.n_tok - base < 64 ? (int)(ht.n_tok - base) : 64;
       const MqTile t = load_tile(base, base + lo, base + hi - 1);
-      process(t, lo, hi);
+      run(t, lo, hi);
     }
   }
 

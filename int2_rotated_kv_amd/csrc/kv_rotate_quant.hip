@@ -12,18 +12,17 @@
 // codes into 8 bytes.  Consecutive quads handle consecutive tokens of one
 // (batch, head), so a wave's code stores cover 512 contiguous bytes.
 //
-// The kernel is bound by VALU issue as much as by HBM (2.4 bytes of traffic
-// per element), so the per-element work is kept small: the fp16->fp32
-// conversion rides on the first butterfly (v_fma_mix), the 1/sqrt(128)
-// normalization rides on the quantizer's subtraction (one FMA), and
-// rounding + clamping + packing take three instructions per code (med3,
-// magic-number add, shift-add).
+// Every write kernel quantizes with one device function, quantize_group32:
+// the exact IEEE fp32 sequence of the format applied to the rotated row the
+// kernel computed (the Hadamard output times fp32(1/sqrt(128)), rounded
+// once), so codes, scales and zeros are bit-exact given the same rotated
+// row.  The conversion to fp32 rides on the first butterfly (v_fma_mix).
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
 namespace kvq {
 
-// Adding 1.5 * 2^23 to t in [0, 3] rounds t to an integer with round half
+// Adding 1.5 * 2^23 to t in [0, 15] rounds t to an integer with round half
 // to even and leaves that integer in the low mantissa bits.
 constexpr float kRoundMagic = 12582912.0f;          // 0x4B400000
 constexpr uint32_t kRoundMagicBits = 0x4B400000u;
@@ -55,11 +54,6 @@ __device__ __forceinline__ uint32_t pack16(F &&f, uint32_t acc) {
   }
 }
 
-__device__ __forceinline__ uint32_t code_bits(float u) {
-  const float t = __builtin_amdgcn_fmed3f(u, 0.0f, 3.0f);
-  return float_as_bits(t + kRoundMagic);            // = 0x4B400000 | code
-}
-
 // Group min/max over 32 values.
 __device__ __forceinline__ void minmax32(const float (&v)[32], float &mn, float &mx) {
   mn = v[0];
@@ -71,87 +65,53 @@ __device__ __forceinline__ void minmax32(const float (&v)[32], float &mn, float 
   }
 }
 
-// Scale and zero of a group whose fp32 min / max are mn / mx:
-// s = fp32(fp32(mx - mn) / 3); scale = fp16(s); zero = fp16(mn + 0), so a
-// zero minimum gives +0 whatever the signs of the group's zeros.
-__device__ __forceinline__ void scale_zero(float mn, float mx, uint16_t &sbits, uint16_t &zbits,
-                                           float &sf, float &zf) {
+// Quantize one group of 32 values of a row to b-bit codes (L = 2^b - 1
+// levels above the zero) with the exact IEEE fp32 sequence of the format:
+//   y     = v * c           (SCALED: v is the unnormalized Hadamard output and
+//                            c = fp32(1/sqrt(128)); otherwise y = v)
+//   s     = fp32(fp32(max y - min y) / L)    correctly rounded (div_by_levels)
+//   scale = fp16(s);  zero = fp16(min y + 0) (a zero minimum gives +0)
+//   inv   = fp32(1 / scale)                 correctly rounded (recip_of_half_value)
+//   code  = clamp(rint_half_even(fp32(fp32(y - zero) * inv)), 0, L)
+// and every code 0 when the scale is 0.  min/max of y are taken as c times
+// min/max of v: a positive scaling with one rounding is monotonic, so they
+// equal the min/max of the rounded y.  Word k of w holds codes
+// 32k/b .. 32(k+1)/b - 1, code i of a word at bits b*i.
+//
+// Two code forms give the same codes.  When every group of the wave has a
+// normal fp16 scale and |zero| <= 8 scale, u = fp32(fp32(y - zero) * inv)
+// lies in [-0.004, L + 0.012]: the fp16 roundings of the zero and the scale
+// move (y - min)/(range/L) in [0, L] by at most 8 2^-11 and L 2^-11.  Then
+// v_cvt_pk_u8_f32 (round half to even, saturating below 0) gives
+// clamp(rint(u), 0, L) directly and drops it into byte i/P of word i%P.
+// Otherwise u is clamped to [0, L] and rounded by adding 1.5 * 2^23 (clamp
+// then round equals round then clamp for integer bounds).
+template <int BITS, bool SCALED>
+__device__ __forceinline__ void quantize_group32(float (&v)[32], uint32_t (&w)[BITS],
+                                                 uint16_t &sbits, uint16_t &zbits) {
 #pragma clang fp contract(off)
-  const float range = mx - mn;
-  const float s32 = range / 3.0f;                   // correctly rounded division
-  sbits = float_to_half_bits(s32);
-  zbits = float_to_half_bits(mn + 0.0f);
-  sf = half_bits_to_float(sbits);
-  zf = half_bits_to_float(zbits);
-}
-
-// Exact quantizer on the rows as given (no rotation): the fixed IEEE fp32
-// sequence u = fp32(fp32(y - zero) * fp32(1/scale)), code = clamp(rint(u), 0, 3),
-// bit-for-bit.  clamp-then-round equals round-then-clamp for [0, 3].
-__device__ __forceinline__ void quantize_group32_exact(const float (&v)[32], uint32_t &w0,
-                                                       uint32_t &w1, uint16_t &sbits,
-                                                       uint16_t &zbits) {
-#pragma clang fp contract(off)
-  float mn, mx, sf, zf;
-  minmax32(v, mn, mx);
-  scale_zero(mn, mx, sbits, zbits, sf, zf);
-  const bool degenerate = (sf == 0.0f);
-  const float inv = 1.0f / (degenerate ? 1.0f : sf);
-  const uint32_t a = pack16([&](int i) { return code_bits((v[i] - zf) * inv); }, 0u);
-  const uint32_t b = pack16([&](int i) { return code_bits((v[16 + i] - zf) * inv); }, 0u);
-  w0 = degenerate ? 0u : a - kPackBias;
-  w1 = degenerate ? 0u : b - kPackBias;
-}
-
-// Quantizer on unnormalized FWHT outputs z (the rotated row is y = z * c,
-// c = fp32(1/sqrt(128))).  min/max of y are taken as c * min/max of z (the
-// rounding of a positive scaling is monotonic, so they equal the min/max of
-// the rounded y).  Per element: d = fp32(fma(z, c, -zero)) (y - zero with one
-// rounding), clamped to [0, L*scale] (L = 2^b - 1 levels above the zero for
-// b-bit codes), then fma(d, 1/scale, magic) rounds
-// d/scale to the nearest code with a single rounding.  This differs from the
-// three-rounding reference sequence only for arguments within a few ulps of
-// a half-integer.
-template <int BITS>
-__device__ __forceinline__ void quantize_group32_fwht(const float (&z)[32], uint32_t (&w)[BITS],
-                                                      uint16_t &sbits, uint16_t &zbits) {
-  // b-bit codes: L = 2^b - 1 levels above the zero; word k holds codes
-  // 32k/b .. 32(k+1)/b - 1, code i of a word at bits b*i.
   constexpr int L = (1 << BITS) - 1;
   constexpr int CPW = 32 / BITS;                    // codes per word
   constexpr int P = 8 / BITS;                       // codes per byte
-  constexpr float inv_levels = BITS == 1 ? 1.0f : BITS == 2 ? 0.3333333432674408f : 0.06666667014360428f;
   constexpr float c = 0.08838834764831845f;         // fp32(1/sqrt(128))
-  float zmn, zmx, sf, zf;
-  minmax32(z, zmn, zmx);
-  {
-    // The rotated path is compared at rounding ties, with a group's scale
-    // allowed one fp16 ulp of slack, so the two divisions of the exact
-    // sequence become a multiply by fp32(1/L) (within one fp32 ulp of the
-    // quotient) and v_rcp_f32 (within one ulp of 1/scale).
-    const float mn = zmn * c, mx = zmx * c;
-    const float s32 = (mx - mn) * inv_levels;
-    sbits = float_to_half_bits(s32);
-    zbits = float_to_half_bits(mn + 0.0f);
-    sf = half_bits_to_float(sbits);
-    zf = half_bits_to_float(zbits);
+  float mn, mx;
+  minmax32(v, mn, mx);
+  if constexpr (SCALED) {
+    mn = mn * c;
+    mx = mx * c;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = v[i] * c;
   }
+  const float range = mx - mn;
+  const float s32 = div_by_levels<L>(range);          // RN(range / L)
+  sbits = fp32_value_to_half_bits(s32);
+  zbits = float_to_half_bits(mn + 0.0f);
+  const float sf = half_bits_to_float(sbits);
+  const float zf = half_bits_to_float(zbits);
   const bool degenerate = (sf == 0.0f);
-  const float inv = __builtin_amdgcn_rcpf(degenerate ? 1.0f : sf);
-  // Fast form: x = z * (c/scale) - zero/scale in one FMA, then
-  // v_cvt_pk_u8_f32 rounds half to even, saturates below 0 and drops the
-  // code into byte i/P of word i%P; the P words merge into the b-bit
-  // layout.  Folding 1/scale into the constants adds an error of about
-  // (|y| + |zero|)/scale ulps, so the wave takes it only while every group
-  // has |zero| <= 8 scale and a normal fp16 scale.  Then x is within
-  // (L + 8) 2^-11 <= 0.012 of (y - min)/(range/L), which lies in [0, L]:
-  // the fp16 roundings of the scale and the zero move it by at most
-  // L 2^-11 and 8 2^-11.  So x rounds to a code in [0, L] with no clamp,
-  // and the codes are those of the clamped argument.  Otherwise the
-  // sequence below keeps y - zero to one rounding.
-  const float ci = c * inv, nzi = -zf * inv;
+  const float inv = recip_of_half_value(degenerate ? 1.0f : sf);   // RN(1 / scale)
   uint32_t r[BITS];
-  if (!__builtin_amdgcn_ballot_w64(fabsf(nzi) > 8.0f || sf < kMinNormalHalf)) {
+  if (!__builtin_amdgcn_ballot_w64(fabsf(zf) > 8.0f * sf || sf < kMinNormalHalf)) {
 #pragma unroll
     for (int k = 0; k < BITS; ++k) {
       uint32_t D[P];
@@ -159,8 +119,8 @@ __device__ __forceinline__ void quantize_group32_fwht(const float (&z)[32], uint
       for (int m = 0; m < P; ++m) D[m] = 0u;
 #pragma unroll
       for (int i = 0; i < CPW; ++i) {
-        const float x = __builtin_fmaf(z[k * CPW + i], ci, nzi);
-        D[i % P] = __builtin_amdgcn_cvt_pk_u8_f32(x, (uint32_t)(i / P), D[i % P]);
+        const float u = (v[k * CPW + i] - zf) * inv;
+        D[i % P] = __builtin_amdgcn_cvt_pk_u8_f32(u, (uint32_t)(i / P), D[i % P]);
       }
       uint32_t word = D[0];
 #pragma unroll
@@ -168,20 +128,22 @@ __device__ __forceinline__ void quantize_group32_fwht(const float (&z)[32], uint
       r[k] = word;
     }
   } else {
-    const float top = (float)L * sf;                  // exact: sf has 11 significant bits
-    auto code = [&](float zz) {
-      const float d = __builtin_amdgcn_fmed3f(__builtin_fmaf(zz, c, -zf), 0.0f, top);
-      return float_as_bits(__builtin_fmaf(d, inv, kRoundMagic));
-    };
+    uint32_t cb[32];                                  // 0x4B400000 | code
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float u = (v[i] - zf) * inv;
+      const float t = __builtin_amdgcn_fmed3f(u, 0.0f, (float)L);
+      cb[i] = float_as_bits(t + kRoundMagic);
+    }
     if constexpr (BITS == 2) {
-      r[0] = pack16([&](int i) { return code(z[i]); }, 0u) - kPackBias;
-      r[1] = pack16([&](int i) { return code(z[16 + i]); }, 0u) - kPackBias;
+      r[0] = pack16([&](int i) { return cb[i]; }, 0u) - kPackBias;
+      r[1] = pack16([&](int i) { return cb[16 + i]; }, 0u) - kPackBias;
     } else {
 #pragma unroll
       for (int k = 0; k < BITS; ++k) {
         uint32_t word = 0u;
 #pragma unroll
-        for (int i = 0; i < CPW; ++i) word |= (code(z[k * CPW + i]) - kRoundMagicBits) << (BITS * i);
+        for (int i = 0; i < CPW; ++i) word |= (cb[k * CPW + i] - kRoundMagicBits) << (BITS * i);
         r[k] = word;
       }
     }
@@ -316,17 +278,15 @@ __global__ __launch_bounds__(256) void kv_rotate_quant_rows(RowsKernelArgs a) {
                    (int64_t)h * a.stride_h + 32 * j;
   float v[32];
   load_row32<TIn, ROT>(src, v);
-  uint32_t w0, w1;
+  uint32_t w2[2];
   uint16_t sb, zb;
-  if (ROT) {
+  if constexpr (ROT) {
     fwht128_quad_rest(v, j);
-    uint32_t w2[2];
-    quantize_group32_fwht<2>(v, w2, sb, zb);
-    w0 = w2[0];
-    w1 = w2[1];
+    quantize_group32<2, true>(v, w2, sb, zb);
   } else {
-    quantize_group32_exact(v, w0, w1, sb, zb);
+    quantize_group32<2, false>(v, w2, sb, zb);
   }
+  const uint32_t w0 = w2[0], w1 = w2[1];
   const int64_t slot = seq_offset(a.offsets, a.t_offset, b) + t;
   if (valid && slot >= 0 && slot < s.T_cap) {       // a per-sequence slot outside the cache is skipped
     const int64_t row = write_row(a.block_table, a.max_pages, a.n_pages, a.page_tokens, a.Hkv, b, h, s.T_cap, slot);
@@ -527,7 +487,7 @@ __device__ __forceinline__ void fwht_f16_body(const RowsKernelArgs &a) {
       }
     }
     uint16_t sb, zb;
-    quantize_group32_fwht<BITS>(z, cw[g], sb, zb);
+    quantize_group32<BITS, true>(z, cw[g], sb, zb);
     csz[g] = (uint32_t)sb | ((uint32_t)zb << 16);
   }
   // Back through LDS to one row per lane (codes: the row's 16 b bytes,

@@ -102,12 +102,23 @@ __device__ __forceinline__ float pair_max(float v) {
 // the group.  Returns the group's 4 BITS code bytes in w (dword k = bytes
 // 4k .. 4k+3) and its scale / zero bits, identical in both lanes of the pair.
 // At 2 bits y[4q .. 4q+3] are the four codes of group byte 2q + half.
+//
+// The codes follow the exact IEEE fp32 sequence of the format on the
+// rotated row y (the matrix cores' fp32 result): s = fp32(fp32(max - min)/L)
+// and inv = fp32(1/scale) as correctly rounded divisions, scale = fp16(s),
+// zero = fp16(min + 0), code = clamp(rint_half_even(fp32(fp32(y - zero) *
+// inv)), 0, L), all codes 0 for a zero scale.  While every group of the
+// wave has a normal fp16 scale and |zero| <= 8 scale the argument lies in
+// [-0.004, L + 0.012] (the fp16 roundings of the zero and the scale move
+// (y - min)/(range/L) by at most 8 2^-11 and L 2^-11), so v_cvt_pk_u8_f32
+// (round half to even, saturating below 0) gives the clamped code
+// directly; otherwise the argument is clamped to [0, L] and rounded by
+// adding 1.5 * 2^23.
 template <int BITS>
 __device__ __forceinline__ void dense_group_codes(const float16_t &y, uint32_t (&w)[BITS],
                                                   uint16_t &sbits, uint16_t &zbits) {
 #pragma clang fp contract(off)
   constexpr int L = (1 << BITS) - 1;
-  constexpr float inv_levels = BITS == 1 ? 1.0f : BITS == 2 ? 0.3333333432674408f : 0.06666667014360428f;
   float mn = y[0], mx = y[0];
 #pragma unroll
   for (int r = 1; r < 16; ++r) {
@@ -116,44 +127,43 @@ __device__ __forceinline__ void dense_group_codes(const float16_t &y, uint32_t (
   }
   mn = pair_min(mn);
   mx = pair_max(mx);
-  // The rotated path is compared at rounding ties with one fp16 ulp of slack
-  // on a group's scale, so s = range * fp32(1/L) and 1/scale = v_rcp_f32.
-  const float s32 = (mx - mn) * inv_levels;
-  sbits = float_to_half_bits(s32);
+  const float range = mx - mn;
+  const float s32 = div_by_levels<L>(range);          // RN(range / L)
+  sbits = fp32_value_to_half_bits(s32);
   zbits = float_to_half_bits(mn + 0.0f);
   const float sf = half_bits_to_float(sbits);
   const float zf = half_bits_to_float(zbits);
-  // scale 0: every code is 0 (inv = 1 and the clamp to [0, 0] give that)
-  const float inv = __builtin_amdgcn_rcpf(sf == 0.0f ? 1.0f : sf);
-  const float nzi = -zf * inv;
-  // Two instructions per code while every group of the wave has
-  // |zero| <= 8 scale and a normal fp16 scale: x = y/scale - zero/scale in
-  // one FMA, then v_cvt_pk_u8_f32 (round half to even, saturating below 0)
-  // into byte r/4 of word r%4; the words merge into the b-bit layout.  x is
-  // then within (L + 8) 2^-11 of (y - min)/(range/L), which lies in [0, L],
-  // so it rounds to a code in [0, L] with no clamp.  Otherwise (or for a
-  // zero scale) the sequence below keeps y - zero to one rounding.
-  const bool fast = !__builtin_amdgcn_ballot_w64(fabsf(nzi) > 8.0f || sf < kMinNormalHalf);
+  const bool degenerate = (sf == 0.0f);
+  const float inv = recip_of_half_value(degenerate ? 1.0f : sf);   // RN(1 / scale)
+  const bool fast = !__builtin_amdgcn_ballot_w64(fabsf(zf) > 8.0f * sf || sf < kMinNormalHalf);
+  // code r of the lane, in byte r/4 of word r%4 (fast) or as 0x4B400000 | code
+  uint32_t D[4] = {0u, 0u, 0u, 0u};
+  uint32_t cb[16];
+  if (fast) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float u = (y[r] - zf) * inv;
+      D[r & 3] = __builtin_amdgcn_cvt_pk_u8_f32(u, (uint32_t)(r >> 2), D[r & 3]);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float u = (y[r] - zf) * inv;
+      const float t = __builtin_amdgcn_fmed3f(u, 0.0f, (float)L);
+      cb[r] = float_as_bits(t + kDenseRoundMagic);
+    }
+  }
   if constexpr (BITS != 2) {
     // D[e] byte q = code of the lane's channel 8q + 4 half + e
-    uint32_t D[4] = {0u, 0u, 0u, 0u};
-    if (fast) {
+    if (!fast) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        D[r & 3] = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(y[r], inv, nzi), (uint32_t)(r >> 2), D[r & 3]);
-    } else {
-      const float top = (float)L * sf;               // exact: sf has 11 significant bits
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float d = __builtin_amdgcn_fmed3f(y[r] - zf, 0.0f, top);
-        D[r & 3] |= (float_as_bits(__builtin_fmaf(d, inv, kDenseRoundMagic)) - 0x4B400000u) << (8 * (r >> 2));
-      }
+      for (int r = 0; r < 16; ++r) D[r & 3] |= (cb[r] - 0x4B400000u) << (8 * (r >> 2));
     }
     if constexpr (BITS == 1) {
       // channel 8q + 4 half + e is bit 4 half + e of group byte q
       const uint32_t mine = D[0] | (D[1] << 1) | (D[2] << 2) | (D[3] << 3);
       const auto ex = __builtin_amdgcn_permlane32_swap(mine, mine, false, false);
-      w[0] = ex[0] | (ex[1] << 4);
+      w[0] = degenerate ? 0u : (ex[0] | (ex[1] << 4));
     } else {
       // channel 8q + 4 half + e is nibble e % 2 of group byte 4q + 2 half + e / 2
       const uint32_t a = D[0] | (D[1] << 4), c = D[2] | (D[3] << 4);
@@ -164,28 +174,18 @@ __device__ __forceinline__ void dense_group_codes(const float16_t &y, uint32_t (
         // bytes 4q .. 4q+3: lower half's (a, c) byte q, then the upper half's
         const uint32_t lo = __builtin_amdgcn_perm(ec[0], ea[0], (uint32_t)(q | (q + 4) << 8) | 0x0C0C0000u);
         const uint32_t hi = __builtin_amdgcn_perm(ec[1], ea[1], 0x0C0Cu | (uint32_t)(q << 16 | (q + 4) << 24));
-        w[q] = lo | hi;
+        w[q] = degenerate ? 0u : (lo | hi);
       }
     }
     return;
   }
   uint32_t mine;
   if (fast) {
-    uint32_t D[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float x = __builtin_fmaf(y[r], inv, nzi);
-      D[r & 3] = __builtin_amdgcn_cvt_pk_u8_f32(x, (uint32_t)(r >> 2), D[r & 3]);
-    }
     mine = D[0] | (D[1] << 2) | (D[2] << 4) | (D[3] << 6);
   } else {
-    const float top = 3.0f * sf;
-    auto code = [&](int r) {
-      const float d = __builtin_amdgcn_fmed3f(y[r] - zf, 0.0f, top);
-      return float_as_bits(__builtin_fmaf(d, inv, kDenseRoundMagic));
-    };
-    mine = dense_pack16(code, 0u) - kDensePackBias;   // byte q = group byte 2q + half
+    mine = dense_pack16([&](int r) { return cb[r]; }, 0u) - kDensePackBias;   // byte q = group byte 2q + half
   }
+  mine = degenerate ? 0u : mine;
   const auto ex = __builtin_amdgcn_permlane32_swap(mine, mine, false, false);
   const uint32_t e = ex[0], o = ex[1];          // bytes of the lower / upper half
   w[0] = __builtin_amdgcn_perm(o, e, 0x05010400u);   // e0 o0 e1 o1

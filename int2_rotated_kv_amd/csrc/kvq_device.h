@@ -31,6 +31,48 @@ __device__ __forceinline__ uint16_t float_to_half_bits(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
+// fp32 -> fp16 (round to nearest even) of a value that must first exist as
+// an fp32 number: the empty asm keeps the compiler from folding the FMA that
+// produced x into a mixed-precision FMA with an fp16 result, which would
+// round once to fp16 instead of to fp32 and then to fp16 as the format's
+// scale is defined (the two differ when the fp32 value lands on an fp16
+// rounding boundary).
+__device__ __forceinline__ uint16_t fp32_value_to_half_bits(float x) {
+  asm volatile("" : "+v"(x));
+  return float_to_half_bits(x);
+}
+
+// The two divisions of the quantizer, correctly rounded, without the
+// general IEEE division sequence.
+// s = RN(range / L) for L = 3 or 15: q0 = range * RN(1/L), then one FMA
+// residual step (Markstein); equal to the correctly rounded quotient for
+// every non-negative finite fp32 range (checked exhaustively on the host by
+// the same operation sequence).  L = 1: s = range.
+template <int L>
+__device__ __forceinline__ float div_by_levels(float range) {
+#pragma clang fp contract(off)
+  if constexpr (L == 1) {
+    return range;
+  } else {
+    static_assert(L == 3 || L == 15, "levels of 2- or 4-bit codes");
+    constexpr float y = L == 3 ? 0.3333333432674408f : 0.06666667014360428f;   // RN(1/L)
+    const float q0 = range * y;
+    const float r = __builtin_fmaf(-(float)L, q0, range);      // exact residual
+    return __builtin_fmaf(r, y, q0);
+  }
+}
+
+// RN(1/s) for a positive finite fp16 value s (held in fp32): v_rcp_f32
+// (within one ulp of 1/s) and one Newton step with FMAs; equal to the
+// correctly rounded reciprocal for every such s and every start within two
+// ulps of 1/s (checked exhaustively on the host).
+__device__ __forceinline__ float recip_of_half_value(float s) {
+#pragma clang fp contract(off)
+  const float y0 = __builtin_amdgcn_rcpf(s);
+  const float e = __builtin_fmaf(-s, y0, 1.0f);
+  return __builtin_fmaf(e, y0, y0);
+}
+
 // First cache slot of sequence b's new rows: the call's t_offset, or
 // offsets[b] for a per-sequence append.
 __device__ __forceinline__ int64_t seq_offset(const int32_t *offsets, int64_t t_offset, int64_t b) {

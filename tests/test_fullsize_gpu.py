@@ -45,6 +45,31 @@ def _contiguous_head(c, b, hk):
     return tuple(a[b, hk] for a in (c.codes, c.scales, c.zeros))
 
 
+# Scale/zero groups that may differ by one fp16 ulp (each only at an fp16
+# rounding boundary of the exact value, which compare_codes_at_ties checks):
+# the rounding of the fp32 Hadamard transform moves about 6e-5 of the groups
+# of these workloads across a boundary, the fp16 hi/lo split of a dense R
+# about 5e-4 (both measured by emulating the transform in numpy float32).
+GROUP_RATE = {"hadamard": 1e-4, "perm": 1e-4, "dense": 1e-3}
+
+
+class GroupTally:
+    """Scale/zero mismatches over the sampled heads of one test."""
+
+    def __init__(self, rot):
+        self.rot, self.diff, self.groups = rot, 0, 0
+
+    def add(self, stats):
+        for side in stats.values():
+            self.diff += side["group_scale_zero_diff"]
+            self.groups += side["groups"]
+
+    def check(self, name):
+        rate = self.diff / max(self.groups, 1)
+        _report(f"{name} scale/zero group mismatch", rate=rate, groups=self.groups)
+        assert rate <= GROUP_RATE[self.rot], f"scale/zero mismatch rate {rate:.3g}"
+
+
 def _check_head(cfg, Kd, Vd, ck, cv, out, q, b, hk, rot, R, t_begin, t_end,
                 sink=None, res=None, code_end=None, head_rows=_contiguous_head):
     """Codes of head (b, hk) vs oracle at ties (rows [t_begin, code_end),
@@ -93,10 +118,13 @@ def test_fullsize_config3_throughput():
     out = kvq.kvq_decode_attention(q, ck, cv, 0, T, rot="hadamard")
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
+    tally = GroupTally("hadamard")
     for b, hk in ((0, 0), (7, 13), (15, 31)):
         stats, err = _check_head(cfg, K, V, ck, cv, out, q, b, hk, "hadamard", None, 0, T)
         _report(f"c3 b={b} h={hk}", normwise=err, K=stats["K"], V=stats["V"])
+        tally.add(stats)
         assert err <= ATTN_TOL
+    tally.check("c3")
 
 
 def test_fullsize_config4_dense_gqa():
@@ -114,10 +142,13 @@ def test_fullsize_config4_dense_gqa():
     out = kvq.kvq_decode_attention(q, ck, cv, 0, T, rot="dense", R=Rg)
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
+    tally = GroupTally("dense")
     for b, hk in ((0, 0), (3, 5)):
         stats, err = _check_head(cfg, K, V, ck, cv, out, q, b, hk, "dense", R, 0, T)
         _report(f"c4 b={b} h={hk}", normwise=err, K=stats["K"], V=stats["V"])
+        tally.add(stats)
         assert err <= ATTN_TOL
+    tally.check("c4")
 
 
 def test_fullsize_config5_sinks_residual():
@@ -136,13 +167,16 @@ def test_fullsize_config5_sinks_residual():
     out_int2 = kvq.kvq_decode_attention(q, ck, cv, tb, te, rot="hadamard")
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all() and torch.isfinite(out_int2.float()).all()
+    tally = GroupTally("hadamard")
     for b, hk in ((0, 0), (5, 27)):
         stats, err = _check_head(cfg, K, V, ck, cv, out, q, b, hk, "hadamard", None, tb, te,
                                  sink=sink, res=res)
         _, err2 = _check_head(cfg, K, V, ck, cv, out_int2, q, b, hk, "hadamard", None, tb, te)
         _report(f"c5 b={b} h={hk}", normwise_full=err, normwise_int2_only=err2,
                 K=stats["K"], V=stats["V"])
+        tally.add(stats)
         assert err <= ATTN_TOL and err2 <= ATTN_TOL
+    tally.check("c5")
 
 
 def test_fullsize_config3_key4_value2():
@@ -158,10 +192,13 @@ def test_fullsize_config3_key4_value2():
     out = kvq.kvq_decode_attention(q, ck, cv, 0, T, rot="hadamard")
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
+    tally = GroupTally("hadamard")
     for b, hk in ((0, 0), (9, 17)):
         stats, err = _check_head(cfg, K, V, ck, cv, out, q, b, hk, "hadamard", None, 0, T)
         _report(f"c3 K4V2 b={b} h={hk}", normwise=err, K=stats["K"], V=stats["V"])
+        tally.add(stats)
         assert err <= ATTN_TOL
+    tally.check("c3 K4V2")
 
 
 def test_fullsize_config3_varlen():
@@ -250,7 +287,10 @@ def test_fullsize_config4_dense_gqa_key4_value2():
     out = kvq.kvq_decode_attention(q, ck, cv, 0, T, rot="dense", R=Rg)
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
+    tally = GroupTally("dense")
     for b, hk in ((1, 2), (3, 7)):
         stats, err = _check_head(cfg, K, V, ck, cv, out, q, b, hk, "dense", R, 0, T)
         _report(f"c4 K4V2 b={b} h={hk}", normwise=err, K=stats["K"], V=stats["V"])
+        tally.add(stats)
         assert err <= ATTN_TOL
+    tally.check("c4 K4V2")
