@@ -369,6 +369,40 @@ kvq_status kvq_decode_attention_paged(const void *q, kvq_dtype q_dtype,
                                       void *workspace, size_t workspace_bytes,
                                       void *stream);
 
+/*
+ * kvq_decode_attention_noalloc -- kvq_decode_attention without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * call allocates nothing (no hipMalloc, no hipFree): its scratch memory (the
+ * prepared queries and the split partials) is a static device array of
+ * KVQ_NOALLOC_SCRATCH_BYTES bytes per GPU, which each GPU the library runs on
+ * holds until the process ends.  Its device address is looked up on the first
+ * call on a GPU (that GPU current), so the first call also makes that lookup;
+ * `stream` must belong to the current GPU.
+ *
+ *  - Sizes whose scratch (kvq_decode_workspace_bytes of the same arguments)
+ *    exceeds KVQ_NOALLOC_SCRATCH_BYTES return KVQ_ERR_WORKSPACE_TOO_SMALL and
+ *    enqueue nothing; use kvq_decode_attention with a workspace there.
+ *  - Every call on one GPU shares that GPU's array, which keeps the last
+ *    call's contents; nothing in it needs to start at zero (each call writes
+ *    every byte it reads).  Calls that overlap on one GPU (different streams,
+ *    or host threads racing) race on the array and give unspecified results;
+ *    calls in one stream are ordered and safe.
+ *  Every other argument, and the result, as for kvq_decode_attention.
+ */
+#define KVQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+kvq_status kvq_decode_attention_noalloc(const void *q, kvq_dtype q_dtype,
+                                        int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
+                                        const kvq_int2_cache *kc,
+                                        const kvq_int2_cache *vc,
+                                        int64_t t_begin, int64_t t_end,
+                                        kvq_rot rot, const void *R, int group,
+                                        const uint16_t *sink_k, const uint16_t *sink_v,
+                                        int64_t n_sink,
+                                        const uint16_t *res_k, const uint16_t *res_v,
+                                        int64_t n_res, float softmax_scale,
+                                        void *out, kvq_dtype out_dtype, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *kvq_status_str(kvq_status s);
 

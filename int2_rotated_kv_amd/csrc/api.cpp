@@ -221,7 +221,7 @@ kvq_status decode_impl(const void *q, kvq_dtype q_dtype, int64_t B, int64_t Hq,
                        const uint16_t *res_k, const uint16_t *res_v, int64_t n_res,
                        float softmax_scale, void *out, kvq_dtype out_dtype,
                        void *workspace, size_t workspace_bytes_given, void *stream,
-                       const Paging *pg = nullptr) {
+                       const Paging *pg = nullptr, bool static_scratch = false) {
   if (!valid_dtype(q_dtype) || !valid_dtype(out_dtype)) return KVQ_ERR_INVALID_ARG;
   if (q == nullptr || out == nullptr || !aligned16(q) || !aligned16(out)) return KVQ_ERR_INVALID_ARG;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return KVQ_ERR_INVALID_ARG;
@@ -246,6 +246,13 @@ kvq_status decode_impl(const void *q, kvq_dtype q_dtype, int64_t B, int64_t Hq,
   if (!(softmax_scale == softmax_scale)) return KVQ_ERR_INVALID_ARG;   // NaN
   const kvq::SplitPlan plan = kvq::plan_splits(B, Hq, Hkv, n_int2);
   const size_t need = workspace_bytes(B, Hq, plan.n_splits);
+  if (static_scratch) {
+    // the library's own scratch array of this GPU (every argument is checked
+    // by now: this is the call's first HIP call)
+    if (need > (size_t)KVQ_NOALLOC_SCRATCH_BYTES) return KVQ_ERR_WORKSPACE_TOO_SMALL;
+    if (kvq::noalloc_scratch(&workspace) != hipSuccess) return KVQ_ERR_HIP;
+    workspace_bytes_given = KVQ_NOALLOC_SCRATCH_BYTES;
+  }
   if (workspace == nullptr || ((uintptr_t)workspace & 255u) != 0) return KVQ_ERR_INVALID_ARG;
   if (workspace_bytes_given < need) return KVQ_ERR_WORKSPACE_TOO_SMALL;
 
@@ -301,6 +308,19 @@ kvq_status kvq_decode_attention(const void *q, kvq_dtype q_dtype, int64_t B, int
   return decode_impl(q, q_dtype, B, Hq, Hkv, d, k2.p, v2.p, t_begin, t_end, nullptr, rot, R, group,
                      sink_k, sink_v, n_sink, res_k, res_v, n_res, softmax_scale, out, out_dtype,
                      workspace, workspace_bytes_given, stream);
+}
+
+kvq_status kvq_decode_attention_noalloc(const void *q, kvq_dtype q_dtype, int64_t B, int64_t Hq,
+                                        int64_t Hkv, int64_t d, const kvq_int2_cache *kc,
+                                        const kvq_int2_cache *vc, int64_t t_begin, int64_t t_end,
+                                        kvq_rot rot, const void *R, int group,
+                                        const uint16_t *sink_k, const uint16_t *sink_v, int64_t n_sink,
+                                        const uint16_t *res_k, const uint16_t *res_v, int64_t n_res,
+                                        float softmax_scale, void *out, kvq_dtype out_dtype, void *stream) {
+  const AsQuant k2(kc), v2(vc);
+  return decode_impl(q, q_dtype, B, Hq, Hkv, d, k2.p, v2.p, t_begin, t_end, nullptr, rot, R, group,
+                     sink_k, sink_v, n_sink, res_k, res_v, n_res, softmax_scale, out, out_dtype,
+                     nullptr, 0, stream, nullptr, true);
 }
 
 kvq_status kvq_decode_attention_bits(const void *q, kvq_dtype q_dtype, int64_t B, int64_t Hq,

@@ -79,4 +79,9 @@ constexpr int kPartialStride = 132;   // o'[128], m, l, 2 pad (16-byte rows)
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 
+// Device address of this GPU's static scratch array (KVQ_NOALLOC_SCRATCH_BYTES
+// bytes, 256-byte aligned), looked up on the first call per GPU; the current
+// device is the GPU.
+hipError_t noalloc_scratch(void **ptr);
+
 }  // namespace kvq

@@ -30,7 +30,7 @@ EXPORTED_SYMBOLS = ("kvq_quantize", "kvq_quantize_at", "kvq_quantize_bits", "kvq
                     "kvq_quantize_paged", "kvq_decode_workspace_bytes", "kvq_decode_attention",
                     "kvq_decode_attention_varlen", "kvq_decode_attention_bits",
                     "kvq_decode_attention_varlen_bits", "kvq_decode_attention_paged",
-                    "kvq_status_str", "kvq_abi_version")
+                    "kvq_decode_attention_noalloc", "kvq_status_str", "kvq_abi_version")
 
 D_HEAD = 128
 GROUP = 32
@@ -92,6 +92,10 @@ def load_library() -> ctypes.CDLL:
     lib.kvq_decode_attention.argtypes = [vp, i32, i64, i64, i64, i64, cp, cp, i64, i64,
                                          i32, vp, i32, vp, vp, i64, vp, vp, i64, f32,
                                          vp, i32, vp, ctypes.c_size_t, vp]
+    lib.kvq_decode_attention_noalloc.restype = i32
+    lib.kvq_decode_attention_noalloc.argtypes = [vp, i32, i64, i64, i64, i64, cp, cp, i64, i64,
+                                                 i32, vp, i32, vp, vp, i64, vp, vp, i64, f32,
+                                                 vp, i32, vp]
     qp = ctypes.POINTER(kvq_quant_cache)
     lib.kvq_quantize_bits.restype = i32
     lib.kvq_quantize_bits.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, i64, i64,
@@ -439,6 +443,49 @@ def kvq_decode_attention(q: torch.Tensor, cache_k: Int2Cache | None,
         float(softmax_scale), _ptr(out), _dtype_code(out),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "kvq_decode_attention")
+    return out
+
+
+def kvq_decode_attention_noalloc(q: torch.Tensor, cache_k: Int2Cache | None,
+                                 cache_v: Int2Cache | None, t_begin: int, t_end: int,
+                                 rot: str = "hadamard", R: torch.Tensor | None = None,
+                                 group: int = GROUP, sink_k=None, sink_v=None, res_k=None,
+                                 res_v=None, softmax_scale: float = 0.0,
+                                 out: torch.Tensor | None = None, stream=None):
+    """kvq_decode_attention over an INT2 cache with the library's static
+    scratch instead of a workspace (kvq_decode_attention_noalloc): the call
+    allocates nothing when `out` is given.  Calls that overlap on one GPU
+    race on that scratch."""
+    _need(q.dim() == 3, "q must be [B, Hq, 128]")
+    B, Hq, d = q.shape
+    _need((cache_k is None) == (cache_v is None), "give both cache sides or neither")
+    Hkv = (cache_k.codes.shape[1] if cache_k is not None
+           else (sink_k if sink_k is not None else res_k).shape[1] if (sink_k is not None or res_k is not None)
+           else 0)
+    _need(Hkv > 0, "no cache and no fp16 tokens")
+    _check_query(q, out, Hkv)
+    if cache_k is not None:
+        for c, what in ((cache_k, "cache_k"), (cache_v, "cache_v")):
+            _check_cache(c, (B, Hkv), what)
+            _need(c.bits == 2, f"{what}: the no-allocation decode takes 2-bit caches")
+            _need(0 <= t_begin <= t_end <= c.T_cap, f"{what}: token range [{t_begin}, {t_end}) "
+                  f"outside the cache's {c.T_cap} slots")
+    n_sink = _check_fp16_tokens(sink_k, sink_v, B, Hkv, "sink")
+    n_res = _check_fp16_tokens(res_k, res_v, B, Hkv, "residual")
+    _check_rotation(rot, R, Hkv)
+    _check_device((q, out, R, sink_k, sink_v, res_k, res_v, *_cache_tensors(cache_k), *_cache_tensors(cache_v)))
+    if out is None:
+        out = torch.empty_like(q)
+    kc = cache_k.c_struct() if cache_k is not None else None
+    vc = cache_v.c_struct() if cache_v is not None else None
+    st = load_library().kvq_decode_attention_noalloc(
+        _ptr(q), _dtype_code(q), B, Hq, Hkv, d,
+        ctypes.byref(kc) if kc is not None else None,
+        ctypes.byref(vc) if vc is not None else None,
+        t_begin, t_end, _ROT[rot], _ptr(R), group,
+        _ptr(sink_k), _ptr(sink_v), n_sink, _ptr(res_k), _ptr(res_v), n_res,
+        float(softmax_scale), _ptr(out), _dtype_code(out), _stream(stream))
+    _check(st, "kvq_decode_attention_noalloc")
     return out
 
 
