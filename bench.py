@@ -73,6 +73,9 @@ def parse():
     p.add_argument("--kbits", type=int, default=2, choices=(1, 2, 4),
                    help="key code width (1 and 4: the b-bit write and decode kernels)")
     p.add_argument("--vbits", type=int, default=2, choices=(1, 2, 4), help="value code width")
+    p.add_argument("--prerope", type=int, default=0, choices=(0, 1, 2, 4), metavar="G",
+                   help="keys written before RoPE with the grouped-head rotation over G heads "
+                        "(kvq_quantize_prerope / kvq_decode_attention_prerope), on a Hadamard workload")
     p.add_argument("--config", type=int, default=3, choices=(3, 4, 5),
                    help="workload id (3 = throughput case, 4 = GQA dense rotation, 5 = sinks)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -184,6 +187,11 @@ def main():
     kbits, vbits = args.kbits, args.vbits
     if (kbits, vbits) != (2, 2):
         workload += f"_k{kbits}v{vbits}"
+    GHP = args.prerope
+    if GHP:
+        if rot != "hadamard" or args.varlen or args.paged or (args.kbits, args.vbits) != (2, 2):
+            sys.exit("--prerope applies to the Hadamard workloads (--config 3 or 5), 2-bit, contiguous")
+        workload += f"_prerope{GHP}"
     P = args.paged
     if P:
         if P % 64 or rot == "dense":
@@ -216,6 +224,8 @@ def main():
         if P:
             offs = offsets if offsets is not None else torch.full((B,), first, dtype=torch.int32, device=dev)
             kvq.kvq_quantize_paged(Kx, Vx, ck, cv, offs, table, rot=rot, R=R)
+        elif GHP:
+            kvq.kvq_quantize_prerope(Kx, Vx, ck, cv, group_heads=GHP, t_offset=first)
         elif offsets is not None:
             kvq.kvq_quantize(Kx, Vx, ck, cv, rot=rot, R=R, t_offsets=offsets)
         else:
@@ -227,7 +237,8 @@ def main():
                     sink_v=V[:, :tb].permute(0, 2, 1, 3).contiguous(),
                     res_k=K[:, te:].permute(0, 2, 1, 3).contiguous(),
                     res_v=V[:, te:].permute(0, 2, 1, 3).contiguous())
-    ws_bytes = kvq.kvq_decode_workspace_bytes(B, cfg.Hq, H, d, te - tb, cfg.n_sink, cfg.n_res)
+    ws_bytes = (kvq.kvq_decode_workspace_bytes_prerope if GHP else kvq.kvq_decode_workspace_bytes)(
+        B, cfg.Hq, H, d, te - tb, cfg.n_sink, cfg.n_res)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
     Kq, Vq = K[:, q0:q1], V[:, q0:q1]
@@ -259,7 +270,10 @@ def main():
             write(Kq, Vq, first=q0)
 
     def decode():
-        if P:
+        if GHP:
+            kvq.kvq_decode_attention_prerope(q, ck, cv, tb, te, group_heads=GHP, out=out, workspace=ws,
+                                             **fp16)
+        elif P:
             kvq.kvq_decode_attention_paged(q, ck, cv, tb, ends, te, table, rot=rot, R=R, out=out,
                                            workspace=ws, **fp16)
         else:
@@ -350,9 +364,12 @@ def main():
               "units_per_launch": B * n_q * H, "avg_ms": round(q_ms, 4)}
     d_kernel, d_src = (("kv_int2_decode_attn", "kv_decode.hip") if cfg.G == 1
                        else ("kv_int2_decode_attn_gqa", "kv_decode_gqa.hip"))
+    if GHP:
+        q_kernel = f"kv_rotate_quant_fwht_grouped_f16<{GHP}> + kv_rotate_quant_fwht_f16" if GHP > 1 else q_kernel
+        d_kernel, d_src = f"kv_prerope_scores<{GHP}> + kv_int2_decode_attn<4, true>", "kv_decode_prerope.hip"
     # the query preparation is its own launch only for a dense rotation or
     # grouped-query attention; otherwise the attention waves do it
-    prep_kernel = cfg.G > 1 or rot in ("dense", "perm")
+    prep_kernel = (cfg.G > 1 or rot in ("dense", "perm")) and not GHP
     if (kbits, vbits) != (2, 2):                   # the b-bit kernel prepares its query itself
         d_kernel, d_src = f"kv_quant_decode_attn<{kbits},{vbits}>", "kv_decode_generic.hip"
         prep_kernel = rot == "dense"                 # except a dense R's
@@ -377,7 +394,8 @@ def main():
                    "kv_input": "f16",
                    "cache": ("int2 codes + f16 scale/zero, group 32" if (kbits, vbits) == (2, 2) else
                              f"{kbits}-bit key / {vbits}-bit value codes + f16 scale/zero, group 32"),
-                   "rotation": rot, "int2_tokens": [tb, te],
+                   "rotation": rot if not GHP else f"keys: pre-RoPE Hadamard over {GHP} heads; values: Hadamard",
+                   "int2_tokens": [tb, te],
                    "quantize_tokens": ("one appended row per sequence, at its own end" if args.varlen
                                        else [q0, q1]),
                    "fp16_tokens": n_f16,
@@ -398,11 +416,11 @@ def main():
     }
     rec["copy_reference_gbs"] = copy_bandwidth()
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(cfg, rot, K, V, q, R, fp16, kbits, vbits)
+        rec["cpu_baseline"] = cpu_baseline(cfg, rot, K, V, q, R, fp16, kbits, vbits, GHP)
     print(json.dumps(rec), flush=True)
 
 
-def cpu_baseline(cfg, rot, K, V, q, R, fp16, kbits=2, vbits=2):
+def cpu_baseline(cfg, rot, K, V, q, R, fp16, kbits=2, vbits=2, ghp=0):
     """The oracle, untouched, on a bounded sample of the same workload:
     batch 0, all KV heads, all tokens of the INT2 range (1/B of the job).
     The sample's inputs are the generator's values (copied from the
@@ -423,10 +441,20 @@ def cpu_baseline(cfg, rot, K, V, q, R, fp16, kbits=2, vbits=2):
     qs = q[0:1].cpu().numpy()
     kw = {k: v[0:1].cpu().numpy() for k, v in fp16.items()}
     t0 = time.perf_counter()
-    kc = O.quantize_cache(kh, Rm, bits=kbits)
-    vc = O.quantize_cache(vh, Rm, bits=vbits)
+    if ghp:
+        # positions are the cache slots [tb, te): the sample's rows shifted to 0
+        # would change the angles, so the decode runs on a cache of te slots
+        kc = O.quantize_cache_grouped(kh, ghp)
+        vc = O.quantize_cache(vh, Rm)
+    else:
+        kc = O.quantize_cache(kh, Rm, bits=kbits)
+        vc = O.quantize_cache(vh, Rm, bits=vbits)
     t1 = time.perf_counter()
-    O.decode_attention(qs, kc, vc, 0, te - tb, Rm, **kw)
+    if ghp:
+        pad = lambda a: np.concatenate([np.zeros(a.shape[:2] + (tb,) + a.shape[3:], a.dtype), a], axis=2)
+        O.decode_attention_prerope(qs, tuple(map(pad, kc)), tuple(map(pad, vc)), tb, te, ghp, **kw)
+    else:
+        O.decode_attention(qs, kc, vc, 0, te - tb, Rm, **kw)
     t2 = time.perf_counter()
     n_f16 = cfg.n_sink + cfg.n_res
     d_bytes = ((te - tb) * cfg.Hkv * (row_bytes(kbits) + row_bytes(vbits))

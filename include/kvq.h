@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 6
+#define KVQ_ABI_VERSION 7
 
 typedef enum {
   KVQ_OK = 0,
@@ -368,6 +368,76 @@ kvq_status kvq_decode_attention_paged(const void *q, kvq_dtype q_dtype,
                                       void *out, kvq_dtype out_dtype,
                                       void *workspace, size_t workspace_bytes,
                                       void *stream);
+
+/*
+ * Pre-RoPE grouped-head rotation of the keys (RotateKV, IJCAI 2025 record,
+ * abstract item (ii): keys are rotated before the rotary position embedding,
+ * and across a group of heads, so that RoPE does not disturb the rotation
+ * and outliers spread over heads).  The record fixes neither the embedding
+ * nor the grouping; this library reads them as follows.
+ *  - Keys are given BEFORE RoPE.  The rows of group_heads (g) consecutive KV
+ *    heads of a token form one row of 128 g channels (head j of the group at
+ *    channels 128 j .. 128 j + 127), rotated by the normalized Sylvester
+ *    Hadamard matrix of size 128 g; head j's 128-channel slice is its cache
+ *    row, in the INT2 format above.  g = 1 is the per-head Hadamard rotation.
+ *  - Values carry no RoPE and keep the per-head Hadamard rotation.
+ *  - RoPE is the rotate-half form: channel i pairs with i + 64, and pair i
+ *    turns by the angle t * rope_base^(-2i/128) at position t.  An INT2 key's
+ *    position is its cache slot t.
+ *  - The decode query is given AFTER RoPE (at its own position), as a model
+ *    produces it; fp16 sink / residual keys are kept as a plain fp16 cache
+ *    keeps them: after RoPE, unrotated.  Their values are unrotated.
+ * The decode therefore computes, for INT2 token t of KV head h,
+ *    s_t = softmax_scale * q . rope_t(slice_h(k_hat_group,t R_g^T)).
+ */
+
+/*
+ * kvq_quantize_prerope -- write pre-RoPE keys with the grouped-head rotation
+ * and values with the per-head Hadamard rotation into INT2 caches.
+ *  group_heads  1, 2 or 4 heads per rotation group; Hkv must be a multiple
+ *               of it (KVQ_ERR_INVALID_ARG), and of 4 when group_heads > 1
+ *               (KVQ_ERR_UNSUPPORTED).
+ *  in_dtype     KVQ_F16 (KVQ_F32 gives KVQ_ERR_UNSUPPORTED).
+ *  Every other argument as for kvq_quantize (rot = KVQ_ROT_HADAMARD, R = NULL).
+ */
+kvq_status kvq_quantize_prerope(const void *K, const void *V, kvq_dtype in_dtype,
+                                int64_t B, int64_t T_new, int64_t Hkv, int64_t d,
+                                int64_t stride_b, int64_t stride_t, int64_t stride_h,
+                                int group_heads, int group, int64_t t_offset,
+                                const kvq_int2_cache *kc, const kvq_int2_cache *vc,
+                                void *stream);
+
+/*
+ * kvq_decode_workspace_bytes_prerope -- workspace bytes of
+ * kvq_decode_attention_prerope (0 on invalid sizes): the split partials and
+ * one fp32 key score per (b, query head, INT2 token).  Pure host arithmetic.
+ */
+size_t kvq_decode_workspace_bytes_prerope(int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
+                                          int64_t n_int2_tokens, int64_t n_sink,
+                                          int64_t n_res);
+
+/*
+ * kvq_decode_attention_prerope -- decode attention over caches written by
+ * kvq_quantize_prerope: INT2 tokens [t_begin, t_end) (positions t_begin ..
+ * t_end - 1, t_end < 2^31) plus the fp16 tokens, as described above.
+ *  group_heads  as written (1, 2 or 4; Hkv a multiple of it); group_heads *
+ *               (Hq / Hkv) must be at most 32 (KVQ_ERR_UNSUPPORTED).
+ *  rope_base    > 1 and finite (10000 for LLaMA-2).
+ *  workspace    at least kvq_decode_workspace_bytes_prerope(...) bytes.
+ *  Every other argument as for kvq_decode_attention (no rotation argument).
+ */
+kvq_status kvq_decode_attention_prerope(const void *q, kvq_dtype q_dtype,
+                                        int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
+                                        const kvq_int2_cache *kc, const kvq_int2_cache *vc,
+                                        int64_t t_begin, int64_t t_end,
+                                        int group_heads, float rope_base, int group,
+                                        const uint16_t *sink_k, const uint16_t *sink_v,
+                                        int64_t n_sink,
+                                        const uint16_t *res_k, const uint16_t *res_v,
+                                        int64_t n_res, float softmax_scale,
+                                        void *out, kvq_dtype out_dtype,
+                                        void *workspace, size_t workspace_bytes,
+                                        void *stream);
 
 /*
  * kvq_decode_attention_noalloc -- kvq_decode_attention without a workspace

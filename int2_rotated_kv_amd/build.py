@@ -10,7 +10,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvq.so")
 
 SOURCES = ["api.cpp", "kv_rotate_quant.hip", "kv_rotate_quant_dense.hip", "kv_decode.hip", "kv_decode_gqa.hip",
-           "kv_decode_generic.hip", "kvq_scratch.hip"]
+           "kv_decode_generic.hip", "kv_decode_prerope.hip", "kvq_scratch.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -95,6 +95,16 @@ size_t workspace_bytes(int64_t B, int64_t Hq, int64_t n_splits) {
   return qprep + parts;
 }
 
+// Score rows per (b, query head) of the pre-RoPE decode: the INT2 tokens plus
+// the attention grid's shift (below 16), rounded up to 16.
+int64_t prerope_score_rows(int64_t n_int2) { return (n_int2 + 16 + 15) / 16 * 16; }
+
+// Pre-RoPE decode workspace: the split partials, then fp32 key scores.
+size_t workspace_bytes_prerope(int64_t B, int64_t Hq, int64_t n_splits, int64_t n_int2) {
+  const size_t parts = (size_t)B * Hq * n_splits * kvq::kPartialStride * sizeof(float);
+  return align256(parts) + (size_t)B * Hq * prerope_score_rows(n_int2) * sizeof(float);
+}
+
 
 // Shared by the common-offset and the per-sequence-offset entry points.
 // offsets == NULL: every sequence's rows start at t_offset (checked against
@@ -105,7 +115,7 @@ kvq_status quantize_impl(const void *K, const void *V, kvq_dtype in_dtype, int64
                          int64_t stride_t, int64_t stride_h, kvq_rot rot, const void *R,
                          int group, int64_t t_offset, const int32_t *offsets,
                          const kvq_quant_cache *kc, const kvq_quant_cache *vc, void *stream,
-                         const Paging *pg = nullptr) {
+                         const Paging *pg = nullptr, int key_group_heads = 1) {
   if (!valid_dtype(in_dtype)) return KVQ_ERR_INVALID_ARG;
   if (B < 0 || T_new < 0 || Hkv <= 0 || t_offset < 0) return KVQ_ERR_INVALID_ARG;
   if (stride_b < 0 || stride_t < 0 || stride_h < 0) return KVQ_ERR_INVALID_ARG;
@@ -158,8 +168,27 @@ kvq_status quantize_impl(const void *K, const void *V, kvq_dtype in_dtype, int64
     a.max_pages = pg->max_pages; a.n_pages = pg->n_pages; a.page_tokens = pg->page_tokens;
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = (rot == KVQ_ROT_DENSE) ? kvq::launch_quantize_dense(a, s)
-                                        : kvq::launch_quantize_rows(a, s);
+  hipError_t e;
+  if (key_group_heads > 1) {
+    // keys with the pre-RoPE grouped-head rotation, values with the per-head
+    // Hadamard rotation: one launch each
+    e = hipSuccess;
+    int next = 0;
+    if (K != nullptr) {
+      kvq::QuantArgs ak = a;
+      ak.n_sides = 1;
+      e = kvq::launch_quantize_grouped(ak, key_group_heads, s);
+      next = 1;
+    }
+    if (e == hipSuccess && V != nullptr) {
+      kvq::QuantArgs av = a;
+      av.side[0] = a.side[next];
+      av.n_sides = 1;
+      e = kvq::launch_quantize_rows(av, s);
+    }
+  } else {
+    e = (rot == KVQ_ROT_DENSE) ? kvq::launch_quantize_dense(a, s) : kvq::launch_quantize_rows(a, s);
+  }
   if (e == hipErrorNotSupported) return KVQ_ERR_UNSUPPORTED;
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
@@ -221,7 +250,8 @@ kvq_status decode_impl(const void *q, kvq_dtype q_dtype, int64_t B, int64_t Hq,
                        const uint16_t *res_k, const uint16_t *res_v, int64_t n_res,
                        float softmax_scale, void *out, kvq_dtype out_dtype,
                        void *workspace, size_t workspace_bytes_given, void *stream,
-                       const Paging *pg = nullptr, bool static_scratch = false) {
+                       const Paging *pg = nullptr, bool static_scratch = false,
+                       int group_heads = 0, double rope_base = 0.0) {
   if (!valid_dtype(q_dtype) || !valid_dtype(out_dtype)) return KVQ_ERR_INVALID_ARG;
   if (q == nullptr || out == nullptr || !aligned16(q) || !aligned16(out)) return KVQ_ERR_INVALID_ARG;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return KVQ_ERR_INVALID_ARG;
@@ -244,8 +274,12 @@ kvq_status decode_impl(const void *q, kvq_dtype q_dtype, int64_t B, int64_t Hq,
   if (n_sink + n_res > kMaxFp16Tokens) return KVQ_ERR_UNSUPPORTED;
   if (B * Hq > 0x7FFFFFFF) return KVQ_ERR_UNSUPPORTED;
   if (!(softmax_scale == softmax_scale)) return KVQ_ERR_INVALID_ARG;   // NaN
-  const kvq::SplitPlan plan = kvq::plan_splits(B, Hq, Hkv, n_int2);
-  const size_t need = workspace_bytes(B, Hq, plan.n_splits);
+  // keys with the pre-RoPE grouped-head rotation: one attention wave per
+  // query head, and the score rows after the partials
+  const kvq::SplitPlan plan = group_heads > 0 ? kvq::plan_splits(B, Hq, Hq, n_int2)
+                                              : kvq::plan_splits(B, Hq, Hkv, n_int2);
+  const size_t need = group_heads > 0 ? workspace_bytes_prerope(B, Hq, plan.n_splits, n_int2)
+                                      : workspace_bytes(B, Hq, plan.n_splits);
   if (static_scratch) {
     // the library's own scratch array of this GPU (every argument is checked
     // by now: this is the call's first HIP call)
@@ -288,6 +322,15 @@ kvq_status decode_impl(const void *q, kvq_dtype q_dtype, int64_t B, int64_t Hq,
   a.partials = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) +
                                          align256((size_t)B * Hq * kvq::kQprepDwordsPerHead * 4));
   a.n_splits = plan.n_splits;
+  if (group_heads > 0) {
+    const size_t parts = (size_t)B * Hq * plan.n_splits * kvq::kPartialStride * sizeof(float);
+    a.qprep = nullptr;
+    a.partials = reinterpret_cast<float *>(workspace);
+    a.scores = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + align256(parts));
+    a.score_rows = prerope_score_rows(n_int2);
+    a.group_heads = group_heads;
+    a.log2_rope_base = log2(rope_base);
+  }
   hipError_t e = kvq::launch_decode(a, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
@@ -413,6 +456,48 @@ kvq_status kvq_decode_attention_paged(const void *q, kvq_dtype q_dtype, int64_t 
   return decode_impl(q, q_dtype, B, Hq, Hkv, d, &kq, &vq, t_begin, t_end_max, t_ends, rot, R, group,
                      sink_k, sink_v, n_sink, res_k, res_v, n_res, softmax_scale, out, out_dtype,
                      workspace, workspace_bytes_given, stream, &pg);
+}
+
+kvq_status kvq_quantize_prerope(const void *K, const void *V, kvq_dtype in_dtype, int64_t B,
+                                int64_t T_new, int64_t Hkv, int64_t d, int64_t stride_b,
+                                int64_t stride_t, int64_t stride_h, int group_heads, int group,
+                                int64_t t_offset, const kvq_int2_cache *kc,
+                                const kvq_int2_cache *vc, void *stream) {
+  if (group_heads != 1 && group_heads != 2 && group_heads != 4) return KVQ_ERR_INVALID_ARG;
+  if (Hkv <= 0 || Hkv % group_heads != 0) return KVQ_ERR_INVALID_ARG;
+  if (group_heads > 1 && Hkv % 4 != 0) return KVQ_ERR_UNSUPPORTED;   // four heads per wave
+  if (in_dtype == KVQ_F32) return KVQ_ERR_UNSUPPORTED;
+  const AsQuant k2(kc), v2(vc);
+  return quantize_impl(K, V, in_dtype, B, T_new, Hkv, d, stride_b, stride_t, stride_h, KVQ_ROT_HADAMARD,
+                       nullptr, group, t_offset, nullptr, k2.p, v2.p, stream, nullptr, group_heads);
+}
+
+size_t kvq_decode_workspace_bytes_prerope(int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
+                                          int64_t n_int2_tokens, int64_t n_sink, int64_t n_res) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || d != 128) return 0;
+  if (n_int2_tokens < 0 || n_sink < 0 || n_res < 0) return 0;
+  const kvq::SplitPlan p = kvq::plan_splits(B, Hq, Hq, n_int2_tokens);
+  return workspace_bytes_prerope(B, Hq, p.n_splits, n_int2_tokens);
+}
+
+kvq_status kvq_decode_attention_prerope(const void *q, kvq_dtype q_dtype, int64_t B, int64_t Hq,
+                                        int64_t Hkv, int64_t d, const kvq_int2_cache *kc,
+                                        const kvq_int2_cache *vc, int64_t t_begin, int64_t t_end,
+                                        int group_heads, float rope_base, int group,
+                                        const uint16_t *sink_k, const uint16_t *sink_v, int64_t n_sink,
+                                        const uint16_t *res_k, const uint16_t *res_v, int64_t n_res,
+                                        float softmax_scale, void *out, kvq_dtype out_dtype,
+                                        void *workspace, size_t workspace_bytes_given, void *stream) {
+  if (group_heads != 1 && group_heads != 2 && group_heads != 4) return KVQ_ERR_INVALID_ARG;
+  if (Hkv <= 0 || Hkv % group_heads != 0) return KVQ_ERR_INVALID_ARG;
+  if (!(rope_base > 1.0f) || !(rope_base <= 3.0e38f)) return KVQ_ERR_INVALID_ARG;
+  if (Hq > 0 && Hq % Hkv == 0 && group_heads * (Hq / Hkv) > 32) return KVQ_ERR_UNSUPPORTED;
+  if (t_end > 0x7FFFFFFF) return KVQ_ERR_UNSUPPORTED;            // positions are 32-bit
+  const AsQuant k2(kc), v2(vc);
+  return decode_impl(q, q_dtype, B, Hq, Hkv, d, k2.p, v2.p, t_begin, t_end, nullptr, KVQ_ROT_HADAMARD,
+                     nullptr, group, sink_k, sink_v, n_sink, res_k, res_v, n_res, softmax_scale, out,
+                     out_dtype, workspace, workspace_bytes_given, stream, nullptr, false, group_heads,
+                     (double)rope_base);
 }
 
 const char *kvq_status_str(kvq_status s) {

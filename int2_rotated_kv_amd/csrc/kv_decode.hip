@@ -36,6 +36,8 @@
 // codes on 1.5 makes the fp16 rounding of w multiply code - 1.5 in
 // [-1.5, 1.5], so it does not get amplified by the cancellation between the
 // code and zero-point terms.
+#include <math.h>
+
 #include "kv_decode_common.h"
 
 namespace kvq {
@@ -226,6 +228,7 @@ struct TileRegs {
   u32x4_t kA, kB, vA, vB;          // codes of tokens A (= ts) and B (= 32 + ts)
   uint32_t ksA, kzA, ksB, kzB;     // two fp16 scales / zeros each
   uint32_t vsA, vzA, vsB, vzB;
+  float sA, sB;                    // precomputed scores (log2 units), PRE only
 };
 
 template <int GC>
@@ -268,7 +271,9 @@ __device__ __forceinline__ int group_dot(const uint32_t (&limb)[20], uint32_t c0
   return acc;
 }
 
-template <int GC>
+// PRE: the key scores come precomputed in r.sA / r.sB (log2 units) and the
+// key fields of r are unused.
+template <int GC, bool PRE = false>
 __device__ __forceinline__ void attn_tile(AttnState<GC> &st, const QueryLimbs<GC> &q,
                                           const TileRegs &r, bool va, bool vb) {
   const uint32_t kAw[4] = {r.kA.x, r.kA.y, r.kA.z, r.kA.w};
@@ -282,24 +287,30 @@ __device__ __forceinline__ void attn_tile(AttnState<GC> &st, const QueryLimbs<GC
   const bool big = st.slack > 0.0f && __builtin_amdgcn_ballot_w64(big_value_scale(r.vsA, r.vsB));
 #pragma unroll
   for (int g = 0; g < GC; ++g) {
-    // score in units of the query step: sum_j s_j * dot_j + z_j * isum_j
+    float xa, xb;
     float ra = 0.0f, rb = 0.0f;
+    if constexpr (PRE) {
+      xa = va ? r.sA - st.m[g] : kNegInf;
+      xb = vb ? r.sB - st.m[g] : kNegInf;
+    } else {
+      // score in units of the query step: sum_j s_j * dot_j + z_j * isum_j
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
-      const int ia = group_dot(q.limb[g][gi], kAw[2 * gi], kAw[2 * gi + 1]);
-      const int ib = group_dot(q.limb[g][gi], kBw[2 * gi], kBw[2 * gi + 1]);
-      ra = __builtin_fmaf((float)ia, (float)ksA[gi], __builtin_fmaf((float)kzA[gi], q.isum[g][gi], ra));
-      rb = __builtin_fmaf((float)ib, (float)ksB[gi], __builtin_fmaf((float)kzB[gi], q.isum[g][gi], rb));
+      for (int gi = 0; gi < 2; ++gi) {
+        const int ia = group_dot(q.limb[g][gi], kAw[2 * gi], kAw[2 * gi + 1]);
+        const int ib = group_dot(q.limb[g][gi], kBw[2 * gi], kBw[2 * gi + 1]);
+        ra = __builtin_fmaf((float)ia, (float)ksA[gi], __builtin_fmaf((float)kzA[gi], q.isum[g][gi], ra));
+        rb = __builtin_fmaf((float)ib, (float)ksB[gi], __builtin_fmaf((float)kzB[gi], q.isum[g][gi], rb));
+      }
+      ra += quad_swap<kQuadXor1>(ra);        // the other half of the row
+      rb += quad_swap<kQuadXor1>(rb);
+      // log2-domain score minus the running reference
+      xa = va ? __builtin_fmaf(q.qstep[g], ra, -st.m[g]) : kNegInf;
+      xb = vb ? __builtin_fmaf(q.qstep[g], rb, -st.m[g]) : kNegInf;
     }
-    ra += quad_swap<kQuadXor1>(ra);          // the other half of the row
-    rb += quad_swap<kQuadXor1>(rb);
-    // log2-domain score minus the running reference
-    float xa = va ? __builtin_fmaf(q.qstep[g], ra, -st.m[g]) : kNegInf;
-    float xb = vb ? __builtin_fmaf(q.qstep[g], rb, -st.m[g]) : kNegInf;
     if (__builtin_amdgcn_ballot_w64(fmaxf(xa, xb) > st.slack) || big) {     // wave-uniform
       if (big) st.slack = 0.0f;              // from here on p <= 1
-      const float ya = va ? q.qstep[g] * ra : kNegInf;
-      const float yb = vb ? q.qstep[g] * rb : kNegInf;
+      const float ya = va ? (PRE ? r.sA : q.qstep[g] * ra) : kNegInf;
+      const float yb = vb ? (PRE ? r.sB : q.qstep[g] * rb) : kNegInf;
       float mx = fmaxf(ya, yb);
       mx = fmaxf(mx, row_ror<2>(mx));
       mx = fmaxf(mx, row_ror<4>(mx));
@@ -433,7 +444,10 @@ __device__ __forceinline__ float wave_prep_query(const void *q, bool q_f32, int6
 // WPB waves per workgroup; wave index gw = ((b*Hkv + hkv)*S + split)*G + g
 // for one length (the variable-length map of wave_place otherwise), so the
 // G heads of a group (same tiles) are neighbours in one workgroup.
-template <int WPB>
+// PRE: the key scores are read from a.scores (keys cached with the pre-RoPE
+// grouped-head rotation, scored by kv_prerope_scores); the key cache and the
+// query are not read.
+template <int WPB, bool PRE = false>
 __global__ __launch_bounds__(64 * WPB) void kv_int2_decode_attn(AttnArgs a) {
   constexpr int GC = 1;
   const int lane = threadIdx.x & 63;
@@ -460,7 +474,9 @@ __global__ __launch_bounds__(64 * WPB) void kv_int2_decode_attn(AttnArgs a) {
 
   QueryLimbs<GC> q;
   __shared__ uint32_t qlds[WPB][84];
-  if (a.fused_prep) {                        // one head per KV head: hq = b*Hq + hkv
+  if constexpr (PRE) {
+    // scores come precomputed
+  } else if (a.fused_prep) {                 // one head per KV head: hq = b*Hq + hkv
     q.qstep[0] = wave_prep_query(a.q, a.q_f32, (b * a.Hq + hkv) * kD, a.rot, a.qscale, qlds[wave]);
     asm volatile("" ::: "memory");           // LDS of one wave is ordered; keep the program order
 #pragma unroll
@@ -505,19 +521,27 @@ __global__ __launch_bounds__(64 * WPB) void kv_int2_decode_attn(AttnArgs a) {
   // are wave-uniform, lane offsets 32-bit.
   const uint32_t oc = (uint32_t)(ts * kCodeBytes + 16 * h);
   const uint32_t os = (uint32_t)(ts * kNGroups + 2 * h);
+  // PRE: the wave's query head's precomputed scores, by shifted-grid row
+  const float *srow = PRE ? a.scores + (b * a.Hq + hkv * a.G + gq) * a.score_rows : nullptr;
   auto load_tile = [&](const TileRows &tr) {
     TileRegs r;
     const uint8_t *kct = a.kcodes + tr.k * kCodeBytes, *vct = a.vcodes + tr.v * kCodeBytes;
     const uint16_t *kst = a.kscales + tr.k * kNGroups, *kzt = a.kzeros + tr.k * kNGroups;
     const uint16_t *vst = a.vscales + tr.v * kNGroups, *vzt = a.vzeros + tr.v * kNGroups;
-    r.kA = *reinterpret_cast<const u32x4_t *>(kct + oc);
-    r.kB = *reinterpret_cast<const u32x4_t *>(kct + oc + 32 * kCodeBytes);
+    if constexpr (PRE) {
+      const int64_t g0 = tr.k - krow0;               // the tile's first shifted-grid row
+      r.sA = srow[g0 + ts];
+      r.sB = srow[g0 + 32 + ts];
+    } else {
+      r.kA = *reinterpret_cast<const u32x4_t *>(kct + oc);
+      r.kB = *reinterpret_cast<const u32x4_t *>(kct + oc + 32 * kCodeBytes);
+      r.ksA = *reinterpret_cast<const uint32_t *>(kst + os);
+      r.kzA = *reinterpret_cast<const uint32_t *>(kzt + os);
+      r.ksB = *reinterpret_cast<const uint32_t *>(kst + os + 32 * kNGroups);
+      r.kzB = *reinterpret_cast<const uint32_t *>(kzt + os + 32 * kNGroups);
+    }
     r.vA = *reinterpret_cast<const u32x4_t *>(vct + oc);
     r.vB = *reinterpret_cast<const u32x4_t *>(vct + oc + 32 * kCodeBytes);
-    r.ksA = *reinterpret_cast<const uint32_t *>(kst + os);
-    r.kzA = *reinterpret_cast<const uint32_t *>(kzt + os);
-    r.ksB = *reinterpret_cast<const uint32_t *>(kst + os + 32 * kNGroups);
-    r.kzB = *reinterpret_cast<const uint32_t *>(kzt + os + 32 * kNGroups);
     r.vsA = *reinterpret_cast<const uint32_t *>(vst + os);
     r.vzA = *reinterpret_cast<const uint32_t *>(vzt + os);
     r.vsB = *reinterpret_cast<const uint32_t *>(vst + os + 32 * kNGroups);
@@ -542,14 +566,14 @@ __global__ __launch_bounds__(64 * WPB) void kv_int2_decode_attn(AttnArgs a) {
     int64_t i = 0;
     for (; i + 3 <= mine; i += 3) {
       r2 = load_tile(at(i + 2));
-      attn_tile<GC>(st, q, r0, true, true);
+      attn_tile<GC, PRE>(st, q, r0, true, true);
       r0 = load_tile(at(i + 3));
-      attn_tile<GC>(st, q, r1, true, true);
+      attn_tile<GC, PRE>(st, q, r1, true, true);
       r1 = load_tile(at(i + 4));
-      attn_tile<GC>(st, q, r2, true, true);
+      attn_tile<GC, PRE>(st, q, r2, true, true);
     }
-    if (i < mine) attn_tile<GC>(st, q, r0, true, true);
-    if (i + 1 < mine) attn_tile<GC>(st, q, r1, true, true);
+    if (i < mine) attn_tile<GC, PRE>(st, q, r0, true, true);
+    if (i + 1 < mine) attn_tile<GC, PRE>(st, q, r1, true, true);
   }
   // partial tiles: masked rows are loaded from the tile's first valid row
   auto masked_tile = [&](int64_t t) {
@@ -563,19 +587,24 @@ __global__ __launch_bounds__(64 * WPB) void kv_int2_decode_attn(AttnArgs a) {
     const uint16_t *vs = a.vscales + tr.v * kNGroups, *vz = a.vzeros + tr.v * kNGroups;
     const int64_t ra = va ? ts : lo, rb = vb ? 32 + ts : lo;   // rows inside the tile
     TileRegs r;
-    r.kA = *reinterpret_cast<const u32x4_t *>(kc + ra * kCodeBytes + 16 * h);
-    r.kB = *reinterpret_cast<const u32x4_t *>(kc + rb * kCodeBytes + 16 * h);
+    if constexpr (PRE) {
+      r.sA = srow[base + ra];
+      r.sB = srow[base + rb];
+    } else {
+      r.kA = *reinterpret_cast<const u32x4_t *>(kc + ra * kCodeBytes + 16 * h);
+      r.kB = *reinterpret_cast<const u32x4_t *>(kc + rb * kCodeBytes + 16 * h);
+      r.ksA = *reinterpret_cast<const uint32_t *>(ks + ra * kNGroups + 2 * h);
+      r.kzA = *reinterpret_cast<const uint32_t *>(kz + ra * kNGroups + 2 * h);
+      r.ksB = *reinterpret_cast<const uint32_t *>(ks + rb * kNGroups + 2 * h);
+      r.kzB = *reinterpret_cast<const uint32_t *>(kz + rb * kNGroups + 2 * h);
+    }
     r.vA = *reinterpret_cast<const u32x4_t *>(vc + ra * kCodeBytes + 16 * h);
     r.vB = *reinterpret_cast<const u32x4_t *>(vc + rb * kCodeBytes + 16 * h);
-    r.ksA = *reinterpret_cast<const uint32_t *>(ks + ra * kNGroups + 2 * h);
-    r.kzA = *reinterpret_cast<const uint32_t *>(kz + ra * kNGroups + 2 * h);
-    r.ksB = *reinterpret_cast<const uint32_t *>(ks + rb * kNGroups + 2 * h);
-    r.kzB = *reinterpret_cast<const uint32_t *>(kz + rb * kNGroups + 2 * h);
     r.vsA = *reinterpret_cast<const uint32_t *>(vs + ra * kNGroups + 2 * h);
     r.vzA = *reinterpret_cast<const uint32_t *>(vz + ra * kNGroups + 2 * h);
     r.vsB = *reinterpret_cast<const uint32_t *>(vs + rb * kNGroups + 2 * h);
     r.vzB = *reinterpret_cast<const uint32_t *>(vz + rb * kNGroups + 2 * h);
-    attn_tile<GC>(st, q, r, va, vb);
+    attn_tile<GC, PRE>(st, q, r, va, vb);
   };
   {
     int64_t p0, p1;
@@ -911,7 +940,69 @@ SplitPlan plan_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_int2) {
   return p;
 }
 
+// Keys with the pre-RoPE grouped-head rotation: the score launch, then the
+// attention over the values with those scores (one wave per query head and
+// split), then the combine with the values' Hadamard un-rotation.
+static hipError_t launch_decode_prerope(const DecodeArgs &d, hipStream_t stream) {
+  const int G = (int)(d.Hq / d.Hkv);
+  const int skip = grid_skip(d);
+  if (d.n_splits > 0) {
+    PreropeArgs p;
+    p.kcodes = d.kcodes; p.kscales = d.kscales; p.kzeros = d.kzeros; p.kT_cap = d.kT_cap;
+    p.t_begin = d.t_begin; p.n_int2 = d.n_int2; p.skip = skip; p.n_rows = d.score_rows;
+    p.B = d.B; p.Hq = (int)d.Hq; p.Hkv = (int)d.Hkv; p.G = G; p.GH = d.group_heads;
+    p.q = d.q; p.q_f32 = d.q_f32;
+    p.qscale = (float)((double)d.qscale / sqrt(128.0 * d.group_heads));
+    p.log2_base = d.log2_rope_base;
+    p.scores = d.scores;
+    p.tiles = (d.n_int2 + 15) / 16;
+    // about two rounds of four waves per CU, at least 8 tiles per wave
+    const int64_t groups = d.B * (d.Hkv / d.group_heads);
+    int64_t chunks = (4096 + groups - 1) / groups;
+    const int64_t by_tiles = (p.tiles + 7) / 8;
+    chunks = chunks < by_tiles ? chunks : by_tiles;
+    chunks = chunks > 0 ? chunks : 1;
+    p.tiles_per_wave = (p.tiles + chunks - 1) / chunks;
+    p.chunks = (p.tiles + p.tiles_per_wave - 1) / p.tiles_per_wave;
+    hipError_t e = launch_prerope_scores(p, stream);
+    if (e != hipSuccess) return e;
+    AttnArgs a;
+    a.kcodes = d.kcodes; a.kscales = d.kscales; a.kzeros = d.kzeros; a.kT_cap = d.kT_cap;
+    a.vcodes = d.vcodes; a.vscales = d.vscales; a.vzeros = d.vzeros; a.vT_cap = d.vT_cap;
+    a.t_begin = d.t_begin; a.n_int2 = d.n_int2; a.t_ends = nullptr;
+    a.n_splits = d.n_splits;
+    a.B = d.B;
+    a.total_waves = d.B * d.Hq * d.n_splits;       // one wave per query head and split
+    a.Hkv = (int)d.Hkv; a.Hq = (int)d.Hq; a.G = G;
+    a.qprep = nullptr;
+    a.partials = d.partials;
+    a.fused_prep = false;
+    a.skip = skip;
+    a.block_table = nullptr;
+    a.max_pages = a.n_pages = a.page_tokens = 0;
+    a.q = d.q; a.q_f32 = d.q_f32; a.rot = 1; a.perm = nullptr; a.qscale = d.qscale;
+    a.scores = d.scores; a.score_rows = d.score_rows;
+    hipLaunchKernelGGL((kv_int2_decode_attn<4, true>), dim3((unsigned)((a.total_waves + 3) / 4)), dim3(256), 0,
+                       stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  CombineArgs c;
+  c.q = d.q; c.q_f32 = d.q_f32; c.out_f32 = d.out_f32;
+  c.Hq = (int)d.Hq; c.Hkv = (int)d.Hkv; c.rot = 1; c.R = nullptr; c.perm = nullptr; c.qscale = d.qscale;
+  c.partials = d.partials; c.n_splits = d.n_splits;
+  c.t_ends = nullptr;
+  c.B = d.B; c.t_begin = d.t_begin; c.n_int2 = d.n_int2; c.skip = skip;
+  c.sink_k = d.sink_k; c.sink_v = d.sink_v; c.n_sink = d.n_sink;
+  c.res_k = d.res_k; c.res_v = d.res_v; c.n_res = d.n_res;
+  c.out = d.out;
+  const size_t lds = (size_t)(d.n_splits + d.n_sink + d.n_res) * sizeof(float);
+  hipLaunchKernelGGL(kv_combine_unrotate, dim3((unsigned)(d.B * d.Hq)), dim3(kCombineThreads), lds, stream, c);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const DecodeArgs &d, hipStream_t stream) {
+  if (d.group_heads > 0) return launch_decode_prerope(d, stream);
   const int G = (int)(d.Hq / d.Hkv);
   // one query head per KV head without a dense rotation: the attention waves
   // prepare the query themselves

@@ -35,7 +35,29 @@ struct AttnArgs {
   // rows per side); NULL: rows (b*Hkv + h)*T_cap + t.
   const int32_t *block_table;
   int64_t max_pages, n_pages, page_tokens;
+  // Precomputed key scores (keys cached with the pre-RoPE grouped-head
+  // rotation): [B][Hq][score_rows] in log2 units, row r = shifted-grid row r
+  // (token t_begin - skip + r); NULL: scores from the key cache.
+  const float *scores;
+  int64_t score_rows;
 };
+
+// The score launch for keys with the pre-RoPE grouped-head rotation
+// (kv_decode_prerope.hip).
+struct PreropeArgs {
+  const uint8_t *kcodes; const uint16_t *kscales; const uint16_t *kzeros; int64_t kT_cap;
+  int64_t t_begin, n_int2;   // INT2 tokens [t_begin, t_begin + n_int2), position = cache slot
+  int skip;                  // score row of token t: t - t_begin + skip
+  int64_t n_rows;            // score rows per (b, query head)
+  int64_t B;
+  int Hq, Hkv, G, GH;        // GH: heads per rotation group
+  const void *q; bool q_f32;
+  float qscale;              // softmax_scale * log2(e) / sqrt(128 GH)
+  double log2_base;          // log2 of the RoPE base
+  float *scores;
+  int64_t tiles, tiles_per_wave, chunks;   // 16-token tiles; per wave; waves per (b, head group)
+};
+hipError_t launch_prerope_scores(const PreropeArgs &a, hipStream_t stream);
 
 // First K and V cache rows of the tile that starts at row r0 of a head's
 // shifted grid (row 0 = token t_begin - skip).  A paged cache's tiles start on

@@ -86,14 +86,18 @@ __device__ __forceinline__ void minmax32(const float (&v)[32], float &mn, float 
 // clamp(rint(u), 0, L) directly and drops it into byte i/P of word i%P.
 // Otherwise u is clamped to [0, L] and rounded by adding 1.5 * 2^23 (clamp
 // then round equals round then clamp for integer bounds).
-template <int BITS, bool SCALED>
+// GH > 1: v is the unnormalized transform over the channels of GH heads
+// (grouped-head rotation) and c = fp32(1/sqrt(128 GH)).
+template <int BITS, bool SCALED, int GH = 1>
 __device__ __forceinline__ void quantize_group32(float (&v)[32], uint32_t (&w)[BITS],
                                                  uint16_t &sbits, uint16_t &zbits) {
 #pragma clang fp contract(off)
   constexpr int L = (1 << BITS) - 1;
   constexpr int CPW = 32 / BITS;                    // codes per word
   constexpr int P = 8 / BITS;                       // codes per byte
-  constexpr float c = 0.08838834764831845f;         // fp32(1/sqrt(128))
+  static_assert(GH == 1 || GH == 2 || GH == 4, "grouped heads");
+  // fp32(1/sqrt(128 GH)): 0x3DB504F3, 0x3D800000, 0x3D3504F3
+  constexpr float c = GH == 1 ? 0.08838834764831845f : GH == 2 ? 0.0625f : 0.04419417382415922f;
   float mn, mx;
   minmax32(v, mn, mx);
   if constexpr (SCALED) {
@@ -327,8 +331,17 @@ constexpr int kStageRowDwords = 64 + 4;     // 128 fp16 + 16-byte pad
 // so each staging load reads the 4 heads' rows of one token, 1 KiB of
 // contiguous input when heads are adjacent, and each store writes runs of
 // 16 rows per head.  HG = 1: 64 consecutive tokens of one head.
-template <bool PERM, int BITS, int HG>
+// GH > 1 (HG = 4, no reordering): the pre-RoPE grouped-head rotation of
+// keys (RotateKV, IJCAI 2025 record, abstract item (ii)): the rows of GH
+// consecutive heads of a token are one row of 128 GH channels, head j of
+// the group at channels 128 j .. 128 j + 127, rotated by the normalized
+// Hadamard matrix of that size.  With the head index as the high bits that
+// matrix is H_GH x H_128, so each head's row is transformed as before, then
+// butterflies across the GH heads (all four heads of a token sit in one
+// lane) complete it, and the normalization is 1/sqrt(128 GH).
+template <bool PERM, int BITS, int HG, int GH = 1>
 __device__ __forceinline__ void fwht_f16_body(const RowsKernelArgs &a) {
+  static_assert(GH == 1 || (HG == 4 && !PERM && (GH == 2 || GH == 4)), "grouped heads need 4 heads per wave");
   constexpr int TPW = 64 / HG;                       // tokens per wave
   __shared__ uint32_t stage[64 * kStageRowDwords];
   const int lane = threadIdx.x;
@@ -449,15 +462,14 @@ __device__ __forceinline__ void fwht_f16_body(const RowsKernelArgs &a) {
   // lane (n, q): stage row r(g) = 16g + n for HG = 1, 4n + g for HG = 4
   auto srow = [&](int g) { return HG == 1 ? 16 * g + n : 4 * n + g; };
   uint32_t cw[4][BITS], csz[4];                      // codes and scale | zero << 16 of stage row srow(g)
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
+  // the transform of stage row srow(g) into z: channel c0 + 8(4q + r') in z[c0 + 8r']
+  auto transform = [&](int g, float (&z)[32]) {
     const int r = srow(g);                           // the lane's stage row
     // channels 8(4q + i) .. 8(4q + i) + 7 of row r, i = 0..3
     u32x4_t u[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       u[i] = *reinterpret_cast<const u32x4_t *>(&stage[r * kStageRowDwords + 4 * (4 * q + i)]);
-    float z[32];                                     // z[c0 + 8r'] = channel c0 + 8(4q + r') after H16
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t w0 = u[0][e], w1 = u[1][e], w2 = u[2][e], w3 = u[3][e];
@@ -486,9 +498,42 @@ __device__ __forceinline__ void fwht_f16_body(const RowsKernelArgs &a) {
         }
       }
     }
-    uint16_t sb, zb;
-    quantize_group32<BITS, true>(z, cw[g], sb, zb);
-    csz[g] = (uint32_t)sb | ((uint32_t)zb << 16);
+  };
+  if constexpr (GH == 1) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float z[32];
+      transform(g, z);
+      uint16_t sb, zb;
+      quantize_group32<BITS, true>(z, cw[g], sb, zb);
+      csz[g] = (uint32_t)sb | ((uint32_t)zb << 16);
+    }
+  } else {
+    // the four heads of the lane's token, then the butterflies across each
+    // group of GH heads (head bits of the grouped transform)
+    float z[4][32];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) transform(g, z[g]);
+#pragma unroll
+    for (int hs = 1; hs < GH; hs <<= 1) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        if ((g & hs) == 0) {
+#pragma unroll
+          for (int i = 0; i < 32; ++i) {
+            const float x = z[g][i], y = z[g + hs][i];
+            z[g][i] = x + y;
+            z[g + hs][i] = x - y;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint16_t sb, zb;
+      quantize_group32<BITS, true, GH>(z[g], cw[g], sb, zb);
+      csz[g] = (uint32_t)sb | ((uint32_t)zb << 16);
+    }
   }
   // Back through LDS to one row per lane (codes: the row's 16 b bytes,
   // 16-byte chunk k of row r at entry b r + k; then scale | zero << 16 of
@@ -557,6 +602,36 @@ __global__ __launch_bounds__(64) void kv_rotate_quant_fwht_perm_b1_f16(RowsKerne
 template <int HG>
 __global__ __launch_bounds__(64) void kv_rotate_quant_fwht_perm_b4_f16(RowsKernelArgs a) {
   fwht_f16_body<true, 4, HG>(a);
+}
+
+// Pre-RoPE keys with the grouped-head rotation over GH heads (2-bit codes).
+template <int GH>
+__global__ __launch_bounds__(64, 2) void kv_rotate_quant_fwht_grouped_f16(RowsKernelArgs a) {
+  fwht_f16_body<false, 2, 4, GH>(a);
+}
+
+hipError_t launch_quantize_grouped(const QuantArgs &q, int group_heads, hipStream_t stream) {
+  // one side (the keys), fp16 rows, Hkv a multiple of 4 (checked by the caller)
+  RowsKernelArgs a;
+  a.side[0] = q.side[0];
+  a.side[1] = q.side[0];
+  a.stride_b = q.stride_b;
+  a.stride_t = q.stride_t;
+  a.stride_h = q.stride_h;
+  a.T_new = q.T_new;
+  a.t_offset = q.t_offset;
+  a.offsets = q.offsets;
+  a.Hkv = (int)q.Hkv;
+  a.n_sides = 1;
+  a.perm = nullptr;
+  a.block_table = nullptr;
+  a.max_pages = a.n_pages = a.page_tokens = 0;
+  const int64_t tiles = (q.T_new + 15) / 16 + 1;
+  const dim3 grid((unsigned)(tiles * (q.Hkv / 4)), 1, (unsigned)q.B), block(64);
+  if (group_heads == 2) hipLaunchKernelGGL(kv_rotate_quant_fwht_grouped_f16<2>, grid, block, 0, stream, a);
+  else if (group_heads == 4) hipLaunchKernelGGL(kv_rotate_quant_fwht_grouped_f16<4>, grid, block, 0, stream, a);
+  else return hipErrorNotSupported;
+  return hipGetLastError();
 }
 
 // The fp16 Hadamard write kernels: a wave takes 16 tokens of 4 heads when

@@ -37,6 +37,9 @@ struct QuantArgs {
 
 hipError_t launch_quantize_rows(const QuantArgs &a, hipStream_t stream);
 hipError_t launch_quantize_dense(const QuantArgs &a, hipStream_t stream);
+// Keys with the pre-RoPE grouped-head rotation over group_heads (2 or 4)
+// heads: side[0] only, fp16 rows, Hkv a multiple of 4.
+hipError_t launch_quantize_grouped(const QuantArgs &a, int group_heads, hipStream_t stream);
 
 // Decode.
 struct DecodeArgs {
@@ -63,6 +66,12 @@ struct DecodeArgs {
                         // B*Hq*n_splits rows, shared by sequence
   int64_t n_splits;     // waves per (b, query head), each taking every n_splits-th tile
                         // (variable length: planned for the longest sequence)
+  // keys with the pre-RoPE grouped-head rotation over group_heads heads
+  // (0: not this mode); scores [B][Hq][score_rows] fp32 in the workspace
+  int group_heads;
+  double log2_rope_base;
+  float *scores;
+  int64_t score_rows;
 };
 
 // Split plan shared by the workspace query and the attention call.

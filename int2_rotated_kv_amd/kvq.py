@@ -30,7 +30,9 @@ EXPORTED_SYMBOLS = ("kvq_quantize", "kvq_quantize_at", "kvq_quantize_bits", "kvq
                     "kvq_quantize_paged", "kvq_decode_workspace_bytes", "kvq_decode_attention",
                     "kvq_decode_attention_varlen", "kvq_decode_attention_bits",
                     "kvq_decode_attention_varlen_bits", "kvq_decode_attention_paged",
-                    "kvq_decode_attention_noalloc", "kvq_status_str", "kvq_abi_version")
+                    "kvq_decode_attention_noalloc", "kvq_quantize_prerope",
+                    "kvq_decode_workspace_bytes_prerope", "kvq_decode_attention_prerope",
+                    "kvq_status_str", "kvq_abi_version")
 
 D_HEAD = 128
 GROUP = 32
@@ -96,6 +98,15 @@ def load_library() -> ctypes.CDLL:
     lib.kvq_decode_attention_noalloc.argtypes = [vp, i32, i64, i64, i64, i64, cp, cp, i64, i64,
                                                  i32, vp, i32, vp, vp, i64, vp, vp, i64, f32,
                                                  vp, i32, vp]
+    lib.kvq_quantize_prerope.restype = i32
+    lib.kvq_quantize_prerope.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, i64, i64,
+                                         i32, i32, i64, cp, cp, vp]
+    lib.kvq_decode_workspace_bytes_prerope.restype = ctypes.c_size_t
+    lib.kvq_decode_workspace_bytes_prerope.argtypes = [i64, i64, i64, i64, i64, i64, i64]
+    lib.kvq_decode_attention_prerope.restype = i32
+    lib.kvq_decode_attention_prerope.argtypes = [vp, i32, i64, i64, i64, i64, cp, cp, i64, i64,
+                                                 i32, f32, i32, vp, vp, i64, vp, vp, i64, f32,
+                                                 vp, i32, vp, ctypes.c_size_t, vp]
     qp = ctypes.POINTER(kvq_quant_cache)
     lib.kvq_quantize_bits.restype = i32
     lib.kvq_quantize_bits.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, i64, i64,
@@ -486,6 +497,80 @@ def kvq_decode_attention_noalloc(q: torch.Tensor, cache_k: Int2Cache | None,
         _ptr(sink_k), _ptr(sink_v), n_sink, _ptr(res_k), _ptr(res_v), n_res,
         float(softmax_scale), _ptr(out), _dtype_code(out), _stream(stream))
     _check(st, "kvq_decode_attention_noalloc")
+    return out
+
+
+ROPE_BASE = 10000.0
+
+
+def kvq_quantize_prerope(K, V, cache_k: Int2Cache | None, cache_v: Int2Cache | None,
+                         group_heads: int = 4, group: int = GROUP, t_offset: int = 0, stream=None):
+    """Write pre-RoPE keys [B, T_new, Hkv, 128] with the grouped-head rotation
+    over group_heads heads, and values with the per-head Hadamard rotation,
+    into 2-bit caches at slots [t_offset, t_offset + T_new)
+    (kvq_quantize_prerope)."""
+    x = _check_rows(K, V)
+    B, T_new, Hkv, d = x.shape
+    _need((K is None) == (cache_k is None) and (V is None) == (cache_v is None),
+          "each side needs both its rows and its cache, or neither")
+    for c, what in ((cache_k, "cache_k"), (cache_v, "cache_v")):
+        if c is not None:
+            _check_cache(c, (B, Hkv), what)
+            _need(c.bits == 2, f"{what}: the pre-RoPE write takes 2-bit caches")
+    _check_device((K, V, *_cache_tensors(cache_k), *_cache_tensors(cache_v)))
+    kc = cache_k.c_struct() if cache_k is not None else None
+    vc = cache_v.c_struct() if cache_v is not None else None
+    st = load_library().kvq_quantize_prerope(
+        _ptr(K), _ptr(V), _dtype_code(x), B, T_new, Hkv, d,
+        x.stride(0), x.stride(1), x.stride(2), int(group_heads), group, t_offset,
+        ctypes.byref(kc) if kc is not None else None,
+        ctypes.byref(vc) if vc is not None else None, _stream(stream))
+    _check(st, "kvq_quantize_prerope")
+
+
+def kvq_decode_workspace_bytes_prerope(B, Hq, Hkv, d, n_int2_tokens, n_sink=0, n_res=0) -> int:
+    return int(load_library().kvq_decode_workspace_bytes_prerope(B, Hq, Hkv, d, n_int2_tokens,
+                                                                 n_sink, n_res))
+
+
+def kvq_decode_attention_prerope(q: torch.Tensor, cache_k: Int2Cache, cache_v: Int2Cache,
+                                 t_begin: int, t_end: int, group_heads: int = 4,
+                                 rope_base: float = ROPE_BASE, group: int = GROUP,
+                                 sink_k=None, sink_v=None, res_k=None, res_v=None,
+                                 softmax_scale: float = 0.0, out: torch.Tensor | None = None,
+                                 workspace: torch.Tensor | None = None, stream=None):
+    """Decode attention for post-RoPE queries q [B, Hq, 128] over caches
+    written by kvq_quantize_prerope: INT2 tokens [t_begin, t_end) at their
+    slot positions, plus fp16 post-RoPE tokens [B, Hkv, n, 128]
+    (kvq_decode_attention_prerope)."""
+    _need(q.dim() == 3, "q must be [B, Hq, 128]")
+    B, Hq, d = q.shape
+    _need(cache_k is not None and cache_v is not None, "the pre-RoPE decode needs both cache sides")
+    Hkv = cache_k.codes.shape[1]
+    _check_query(q, out, Hkv)
+    for c, what in ((cache_k, "cache_k"), (cache_v, "cache_v")):
+        _check_cache(c, (B, Hkv), what)
+        _need(c.bits == 2, f"{what}: the pre-RoPE decode takes 2-bit caches")
+        _need(0 <= t_begin <= t_end <= c.T_cap, f"{what}: token range [{t_begin}, {t_end}) "
+              f"outside the cache's {c.T_cap} slots")
+    n_sink = _check_fp16_tokens(sink_k, sink_v, B, Hkv, "sink")
+    n_res = _check_fp16_tokens(res_k, res_v, B, Hkv, "residual")
+    _check_device((q, out, workspace, sink_k, sink_v, res_k, res_v,
+                   *_cache_tensors(cache_k), *_cache_tensors(cache_v)))
+    need = kvq_decode_workspace_bytes_prerope(B, Hq, Hkv, d, t_end - t_begin, n_sink, n_res)
+    _check_workspace(workspace, need)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    kc, vc = cache_k.c_struct(), cache_v.c_struct()
+    st = load_library().kvq_decode_attention_prerope(
+        _ptr(q), _dtype_code(q), B, Hq, Hkv, d, ctypes.byref(kc), ctypes.byref(vc),
+        t_begin, t_end, int(group_heads), float(rope_base), group,
+        _ptr(sink_k), _ptr(sink_v), n_sink, _ptr(res_k), _ptr(res_v), n_res,
+        float(softmax_scale), _ptr(out), _dtype_code(out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "kvq_decode_attention_prerope")
     return out
 
 

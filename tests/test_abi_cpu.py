@@ -304,3 +304,74 @@ def test_paged_rejects(lib):
     assert quant(dt=K.KVQ_F32, rot=K.KVQ_ROT_DENSE, R=FAKE) == K.KVQ_ERR_UNSUPPORTED
     assert quant(dt=K.KVQ_F32, rot=K.KVQ_ROT_PERM_HADAMARD, R=FAKE) == K.KVQ_ERR_UNSUPPORTED
     assert quant(rot=K.KVQ_ROT_DENSE, R=None) == K.KVQ_ERR_INVALID_ARG
+
+
+# ------------------------------------------------ pre-RoPE grouped-head keys
+def _quant_prerope(lib, **kw):
+    a = dict(K=FAKE, V=FAKE, dt=K.KVQ_F16, B=1, T=8, H=4, d=128, sb=8 * 4 * 128,
+             st=4 * 128, sh=128, gh=4, group=32, toff=0, kc=_cache(), vc=_cache())
+    a.update(kw)
+    kc = ctypes.byref(a["kc"]) if a["kc"] is not None else None
+    vc = ctypes.byref(a["vc"]) if a["vc"] is not None else None
+    return lib.kvq_quantize_prerope(a["K"], a["V"], a["dt"], a["B"], a["T"], a["H"], a["d"],
+                                    a["sb"], a["st"], a["sh"], a["gh"], a["group"], a["toff"],
+                                    kc, vc, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(gh=3), K.KVQ_ERR_INVALID_ARG),
+    (dict(gh=8), K.KVQ_ERR_INVALID_ARG),
+    (dict(H=6, gh=4), K.KVQ_ERR_INVALID_ARG),              # heads not a multiple of the group
+    (dict(H=6, gh=2, sb=8 * 6 * 128, st=6 * 128), K.KVQ_ERR_UNSUPPORTED),   # grouped: 4 heads per wave
+    (dict(dt=K.KVQ_F32, sb=8 * 4 * 128, st=4 * 128), K.KVQ_ERR_UNSUPPORTED),
+    (dict(d=64), K.KVQ_ERR_UNSUPPORTED),
+    (dict(toff=60), K.KVQ_ERR_INVALID_ARG),
+    (dict(K=None), K.KVQ_ERR_INVALID_ARG),
+    (dict(kc=_cache(codes=0)), K.KVQ_ERR_INVALID_ARG),
+])
+def test_quantize_prerope_rejects(lib, kw, want):
+    assert _quant_prerope(lib, **kw) == want
+
+
+def test_quantize_prerope_empty_is_noop(lib):
+    assert _quant_prerope(lib, T=0) == K.KVQ_OK
+    assert _quant_prerope(lib, B=0, gh=1) == K.KVQ_OK
+
+
+def _decode_prerope(lib, **kw):
+    a = dict(q=FAKE, qdt=K.KVQ_F16, B=2, Hq=8, Hkv=4, d=128, kc=_cache(), vc=_cache(),
+             tb=0, te=64, gh=4, base=10000.0, group=32, sk=None, sv=None, ns=0, rk=None,
+             rv=None, nr=0, scale=0.0, out=FAKE, odt=K.KVQ_F16, ws=FAKE * 16, wsb=1 << 30)
+    a.update(kw)
+    kc = ctypes.byref(a["kc"]) if a["kc"] is not None else None
+    vc = ctypes.byref(a["vc"]) if a["vc"] is not None else None
+    return lib.kvq_decode_attention_prerope(a["q"], a["qdt"], a["B"], a["Hq"], a["Hkv"], a["d"],
+                                            kc, vc, a["tb"], a["te"], a["gh"], a["base"], a["group"],
+                                            a["sk"], a["sv"], a["ns"], a["rk"], a["rv"], a["nr"],
+                                            a["scale"], a["out"], a["odt"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(gh=3), K.KVQ_ERR_INVALID_ARG),
+    (dict(Hkv=2, Hq=8), K.KVQ_ERR_INVALID_ARG),            # Hkv not a multiple of the group
+    (dict(base=1.0), K.KVQ_ERR_INVALID_ARG),
+    (dict(base=float("nan")), K.KVQ_ERR_INVALID_ARG),
+    (dict(base=float("inf")), K.KVQ_ERR_INVALID_ARG),
+    (dict(Hq=48, Hkv=4), K.KVQ_ERR_UNSUPPORTED),           # 4 x 12 query heads per group
+    (dict(te=65), K.KVQ_ERR_INVALID_ARG),                  # past T_cap
+    (dict(tb=5, te=4), K.KVQ_ERR_INVALID_ARG),
+    (dict(wsb=100), K.KVQ_ERR_WORKSPACE_TOO_SMALL),
+    (dict(ws=FAKE + 16), K.KVQ_ERR_INVALID_ARG),           # workspace not 256-aligned
+    (dict(d=256), K.KVQ_ERR_UNSUPPORTED),
+])
+def test_decode_prerope_rejects(lib, kw, want):
+    assert _decode_prerope(lib, **kw) == want
+
+
+def test_workspace_bytes_prerope():
+    assert K.kvq_decode_workspace_bytes_prerope(0, 4, 4, 128, 10) == 0
+    # one fp32 score per (b, query head, token) on top of the partials
+    a = K.kvq_decode_workspace_bytes_prerope(2, 8, 4, 128, 1000)
+    b = K.kvq_decode_workspace_bytes_prerope(2, 8, 4, 128, 1016)
+    assert a >= 2 * 8 * 1000 * 4 and b - a >= 2 * 8 * 16 * 4
+    assert K.kvq_decode_workspace_bytes_prerope(1, 4, 4, 128, 0, 4, 8) >= 0

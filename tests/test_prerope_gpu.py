@@ -1,0 +1,176 @@
+"""GPU parity of the pre-RoPE grouped-head rotation of the keys (RotateKV,
+IJCAI 2025 record, abstract item (ii)) against the oracle.
+
+* Write: keys rotated over groups of g heads (the oracle's
+  quantize_cache_grouped), values with the per-head Hadamard rotation;
+  codes at rounding ties as for every rotated path, and bit-exact on inputs
+  whose grouped rotation is exact on both sides (small integers times
+  Hadamard rows).
+* Decode: post-RoPE queries over the cache (keys un-rotated and
+  rotary-embedded at their slots), optionally with fp16 post-RoPE sink and
+  residual tokens, within 2e-3 normwise of the oracle run on the GPU's own
+  cache bytes.
+"""
+import json
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import kvq_oracle as O
+import workloads as W
+import int2_rotated_kv_amd as kvq
+from parity_util import (SENTINEL, require_gpu, empty_cache, cache_to_numpy, rot_matrix,
+                         compare_codes_at_ties, normwise_rel_err)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+ATTN_TOL = 2e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _report(name, **kw):
+    print(f"[prerope] {name} " + json.dumps(kw), flush=True)
+
+
+def _group_rows(a, g, k):
+    """Concatenate heads g k .. g k + g - 1 of a [B, H, T, ...] array along the last axis."""
+    return np.concatenate([a[:, g * k + i] for i in range(g)], axis=-1)
+
+
+def _outlier_kv(cfg, which):
+    return W.kv_tokens(cfg, which)          # [B, T, H, 128] fp16, outlier channels
+
+
+@pytest.mark.parametrize("g", [1, 2, 4])
+def test_quantize_prerope_ties(g):
+    """Keys with the grouped rotation (outlier data, ragged T at an offset,
+    two batches), values with the per-head Hadamard rotation; untouched slots
+    keep their sentinel bytes."""
+    cfg = W.small_config(W.config(2), B=2, T=700, Hkv=8, Hq=8)
+    K, V = _outlier_kv(cfg, "K"), _outlier_kv(cfg, "V")
+    toff, T_cap = 9, cfg.T + 20
+    kc, vc = empty_cache(cfg.B, cfg.Hkv, T_cap), empty_cache(cfg.B, cfg.Hkv, T_cap)
+    kvq.kvq_quantize_prerope(K.to(DEV), V.to(DEV), kc, vc, group_heads=g, t_offset=toff)
+    torch.cuda.synchronize()
+    gk, gv = cache_to_numpy(kc), cache_to_numpy(vc)
+    for arr in (*gk, *gv):
+        a8 = arr.view(np.uint8)
+        assert np.all(a8[:, :, :toff] == SENTINEL) and np.all(a8[:, :, toff + cfg.T:] == SENTINEL)
+    sl = slice(toff, toff + cfg.T)
+    xk = K.permute(0, 2, 1, 3).contiguous().numpy()
+    ok = O.quantize_cache_grouped(xk, g)
+    Rg = O.grouped_hadamard_rotation(g)
+    tot = dict(elements=0, code_mismatch=0, group_scale_zero_diff=0)
+    for k in range(cfg.Hkv // g):
+        st = compare_codes_at_ties(_group_rows(xk, g, k), Rg,
+                                   tuple(_group_rows(a[:, :, sl], g, k) for a in gk),
+                                   tuple(_group_rows(a, g, k) for a in ok), max_frac=1.0)
+        for key in tot:
+            tot[key] += st[key]
+    _report(f"write keys g={g}", **tot)
+    assert tot["code_mismatch"] <= 1e-5 * tot["elements"]
+    xv = V.permute(0, 2, 1, 3).contiguous().numpy()
+    ov = O.quantize_cache(xv, rot_matrix("hadamard"))
+    st = compare_codes_at_ties(xv, rot_matrix("hadamard"), tuple(a[:, :, sl] for a in gv), ov)
+    _report(f"write values g={g}", **st)
+
+
+C_G = {2: np.float32(1.0 / 16.0), 4: np.float32(1.0 / np.sqrt(512.0))}
+
+
+@pytest.mark.parametrize("g", [2, 4])
+def test_quantize_prerope_exact_bitexact(g):
+    """Rows whose grouped rotation is exact on both sides: integers z (|z| at
+    most 7 for g = 2, 3 for g = 4) in the rotated basis, x = z H / (128 g)
+    exact in fp16, and z restricted to values whose product with
+    fp32(1/sqrt(128 g)) rounds like the fp64 rotation (checked).  Codes,
+    scales and zeros must be bit-exact, including constant and zero groups."""
+    rng = np.random.default_rng(60 + g)
+    n = 128 * g
+    zmax = 7 if g == 2 else 3
+    zok = [z for z in range(-zmax, zmax + 1)
+           if z != 0 and np.float32(np.float32(z) * C_G[g]) == np.float32(z / np.sqrt(float(n)))]
+    B, T, H = 2, 40, 8
+    z = rng.choice(zok, size=(B, T, H // g, n))
+    z[:, 1::5] = 0                                                    # zero rows
+    for t in range(2, T, 5):                                          # constant groups
+        for c in range(0, n, 32):
+            z[:, t, :, c:c + 32] = rng.choice(zok)
+    Hn = np.rint(O.grouped_hadamard_rotation(g) * np.sqrt(float(n))).astype(np.int64)
+    xg = (z @ Hn).astype(np.float64) / n
+    x16 = xg.astype(np.float16)
+    assert np.array_equal(x16.astype(np.float64), xg)
+    x = x16.reshape(B, T, H // g, g, 128).reshape(B, T, H, 128)      # head g k + i = slice i
+    xt = torch.from_numpy(np.ascontiguousarray(x))
+    kc = empty_cache(B, H, T)
+    kvq.kvq_quantize_prerope(xt.to(DEV), None, kc, None, group_heads=g)
+    torch.cuda.synchronize()
+    gk = cache_to_numpy(kc)
+    xk = xt.permute(0, 2, 1, 3).contiguous().numpy()
+    Rg = O.grouped_hadamard_rotation(g)
+    y = (z.astype(np.float32) * C_G[g]).astype(np.float32)            # [B, T, H/g, n]
+    for k in range(H // g):
+        assert np.array_equal(O.rotate_rows(_group_rows(xk, g, k), Rg), y[:, :, k])
+    ok = O.quantize_cache_grouped(xk, g)
+    for a_g, a_o, what in zip(gk, ok, ("codes", "scales", "zeros")):
+        assert np.array_equal(a_g.view(np.uint8), a_o.view(np.uint8)), what
+
+
+def _prerope_case(cfg, g, t_begin, t_end, T_cap, sinks=False, q_f32=False, seed=0):
+    """Write K/V rows [0, T_cap) of the workload's generator through the
+    pre-RoPE write, decode over [t_begin, t_end) with post-RoPE queries (the
+    oracle's rope of the generator's queries at position T_cap), and compare
+    with the oracle on the GPU's cache bytes."""
+    K, V = W.kv_tokens(cfg, "K"), W.kv_tokens(cfg, "V")
+    q = W.queries(cfg).to(torch.float32 if q_f32 else torch.float16)
+    qp = O.rope(q.numpy().astype(np.float64), np.full(q.shape[1], T_cap))      # post-RoPE at T_cap
+    qd = torch.from_numpy(qp.astype(np.float32 if q_f32 else np.float16))
+    kc, vc = empty_cache(cfg.B, cfg.Hkv, T_cap), empty_cache(cfg.B, cfg.Hkv, T_cap)
+    kvq.kvq_quantize_prerope(K.to(DEV), V.to(DEV), kc, vc, group_heads=g)
+    kw = {}
+    if sinks:
+        # fp16 tokens kept as a plain cache keeps them: keys after RoPE at their
+        # positions (the first tokens and the last ones), values as they are
+        ns, nr = 3, 5
+        kh = K.permute(0, 2, 1, 3).numpy().astype(np.float64)
+        vh = V.permute(0, 2, 1, 3).numpy()
+        sk = O.rope(kh[:, :, :ns], np.arange(ns)).astype(np.float16)
+        rk = O.rope(kh[:, :, T_cap - nr:], np.arange(T_cap - nr, T_cap)).astype(np.float16)
+        kw = dict(sink_k=sk, sink_v=vh[:, :, :ns].copy(), res_k=rk, res_v=vh[:, :, T_cap - nr:].copy())
+    dk = {k: torch.from_numpy(np.ascontiguousarray(v)).to(DEV) for k, v in kw.items()}
+    out = kvq.kvq_decode_attention_prerope(qd.to(DEV), kc, vc, t_begin, t_end, group_heads=g, **dk)
+    torch.cuda.synchronize()
+    ref = O.decode_attention_prerope(qd.numpy(), cache_to_numpy(kc), cache_to_numpy(vc), t_begin, t_end, g,
+                                     **kw)
+    o = out.float().cpu().numpy()
+    assert np.all(np.isfinite(o))
+    return normwise_rel_err(o, ref)
+
+
+@pytest.mark.parametrize("cid,g,Hkv,Hq,T,t_begin,sinks", [
+    (2, 1, 4, 4, 300, 0, False),
+    (2, 2, 4, 4, 517, 7, False),
+    (2, 4, 8, 8, 1000, 3, True),
+    (5, 4, 4, 8, 777, 11, True),            # two query heads per KV head
+    (3, 4, 4, 4, 64, 0, False),             # a single tile of the attention grid
+    (2, 2, 8, 16, 35, 1, False),
+])
+def test_decode_prerope(cid, g, Hkv, Hq, T, t_begin, sinks):
+    cfg = W.small_config(W.config(cid), B=2, T=T, Hkv=Hkv, Hq=Hq)
+    err = _prerope_case(cfg, g, t_begin, T, T, sinks=sinks)
+    _report(f"decode cid={cid} g={g} Hkv={Hkv} Hq={Hq} T={T} t_begin={t_begin} sinks={sinks}", normwise=err)
+    assert err <= ATTN_TOL
+
+
+def test_decode_prerope_far_positions():
+    """A window at positions around 60000 (large RoPE angles on the fast
+    pairs) of a 65536-slot cache, fp32 queries."""
+    cfg = W.small_config(W.config(5), B=1, T=65536, Hkv=4, Hq=4)
+    err = _prerope_case(cfg, 4, 60000, 61000, 65536, q_f32=True)
+    _report("decode far positions", normwise=err)
+    assert err <= ATTN_TOL
