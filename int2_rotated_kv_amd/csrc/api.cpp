@@ -99,10 +99,12 @@ size_t workspace_bytes(int64_t B, int64_t Hq, int64_t n_splits) {
 // the attention grid's shift (below 16), rounded up to 16.
 int64_t prerope_score_rows(int64_t n_int2) { return (n_int2 + 16 + 15) / 16 * 16; }
 
-// Pre-RoPE decode workspace: the split partials, then fp32 key scores.
+// Pre-RoPE decode workspace: the split partials, fp32 key scores, then the
+// RoPE table (frequencies and per-step turns of the 64 channel pairs).
 size_t workspace_bytes_prerope(int64_t B, int64_t Hq, int64_t n_splits, int64_t n_int2) {
   const size_t parts = (size_t)B * Hq * n_splits * kvq::kPartialStride * sizeof(float);
-  return align256(parts) + (size_t)B * Hq * prerope_score_rows(n_int2) * sizeof(float);
+  const size_t scores = (size_t)B * Hq * prerope_score_rows(n_int2) * sizeof(float);
+  return align256(parts) + align256(scores) + kvq::kRopeTableBytes;
 }
 
 
@@ -328,6 +330,8 @@ kvq_status decode_impl(const void *q, kvq_dtype q_dtype, int64_t B, int64_t Hq,
     a.partials = reinterpret_cast<float *>(workspace);
     a.scores = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + align256(parts));
     a.score_rows = prerope_score_rows(n_int2);
+    a.rope_table = reinterpret_cast<uint32_t *>(
+        reinterpret_cast<char *>(a.scores) + align256((size_t)B * Hq * a.score_rows * sizeof(float)));
     a.group_heads = group_heads;
     a.log2_rope_base = log2(rope_base);
   }

@@ -954,17 +954,22 @@ static hipError_t launch_decode_prerope(const DecodeArgs &d, hipStream_t stream)
     p.q = d.q; p.q_f32 = d.q_f32;
     p.qscale = (float)((double)d.qscale / sqrt(128.0 * d.group_heads));
     p.log2_base = d.log2_rope_base;
+    p.rope_table = d.rope_table;
     p.scores = d.scores;
+    // steps of 16 tokens; at most 128 steps per wave (the kernel turns its
+    // RoPE angles step by step from an exact start), at least 8, and about
+    // two rounds of the chip's resident waves
     p.tiles = (d.n_int2 + 15) / 16;
-    // about two rounds of four waves per CU, at least 8 tiles per wave
     const int64_t groups = d.B * (d.Hkv / d.group_heads);
-    int64_t chunks = (4096 + groups - 1) / groups;
+    int64_t chunks = (8192 + groups - 1) / groups;
     const int64_t by_tiles = (p.tiles + 7) / 8;
     chunks = chunks < by_tiles ? chunks : by_tiles;
+    const int64_t min_chunks = (p.tiles + 127) / 128;
+    chunks = chunks > min_chunks ? chunks : min_chunks;
     chunks = chunks > 0 ? chunks : 1;
     p.tiles_per_wave = (p.tiles + chunks - 1) / chunks;
     p.chunks = (p.tiles + p.tiles_per_wave - 1) / p.tiles_per_wave;
-    hipError_t e = launch_prerope_scores(p, stream);
+    hipError_t e = p.tiles > 0 ? launch_prerope_scores(p, stream) : hipSuccess;
     if (e != hipSuccess) return e;
     AttnArgs a;
     a.kcodes = d.kcodes; a.kscales = d.kscales; a.kzeros = d.kzeros; a.kT_cap = d.kT_cap;

@@ -54,8 +54,9 @@ struct PreropeArgs {
   const void *q; bool q_f32;
   float qscale;              // softmax_scale * log2(e) / sqrt(128 GH)
   double log2_base;          // log2 of the RoPE base
+  uint32_t *rope_table;      // written by the table kernel, read by the score kernel
   float *scores;
-  int64_t tiles, tiles_per_wave, chunks;   // 16-token tiles; per wave; waves per (b, head group)
+  int64_t tiles, tiles_per_wave, chunks;   // steps of 16 tokens; per wave (<= 128); waves per (b, head group)
 };
 hipError_t launch_prerope_scores(const PreropeArgs &a, hipStream_t stream);
 

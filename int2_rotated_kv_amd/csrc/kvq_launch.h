@@ -70,6 +70,7 @@ struct DecodeArgs {
   // (0: not this mode); scores [B][Hq][score_rows] fp32 in the workspace
   int group_heads;
   double log2_rope_base;
+  uint32_t *rope_table;      // kRopeTableBytes of the workspace
   float *scores;
   int64_t score_rows;
 };
@@ -85,6 +86,10 @@ SplitPlan plan_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_int2);
 constexpr int kQprepDwordsPerHead = 256;
 constexpr int kQprepFixedOffset = 128;
 constexpr int kPartialStride = 132;   // o'[128], m, l, 2 pad (16-byte rows)
+// RoPE table of the pre-RoPE decode: per channel pair i < 64 the frequency in
+// revolutions per position as 64-bit fixed point (high, low word), then the
+// cosine and sine (fp32 bits) of 16 positions' angle
+constexpr size_t kRopeTableBytes = 64 * 4 * sizeof(uint32_t);
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 
