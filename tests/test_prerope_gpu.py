@@ -174,3 +174,59 @@ def test_decode_prerope_far_positions():
     err = _prerope_case(cfg, 4, 60000, 61000, 65536, q_f32=True)
     _report("decode far positions", normwise=err)
     assert err <= ATTN_TOL
+
+
+def test_fullsize_config5_prerope():
+    """The LLaMA-2-13B-shaped workload (B 8, T 65536, 40 heads) written and
+    decoded through the pre-RoPE path with groups of 4 heads, in the launch
+    plan of the benchmark: post-RoPE fp16 sinks (tokens 0-3) and residual
+    window (last 128 tokens).  Sampled head groups: codes at ties against the
+    oracle's grouped quantization, and the group's query heads against the
+    oracle decode on the GPU's own cache bytes of the group."""
+    g = 4
+    cfg = W.config(5)
+    B, T, H = cfg.B, cfg.T, cfg.Hkv
+    tb, te = cfg.int2_range
+    K = W.kv_tokens(cfg, "K", device=DEV)
+    V = W.kv_tokens(cfg, "V", device=DEV)
+    q = W.queries(cfg, device=DEV)
+    ck, cv = kvq.Int2Cache.empty(B, H, T), kvq.Int2Cache.empty(B, H, T)
+    kvq.kvq_quantize_prerope(K[:, tb:te], V[:, tb:te], ck, cv, group_heads=g, t_offset=tb)
+    # fp16 tokens as a plain cache keeps them: keys after RoPE at their positions
+    sink_k = O.rope(K[:, :tb].permute(0, 2, 1, 3).cpu().numpy(), np.arange(tb)).astype(np.float16)
+    res_k = O.rope(K[:, te:].permute(0, 2, 1, 3).cpu().numpy(), np.arange(te, T)).astype(np.float16)
+    sink_v = V[:, :tb].permute(0, 2, 1, 3).contiguous()
+    res_v = V[:, te:].permute(0, 2, 1, 3).contiguous()
+    sink_k, res_k = np.ascontiguousarray(sink_k), np.ascontiguousarray(res_k)
+    fp16 = dict(sink_k=torch.from_numpy(sink_k).to(DEV), sink_v=sink_v,
+                res_k=torch.from_numpy(res_k).to(DEV), res_v=res_v)
+    out = kvq.kvq_decode_attention_prerope(q, ck, cv, tb, te, group_heads=g, **fp16)
+    out_int2 = kvq.kvq_decode_attention_prerope(q, ck, cv, tb, te, group_heads=g)   # the x50 sinks dominate `out`
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(out_int2.float()).all()
+    Rg = O.grouped_hadamard_rotation(g)
+    G = cfg.G
+    for b, k in ((0, 0), (5, 7)):
+        hs = slice(g * k, g * k + g)
+        xk = K[b:b + 1, tb:te, hs].permute(0, 2, 1, 3).cpu().numpy()      # [1, g, n, 128]
+        kg = tuple(a[b:b + 1, hs].cpu().numpy() for a in (ck.codes, ck.scales, ck.zeros))
+        vg = tuple(a[b:b + 1, hs].cpu().numpy() for a in (cv.codes, cv.scales, cv.zeros))
+        st = compare_codes_at_ties(_group_rows(xk, g, 0), Rg,
+                                   tuple(_group_rows(a[:, :, tb:te], g, 0) for a in kg),
+                                   tuple(_group_rows(a, g, 0) for a in O.quantize_cache_grouped(xk, g)),
+                                   max_frac=1e-5)
+        hq = slice(g * k * G, (g * k + g) * G)
+        ref = O.decode_attention_prerope(q[b:b + 1, hq].cpu().numpy(), kg, vg, tb, te, g,
+                                         sink_k=sink_k[b:b + 1, hs], sink_v=sink_v[b:b + 1, hs].cpu().numpy(),
+                                         res_k=res_k[b:b + 1, hs], res_v=res_v[b:b + 1, hs].cpu().numpy())
+        err = normwise_rel_err(out[b:b + 1, hq].float().cpu().numpy(), ref)
+        ref2 = O.decode_attention_prerope(q[b:b + 1, hq].cpu().numpy(), kg, vg, tb, te, g)
+        err2 = normwise_rel_err(out_int2[b:b + 1, hq].float().cpu().numpy(), ref2)
+        rate = st["group_scale_zero_diff"] / st["groups"]
+        _report(f"fullsize c5 prerope g={g} b={b} group={k}", normwise=err, normwise_int2_only=err2, keys=st,
+                group_rate=rate)
+        assert err <= ATTN_TOL and err2 <= ATTN_TOL
+        # scale/zero groups moved across an fp16 boundary by the rounding of
+        # the 512-point fp32 transform (two butterfly stages more than the
+        # per-head one): about 9e-5 of the groups here
+        assert rate <= 2e-4
