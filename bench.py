@@ -95,6 +95,27 @@ ARITHMETIC_GQA = {"write": ARITHMETIC_WRITE,
                             "f32 scale/zero terms",
                   "values": "f16 weights x f16 (code*s - 1.5s) on the matrix cores, f32 accumulation",
                   "combine": "f32 merge and un-rotation, output in the query dtype"}
+ARITHMETIC_PREROPE = {"write": ARITHMETIC_WRITE + "; keys rotated over the group's heads",
+                      "scores": "exact integer H_32 of the codes on the matrix cores (fp4), f32 scales, butterflies "
+                                "over groups and heads, RoPE and dot with the post-RoPE query",
+                      "values": "f16 weights p*s times the codes (f16 dot2), f32 accumulation",
+                      "combine": "f32 merge and un-rotation, output in the query dtype"}
+# Vector ALU issue peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, one fp32
+# instruction per lane per cycle (an FMA counts as one operation; packed fp32
+# is not used), in tera lane-operations per second
+PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+
+
+def prerope_ops_per_unit(gh: int, g: int) -> int:
+    """fp32 VALU operations per (INT2 token, KV head) of the pre-RoPE score
+    step, H_32 of the codes aside (exact, on the matrix cores): scales with
+    the first group butterfly (1.5 per channel), the second group butterfly
+    fused with RoPE (4 per channel pair), log2(gh) head butterflies per
+    channel, one FMA per channel and query head, and the angle turn of the
+    64 pairs (4 each) shared by the gh heads."""
+    return 192 + 256 + 128 * (gh.bit_length() - 1) + 128 * g + 256 // gh
+
+
 ARITHMETIC_BBIT = {"write": ARITHMETIC_WRITE.replace("2-bit", "b-bit"),
                    "scores": "int32 dot of the codes with a 19-bit fixed-point rotated query, f32 scale/zero terms",
                    "values": "f32 FMA per code, f32 accumulation",
@@ -380,6 +401,17 @@ def main():
               "algorithmic_bytes_per_launch": d_bytes,
               "bytes_per_unit": d_unit, "unit_of_work": "(INT2 token, kv head)",
               "units_per_launch": int2_tokens * H, "avg_ms": round(d_ms, 4)}
+    if GHP:
+        # the decode call is bound by the score step's vector arithmetic
+        ops = int2_tokens * H * prerope_ops_per_unit(GHP, cfg.G)
+        tops = ops / (d_ms * 1e-3) / 1e12
+        roof_d = {"bound": "alu", "achieved": round(tops, 2), "peak": round(PEAK_VALU_TOPS, 2),
+                  "unit": "Top/s", "frac": round(tops / PEAK_VALU_TOPS, 4), "traffic": None,
+                  "kernel": f"decode call (kv_rope_table + kv_prerope_scores<{GHP}> + kv_int2_decode_attn<4, true>"
+                            " + kv_combine_unrotate)",
+                  "algorithmic_ops_per_launch": ops, "ops_per_unit": prerope_ops_per_unit(GHP, cfg.G),
+                  "unit_of_work": "(INT2 token, kv head)", "units_per_launch": int2_tokens * H,
+                  "avg_ms": round(d_ms, 4), "hbm_gbs": round(dec_gbs, 1)}
     dominant, other = (roof_q, roof_d) if q_ms >= d_ms else (roof_d, roof_q)
     cache_tag = "int2" if (kbits, vbits) == (2, 2) else f"k{kbits}v{vbits}-bit"
 
@@ -388,7 +420,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": f"f16 in / {cache_tag} cache", "data": "synthetic",
-        "arithmetic": (ARITHMETIC_BBIT if (kbits, vbits) != (2, 2) else
+        "arithmetic": (ARITHMETIC_PREROPE if GHP else ARITHMETIC_BBIT if (kbits, vbits) != (2, 2) else
                        ARITHMETIC_G1 if cfg.G == 1 else ARITHMETIC_GQA),
         "config": {"workload": workload, "B": B, "T": T, "Hkv": H, "Hq": cfg.Hq, "d": d,
                    "kv_input": "f16",

@@ -905,19 +905,6 @@ __global__ __launch_bounds__(kCombineThreads) void kv_combine_unrotate(CombineAr
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-// Enough waves to fill the chip once: 256 CUs x 4 SIMDs x 2 resident waves
-// of the attention kernel (its register budget allows two per SIMD).  One
-// round of resident waves, each streaming every S-th tile of its head,
-// measured faster than more, shorter waves.
-constexpr int64_t kTargetWaves = 2048;
-
-// Waves per split unit: one per query head for G = 1, one per four query
-// heads of a KV head for G >= 2 (the matrix-core GQA kernel).
-static int64_t split_units(int64_t B, int64_t Hq, int64_t Hkv) {
-  const int64_t G = Hq / Hkv;
-  return G == 1 ? B * Hq : B * Hkv * ((G + 3) / 4);
-}
-
 // Tile grid shift: start the grid t_begin mod 16 rows early when both caches
 // keep the rows of a head on 16-row boundaries.
 // A paged cache starts the grid on a 64-token boundary instead, so that no
@@ -925,19 +912,6 @@ static int64_t split_units(int64_t B, int64_t Hq, int64_t Hkv) {
 static int grid_skip(const DecodeArgs &d) {
   if (d.block_table != nullptr) return (int)(d.t_begin % 64);
   return (d.kT_cap % 16 == 0 && d.vT_cap % 16 == 0) ? (int)(d.t_begin % 16) : 0;
-}
-
-SplitPlan plan_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_int2) {
-  SplitPlan p{0};
-  if (n_int2 <= 0 || B <= 0 || Hq <= 0 || Hkv <= 0) return p;
-  const int64_t units = split_units(B, Hq, Hkv);
-  int64_t s = kTargetWaves / units;              // stay within one round of resident waves
-  const int64_t by_len = (n_int2 + 255) / 256;   // at least ~256 tokens per wave
-  if (s > by_len) s = by_len;
-  if (s > 4096) s = 4096;
-  if (s < 1) s = 1;
-  p.n_splits = s;
-  return p;
 }
 
 // Keys with the pre-RoPE grouped-head rotation: the score launch, then the

@@ -80,6 +80,9 @@ struct SplitPlan {
   int64_t n_splits;
 };
 SplitPlan plan_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_int2);
+// attention waves per split: one per query head for G = 1, one per four
+// query heads of a KV head for G >= 2 (the matrix-core GQA kernel)
+int64_t split_units(int64_t B, int64_t Hq, int64_t Hkv);
 
 // Per query head: 128 dwords of nibble limbs and group sums, then the 128
 // fixed-point query values (int32).
