@@ -377,16 +377,21 @@ def main():
         stem = "kv_rotate_quant_fwht_perm" if rot == "perm" else "kv_rotate_quant_fwht"
         names = [f"{stem}_f16" if b == 2 else f"{stem}_b{b}_f16" for b in (kbits, vbits)]
         q_kernel = names[0] if kbits == vbits else " + ".join(names)
+    q_traffic_key = q_kernel
+    if GHP:
+        # grouped keys and per-head values: two write launches, one traffic record
+        q_kernel = (f"kv_rotate_quant_fwht_grouped_f16<{GHP}> + kv_rotate_quant_fwht_f16" if GHP > 1
+                    else "kv_rotate_quant_fwht_f16")
+        q_traffic_key = "kv_rotate_quant_prerope"
     roof_q = {"bound": "hbm", "achieved": round(q_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
               "frac": round(q_gbs / PEAK_HBM_GBS, 4),
-              "traffic": traffic_from_profile(q_kernel, workload, os.path.join(csrc, q_src)),
+              "traffic": traffic_from_profile(q_traffic_key, workload, os.path.join(csrc, q_src)),
               "kernel": q_kernel, "algorithmic_bytes_per_launch": q_bytes,
               "bytes_per_unit": q_unit, "unit_of_work": "(token, kv head)",
               "units_per_launch": B * n_q * H, "avg_ms": round(q_ms, 4)}
     d_kernel, d_src = (("kv_int2_decode_attn", "kv_decode.hip") if cfg.G == 1
                        else ("kv_int2_decode_attn_gqa", "kv_decode_gqa.hip"))
     if GHP:
-        q_kernel = f"kv_rotate_quant_fwht_grouped_f16<{GHP}> + kv_rotate_quant_fwht_f16" if GHP > 1 else q_kernel
         d_kernel, d_src = f"kv_prerope_scores<{GHP}> + kv_int2_decode_attn<4, true>", "kv_decode_prerope.hip"
     # the query preparation is its own launch only for a dense rotation or
     # grouped-query attention; otherwise the attention waves do it

@@ -69,20 +69,45 @@ __device__ __forceinline__ double frac_revolutions(uint32_t t, uint32_t fhi, uin
 // round(4 rev), remainder r = 2 pi (rev - k / 4) in [-pi/4, pi/4], Taylor
 // series of sin r and cos r to degree 19 and 18 (truncation below 1e-19),
 // then the quarter turns.  No large-argument reduction is needed here.
-__host__ __device__ constexpr double factorial(int i) { return i <= 1 ? 1.0 : i * factorial(i - 1); }
+// 1/i! for i <= 22 (each rounded once from the exact factorial, which is
+// exact in fp64 up to 22!)
+struct InvFactorials {
+  double v[23];
+  constexpr InvFactorials() : v() {
+    double f = 1.0;
+    for (int i = 0; i < 23; ++i) {
+      if (i > 0) f *= i;
+      v[i] = 1.0 / f;
+    }
+  }
+};
+__device__ constexpr InvFactorials kInvFact{};
 __device__ __forceinline__ void sincos_turns(double rev, double *sn, double *cs) {
   const double k = rint(4.0 * rev);
   const double r = (rev - 0.25 * k) * 6.283185307179586;
   const double r2 = r * r;
-  double ps = 1.0 / factorial(19), pc = 1.0 / factorial(18);
+  double ps = kInvFact.v[19], pc = kInvFact.v[18];
 #pragma unroll
-  for (int i = 17; i >= 3; i -= 2) ps = fma(ps, -r2, 1.0 / factorial(i));
+  for (int i = 17; i >= 3; i -= 2) ps = fma(ps, -r2, kInvFact.v[i]);
 #pragma unroll
-  for (int i = 16; i >= 2; i -= 2) pc = fma(pc, -r2, 1.0 / factorial(i));
+  for (int i = 16; i >= 2; i -= 2) pc = fma(pc, -r2, kInvFact.v[i]);
   const double sr = r * fma(ps, -r2, 1.0), cr = fma(pc, -r2, 1.0);
   const int q = (int)k & 3;
   *sn = q == 0 ? sr : q == 1 ? cr : q == 2 ? -sr : -cr;
   *cs = q == 0 ? cr : q == 1 ? -sr : q == 2 ? -cr : sr;
+}
+
+// 2^x in fp64 for x <= 0 of moderate size: 2^floor(x) exactly (ldexp) times
+// e^(r ln 2), r = x - floor(x) in [0, 1), by its Taylor series to degree 22
+// (truncation below 1e-24).  Written out so that the table kernel needs no
+// library call (and no call stack).
+__device__ __forceinline__ double exp2_f64(double x) {
+  const double k = floor(x);
+  const double u = (x - k) * 0.6931471805599453;                    // ln 2
+  double p = kInvFact.v[22];
+#pragma unroll
+  for (int i = 21; i >= 0; --i) p = fma(p, u, kInvFact.v[i]);
+  return ldexp(p, (int)k);
 }
 
 // The RoPE table: thread i (< 64) writes pair i's frequency base^(-i/64)
@@ -90,7 +115,7 @@ __device__ __forceinline__ void sincos_turns(double rev, double *sn, double *cs)
 // and the cosine and sine of 16 positions' angle.
 __global__ __launch_bounds__(64) void kv_rope_table(double log2_base, uint32_t *tab) {
   const int i = threadIdx.x;
-  const double f = exp2(-(double)i / 64.0 * log2_base) * 0.15915494309189535;   // / (2 pi)
+  const double f = exp2_f64(-(double)i / 64.0 * log2_base) * 0.15915494309189535;   // / (2 pi)
   const double hi = floor(f * 4294967296.0);
   const uint32_t fhi = (uint32_t)hi, flo = (uint32_t)((f * 4294967296.0 - hi) * 4294967296.0);
   double sv, cv;
