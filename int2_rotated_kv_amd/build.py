@@ -9,7 +9,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvq.so")
 
-SOURCES = ["api.cpp", "kvq_plan.cpp", "kv_rotate_quant.hip", "kv_rotate_quant_dense.hip", "kv_decode.hip", "kv_decode_gqa.hip",
+SOURCES = ["api.cpp", "kvq_plan.cpp", "kv_rotate_quant.hip", "kv_rotate_quant_dense.hip", "kv_decode.hip", "kv_decode_gqa.hip", "kv_decode_gqa_bits.hip",
            "kv_decode_generic.hip", "kv_decode_prerope.hip", "kvq_scratch.hip"]
 
 FLAGS = [

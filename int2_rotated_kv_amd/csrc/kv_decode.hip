@@ -986,10 +986,13 @@ hipError_t launch_decode(const DecodeArgs &d, hipStream_t stream) {
   // one query head per KV head without a dense rotation: the attention waves
   // prepare the query themselves
   const bool fused_prep = G == 1 && (d.rot == 0 || d.rot == 1);
-  // other code widths: the b-bit kernel, which prepares its query itself
+  // other code widths: the b-bit kernel for one query head per KV head
+  // (which prepares its query itself), the b-bit grouped-query kernel
+  // otherwise (which reads the prepared query like the 2-bit one)
   const bool generic = d.kbits != 2 || d.vbits != 2;
+  const bool generic_gqa = generic && G >= 2;
   // the b-bit kernel takes a dense R's query from the preparation launch
-  if (((!generic && !fused_prep) || (generic && d.rot == 2)) && d.n_splits > 0) {
+  if (((!generic && !fused_prep) || (generic && (d.rot == 2 || generic_gqa))) && d.n_splits > 0) {
     PrepArgs p;
     p.q = d.q; p.q_f32 = d.q_f32; p.Hq = (int)d.Hq; p.Hkv = (int)d.Hkv;
     p.rot = d.rot; p.R = d.R; p.perm = d.perm; p.qscale = d.qscale;
@@ -1005,8 +1008,8 @@ hipError_t launch_decode(const DecodeArgs &d, hipStream_t stream) {
     a.t_begin = d.t_begin; a.n_int2 = d.n_int2; a.t_ends = d.t_ends;
     a.n_splits = d.n_splits;
     a.B = d.B;
-    // B*S split rows; the b-bit kernel runs one wave per query head
-    a.total_waves = (generic ? d.B * d.Hq : split_units(d.B, d.Hq, d.Hkv)) * d.n_splits;
+    // B*S split rows; the b-bit kernel for G = 1 runs one wave per query head
+    a.total_waves = (generic && !generic_gqa ? d.B * d.Hq : split_units(d.B, d.Hq, d.Hkv)) * d.n_splits;
     a.Hkv = (int)d.Hkv; a.Hq = (int)d.Hq; a.G = G;
     a.qprep = reinterpret_cast<const uint32_t *>(d.qprep);
     a.partials = d.partials;
@@ -1015,7 +1018,10 @@ hipError_t launch_decode(const DecodeArgs &d, hipStream_t stream) {
     a.block_table = d.block_table;
     a.max_pages = d.max_pages; a.n_pages = d.n_pages; a.page_tokens = d.page_tokens;
     a.q = d.q; a.q_f32 = d.q_f32; a.rot = d.rot; a.perm = d.perm; a.qscale = d.qscale;
-    if (generic) {
+    if (generic_gqa) {
+      hipError_t e = launch_attn_gqa_bits(a, d.kbits, d.vbits, stream);
+      if (e != hipSuccess) return e;
+    } else if (generic) {
       hipError_t e = launch_attn_generic(a, d.kbits, d.vbits, stream);
       if (e != hipSuccess) return e;
     } else if (G == 1) {

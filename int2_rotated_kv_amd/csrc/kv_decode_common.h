@@ -424,5 +424,6 @@ struct PagedTileRows {
 
 hipError_t launch_attn_gqa(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_attn_generic(const AttnArgs &a, int kbits, int vbits, hipStream_t stream);
+hipError_t launch_attn_gqa_bits(const AttnArgs &a, int kbits, int vbits, hipStream_t stream);
 
 }  // namespace kvq

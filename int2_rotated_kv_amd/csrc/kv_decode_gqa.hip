@@ -41,17 +41,10 @@
 // softmax layout.
 #include <type_traits>
 
-#include "kv_decode_common.h"
+#include "kv_decode_mq.h"
 
 namespace kvq {
 
-typedef int v8i_t __attribute__((ext_vector_type(8)));
-typedef float float4v_t __attribute__((ext_vector_type(4)));
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef half8_t v8h_t;
-
-constexpr int kMqHeads = 4;          // query heads per wave
-constexpr int kMqWaves = 4;          // waves per workgroup
 // LDS per wave, in dwords: per-token records, the tile's value codes and the
 // fp16 weights of the four heads.
 constexpr int kMqRecDwords = 12;     // ks, kz (4) | (s_j, -fp16(1.5 s_j)) (4) | z_j + fp16(1.5 s_j) fp32 (4)
@@ -59,40 +52,6 @@ constexpr int kMqRecOff = 0;
 constexpr int kMqCodeOff = kMqRecOff + 64 * kMqRecDwords;          // 64 tokens x 32 bytes
 constexpr int kMqPwOff = kMqCodeOff + 64 * kCodeBytes / 4;          // [head][64 tokens] fp16
 constexpr int kMqLdsDwords = kMqPwOff + kMqHeads * 64 / 2;
-
-// Score slot k <-> channel of the head: slot 32 kb + 8 u + e holds nibble e
-// of unpacked code dword u of group kb (mq_unpack).
-__device__ __forceinline__ constexpr int mq_channel(int k) {
-  return 32 * (k >> 5) + 16 * ((k >> 4) & 1) + 4 * ((k & 7) >> 1) + 2 * (k & 1) + ((k >> 3) & 1);
-}
-
-// One group's 32 codes (two packed dwords) as nibbles 0b00cc: the masked
-// copy of a dword keeps channels 4b and 4b+2 of byte b (low and high nibble),
-// the shifted copy channels 4b+1 and 4b+3.
-__device__ __forceinline__ v8i_t mq_unpack(u32x2_t c) {
-  v8i_t b;
-  b[0] = (int)(c.x & 0x33333333u);
-  b[1] = (int)((c.x >> 2) & 0x33333333u);
-  b[2] = (int)(c.y & 0x33333333u);
-  b[3] = (int)((c.y >> 2) & 0x33333333u);
-  b[4] = 0; b[5] = 0; b[6] = 0; b[7] = 0;
-  return b;
-}
-
-// Balanced base-32 digit L (0 = most significant) of |q| < 2^19.
-__device__ __forceinline__ int mq_digit(int q, int L) {
-  int r = q, d = 0;
-#pragma unroll
-  for (int i = 3; i >= 0; --i) {
-    const int di = ((r + 16) & 31) - 16;
-    if (i == L) d = di;
-    r = (r - di) >> 5;
-  }
-  return d;
-}
-
-// E8M0 block scales of the four digit positions: 2^15, 2^10, 2^5, 1.
-__device__ __forceinline__ constexpr int mq_scale(int L) { return 127 + 15 - 5 * L; }
 
 // Loads of one 64-token tile.  K side: lane (token slot lane%16, group
 // lane/16); tokens 16k + lane%16 for block k.  Token scales and zeros: lane =
@@ -108,44 +67,6 @@ struct MqState {
   float m, l, zacc[4];     // softmax layout: the lane's head (lane / 16)
   float4v_t o[2];          // value layout: rows (head lane/16, e = 0..3), byte 2 (lane%16) + blk
 };
-
-// Sums / maxima over the 16 lanes of a row.
-__device__ __forceinline__ float row_sum16(float v) {
-  v += row_ror<1>(v);
-  v += row_ror<2>(v);
-  v += row_ror<4>(v);
-  v += row_ror<8>(v);
-  return v;
-}
-__device__ __forceinline__ float row_max16(float v) {
-  v = fmaxf(v, row_ror<1>(v));
-  v = fmaxf(v, row_ror<2>(v));
-  v = fmaxf(v, row_ror<4>(v));
-  v = fmaxf(v, row_ror<8>(v));
-  return v;
-}
-__device__ __forceinline__ float lane_read(float v, int l) {
-  return bits_as_float((uint32_t)__builtin_amdgcn_readlane((int)float_as_bits(v), l));
-}
-
-// Value operand of code byte block BLK: in y (nibble form, positions
-// (0, 2) in y02 and (1, 3) in y13), byte BLK is token t0's and byte 2 + BLK
-// token t0 + 1's.  Each pair of codes (exact in fp16 after the fp4
-// conversion) becomes code * s - nb with (s, nb) the fp16 halves of sv.
-template <int BLK>
-__device__ __forceinline__ half8_t mq_bvals(uint32_t y02, uint32_t y13, uint32_t sv0, uint32_t sv1) {
-  const half2_t c0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y02, 2.0f, BLK);
-  const half2_t c1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y13, 2.0f, BLK);
-  const half2_t c2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y02, 2.0f, 2 + BLK);
-  const half2_t c3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y13, 2.0f, 2 + BLK);
-  const half2_t p0 = __builtin_bit_cast(half2_t, sv0), p1 = __builtin_bit_cast(half2_t, sv1);
-  const _Float16 s0 = p0.x, n0 = p0.y, s1 = p1.x, n1 = p1.y;
-  const half2_t a = __builtin_elementwise_fma(c0, half2_t{s0, s0}, half2_t{n0, n0});
-  const half2_t b = __builtin_elementwise_fma(c1, half2_t{s0, s0}, half2_t{n0, n0});
-  const half2_t c = __builtin_elementwise_fma(c2, half2_t{s1, s1}, half2_t{n1, n1});
-  const half2_t d = __builtin_elementwise_fma(c3, half2_t{s1, s1}, half2_t{n1, n1});
-  return half8_t{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
-}
 
 // grid: ceil(total_waves / 4) workgroups of 4 waves; wave index
 // gw = ((b*Hkv + hkv)*S + split)*quads + quad for one length, the

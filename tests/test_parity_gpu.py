@@ -703,6 +703,53 @@ def test_decode_bits(kbits, vbits, rot, cid, G):
     assert err <= ATTN_TOL
 
 
+@pytest.mark.parametrize("kbits,vbits,rot,cid,G", [
+    (1, 1, "hadamard", 2, 4), (1, 2, "perm", 2, 2), (1, 4, "dense", 4, 8), (2, 1, "none", 1, 3),
+    (2, 4, "hadamard", 5, 4), (4, 1, "hadamard", 2, 2), (4, 2, "perm", 2, 8), (4, 4, "dense", 4, 4),
+    (4, 4, "hadamard", 2, 3)])
+def test_decode_bits_gqa(kbits, vbits, rot, cid, G):
+    """Grouped-query decode at widths other than 2/2 (the matrix-core b-bit
+    kernel: 1-bit codes spread to 2-bit fields, 4-bit codes as two 2-bit
+    planes) against the oracle on the same cache bytes: every width pair,
+    query groups of 2, 3 (a partial group of four heads), 4 and 8 (two
+    groups), every rotation, fp16 sinks and residual tokens (LLaMA-2-13B
+    recipe), a ragged INT2 range that starts inside a tile."""
+    T = 900
+    extra = dict(t_new=0) if cid == 4 else {}
+    cfg = W.small_config(W.config(cid), T=T, B=2, Hkv=2, Hq=2 * G, **extra)
+    perm = (W.channel_orders(cfg) if rot == "perm" else
+            W.dense_rotations(cfg) if rot == "dense" else None)
+    Rm = rot_matrix(rot, perm)
+    kh = W.kv_tokens(cfg, "K").permute(0, 2, 1, 3).contiguous().numpy()
+    vh = W.kv_tokens(cfg, "V").permute(0, 2, 1, 3).contiguous().numpy()
+    kcache = O.quantize_cache(kh, Rm, bits=kbits)
+    vcache = O.quantize_cache(vh, Rm, bits=vbits)
+    q = W.queries(cfg)
+    fp16 = {}
+    tb, te = (cfg.n_sink, T - cfg.n_res) if (cfg.n_sink or cfg.n_res) else (7, T - 5)
+    if cfg.n_sink or cfg.n_res:
+        fp16 = dict(sink_k=np.ascontiguousarray(kh[:, :, :cfg.n_sink]).astype(np.float16),
+                    sink_v=np.ascontiguousarray(vh[:, :, :cfg.n_sink]).astype(np.float16),
+                    res_k=np.ascontiguousarray(kh[:, :, T - cfg.n_res:]).astype(np.float16),
+                    res_v=np.ascontiguousarray(vh[:, :, T - cfg.n_res:]).astype(np.float16))
+    up = {k: torch.from_numpy(v).to(DEV) for k, v in fp16.items()}
+    out = kvq.kvq_decode_attention(q.to(DEV), cache_from_numpy(*kcache), cache_from_numpy(*vcache),
+                                   tb, te, rot=rot, R=_rot_arg(rot, perm), **up)
+    torch.cuda.synchronize()
+    ref = O.decode_attention(q.numpy(), kcache, vcache, tb, te, Rm, **fp16)
+    err = normwise_rel_err(out.float().cpu().numpy(), ref)
+    _report(f"decode bits gqa K{kbits}V{vbits} {rot} c{cid} G={G}", normwise=err)
+    assert err <= ATTN_TOL
+    if fp16:                                   # the INT2 part alone (the x50 sinks dominate)
+        out2 = kvq.kvq_decode_attention(q.to(DEV), cache_from_numpy(*kcache), cache_from_numpy(*vcache),
+                                        tb, te, rot=rot, R=_rot_arg(rot, perm))
+        torch.cuda.synchronize()
+        ref2 = O.decode_attention(q.numpy(), kcache, vcache, tb, te, Rm)
+        err2 = normwise_rel_err(out2.float().cpu().numpy(), ref2)
+        _report(f"decode bits gqa K{kbits}V{vbits} INT2 only", normwise=err2)
+        assert err2 <= ATTN_TOL
+
+
 @pytest.mark.parametrize("kbits,vbits,rot,cid,G,P", [
     (4, 2, "hadamard", 2, 1, 128), (1, 4, "perm", 2, 2, 64), (2, 1, "hadamard", 5, 1, 64),
     (4, 1, "dense", 4, 4, 64)])
