@@ -116,6 +116,11 @@ def prerope_ops_per_unit(gh: int, g: int) -> int:
     return 192 + 256 + 128 * (gh.bit_length() - 1) + 128 * g + 256 // gh
 
 
+ARITHMETIC_BBIT_GQA = {"write": ARITHMETIC_WRITE.replace("2-bit", "b-bit"),
+                       "scores": "fp8 digits of a 19-bit fixed-point query x 2-bit planes of the codes (fp4) on the "
+                                 "matrix cores (exact), f32 scale/zero terms",
+                       "values": "f16 weights x f16 (plane*s - 1.5 s) on the matrix cores, f32 accumulation",
+                       "combine": "f32 merge and un-rotation, output in the query dtype"}
 ARITHMETIC_BBIT = {"write": ARITHMETIC_WRITE.replace("2-bit", "b-bit"),
                    "scores": "int32 dot of the codes with a 19-bit fixed-point rotated query, f32 scale/zero terms",
                    "values": "f32 FMA per code, f32 accumulation",
@@ -396,9 +401,11 @@ def main():
     # the query preparation is its own launch only for a dense rotation or
     # grouped-query attention; otherwise the attention waves do it
     prep_kernel = (cfg.G > 1 or rot in ("dense", "perm")) and not GHP
-    if (kbits, vbits) != (2, 2):                   # the b-bit kernel prepares its query itself
+    if (kbits, vbits) != (2, 2) and cfg.G == 1:    # the b-bit kernel prepares its query itself
         d_kernel, d_src = f"kv_quant_decode_attn<{kbits},{vbits}>", "kv_decode_generic.hip"
         prep_kernel = rot == "dense"                 # except a dense R's
+    elif (kbits, vbits) != (2, 2):                 # grouped-query b-bit kernel, prepared query
+        d_kernel, d_src = f"kv_quant_decode_attn_gqa<{kbits},{vbits}>", "kv_decode_gqa_bits.hip"
     roof_d = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
               "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
               "traffic": traffic_from_profile(d_kernel, workload, os.path.join(csrc, d_src)),
@@ -425,7 +432,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": f"f16 in / {cache_tag} cache", "data": "synthetic",
-        "arithmetic": (ARITHMETIC_PREROPE if GHP else ARITHMETIC_BBIT if (kbits, vbits) != (2, 2) else
+        "arithmetic": (ARITHMETIC_PREROPE if GHP else
+                       (ARITHMETIC_BBIT if cfg.G == 1 else ARITHMETIC_BBIT_GQA) if (kbits, vbits) != (2, 2) else
                        ARITHMETIC_G1 if cfg.G == 1 else ARITHMETIC_GQA),
         "config": {"workload": workload, "B": B, "T": T, "Hkv": H, "Hq": cfg.Hq, "d": d,
                    "kv_input": "f16",

@@ -96,7 +96,7 @@ struct MbState {
 // grid: ceil(total_waves / 4) workgroups of 4 waves; the wave map of the
 // 2-bit grouped-query kernel.
 template <int KB, int VB>
-__global__ __launch_bounds__(64 * kMqWaves) void kv_quant_decode_attn_gqa(AttnArgs a) {
+__global__ __launch_bounds__(64 * kMqWaves, 2) void kv_quant_decode_attn_gqa(AttnArgs a) {
   typedef MbLds<VB> L;
   constexpr int kKRow = 16 * KB;                   // key row bytes
   constexpr int kPV = VB == 4 ? 2 : 1;             // value planes
