@@ -22,7 +22,9 @@ bandwidth (algorithmic bytes / time of the decode call); the quantize
 throughput, per-kernel rooflines and the oracle's CPU throughput on a
 bounded sample are extra fields.  --config 4 (GQA, dense rotation, prefill
 slice) and --config 5 (13B-shaped, fp16 sinks and residual) give the same
-line for those workloads.
+line for those workloads; the default invocation also runs both as child
+processes and summarizes them under other_workloads (--headline-only skips
+that).
 """
 import argparse
 import hashlib
@@ -79,6 +81,9 @@ def parse():
     p.add_argument("--config", type=int, default=3, choices=(3, 4, 5),
                    help="workload id (3 = throughput case, 4 = GQA dense rotation, 5 = sinks)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--headline-only", action="store_true",
+                   help="skip the short child runs of the GQA and LLaMA-2-13B workloads that the default "
+                        "invocation adds to its line (other_workloads)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a 1 GiB elementwise device copy (counter calibration)")
     return p.parse_args()
@@ -462,7 +467,38 @@ def main():
     rec["copy_reference_gbs"] = copy_bandwidth()
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, rot, K, V, q, R, fp16, kbits, vbits, GHP)
+    default_run = (args.config == 3 and not (args.perm or args.varlen or args.paged or GHP)
+                   and (kbits, vbits) == (2, 2))
+    if default_run and not args.headline_only:
+        rec["other_workloads"] = other_workloads(args)
     print(json.dumps(rec), flush=True)
+
+
+def other_workloads(args):
+    """The GQA (dense R, 131072 context) and LLaMA-2-13B (sinks + residual)
+    workloads, each measured by a child run of this script, summarized next
+    to the headline so that every workload's distance to the roofline is in
+    the one line."""
+    import subprocess
+    out = {}
+    for c in (4, 5):
+        cmd = [sys.executable, os.path.abspath(__file__), "--config", str(c), "--no-cpu-baseline",
+               "--steps", str(args.steps), "--warmup", str(args.warmup)]
+        print(f"[bench] child run: config {c}", file=sys.stderr, flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+        lines = [ln for ln in res.stdout.splitlines() if ln.startswith("{")]
+        if res.returncode != 0 or not lines:
+            out[f"config{c}"] = {"error": f"child run failed ({res.returncode})"}
+            continue
+        r = json.loads(lines[-1])
+        out[r["config"]["workload"]] = {
+            "decode_ms": r["decode_ms"], "decode_gbs": r["value"], "decode_pct_of_peak": r["decode_pct_of_peak"],
+            "quantize_ms": r["quantize_ms"], "quantize_gbs": r["quantize_gbs"],
+            "quantize_pct_of_peak": round(100 * r["quantize_gbs"] / PEAK_HBM_GBS, 2),
+            "roofline": {k: r["roofline"][k] for k in ("kernel", "bound", "achieved", "peak", "unit", "frac")},
+            "roofline_other": {k: r["roofline_other"][k] for k in ("kernel", "bound", "achieved", "peak", "unit",
+                                                                    "frac")}}
+    return out
 
 
 def cpu_baseline(cfg, rot, K, V, q, R, fp16, kbits=2, vbits=2, ghp=0):
