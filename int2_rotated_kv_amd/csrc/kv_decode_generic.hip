@@ -19,7 +19,9 @@
 // summed by a reduce-scatter that leaves two channels in each lane, and the
 // wave writes the same partial (o', m, l) as the INT2 kernels, so the
 // combine and un-rotation are shared.
-#include "kv_decode_common.h"
+#include <type_traits>
+
+#include "kv_decode_mq.h"
 
 namespace kvq {
 
@@ -108,7 +110,7 @@ __device__ __forceinline__ float gen_half(const u32x2_t &v, int g) {
 
 // grid: ceil(total_waves / 4) blocks of 4 waves; wave index as in
 // wave_place with one wave per query head (`per` = G).
-template <int KB, int VB>
+template <int KB, int VB, bool VM>
 __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs a) {
   // the query as a 19-bit fixed point in five signed 4-bit limbs: limb L,
   // nibble 8u + h at the position of the key nibble it multiplies (nib_pos);
@@ -116,6 +118,12 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
   __shared__ __attribute__((aligned(16))) uint32_t ql_all[kGenWaves][5][16];
   __shared__ uint8_t qn_all[kGenWaves][5][kD];
   __shared__ float qsum_all[kGenWaves][4];
+  // value step on the matrix cores: the tile's value rows, per-token
+  // (s, -fp16(1.5 s)) of each group, and the fp16 weights
+  constexpr int kVRow = 16 * VB;
+  __shared__ __attribute__((aligned(16))) uint8_t vcl_all[VM ? kGenWaves : 1][VM ? 64 * kVRow : 16];
+  __shared__ __attribute__((aligned(16))) uint32_t vrec_all[VM ? kGenWaves : 1][VM ? 64 * 4 : 4];
+  __shared__ __attribute__((aligned(16))) _Float16 pw_all[VM ? kGenWaves : 1][VM ? 64 : 8];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t gw = (int64_t)blockIdx.x * kGenWaves + wave;
@@ -206,16 +214,29 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
 #pragma unroll
   for (int g = 0; g < 4; ++g) qsum[g] = qsum_all[wave][g];
 
-  float acc[kD];                                      // value accumulators, value-code order
+  float acc[VM ? 1 : kD];                             // value accumulators, value-code order
 #pragma unroll
-  for (int i = 0; i < kD; ++i) acc[i] = 0.0f;
+  for (int i = 0; i < (VM ? 1 : kD); ++i) acc[i] = 0.0f;
+  // matrix-core value step: lane (byte pair vn, token pair vkb) of B; the A
+  // rows of head 0 (ha = vn / 4 = 0) carry the weights, the other rows zero
+  float4v_t o[2] = {float4v_t{0.0f, 0.0f, 0.0f, 0.0f}, float4v_t{0.0f, 0.0f, 0.0f, 0.0f}};
+  const int vn = lane & 15, vkb = lane >> 4;
+  uint32_t selA[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const int ve = vn & 3;
+    const uint32_t src = (d >> 1) ? 0x0706u : 0x0504u;
+    const bool on = (vn >> 2) == 0 && (d & 1) == (ve & 1);
+    selA[d] = !on ? 0x0C0C0C0Cu : (ve >> 1) ? ((src << 16) | 0x0C0Cu) : (0x0C0C0000u | src);
+  }
   float zacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   float l = 0.0f, m_run = kNegInf;
 
   const int64_t krow0 = bh * a.kT_cap + a.t_begin - a.skip;   // row 0 of the shifted grid
   const int64_t vrow0 = bh * a.vT_cap + a.t_begin - a.skip;
 
-  auto token = [&](const GenRow<KB> &kr, const GenRow<VB> &vr, bool valid) {
+  auto token = [&](const GenRow<KB> &kr, const GenRow<VB> &vr, bool valid, auto big_c) {
+    constexpr bool BIG = decltype(big_c)::value;
     // The query limbs are re-read from LDS for every token: a query held
     // in registers leaves one wave per SIMD (measured 12-19% slower).
     asm volatile("" ::: "memory");
@@ -242,21 +263,101 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
     if (mt > m_run + kSlack) {                         // wave-uniform
       const float f = __builtin_amdgcn_exp2f(m_run - mt);
 #pragma unroll
-      for (int i = 0; i < kD; ++i) acc[i] *= f;
+      for (int i = 0; i < (VM ? 1 : kD); ++i) acc[i] *= f;
+      o[0] *= f;
+      o[1] *= f;
 #pragma unroll
       for (int g = 0; g < 4; ++g) zacc[g] *= f;
       l *= f;
       m_run = mt;
     }
     const float p = valid ? __builtin_amdgcn_exp2f(s - m_run) : 0.0f;
-    l += p;
+    if constexpr (!VM) {
+      l += p;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const float pv = p * gen_half(vr.s, g);
-      zacc[g] = __builtin_fmaf(p, gen_half(vr.z, g), zacc[g]);
+      for (int g = 0; g < 4; ++g) {
+        const float pv = p * gen_half(vr.s, g);
+        zacc[g] = __builtin_fmaf(p, gen_half(vr.z, g), zacc[g]);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) acc[32 * g + i] = __builtin_fmaf(pv, gen_code<VB>(vr, 32 * g + i), acc[32 * g + i]);
+        for (int i = 0; i < 32; ++i)
+          acc[32 * g + i] = __builtin_fmaf(pv, gen_code<VB>(vr, 32 * g + i), acc[32 * g + i]);
+      }
+    } else {
+      // The grouped-query kernels' value step with one head: weights p~ =
+      // fp16(p) everywhere, B entries code * s - fp16(1.5 s) over the 2-bit
+      // layout (1-bit codes spread to 2-bit fields), the zero-point term
+      // accumulated per token lane.  BIG (a value scale of 2^15 or more
+      // met): entries from s/2, weights doubled.
+      static_assert(VB == 1 || VB == 2, "matrix-core value step: 1- and 2-bit values");
+      constexpr float kB = BIG ? 2.0f : 1.0f;
+      uint8_t *vcl = vcl_all[wave];
+      uint32_t *vrec = vrec_all[wave];
+      _Float16 *pw = pw_all[wave];
+      const _Float16 ph = (_Float16)p;
+      const float pf = (float)ph;
+      l += pf;
+      // vector elements are copied out before the bit casts: hipcc lowers a
+      // bit cast of an element such as vr.s.y as a read of the vector's first
+      // element
+      const uint32_t vs0 = vr.s.x, vs1 = vr.s.y, vz0 = vr.z.x, vz1 = vr.z.y;
+      half2_t s01 = __builtin_bit_cast(half2_t, vs0), s23 = __builtin_bit_cast(half2_t, vs1);
+      if constexpr (BIG) {
+        s01 = s01 * half2_t{(_Float16)0.5f, (_Float16)0.5f};
+        s23 = s23 * half2_t{(_Float16)0.5f, (_Float16)0.5f};
+      }
+      const half2_t n01 = s01 * half2_t{(_Float16)-1.5f, (_Float16)-1.5f};   // -fp16(1.5 s)
+      const half2_t n23 = s23 * half2_t{(_Float16)-1.5f, (_Float16)-1.5f};
+      const half2_t z01 = __builtin_bit_cast(half2_t, vz0), z23 = __builtin_bit_cast(half2_t, vz1);
+      zacc[0] = __builtin_fmaf(pf, __builtin_fmaf(-kB, (float)n01.x, (float)z01.x), zacc[0]);
+      zacc[1] = __builtin_fmaf(pf, __builtin_fmaf(-kB, (float)n01.y, (float)z01.y), zacc[1]);
+      zacc[2] = __builtin_fmaf(pf, __builtin_fmaf(-kB, (float)n23.x, (float)z23.x), zacc[2]);
+      zacc[3] = __builtin_fmaf(pf, __builtin_fmaf(-kB, (float)n23.y, (float)z23.y), zacc[3]);
+      const uint32_t us01 = __builtin_bit_cast(uint32_t, s01), us23 = __builtin_bit_cast(uint32_t, s23);
+      const uint32_t un01 = __builtin_bit_cast(uint32_t, n01), un23 = __builtin_bit_cast(uint32_t, n23);
+      reinterpret_cast<u32x4_t *>(vrec)[lane] =
+          u32x4_t{__builtin_amdgcn_perm(un01, us01, 0x05040100u), __builtin_amdgcn_perm(un01, us01, 0x07060302u),
+                  __builtin_amdgcn_perm(un23, us23, 0x05040100u), __builtin_amdgcn_perm(un23, us23, 0x07060302u)};
+#pragma unroll
+      for (int k = 0; k < VB; ++k) reinterpret_cast<u32x4_t *>(vcl + lane * kVRow)[k] = vr.w[k];
+      pw[lane] = BIG ? ph * (_Float16)2.0f : ph;
+      asm volatile("" ::: "memory");                   // LDS of one wave is ordered; keep the program order
+#pragma unroll
+      for (int tb = 0; tb < 8; ++tb) {
+        const int t0 = 8 * tb + 2 * vkb;
+        // byte pair vn of tokens t0 and t0 + 1 in the 2-bit layout
+        const uint32_t y =
+            VB == 2 ? ((uint32_t)*reinterpret_cast<const uint16_t *>(vcl + t0 * kVRow + 2 * vn) |
+                       ((uint32_t)*reinterpret_cast<const uint16_t *>(vcl + (t0 + 1) * kVRow + 2 * vn) << 16))
+                    : mb_spread_pair(vcl[t0 * kVRow + vn], vcl[(t0 + 1) * kVRow + vn]);
+        const int jv = vn >> 2;
+        const uint32_t sv0 = vrec[t0 * 4 + jv], sv1 = vrec[(t0 + 1) * 4 + jv];
+        const uint32_t P = *reinterpret_cast<const uint32_t *>(pw + t0);
+        v8h_t Aop;
+        {
+          const uint32_t a0 = __builtin_amdgcn_perm(P, P, selA[0]), a1 = __builtin_amdgcn_perm(P, P, selA[1]);
+          const uint32_t a2 = __builtin_amdgcn_perm(P, P, selA[2]), a3 = __builtin_amdgcn_perm(P, P, selA[3]);
+          const half2_t h0 = __builtin_bit_cast(half2_t, a0), h1 = __builtin_bit_cast(half2_t, a1);
+          const half2_t h2 = __builtin_bit_cast(half2_t, a2), h3 = __builtin_bit_cast(half2_t, a3);
+          Aop = half8_t{h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
+        }
+        const uint32_t y02 = y & 0x33333333u, y13 = (y >> 2) & 0x33333333u;
+        o[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aop, mq_bvals<0>(y02, y13, sv0, sv1), o[0], 0, 0, 0);
+        o[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aop, mq_bvals<1>(y02, y13, sv0, sv1), o[1], 0, 0, 0);
+      }
+      asm volatile("" ::: "memory");                   // the next tile's writes come after these reads
     }
+  };
+  // Value scales of 2^15 or more switch the matrix-core value step to the
+  // halved entries for good (the fp32 step needs no switch).
+  bool big = false;
+  auto run = [&](const GenRow<KB> &kr, const GenRow<VB> &vr, bool valid) {
+    if constexpr (VM) {
+      if (!big && __builtin_amdgcn_ballot_w64((((vr.s.x + 0x08000800u) | (vr.s.y + 0x08000800u)) &
+                                               0x80008000u) != 0u))
+        big = true;
+    }
+    if (VM && big) token(kr, vr, valid, std::true_type{});
+    else token(kr, vr, valid, std::false_type{});
   };
 
   const HeadTiles ht(seq_int2(a, b), a.skip, split, S);
@@ -280,7 +381,7 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
       const TileRows tn = full_rows(i + 1);
       const GenRow<KB> kn = gen_load<KB>(a.kcodes, a.kscales, a.kzeros, tn.k + lane);
       const GenRow<VB> vn = gen_load<VB>(a.vcodes, a.vscales, a.vzeros, tn.v + lane);
-      token(kr, vr, true);
+      run(kr, vr, true);
       kr = kn;
       vr = vn;
     }
@@ -297,8 +398,8 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
       const bool valid = lane >= lo && lane < hi;
       const int64_t r = valid ? lane : lo;
       const TileRows tr = tile_rows(a, b, hkv, krow0, vrow0, base);
-      token(gen_load<KB>(a.kcodes, a.kscales, a.kzeros, tr.k + r),
-            gen_load<VB>(a.vcodes, a.vscales, a.vzeros, tr.v + r), valid);
+      run(gen_load<KB>(a.kcodes, a.kscales, a.kzeros, tr.k + r),
+          gen_load<VB>(a.vcodes, a.vscales, a.vzeros, tr.v + r), valid);
     }
   }
 
@@ -306,6 +407,21 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
   l = gen_wave_sum(l);
 #pragma unroll
   for (int g = 0; g < 4; ++g) zacc[g] = gen_wave_sum(zacc[g]);
+  float *dst = a.partials + partial_row(a, wp, hq) * kPartialStride;
+  if constexpr (VM) {
+    // head 0's accumulator rows sit in lanes 0..15: channels 8 vn .. 8 vn + 7
+    if (lane < 16) {
+      const float zl = (vn >> 2) == 0 ? zacc[0] : (vn >> 2) == 1 ? zacc[1] : (vn >> 2) == 2 ? zacc[2] : zacc[3];
+      const float4v_t z4 = {zl, zl, zl, zl};
+      reinterpret_cast<float4v_t *>(dst + 8 * vn)[0] = o[0] + z4;
+      reinterpret_cast<float4v_t *>(dst + 8 * vn)[1] = o[1] + z4;
+    }
+    if (lane == 0) {
+      dst[128] = m_run;
+      dst[129] = l;
+    }
+    return;
+  }
   // reduce-scatter: at the step with lane mask M a lane keeps the half of
   // its values whose index bit matches its lane bit and adds the partner's
   // copy of that half; after six steps lane l holds indices 2l and 2l + 1
@@ -321,7 +437,6 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
       acc[i] = keep + __shfl_xor(send, M, 64);
     }
   }
-  float *dst = a.partials + partial_row(a, wp, hq) * kPartialStride;
   const float zl = (lane >> 4) == 0 ? zacc[0] : (lane >> 4) == 1 ? zacc[1] : (lane >> 4) == 2 ? zacc[2] : zacc[3];
   // the value at index 2l + e (value-code order) belongs to channel chan_of(2l + e)
   dst[chan_of<VB>(2 * lane)] = acc[0] + zl;
@@ -332,11 +447,18 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
   }
 }
 
+// The matrix-core value step prepares every B entry (code * s - fp16(1.5 s))
+// for one head only, so it saves little over the fp32 step: at 1- and 2-bit
+// values it is 0-3% faster, at 4-bit values (two planes, twice the entries
+// and matrix-core work) 10-50% slower.
+template <int VB>
+constexpr bool gen_value_mfma() { return VB != 4; }
+
 hipError_t launch_attn_generic(const AttnArgs &a, int kbits, int vbits, hipStream_t stream) {
   const dim3 grid((unsigned)((a.total_waves + kGenWaves - 1) / kGenWaves)), block(64 * kGenWaves);
 #define KVQ_GEN_CASE(KB, VB)                                                       \
   if (kbits == KB && vbits == VB) {                                                \
-    hipLaunchKernelGGL((kv_quant_decode_attn<KB, VB>), grid, block, 0, stream, a); \
+    hipLaunchKernelGGL((kv_quant_decode_attn<KB, VB, gen_value_mfma<VB>()>), grid, block, 0, stream, a); \
     return hipGetLastError();                                                      \
   }
   KVQ_GEN_CASE(1, 1) KVQ_GEN_CASE(1, 2) KVQ_GEN_CASE(1, 4)

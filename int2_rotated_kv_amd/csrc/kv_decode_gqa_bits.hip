@@ -52,29 +52,6 @@ template <> struct MbKeyWord<1> { typedef uint32_t type; };
 template <> struct MbKeyWord<2> { typedef u32x2_t type; };
 template <> struct MbKeyWord<4> { typedef u32x4_t type; };
 
-// Bits 0..15 of x spread to the even bits of a dword (bit i -> bit 2i).
-__device__ __forceinline__ uint32_t mb_spread16(uint32_t x) {
-  x = (x | (x << 8)) & 0x00FF00FFu;
-  x = (x | (x << 4)) & 0x0F0F0F0Fu;
-  x = (x | (x << 2)) & 0x33333333u;
-  return (x | (x << 1)) & 0x55555555u;
-}
-// Bytes b0, b1 spread to the 2-bit layout: b0 -> bits 0..15, b1 -> bits 16..31.
-__device__ __forceinline__ uint32_t mb_spread_pair(uint32_t b0, uint32_t b1) {
-  uint32_t x = b0 | (b1 << 16);
-  x = (x | (x << 4)) & 0x0F0F0F0Fu;
-  x = (x | (x << 2)) & 0x33333333u;
-  return (x | (x << 1)) & 0x55555555u;
-}
-// Plane p of eight 4-bit codes (nibble c = channel c) in the 2-bit layout:
-// 16 bits, field c = bits (4c + 2p, 4c + 2p + 1) of w.
-__device__ __forceinline__ uint32_t mb_plane16(uint32_t w, int p) {
-  uint32_t x = (w >> (2 * p)) & 0x33333333u;
-  x = (x | (x >> 2)) & 0x0F0F0F0Fu;
-  x = (x | (x >> 4)) & 0x00FF00FFu;
-  return (x | (x >> 8)) & 0x0000FFFFu;
-}
-
 // Channel of score slot k (32 slots per group) for key width KB.
 template <int KB>
 __device__ __forceinline__ constexpr int mb_channel(int k) {

@@ -1,6 +1,8 @@
-// Pieces shared by the grouped-query attention kernels (kv_decode_gqa.hip
-// for 2-bit keys and values, kv_decode_gqa_bits.hip for other widths): the
-// matrix-core operand layouts of the scores and values, and row reductions.
+// Pieces shared by the attention kernels that run on the matrix cores
+// (kv_decode_gqa.hip for 2-bit grouped-query attention, kv_decode_gqa_bits.hip
+// for other widths, kv_decode_generic.hip's value step): the operand layouts
+// of the scores and values, row reductions, and the conversions of 1- and
+// 4-bit codes to the 2-bit layout.
 #pragma once
 
 #include "kv_decode_common.h"
@@ -84,6 +86,29 @@ __device__ __forceinline__ half8_t mq_bvals(uint32_t y02, uint32_t y13, uint32_t
   const half2_t c = __builtin_elementwise_fma(c2, half2_t{s1, s1}, half2_t{n1, n1});
   const half2_t d = __builtin_elementwise_fma(c3, half2_t{s1, s1}, half2_t{n1, n1});
   return half8_t{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+// Bits 0..15 of x spread to the even bits of a dword (bit i -> bit 2i).
+__device__ __forceinline__ uint32_t mb_spread16(uint32_t x) {
+  x = (x | (x << 8)) & 0x00FF00FFu;
+  x = (x | (x << 4)) & 0x0F0F0F0Fu;
+  x = (x | (x << 2)) & 0x33333333u;
+  return (x | (x << 1)) & 0x55555555u;
+}
+// Bytes b0, b1 spread to the 2-bit layout: b0 -> bits 0..15, b1 -> bits 16..31.
+__device__ __forceinline__ uint32_t mb_spread_pair(uint32_t b0, uint32_t b1) {
+  uint32_t x = b0 | (b1 << 16);
+  x = (x | (x << 4)) & 0x0F0F0F0Fu;
+  x = (x | (x << 2)) & 0x33333333u;
+  return (x | (x << 1)) & 0x55555555u;
+}
+// Plane p of eight 4-bit codes (nibble c = channel c) in the 2-bit layout:
+// 16 bits, field c = bits (4c + 2p, 4c + 2p + 1) of w.
+__device__ __forceinline__ uint32_t mb_plane16(uint32_t w, int p) {
+  uint32_t x = (w >> (2 * p)) & 0x33333333u;
+  x = (x | (x >> 2)) & 0x0F0F0F0Fu;
+  x = (x | (x >> 4)) & 0x00FF00FFu;
+  return (x | (x >> 8)) & 0x0000FFFFu;
 }
 
 }  // namespace kvq

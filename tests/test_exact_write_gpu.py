@@ -275,8 +275,8 @@ def _random_cache_np(rng, B, H, T, bits, big_frac):
     return O.pack_codes(codes, bits), scales.astype(np.float16), zeros.astype(np.float16)
 
 
-@pytest.mark.parametrize("kind", ["g1_hadamard", "g1_none", "gqa_dense", "gqa_hadamard", "k4v2", "k4v4_gqa",
-                                  "k2v1_gqa"])
+@pytest.mark.parametrize("kind", ["g1_hadamard", "g1_none", "gqa_dense", "gqa_hadamard", "k4v2", "k1v1", "k4v4",
+                                  "k4v4_gqa", "k2v1_gqa"])
 def test_decode_large_value_scales(kind):
     """Value scales up to 6e4 (any finite fp16 scale is admitted): the G = 1
     kernel's fp16 weights p * s and the grouped-query kernel's fp16 value
@@ -286,7 +286,8 @@ def test_decode_large_value_scales(kind):
     B, Hkv, T = 2, 2, 900
     G = 4 if "gqa" in kind else 1
     Hq = Hkv * G
-    kbits, vbits = {"k4v2": (4, 2), "k4v4_gqa": (4, 4), "k2v1_gqa": (2, 1)}.get(kind, (2, 2))
+    kbits, vbits = {"k4v2": (4, 2), "k1v1": (1, 1), "k4v4": (4, 4), "k4v4_gqa": (4, 4),
+                    "k2v1_gqa": (2, 1)}.get(kind, (2, 2))
     rot = "dense" if "dense" in kind else "none" if kind == "g1_none" else "hadamard"
     kp, ks, kz = _random_cache_np(rng, B, Hkv, T, kbits, 0.0)
     vp, vs, vz = _random_cache_np(rng, B, Hkv, T, vbits, 0.3)
