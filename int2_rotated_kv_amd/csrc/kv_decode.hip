@@ -71,43 +71,54 @@ __device__ __forceinline__ float block_fwht128(float x, float *buf) {
 // independent 16-byte loads in flight:
 //   M[k][c]: thread t owns columns 4 (t%32) .. +3 over rows 16 (t/32) .. +15;
 //   M[c][k]: thread t owns row c = t%128 over columns 64 (t/128) .. +63.
+// The thread's part of M is loaded first (mat_load128, which the callers
+// issue before the loads that x depends on), then block_matvec128 takes it.
 // Partial sums meet in `red` (8 x 128 floats).
 constexpr int kMatThreads = 256;
-__device__ __forceinline__ float block_matvec128(float x, const float *__restrict__ M,
-                                                 bool transpose, float *buf, float *red) {
+struct MatRegs {
+  float4_t m[16];
+};
+__device__ __forceinline__ MatRegs mat_load128(const float *__restrict__ M, bool transpose) {
+  const int t = threadIdx.x;
+  MatRegs r;
+  if (!transpose) {
+    const float4_t *col = reinterpret_cast<const float4_t *>(M + 16 * (t >> 5) * 128) + (t & 31);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r.m[i] = col[32 * i];
+  } else {
+    const float4_t *row = reinterpret_cast<const float4_t *>(M + (t & 127) * 128 + 64 * (t >> 7));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r.m[i] = row[i];
+  }
+  return r;
+}
+__device__ __forceinline__ float block_matvec128(float x, const MatRegs &mr, bool transpose, float *buf,
+                                                 float *red) {
   const int t = threadIdx.x;
   if (t < 128) buf[t] = x;
   __syncthreads();
   if (!transpose) {
     const int cg = t & 31, sl = t >> 5;
-    const float4_t *col = reinterpret_cast<const float4_t *>(M + 16 * sl * 128) + cg;
-    float4_t m[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) m[i] = col[32 * i];
     float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float xk = buf[16 * sl + i];
-      acc.x = __builtin_fmaf(xk, m[i].x, acc.x);
-      acc.y = __builtin_fmaf(xk, m[i].y, acc.y);
-      acc.z = __builtin_fmaf(xk, m[i].z, acc.z);
-      acc.w = __builtin_fmaf(xk, m[i].w, acc.w);
+      acc.x = __builtin_fmaf(xk, mr.m[i].x, acc.x);
+      acc.y = __builtin_fmaf(xk, mr.m[i].y, acc.y);
+      acc.z = __builtin_fmaf(xk, mr.m[i].z, acc.z);
+      acc.w = __builtin_fmaf(xk, mr.m[i].w, acc.w);
     }
     reinterpret_cast<float4_t *>(red + 128 * sl)[cg] = acc;
   } else {
     const int c = t & 127, hh = t >> 7;
-    const float4_t *row = reinterpret_cast<const float4_t *>(M + c * 128 + 64 * hh);
-    float4_t m[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) m[i] = row[i];
     float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float *xb = buf + 64 * hh + 4 * i;
-      acc0 = __builtin_fmaf(xb[0], m[i].x, acc0);
-      acc1 = __builtin_fmaf(xb[1], m[i].y, acc1);
-      acc0 = __builtin_fmaf(xb[2], m[i].z, acc0);
-      acc1 = __builtin_fmaf(xb[3], m[i].w, acc1);
+      acc0 = __builtin_fmaf(xb[0], mr.m[i].x, acc0);
+      acc1 = __builtin_fmaf(xb[1], mr.m[i].y, acc1);
+      acc0 = __builtin_fmaf(xb[2], mr.m[i].z, acc0);
+      acc1 = __builtin_fmaf(xb[3], mr.m[i].w, acc1);
     }
     red[128 * hh + c] = acc0 + acc1;
   }
@@ -151,12 +162,15 @@ __global__ __launch_bounds__(kMatThreads) void kv_prep_query(PrepArgs a) {
   const int hq = (int)(bh % a.Hq);
   const int hkv = hq / (a.Hq / a.Hkv);
   float x = 0.0f;
+  // dense R: the thread's part of R is requested together with q
+  MatRegs Rm;
+  if (a.rot == 2) Rm = mat_load128(a.R + (int64_t)hkv * kD * kD, false);
   // permuted Hadamard: thread c takes channel pi[c] of q (q_pi), then the transform
   const int cin = a.rot == 3 ? (a.perm[(int64_t)hkv * kD + (c & (kD - 1))] & (kD - 1)) : c;
   if (own) x = a.q_f32 ? reinterpret_cast<const float *>(a.q)[bh * kD + cin]
                        : (float)reinterpret_cast<const _Float16 *>(a.q)[bh * kD + cin];
   if (a.rot == 1 || a.rot == 3) x = block_fwht128(x, buf);
-  else if (a.rot == 2) x = block_matvec128(x, a.R + (int64_t)hkv * kD * kD, false, buf, red);
+  else if (a.rot == 2) x = block_matvec128(x, Rm, false, buf, red);
   x *= a.qscale;
 
   // maximum magnitude over the head -> exponent of the fixed point (one step
@@ -743,6 +757,24 @@ __global__ __launch_bounds__(kCombineThreads) void kv_combine_unrotate(CombineAr
   const int rs = c >> 4;                     // token row slot of the fp16 phases
   const int cl = c & 15;                     // channels 8cl .. 8cl+7
 
+  // Loads that no reduction waits for go out first, so that their latency
+  // overlaps the fp16 phase and the first reductions: the thread's part of a
+  // dense R, the (m, l) of split c, and the values of channel c % 128 in the
+  // first 2 kPre splits of parity c / 128.
+  MatRegs Rm;
+  if (a.rot == 2) Rm = mat_load128(a.R + (int64_t)hkv * kD * kD, true);
+  const float *part = a.partials + (first * a.Hq + hq * ns) * kPartialStride;
+  const int ch = c & 127, par = c >> 7;
+  constexpr int kPre = 32;
+  float pv[kPre];
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) {
+    const int64_t i = par + 2 * u;
+    pv[u] = i < ns ? part[i * kPartialStride + ch] : 0.0f;
+  }
+  const float m0 = c < ns ? part[c * kPartialStride + 128] : kNegInf;
+  const float l0 = c < ns ? part[c * kPartialStride + 129] : 0.0f;
+
   // fp16 token scores in the original basis (independent of the partials,
   // so they go first): scale * q . k, log2 units
   float Mf = kNegInf;
@@ -802,12 +834,17 @@ __global__ __launch_bounds__(kCombineThreads) void kv_combine_unrotate(CombineAr
   }
 
   // INT2 partials: M2 = max m_i, weights 2^(m_i - M2)
-  const float *part = a.partials + (first * a.Hq + hq * ns) * kPartialStride;
-  float mloc = kNegInf;
-  for (int64_t i = c; i < ns; i += kCombineThreads) mloc = fmaxf(mloc, part[i * kPartialStride + 128]);
+  float mloc = m0;
+  for (int64_t i = c + kCombineThreads; i < ns; i += kCombineThreads)
+    mloc = fmaxf(mloc, part[i * kPartialStride + 128]);
   const float M2 = block_max(mloc, red);
   float lloc = 0.0f;
-  for (int64_t i = c; i < ns; i += kCombineThreads) {
+  if (c < ns) {
+    const float w0 = (m0 == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(m0 - M2);
+    wsplit[c] = w0;
+    lloc = w0 * l0;
+  }
+  for (int64_t i = c + kCombineThreads; i < ns; i += kCombineThreads) {
     const float mi = part[i * kPartialStride + 128];
     const float wi = (mi == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(mi - M2);
     wsplit[i] = wi;
@@ -815,12 +852,17 @@ __global__ __launch_bounds__(kCombineThreads) void kv_combine_unrotate(CombineAr
   }
   const float L2 = block_sum(lloc, red);     // its barrier also publishes wsplit
   // weighted sum of the partial outputs: thread t takes channel t%128 of the
-  // splits with parity t/128, eight loads in flight
+  // splits with parity t/128; split par + 2u goes to accumulator u % 8, the
+  // first 2 kPre from the early loads, the rest eight loads in flight
   float o = 0.0f;
   {
-    const int ch = c & 127;
     float o8[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    int64_t i = c >> 7;
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      const int64_t i = par + 2 * u;
+      if (i < ns) o8[u & 7] = __builtin_fmaf(wsplit[i], pv[u], o8[u & 7]);
+    }
+    int64_t i = par + 2 * kPre;
     for (; i + 14 < ns; i += 16) {
 #pragma unroll
       for (int u = 0; u < 8; ++u)
@@ -835,7 +877,7 @@ __global__ __launch_bounds__(kCombineThreads) void kv_combine_unrotate(CombineAr
 
   // un-rotate the INT2 part (linear, so once after the merge)
   if (a.rot == 1) o = block_fwht128(o, buf);
-  else if (a.rot == 2) o = block_matvec128(o, a.R + (int64_t)hkv * kD * kD, true, buf, vred);
+  else if (a.rot == 2) o = block_matvec128(o, Rm, true, buf, vred);
   else if (a.rot == 3) {
     // o' R^T = (o' H / sqrt(d)) P^T: transform, then output j goes to channel pi[j]
     o = block_fwht128(o, buf);

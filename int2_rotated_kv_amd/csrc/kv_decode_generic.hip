@@ -10,14 +10,18 @@
 //
 // One wave per (batch, query head, split).  The wave rotates and scales its
 // query itself (none, Hadamard or reordered Hadamard; a dense R comes from
-// the query preparation launch as a fixed point) and keeps it in LDS as
-// a 19-bit fixed point in five 4-bit limbs, laid out in the nibble order of
-// the key codes.  Every 64-token tile gives one token to each lane: the lane
-// scores its token with v_dot8_i32_i4 on the key codes, the wave shares a
-// running maximum, and the lane adds its token's weighted value codes into
-// 128 accumulators of its own.  At the end the 64 lanes' accumulators are
-// summed by a reduce-scatter that leaves two channels in each lane, and the
-// wave writes the same partial (o', m, l) as the INT2 kernels, so the
+// the query preparation launch as a fixed point), as a 19-bit fixed point.
+// Every 64-token tile gives one token to each lane for the softmax, and the
+// wave shares a running maximum.
+//   - Key scores: at 4-bit keys (or 4-bit values) the lane scores its token
+//     with v_dot8_i32_i4 on the key codes against the query in five 4-bit
+//     limbs kept in LDS in the codes' nibble order; at 1- and 2-bit keys
+//     with 1- or 2-bit values they run on the matrix cores (MS below).
+//   - Values: at 1- and 2-bit values the grouped-query kernels' matrix-core
+//     value step with one head (VM); at 4-bit values the lane adds its
+//     token's weighted codes into 128 fp32 accumulators of its own, summed
+//     at the end by a reduce-scatter over the 64 lanes.
+// The wave writes the same partial (o', m, l) as the INT2 kernels, so the
 // combine and un-rotation are shared.
 #include <type_traits>
 
@@ -108,9 +112,48 @@ __device__ __forceinline__ float gen_half(const u32x2_t &v, int g) {
   return half_bits_to_float((uint16_t)((g & 1) ? (w >> 16) : (w & 0xFFFFu)));
 }
 
+// Matrix-core key scores (MS): the 4 x 16 tokens of a tile as four B
+// blocks of v_mfma_scale_f32_16x16x128_f8f6f4, lane (token 16 k + lane % 16,
+// group lane / 16) of block k, with the codes as fp4 nibbles 0b0..c (value
+// c / 2).  Score slot k (32 per group) holds the channel ms_channel(k):
+// 1-bit codes as four shifted copies of the group's dword (copy d keeps
+// bits 4 j + d in nibble j), 2-bit codes as mq_unpack, 4-bit codes per
+// 2-bit plane in place.
+template <int KB>
+__host__ __device__ __forceinline__ constexpr int ms_channel(int k) {
+  return KB == 4 ? k : KB == 2 ? mq_channel(k) : 32 * (k >> 5) + 4 * (k & 7) + ((k >> 3) & 3);
+}
+
+// A tile's keys for the matrix-core scores: the code words of block k and
+// the scale / zero of the lane's own token.
+template <int KB>
+struct MsKeys {
+  typename MbKeyWord<KB>::type kc[4];
+  u32x2_t s, z;
+};
+
+// Rows r0 + t of a tile; tokens outside [lo, hi) read row r0 + lo.
+template <int KB>
+__device__ __forceinline__ MsKeys<KB> ms_load(const AttnArgs &a, int64_t r0, int lo, int hi) {
+  constexpr int kRow = 16 * KB;
+  typedef typename MbKeyWord<KB>::type KWord;
+  const int lane = threadIdx.x & 63, tk = lane & 15, kg = lane >> 4;
+  MsKeys<KB> r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int t = 16 * k + tk;
+    const int64_t row = r0 + (t >= lo && t < hi ? t : lo);
+    r.kc[k] = *reinterpret_cast<const KWord *>(a.kcodes + row * kRow + (kRow / 4) * kg);
+  }
+  const int64_t row = r0 + (lane >= lo && lane < hi ? lane : lo);
+  r.s = *reinterpret_cast<const u32x2_t *>(a.kscales + row * kNGroups);
+  r.z = *reinterpret_cast<const u32x2_t *>(a.kzeros + row * kNGroups);
+  return r;
+}
+
 // grid: ceil(total_waves / 4) blocks of 4 waves; wave index as in
 // wave_place with one wave per query head (`per` = G).
-template <int KB, int VB, bool VM>
+template <int KB, int VB, bool VM, bool MS>
 __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs a) {
   // the query as a 19-bit fixed point in five signed 4-bit limbs: limb L,
   // nibble 8u + h at the position of the key nibble it multiplies (nib_pos);
@@ -118,6 +161,7 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
   __shared__ __attribute__((aligned(16))) uint32_t ql_all[kGenWaves][5][16];
   __shared__ uint8_t qn_all[kGenWaves][5][kD];
   __shared__ float qsum_all[kGenWaves][4];
+  __shared__ int32_t qi_all[MS ? kGenWaves : 1][MS ? kD : 1];   // the fixed point (MS)
   // value step on the matrix cores: the tile's value rows, per-token
   // (s, -fp16(1.5 s)) of each group, and the fp16 weights
   constexpr int kVRow = 16 * VB;
@@ -191,13 +235,18 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
     }
     float gs = (float)q0i + (float)q1i;               // group g = lane / 16, exact
     uint8_t(*qn)[kD] = qn_all[wave];
+    if constexpr (MS) {
+      qi_all[wave][2 * lane] = q0i;
+      qi_all[wave][2 * lane + 1] = q1i;
+    } else {
 #pragma unroll
-    for (int L = 0; L < 5; ++L) {                     // balanced base-16 digits
-      const int d0 = ((q0i + 8) & 15) - 8, d1 = ((q1i + 8) & 15) - 8;
-      q0i = (q0i - d0) >> 4;
-      q1i = (q1i - d1) >> 4;
-      qn[L][nib_pos<KB>(2 * lane)] = (uint8_t)(d0 & 15);
-      qn[L][nib_pos<KB>(2 * lane + 1)] = (uint8_t)(d1 & 15);
+      for (int L = 0; L < 5; ++L) {                   // balanced base-16 digits
+        const int d0 = ((q0i + 8) & 15) - 8, d1 = ((q1i + 8) & 15) - 8;
+        q0i = (q0i - d0) >> 4;
+        q1i = (q1i - d1) >> 4;
+        qn[L][nib_pos<KB>(2 * lane)] = (uint8_t)(d0 & 15);
+        qn[L][nib_pos<KB>(2 * lane + 1)] = (uint8_t)(d1 & 15);
+      }
     }
     gs += quad_swap<kQuadXor1>(gs);
     gs += quad_swap<kQuadXor2>(gs);
@@ -205,14 +254,49 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
     gs += row_ror<8>(gs);
     if ((lane & 15) == 0) qsum_all[wave][lane >> 4] = gs;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's LDS writes are done
-    uint8_t *lb = reinterpret_cast<uint8_t *>(ql_all[wave]);
+    if constexpr (!MS) {
+      uint8_t *lb = reinterpret_cast<uint8_t *>(ql_all[wave]);
 #pragma unroll
-    for (int L = 0; L < 5; ++L) lb[64 * L + lane] = (uint8_t)(qn[L][2 * lane] | (qn[L][2 * lane + 1] << 4));
+      for (int L = 0; L < 5; ++L) lb[64 * L + lane] = (uint8_t)(qn[L][2 * lane] | (qn[L][2 * lane + 1] << 4));
+    }
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   float qsum[4];                                      // sum of qi over each group
 #pragma unroll
   for (int g = 0; g < 4; ++g) qsum[g] = qsum_all[wave][g];
+  // MS: fp8 digit operands of the fixed point, as in the grouped-query
+  // kernels with the one head in all four row blocks: row (block j, group
+  // ja) carries the digits of group ja's channels.  A lane keeps the rows
+  // of block lane / 16, which the scores of tokens 16 j .. 16 j + 15 use.
+  v8i_t A[MS ? 4 : 1];
+  if constexpr (MS) {
+    const int32_t *qi = qi_all[wave];
+    const int ja = lane & 3, kba = lane >> 4;
+    // bytes 0..15: slots 16 kba + i (group kba / 2); bytes 16..31: slots
+    // 64 + 16 kba + i (group 2 + kba / 2); only the half in group ja is nonzero
+    const bool lo_on = (kba >> 1) == ja, hi_on = 2 + (kba >> 1) == ja;
+    const int kbase = hi_on ? 64 + 16 * kba : 16 * kba;
+    int q16[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) q16[i] = (lo_on || hi_on) ? qi[ms_channel<KB>(kbase + i)] : 0;
+#pragma unroll
+    for (int Ld = 0; Ld < 4; ++Ld) {
+      int dw[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        int v = __builtin_amdgcn_cvt_pk_fp8_f32((float)mq_digit(q16[4 * w], Ld),
+                                                (float)mq_digit(q16[4 * w + 1], Ld), 0, false);
+        v = __builtin_amdgcn_cvt_pk_fp8_f32((float)mq_digit(q16[4 * w + 2], Ld),
+                                            (float)mq_digit(q16[4 * w + 3], Ld), v, true);
+        dw[w] = v;
+      }
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        A[Ld][w] = lo_on ? dw[w] : 0;
+        A[Ld][4 + w] = hi_on ? dw[w] : 0;
+      }
+    }
+  }
 
   float acc[VM ? 1 : kD];                             // value accumulators, value-code order
 #pragma unroll
@@ -235,27 +319,75 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
   const int64_t krow0 = bh * a.kT_cap + a.t_begin - a.skip;   // row 0 of the shifted grid
   const int64_t vrow0 = bh * a.vT_cap + a.t_begin - a.skip;
 
-  auto token = [&](const GenRow<KB> &kr, const GenRow<VB> &vr, bool valid, auto big_c) {
+  auto token = [&](const auto &kr, const GenRow<VB> &vr, bool valid, auto big_c) {
     constexpr bool BIG = decltype(big_c)::value;
-    // The query limbs are re-read from LDS for every token: a query held
-    // in registers leaves one wave per SIMD (measured 12-19% slower).
-    asm volatile("" ::: "memory");
-    // per group: sum qi c from v_dot8_i32_i4, one accumulator per limb
-    // (4-bit codes read as c - 8, so + 8 sum qi restores sum qi c)
     float s = 0.0f;
-    const uint32_t *ql = &ql_all[wave][0][0];
+    if constexpr (MS) {
+      // per block k: (1/2) sum qi c of each group for token 16 k + lane % 16
+      // in every row block; the lane keeps block lane / 16's, its own token's
+      float dsel[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      int acc5[5] = {0, 0, 0, 0, 0};
+      for (int k = 0; k < 4; ++k) {
+        float4v_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (KB == 4) {
+          const u32x4_t w = kr.kc[k];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int kn = (int)key_nibbles<KB>(kr, 4 * g + e);
+          for (int p = 0; p < 2; ++p) {                // code = lo + 4 hi: the hi plane's B scale is 2^2
+            v8i_t Bop;
+            Bop[0] = (int)((w.x >> (2 * p)) & 0x33333333u);
+            Bop[1] = (int)((w.y >> (2 * p)) & 0x33333333u);
+            Bop[2] = (int)((w.z >> (2 * p)) & 0x33333333u);
+            Bop[3] = (int)((w.w >> (2 * p)) & 0x33333333u);
+            Bop[4] = 0; Bop[5] = 0; Bop[6] = 0; Bop[7] = 0;
 #pragma unroll
-        for (int L = 0; L < 5; ++L) acc5[L] = __builtin_amdgcn_sdot8((int)ql[16 * L + 4 * g + e], kn, acc5[L], false);
+            for (int Ld = 0; Ld < 4; ++Ld)
+              d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[Ld], Bop, d, 0, 4, 0, mq_scale(Ld), 0,
+                                                                   127 + 2 * p);
+          }
+        } else {
+          v8i_t Bop;
+          if constexpr (KB == 2) {
+            Bop = mq_unpack(kr.kc[k]);
+          } else {
+            const uint32_t w = kr.kc[k];
+            Bop[0] = (int)(w & 0x11111111u);
+            Bop[1] = (int)((w >> 1) & 0x11111111u);
+            Bop[2] = (int)((w >> 2) & 0x11111111u);
+            Bop[3] = (int)((w >> 3) & 0x11111111u);
+            Bop[4] = 0; Bop[5] = 0; Bop[6] = 0; Bop[7] = 0;
+          }
+#pragma unroll
+          for (int Ld = 0; Ld < 4; ++Ld)
+            d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[Ld], Bop, d, 0, 4, 0, mq_scale(Ld), 0, 127);
+        }
+        const bool mine = (lane >> 4) == k;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) dsel[g] = mine ? d[g] : dsel[g];
       }
-      const int v = acc5[0] + (acc5[1] << 4) + (acc5[2] << 8) + (acc5[3] << 12) + (acc5[4] << 16);
-      const float dot = KB == 4 ? (float)v + 8.0f * qsum[g] : (float)v;   // exact in fp32 (< 2^24)
-      s = __builtin_fmaf(gen_half(kr.s, g), dot, __builtin_fmaf(gen_half(kr.z, g), qsum[g], s));
+#pragma unroll
+      for (int g = 0; g < 4; ++g)                      // 2 dsel = sum qi c, exact
+        s = __builtin_fmaf(gen_half(kr.s, g), 2.0f * dsel[g], __builtin_fmaf(gen_half(kr.z, g), qsum[g], s));
+    } else {
+      // The query limbs are re-read from LDS for every token: a query held
+      // in registers leaves one wave per SIMD (measured 12-19% slower).
+      asm volatile("" ::: "memory");
+      // per group: sum qi c from v_dot8_i32_i4, one accumulator per limb
+      // (4-bit codes read as c - 8, so + 8 sum qi restores sum qi c)
+      const uint32_t *ql = &ql_all[wave][0][0];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        int acc5[5] = {0, 0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int kn = (int)key_nibbles<KB>(kr, 4 * g + e);
+#pragma unroll
+          for (int L = 0; L < 5; ++L)
+            acc5[L] = __builtin_amdgcn_sdot8((int)ql[16 * L + 4 * g + e], kn, acc5[L], false);
+        }
+        const int v = acc5[0] + (acc5[1] << 4) + (acc5[2] << 8) + (acc5[3] << 12) + (acc5[4] << 16);
+        const float dot = KB == 4 ? (float)v + 8.0f * qsum[g] : (float)v;   // exact in fp32 (< 2^24)
+        s = __builtin_fmaf(gen_half(kr.s, g), dot, __builtin_fmaf(gen_half(kr.z, g), qsum[g], s));
+      }
     }
     s *= qstep;
     s = valid ? s : kNegInf;
@@ -350,7 +482,7 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
   // Value scales of 2^15 or more switch the matrix-core value step to the
   // halved entries for good (the fp32 step needs no switch).
   bool big = false;
-  auto run = [&](const GenRow<KB> &kr, const GenRow<VB> &vr, bool valid) {
+  auto run = [&](const auto &kr, const GenRow<VB> &vr, bool valid) {
     if constexpr (VM) {
       if (!big && __builtin_amdgcn_ballot_w64((((vr.s.x + 0x08000800u) | (vr.s.y + 0x08000800u)) &
                                                0x80008000u) != 0u))
@@ -372,18 +504,55 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
       const int64_t r = pages.row(a, b, hkv, ht, split, S, i);
       return TileRows{r, r};
     };
-    const TileRows t0 = full_rows(0);
-    GenRow<KB> kr = gen_load<KB>(a.kcodes, a.kscales, a.kzeros, t0.k + lane);
-    GenRow<VB> vr = gen_load<VB>(a.vcodes, a.vscales, a.vzeros, t0.v + lane);
-    for (int64_t i = 0; i < ht.mine; ++i) {
-      // the next tile's rows are loaded while this one is computed (the
-      // last prefetch re-reads the wave's last tile)
-      const TileRows tn = full_rows(i + 1);
-      const GenRow<KB> kn = gen_load<KB>(a.kcodes, a.kscales, a.kzeros, tn.k + lane);
-      const GenRow<VB> vn = gen_load<VB>(a.vcodes, a.vscales, a.vzeros, tn.v + lane);
-      run(kr, vr, true);
-      kr = kn;
-      vr = vn;
+    auto lk = [&](const TileRows &t) {
+      if constexpr (MS) return ms_load<KB>(a, t.k, 0, 64);
+      else return gen_load<KB>(a.kcodes, a.kscales, a.kzeros, t.k + lane);
+    };
+    auto lv = [&](const TileRows &t) { return gen_load<VB>(a.vcodes, a.vscales, a.vzeros, t.v + lane); };
+    if constexpr (MS) {
+      // narrow rows leave registers for a three-deep pipeline: while tile i
+      // is computed the loads of tiles i + 1 and i + 2 are in flight (2-5%
+      // faster than one tile ahead); prefetches past the wave's last tile
+      // re-read it
+      TileRows t = full_rows(0);
+      auto k0 = lk(t);
+      auto v0 = lv(t);
+      t = full_rows(1);
+      auto k1 = lk(t);
+      auto v1 = lv(t);
+      decltype(k0) k2;
+      decltype(v0) v2;
+      int64_t i = 0;
+      for (; i + 3 <= ht.mine; i += 3) {
+        t = full_rows(i + 2);
+        k2 = lk(t);
+        v2 = lv(t);
+        run(k0, v0, true);
+        t = full_rows(i + 3);
+        k0 = lk(t);
+        v0 = lv(t);
+        run(k1, v1, true);
+        t = full_rows(i + 4);
+        k1 = lk(t);
+        v1 = lv(t);
+        run(k2, v2, true);
+      }
+      if (i < ht.mine) run(k0, v0, true);
+      if (i + 1 < ht.mine) run(k1, v1, true);
+    } else {
+      const TileRows t0 = full_rows(0);
+      auto kr = lk(t0);
+      GenRow<VB> vr = lv(t0);
+      for (int64_t i = 0; i < ht.mine; ++i) {
+        // the next tile's rows are loaded while this one is computed (the
+        // last prefetch re-reads the wave's last tile)
+        const TileRows tn = full_rows(i + 1);
+        const auto kn = lk(tn);
+        const GenRow<VB> vn = lv(tn);
+        run(kr, vr, true);
+        kr = kn;
+        vr = vn;
+      }
     }
   }
   {
@@ -398,8 +567,9 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
       const bool valid = lane >= lo && lane < hi;
       const int64_t r = valid ? lane : lo;
       const TileRows tr = tile_rows(a, b, hkv, krow0, vrow0, base);
-      run(gen_load<KB>(a.kcodes, a.kscales, a.kzeros, tr.k + r),
-          gen_load<VB>(a.vcodes, a.vscales, a.vzeros, tr.v + r), valid);
+      const GenRow<VB> vr = gen_load<VB>(a.vcodes, a.vscales, a.vzeros, tr.v + r);
+      if constexpr (MS) run(ms_load<KB>(a, tr.k, (int)lo, (int)hi), vr, valid);
+      else run(gen_load<KB>(a.kcodes, a.kscales, a.kzeros, tr.k + r), vr, valid);
     }
   }
 
@@ -453,13 +623,21 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
 // and matrix-core work) 10-50% slower.
 template <int VB>
 constexpr bool gen_value_mfma() { return VB != 4; }
+// The matrix-core key scores (MS) replace about 90 vector operations per
+// tile by 16 matrix-core products; measured 2-3% faster at 1- and 2-bit
+// keys with 1- or 2-bit values.  With 4-bit values (the fp32 value step's
+// 128 accumulators) the kernel would pass 256 registers and run one wave
+// per SIMD (K1 V4 6% slower), and 4-bit keys are bandwidth-bound already.
+template <int KB, int VB>
+constexpr bool gen_score_mfma() { return KB != 4 && VB != 4; }
 
 hipError_t launch_attn_generic(const AttnArgs &a, int kbits, int vbits, hipStream_t stream) {
   const dim3 grid((unsigned)((a.total_waves + kGenWaves - 1) / kGenWaves)), block(64 * kGenWaves);
-#define KVQ_GEN_CASE(KB, VB)                                                       \
-  if (kbits == KB && vbits == VB) {                                                \
-    hipLaunchKernelGGL((kv_quant_decode_attn<KB, VB, gen_value_mfma<VB>()>), grid, block, 0, stream, a); \
-    return hipGetLastError();                                                      \
+#define KVQ_GEN_CASE(KB, VB)                                                                  \
+  if (kbits == KB && vbits == VB) {                                                           \
+    constexpr bool kVm = gen_value_mfma<VB>(), kMs = gen_score_mfma<KB, VB>();                \
+    hipLaunchKernelGGL((kv_quant_decode_attn<KB, VB, kVm, kMs>), grid, block, 0, stream, a);  \
+    return hipGetLastError();                                                                 \
   }
   KVQ_GEN_CASE(1, 1) KVQ_GEN_CASE(1, 2) KVQ_GEN_CASE(1, 4)
   KVQ_GEN_CASE(2, 1) KVQ_GEN_CASE(2, 2) KVQ_GEN_CASE(2, 4)

@@ -46,12 +46,6 @@ struct MbLds {
   static constexpr int kDwords = kPwOff + kMqHeads * 64 / 2;
 };
 
-// The key bytes of one group for one token: 4, 8 or 16 bytes.
-template <int KB> struct MbKeyWord;
-template <> struct MbKeyWord<1> { typedef uint32_t type; };
-template <> struct MbKeyWord<2> { typedef u32x2_t type; };
-template <> struct MbKeyWord<4> { typedef u32x4_t type; };
-
 // Channel of score slot k (32 slots per group) for key width KB.
 template <int KB>
 __device__ __forceinline__ constexpr int mb_channel(int k) {

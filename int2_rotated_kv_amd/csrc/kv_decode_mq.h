@@ -35,6 +35,12 @@ __device__ __forceinline__ v8i_t mq_unpack(u32x2_t c) {
   return b;
 }
 
+// The key bytes of one group for one token: 4, 8 or 16 bytes.
+template <int KB> struct MbKeyWord;
+template <> struct MbKeyWord<1> { typedef uint32_t type; };
+template <> struct MbKeyWord<2> { typedef u32x2_t type; };
+template <> struct MbKeyWord<4> { typedef u32x4_t type; };
+
 // Balanced base-32 digit L (0 = most significant) of |q| < 2^19.
 __device__ __forceinline__ int mq_digit(int q, int L) {
   int r = q, d = 0;
