@@ -13,10 +13,10 @@
 // the query preparation launch as a fixed point), as a 19-bit fixed point.
 // Every 64-token tile gives one token to each lane for the softmax, and the
 // wave shares a running maximum.
-//   - Key scores: at 4-bit keys (or 4-bit values) the lane scores its token
-//     with v_dot8_i32_i4 on the key codes against the query in five 4-bit
-//     limbs kept in LDS in the codes' nibble order; at 1- and 2-bit keys
-//     with 1- or 2-bit values they run on the matrix cores (MS below).
+//   - Key scores run on the matrix cores: the fixed point's four balanced
+//     base-32 digits as one fp8 operand (a digit per row block, its weight
+//     in the E8M0 A scale) against the codes as fp4, then a sum across the
+//     row blocks that leaves each lane its own token's group sums.
 //   - Values: at 1- and 2-bit values the grouped-query kernels' matrix-core
 //     value step with one head (VM); at 4-bit values the lane adds its
 //     token's weighted codes into 128 fp32 accumulators of its own, summed
@@ -77,26 +77,6 @@ __device__ __forceinline__ GenRow<BITS> gen_load(const uint8_t *codes, const uin
   return r;
 }
 
-// Key codes as signed nibbles for v_dot8_i32_i4.  Limb dword u (0..15) of a
-// b-bit row is code dword j = u / (4/b), shifted right by b (u mod 4/b) and
-// masked to b bits per nibble: nibble h then holds the code of channel
-// (32/b) j + (4/b) h + (u mod 4/b).  4-bit codes are flipped in their top bit,
-// so that the signed nibble reads c - 8.
-template <int BITS>
-__host__ __device__ __forceinline__ constexpr int nib_pos(int c) {   // 8 u + h of channel c
-  constexpr int CPW = 32 / BITS, SUB = 4 / BITS;
-  return 8 * ((c / CPW) * SUB + (c % CPW) % SUB) + (c % CPW) / SUB;
-}
-template <int BITS>
-__device__ __forceinline__ uint32_t key_nibbles(const GenRow<BITS> &r, int u) {
-  constexpr int SUB = 4 / BITS;
-  const int j = u / SUB;
-  const uint32_t w = r.w[j >> 2][j & 3];
-  if constexpr (BITS == 4) return w ^ 0x88888888u;
-  else if constexpr (BITS == 2) return (w >> (2 * (u % SUB))) & 0x33333333u;
-  else return (w >> (u % SUB)) & 0x11111111u;
-}
-
 // Code of index i (code order) of a row held as BITS x 4 dwords.
 template <int BITS>
 __device__ __forceinline__ float gen_code(const GenRow<BITS> &r, int i) {
@@ -112,7 +92,7 @@ __device__ __forceinline__ float gen_half(const u32x2_t &v, int g) {
   return half_bits_to_float((uint16_t)((g & 1) ? (w >> 16) : (w & 0xFFFFu)));
 }
 
-// Matrix-core key scores (MS): the 4 x 16 tokens of a tile as four B
+// Matrix-core key scores: the 4 x 16 tokens of a tile as four B
 // blocks of v_mfma_scale_f32_16x16x128_f8f6f4, lane (token 16 k + lane % 16,
 // group lane / 16) of block k, with the codes as fp4 nibbles 0b0..c (value
 // c / 2).  Score slot k (32 per group) holds the channel ms_channel(k):
@@ -122,6 +102,20 @@ __device__ __forceinline__ float gen_half(const u32x2_t &v, int g) {
 template <int KB>
 __host__ __device__ __forceinline__ constexpr int ms_channel(int k) {
   return KB == 4 ? k : KB == 2 ? mq_channel(k) : 32 * (k >> 5) + 4 * (k & 7) + ((k >> 3) & 3);
+}
+
+// x_k (k = 0..3) hold, in lane (row block j, n), the part of row j of
+// block k.  Returns in lane (r, n) the sum over j of block r's rows: row
+// blocks 2,3 of x0 / x1 trade places with rows 0,1 of x2 / x3 and the
+// halves add (rows j and j + 2 meet), then the odd rows of the first sum
+// trade with the even rows of the second and add (rows j and j + 1 meet).
+__device__ __forceinline__ float ms_digit_sum(float x0, float x1, float x2, float x3) {
+  const auto a = __builtin_amdgcn_permlane32_swap(float_as_bits(x0), float_as_bits(x2), false, false);
+  const float u02 = bits_as_float(a[0]) + bits_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(float_as_bits(x1), float_as_bits(x3), false, false);
+  const float u13 = bits_as_float(b[0]) + bits_as_float(b[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(float_as_bits(u02), float_as_bits(u13), false, false);
+  return bits_as_float(c[0]) + bits_as_float(c[1]);
 }
 
 // A tile's keys for the matrix-core scores: the code words of block k and
@@ -153,15 +147,11 @@ __device__ __forceinline__ MsKeys<KB> ms_load(const AttnArgs &a, int64_t r0, int
 
 // grid: ceil(total_waves / 4) blocks of 4 waves; wave index as in
 // wave_place with one wave per query head (`per` = G).
-template <int KB, int VB, bool VM, bool MS>
+template <int KB, int VB, bool VM>
 __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs a) {
-  // the query as a 19-bit fixed point in five signed 4-bit limbs: limb L,
-  // nibble 8u + h at the position of the key nibble it multiplies (nib_pos);
-  // nibbles staged one per byte first, then packed; group sums of qi last
-  __shared__ __attribute__((aligned(16))) uint32_t ql_all[kGenWaves][5][16];
-  __shared__ uint8_t qn_all[kGenWaves][5][kD];
+  // the query as a 19-bit fixed point, and its group sums
+  __shared__ int32_t qi_all[kGenWaves][kD];
   __shared__ float qsum_all[kGenWaves][4];
-  __shared__ int32_t qi_all[MS ? kGenWaves : 1][MS ? kD : 1];   // the fixed point (MS)
   // value step on the matrix cores: the tile's value rows, per-token
   // (s, -fp16(1.5 s)) of each group, and the fp16 weights
   constexpr int kVRow = 16 * VB;
@@ -223,9 +213,9 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
     x0 *= scale;
     x1 *= scale;
     // qi = rint(q' 2^E) with |qi| < 2^18 for the head's largest |q'|; the
-    // scores are then exact integer dot products of qi with the codes, and
-    // the fixed-point rounding (below 2^-18 of the largest |q'|) is their
-    // only approximation
+    // group sums of qi c are integers, exact in fp32 below 2^24 and rounded
+    // once above (relative 2^-24), so the fixed-point rounding (below 2^-18
+    // of the largest |q'|) is the scores' main approximation
     const float amax = gen_wave_max(fmaxf(fabsf(x0), fabsf(x1)));
     // amax = m 2^e with m in [0.5, 1): E = 18 - e puts amax 2^E in [2^17, 2^18)
     const int E = amax > 0.0f ? 18 - __builtin_amdgcn_frexp_expf(amax) : 0;
@@ -234,67 +224,48 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
     q1i = (int)__builtin_rintf(__builtin_amdgcn_ldexpf(x1, E));
     }
     float gs = (float)q0i + (float)q1i;               // group g = lane / 16, exact
-    uint8_t(*qn)[kD] = qn_all[wave];
-    if constexpr (MS) {
-      qi_all[wave][2 * lane] = q0i;
-      qi_all[wave][2 * lane + 1] = q1i;
-    } else {
-#pragma unroll
-      for (int L = 0; L < 5; ++L) {                   // balanced base-16 digits
-        const int d0 = ((q0i + 8) & 15) - 8, d1 = ((q1i + 8) & 15) - 8;
-        q0i = (q0i - d0) >> 4;
-        q1i = (q1i - d1) >> 4;
-        qn[L][nib_pos<KB>(2 * lane)] = (uint8_t)(d0 & 15);
-        qn[L][nib_pos<KB>(2 * lane + 1)] = (uint8_t)(d1 & 15);
-      }
-    }
+    qi_all[wave][2 * lane] = q0i;
+    qi_all[wave][2 * lane + 1] = q1i;
     gs += quad_swap<kQuadXor1>(gs);
     gs += quad_swap<kQuadXor2>(gs);
     gs += row_ror<4>(gs);
     gs += row_ror<8>(gs);
     if ((lane & 15) == 0) qsum_all[wave][lane >> 4] = gs;
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's LDS writes are done
-    if constexpr (!MS) {
-      uint8_t *lb = reinterpret_cast<uint8_t *>(ql_all[wave]);
-#pragma unroll
-      for (int L = 0; L < 5; ++L) lb[64 * L + lane] = (uint8_t)(qn[L][2 * lane] | (qn[L][2 * lane + 1] << 4));
-    }
   }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's LDS writes are done
   float qsum[4];                                      // sum of qi over each group
 #pragma unroll
   for (int g = 0; g < 4; ++g) qsum[g] = qsum_all[wave][g];
-  // MS: fp8 digit operands of the fixed point, as in the grouped-query
-  // kernels with the one head in all four row blocks: row (block j, group
-  // ja) carries the digits of group ja's channels.  A lane keeps the rows
-  // of block lane / 16, which the scores of tokens 16 j .. 16 j + 15 use.
-  v8i_t A[MS ? 4 : 1];
-  if constexpr (MS) {
+  // Key scores: one fp8 operand for the four digits of the fixed point.  A row
+  // (block jr, group ja) holds digit L(jr) of group ja's channels (zero in
+  // the other groups' slots), and the lane's E8M0 A scale is that digit's
+  // weight 2^(5 (3 - L)).  Rows 0 and 2 carry digits 0 and 1, rows 1 and 3
+  // digits 2 and 3, so that the first pairwise sums across the row blocks
+  // (below) add digits of neighbouring weight and stay exact.
+  v8i_t Aq;
+  int sa;
+  {
     const int32_t *qi = qi_all[wave];
-    const int ja = lane & 3, kba = lane >> 4;
+    const int ja = lane & 3, jr = (lane & 15) >> 2, kba = lane >> 4;
+    const int Ld = (jr >> 1) | ((jr & 1) << 1);
+    sa = mq_scale(Ld);
     // bytes 0..15: slots 16 kba + i (group kba / 2); bytes 16..31: slots
     // 64 + 16 kba + i (group 2 + kba / 2); only the half in group ja is nonzero
     const bool lo_on = (kba >> 1) == ja, hi_on = 2 + (kba >> 1) == ja;
     const int kbase = hi_on ? 64 + 16 * kba : 16 * kba;
-    int q16[16];
+    int dw[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) q16[i] = (lo_on || hi_on) ? qi[ms_channel<KB>(kbase + i)] : 0;
+    for (int w = 0; w < 4; ++w) {
+      int d4[4];
 #pragma unroll
-    for (int Ld = 0; Ld < 4; ++Ld) {
-      int dw[4];
+      for (int e = 0; e < 4; ++e) d4[e] = (lo_on || hi_on) ? mq_digit(qi[ms_channel<KB>(kbase + 4 * w + e)], Ld) : 0;
+      int v = __builtin_amdgcn_cvt_pk_fp8_f32((float)d4[0], (float)d4[1], 0, false);
+      dw[w] = __builtin_amdgcn_cvt_pk_fp8_f32((float)d4[2], (float)d4[3], v, true);
+    }
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        int v = __builtin_amdgcn_cvt_pk_fp8_f32((float)mq_digit(q16[4 * w], Ld),
-                                                (float)mq_digit(q16[4 * w + 1], Ld), 0, false);
-        v = __builtin_amdgcn_cvt_pk_fp8_f32((float)mq_digit(q16[4 * w + 2], Ld),
-                                            (float)mq_digit(q16[4 * w + 3], Ld), v, true);
-        dw[w] = v;
-      }
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        A[Ld][w] = lo_on ? dw[w] : 0;
-        A[Ld][4 + w] = hi_on ? dw[w] : 0;
-      }
+    for (int w = 0; w < 4; ++w) {
+      Aq[w] = lo_on ? dw[w] : 0;
+      Aq[4 + w] = hi_on ? dw[w] : 0;
     }
   }
 
@@ -322,13 +293,13 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
   auto token = [&](const auto &kr, const GenRow<VB> &vr, bool valid, auto big_c) {
     constexpr bool BIG = decltype(big_c)::value;
     float s = 0.0f;
-    if constexpr (MS) {
-      // per block k: (1/2) sum qi c of each group for token 16 k + lane % 16
-      // in every row block; the lane keeps block lane / 16's, its own token's
-      float dsel[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    {
+      // block k (tokens 16 k .. 16 k + 15): lane (row block jr, token n) gets
+      // digit L(jr)'s part of (1/2) sum qi c for each group of token 16 k + n
+      float4v_t d[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        float4v_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+        d[k] = float4v_t{0.0f, 0.0f, 0.0f, 0.0f};
         if constexpr (KB == 4) {
           const u32x4_t w = kr.kc[k];
 #pragma unroll
@@ -339,10 +310,7 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
             Bop[2] = (int)((w.z >> (2 * p)) & 0x33333333u);
             Bop[3] = (int)((w.w >> (2 * p)) & 0x33333333u);
             Bop[4] = 0; Bop[5] = 0; Bop[6] = 0; Bop[7] = 0;
-#pragma unroll
-            for (int Ld = 0; Ld < 4; ++Ld)
-              d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[Ld], Bop, d, 0, 4, 0, mq_scale(Ld), 0,
-                                                                   127 + 2 * p);
+            d[k] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Aq, Bop, d[k], 0, 4, 0, sa, 0, 127 + 2 * p);
           }
         } else {
           v8i_t Bop;
@@ -356,36 +324,14 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
             Bop[3] = (int)((w >> 3) & 0x11111111u);
             Bop[4] = 0; Bop[5] = 0; Bop[6] = 0; Bop[7] = 0;
           }
-#pragma unroll
-          for (int Ld = 0; Ld < 4; ++Ld)
-            d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[Ld], Bop, d, 0, 4, 0, mq_scale(Ld), 0, 127);
+          d[k] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Aq, Bop, d[k], 0, 4, 0, sa, 0, 127);
         }
-        const bool mine = (lane >> 4) == k;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) dsel[g] = mine ? d[g] : dsel[g];
       }
-#pragma unroll
-      for (int g = 0; g < 4; ++g)                      // 2 dsel = sum qi c, exact
-        s = __builtin_fmaf(gen_half(kr.s, g), 2.0f * dsel[g], __builtin_fmaf(gen_half(kr.z, g), qsum[g], s));
-    } else {
-      // The query limbs are re-read from LDS for every token: a query held
-      // in registers leaves one wave per SIMD (measured 12-19% slower).
-      asm volatile("" ::: "memory");
-      // per group: sum qi c from v_dot8_i32_i4, one accumulator per limb
-      // (4-bit codes read as c - 8, so + 8 sum qi restores sum qi c)
-      const uint32_t *ql = &ql_all[wave][0][0];
+      // sum over the digit rows with the blocks spread over the row blocks:
+      // lane (r, n) ends with the group sums of token 16 r + n, its own
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        int acc5[5] = {0, 0, 0, 0, 0};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int kn = (int)key_nibbles<KB>(kr, 4 * g + e);
-#pragma unroll
-          for (int L = 0; L < 5; ++L)
-            acc5[L] = __builtin_amdgcn_sdot8((int)ql[16 * L + 4 * g + e], kn, acc5[L], false);
-        }
-        const int v = acc5[0] + (acc5[1] << 4) + (acc5[2] << 8) + (acc5[3] << 12) + (acc5[4] << 16);
-        const float dot = KB == 4 ? (float)v + 8.0f * qsum[g] : (float)v;   // exact in fp32 (< 2^24)
+        const float dot = 2.0f * ms_digit_sum(d[0][g], d[1][g], d[2][g], d[3][g]);   // sum qi c
         s = __builtin_fmaf(gen_half(kr.s, g), dot, __builtin_fmaf(gen_half(kr.z, g), qsum[g], s));
       }
     }
@@ -505,11 +451,10 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
       return TileRows{r, r};
     };
     auto lk = [&](const TileRows &t) {
-      if constexpr (MS) return ms_load<KB>(a, t.k, 0, 64);
-      else return gen_load<KB>(a.kcodes, a.kscales, a.kzeros, t.k + lane);
+      return ms_load<KB>(a, t.k, 0, 64);
     };
     auto lv = [&](const TileRows &t) { return gen_load<VB>(a.vcodes, a.vscales, a.vzeros, t.v + lane); };
-    if constexpr (MS) {
+    if constexpr (KB != 4 && VB != 4) {
       // narrow rows leave registers for a three-deep pipeline: while tile i
       // is computed the loads of tiles i + 1 and i + 2 are in flight (2-5%
       // faster than one tile ahead); prefetches past the wave's last tile
@@ -568,8 +513,7 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
       const int64_t r = valid ? lane : lo;
       const TileRows tr = tile_rows(a, b, hkv, krow0, vrow0, base);
       const GenRow<VB> vr = gen_load<VB>(a.vcodes, a.vscales, a.vzeros, tr.v + r);
-      if constexpr (MS) run(ms_load<KB>(a, tr.k, (int)lo, (int)hi), vr, valid);
-      else run(gen_load<KB>(a.kcodes, a.kscales, a.kzeros, tr.k + r), vr, valid);
+      run(ms_load<KB>(a, tr.k, (int)lo, (int)hi), vr, valid);
     }
   }
 
@@ -623,24 +567,17 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
 // and matrix-core work) 10-50% slower.
 template <int VB>
 constexpr bool gen_value_mfma() { return VB != 4; }
-// The matrix-core key scores (MS) replace about 90 vector operations per
-// tile by 16 matrix-core products; measured 2-3% faster at 1- and 2-bit
-// keys with 1- or 2-bit values.  With 4-bit values (the fp32 value step's
-// 128 accumulators) the kernel would pass 256 registers and run one wave
-// per SIMD (K1 V4 6% slower), and 4-bit keys are bandwidth-bound already.
-template <int KB, int VB>
-constexpr bool gen_score_mfma() { return KB != 4 && VB != 4; }
-
 hipError_t launch_attn_generic(const AttnArgs &a, int kbits, int vbits, hipStream_t stream) {
   const dim3 grid((unsigned)((a.total_waves + kGenWaves - 1) / kGenWaves)), block(64 * kGenWaves);
 #define KVQ_GEN_CASE(KB, VB)                                                                  \
   if (kbits == KB && vbits == VB) {                                                           \
-    constexpr bool kVm = gen_value_mfma<VB>(), kMs = gen_score_mfma<KB, VB>();                \
-    hipLaunchKernelGGL((kv_quant_decode_attn<KB, VB, kVm, kMs>), grid, block, 0, stream, a);  \
+    constexpr bool kVm = gen_value_mfma<VB>();                                                \
+    hipLaunchKernelGGL((kv_quant_decode_attn<KB, VB, kVm>), grid, block, 0, stream, a);       \
     return hipGetLastError();                                                                 \
   }
+  // 2-bit keys and values take the INT2 kernels
   KVQ_GEN_CASE(1, 1) KVQ_GEN_CASE(1, 2) KVQ_GEN_CASE(1, 4)
-  KVQ_GEN_CASE(2, 1) KVQ_GEN_CASE(2, 2) KVQ_GEN_CASE(2, 4)
+  KVQ_GEN_CASE(2, 1) KVQ_GEN_CASE(2, 4)
   KVQ_GEN_CASE(4, 1) KVQ_GEN_CASE(4, 2) KVQ_GEN_CASE(4, 4)
 #undef KVQ_GEN_CASE
   return hipErrorNotSupported;
