@@ -92,17 +92,10 @@ __device__ __forceinline__ float gen_half(const u32x2_t &v, int g) {
   return half_bits_to_float((uint16_t)((g & 1) ? (w >> 16) : (w & 0xFFFFu)));
 }
 
-// Matrix-core key scores: the 4 x 16 tokens of a tile as four B
-// blocks of v_mfma_scale_f32_16x16x128_f8f6f4, lane (token 16 k + lane % 16,
-// group lane / 16) of block k, with the codes as fp4 nibbles 0b0..c (value
-// c / 2).  Score slot k (32 per group) holds the channel ms_channel(k):
-// 1-bit codes as four shifted copies of the group's dword (copy d keeps
-// bits 4 j + d in nibble j), 2-bit codes as mq_unpack, 4-bit codes per
-// 2-bit plane in place.
-template <int KB>
-__host__ __device__ __forceinline__ constexpr int ms_channel(int k) {
-  return KB == 4 ? k : KB == 2 ? mq_channel(k) : 32 * (k >> 5) + 4 * (k & 7) + ((k >> 3) & 3);
-}
+// Matrix-core key scores: the 4 x 16 tokens of a tile as four B blocks of
+// v_mfma_scale_f32_16x16x128_f8f6f4, lane (token 16 k + lane % 16, group
+// lane / 16) of block k, the codes as fp4 (mq_key_operand, slot order
+// mq_key_channel).
 
 // x_k (k = 0..3) hold, in lane (row block j, n), the part of row j of
 // block k.  Returns in lane (r, n) the sum over j of block r's rows: row
@@ -258,7 +251,7 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
     for (int w = 0; w < 4; ++w) {
       int d4[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) d4[e] = (lo_on || hi_on) ? mq_digit(qi[ms_channel<KB>(kbase + 4 * w + e)], Ld) : 0;
+      for (int e = 0; e < 4; ++e) d4[e] = (lo_on || hi_on) ? mq_digit(qi[mq_key_channel<KB>(kbase + 4 * w + e)], Ld) : 0;
       int v = __builtin_amdgcn_cvt_pk_fp8_f32((float)d4[0], (float)d4[1], 0, false);
       dw[w] = __builtin_amdgcn_cvt_pk_fp8_f32((float)d4[2], (float)d4[3], v, true);
     }
@@ -300,32 +293,10 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         d[k] = float4v_t{0.0f, 0.0f, 0.0f, 0.0f};
-        if constexpr (KB == 4) {
-          const u32x4_t w = kr.kc[k];
 #pragma unroll
-          for (int p = 0; p < 2; ++p) {                // code = lo + 4 hi: the hi plane's B scale is 2^2
-            v8i_t Bop;
-            Bop[0] = (int)((w.x >> (2 * p)) & 0x33333333u);
-            Bop[1] = (int)((w.y >> (2 * p)) & 0x33333333u);
-            Bop[2] = (int)((w.z >> (2 * p)) & 0x33333333u);
-            Bop[3] = (int)((w.w >> (2 * p)) & 0x33333333u);
-            Bop[4] = 0; Bop[5] = 0; Bop[6] = 0; Bop[7] = 0;
-            d[k] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Aq, Bop, d[k], 0, 4, 0, sa, 0, 127 + 2 * p);
-          }
-        } else {
-          v8i_t Bop;
-          if constexpr (KB == 2) {
-            Bop = mq_unpack(kr.kc[k]);
-          } else {
-            const uint32_t w = kr.kc[k];
-            Bop[0] = (int)(w & 0x11111111u);
-            Bop[1] = (int)((w >> 1) & 0x11111111u);
-            Bop[2] = (int)((w >> 2) & 0x11111111u);
-            Bop[3] = (int)((w >> 3) & 0x11111111u);
-            Bop[4] = 0; Bop[5] = 0; Bop[6] = 0; Bop[7] = 0;
-          }
-          d[k] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Aq, Bop, d[k], 0, 4, 0, sa, 0, 127);
-        }
+        for (int p = 0; p < (KB == 4 ? 2 : 1); ++p)   // 4 bits: code = lo + 4 hi
+          d[k] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Aq, mq_key_operand<KB>(kr.kc[k], p), d[k], 0, 4, 0,
+                                                                  sa, 0, 127 + 2 * p);
       }
       // sum over the digit rows with the blocks spread over the row blocks:
       // lane (r, n) ends with the group sums of token 16 r + n, its own

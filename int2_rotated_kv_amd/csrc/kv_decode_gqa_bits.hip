@@ -13,8 +13,8 @@
 //   v_mfma_scale_f32_16x16x128_f8f6f4 (fp8 digits of the fixed-point query
 //   times fp4 nibbles 0b00cc = code/2).
 //   - 2 bits: the packed codes as in the 2-bit kernel (slot order mq_channel).
-//   - 1 bit: each group's 32 bits are spread into the 2-bit layout first
-//     (bit i -> field i), then as 2 bits.
+//   - 1 bit: four shifted copies of the group's dword, each masked to the
+//     low bit of its nibbles (mq_key_operand).
 //   - 4 bits: code = lo + 4 hi with 2-bit planes; a nibble's plane p is
 //     (w >> 2p) & 0x33333333 in place, so slot 8u + e of a group is channel
 //     8u + e (the query digits are laid out in that order), and the high
@@ -45,12 +45,6 @@ struct MbLds {
   static constexpr int kPwOff = kCodeOff + 64 * kRowBytes / 4;     // [head][64 tokens] fp16
   static constexpr int kDwords = kPwOff + kMqHeads * 64 / 2;
 };
-
-// Channel of score slot k (32 slots per group) for key width KB.
-template <int KB>
-__device__ __forceinline__ constexpr int mb_channel(int k) {
-  return KB == 4 ? k : mq_channel(k);
-}
 
 template <int KB, int VB>
 struct MbTile {
@@ -112,7 +106,7 @@ __global__ __launch_bounds__(64 * kMqWaves, 2) void kv_quant_decode_attn_gqa(Att
     const int kbase = hi_on ? 64 + 16 * kba : 16 * kba;
     int q16[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) q16[i] = (lo_on || hi_on) ? qi[mb_channel<KB>(kbase + i)] : 0;
+    for (int i = 0; i < 16; ++i) q16[i] = (lo_on || hi_on) ? qi[mq_key_channel<KB>(kbase + i)] : 0;
 #pragma unroll
     for (int Ld = 0; Ld < 4; ++Ld) {
       int dw[4];
@@ -241,32 +235,12 @@ __global__ __launch_bounds__(64 * kMqWaves, 2) void kv_quant_decode_attn_gqa(Att
     for (int k = 0; k < 4; ++k) {
       const int tt = 16 * k + tk;
       float4v_t d = {0.0f, 0.0f, 0.0f, 0.0f};
-      if constexpr (KB == 4) {
-        const u32x4_t w = t.kc[k];
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          v8i_t Bop;
-          Bop[0] = (int)((w.x >> (2 * p)) & 0x33333333u);
-          Bop[1] = (int)((w.y >> (2 * p)) & 0x33333333u);
-          Bop[2] = (int)((w.z >> (2 * p)) & 0x33333333u);
-          Bop[3] = (int)((w.w >> (2 * p)) & 0x33333333u);
-          Bop[4] = 0; Bop[5] = 0; Bop[6] = 0; Bop[7] = 0;
-#pragma unroll
-          for (int Ld = 0; Ld < 4; ++Ld)
-            d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[Ld], Bop, d, 0, 4, 0, mq_scale(Ld), 0,
-                                                                 127 + 2 * p);
-        }
-      } else {
-        u32x2_t c2;
-        if constexpr (KB == 1) {
-          c2 = u32x2_t{mb_spread16(t.kc[k] & 0xFFFFu), mb_spread16(t.kc[k] >> 16)};
-        } else {
-          c2 = t.kc[k];
-        }
-        const v8i_t Bop = mq_unpack(c2);
+      for (int p = 0; p < (KB == 4 ? 2 : 1); ++p) {   // 4 bits: code = lo + 4 hi
+        const v8i_t Bop = mq_key_operand<KB>(t.kc[k], p);
 #pragma unroll
         for (int Ld = 0; Ld < 4; ++Ld)
-          d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[Ld], Bop, d, 0, 4, 0, mq_scale(Ld), 0, 127);
+          d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[Ld], Bop, d, 0, 4, 0, mq_scale(Ld), 0, 127 + 2 * p);
       }
       const u32x4_t kq = reinterpret_cast<const u32x4_t *>(rec + tt * kMbRecDwords)[0];
       const uint32_t kq0 = kq.x, kq1 = kq.y, kq2 = kq.z, kq3 = kq.w;

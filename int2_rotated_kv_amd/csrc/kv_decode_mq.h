@@ -1,8 +1,8 @@
 // Pieces shared by the attention kernels that run on the matrix cores
 // (kv_decode_gqa.hip for 2-bit grouped-query attention, kv_decode_gqa_bits.hip
-// for other widths, kv_decode_generic.hip's value step): the operand layouts
-// of the scores and values, row reductions, and the conversions of 1- and
-// 4-bit codes to the 2-bit layout.
+// for other widths, kv_decode_generic.hip for one query head per KV head):
+// the operand layouts of the scores and values, row reductions, and the
+// conversions of 1- and 4-bit codes to the 2-bit layout.
 #pragma once
 
 #include "kv_decode_common.h"
@@ -40,6 +40,39 @@ template <int KB> struct MbKeyWord;
 template <> struct MbKeyWord<1> { typedef uint32_t type; };
 template <> struct MbKeyWord<2> { typedef u32x2_t type; };
 template <> struct MbKeyWord<4> { typedef u32x4_t type; };
+
+// The fp4 key operand of one group (slot 8 d + j: nibble j of dword d) from
+// its packed codes, and the channel each slot holds:
+//   - 1 bit: four shifted copies of the group's dword (copy d keeps bits
+//     4 j + d in nibble j), so slot 8 d + j holds channel 4 j + d;
+//   - 2 bits: mq_unpack (slot order mq_channel);
+//   - 4 bits: 2-bit plane p of the nibbles in place (slot = channel); the
+//     high plane's product takes the B block scale 2^2.
+template <int KB>
+__host__ __device__ __forceinline__ constexpr int mq_key_channel(int k) {
+  return KB == 4 ? k : KB == 2 ? mq_channel(k) : 32 * (k >> 5) + 4 * (k & 7) + ((k >> 3) & 3);
+}
+template <int KB>
+__device__ __forceinline__ v8i_t mq_key_operand(const typename MbKeyWord<KB>::type &w, int p) {
+  v8i_t b;
+  if constexpr (KB == 2) {
+    b = mq_unpack(w);
+  } else {
+    if constexpr (KB == 4) {
+      b[0] = (int)((w.x >> (2 * p)) & 0x33333333u);
+      b[1] = (int)((w.y >> (2 * p)) & 0x33333333u);
+      b[2] = (int)((w.z >> (2 * p)) & 0x33333333u);
+      b[3] = (int)((w.w >> (2 * p)) & 0x33333333u);
+    } else {
+      b[0] = (int)(w & 0x11111111u);
+      b[1] = (int)((w >> 1) & 0x11111111u);
+      b[2] = (int)((w >> 2) & 0x11111111u);
+      b[3] = (int)((w >> 3) & 0x11111111u);
+    }
+    b[4] = 0; b[5] = 0; b[6] = 0; b[7] = 0;
+  }
+  return b;
+}
 
 // Balanced base-32 digit L (0 = most significant) of |q| < 2^19.
 __device__ __forceinline__ int mq_digit(int q, int L) {
@@ -94,13 +127,6 @@ __device__ __forceinline__ half8_t mq_bvals(uint32_t y02, uint32_t y13, uint32_t
   return half8_t{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
-// Bits 0..15 of x spread to the even bits of a dword (bit i -> bit 2i).
-__device__ __forceinline__ uint32_t mb_spread16(uint32_t x) {
-  x = (x | (x << 8)) & 0x00FF00FFu;
-  x = (x | (x << 4)) & 0x0F0F0F0Fu;
-  x = (x | (x << 2)) & 0x33333333u;
-  return (x | (x << 1)) & 0x55555555u;
-}
 // Bytes b0, b1 spread to the 2-bit layout: b0 -> bits 0..15, b1 -> bits 16..31.
 __device__ __forceinline__ uint32_t mb_spread_pair(uint32_t b0, uint32_t b1) {
   uint32_t x = b0 | (b1 << 16);
