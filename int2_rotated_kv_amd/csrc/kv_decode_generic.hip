@@ -283,8 +283,11 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
   const int64_t krow0 = bh * a.kT_cap + a.t_begin - a.skip;   // row 0 of the shifted grid
   const int64_t vrow0 = bh * a.vT_cap + a.t_begin - a.skip;
 
-  auto token = [&](const auto &kr, const GenRow<VB> &vr, bool valid, auto big_c) {
-    constexpr bool BIG = decltype(big_c)::value;
+  // Value scales of 2^15 or more switch the matrix-core value step to the
+  // halved entries for good (the fp32 step needs no switch); the mode enters
+  // as wave-uniform factors, so consecutive tiles share one basic block.
+  bool big = false;
+  auto token = [&](const auto &kr, const GenRow<VB> &vr, bool valid) {
     float s = 0.0f;
     {
       // block k (tokens 16 k .. 16 k + 15): lane (row block jr, token n) gets
@@ -335,10 +338,14 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
       // The grouped-query kernels' value step with one head: weights p~ =
       // fp16(p) everywhere, B entries code * s - fp16(1.5 s) over the 2-bit
       // layout (1-bit codes spread to 2-bit fields), the zero-point term
-      // accumulated per token lane.  BIG (a value scale of 2^15 or more
+      // accumulated per token lane.  big (a value scale of 2^15 or more
       // met): entries from s/2, weights doubled.
       static_assert(VB == 1 || VB == 2, "matrix-core value step: 1- and 2-bit values");
-      constexpr float kB = BIG ? 2.0f : 1.0f;
+      if (!big && __builtin_amdgcn_ballot_w64((((vr.s.x + 0x08000800u) | (vr.s.y + 0x08000800u)) &
+                                               0x80008000u) != 0u))
+        big = true;
+      const float kB = big ? 2.0f : 1.0f;
+      const _Float16 hb = big ? (_Float16)0.5f : (_Float16)1.0f, wb = big ? (_Float16)2.0f : (_Float16)1.0f;
       uint8_t *vcl = vcl_all[wave];
       uint32_t *vrec = vrec_all[wave];
       _Float16 *pw = pw_all[wave];
@@ -350,10 +357,8 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
       // element
       const uint32_t vs0 = vr.s.x, vs1 = vr.s.y, vz0 = vr.z.x, vz1 = vr.z.y;
       half2_t s01 = __builtin_bit_cast(half2_t, vs0), s23 = __builtin_bit_cast(half2_t, vs1);
-      if constexpr (BIG) {
-        s01 = s01 * half2_t{(_Float16)0.5f, (_Float16)0.5f};
-        s23 = s23 * half2_t{(_Float16)0.5f, (_Float16)0.5f};
-      }
+      s01 = s01 * half2_t{hb, hb};
+      s23 = s23 * half2_t{hb, hb};
       const half2_t n01 = s01 * half2_t{(_Float16)-1.5f, (_Float16)-1.5f};   // -fp16(1.5 s)
       const half2_t n23 = s23 * half2_t{(_Float16)-1.5f, (_Float16)-1.5f};
       const half2_t z01 = __builtin_bit_cast(half2_t, vz0), z23 = __builtin_bit_cast(half2_t, vz1);
@@ -368,7 +373,7 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
                   __builtin_amdgcn_perm(un23, us23, 0x05040100u), __builtin_amdgcn_perm(un23, us23, 0x07060302u)};
 #pragma unroll
       for (int k = 0; k < VB; ++k) reinterpret_cast<u32x4_t *>(vcl + lane * kVRow)[k] = vr.w[k];
-      pw[lane] = BIG ? ph * (_Float16)2.0f : ph;
+      pw[lane] = ph * wb;
       asm volatile("" ::: "memory");                   // LDS of one wave is ordered; keep the program order
 #pragma unroll
       for (int tb = 0; tb < 8; ++tb) {
@@ -396,18 +401,8 @@ __global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs 
       asm volatile("" ::: "memory");                   // the next tile's writes come after these reads
     }
   };
-  // Value scales of 2^15 or more switch the matrix-core value step to the
-  // halved entries for good (the fp32 step needs no switch).
-  bool big = false;
-  auto run = [&](const auto &kr, const GenRow<VB> &vr, bool valid) {
-    if constexpr (VM) {
-      if (!big && __builtin_amdgcn_ballot_w64((((vr.s.x + 0x08000800u) | (vr.s.y + 0x08000800u)) &
-                                               0x80008000u) != 0u))
-        big = true;
-    }
-    if (VM && big) token(kr, vr, valid, std::true_type{});
-    else token(kr, vr, valid, std::false_type{});
-  };
+  auto run = token;
+
 
   const HeadTiles ht(seq_int2(a, b), a.skip, split, S);
   if (ht.mine > 0) {

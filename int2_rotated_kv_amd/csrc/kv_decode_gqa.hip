@@ -18,8 +18,9 @@
 //   B (fp4 e2m1, 128 x 16): a 2-bit code zero-extended to a nibble is the
 //                           e2m1 value code/2, so the packed codes become the
 //                           operand with two masks and a shift.
-// Every product and partial sum is a multiple of 1/2 below 2^25, so D =
-// (1/2) sum_{c in j} qi_c code_c up to the last bit of fp32.  D lands as
+// With codes <= 3 the result is a multiple of 1/2 below 2^22.6 and the
+// partial sums after the leading digits are multiples of larger powers of
+// two in the same range, so D = (1/2) sum_{c in j} qi_c code_c exactly.  D lands as
 // lane (head g = lane/16, token lane%16) holding the four groups.
 //
 // Softmax runs per head on a 16-lane row (lazy reference as for G = 1).  The
@@ -207,28 +208,35 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
     return t;
   };
 
-  // One tile whose tokens [lo, hi) are valid.  BIG: the wave has met a value
-  // scale of 2^15 or more, for which fp16(1.5 s) and the B entries could
-  // overflow; the B entries are then built from s/2 and each weight in the A
-  // operand is doubled (2 p~ (code s/2 - fp16(0.75 s)) = p~ (code s - 2
-  // fp16(0.75 s)), exact power-of-two scalings), with the zero-point term
-  // z + 2 fp16(0.75 s) to match.  Either form may follow the other in one
-  // accumulator: each token's product is the same.
-  auto process = [&](const MqTile &t, int lo, int hi, auto big_c) {
-    constexpr bool BIG = decltype(big_c)::value;
-    constexpr float kB = BIG ? 2.0f : 1.0f;
+  // One tile whose tokens [lo, hi) are valid.  big: the wave has met a value
+  // scale of 2^15 or more (fp16 bits 0x7800 and up; adding 0x0800 sets bit
+  // 15 of such a half, with no carry for finite halves), for which
+  // fp16(1.5 s) and the B entries could overflow; from then on the B entries
+  // are built from s/2 and each weight in the A operand is doubled
+  // (2 p~ (code s/2 - fp16(0.75 s)) = p~ (code s - 2 fp16(0.75 s)), exact
+  // power-of-two scalings), with the zero-point term z + 2 fp16(0.75 s) to
+  // match.  Either form may follow the other in one accumulator: each
+  // token's product is the same.  The mode enters as wave-uniform factors
+  // (1 or 2, 1 or 1/2), not as a second copy of the tile code, so that one
+  // tile's value products and the next tile's score products fall in one
+  // basic block and can interleave.
+  bool big = false;
+  auto process = [&](const MqTile &t, int lo, int hi) {
+    if (!big && __builtin_amdgcn_ballot_w64(
+                    (((t.vs.x + 0x08000800u) | (t.vs.y + 0x08000800u)) & 0x80008000u) != 0u))
+      big = true;
+    const float kB = big ? 2.0f : 1.0f;
+    const _Float16 hb = big ? (_Float16)0.5f : (_Float16)1.0f, wb = big ? (_Float16)2.0f : (_Float16)1.0f;
     {
       // per-token record (lane = token) and the value codes
       uint32_t *rl = rec + lane * kMqRecDwords;
       uint32_t vs0 = t.vs.x, vs1 = t.vs.y;
       const uint32_t vz0 = t.vz.x, vz1 = t.vz.y;
       half2_t s01 = __builtin_bit_cast(half2_t, vs0), s23 = __builtin_bit_cast(half2_t, vs1);
-      if constexpr (BIG) {
-        s01 = s01 * half2_t{(_Float16)0.5f, (_Float16)0.5f};
-        s23 = s23 * half2_t{(_Float16)0.5f, (_Float16)0.5f};
-        vs0 = __builtin_bit_cast(uint32_t, s01);
-        vs1 = __builtin_bit_cast(uint32_t, s23);
-      }
+      s01 = s01 * half2_t{hb, hb};
+      s23 = s23 * half2_t{hb, hb};
+      vs0 = __builtin_bit_cast(uint32_t, s01);
+      vs1 = __builtin_bit_cast(uint32_t, s23);
       const half2_t z01 = __builtin_bit_cast(half2_t, vz0), z23 = __builtin_bit_cast(half2_t, vz1);
       const half2_t n01 = s01 * half2_t{(_Float16)-1.5f, (_Float16)-1.5f};   // -fp16(1.5 s)
       const half2_t n23 = s23 * half2_t{(_Float16)-1.5f, (_Float16)-1.5f};
@@ -310,7 +318,7 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
       st.zacc[1] = __builtin_fmaf(pf, zb[1], st.zacc[1]);
       st.zacc[2] = __builtin_fmaf(pf, zb[2], st.zacc[2]);
       st.zacc[3] = __builtin_fmaf(pf, zb[3], st.zacc[3]);
-      pw[gk * 64 + tt] = BIG ? ph * (_Float16)2.0f : ph;
+      pw[gk * 64 + tt] = ph * wb;
     }
     asm volatile("" ::: "memory");
     // values: 8 blocks of 8 tokens; lane's tokens t0 = 8 tb + 2 kb and t0 + 1
@@ -339,17 +347,8 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
     asm volatile("" ::: "memory");
   };
 
-  // Value scales of 2^15 or more (fp16 bits 0x7800 and up; adding 0x0800
-  // sets bit 15 of a half exactly then, with no carry for finite halves)
-  // switch the wave to the halved B entries for good.
-  bool big = false;
-  auto run = [&](const MqTile &t, int lo, int hi) {
-    if (!big && __builtin_amdgcn_ballot_w64(
-                    (((t.vs.x + 0x08000800u) | (t.vs.y + 0x08000800u)) & 0x80008000u) != 0u))
-      big = true;
-    if (big) process(t, lo, hi, std::true_type{});
-    else process(t, lo, hi, std::false_type{});
-  };
+  auto run = process;
+
 
   // this wave's full tiles, loads one tile ahead
   const HeadTiles ht(seq_int2(a, b), a.skip, split, S);

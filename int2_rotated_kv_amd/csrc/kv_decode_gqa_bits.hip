@@ -195,23 +195,26 @@ __global__ __launch_bounds__(64 * kMqWaves, 2) void kv_quant_decode_attn_gqa(Att
     return t;
   };
 
-  // One tile whose tokens [lo, hi) are valid; BIG as in the 2-bit kernel
-  // (value scales of 2^15 or more: entries from s/2, weights doubled).
-  auto process = [&](const MbTile<KB, VB> &t, int lo, int hi, auto big_c) {
-    constexpr bool BIG = decltype(big_c)::value;
-    constexpr float kB = BIG ? 2.0f : 1.0f;
+  // One tile whose tokens [lo, hi) are valid; big as in the 2-bit kernel
+  // (value scales of 2^15 or more: entries from s/2, weights doubled; the
+  // mode enters as wave-uniform factors).
+  bool big = false;
+  auto process = [&](const MbTile<KB, VB> &t, int lo, int hi) {
+    if (!big && __builtin_amdgcn_ballot_w64(
+                    (((t.vs.x + 0x08000800u) | (t.vs.y + 0x08000800u)) & 0x80008000u) != 0u))
+      big = true;
+    const float kB = big ? 2.0f : 1.0f;
+    const _Float16 hb = big ? (_Float16)0.5f : (_Float16)1.0f, wb = big ? (_Float16)2.0f : (_Float16)1.0f;
     constexpr float kZ = VB == 4 ? 5.0f : 1.0f;    // planes: 1.5 s (1 + 4)
     {
       uint32_t *rl = rec + lane * kMbRecDwords;
       uint32_t vs0 = t.vs.x, vs1 = t.vs.y;
       const uint32_t vz0 = t.vz.x, vz1 = t.vz.y;
       half2_t s01 = __builtin_bit_cast(half2_t, vs0), s23 = __builtin_bit_cast(half2_t, vs1);
-      if constexpr (BIG) {
-        s01 = s01 * half2_t{(_Float16)0.5f, (_Float16)0.5f};
-        s23 = s23 * half2_t{(_Float16)0.5f, (_Float16)0.5f};
-        vs0 = __builtin_bit_cast(uint32_t, s01);
-        vs1 = __builtin_bit_cast(uint32_t, s23);
-      }
+      s01 = s01 * half2_t{hb, hb};
+      s23 = s23 * half2_t{hb, hb};
+      vs0 = __builtin_bit_cast(uint32_t, s01);
+      vs1 = __builtin_bit_cast(uint32_t, s23);
       const half2_t z01 = __builtin_bit_cast(half2_t, vz0), z23 = __builtin_bit_cast(half2_t, vz1);
       const half2_t n01 = s01 * half2_t{(_Float16)-1.5f, (_Float16)-1.5f};   // -fp16(1.5 s)
       const half2_t n23 = s23 * half2_t{(_Float16)-1.5f, (_Float16)-1.5f};
@@ -293,7 +296,7 @@ __global__ __launch_bounds__(64 * kMqWaves, 2) void kv_quant_decode_attn_gqa(Att
       st.zacc[1] = __builtin_fmaf(pf, zb[1], st.zacc[1]);
       st.zacc[2] = __builtin_fmaf(pf, zb[2], st.zacc[2]);
       st.zacc[3] = __builtin_fmaf(pf, zb[3], st.zacc[3]);
-      pw[gk * 64 + tt] = BIG ? ph * (_Float16)2.0f : ph;
+      pw[gk * 64 + tt] = ph * wb;
     }
     asm volatile("" ::: "memory");
     // values: 8 blocks of 8 tokens; lane's tokens t0 = 8 tb + 2 kb and t0 + 1,
@@ -339,14 +342,7 @@ __global__ __launch_bounds__(64 * kMqWaves, 2) void kv_quant_decode_attn_gqa(Att
     asm volatile("" ::: "memory");
   };
 
-  bool big = false;
-  auto run = [&](const MbTile<KB, VB> &t, int lo, int hi) {
-    if (!big && __builtin_amdgcn_ballot_w64(
-                    (((t.vs.x + 0x08000800u) | (t.vs.y + 0x08000800u)) & 0x80008000u) != 0u))
-      big = true;
-    if (big) process(t, lo, hi, std::true_type{});
-    else process(t, lo, hi, std::false_type{});
-  };
+  auto run = process;
 
   const HeadTiles ht(seq_int2(a, b), a.skip, split, S);
   const int64_t mine = ht.mine;
