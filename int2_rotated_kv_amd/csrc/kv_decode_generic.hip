@@ -23,8 +23,6 @@
 //     at the end by a reduce-scatter over the 64 lanes.
 // The wave writes the same partial (o', m, l) as the INT2 kernels, so the
 // combine and un-rotation are shared.
-#include <type_traits>
-
 #include "kv_decode_mq.h"
 
 namespace kvq {

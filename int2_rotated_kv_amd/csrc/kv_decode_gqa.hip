@@ -40,8 +40,6 @@
 // 8n .. 8n+7 of its head, summed over every token of the split.  The
 // zero-point term sum p~ (z + fp16(1.5 s)) is accumulated per group in the
 // softmax layout.
-#include <type_traits>
-
 #include "kv_decode_mq.h"
 
 namespace kvq {

@@ -28,8 +28,6 @@
 //   - 4 bits: two 2-bit planes compacted from the nibbles, the high plane
 //     with weights 4 p~ (exact); the zero-point term is then
 //     z + 5 fp16(1.5 s).
-#include <type_traits>
-
 #include "kv_decode_mq.h"
 
 namespace kvq {
