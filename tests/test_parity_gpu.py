@@ -666,7 +666,7 @@ def test_quantize_bits_ties(kbits, vbits, rot):
     (4, 2, "hadamard", 2, 1), (2, 4, "hadamard", 2, 1), (1, 1, "hadamard", 2, 1),
     (4, 4, "hadamard", 2, 1), (1, 2, "none", 1, 1), (4, 2, "perm", 2, 1),
     (4, 2, "hadamard", 2, 4), (4, 2, "hadamard", 5, 1), (2, 1, "hadamard", 1, 2),
-    (4, 2, "dense", 4, 4), (1, 4, "dense", 4, 1)])
+    (4, 2, "dense", 4, 4), (1, 4, "dense", 4, 1), (2, 1, "dense", 4, 1), (4, 1, "perm", 2, 1)])
 def test_decode_bits(kbits, vbits, rot, cid, G):
     """b-bit decode (the kernel for widths other than 2/2) against the
     oracle on the same cache bytes: keys and values at their own widths,
@@ -709,8 +709,9 @@ def test_decode_bits(kbits, vbits, rot, cid, G):
     (4, 4, "hadamard", 2, 3)])
 def test_decode_bits_gqa(kbits, vbits, rot, cid, G):
     """Grouped-query decode at widths other than 2/2 (the matrix-core b-bit
-    kernel: 1-bit codes spread to 2-bit fields, 4-bit codes as two 2-bit
-    planes) against the oracle on the same cache bytes: every width pair,
+    kernel: 1-bit keys as four shifted copies, 1-bit values spread to 2-bit
+    fields, 4-bit codes as two 2-bit planes) against the oracle on the same
+    cache bytes: every width pair,
     query groups of 2, 3 (a partial group of four heads), 4 and 8 (two
     groups), every rotation, fp16 sinks and residual tokens (LLaMA-2-13B
     recipe), a ragged INT2 range that starts inside a tile."""
