@@ -201,6 +201,29 @@ def test_fullsize_config3_key4_value2():
     tally.check("c3 K4V2")
 
 
+def test_fullsize_config3_key1_value1():
+    """Throughput shapes at 1-bit keys and values (bench.py --kbits 1
+    --vbits 1): the one-head b-bit decode with its matrix-core key scores and
+    value step at the workload's grid and split plan."""
+    cfg = W.config(3)
+    B, T, H, d = cfg.B, cfg.T, cfg.Hkv, cfg.d
+    K = W.kv_tokens(cfg, "K", device=DEV)
+    V = W.kv_tokens(cfg, "V", device=DEV)
+    q = W.queries(cfg, device=DEV)
+    ck, cv = kvq.Int2Cache.empty(B, H, T, bits=1), kvq.Int2Cache.empty(B, H, T, bits=1)
+    kvq.kvq_quantize(K, V, ck, cv, rot="hadamard")
+    out = kvq.kvq_decode_attention(q, ck, cv, 0, T, rot="hadamard")
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    tally = GroupTally("hadamard")
+    for b, hk in ((0, 0), (13, 30)):
+        stats, err = _check_head(cfg, K, V, ck, cv, out, q, b, hk, "hadamard", None, 0, T)
+        _report(f"c3 K1V1 b={b} h={hk}", normwise=err, K=stats["K"], V=stats["V"])
+        tally.add(stats)
+        assert err <= ATTN_TOL
+    tally.check("c3 K1V1")
+
+
 def test_fullsize_config3_varlen():
     """Throughput shapes as a mixed-length batch (the ends bench.py --varlen
     draws): sampled sequences against the oracle over their own ranges."""
