@@ -122,14 +122,21 @@ def prerope_ops_per_unit(gh: int, g: int) -> int:
 
 
 ARITHMETIC_BBIT_GQA = {"write": ARITHMETIC_WRITE.replace("2-bit", "b-bit"),
-                       "scores": "fp8 digits of a 19-bit fixed-point query x 2-bit planes of the codes (fp4) on the "
-                                 "matrix cores (exact), f32 scale/zero terms",
+                       "scores": "fp8 digits of a 19-bit fixed-point query x fp4 codes (4-bit codes as two 2-bit "
+                                 "planes) on the matrix cores (exact at 1- and 2-bit keys), f32 scale/zero terms",
                        "values": "f16 weights x f16 (plane*s - 1.5 s) on the matrix cores, f32 accumulation",
                        "combine": "f32 merge and un-rotation, output in the query dtype"}
-ARITHMETIC_BBIT = {"write": ARITHMETIC_WRITE.replace("2-bit", "b-bit"),
-                   "scores": "int32 dot of the codes with a 19-bit fixed-point rotated query, f32 scale/zero terms",
-                   "values": "f32 FMA per code, f32 accumulation",
-                   "combine": "f32 merge and un-rotation, output in the query dtype"}
+
+
+def arithmetic_bbit_g1(vbits):
+    """The one-query-head b-bit decode: matrix-core scores at every width, the
+    matrix-core value step at 1- and 2-bit values, fp32 FMAs at 4-bit values."""
+    return {"write": ARITHMETIC_WRITE.replace("2-bit", "b-bit"),
+            "scores": "fp8 digits of a 19-bit fixed-point query (one per row block) x fp4 codes (4-bit codes as "
+                      "two 2-bit planes) on the matrix cores, f32 scale/zero terms",
+            "values": ("f32 FMA per code, f32 accumulation" if vbits == 4 else
+                       "f16 weights x f16 (code*s - 1.5 s) on the matrix cores, f32 accumulation"),
+            "combine": "f32 merge and un-rotation, output in the query dtype"}
 
 PREROLL_MS = 30.0        # untimed calls before each timed phase
 FLUSH_BYTES = 1 << 30    # read between timed calls
@@ -438,7 +445,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": f"f16 in / {cache_tag} cache", "data": "synthetic",
         "arithmetic": (ARITHMETIC_PREROPE if GHP else
-                       (ARITHMETIC_BBIT if cfg.G == 1 else ARITHMETIC_BBIT_GQA) if (kbits, vbits) != (2, 2) else
+                       (arithmetic_bbit_g1(vbits) if cfg.G == 1 else ARITHMETIC_BBIT_GQA) if (kbits, vbits) != (2, 2) else
                        ARITHMETIC_G1 if cfg.G == 1 else ARITHMETIC_GQA),
         "config": {"workload": workload, "B": B, "T": T, "Hkv": H, "Hq": cfg.Hq, "d": d,
                    "kv_input": "f16",
