@@ -233,7 +233,7 @@ size_t kvq_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
                                   int64_t n_int2_tokens, int64_t n_sink, int64_t n_res) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || d != 128) return 0;
   if (n_int2_tokens < 0 || n_sink < 0 || n_res < 0) return 0;
-  const kvq::SplitPlan p = kvq::plan_splits(B, Hq, Hkv, n_int2_tokens);
+  const kvq::SplitPlan p = kvq::plan_splits(B, Hq, Hkv, n_int2_tokens, kvq::workspace_target_waves(Hq / Hkv));
   return workspace_bytes(B, Hq, p.n_splits);
 }
 
@@ -278,8 +278,10 @@ kvq_status decode_impl(const void *q, kvq_dtype q_dtype, int64_t B, int64_t Hq,
   if (!(softmax_scale == softmax_scale)) return KVQ_ERR_INVALID_ARG;   // NaN
   // keys with the pre-RoPE grouped-head rotation: one attention wave per
   // query head, and the score rows after the partials
-  const kvq::SplitPlan plan = group_heads > 0 ? kvq::plan_splits(B, Hq, Hq, n_int2)
-                                              : kvq::plan_splits(B, Hq, Hkv, n_int2);
+  const int kbits = n_int2 > 0 ? kc->bits : 2, vbits = n_int2 > 0 ? vc->bits : 2;
+  const kvq::SplitPlan plan =
+      group_heads > 0 ? kvq::plan_splits(B, Hq, Hq, n_int2)
+                      : kvq::plan_splits(B, Hq, Hkv, n_int2, kvq::decode_target_waves(Hq / Hkv, kbits, vbits));
   const size_t need = group_heads > 0 ? workspace_bytes_prerope(B, Hq, plan.n_splits, n_int2)
                                       : workspace_bytes(B, Hq, plan.n_splits);
   if (static_scratch) {
@@ -301,8 +303,8 @@ kvq_status decode_impl(const void *q, kvq_dtype q_dtype, int64_t B, int64_t Hq,
     a.kcodes = kc->codes; a.kscales = kc->scales; a.kzeros = kc->zeros; a.kT_cap = kc->T_cap;
     a.vcodes = vc->codes; a.vscales = vc->scales; a.vzeros = vc->zeros; a.vT_cap = vc->T_cap;
   }
-  a.kbits = n_int2 > 0 ? kc->bits : 2;
-  a.vbits = n_int2 > 0 ? vc->bits : 2;
+  a.kbits = kbits;
+  a.vbits = vbits;
   if (pg != nullptr && n_int2 > 0) {
     // paged caches: rows per page instead of per (b, head)
     a.block_table = pg->block_table;

@@ -136,10 +136,17 @@ __device__ __forceinline__ MsKeys<KB> ms_load(const AttnArgs &a, int64_t r0, int
   return r;
 }
 
+// Waves per SIMD the register budget is held to: three with the matrix-core
+// value step (144-164 registers without spills; the tighter allocation
+// measured 1-4% faster even at two resident waves), except at 1-bit keys
+// with 2-bit values, which would spill; one with the fp32 value step.
+template <int KB, int VB, bool VM>
+constexpr int gen_min_waves() { return VM && !(KB == 1 && VB == 2) ? 3 : 1; }
+
 // grid: ceil(total_waves / 4) blocks of 4 waves; wave index as in
 // wave_place with one wave per query head (`per` = G).
 template <int KB, int VB, bool VM>
-__global__ __launch_bounds__(64 * kGenWaves) void kv_quant_decode_attn(AttnArgs a) {
+__global__ __launch_bounds__(64 * kGenWaves, (gen_min_waves<KB, VB, VM>())) void kv_quant_decode_attn(AttnArgs a) {
   // the query as a 19-bit fixed point, and its group sums
   __shared__ int32_t qi_all[kGenWaves][kD];
   __shared__ float qsum_all[kGenWaves][4];

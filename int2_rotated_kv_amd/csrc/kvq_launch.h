@@ -79,7 +79,13 @@ struct DecodeArgs {
 struct SplitPlan {
   int64_t n_splits;
 };
-SplitPlan plan_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_int2);
+// target_waves: the attention waves of one resident round (2048 at two
+// waves per SIMD); decode_target_waves picks it for a call, and
+// workspace_target_waves bounds it for the workspace query, which does not
+// see the code widths.
+SplitPlan plan_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t n_int2, int64_t target_waves = 2048);
+int64_t decode_target_waves(int64_t G, int kbits, int vbits);
+int64_t workspace_target_waves(int64_t G);
 // attention waves per split: one per query head for G = 1, one per four
 // query heads of a KV head for G >= 2 (the matrix-core GQA kernel)
 int64_t split_units(int64_t B, int64_t Hq, int64_t Hkv);
