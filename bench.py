@@ -135,7 +135,7 @@ def arithmetic_bbit_g1(vbits):
             "scores": "fp8 digits of a 19-bit fixed-point query (one per row block) x fp4 codes (4-bit codes as "
                       "two 2-bit planes) on the matrix cores, f32 scale/zero terms",
             "values": ("f32 FMA per code, f32 accumulation" if vbits == 4 else
-                       "f16 weights x f16 (code*s - 1.5 s) on the matrix cores, f32 accumulation"),
+                       "f16 weights fp16(p*s) per value group x f16 codes on the matrix cores, f32 accumulation"),
             "combine": "f32 merge and un-rotation, output in the query dtype"}
 
 PREROLL_MS = 30.0        # untimed calls before each timed phase

@@ -254,13 +254,6 @@ struct AttnState {
   float slack;
 };
 
-// Any of the four fp16 value scales (two per dword, all >= 0) at 2^11 or
-// above: with p < 2^kSlack, p * s could then round past the fp16 range.
-// Adding 0x1800 to each half sets its bit 15 exactly for 0x6800 (= 2048)
-// and above; finite halves stay below 0x10000, so nothing carries across.
-__device__ __forceinline__ bool big_value_scale(uint32_t s0, uint32_t s1) {
-  return (((s0 + 0x18001800u) | (s1 + 0x18001800u)) & 0x80008000u) != 0u;
-}
 
 // Per-lane query data for the lane's two channel groups of GC heads.
 template <int GC>

@@ -340,6 +340,14 @@ __device__ __forceinline__ constexpr float chan_unscale(int x) {
 // (m, l, o') is exact for any reference m, so the merge is unchanged.
 constexpr float kSlack = 4.0f;
 
+// Any of the four fp16 value scales (two per dword, all >= 0) at 2^11 or
+// above: with p < 2^kSlack, p * s could then round past the fp16 range.
+// Adding 0x1800 to each half sets its bit 15 exactly for 0x6800 (= 2048)
+// and above; finite halves stay below 0x10000, so nothing carries across.
+__device__ __forceinline__ bool big_value_scale(uint32_t s0, uint32_t s1) {
+  return (((s0 + 0x18001800u) | (s1 + 0x18001800u)) & 0x80008000u) != 0u;
+}
+
 constexpr uint32_t kHalf2Ones = 0x3C003C00u;   // (1.0, 1.0) in fp16
 
 // Sum / max over the two 16-lane rows of each 32-lane half (xor 16) and over

@@ -17,10 +17,13 @@
 //     base-32 digits as one fp8 operand (a digit per row block, its weight
 //     in the E8M0 A scale) against the codes as fp4, then a sum across the
 //     row blocks that leaves each lane its own token's group sums.
-//   - Values: at 1- and 2-bit values the grouped-query kernels' matrix-core
-//     value step with one head (VM); at 4-bit values the lane adds its
-//     token's weighted codes into 128 fp32 accumulators of its own, summed
-//     at the end by a reduce-scatter over the 64 lanes.
+//   - Values: at 1- and 2-bit values on the matrix cores (VM), in the
+//     operand layout of the grouped-query kernels' value step, with the
+//     A rows given to the four value groups instead of four heads: row
+//     (group g, position e) carries w = fp16(p s_g) of each token, B the
+//     plain codes, so the scale costs nothing per code; at 4-bit values the
+//     lane adds its token's weighted codes into 128 fp32 accumulators of its
+//     own, summed at the end by a reduce-scatter over the 64 lanes.
 // The wave writes the same partial (o', m, l) as the INT2 kernels, so the
 // combine and un-rotation are shared.
 #include "kv_decode_mq.h"
@@ -137,11 +140,11 @@ __device__ __forceinline__ MsKeys<KB> ms_load(const AttnArgs &a, int64_t r0, int
 }
 
 // Waves per SIMD the register budget is held to: three with the matrix-core
-// value step (144-164 registers without spills; the tighter allocation
-// measured 1-4% faster even at two resident waves), except at 1-bit keys
-// with 2-bit values, which would spill; one with the fp32 value step.
+// value step (132-156 registers without spills; the tighter allocation
+// measured 1-4% faster even at two resident waves), one with the fp32 value
+// step.
 template <int KB, int VB, bool VM>
-constexpr int gen_min_waves() { return VM && !(KB == 1 && VB == 2) ? 3 : 1; }
+constexpr int gen_min_waves() { return VM ? 3 : 1; }
 
 // grid: ceil(total_waves / 4) blocks of 4 waves; wave index as in
 // wave_place with one wave per query head (`per` = G).
@@ -150,12 +153,11 @@ __global__ __launch_bounds__(64 * kGenWaves, (gen_min_waves<KB, VB, VM>())) void
   // the query as a 19-bit fixed point, and its group sums
   __shared__ int32_t qi_all[kGenWaves][kD];
   __shared__ float qsum_all[kGenWaves][4];
-  // value step on the matrix cores: the tile's value rows, per-token
-  // (s, -fp16(1.5 s)) of each group, and the fp16 weights
+  // value step on the matrix cores: the tile's value rows and the fp16
+  // weights w = fp16(p s_g), [group][token]
   constexpr int kVRow = 16 * VB;
   __shared__ __attribute__((aligned(16))) uint8_t vcl_all[VM ? kGenWaves : 1][VM ? 64 * kVRow : 16];
-  __shared__ __attribute__((aligned(16))) uint32_t vrec_all[VM ? kGenWaves : 1][VM ? 64 * 4 : 4];
-  __shared__ __attribute__((aligned(16))) _Float16 pw_all[VM ? kGenWaves : 1][VM ? 64 : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 pw_all[VM ? kGenWaves : 1][VM ? 4 * 64 : 8];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t gw = (int64_t)blockIdx.x * kGenWaves + wave;
@@ -270,16 +272,18 @@ __global__ __launch_bounds__(64 * kGenWaves, (gen_min_waves<KB, VB, VM>())) void
   float acc[VM ? 1 : kD];                             // value accumulators, value-code order
 #pragma unroll
   for (int i = 0; i < (VM ? 1 : kD); ++i) acc[i] = 0.0f;
-  // matrix-core value step: lane (byte pair vn, token pair vkb) of B; the A
-  // rows of head 0 (ha = vn / 4 = 0) carry the weights, the other rows zero
+  // matrix-core value step: lane (byte pair vn, token pair vkb) of B; lane
+  // (group ga = vn / 4, position e = vn % 4, vkb) of A.  The A dword d holds
+  // token 2 vkb + d / 2 at positions (d % 2, d % 2 + 2); v_perm selectors
+  // pick that token's weight into the half of position e, or zero.
   float4v_t o[2] = {float4v_t{0.0f, 0.0f, 0.0f, 0.0f}, float4v_t{0.0f, 0.0f, 0.0f, 0.0f}};
-  const int vn = lane & 15, vkb = lane >> 4;
+  const int vn = lane & 15, vkb = lane >> 4, ga = vn >> 2;
   uint32_t selA[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const int ve = vn & 3;
     const uint32_t src = (d >> 1) ? 0x0706u : 0x0504u;
-    const bool on = (vn >> 2) == 0 && (d & 1) == (ve & 1);
+    const bool on = (d & 1) == (ve & 1);
     selA[d] = !on ? 0x0C0C0C0Cu : (ve >> 1) ? ((src << 16) | 0x0C0Cu) : (0x0C0C0000u | src);
   }
   float zacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -288,10 +292,11 @@ __global__ __launch_bounds__(64 * kGenWaves, (gen_min_waves<KB, VB, VM>())) void
   const int64_t krow0 = bh * a.kT_cap + a.t_begin - a.skip;   // row 0 of the shifted grid
   const int64_t vrow0 = bh * a.vT_cap + a.t_begin - a.skip;
 
-  // Value scales of 2^15 or more switch the matrix-core value step to the
-  // halved entries for good (the fp32 step needs no switch); the mode enters
-  // as wave-uniform factors, so consecutive tiles share one basic block.
-  bool big = false;
+  // Weights stay below 2^slack: kSlack, or, in the matrix-core value step,
+  // 0 once the wave has met a value scale of 2^11 or more, so that
+  // w = fp16(p s) stays inside the fp16 range for every finite scale (the
+  // fp32 step needs no switch).
+  float slack = kSlack;
   auto token = [&](const auto &kr, const GenRow<VB> &vr, bool valid) {
     float s = 0.0f;
     {
@@ -317,7 +322,11 @@ __global__ __launch_bounds__(64 * kGenWaves, (gen_min_waves<KB, VB, VM>())) void
     s *= qstep;
     s = valid ? s : kNegInf;
     const float mt = gen_wave_max(s);
-    if (mt > m_run + kSlack) {                         // wave-uniform
+    if constexpr (VM) {
+      const uint32_t vs0 = vr.s.x, vs1 = vr.s.y;
+      if (slack > 0.0f && __builtin_amdgcn_ballot_w64(big_value_scale(vs0, vs1))) slack = 0.0f;
+    }
+    if (mt > m_run + slack) {                          // wave-uniform
       const float f = __builtin_amdgcn_exp2f(m_run - mt);
 #pragma unroll
       for (int i = 0; i < (VM ? 1 : kD); ++i) acc[i] *= f;
@@ -340,19 +349,14 @@ __global__ __launch_bounds__(64 * kGenWaves, (gen_min_waves<KB, VB, VM>())) void
           acc[32 * g + i] = __builtin_fmaf(pv, gen_code<VB>(vr, 32 * g + i), acc[32 * g + i]);
       }
     } else {
-      // The grouped-query kernels' value step with one head: weights p~ =
-      // fp16(p) everywhere, B entries code * s - fp16(1.5 s) over the 2-bit
-      // layout (1-bit codes spread to 2-bit fields), the zero-point term
-      // accumulated per token lane.  big (a value scale of 2^15 or more
-      // met): entries from s/2, weights doubled.
+      // Weights w_g = fp16(p~ s_g) with p~ = fp16(p), B entries the plain
+      // codes over the 2-bit layout (1-bit codes spread to 2-bit fields).
+      // Centered on c = (2^VB - 1) / 2: o' = sum w code - c sum w +
+      // sum p~ (z + c s), so the rounding of w multiplies code - c; the last
+      // two terms are accumulated per token lane.
       static_assert(VB == 1 || VB == 2, "matrix-core value step: 1- and 2-bit values");
-      if (!big && __builtin_amdgcn_ballot_w64((((vr.s.x + 0x08000800u) | (vr.s.y + 0x08000800u)) &
-                                               0x80008000u) != 0u))
-        big = true;
-      const float kB = big ? 2.0f : 1.0f;
-      const _Float16 hb = big ? (_Float16)0.5f : (_Float16)1.0f, wb = big ? (_Float16)2.0f : (_Float16)1.0f;
+      constexpr float kC = 0.5f * (float)((1 << VB) - 1);
       uint8_t *vcl = vcl_all[wave];
-      uint32_t *vrec = vrec_all[wave];
       _Float16 *pw = pw_all[wave];
       const _Float16 ph = (_Float16)p;
       const float pf = (float)ph;
@@ -361,24 +365,19 @@ __global__ __launch_bounds__(64 * kGenWaves, (gen_min_waves<KB, VB, VM>())) void
       // bit cast of an element such as vr.s.y as a read of the vector's first
       // element
       const uint32_t vs0 = vr.s.x, vs1 = vr.s.y, vz0 = vr.z.x, vz1 = vr.z.y;
-      half2_t s01 = __builtin_bit_cast(half2_t, vs0), s23 = __builtin_bit_cast(half2_t, vs1);
-      s01 = s01 * half2_t{hb, hb};
-      s23 = s23 * half2_t{hb, hb};
-      const half2_t n01 = s01 * half2_t{(_Float16)-1.5f, (_Float16)-1.5f};   // -fp16(1.5 s)
-      const half2_t n23 = s23 * half2_t{(_Float16)-1.5f, (_Float16)-1.5f};
+      const half2_t s01 = __builtin_bit_cast(half2_t, vs0), s23 = __builtin_bit_cast(half2_t, vs1);
       const half2_t z01 = __builtin_bit_cast(half2_t, vz0), z23 = __builtin_bit_cast(half2_t, vz1);
-      zacc[0] = __builtin_fmaf(pf, __builtin_fmaf(-kB, (float)n01.x, (float)z01.x), zacc[0]);
-      zacc[1] = __builtin_fmaf(pf, __builtin_fmaf(-kB, (float)n01.y, (float)z01.y), zacc[1]);
-      zacc[2] = __builtin_fmaf(pf, __builtin_fmaf(-kB, (float)n23.x, (float)z23.x), zacc[2]);
-      zacc[3] = __builtin_fmaf(pf, __builtin_fmaf(-kB, (float)n23.y, (float)z23.y), zacc[3]);
-      const uint32_t us01 = __builtin_bit_cast(uint32_t, s01), us23 = __builtin_bit_cast(uint32_t, s23);
-      const uint32_t un01 = __builtin_bit_cast(uint32_t, n01), un23 = __builtin_bit_cast(uint32_t, n23);
-      reinterpret_cast<u32x4_t *>(vrec)[lane] =
-          u32x4_t{__builtin_amdgcn_perm(un01, us01, 0x05040100u), __builtin_amdgcn_perm(un01, us01, 0x07060302u),
-                  __builtin_amdgcn_perm(un23, us23, 0x05040100u), __builtin_amdgcn_perm(un23, us23, 0x07060302u)};
+      const half2_t w01 = s01 * half2_t{ph, ph}, w23 = s23 * half2_t{ph, ph};
+      zacc[0] = __builtin_fmaf(pf, __builtin_fmaf(kC, (float)s01.x, (float)z01.x), __builtin_fmaf(-kC, (float)w01.x, zacc[0]));
+      zacc[1] = __builtin_fmaf(pf, __builtin_fmaf(kC, (float)s01.y, (float)z01.y), __builtin_fmaf(-kC, (float)w01.y, zacc[1]));
+      zacc[2] = __builtin_fmaf(pf, __builtin_fmaf(kC, (float)s23.x, (float)z23.x), __builtin_fmaf(-kC, (float)w23.x, zacc[2]));
+      zacc[3] = __builtin_fmaf(pf, __builtin_fmaf(kC, (float)s23.y, (float)z23.y), __builtin_fmaf(-kC, (float)w23.y, zacc[3]));
+      pw[lane] = w01.x;
+      pw[64 + lane] = w01.y;
+      pw[128 + lane] = w23.x;
+      pw[192 + lane] = w23.y;
 #pragma unroll
       for (int k = 0; k < VB; ++k) reinterpret_cast<u32x4_t *>(vcl + lane * kVRow)[k] = vr.w[k];
-      pw[lane] = ph * wb;
       asm volatile("" ::: "memory");                   // LDS of one wave is ordered; keep the program order
 #pragma unroll
       for (int tb = 0; tb < 8; ++tb) {
@@ -388,9 +387,7 @@ __global__ __launch_bounds__(64 * kGenWaves, (gen_min_waves<KB, VB, VM>())) void
             VB == 2 ? ((uint32_t)*reinterpret_cast<const uint16_t *>(vcl + t0 * kVRow + 2 * vn) |
                        ((uint32_t)*reinterpret_cast<const uint16_t *>(vcl + (t0 + 1) * kVRow + 2 * vn) << 16))
                     : mb_spread_pair(vcl[t0 * kVRow + vn], vcl[(t0 + 1) * kVRow + vn]);
-        const int jv = vn >> 2;
-        const uint32_t sv0 = vrec[t0 * 4 + jv], sv1 = vrec[(t0 + 1) * 4 + jv];
-        const uint32_t P = *reinterpret_cast<const uint32_t *>(pw + t0);
+        const uint32_t P = *reinterpret_cast<const uint32_t *>(pw + 64 * ga + t0);
         v8h_t Aop;
         {
           const uint32_t a0 = __builtin_amdgcn_perm(P, P, selA[0]), a1 = __builtin_amdgcn_perm(P, P, selA[1]);
@@ -400,8 +397,8 @@ __global__ __launch_bounds__(64 * kGenWaves, (gen_min_waves<KB, VB, VM>())) void
           Aop = half8_t{h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
         }
         const uint32_t y02 = y & 0x33333333u, y13 = (y >> 2) & 0x33333333u;
-        o[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aop, mq_bvals<0>(y02, y13, sv0, sv1), o[0], 0, 0, 0);
-        o[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aop, mq_bvals<1>(y02, y13, sv0, sv1), o[1], 0, 0, 0);
+        o[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aop, mq_bcodes<0>(y02, y13), o[0], 0, 0, 0);
+        o[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aop, mq_bcodes<1>(y02, y13), o[1], 0, 0, 0);
       }
       asm volatile("" ::: "memory");                   // the next tile's writes come after these reads
     }
@@ -494,9 +491,11 @@ __global__ __launch_bounds__(64 * kGenWaves, (gen_min_waves<KB, VB, VM>())) void
   for (int g = 0; g < 4; ++g) zacc[g] = gen_wave_sum(zacc[g]);
   float *dst = a.partials + partial_row(a, wp, hq) * kPartialStride;
   if constexpr (VM) {
-    // head 0's accumulator rows sit in lanes 0..15: channels 8 vn .. 8 vn + 7
-    if (lane < 16) {
-      const float zl = (vn >> 2) == 0 ? zacc[0] : (vn >> 2) == 1 ? zacc[1] : (vn >> 2) == 2 ? zacc[2] : zacc[3];
+    // lane 16 g + vn holds the rows of group g for byte columns 2 vn and
+    // 2 vn + 1, channels 8 vn .. 8 vn + 7, which lie in group vn / 4: the
+    // lanes with g = vn / 4 hold the result
+    if ((lane >> 4) == ga) {
+      const float zl = ga == 0 ? zacc[0] : ga == 1 ? zacc[1] : ga == 2 ? zacc[2] : zacc[3];
       const float4v_t z4 = {zl, zl, zl, zl};
       reinterpret_cast<float4v_t *>(dst + 8 * vn)[0] = o[0] + z4;
       reinterpret_cast<float4v_t *>(dst + 8 * vn)[1] = o[1] + z4;
@@ -532,10 +531,8 @@ __global__ __launch_bounds__(64 * kGenWaves, (gen_min_waves<KB, VB, VM>())) void
   }
 }
 
-// The matrix-core value step prepares every B entry (code * s - fp16(1.5 s))
-// for one head only, so it saves little over the fp32 step: at 1- and 2-bit
-// values it is 0-3% faster, at 4-bit values (two planes, twice the entries
-// and matrix-core work) 10-50% slower.
+// The matrix-core value step at 1- and 2-bit values; 4-bit values keep the
+// fp32 step.
 template <int VB>
 constexpr bool gen_value_mfma() { return VB != 4; }
 hipError_t launch_attn_generic(const AttnArgs &a, int kbits, int vbits, hipStream_t stream) {

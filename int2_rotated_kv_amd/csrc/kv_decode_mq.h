@@ -127,6 +127,17 @@ __device__ __forceinline__ half8_t mq_bvals(uint32_t y02, uint32_t y13, uint32_t
   return half8_t{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
+// The same positions as plain codes (0..3, exact in fp16), for a value step
+// whose A operand carries the scale.
+template <int BLK>
+__device__ __forceinline__ half8_t mq_bcodes(uint32_t y02, uint32_t y13) {
+  const half2_t c0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y02, 2.0f, BLK);
+  const half2_t c1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y13, 2.0f, BLK);
+  const half2_t c2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y02, 2.0f, 2 + BLK);
+  const half2_t c3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y13, 2.0f, 2 + BLK);
+  return half8_t{c0.x, c0.y, c1.x, c1.y, c2.x, c2.y, c3.x, c3.y};
+}
+
 // Bytes b0, b1 spread to the 2-bit layout: b0 -> bits 0..15, b1 -> bits 16..31.
 __device__ __forceinline__ uint32_t mb_spread_pair(uint32_t b0, uint32_t b1) {
   uint32_t x = b0 | (b1 << 16);
