@@ -29,8 +29,10 @@
 // Scores never dequantize a key: with per-group scale s and zero z,
 //   q'.k_hat = sum_j s_j * (sum_{c in j} q'_c code_c) + z_j * (sum_{c in j} q'_c),
 // and the inner sum is an exact int32 dot product (v_dot8 on 4-bit code
-// nibbles and 4-bit query limbs).  Values: with w_t = fp16(p_t s_{t,j}),
-//   o'_c = sum_t w_t code_{t,c} - 1.5 sum_t w_t + sum_t p_t (z_{t,j} + 1.5 s_{t,j});
+// nibbles and 4-bit query limbs).  Values: with w_t = fp16(p_t s_{t,j} 2^kx)
+// (2^kx the wave's value pre-scale, which keeps every w a normal fp16
+// number below 2^15),
+//   o'_c = 2^-kx (sum_t w_t code_{t,c} - 1.5 sum_t w_t) + sum_t p_t (z_{t,j} + 1.5 s_{t,j});
 // the first term runs as v_dot2 over token pairs with codes placed in fp16
 // subnormal encodings (code * 2^(e-24)), accumulated in fp32.  Centering the
 // codes on 1.5 makes the fp16 rounding of w multiply code - 1.5 in
@@ -248,10 +250,7 @@ struct TileRegs {
 template <int GC>
 struct AttnState {
   float m[GC], l[GC], zacc[GC][2], wsum[GC][2], acc[GC][64];
-  // Weights are kept below 2^slack (log2 units above the reference m):
-  // kSlack, or 0 once the wave has met a value scale of 2^11 or more, so
-  // that w = p * s stays inside the fp16 range for every finite fp16 scale.
-  float slack;
+  ValuePrescale ps;           // acc and wsum carry the factor 2^kx
 };
 
 
@@ -290,8 +289,20 @@ __device__ __forceinline__ void attn_tile(AttnState<GC> &st, const QueryLimbs<GC
   const half2_t vsA = __builtin_bit_cast(half2_t, r.vsA), vzA = __builtin_bit_cast(half2_t, r.vzA);
   const half2_t vsB = __builtin_bit_cast(half2_t, r.vsB), vzB = __builtin_bit_cast(half2_t, r.vzB);
   half2_t wp[GC][2];
-  // a value scale that could overflow w at the current slack: lower the slack
-  const bool big = st.slack > 0.0f && __builtin_amdgcn_ballot_w64(big_value_scale(r.vsA, r.vsB));
+  {
+    // a value scale beyond the wave's pre-scale: lower it (wave-uniform, rare)
+    const uint32_t mb = max_half_bits(r.vsA, r.vsB);
+    if (__builtin_amdgcn_ballot_w64(mb >= st.ps.lim)) {
+      const float f = prescale_lower(st.ps, mb);
+#pragma unroll
+      for (int g = 0; g < GC; ++g) {
+        st.wsum[g][0] *= f;
+        st.wsum[g][1] *= f;
+#pragma unroll
+        for (int i = 0; i < 64; ++i) st.acc[g][i] *= f;
+      }
+    }
+  }
 #pragma unroll
   for (int g = 0; g < GC; ++g) {
     float xa, xb;
@@ -314,8 +325,7 @@ __device__ __forceinline__ void attn_tile(AttnState<GC> &st, const QueryLimbs<GC
       xa = va ? __builtin_fmaf(q.qstep[g], ra, -st.m[g]) : kNegInf;
       xb = vb ? __builtin_fmaf(q.qstep[g], rb, -st.m[g]) : kNegInf;
     }
-    if (__builtin_amdgcn_ballot_w64(fmaxf(xa, xb) > st.slack) || big) {     // wave-uniform
-      if (big) st.slack = 0.0f;              // from here on p <= 1
+    if (__builtin_amdgcn_ballot_w64(fmaxf(xa, xb) > kSlack)) {     // wave-uniform
       const float ya = va ? (PRE ? r.sA : q.qstep[g] * ra) : kNegInf;
       const float yb = vb ? (PRE ? r.sB : q.qstep[g] * rb) : kNegInf;
       float mx = fmaxf(ya, yb);
@@ -348,8 +358,8 @@ __device__ __forceinline__ void attn_tile(AttnState<GC> &st, const QueryLimbs<GC
       st.zacc[g][gi] = __builtin_fmaf(pA, __builtin_fmaf(1.5f, svA, (float)vzA[gi]),
                                       __builtin_fmaf(pB, __builtin_fmaf(1.5f, svB, (float)vzB[gi]),
                                                      st.zacc[g][gi]));
-      wp[g][gi].x = (_Float16)(pA * svA);
-      wp[g][gi].y = (_Float16)(pB * svB);
+      wp[g][gi].x = (_Float16)(pA * (svA * st.ps.f));
+      wp[g][gi].y = (_Float16)(pB * (svB * st.ps.f));
       st.wsum[g][gi] = __builtin_amdgcn_fdot2(wp[g][gi], __builtin_bit_cast(half2_t, kHalf2Ones),
                                               st.wsum[g][gi], false);
     }
@@ -509,10 +519,10 @@ __global__ __launch_bounds__(64 * WPB) void kv_int2_decode_attn(AttnArgs a) {
   }
 
   AttnState<GC> st;
+  st.ps = prescale_init();
 #pragma unroll
   for (int g = 0; g < GC; ++g) {
     st.m[g] = kNegInf; st.l[g] = 0.0f; st.zacc[g][0] = 0.0f; st.zacc[g][1] = 0.0f;
-    st.slack = kSlack;
     st.wsum[g][0] = 0.0f; st.wsum[g][1] = 0.0f;
 #pragma unroll
     for (int i = 0; i < 64; ++i) st.acc[g][i] = 0.0f;
@@ -624,8 +634,9 @@ __global__ __launch_bounds__(64 * WPB) void kv_int2_decode_attn(AttnArgs a) {
 #pragma unroll
   for (int g = 0; g < GC; ++g) {
     float l = st.l[g];
-    float z0 = __builtin_fmaf(-1.5f, st.wsum[g][0], st.zacc[g][0]);
-    float z1 = __builtin_fmaf(-1.5f, st.wsum[g][1], st.zacc[g][1]);
+    // acc and wsum carry the pre-scale 2^kx, zacc does not
+    float z0 = __builtin_fmaf(-1.5f * st.ps.inv, st.wsum[g][0], st.zacc[g][0]);
+    float z1 = __builtin_fmaf(-1.5f * st.ps.inv, st.wsum[g][1], st.zacc[g][1]);
     // sum over the 32 token slots sharing h: lane bits 1..3 inside the row
     // (DPP), then the rows (xor 16, xor 32)
     auto reduce = [](float v) {
@@ -645,7 +656,7 @@ __global__ __launch_bounds__(64 * WPB) void kv_int2_decode_attn(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 64; ++i) {
         const int x = i & 7;
-        dst[64 * h + i] = __builtin_fmaf(st.acc[g][i], chan_unscale(x), i < 32 ? z0 : z1);
+        dst[64 * h + i] = __builtin_fmaf(st.acc[g][i], chan_unscale(x) * st.ps.inv, i < 32 ? z0 : z1);
       }
       if (h == 0) {
         dst[128] = st.m[g];

@@ -336,16 +336,45 @@ __device__ __forceinline__ constexpr float chan_unscale(int x) {
 
 // Lazy rescaling: the running reference m is moved only when a score
 // exceeds it by more than kSlack (log2 units), so p = 2^(s - m) stays below
-// 2^kSlack and w = p * s_v stays far inside the fp16 range.  The partial
-// (m, l, o') is exact for any reference m, so the merge is unchanged.
+// 2^kSlack.  The partial (m, l, o') is exact for any reference m, so the
+// merge is unchanged.
 constexpr float kSlack = 4.0f;
 
-// Any of the four fp16 value scales (two per dword, all >= 0) at 2^11 or
-// above: with p < 2^kSlack, p * s could then round past the fp16 range.
-// Adding 0x1800 to each half sets its bit 15 exactly for 0x6800 (= 2048)
-// and above; finite halves stay below 0x10000, so nothing carries across.
-__device__ __forceinline__ bool big_value_scale(uint32_t s0, uint32_t s1) {
-  return (((s0 + 0x18001800u) | (s1 + 0x18001800u)) & 0x80008000u) != 0u;
+// Value pre-scale of the one-head decode kernels, whose fp16 weights are
+// w = fp16(p s 2^kx) with one power of two 2^kx per wave.  kx = 25 - E for
+// the largest biased fp16 exponent field E (at least 1) among the value
+// scales the wave has met, so s 2^kx < 2^11 and, with p < 2^kSlack,
+// w < 2^15 stays inside the fp16 range for every finite scale; the largest
+// scales give w >= p 2^10, so the weights stay normal fp16 numbers (2^-11
+// relative rounding) even for scales that are fp16 subnormals.  kx only
+// goes down; the accumulators that carry the factor are multiplied by
+// 2^(new - old) when it does, an exact power of two.
+struct ValuePrescale {
+  int kx;          // -6 .. 24, wave-uniform
+  uint32_t lim;    // scale magnitude bits from which kx must go down: (26 - kx) << 10
+  float f, inv;    // 2^kx, 2^-kx
+};
+__device__ __forceinline__ ValuePrescale prescale_init() {
+  return ValuePrescale{24, 2u << 10, 16777216.0f, 1.0f / 16777216.0f};
+}
+// Largest magnitude bits of four fp16 value scales (two per dword); the
+// bits of a magnitude order like its value.
+__device__ __forceinline__ uint32_t max_half_bits(uint32_t s0, uint32_t s1) {
+  s0 &= 0x7FFF7FFFu;
+  s1 &= 0x7FFF7FFFu;
+  return umax32(umax32(s0 & 0xFFFFu, s0 >> 16), umax32(s1 & 0xFFFFu, s1 >> 16));
+}
+// Lowers kx to fit the wave's largest scale (mbits from max_half_bits);
+// returns 2^(new - old) for the accumulators.  Call wave-uniformly.
+__device__ __forceinline__ float prescale_lower(ValuePrescale &ps, uint32_t mbits) {
+  const int E = (int)(wave_max_u32(mbits) >> 10);     // 31 only for inf / nan scales
+  const int kx = 25 - (E > 1 ? E : 1);
+  const float f = __builtin_amdgcn_ldexpf(1.0f, kx - ps.kx);
+  ps.kx = kx;
+  ps.lim = (uint32_t)(26 - kx) << 10;
+  ps.f = __builtin_amdgcn_ldexpf(1.0f, kx);
+  ps.inv = __builtin_amdgcn_ldexpf(1.0f, -kx);
+  return f;
 }
 
 constexpr uint32_t kHalf2Ones = 0x3C003C00u;   // (1.0, 1.0) in fp16

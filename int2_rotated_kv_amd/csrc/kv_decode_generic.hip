@@ -292,11 +292,10 @@ __global__ __launch_bounds__(64 * kGenWaves, (gen_min_waves<KB, VB, VM>())) void
   const int64_t krow0 = bh * a.kT_cap + a.t_begin - a.skip;   // row 0 of the shifted grid
   const int64_t vrow0 = bh * a.vT_cap + a.t_begin - a.skip;
 
-  // Weights stay below 2^slack: kSlack, or, in the matrix-core value step,
-  // 0 once the wave has met a value scale of 2^11 or more, so that
-  // w = fp16(p s) stays inside the fp16 range for every finite scale (the
-  // fp32 step needs no switch).
-  float slack = kSlack;
+  // matrix-core value step: the weights carry the wave's value pre-scale
+  // 2^kx (normal fp16 numbers below 2^15 for every finite scale), and so
+  // does o; the fp32 step needs none
+  ValuePrescale ps = prescale_init();
   auto token = [&](const auto &kr, const GenRow<VB> &vr, bool valid) {
     float s = 0.0f;
     {
@@ -322,11 +321,7 @@ __global__ __launch_bounds__(64 * kGenWaves, (gen_min_waves<KB, VB, VM>())) void
     s *= qstep;
     s = valid ? s : kNegInf;
     const float mt = gen_wave_max(s);
-    if constexpr (VM) {
-      const uint32_t vs0 = vr.s.x, vs1 = vr.s.y;
-      if (slack > 0.0f && __builtin_amdgcn_ballot_w64(big_value_scale(vs0, vs1))) slack = 0.0f;
-    }
-    if (mt > m_run + slack) {                          // wave-uniform
+    if (mt > m_run + kSlack) {                         // wave-uniform
       const float f = __builtin_amdgcn_exp2f(m_run - mt);
 #pragma unroll
       for (int i = 0; i < (VM ? 1 : kD); ++i) acc[i] *= f;
@@ -349,11 +344,12 @@ __global__ __launch_bounds__(64 * kGenWaves, (gen_min_waves<KB, VB, VM>())) void
           acc[32 * g + i] = __builtin_fmaf(pv, gen_code<VB>(vr, 32 * g + i), acc[32 * g + i]);
       }
     } else {
-      // Weights w_g = fp16(p~ s_g) with p~ = fp16(p), B entries the plain
-      // codes over the 2-bit layout (1-bit codes spread to 2-bit fields).
-      // Centered on c = (2^VB - 1) / 2: o' = sum w code - c sum w +
-      // sum p~ (z + c s), so the rounding of w multiplies code - c; the last
-      // two terms are accumulated per token lane.
+      // Weights w_g = fp16(p~ s_g 2^kx) with p~ = fp16(p), B entries the
+      // plain codes over the 2-bit layout (1-bit codes spread to 2-bit
+      // fields).  Centered on c = (2^VB - 1) / 2:
+      // o' = 2^-kx (sum w code - c sum w) + sum p~ (z + c s), so the rounding
+      // of w multiplies code - c; the last two terms are accumulated per
+      // token lane, without the pre-scale.
       static_assert(VB == 1 || VB == 2, "matrix-core value step: 1- and 2-bit values");
       constexpr float kC = 0.5f * (float)((1 << VB) - 1);
       uint8_t *vcl = vcl_all[wave];
@@ -365,17 +361,25 @@ __global__ __launch_bounds__(64 * kGenWaves, (gen_min_waves<KB, VB, VM>())) void
       // bit cast of an element such as vr.s.y as a read of the vector's first
       // element
       const uint32_t vs0 = vr.s.x, vs1 = vr.s.y, vz0 = vr.z.x, vz1 = vr.z.y;
+      {
+        // a value scale beyond the wave's pre-scale: lower it (wave-uniform, rare)
+        const uint32_t mb = max_half_bits(vs0, vs1);
+        if (__builtin_amdgcn_ballot_w64(mb >= ps.lim)) {
+          const float f = prescale_lower(ps, mb);
+          o[0] *= f;
+          o[1] *= f;
+        }
+      }
       const half2_t s01 = __builtin_bit_cast(half2_t, vs0), s23 = __builtin_bit_cast(half2_t, vs1);
       const half2_t z01 = __builtin_bit_cast(half2_t, vz0), z23 = __builtin_bit_cast(half2_t, vz1);
-      const half2_t w01 = s01 * half2_t{ph, ph}, w23 = s23 * half2_t{ph, ph};
-      zacc[0] = __builtin_fmaf(pf, __builtin_fmaf(kC, (float)s01.x, (float)z01.x), __builtin_fmaf(-kC, (float)w01.x, zacc[0]));
-      zacc[1] = __builtin_fmaf(pf, __builtin_fmaf(kC, (float)s01.y, (float)z01.y), __builtin_fmaf(-kC, (float)w01.y, zacc[1]));
-      zacc[2] = __builtin_fmaf(pf, __builtin_fmaf(kC, (float)s23.x, (float)z23.x), __builtin_fmaf(-kC, (float)w23.x, zacc[2]));
-      zacc[3] = __builtin_fmaf(pf, __builtin_fmaf(kC, (float)s23.y, (float)z23.y), __builtin_fmaf(-kC, (float)w23.y, zacc[3]));
-      pw[lane] = w01.x;
-      pw[64 + lane] = w01.y;
-      pw[128 + lane] = w23.x;
-      pw[192 + lane] = w23.y;
+      const float sg[4] = {(float)s01.x, (float)s01.y, (float)s23.x, (float)s23.y};
+      const float zg[4] = {(float)z01.x, (float)z01.y, (float)z23.x, (float)z23.y};
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const _Float16 w = (_Float16)(pf * (sg[g] * ps.f));
+        zacc[g] = __builtin_fmaf(pf, __builtin_fmaf(kC, sg[g], zg[g]), __builtin_fmaf(-kC * ps.inv, (float)w, zacc[g]));
+        pw[64 * g + lane] = w;
+      }
 #pragma unroll
       for (int k = 0; k < VB; ++k) reinterpret_cast<u32x4_t *>(vcl + lane * kVRow)[k] = vr.w[k];
       asm volatile("" ::: "memory");                   // LDS of one wave is ordered; keep the program order
@@ -497,8 +501,9 @@ __global__ __launch_bounds__(64 * kGenWaves, (gen_min_waves<KB, VB, VM>())) void
     if ((lane >> 4) == ga) {
       const float zl = ga == 0 ? zacc[0] : ga == 1 ? zacc[1] : ga == 2 ? zacc[2] : zacc[3];
       const float4v_t z4 = {zl, zl, zl, zl};
-      reinterpret_cast<float4v_t *>(dst + 8 * vn)[0] = o[0] + z4;
-      reinterpret_cast<float4v_t *>(dst + 8 * vn)[1] = o[1] + z4;
+      const float4v_t u4 = {ps.inv, ps.inv, ps.inv, ps.inv};
+      reinterpret_cast<float4v_t *>(dst + 8 * vn)[0] = o[0] * u4 + z4;
+      reinterpret_cast<float4v_t *>(dst + 8 * vn)[1] = o[1] * u4 + z4;
     }
     if (lane == 0) {
       dst[128] = m_run;

@@ -309,3 +309,43 @@ def test_decode_large_value_scales(kind):
     err = normwise_rel_err(o, ref)
     _report(f"decode large value scales {kind}", err=err, max_abs_out=float(np.abs(ref).max()))
     assert err <= 2e-3
+
+
+
+@pytest.mark.parametrize("kind", ["g1_hadamard", "g1_none", "gqa_dense", "k1v1", "k1v2", "k2v1", "k4v2", "k4v4",
+                                  "k2v1_gqa"])
+def test_decode_small_value_scales(kind):
+    """Value scales in fp16's subnormal range (values of order 1e-6): every
+    weight that enters an fp16 operand stays a normal fp16 number relative
+    to its own head's values, so the output keeps the relative tolerance of
+    ordinary inputs (fp32 query and output; the oracle on the same bytes)."""
+    rng = np.random.default_rng(7 + sum(map(ord, kind)))
+    B, Hkv, T = 2, 2, 900
+    G = 4 if "gqa" in kind else 1
+    Hq = Hkv * G
+    kbits, vbits = {"k1v1": (1, 1), "k1v2": (1, 2), "k2v1": (2, 1), "k4v2": (4, 2), "k4v4": (4, 4),
+                    "k2v1_gqa": (2, 1)}.get(kind, (2, 2))
+    rot = "dense" if "dense" in kind else "none" if kind == "g1_none" else "hadamard"
+    kp, ks, kz = _random_cache_np(rng, B, Hkv, T, kbits, 0.0)
+    L = (1 << vbits) - 1
+    vp = O.pack_codes(rng.integers(0, L + 1, size=(B, Hkv, T, 128)).astype(np.uint8), vbits)
+    vs = rng.uniform(1e-7, 3e-6, size=(B, Hkv, T, 4))
+    vz = -0.5 * L * vs * rng.uniform(0.8, 1.2, size=vs.shape)
+    vs, vz = vs.astype(np.float16), vz.astype(np.float16)
+    assert float(vs.max()) < 2.0 ** -14                # every value scale is an fp16 subnormal
+    R = None
+    if rot == "dense":
+        qm = [np.linalg.qr(rng.standard_normal((128, 128))) for _ in range(Hkv)]
+        R = np.stack([q * np.sign(np.diag(r))[None, :] for q, r in qm]).astype(np.float32)
+    q = rng.standard_normal((B, Hq, 128)).astype(np.float32)
+    kc = kvq.Int2Cache(*(torch.from_numpy(np.ascontiguousarray(a)).to(DEV) for a in (kp, ks, kz)), bits=kbits)
+    vc = kvq.Int2Cache(*(torch.from_numpy(np.ascontiguousarray(a)).to(DEV) for a in (vp, vs, vz)), bits=vbits)
+    out = kvq.kvq_decode_attention(torch.from_numpy(q).to(DEV), kc, vc, 3, T, rot=rot,
+                                   R=torch.from_numpy(R).to(DEV) if R is not None else None)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    Rm = R if rot == "dense" else rot_matrix(rot)
+    ref = O.decode_attention(q, (kp, ks, kz), (vp, vs, vz), 3, T, Rm)
+    err = normwise_rel_err(o, ref)
+    _report(f"decode small value scales {kind}", err=err, max_abs_out=float(np.abs(ref).max()))
+    assert err <= 2e-3
