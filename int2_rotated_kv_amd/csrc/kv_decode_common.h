@@ -328,6 +328,33 @@ __device__ __forceinline__ int64_t partial_row(const AttnArgs &a, const WavePlac
   return w.first * a.Hq + (int64_t)hq * w.S + w.split;
 }
 
+// Issue priority tied to a wave's progress through its full tiles: 3 in the
+// first quarter, 2, 1, then 0 in the last quarter (grouped-query kernels).
+// Two attention waves that share a SIMD have the same work, but at equal
+// priority the older one wins issue arbitration and finishes well ahead of
+// the younger one, which then runs the last part alone.  With the priority
+// falling as a wave advances, the wave that is behind is favoured and the
+// two finish closer together.  `done` is wave-uniform.
+struct ProgressPrio {
+  int64_t q1, q2, q3;
+  int level;
+  __device__ __forceinline__ explicit ProgressPrio(int64_t total)
+      : q1(total / 4), q2(total / 2), q3(total - total / 4), level(3) {
+    __builtin_amdgcn_s_setprio(3);
+  }
+  __device__ __forceinline__ void update(int64_t done) {
+    const int want = 3 - (done >= q1) - (done >= q2) - (done >= q3);
+    if (want == level) return;
+    level = want;
+    switch (want) {
+      case 2: __builtin_amdgcn_s_setprio(2); break;
+      case 1: __builtin_amdgcn_s_setprio(1); break;
+      case 0: __builtin_amdgcn_s_setprio(0); break;
+      default: __builtin_amdgcn_s_setprio(3); break;
+    }
+  }
+};
+
 // Reassemble the fp16 subnormal channel factor: code at position x of a
 // 16-bit half is read with weight 2^(2x-24) (x <= 4) or 2^(2x-30) (x >= 5).
 __device__ __forceinline__ constexpr float chan_unscale(int x) {

@@ -362,8 +362,10 @@ __global__ __launch_bounds__(64 * kMqWaves) void kv_int2_decode_attn_gqa(AttnArg
       return TileRows{r, r};
     };
     MqTile t0 = load_full(row_of(0)), t1;
+    ProgressPrio prio(mine);
     int64_t i = 0;
     for (; i + 2 <= mine; i += 2) {
+      prio.update(i);
       t1 = load_full(row_of(i + 1));
       run(t0, 0, 64);
       t0 = load_full(row_of(i + 2));

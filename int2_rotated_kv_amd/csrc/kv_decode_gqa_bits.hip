@@ -355,8 +355,10 @@ __global__ __launch_bounds__(64 * kMqWaves, 2) void kv_quant_decode_attn_gqa(Att
       return TileRows{r, r};
     };
     MbTile<KB, VB> t0 = load_full(row_of(0)), t1;
+    ProgressPrio prio(mine);
     int64_t i = 0;
     for (; i + 2 <= mine; i += 2) {
+      prio.update(i);
       t1 = load_full(row_of(i + 1));
       run(t0, 0, 64);
       t0 = load_full(row_of(i + 2));
