@@ -723,6 +723,87 @@ __device__ __forceinline__ const uint16_t *fp16_row(const uint16_t *sink, const 
   return t < n_sink ? sink + (bkv * n_sink + t) * kD : res + (bkv * n_res + (t - n_sink)) * kD;
 }
 
+// Merge of one (b, query head) by one wave, for the common case: one INT2
+// range for the whole batch, no fp16 tokens, Hadamard or no rotation.  Lane
+// l owns channels 2l and 2l + 1; the split weights 2^(m_i - M) and the sums
+// are wave reductions, and the FWHT over the 128 merged channels is one
+// in-lane butterfly and six lane exchanges, so no LDS or barrier is needed.
+// Same merge as kv_combine_unrotate (summation order aside).
+// grid: ceil(B*Hq / kWaveCombineWaves) workgroups of kWaveCombineWaves waves.
+constexpr int kWaveCombineWaves = 4;
+__global__ __launch_bounds__(64 * kWaveCombineWaves) void kv_combine_wave(CombineArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t bh = (int64_t)blockIdx.x * kWaveCombineWaves + (threadIdx.x >> 6);   // b*Hq + hq
+  if (bh >= a.B * a.Hq) return;                  // whole wave leaves; no barrier follows
+  const int64_t ns = a.n_splits;
+  const float *part = a.partials + bh * ns * kPartialStride;   // rows (b*Hq + hq)*S + split
+  // M = max m_i, L = sum 2^(m_i - M) l_i
+  float mloc = kNegInf;
+  for (int64_t i = lane; i < ns; i += 64) mloc = fmaxf(mloc, part[i * kPartialStride + 128]);
+  for (int k = 1; k < 64; k <<= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, k, 64));
+  const float M = mloc;
+  float lloc = 0.0f;
+  for (int64_t i = lane; i < ns; i += 64) {
+    const float mi = part[i * kPartialStride + 128];
+    const float wi = (mi == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(mi - M);
+    lloc = __builtin_fmaf(wi, part[i * kPartialStride + 129], lloc);
+  }
+  for (int k = 1; k < 64; k <<= 1) lloc += __shfl_xor(lloc, k, 64);
+  const float L = lloc;
+  // weighted sum of the partial outputs, eight splits' loads in flight
+  float o0[2] = {0.0f, 0.0f}, o1[2] = {0.0f, 0.0f};
+  int64_t i = 0;
+  for (; i + 8 <= ns; i += 8) {
+    float2_t v[8];
+    float m8[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      v[u] = *reinterpret_cast<const float2_t *>(part + (i + u) * kPartialStride + 2 * lane);
+      m8[u] = part[(i + u) * kPartialStride + 128];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float w = (m8[u] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(m8[u] - M);
+      o0[u & 1] = __builtin_fmaf(w, v[u].x, o0[u & 1]);
+      o1[u & 1] = __builtin_fmaf(w, v[u].y, o1[u & 1]);
+    }
+  }
+  for (; i < ns; ++i) {
+    const float2_t v = *reinterpret_cast<const float2_t *>(part + i * kPartialStride + 2 * lane);
+    const float mi = part[i * kPartialStride + 128];
+    const float w = (mi == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(mi - M);
+    o0[0] = __builtin_fmaf(w, v.x, o0[0]);
+    o1[0] = __builtin_fmaf(w, v.y, o1[0]);
+  }
+  float x0 = o0[0] + o0[1], x1 = o1[0] + o1[1];
+  if (a.rot == 1) {
+    // normalized FWHT: channels (2l, 2l+1) in lane, then channel c pairs with
+    // c ^ 2k, i.e. lane l with lane l ^ k; the lower channel takes the sum
+    {
+      const float s = x0 + x1, d = x0 - x1;
+      x0 = s;
+      x1 = d;
+    }
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) {
+      const float p0 = __shfl_xor(x0, k, 64), p1 = __shfl_xor(x1, k, 64);
+      const bool upper = (lane & k) != 0;
+      x0 = upper ? p0 - x0 : x0 + p0;
+      x1 = upper ? p1 - x1 : x1 + p1;
+    }
+    x0 *= 0.08838834764831845f;
+    x1 *= 0.08838834764831845f;
+  }
+  const bool any = M != kNegInf && L > 0.0f;     // no token at all: 0
+  const float r0 = any ? x0 / L : 0.0f, r1 = any ? x1 / L : 0.0f;
+  if (a.out_f32) {
+    *reinterpret_cast<float2_t *>(reinterpret_cast<float *>(a.out) + bh * kD + 2 * lane) = float2_t{r0, r1};
+  } else {
+    const half2_t h2 = {(_Float16)r0, (_Float16)r1};
+    *reinterpret_cast<half2_t *>(reinterpret_cast<_Float16 *>(a.out) + bh * kD + 2 * lane) = h2;
+  }
+}
+
 // grid: B*Hq blocks of kCombineThreads threads; threads c < 128 own channel c
 // in the merge and the un-rotation.  Dynamic LDS: (most splits of one head)
 // + n_sink + n_res floats.
@@ -1022,7 +1103,11 @@ static hipError_t launch_decode_prerope(const DecodeArgs &d, hipStream_t stream)
   c.res_k = d.res_k; c.res_v = d.res_v; c.n_res = d.n_res;
   c.out = d.out;
   const size_t lds = (size_t)(d.n_splits + d.n_sink + d.n_res) * sizeof(float);
-  hipLaunchKernelGGL(kv_combine_unrotate, dim3((unsigned)(d.B * d.Hq)), dim3(kCombineThreads), lds, stream, c);
+  if (c.t_ends == nullptr && c.n_sink == 0 && c.n_res == 0 && (c.rot == 0 || c.rot == 1))
+      hipLaunchKernelGGL(kv_combine_wave, dim3((unsigned)((d.B * d.Hq + kWaveCombineWaves - 1) / kWaveCombineWaves)),
+                         dim3(64 * kWaveCombineWaves), 0, stream, c);
+    else
+      hipLaunchKernelGGL(kv_combine_unrotate, dim3((unsigned)(d.B * d.Hq)), dim3(kCombineThreads), lds, stream, c);
   return hipGetLastError();
 }
 
@@ -1092,7 +1177,11 @@ hipError_t launch_decode(const DecodeArgs &d, hipStream_t stream) {
     c.out = d.out;
     const int64_t lds_splits = c.t_ends != nullptr ? varlen_lds_splits(d.B, d.n_splits) : d.n_splits;
     const size_t lds = (size_t)(lds_splits + d.n_sink + d.n_res) * sizeof(float);
-    hipLaunchKernelGGL(kv_combine_unrotate, dim3((unsigned)(d.B * d.Hq)), dim3(kCombineThreads), lds, stream, c);
+    if (c.t_ends == nullptr && c.n_sink == 0 && c.n_res == 0 && (c.rot == 0 || c.rot == 1))
+      hipLaunchKernelGGL(kv_combine_wave, dim3((unsigned)((d.B * d.Hq + kWaveCombineWaves - 1) / kWaveCombineWaves)),
+                         dim3(64 * kWaveCombineWaves), 0, stream, c);
+    else
+      hipLaunchKernelGGL(kv_combine_unrotate, dim3((unsigned)(d.B * d.Hq)), dim3(kCombineThreads), lds, stream, c);
     return hipGetLastError();
   }
 }
