@@ -418,10 +418,14 @@ def main():
         prep_kernel = rot == "dense"                 # except a dense R's
     elif (kbits, vbits) != (2, 2):                 # grouped-query b-bit kernel, prepared query
         d_kernel, d_src = f"kv_quant_decode_attn_gqa<{kbits},{vbits}>", "kv_decode_gqa_bits.hip"
+    # the merge runs one wave per head for one INT2 range, no fp16 tokens and
+    # the Hadamard or no rotation; a block per head otherwise
+    merge_kernel = ("kv_combine_wave" if not args.varlen and not P and not fp16 and rot in ("hadamard", "none")
+                    else "kv_combine_unrotate")
     roof_d = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
               "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
               "traffic": traffic_from_profile(d_kernel, workload, os.path.join(csrc, d_src)),
-              "kernel": f"decode call ({'kv_prep_query + ' if prep_kernel else ''}{d_kernel} + kv_combine_unrotate)",
+              "kernel": f"decode call ({'kv_prep_query + ' if prep_kernel else ''}{d_kernel} + {merge_kernel})",
               "algorithmic_bytes_per_launch": d_bytes,
               "bytes_per_unit": d_unit, "unit_of_work": "(INT2 token, kv head)",
               "units_per_launch": int2_tokens * H, "avg_ms": round(d_ms, 4)}
@@ -432,7 +436,7 @@ def main():
         roof_d = {"bound": "alu", "achieved": round(tops, 2), "peak": round(PEAK_VALU_TOPS, 2),
                   "unit": "Top/s", "frac": round(tops / PEAK_VALU_TOPS, 4), "traffic": None,
                   "kernel": f"decode call (kv_rope_table + kv_prerope_scores<{GHP}> + kv_int2_decode_attn<4, true>"
-                            " + kv_combine_unrotate)",
+                            f" + {merge_kernel})",
                   "algorithmic_ops_per_launch": ops, "ops_per_unit": prerope_ops_per_unit(GHP, cfg.G),
                   "unit_of_work": "(INT2 token, kv head)", "units_per_launch": int2_tokens * H,
                   "avg_ms": round(d_ms, 4), "hbm_gbs": round(dec_gbs, 1)}
