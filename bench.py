@@ -419,8 +419,8 @@ def main():
     elif (kbits, vbits) != (2, 2):                 # grouped-query b-bit kernel, prepared query
         d_kernel, d_src = f"kv_quant_decode_attn_gqa<{kbits},{vbits}>", "kv_decode_gqa_bits.hip"
     # the merge runs one wave per head for one INT2 range, no fp16 tokens and
-    # the Hadamard or no rotation; a block per head otherwise
-    merge_kernel = ("kv_combine_wave" if not args.varlen and not P and not fp16 and rot in ("hadamard", "none")
+    # no dense rotation, a block per head otherwise
+    merge_kernel = ("kv_combine_wave" if not args.varlen and not P and not fp16 and rot != "dense"
                     else "kv_combine_unrotate")
     roof_d = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
               "frac": round(dec_gbs / PEAK_HBM_GBS, 4),

@@ -724,11 +724,14 @@ __device__ __forceinline__ const uint16_t *fp16_row(const uint16_t *sink, const 
 }
 
 // Merge of one (b, query head) by one wave, for the common case: one INT2
-// range for the whole batch, no fp16 tokens, Hadamard or no rotation.  Lane
-// l owns channels 2l and 2l + 1; the split weights 2^(m_i - M) and the sums
-// are wave reductions, and the FWHT over the 128 merged channels is one
-// in-lane butterfly and six lane exchanges, so no LDS or barrier is needed.
-// Same merge as kv_combine_unrotate (summation order aside).
+// range for the whole batch, no fp16 tokens, and no rotation, the Hadamard
+// or the reordered Hadamard.  Lane l owns channels 2l and 2l + 1; the split
+// weights 2^(m_i - M) and the sums are wave reductions.  Un-rotation: the
+// FWHT over the 128 merged channels is one in-lane butterfly and six lane
+// exchanges, then, for the reordered Hadamard, output j goes to channel
+// pi(j).  No LDS or barrier.  Same merge as kv_combine_unrotate (summation
+// order aside).  (A dense R^T applied by one wave, from the lane's two rows
+// of R, measured slower than the block's matvec.)
 // grid: ceil(B*Hq / kWaveCombineWaves) workgroups of kWaveCombineWaves waves.
 constexpr int kWaveCombineWaves = 4;
 __global__ __launch_bounds__(64 * kWaveCombineWaves) void kv_combine_wave(CombineArgs a) {
@@ -776,7 +779,9 @@ __global__ __launch_bounds__(64 * kWaveCombineWaves) void kv_combine_wave(Combin
     o1[0] = __builtin_fmaf(w, v.y, o1[0]);
   }
   float x0 = o0[0] + o0[1], x1 = o1[0] + o1[1];
-  if (a.rot == 1) {
+  const int hq = (int)(bh % a.Hq);
+  const int hkv = hq / (a.Hq / a.Hkv);
+  if (a.rot == 1 || a.rot == 3) {
     // normalized FWHT: channels (2l, 2l+1) in lane, then channel c pairs with
     // c ^ 2k, i.e. lane l with lane l ^ k; the lower channel takes the sum
     {
@@ -796,6 +801,19 @@ __global__ __launch_bounds__(64 * kWaveCombineWaves) void kv_combine_wave(Combin
   }
   const bool any = M != kNegInf && L > 0.0f;     // no token at all: 0
   const float r0 = any ? x0 / L : 0.0f, r1 = any ? x1 / L : 0.0f;
+  if (a.rot == 3) {
+    // o' R^T = (o' H / sqrt(d)) P^T: output j goes to channel pi(j)
+    const int32_t *pi = a.perm + (int64_t)hkv * kD;
+    const int c0 = pi[2 * lane] & (kD - 1), c1 = pi[2 * lane + 1] & (kD - 1);
+    if (a.out_f32) {
+      reinterpret_cast<float *>(a.out)[bh * kD + c0] = r0;
+      reinterpret_cast<float *>(a.out)[bh * kD + c1] = r1;
+    } else {
+      reinterpret_cast<_Float16 *>(a.out)[bh * kD + c0] = (_Float16)r0;
+      reinterpret_cast<_Float16 *>(a.out)[bh * kD + c1] = (_Float16)r1;
+    }
+    return;
+  }
   if (a.out_f32) {
     *reinterpret_cast<float2_t *>(reinterpret_cast<float *>(a.out) + bh * kD + 2 * lane) = float2_t{r0, r1};
   } else {
@@ -1103,7 +1121,7 @@ static hipError_t launch_decode_prerope(const DecodeArgs &d, hipStream_t stream)
   c.res_k = d.res_k; c.res_v = d.res_v; c.n_res = d.n_res;
   c.out = d.out;
   const size_t lds = (size_t)(d.n_splits + d.n_sink + d.n_res) * sizeof(float);
-  if (c.t_ends == nullptr && c.n_sink == 0 && c.n_res == 0 && (c.rot == 0 || c.rot == 1))
+  if (c.t_ends == nullptr && c.n_sink == 0 && c.n_res == 0 && c.rot != 2)
       hipLaunchKernelGGL(kv_combine_wave, dim3((unsigned)((d.B * d.Hq + kWaveCombineWaves - 1) / kWaveCombineWaves)),
                          dim3(64 * kWaveCombineWaves), 0, stream, c);
     else
@@ -1177,7 +1195,7 @@ hipError_t launch_decode(const DecodeArgs &d, hipStream_t stream) {
     c.out = d.out;
     const int64_t lds_splits = c.t_ends != nullptr ? varlen_lds_splits(d.B, d.n_splits) : d.n_splits;
     const size_t lds = (size_t)(lds_splits + d.n_sink + d.n_res) * sizeof(float);
-    if (c.t_ends == nullptr && c.n_sink == 0 && c.n_res == 0 && (c.rot == 0 || c.rot == 1))
+    if (c.t_ends == nullptr && c.n_sink == 0 && c.n_res == 0 && c.rot != 2)
       hipLaunchKernelGGL(kv_combine_wave, dim3((unsigned)((d.B * d.Hq + kWaveCombineWaves - 1) / kWaveCombineWaves)),
                          dim3(64 * kWaveCombineWaves), 0, stream, c);
     else
